@@ -1,0 +1,234 @@
+"""ctypes wrapper around the plain-C oracle (``oracle/sv_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` are the only
+callers.  The product path (``token_sampling_amd``) never imports this module.
+
+The oracle computes, per session and in IEEE binary64, the acceptance step of
+the SDCP Internet-Draft ("Speculative Decoding Coordination Protocol (SDCP) for
+Distributed Inference with Multi-Level Caches"), Sec. 4.1 (sampling profile)
+and Sec. 6.4 (Rule 1 greedy, Rule 2 speculative sampling), with uniforms from
+Philox4x64-10 (Salmon et al., SC'11).  See the header of ``sv_oracle.c`` for
+every reading taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sv_oracle.c")
+_LIB = os.path.join(_HERE, "libsv_oracle.so")
+
+BF16 = 0
+FP32 = 1
+RULE_GREEDY = 1
+RULE_SPECULATIVE = 2
+S_BAD_PROPOSAL = -1
+S_LIMIT = -2
+S_Q_UNAVAILABLE = -3
+S_BAD_PROFILE = -4
+S_BAD_LOGITS = -5
+
+SAMPLING_DTYPE = np.dtype(
+    [
+        ("temperature_milli", "<u4"),
+        ("top_k", "<u4"),
+        ("top_p_milli", "<u4"),
+        ("reserved", "<u4"),
+        ("session_key", "<u8"),
+    ],
+    align=True,
+)
+assert SAMPLING_DTYPE.itemsize == 24
+
+
+class _Sampling(ctypes.Structure):
+    _fields_ = [
+        ("temperature_milli", ctypes.c_uint32),
+        ("top_k", ctypes.c_uint32),
+        ("top_p_milli", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("session_key", ctypes.c_uint64),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libsv_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-shared", "-fPIC",
+             "-o", tmp, _SRC, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.ov_philox4x64_10.argtypes = [u64p, u64p, u64p]
+        L.ov_philox4x64_10.restype = None
+        L.ov_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint32,
+                                 ctypes.c_uint32, ctypes.c_int]
+        L.ov_uniform.restype = ctypes.c_double
+        L.ov_profile_row.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                     ctypes.POINTER(_Sampling), dp, dp]
+        L.ov_profile_row.restype = ctypes.c_int
+        L.ov_inverse_cdf.argtypes = [dp, ctypes.c_int, ctypes.c_double, dp]
+        L.ov_inverse_cdf.restype = ctypes.c_int
+        L.ov_residual_pick.argtypes = [dp, dp, ctypes.c_int, ctypes.c_double, dp]
+        L.ov_residual_pick.restype = ctypes.c_int
+        L.ov_verify.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i32p, i32p, i32p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp, dp,
+        ]
+        L.ov_verify.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ---------------------------------------------------------------- generator
+def philox4x64_10(counter, key):
+    """One Philox4x64-10 block: 4 x uint64 counter, 2 x uint64 key -> 4 x uint64."""
+    c = np.asarray(counter, dtype=np.uint64).copy()
+    k = np.asarray(key, dtype=np.uint64).copy()
+    o = np.zeros(4, dtype=np.uint64)
+    lib().ov_philox4x64_10(_ptr(c, ctypes.c_uint64), _ptr(k, ctypes.c_uint64),
+                           _ptr(o, ctypes.c_uint64))
+    return o
+
+
+def uniform(seed: int, session_key: int, round_: int, i: int, purpose: int) -> float:
+    """The verifier's uniform for (seed, session, round, position i, purpose)."""
+    return lib().ov_uniform(seed, session_key, round_, i, purpose)
+
+
+# ------------------------------------------------------------------ profile
+def _as_row(row):
+    row = np.ascontiguousarray(row)
+    if row.dtype == np.uint16:
+        return row, BF16
+    if row.dtype == np.float32:
+        return row, FP32
+    raise TypeError("rows are bf16 bits (uint16) or float32")
+
+
+def profile(row, temperature_milli=1000, top_k=0, top_p_milli=1000):
+    """Return (status, prob[V] float64, delta_topp) for one logits row."""
+    row, dt = _as_row(row)
+    V = row.shape[-1]
+    s = _Sampling(temperature_milli, top_k, top_p_milli, 0, 0)
+    prob = np.zeros(V, dtype=np.float64)
+    d = np.zeros(1, dtype=np.float64)
+    st = lib().ov_profile_row(row.ctypes.data, dt, V, ctypes.byref(s),
+                              _ptr(prob, ctypes.c_double), _ptr(d, ctypes.c_double))
+    return st, prob, float(d[0])
+
+
+def inverse_cdf(w, u):
+    """Return (token, delta) for the inverse CDF of weights w (ascending ids)."""
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    d = np.zeros(1, dtype=np.float64)
+    y = lib().ov_inverse_cdf(_ptr(w, ctypes.c_double), w.shape[0], u, _ptr(d, ctypes.c_double))
+    return y, float(d[0])
+
+
+def residual_pick(p, q, u):
+    """Return (token, delta): the draw from norm(max(0, p - q)) (p if that has no mass)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    d = np.zeros(1, dtype=np.float64)
+    y = lib().ov_residual_pick(_ptr(p, ctypes.c_double), _ptr(q, ctypes.c_double), p.shape[0],
+                               u, _ptr(d, ctypes.c_double))
+    return y, float(d[0])
+
+
+# ------------------------------------------------------------- batched step
+def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_key=None):
+    s = np.zeros(B, dtype=SAMPLING_DTYPE)
+    s["temperature_milli"] = temperature_milli
+    s["top_k"] = top_k
+    s["top_p_milli"] = top_p_milli
+    s["session_key"] = np.arange(B, dtype=np.uint64) if session_key is None else session_key
+    return s
+
+
+def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=True):
+    """Run the oracle over a batch.
+
+    target: [B, M+1, V] uint16 (bf16 bits) or float32; draft: [B, M, V] of the
+    same dtype, or None.  tokens [B, M] int32, m [B] int32, rule [B] int32,
+    sampling [B] of ``SAMPLING_DTYPE``.  Returns a dict with accepted_len,
+    out_tokens, p_tok, q_tok and (if diagnostics) d_acc, d_topp_t, d_topp_d,
+    d_cdf.
+    """
+    target = np.ascontiguousarray(target)
+    _, dt = _as_row(target[..., :1].reshape(-1)[:1]) if target.size else (None, BF16)
+    B, M1, V = target.shape
+    M = M1 - 1
+    if draft is not None:
+        draft = np.ascontiguousarray(draft)
+        assert draft.dtype == target.dtype and draft.shape == (B, M, V)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, M)
+    m = np.ascontiguousarray(m, dtype=np.int32).reshape(B)
+    rule = np.ascontiguousarray(rule, dtype=np.int32).reshape(B)
+    sampling = np.ascontiguousarray(sampling, dtype=SAMPLING_DTYPE).reshape(B)
+    out = {
+        "accepted_len": np.zeros(B, dtype=np.int32),
+        "out_tokens": np.zeros((B, M + 1), dtype=np.int32),
+        "p_tok": np.zeros((B, M), dtype=np.float64),
+        "q_tok": np.zeros((B, M), dtype=np.float64),
+    }
+    if diagnostics:
+        out["d_acc"] = np.zeros((B, M), dtype=np.float64)
+        out["d_topp_t"] = np.zeros((B, M + 1), dtype=np.float64)
+        out["d_topp_d"] = np.zeros((B, M), dtype=np.float64)
+        out["d_cdf"] = np.zeros(B, dtype=np.float64)
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def opt(name):
+        return _ptr(out[name], ctypes.c_double) if name in out else ctypes.cast(None, dp)
+
+    rc = lib().ov_verify(
+        target.ctypes.data, None if draft is None else draft.ctypes.data, dt,
+        _ptr(tokens, ctypes.c_int32), _ptr(m, ctypes.c_int32), _ptr(rule, ctypes.c_int32),
+        sampling.ctypes.data, B, M, V, seed, round_,
+        _ptr(out["accepted_len"], ctypes.c_int32), _ptr(out["out_tokens"], ctypes.c_int32),
+        opt("p_tok"), opt("q_tok"), opt("d_acc"), opt("d_topp_t"), opt("d_topp_d"), opt("d_cdf"),
+    )
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call (code {rc})")
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest even) and return the bit pattern."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    nan = np.isnan(x)
+    bits = (rounded >> np.uint32(16)).astype(np.uint16)
+    bits[nan] = np.uint16(0x7FC0)
+    return bits
+
+
+def bf16_to_float(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)

@@ -1,0 +1,470 @@
+/*
+ * sv_oracle.c -- plain, slow, single-threaded CPU oracle for the verifier's
+ * batched speculative-decoding acceptance step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file.  Only the test suite, the smoke check of the package entry
+ * module and the CPU-baseline leg of the benchmark use it.  It shares no code,
+ * header, table or constant with the GPU library; the two are compared, never
+ * combined.
+ *
+ * Sources (cited by page title and section):
+ *  [SDCP]  "Speculative Decoding Coordination Protocol (SDCP) for Distributed
+ *          Inference with Multi-Level Caches" (IETF Internet-Draft
+ *          draft-li-mlc-inference-acceleration-00):
+ *          Sec. 2 (rounds are numbered from 1), Sec. 4.1 (sampling profile:
+ *          temperature, then top-k, then top-p; temperature 0 = argmax with
+ *          ties to the smallest id), Sec. 5.2 (verdict: 0 <= accepted <= M),
+ *          Sec. 6.3 steps 5-7 (q rows checked before any random draw),
+ *          Sec. 6.4 (Rule 1 greedy, Rule 2 speculative sampling, 53-bit
+ *          uniforms with purpose 0 = acceptance test, 1 = additional token),
+ *          Table 2 (problem types), Appendix A (worked greedy round).
+ *  [TXT]   "Inference: KV Cache, Batching, Speculative Decoding", section
+ *          "Speculative decoding" / "The acceptance rule" (rejection sampling,
+ *          residual distribution proportional to max(0, p - q), bonus token
+ *          when every proposal is accepted).
+ *  [PHX]   Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+ *          1, 2, 3", SC'11 -- the Philox4x64 counter-based generator.
+ *
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *  - the verifier's uniforms come from Philox4x64-10 keyed by (seed,
+ *    session_key) at counter (round, i, 0, 0); word 0 gives the acceptance
+ *    uniform and word 1 the additional-token uniform, each as its top 53 bits
+ *    times 2^-53 (the SDCP text derives them from HMAC-SHA-256 instead);
+ *  - q_i is the same sampling profile applied to the draft logits row i;
+ *  - top-k keeps exactly k tokens in the order (logit desc, id asc);
+ *  - top-p keeps the shortest non-empty prefix of that order whose mass C
+ *    satisfies 1000*C >= top_p_milli * Z_k (Z_k = mass after top-k);
+ *    top_p_milli = 1000 and top_k = 0 (or >= number of finite logits) are "off";
+ *  - a -inf logit has probability 0; a NaN or +inf logit, or a row with no
+ *    finite logit, makes the session fail with status BAD_LOGITS;
+ *  - the inverse CDF walks token ids in ascending order and returns the first
+ *    y whose running sum exceeds u*S;
+ *  - an all-zero residual (reachable only through rounding) falls back to p_i.
+ *
+ * All floating-point arithmetic is IEEE binary64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OV_BF16 = 0, OV_FP32 = 1 };
+enum { OV_RULE_GREEDY = 1, OV_RULE_SPECULATIVE = 2 };
+enum {
+  OV_OK = 0,
+  OV_ERR_ARG = -1,
+  OV_ERR_NOMEM = -2,
+  /* per-session statuses, SDCP Table 2 */
+  OV_S_BAD_PROPOSAL = -1,
+  OV_S_LIMIT = -2,
+  OV_S_Q_UNAVAILABLE = -3,
+  OV_S_BAD_PROFILE = -4,
+  OV_S_BAD_LOGITS = -5
+};
+
+/* SDCP Sec. 4.1 "sampling" map; the session identity enters the generator key. */
+typedef struct {
+  uint32_t temperature_milli;
+  uint32_t top_k;
+  uint32_t top_p_milli;
+  uint32_t reserved;
+  uint64_t session_key;
+} ov_sampling;
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x64-10 [PHX]: ten rounds of two 64x64->128 multiplies, with the    */
+/* key bumped by two Weyl constants between rounds.                          */
+/* ------------------------------------------------------------------------ */
+static const uint64_t PHX_MUL0 = 0xD2E7470EE14C6C93ULL;
+static const uint64_t PHX_MUL1 = 0xCA5A826395121157ULL;
+static const uint64_t PHX_WEYL0 = 0x9E3779B97F4A7C15ULL; /* golden ratio */
+static const uint64_t PHX_WEYL1 = 0xBB67AE8584CAA73BULL; /* sqrt(3) - 1  */
+
+void ov_philox4x64_10(const uint64_t counter[4], const uint64_t key[2], uint64_t out[4]) {
+  uint64_t x0 = counter[0], x1 = counter[1], x2 = counter[2], x3 = counter[3];
+  uint64_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    unsigned __int128 p0 = (unsigned __int128)PHX_MUL0 * x0;
+    unsigned __int128 p1 = (unsigned __int128)PHX_MUL1 * x2;
+    uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    uint64_t y0 = hi1 ^ x1 ^ k0;
+    uint64_t y1 = lo1;
+    uint64_t y2 = hi0 ^ x3 ^ k1;
+    uint64_t y3 = lo0;
+    x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    k0 += PHX_WEYL0;
+    k1 += PHX_WEYL1;
+  }
+  out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* SDCP Sec. 6.4: a uniform in [0,1) is the first 53 bits of a random word
+ * divided by 2^53.  purpose 0 = acceptance test, 1 = additional token. */
+double ov_uniform(uint64_t seed, uint64_t session_key, uint32_t round, uint32_t i, int purpose) {
+  uint64_t ctr[4] = {round, i, 0, 0};
+  uint64_t key[2] = {seed, session_key};
+  uint64_t o[4];
+  ov_philox4x64_10(ctr, key, o);
+  uint64_t word = purpose == 0 ? o[0] : o[1];
+  return ldexp((double)(word >> 11), -53);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rows                                                                      */
+/* ------------------------------------------------------------------------ */
+static double widen_bf16(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static void load_row(const void *base, int dtype, int64_t row, int V, double *out) {
+  if (dtype == OV_BF16) {
+    const uint16_t *p = (const uint16_t *)base + row * (int64_t)V;
+    for (int y = 0; y < V; ++y) out[y] = widen_bf16(p[y]);
+  } else {
+    const float *p = (const float *)base + row * (int64_t)V;
+    for (int y = 0; y < V; ++y) out[y] = (double)p[y];
+  }
+}
+
+/* 1 if the row holds a NaN or +inf, or no finite logit (the BAD_LOGITS reading). */
+static int row_is_bad(const double *l, int V) {
+  int finite = 0;
+  for (int y = 0; y < V; ++y) {
+    if (isnan(l[y]) || (isinf(l[y]) && l[y] > 0)) return 1;
+    if (!isinf(l[y])) finite = 1;
+  }
+  return !finite;
+}
+
+/* Smallest token id attaining the largest logit (SDCP Sec. 4.1 / Sec. 6.4 Rule 1). */
+static int row_argmax(const double *l, int V) {
+  int g = 0;
+  for (int y = 1; y < V; ++y)
+    if (l[y] > l[g]) g = y;
+  return g;
+}
+
+typedef struct {
+  double logit;
+  int id;
+} ov_entry;
+
+/* total order of the profile: logit descending, token id ascending */
+static int entry_cmp(const void *a, const void *b) {
+  const ov_entry *x = (const ov_entry *)a, *y = (const ov_entry *)b;
+  if (x->logit > y->logit) return -1;
+  if (x->logit < y->logit) return 1;
+  return (x->id > y->id) - (x->id < y->id);
+}
+
+/*
+ * SDCP Sec. 4.1: the distribution after temperature, top-k and top-p, in that
+ * order.  Writes prob[0..V-1]; returns OV_OK or OV_S_BAD_LOGITS.
+ * *delta_topp receives |1000*C - P*Z_k| / (1000*Z_k), the smallest over the
+ * cutoff step and the step before it (INFINITY when top-p is off or T = 0).
+ * ent: caller scratch of V entries.
+ */
+static int profile_row(const double *l, int V, const ov_sampling *s, double *prob,
+                       double *delta_topp, ov_entry *ent) {
+  *delta_topp = INFINITY;
+  if (row_is_bad(l, V)) return OV_S_BAD_LOGITS;
+  for (int y = 0; y < V; ++y) prob[y] = 0.0;
+
+  if (s->temperature_milli == 0) { /* one-hot argmax */
+    prob[row_argmax(l, V)] = 1.0;
+    return OV_OK;
+  }
+  const double T = (double)s->temperature_milli / 1000.0;
+
+  int n = 0; /* finite tokens only: a -inf logit has probability zero */
+  for (int y = 0; y < V; ++y)
+    if (!isinf(l[y])) { ent[n].logit = l[y]; ent[n].id = y; ++n; }
+  qsort(ent, (size_t)n, sizeof *ent, entry_cmp);
+
+  int kept = n; /* top-k: the first k tokens of the order */
+  if (s->top_k > 0 && (int64_t)s->top_k < (int64_t)n) kept = (int)s->top_k;
+
+  const double lmax = ent[0].logit;
+  double Zk = 0.0;
+  for (int j = 0; j < kept; ++j) Zk += exp((ent[j].logit - lmax) / T);
+
+  int cut = kept; /* top-p: shortest prefix with 1000*C >= P*Z_k */
+  double Zp = Zk;
+  if (s->top_p_milli < 1000) {
+    const double P = (double)s->top_p_milli;
+    double C = 0.0, Cprev = 0.0;
+    cut = 0;
+    for (int j = 0; j < kept; ++j) {
+      Cprev = C;
+      C += exp((ent[j].logit - lmax) / T);
+      if (1000.0 * C >= P * Zk) { cut = j + 1; break; }
+    }
+    if (cut == 0) { cut = kept; C = Zk; } /* unreachable: C reaches Z_k at the end */
+    double d = fabs(1000.0 * C - P * Zk);
+    if (cut > 1) {
+      double d2 = fabs(1000.0 * Cprev - P * Zk);
+      if (d2 < d) d = d2;
+    }
+    *delta_topp = d / (1000.0 * Zk);
+    Zp = C;
+  }
+  for (int j = 0; j < cut; ++j) prob[ent[j].id] = exp((ent[j].logit - lmax) / T) / Zp;
+  return OV_OK;
+}
+
+/*
+ * Inverse CDF in ascending token-id order: the smallest y with
+ * sum_{t<=y} w(t) > u * S, S = sum of all w.  If rounding leaves no such y,
+ * the largest y with w(y) > 0.  *delta = distance of u*S to the nearest CDF
+ * boundary around the pick, divided by S.
+ */
+static int inverse_cdf(const double *w, int V, double u, double *delta) {
+  double S = 0.0;
+  for (int y = 0; y < V; ++y) S += w[y];
+  const double target = u * S;
+  double C = 0.0;
+  for (int y = 0; y < V; ++y) {
+    double Cprev = C;
+    C += w[y];
+    if (C > target) {
+      double d1 = target - Cprev, d2 = C - target;
+      *delta = (d1 < d2 ? d1 : d2) / S;
+      return y;
+    }
+  }
+  *delta = 0.0;
+  for (int y = V - 1; y >= 0; --y)
+    if (w[y] > 0.0) return y;
+  return -1;
+}
+
+/*
+ * SDCP Sec. 6.4 Rule 2 / textbook "The acceptance rule": at the first
+ * rejection the additional token is drawn from norm(max(0, p - q)) with the
+ * purpose-1 uniform.  If rounding leaves that residual with no mass, draw
+ * from p instead.  w: caller scratch of V doubles.
+ */
+static int residual_pick(const double *p, const double *q, int V, double u, double *w,
+                         double *delta) {
+  double S = 0.0;
+  for (int y = 0; y < V; ++y) {
+    double r = p[y] - q[y];
+    w[y] = r > 0.0 ? r : 0.0;
+    S += w[y];
+  }
+  if (S == 0.0) memcpy(w, p, sizeof(double) * (size_t)V);
+  return inverse_cdf(w, V, u, delta);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exported single-row helpers (for the oracle's own pins)                   */
+/* ------------------------------------------------------------------------ */
+int ov_profile_row(const void *row, int dtype, int V, const ov_sampling *s, double *prob,
+                   double *delta_topp) {
+  if (!row || !s || !prob || !delta_topp || V < 1 || (dtype != OV_BF16 && dtype != OV_FP32))
+    return OV_ERR_ARG;
+  double *l = (double *)malloc(sizeof(double) * (size_t)V);
+  ov_entry *ent = (ov_entry *)malloc(sizeof(ov_entry) * (size_t)V);
+  if (!l || !ent) { free(l); free(ent); return OV_ERR_NOMEM; }
+  load_row(row, dtype, 0, V, l);
+  int st = profile_row(l, V, s, prob, delta_topp, ent);
+  free(l);
+  free(ent);
+  return st;
+}
+
+int ov_inverse_cdf(const double *w, int V, double u, double *delta) {
+  if (!w || V < 1 || !delta) return OV_ERR_ARG;
+  return inverse_cdf(w, V, u, delta);
+}
+
+int ov_residual_pick(const double *p, const double *q, int V, double u, double *delta) {
+  if (!p || !q || V < 1 || !delta) return OV_ERR_ARG;
+  double *w = (double *)malloc(sizeof(double) * (size_t)V);
+  if (!w) return OV_ERR_NOMEM;
+  int y = residual_pick(p, q, V, u, w, delta);
+  free(w);
+  return y;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The batched step                                                          */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  double *l, *p, *q, *w;
+  ov_entry *ent;
+} ov_scratch;
+
+static void set_if(double *arr, int64_t idx, double v) {
+  if (arr) arr[idx] = v;
+}
+
+/*
+ * One session.  Returns a = accepted count (>= 0) or a negative status; on
+ * success writes out[0..a] (a accepted tokens, then the additional token).
+ */
+static int verify_session(int64_t b, const void *target, const void *draft, int dtype,
+                          const int32_t *x, int m, int rule, const ov_sampling *s, int M, int V,
+                          uint64_t seed, uint32_t round, int32_t *out, double *p_tok,
+                          double *q_tok, double *d_acc, double *d_topp_t, double *d_topp_d,
+                          double *d_cdf, ov_scratch *sc) {
+  /* SDCP Sec. 6.2 / Table 2 "sdcp-limit": 1 <= M <= m_max (<= 64) */
+  if (m < 1 || m > M) return OV_S_LIMIT;
+  if ((rule != OV_RULE_GREEDY && rule != OV_RULE_SPECULATIVE) || s->reserved != 0 ||
+      s->top_p_milli > 1000)
+    return OV_S_BAD_PROFILE;
+  /* SDCP Sec. 6.3 step 5: no q rows for a rule that needs them */
+  if (rule == OV_RULE_SPECULATIVE && draft == NULL) return OV_S_Q_UNAVAILABLE;
+  for (int i = 0; i < m; ++i)
+    if (x[i] < 0 || x[i] >= V) return OV_S_BAD_PROPOSAL;
+
+  const int64_t trow0 = b * (int64_t)(M + 1); /* target row i (1-based) = trow0 + i - 1 */
+  const int64_t drow0 = b * (int64_t)M;       /* draft row i (1-based)  = drow0 + i - 1 */
+
+  /* every row the rule reads must be usable before any decision */
+  for (int i = 1; i <= m + 1; ++i) {
+    load_row(target, dtype, trow0 + i - 1, V, sc->l);
+    if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
+  }
+  if (rule == OV_RULE_SPECULATIVE)
+    for (int i = 1; i <= m; ++i) {
+      load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+      if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
+    }
+
+  if (rule == OV_RULE_GREEDY) {
+    /* SDCP Sec. 6.4 Rule 1: accept x_i while it equals argmax p_i (the argmax
+     * of p_i is the argmax of the raw logits; ties to the smallest id); the
+     * additional token is argmax p_{a+1}. */
+    int a = 0;
+    while (a < m) {
+      load_row(target, dtype, trow0 + a, V, sc->l);
+      if (x[a] != row_argmax(sc->l, V)) break;
+      out[a] = x[a];
+      ++a;
+    }
+    load_row(target, dtype, trow0 + a, V, sc->l);
+    out[a] = row_argmax(sc->l, V);
+    return a;
+  }
+
+  /* SDCP Sec. 6.3 step 5 and Sec. 6.4 Rule 2: q_i(x_i) != 0 for every i,
+   * checked before any random value is drawn. */
+  double qx[64];
+  for (int i = 1; i <= m; ++i) {
+    double dt;
+    load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+    profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+    set_if(d_topp_d, b * (int64_t)M + i - 1, dt);
+    qx[i - 1] = sc->q[x[i - 1]];
+    set_if(q_tok, b * (int64_t)M + i - 1, qx[i - 1]);
+  }
+  for (int i = 0; i < m; ++i)
+    if (qx[i] == 0.0) return OV_S_BAD_PROPOSAL;
+
+  /* Rule 2, positions in order: accept x_i if u < min(1, p_i(x_i)/q_i(x_i)). */
+  int a = m, decided = 0;
+  for (int i = 1; i <= m; ++i) {
+    if (decided && !p_tok) break; /* the rest only feeds the probe */
+    double dt;
+    load_row(target, dtype, trow0 + i - 1, V, sc->l);
+    profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+    set_if(d_topp_t, b * (int64_t)(M + 1) + i - 1, dt);
+    const double px = sc->p[x[i - 1]];
+    set_if(p_tok, b * (int64_t)M + i - 1, px);
+    if (decided) continue;
+
+    const double ratio = px / qx[i - 1];
+    const double acc = ratio < 1.0 ? ratio : 1.0;
+    const double u = ov_uniform(seed, s->session_key, round, (uint32_t)i, 0);
+    set_if(d_acc, b * (int64_t)M + i - 1, fabs(u - acc));
+    if (u < acc) {
+      out[i - 1] = x[i - 1];
+      continue;
+    }
+    /* first rejection: additional token from norm(max(0, p_i - q_i)) */
+    load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+    profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+    double dc;
+    out[i - 1] = residual_pick(sc->p, sc->q, V,
+                               ov_uniform(seed, s->session_key, round, (uint32_t)i, 1), sc->w, &dc);
+    set_if(d_cdf, b, dc);
+    a = i - 1;
+    decided = 1;
+  }
+  if (!decided) {
+    /* every proposal accepted: bonus token from p_{m+1} */
+    double dt, dc;
+    load_row(target, dtype, trow0 + m, V, sc->l);
+    profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+    set_if(d_topp_t, b * (int64_t)(M + 1) + m, dt);
+    out[m] = inverse_cdf(sc->p, V, ov_uniform(seed, s->session_key, round, (uint32_t)(m + 1), 1), &dc);
+    set_if(d_cdf, b, dc);
+  }
+  return a;
+}
+
+/*
+ * The batched step over B sessions (same layout as the GPU entry point):
+ *   target   [B, M+1, V]  dtype (bf16 bits as uint16, or float32)
+ *   draft    [B, M,   V]  dtype, or NULL
+ *   tokens   [B, M]; m [B]; rule [B]; sampling [B]
+ * Outputs: accepted_len[B] (a, or a negative status), out_tokens[B, M+1]
+ * (a+1 tokens, then -1).  Optional (NULL to skip), all [B, M] unless noted,
+ * -1 / +inf where not computed: p_tok, q_tok (rule 2 only), d_acc,
+ * d_topp_t [B, M+1], d_topp_d, d_cdf [B].
+ * Returns OV_OK or OV_ERR_*.
+ */
+int ov_verify(const void *target, const void *draft, int dtype, const int32_t *tokens,
+              const int32_t *m, const int32_t *rule, const ov_sampling *sampling, int64_t B,
+              int M, int V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+              int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
+              double *d_topp_t, double *d_topp_d, double *d_cdf) {
+  if (!target || !tokens || !m || !rule || !sampling || !accepted_len || !out_tokens)
+    return OV_ERR_ARG;
+  if (B < 1 || M < 1 || M > 64 || V < 1 || (dtype != OV_BF16 && dtype != OV_FP32))
+    return OV_ERR_ARG;
+
+  ov_scratch sc;
+  sc.l = (double *)malloc(sizeof(double) * (size_t)V);
+  sc.p = (double *)malloc(sizeof(double) * (size_t)V);
+  sc.q = (double *)malloc(sizeof(double) * (size_t)V);
+  sc.w = (double *)malloc(sizeof(double) * (size_t)V);
+  sc.ent = (ov_entry *)malloc(sizeof(ov_entry) * (size_t)V);
+  if (!sc.l || !sc.p || !sc.q || !sc.w || !sc.ent) {
+    free(sc.l); free(sc.p); free(sc.q); free(sc.w); free(sc.ent);
+    return OV_ERR_NOMEM;
+  }
+
+  for (int64_t b = 0; b < B; ++b) {
+    int32_t *out = out_tokens + b * (int64_t)(M + 1);
+    for (int j = 0; j <= M; ++j) out[j] = -1;
+    for (int j = 0; j < M; ++j) {
+      set_if(p_tok, b * (int64_t)M + j, -1.0);
+      set_if(q_tok, b * (int64_t)M + j, -1.0);
+      set_if(d_acc, b * (int64_t)M + j, INFINITY);
+      set_if(d_topp_d, b * (int64_t)M + j, INFINITY);
+    }
+    for (int j = 0; j <= M; ++j) set_if(d_topp_t, b * (int64_t)(M + 1) + j, INFINITY);
+    set_if(d_cdf, b, INFINITY);
+
+    int a = verify_session(b, target, draft, dtype, tokens + b * (int64_t)M, m[b], rule[b],
+                           &sampling[b], M, V, seed, round, out, p_tok, q_tok, d_acc, d_topp_t,
+                           d_topp_d, d_cdf, &sc);
+    accepted_len[b] = a;
+    if (a < 0) { /* a failed session emits nothing; its diagnostics are kept */
+      for (int j = 0; j <= M; ++j) out[j] = -1;
+      for (int j = 0; j < M; ++j) {
+        set_if(p_tok, b * (int64_t)M + j, -1.0);
+        set_if(q_tok, b * (int64_t)M + j, -1.0);
+      }
+    }
+  }
+  free(sc.l); free(sc.p); free(sc.q); free(sc.w); free(sc.ent);
+  return OV_OK;
+}
