@@ -1,0 +1,158 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the MI355X (gfx950) verifier
+ * acceptance step for speculative decoding.
+ *
+ * The operation follows the SDCP Internet-Draft "Speculative Decoding
+ * Coordination Protocol (SDCP) for Distributed Inference with Multi-Level
+ * Caches" (draft-li-mlc-inference-acceleration-00):
+ *   Sec. 4.1  sampling profile: temperature, then top-k, then top-p; a
+ *             temperature of zero is the argmax with ties to the smallest id;
+ *   Sec. 6.3  step 5: for a rule that needs draft probabilities, q_i(x_i) must
+ *             be non-zero at every proposed position before any random draw;
+ *             step 7: the acceptance rule yields a accepted tokens plus one;
+ *   Sec. 6.4  Rule 1 (greedy) and Rule 2 (speculative sampling), positions
+ *             evaluated in order; verifier uniforms are 53-bit values keyed by
+ *             seed, session, round, position and purpose (0 = acceptance
+ *             test, 1 = additional token);
+ *   Sec. 5.2  verdict: accepted a with 0 <= a <= M, emitted tokens;
+ *   Table 2   problem types (sdcp-bad-proposal, sdcp-limit, sdcp-q-unavailable);
+ *   Sec. 10.2.2  rule registry: 1 = greedy, 2 = speculative sampling.
+ * and the textbook chapter "Inference: KV Cache, Batching, Speculative
+ * Decoding", section "The acceptance rule" (residual max(0, p - q), bonus
+ * token from p at position M+1).
+ *
+ * Readings where the pages are silent (the library implements exactly these):
+ *  - draft distribution q_i = the same profile applied to draft logits row i;
+ *  - uniforms: Philox4x64-10 (Salmon et al., SC'11) with key (seed,
+ *    session_key) and counter (round, i, 0, 0), i = 1-based position; word 0
+ *    >> 11 times 2^-53 is the acceptance uniform, word 1 the additional-token
+ *    uniform (the draft derives them from HMAC-SHA-256 instead);
+ *  - top-k keeps exactly k tokens in the order (logit desc, id asc); top_k = 0
+ *    or >= the number of finite logits is "off";
+ *  - top-p keeps the shortest non-empty prefix of that order whose mass C
+ *    (after top-k) satisfies 1000*C >= top_p_milli * Z_k; top_p_milli = 1000
+ *    is "off";
+ *  - -inf logits have probability zero; -0 and +0 are equal logits;
+ *  - the additional token is the inverse CDF over ascending token ids;
+ *  - NaN or +inf logits, or a row with no finite logit, in a row the rule
+ *    reads: the session fails with SV_S_BAD_LOGITS.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_VERSION 1
+#define SV_M_MAX 64          /* SDCP Sec. 4.1: m_max <= 64 */
+#define SV_V_MAX (1 << 24)   /* largest vocabulary accepted */
+
+/* Per-session sampling profile (SDCP Sec. 4.1 "sampling"), 24 bytes,
+ * 8-byte aligned; passed as a DEVICE array [B]. */
+typedef struct sv_sampling {
+  uint32_t temperature_milli; /* T * 1000; 0 => one-hot argmax */
+  uint32_t top_k;             /* 0 (or >= finite count) => off */
+  uint32_t top_p_milli;       /* 0..1000; 1000 => off; > 1000 => SV_S_BAD_PROFILE */
+  uint32_t reserved;          /* must be 0, else SV_S_BAD_PROFILE */
+  uint64_t session_key;       /* the session's identity in the generator key */
+} sv_sampling;
+
+/* Optional per-call probe (host struct; every member may be NULL):
+ *  p_tok, q_tok: DEVICE arrays [B, M] of float64, written for
+ *    speculative-sampling sessions with p_i(x_i) and q_i(x_i) for i <= m[b]
+ *    (every position, also past the first rejection); -1 elsewhere and for
+ *    greedy or failed sessions.
+ *  rows_start, rows_stop: hipEvent_t handles recorded on the launch stream
+ *    immediately before and after the row-profile kernels (the step's
+ *    dominant, HBM-streaming part), for timing it. */
+typedef struct sv_probe {
+  double *p_tok;
+  double *q_tok;
+  void *rows_start;
+  void *rows_stop;
+} sv_probe;
+
+enum { SV_RULE_GREEDY = 1, SV_RULE_SPECULATIVE = 2 }; /* SDCP Sec. 10.2.2 */
+enum { SV_BF16 = 0, SV_FP32 = 1 };                   /* logits element type */
+
+/* Call-level return codes of sv_verify. */
+enum {
+  SV_OK = 0,
+  SV_ERR_ARG = -1,       /* null pointer, bad size or dtype, size overflow */
+  SV_ERR_DEVICE = -2,    /* a kernel launch failed */
+  SV_ERR_WORKSPACE = -3  /* workspace smaller than sv_workspace_bytes() */
+};
+
+/* Per-session statuses written to accepted_len[b] (< 0) when a session fails;
+ * that session's out_tokens row is then all -1.  Other sessions are unaffected.
+ * Checked in this order. */
+enum {
+  SV_S_LIMIT = -2,         /* m[b] outside [1, M]          (sdcp-limit) */
+  SV_S_BAD_PROFILE = -4,   /* rule not 1/2, top_p_milli > 1000, reserved != 0 */
+  SV_S_Q_UNAVAILABLE = -3, /* rule 2 and draft_logits == NULL (sdcp-q-unavailable) */
+  SV_S_BAD_PROPOSAL = -1,  /* a token outside [0, V); or, after the logits check,
+                              q_i(x_i) == 0 for some i <= m[b] (sdcp-bad-proposal) */
+  SV_S_BAD_LOGITS = -5     /* NaN / +inf, or no finite logit, in a row the rule reads */
+};
+
+/* Bytes of device workspace sv_verify needs for (B, M, V).  0 if the sizes
+ * are out of range. */
+size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V);
+
+/*
+ * The batched acceptance step.  All array pointers are caller-owned DEVICE
+ * memory, row-major and contiguous:
+ *   target_logits [B, M+1, V] of dtype: target row i (1-based) of session b is
+ *                 target_logits[b, i-1, :]; row M+1 scores the bonus position.
+ *   draft_logits  [B, M, V] of dtype: draft row i is draft_logits[b, i-1, :];
+ *                 may be NULL when no session uses rule 2 (a rule-2 session
+ *                 then fails with SV_S_Q_UNAVAILABLE).  Greedy sessions never
+ *                 read it.
+ *   draft_tokens  [B, M] int32: x_i = draft_tokens[b, i-1]; entries i > m[b]
+ *                 are ignored.
+ *   m [B], rule [B] int32; sampling [B] sv_sampling.
+ *   B >= 1, 1 <= M <= 64, 1 <= V <= SV_V_MAX; a session uses rows
+ *   1..m[b]+1 of the target and, for rule 2, rows 1..m[b] of the draft.
+ *   seed, round: the generator key and counter for this call (SDCP rounds are
+ *   numbered from 1; any value is accepted).
+ * Outputs:
+ *   accepted_len [B] int32: a in [0, m[b]] or a negative SV_S_* status;
+ *   out_tokens [B, M+1] int32: x_1..x_a, then the additional token, then -1.
+ *   probe: host struct pointer or NULL.
+ * workspace: DEVICE memory of at least sv_workspace_bytes(B, M, V) bytes, not
+ *   aliased with any other argument; its contents need not be initialised.
+ * stream: hipStream_t to launch on; NULL = the default stream.
+ *
+ * The call only enqueues work: it is asynchronous with respect to the host,
+ * allocates nothing, and keeps no pointer after returning.  Outputs are valid
+ * once the stream has completed.  Concurrent calls need distinct workspaces
+ * and outputs.  A session's result depends only on its own rows, tokens, m,
+ * rule, sampling record, seed and round (not on B, its batch position, the
+ * stream or repetition).
+ * Returns SV_OK or an SV_ERR_* code; on an error nothing has been enqueued
+ * (except for SV_ERR_DEVICE, where some kernels may have been launched).
+ */
+int sv_verify(const void *target_logits, const void *draft_logits, int32_t dtype,
+              const int32_t *draft_tokens, const int32_t *m, const int32_t *rule,
+              const sv_sampling *sampling, int32_t B, int32_t M, int32_t V, uint64_t seed,
+              uint32_t round, int32_t *accepted_len, int32_t *out_tokens, void *workspace,
+              size_t workspace_bytes, const sv_probe *probe, void *stream);
+
+/* Text for an sv_verify return code; never NULL. */
+const char *sv_strerror(int code);
+
+/* Text for a per-session status (accepted_len < 0); never NULL. */
+const char *sv_status_str(int status);
+
+/* SV_VERSION of the built library. */
+int sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle, element by
+element, on seeded synthetic inputs.
+
+Small cases span many profiles, ragged m, both dtypes, ties, -inf masks and
+every per-session status; the workload shapes are checked in full (tiny, b64)
+or on sampled sessions (b256_topk_topp, ragged, large) in the same launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import parity
+from token_sampling_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+PROFILES = [
+    (1000, 0, 1000), (700, 50, 900), (800, 0, 950), (0, 0, 1000), (1300, 7, 1000),
+    (500, 0, 0), (1000, 1, 1000), (900, 2000, 1000), (600, 30, 500), (2000, 0, 990),
+    (1, 0, 1000), (1000, 100000, 999), (700, 3, 300), (1000, 0, 1),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_sampling_amd as sv
+    sv.lib()
+    yield
+
+
+def mixed_case(seed, B, M, V, dtype="bf16", identical_every=5, mask_every=7):
+    rng = np.random.default_rng(seed)
+    t32 = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
+    t32 += (rng.random(t32.shape) < 0.005) * np.float32(8)
+    d32 = (0.7 * t32[:, :M] + rng.normal(0, 1.2, size=(B, M, V))).astype(np.float32)
+    for b in range(0, B, identical_every):
+        d32[b] = t32[b, :M]
+    for b in range(3, B, mask_every):  # grammar-style -inf masks
+        mask = rng.random(V) < 0.6
+        mask[rng.integers(0, V)] = False
+        t32[b, :, mask] = -np.inf
+        d32[b, :, mask] = -np.inf
+    if dtype == "bf16":
+        target, draft = oracle.bf16_bits(t32), oracle.bf16_bits(d32)
+    else:
+        target, draft = t32, d32
+    s = oracle.make_sampling(B)
+    for b in range(B):
+        s[b]["temperature_milli"], s[b]["top_k"], s[b]["top_p_milli"] = PROFILES[b % len(PROFILES)]
+    h = dict(target=target, draft=draft, tokens=np.zeros((B, M), np.int32),
+             m=rng.integers(1, M + 1, size=B).astype(np.int32),
+             rule=np.where(rng.random(B) < 0.3, 1, 2).astype(np.int32),
+             sampling=s, seed=int(rng.integers(0, 1 << 62)), round=int(rng.integers(1, 1000)))
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    return h
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("seed,B,M,V", [(11, 28, 6, 2500), (12, 14, 3, 9000), (13, 20, 9, 777)])
+def test_mixed_profiles(dtype, seed, B, M, V):
+    parity.log(f"[case] mixed dtype={dtype} seed={seed} B={B} M={M} V={V}")
+    h = mixed_case(seed, B, M, V, dtype)
+    g = parity.run_gpu(h)
+    o = parity.run_oracle(h)
+    parity.compare(g, o, f"mixed-{dtype}-{seed}")
+
+
+def test_edge_cases():
+    parity.log("[case] edge cases")
+    B, M, V = 16, 4, 300
+    rng = np.random.default_rng(21)
+    t = rng.normal(0, 1, size=(B, M + 1, V)).astype(np.float32)
+    d = (t[:, :M] + rng.normal(0, 0.5, size=(B, M, V))).astype(np.float32)
+    s = oracle.make_sampling(B, 1000, 0, 1000)
+    m = np.full(B, M, np.int32)
+    rule = np.full(B, 2, np.int32)
+    # 0: all logits equal (every token tied), top-k 3
+    t[0] = 0.0; d[0] = 0.0; s[0]["top_k"] = 3
+    # 1: all equal, top-p 0.5
+    t[1] = 1.5; d[1] = 1.5; s[1]["top_p_milli"] = 500
+    # 2: signed zeros and ties at the top
+    t[2] = -1.0; t[2, :, ::2] = -0.0; t[2, :, 1::2] = 0.0; d[2] = t[2, :M]; s[2]["top_k"] = 5
+    # 3: only two finite tokens
+    t[3] = -np.inf; t[3, :, 7] = 1.0; t[3, :, 200] = 1.0; d[3] = t[3, :M]
+    # 4: NaN in a draft row -> bad logits
+    d[4, 2, 17] = np.nan
+    # 5: +inf in the bonus row
+    t[5, M, 3] = np.inf
+    # 6: m = 0 and 7: m = M + 1 -> limit
+    m[6] = 0; m[7] = M + 1
+    # 8: top_p 1001 -> bad profile; 9: reserved != 0; 10: unknown rule
+    s[8]["top_p_milli"] = 1001; s[9]["reserved"] = 7; rule[10] = 5
+    # 11: greedy with a NaN only in the (unread) draft
+    rule[11] = 1; d[11, 0, 0] = np.nan
+    # 12: temperature 0 under rule 2
+    s[12]["temperature_milli"] = 0
+    # 13: top_k 1 and 14: top_p 0 (both one-hot)
+    s[13]["top_k"] = 1; s[14]["top_p_milli"] = 0
+    # 15: huge temperature (near uniform)
+    s[15]["temperature_milli"] = 4_000_000_000
+    h = dict(target=oracle.bf16_bits(t), draft=oracle.bf16_bits(d), tokens=np.zeros((B, M), np.int32),
+             m=m, rule=rule, sampling=s, seed=5, round=3)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    h["tokens"][12] = np.argmax(oracle.bf16_to_float(h["draft"][12]), axis=-1)
+    tok = h["tokens"]
+    tok[9, 1] = V  # (also out of range, but the profile check comes first)
+    bad = dict(h)
+    g = parity.run_gpu(h)
+    o = parity.run_oracle(h)
+    assert o["accepted_len"][4] == oracle.S_BAD_LOGITS
+    assert o["accepted_len"][5] == oracle.S_BAD_LOGITS
+    assert o["accepted_len"][6] == o["accepted_len"][7] == oracle.S_LIMIT
+    assert o["accepted_len"][8] == o["accepted_len"][9] == o["accepted_len"][10] == oracle.S_BAD_PROFILE
+    assert o["accepted_len"][11] >= 0
+    parity.compare(g, o, "edge")
+    # tokens out of range and q(x) = 0
+    bad["tokens"] = h["tokens"].copy()
+    bad["tokens"][0, 2] = -3
+    bad["tokens"][1, 0] = V
+    dd = oracle.bf16_to_float(h["draft"]).copy()
+    dd[2, 1, bad["tokens"][2, 1]] = -np.inf
+    bad["draft"] = oracle.bf16_bits(dd)
+    g = parity.run_gpu(bad)
+    o = parity.run_oracle(bad)
+    assert o["accepted_len"][0] == o["accepted_len"][1] == o["accepted_len"][2] == oracle.S_BAD_PROPOSAL
+    parity.compare(g, o, "edge-bad-proposal")
+
+
+def test_full_speculation_length_and_tiny_vocab():
+    parity.log("[case] M=64 and V=1")
+    h = mixed_case(31, 5, 64, 300)
+    h["m"] = np.array([64, 1, 33, 64, 17], np.int32)
+    h["rule"] = np.array([2, 2, 2, 1, 2], np.int32)
+    h["tokens"] = parity.draw_valid_tokens(h, np.random.default_rng(3))
+    h["draft"] = oracle.bf16_bits(oracle.bf16_to_float(h["draft"]))
+    h["draft"][0] = h["target"][0, :64]  # identical draft: all 64 accepted, then the bonus
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), "m64")
+    one = dict(target=np.zeros((2, 2, 1), np.float32), draft=np.zeros((2, 1, 1), np.float32),
+               tokens=np.zeros((2, 1), np.int32), m=np.array([1, 1], np.int32),
+               rule=np.array([1, 2], np.int32), sampling=oracle.make_sampling(2), seed=0, round=1)
+    g = parity.run_gpu(one)
+    assert g["accepted_len"].tolist() == [1, 1] and g["out_tokens"].tolist() == [[0, 0], [0, 0]]
+    parity.compare(g, parity.run_oracle(one), "V1")
+
+
+def test_no_draft_rows():
+    parity.log("[case] draft = NULL")
+    h = mixed_case(41, 10, 4, 1000)
+    h["draft"] = None
+    h["rule"] = np.array([1, 2] * 5, np.int32)
+    g = parity.run_gpu(h)
+    o = parity.run_oracle(h)
+    assert (o["accepted_len"][1::2] == oracle.S_Q_UNAVAILABLE).all()
+    parity.compare(g, o, "no-draft")
+
+
+def test_deterministic_and_batch_invariant():
+    parity.log("[case] determinism and batch invariance")
+    h = mixed_case(51, 12, 5, 4000)
+    g1 = parity.run_gpu(h)
+    g2 = parity.run_gpu(h)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+    for b in (0, 5, 11):
+        one = {k: (v[b:b + 1] if isinstance(v, np.ndarray) else v) for k, v in h.items()}
+        g = parity.run_gpu(one)
+        for k in g:
+            assert np.array_equal(g[k][0], g1[k][b]), (b, k)
+
+
+@pytest.mark.parametrize("name", ["tiny", "b64"])
+def test_workload_in_full(name):
+    parity.log(f"[case] workload {name} (all sessions)")
+    w = W.make(name, device="cuda")
+    h = W.to_numpy(w)
+    g = parity.run_gpu(h)
+    o = parity.run_oracle(h)
+    parity.compare(g, o, name)
+
+
+@pytest.mark.parametrize("name,sessions", [("b256_topk_topp", (0, 1, 77, 255)),
+                                           ("ragged", (0, 3, 200, 511)),
+                                           ("large", (0, 1023))])
+def test_workload_full_size_sampled_sessions(name, sessions):
+    parity.log(f"[case] workload {name} full size, oracle on sessions {sessions}")
+    w = W.make(name, device="cuda")
+    import token_sampling_amd as sv
+    out = sv.verify(w.target, w.draft, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"),
+                    w.seed, w.round, probe=True)
+    torch.cuda.synchronize()
+    g_all = {k: v.cpu().numpy() for k, v in out.items()}
+    a = g_all["accepted_len"]
+    assert np.all((a >= 0) | (a == oracle.S_BAD_PROPOSAL))
+    idx = np.array(sessions)
+    sub = W.to_numpy(w, sessions=torch.as_tensor(idx, device="cuda"))
+    del w, out
+    torch.cuda.empty_cache()
+    o = parity.run_oracle(sub)
+    g = {k: v[idx] for k, v in g_all.items()}
+    parity.compare(g, o, f"{name}-sampled")
+    parity.log(f"[workload] {name}: mean accepted {a[a >= 0].mean():.3f}, "
+               f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")

@@ -1,1 +1,227 @@
-"""MI355X-native verifier acceptance step (placeholder, binding added with the library)."""
+"""token_sampling_amd -- Python binding of libspecverify, the MI355X (gfx950)
+verifier acceptance step for speculative decoding.
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs and the workspace with torch, and calls the C ABI
+declared in ``include/specverify.h`` on the current torch stream.  Every step
+of the computation runs in the HIP kernels of ``libspecverify.so``; there is
+no CPU or PyTorch fallback, and the calls raise if the library is missing.
+
+The operation is the acceptance step of the SDCP Internet-Draft ("Speculative
+Decoding Coordination Protocol (SDCP) for Distributed Inference with
+Multi-Level Caches"), Sec. 4.1 (sampling profile) and Sec. 6.4 (Rule 1 greedy,
+Rule 2 speculative sampling).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+BF16 = 0
+FP32 = 1
+RULE_GREEDY = 1
+RULE_SPECULATIVE = 2
+OK = 0
+ERR_ARG = -1
+ERR_DEVICE = -2
+ERR_WORKSPACE = -3
+S_BAD_PROPOSAL = -1
+S_LIMIT = -2
+S_Q_UNAVAILABLE = -3
+S_BAD_PROFILE = -4
+S_BAD_LOGITS = -5
+
+SAMPLING_DTYPE = np.dtype(
+    [("temperature_milli", "<u4"), ("top_k", "<u4"), ("top_p_milli", "<u4"),
+     ("reserved", "<u4"), ("session_key", "<u8")],
+    align=True,
+)
+EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_strerror", "sv_status_str", "sv_version")
+
+
+class SvError(RuntimeError):
+    pass
+
+
+class _Probe(ctypes.Structure):
+    _fields_ = [("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
+                ("rows_start", ctypes.c_void_p), ("rows_stop", ctypes.c_void_p)]
+
+
+class HipEvent:
+    """A raw hipEvent_t (for the probe's row-kernel timing slots)."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = h
+        self.handle = ctypes.c_void_p()
+        rc = HipEvent._hip.hipEventCreate(ctypes.byref(self.handle))
+        if rc != 0:
+            raise SvError(f"hipEventCreate failed ({rc})")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        HipEvent._hip.hipEventSynchronize(end.handle)
+        ms = ctypes.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise SvError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.handle:
+            HipEvent._hip.hipEventDestroy(self.handle)
+
+
+_lib = None
+
+
+def lib():
+    """Load libspecverify.so (raises SvError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SvError(f"{LIB_PATH} is missing: run token_sampling_amd.build.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.sv_workspace_bytes.argtypes = [ctypes.c_int32] * 3
+        L.sv_workspace_bytes.restype = ctypes.c_size_t
+        L.sv_verify.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify.restype = ctypes.c_int
+        L.sv_strerror.argtypes = [ctypes.c_int]
+        L.sv_strerror.restype = ctypes.c_char_p
+        L.sv_status_str.argtypes = [ctypes.c_int]
+        L.sv_status_str.restype = ctypes.c_char_p
+        L.sv_version.argtypes = []
+        L.sv_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def workspace_bytes(B: int, M: int, V: int) -> int:
+    return int(lib().sv_workspace_bytes(B, M, V))
+
+
+def strerror(code: int) -> str:
+    return lib().sv_strerror(code).decode()
+
+
+def status_str(status: int) -> str:
+    return lib().sv_status_str(status).decode()
+
+
+def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_key=None,
+                  device="cuda"):
+    """Pack per-session profiles into the [B] x 24-byte device array."""
+    import torch
+
+    s = np.zeros(B, dtype=SAMPLING_DTYPE)
+    s["temperature_milli"] = temperature_milli
+    s["top_k"] = top_k
+    s["top_p_milli"] = top_p_milli
+    s["session_key"] = np.arange(B, dtype=np.uint64) if session_key is None else session_key
+    raw = np.ascontiguousarray(s).view(np.uint8).reshape(B, 24)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def _check(t, name, dtype, shape, device):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, probe: bool = False,
+           workspace=None, out=None, stream=None, row_events=None):
+    """sv_verify on torch tensors (all on one GPU device).
+
+    target [B, M+1, V] bf16/fp32, draft [B, M, V] same dtype or None, tokens
+    [B, M] int32, m [B] int32, rule [B] int32, sampling [B, 24] uint8 (see
+    make_sampling).  Returns a dict with accepted_len [B] and out_tokens
+    [B, M+1] (int32), plus p_tok and q_tok [B, M] float64 if probe.  The call
+    is asynchronous on ``stream`` (default: torch's current stream).
+    row_events: optional (HipEvent, HipEvent) recorded around the row kernels.
+    """
+    import torch
+
+    if not (isinstance(target, torch.Tensor) and target.dim() == 3):
+        raise ValueError("target must be a [B, M+1, V] tensor")
+    dev = target.device
+    if dev.type != "cuda":
+        raise ValueError("target must be a GPU tensor")
+    B, M1, V = target.shape
+    M = M1 - 1
+    if target.dtype == torch.bfloat16:
+        dt = BF16
+    elif target.dtype == torch.float32:
+        dt = FP32
+    else:
+        raise TypeError("logits must be bfloat16 or float32")
+    _check(target, "target", None, None, dev)
+    if draft is not None:
+        _check(draft, "draft", target.dtype, (B, M, V), dev)
+    _check(tokens, "tokens", torch.int32, (B, M), dev)
+    _check(m, "m", torch.int32, (B,), dev)
+    _check(rule, "rule", torch.int32, (B,), dev)
+    _check(sampling, "sampling", None, None, dev)
+    if sampling.numel() * sampling.element_size() != 24 * B:
+        raise ValueError("sampling must hold B 24-byte records")
+
+    need = workspace_bytes(B, M, V)
+    if need == 0:
+        raise SvError("sizes out of range")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise SvError("workspace too small")
+    if out is None:
+        out = {
+            "accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((B, M + 1), dtype=torch.int32, device=dev),
+        }
+        if probe:
+            out["p_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
+            out["q_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
+    pr = None
+    if "p_tok" in out or row_events is not None:
+        ev0, ev1 = (row_events[0].handle, row_events[1].handle) if row_events else (None, None)
+        pr = ctypes.byref(_Probe(out["p_tok"].data_ptr() if "p_tok" in out else None,
+                                 out["q_tok"].data_ptr() if "q_tok" in out else None, ev0, ev1))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib().sv_verify(
+        target.data_ptr(), None if draft is None else draft.data_ptr(), dt,
+        tokens.data_ptr(), m.data_ptr(), rule.data_ptr(), sampling.data_ptr(),
+        B, M, V, seed, round_,
+        out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
+        stream.cuda_stream,
+    )
+    if rc != OK:
+        raise SvError(f"sv_verify failed: {strerror(rc)} ({rc})")
+    return out

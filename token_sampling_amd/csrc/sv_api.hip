@@ -1,0 +1,116 @@
+// sv_api.hip -- the C ABI of libspecverify (declared in include/specverify.h).
+//
+// sv_verify checks its scalar arguments on the host, carves the caller's
+// workspace and enqueues the kernels on the caller's stream:
+//   validate -> row profiles -> finalize (acceptance) -> sample (extra token).
+// It never synchronises and never allocates.
+#include <limits.h>
+
+#include "sv_kernels.hpp"
+
+namespace sv {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
+  (void)V;
+  WorkspaceLayout L;
+  size_t off = 0;
+  L.rows_off = off;
+  off = align_up(off + (size_t)B * (2 * (size_t)M + 1) * sizeof(RowRec), 256);
+  L.status_off = off;
+  off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+  L.jobs_off = off;
+  off = align_up(off + (size_t)B * sizeof(Job), 256);
+  L.total = off;
+  return L;
+}
+
+static bool sizes_ok(int32_t B, int32_t M, int32_t V, int32_t dtype) {
+  if (B < 1 || M < 1 || M > SV_M_MAX || V < 1 || V > SV_V_MAX) return false;
+  if (dtype != SV_BF16 && dtype != SV_FP32) return false;
+  // one workgroup per row slot; element counts must fit a signed 64-bit index
+  const unsigned long long slots = (unsigned long long)B * (2ull * (unsigned)M + 1ull);
+  if (slots > (unsigned long long)INT_MAX) return false;
+  const unsigned long long elems = (unsigned long long)B * ((unsigned)M + 1ull) * (unsigned)V;
+  if (elems > (unsigned long long)(LLONG_MAX / 4)) return false;
+  return true;
+}
+
+}  // namespace sv
+
+extern "C" size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V) {
+  if (!sv::sizes_ok(B, M, V, SV_BF16)) return 0;
+  return sv::workspace_layout(B, M, V).total;
+}
+
+extern "C" int sv_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                         const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
+                         const sv_sampling* sampling, int32_t B, int32_t M, int32_t V,
+                         uint64_t seed, uint32_t round, int32_t* accepted_len,
+                         int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                         const sv_probe* probe, void* stream) {
+  if (!target_logits || !draft_tokens || !m || !rule || !sampling || !accepted_len ||
+      !out_tokens || !workspace)
+    return SV_ERR_ARG;
+  if (!sv::sizes_ok(B, M, V, dtype)) return SV_ERR_ARG;
+  const sv::WorkspaceLayout L = sv::workspace_layout(B, M, V);
+  if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+
+  sv::LaunchArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.dtype = dtype;
+  a.tokens = draft_tokens;
+  a.m = m;
+  a.rule = rule;
+  a.sampling = sampling;
+  a.B = B;
+  a.M = M;
+  a.V = V;
+  a.seed = seed;
+  a.round = round;
+  a.accepted_len = accepted_len;
+  a.out_tokens = out_tokens;
+  a.p_tok = probe ? probe->p_tok : nullptr;
+  a.q_tok = probe ? probe->q_tok : nullptr;
+  char* ws = (char*)workspace;
+  a.rows = (sv::RowRec*)(ws + L.rows_off);
+  a.sess_status = (int32_t*)(ws + L.status_off);
+  a.jobs = (sv::Job*)(ws + L.jobs_off);
+
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();  // report only errors raised by the launches below
+  sv::launch_validate(a, st);
+  if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
+  sv::launch_rows_generic(a, st);
+  if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
+  sv::launch_finalize(a, st);
+  sv::launch_sample(a, st);
+  if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
+  return SV_OK;
+}
+
+extern "C" const char* sv_strerror(int code) {
+  switch (code) {
+    case SV_OK: return "ok";
+    case SV_ERR_ARG: return "invalid argument (null pointer, size out of range or unknown dtype)";
+    case SV_ERR_DEVICE: return "a kernel launch failed";
+    case SV_ERR_WORKSPACE: return "workspace smaller than sv_workspace_bytes()";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" const char* sv_status_str(int status) {
+  if (status >= 0) return "accepted";
+  switch (status) {
+    case SV_S_BAD_PROPOSAL: return "sdcp-bad-proposal: token out of range or q_i(x_i) == 0";
+    case SV_S_LIMIT: return "sdcp-limit: m outside [1, M]";
+    case SV_S_Q_UNAVAILABLE: return "sdcp-q-unavailable: rule 2 without draft logits";
+    case SV_S_BAD_PROFILE: return "bad profile: unknown rule, top_p_milli > 1000 or reserved != 0";
+    case SV_S_BAD_LOGITS: return "bad logits: NaN or +inf, or no finite logit, in a row read";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int sv_version(void) { return SV_VERSION; }

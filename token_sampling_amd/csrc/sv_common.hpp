@@ -1,0 +1,157 @@
+// sv_common.hpp -- device-side building blocks of libspecverify (gfx950).
+//
+// Ordered keys: every logit is mapped to an unsigned key whose integer order
+// is the float order, with -0 and +0 mapped to the same key (equal logits tie
+// by token id).  The profile's total order (logit desc, id asc) is then
+// (key desc, id asc) on exact integers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- row record
+// Everything the per-session kernels need about one logits row, written by
+// the row kernel.  The profile's support is {y : key(y) > kcut} plus the
+// tokens with key(y) == kcut and y <= idcut; every member has the weight
+// 2^((l_y - lmax) * scale), and the normaliser of the support is zsum.
+struct RowRec {
+  int32_t status;  // 0, or SV_S_BAD_LOGITS
+  int32_t argmax;  // smallest id attaining the largest logit
+  uint32_t kcut;   // key of the last token of the support (in profile order)
+  int32_t idcut;   // its token id
+  float lmax;      // largest logit
+  uint32_t pad;
+  double scale;    // log2(e) * 1000 / temperature_milli; 0 when T = 0
+  double zsum;     // mass of the support
+  double ptok;     // probability of the drafted token; -1 for the bonus row
+};
+static_assert(sizeof(RowRec) == 48, "RowRec layout");
+
+// Per-session draw left for the sampling kernel.
+enum JobKind : int32_t { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };
+struct Job {
+  int32_t kind;
+  int32_t pos;   // 0-based output position of the additional token (= a)
+  int32_t trow;  // 0-based target row index inside the session
+  int32_t drow;  // 0-based draft row index (residual only)
+  double u;      // purpose-1 uniform
+};
+static_assert(sizeof(Job) == 24, "Job layout");
+
+// ---------------------------------------------------------------- element traits
+struct Bf16 {
+  using elem_t = uint16_t;
+  static constexpr uint32_t kSign = 0x8000u;
+  static constexpr uint32_t kInfKey = 0x8000u + 0x7F80u;  // key(+inf)
+  static constexpr uint32_t kNegInfKey = 0x8000u - 0x7F80u;  // key(-inf)
+  static constexpr int kKeyBits = 16;
+  __device__ static inline uint32_t bits(elem_t e) { return e; }
+  __device__ static inline float value(uint32_t u) { return __uint_as_float(u << 16); }
+  __device__ static inline uint32_t key(uint32_t u) {
+    uint32_t mag = u & 0x7FFFu;
+    return (u & kSign) ? kSign - mag : kSign + mag;
+  }
+  __device__ static inline uint32_t unkey(uint32_t k) {
+    return k >= kSign ? k - kSign : (kSign | (kSign - k));
+  }
+};
+
+struct F32 {
+  using elem_t = uint32_t;
+  static constexpr uint32_t kSign = 0x80000000u;
+  static constexpr uint32_t kInfKey = 0x80000000u + 0x7F800000u;
+  static constexpr uint32_t kNegInfKey = 0x80000000u - 0x7F800000u;
+  static constexpr int kKeyBits = 32;
+  __device__ static inline uint32_t bits(elem_t e) { return e; }
+  __device__ static inline float value(uint32_t u) { return __uint_as_float(u); }
+  __device__ static inline uint32_t key(uint32_t u) {
+    uint32_t mag = u & 0x7FFFFFFFu;
+    return (u & kSign) ? kSign - mag : kSign + mag;
+  }
+  __device__ static inline uint32_t unkey(uint32_t k) {
+    return k >= kSign ? k - kSign : (kSign | (kSign - k));
+  }
+};
+
+// Weight of a support member: exp((l - lmax) / T) = 2^((l - lmax) * scale),
+// evaluated in binary64.  The difference of two binary32 values is exact in
+// binary64.
+__device__ inline double weight64(float l, float lmax, double scale) {
+  return exp2(((double)l - (double)lmax) * scale);
+}
+
+// ---------------------------------------------------------------- Philox4x64-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): ten rounds of two 64x64->128-bit products; the key is bumped by two
+// Weyl constants after each round.
+__device__ inline void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
+  const uint64_t w0 = 0x9E3779B97F4A7C15ull, w1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t lo0 = m0 * c[0], hi0 = __umul64hi(m0, c[0]);
+    const uint64_t lo1 = m1 * c[2], hi1 = __umul64hi(m1, c[2]);
+    const uint64_t n0 = hi1 ^ c[1] ^ k0;
+    const uint64_t n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += w0;
+    k1 += w1;
+  }
+}
+
+// Verifier uniforms (SDCP Sec. 6.4 structure): word 0 -> acceptance test,
+// word 1 -> additional token; the top 53 bits times 2^-53.
+__device__ inline void verifier_uniforms(uint64_t seed, uint64_t session_key, uint32_t round,
+                                         uint32_t pos1, double* u_acc, double* u_add) {
+  uint64_t c[4] = {round, pos1, 0, 0};
+  philox4x64_10(c, seed, session_key);
+  *u_acc = (double)(c[0] >> 11) * 0x1p-53;
+  *u_add = (double)(c[1] >> 11) * 0x1p-53;
+}
+
+// ---------------------------------------------------------------- reductions
+// Deterministic block-wide reductions: a fixed xor-butterfly inside each
+// wave64, then the wave totals combined in wave order by every thread.
+template <typename T, typename Op>
+__device__ inline T wave_reduce(T v, Op op) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+template <int NT, typename T, typename Op>
+__device__ inline T block_reduce(T v, Op op, T* smem) {
+  static_assert(NT % kWave == 0, "block of whole waves");
+  v = wave_reduce(v, op);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) smem[threadIdx.x / kWave] = v;
+  __syncthreads();
+  T r = smem[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) r = op(r, smem[w]);
+  return r;
+}
+
+struct OpAdd {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a > b ? a : b; }
+};
+struct OpMin {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a < b ? a : b; }
+};
+
+}  // namespace sv

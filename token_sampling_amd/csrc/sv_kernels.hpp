@@ -1,0 +1,41 @@
+// sv_kernels.hpp -- launch interface between the host entry points and the
+// kernels of libspecverify.
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+struct LaunchArgs {
+  const void* target;
+  const void* draft;  // may be null
+  int32_t dtype;
+  const int32_t* tokens;
+  const int32_t* m;
+  const int32_t* rule;
+  const sv_sampling* sampling;
+  int32_t B, M, V;
+  uint64_t seed;
+  uint32_t round;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  double* p_tok;  // may be null
+  double* q_tok;  // may be null
+  // workspace carve-up
+  RowRec* rows;         // [B, 2M+1]: target rows 1..M+1, then draft rows 1..M
+  int32_t* sess_status; // [B]
+  Job* jobs;            // [B]
+};
+
+struct WorkspaceLayout {
+  size_t rows_off, status_off, jobs_off, total;
+};
+
+WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
+
+void launch_validate(const LaunchArgs& a, hipStream_t st);
+void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
+void launch_finalize(const LaunchArgs& a, hipStream_t st);
+void launch_sample(const LaunchArgs& a, hipStream_t st);
+
+}  // namespace sv

@@ -1,0 +1,282 @@
+// sv_session.hip -- per-session kernels of libspecverify:
+//   validate  (one thread per session): argument checks that need no logits;
+//   finalize  (one wave64 per session, lane i = position i+1): the acceptance
+//             rule with a 64-bit ballot for the first rejection;
+//   sample    (one workgroup per session): the additional token as an inverse
+//             CDF over ascending token ids.
+#include "sv_kernels.hpp"
+
+namespace sv {
+
+namespace {
+
+// SDCP Table 2 / Sec. 6.3: statuses decidable before any logit is read.
+__global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ tokens,
+                                                  const int32_t* __restrict__ m,
+                                                  const int32_t* __restrict__ rule,
+                                                  const sv_sampling* __restrict__ sampling,
+                                                  int B, int M, int V, int has_draft,
+                                                  int32_t* __restrict__ sess_status) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int mb = m[b];
+  const int rl = rule[b];
+  const sv_sampling s = sampling[b];
+  int32_t st = 0;
+  if (mb < 1 || mb > M) {
+    st = SV_S_LIMIT;
+  } else if ((rl != SV_RULE_GREEDY && rl != SV_RULE_SPECULATIVE) || s.reserved != 0 ||
+             s.top_p_milli > 1000) {
+    st = SV_S_BAD_PROFILE;
+  } else if (rl == SV_RULE_SPECULATIVE && !has_draft) {
+    st = SV_S_Q_UNAVAILABLE;
+  } else {
+    for (int i = 0; i < mb; ++i) {
+      const int32_t x = tokens[(size_t)b * M + i];
+      if (x < 0 || x >= V) {
+        st = SV_S_BAD_PROPOSAL;
+        break;
+      }
+    }
+  }
+  sess_status[b] = st;
+}
+
+// SDCP Sec. 6.4.  Lane i examines position i+1.
+__global__ __launch_bounds__(kWave) void k_finalize(
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M,
+    uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
+    const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
+    Job* __restrict__ jobs) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (b >= B) return;
+  const int R = 2 * M + 1;
+  const RowRec* rr = rows + (size_t)b * R;
+  int32_t* out = out_tokens + (size_t)b * (M + 1);
+  int st = sess_status[b];
+  const int mb = m[b];
+  const int rl = rule[b];
+  const int32_t x = (st == 0 && lane < mb) ? tokens[(size_t)b * M + lane] : -1;
+
+  // every row the rule reads must be usable (target rows 1..m+1, draft rows 1..m)
+  if (st == 0) {
+    bool bad = false;
+    for (int j = lane; j <= mb; j += kWave) bad |= rr[j].status != 0;
+    if (rl == SV_RULE_SPECULATIVE && lane < mb) bad |= rr[M + 1 + lane].status != 0;
+    if (__any(bad)) st = SV_S_BAD_LOGITS;
+  }
+  // Sec. 6.3 step 5: q_i(x_i) != 0 at every position, before any draw
+  double qx = 1.0, px = -1.0;
+  if (st == 0 && rl == SV_RULE_SPECULATIVE) {
+    if (lane < mb) {
+      qx = rr[M + 1 + lane].ptok;
+      px = rr[lane].ptok;
+    }
+    if (__any(lane < mb && qx == 0.0)) st = SV_S_BAD_PROPOSAL;
+  }
+
+  if (st < 0) {
+    if (lane == 0) {
+      accepted_len[b] = st;
+      jobs[b] = Job{kJobNone, 0, 0, 0, 0.0};
+    }
+    for (int j = lane; j <= M; j += kWave) out[j] = -1;
+    for (int j = lane; j < M; j += kWave) {
+      if (p_tok) p_tok[(size_t)b * M + j] = -1.0;
+      if (q_tok) q_tok[(size_t)b * M + j] = -1.0;
+    }
+    return;
+  }
+
+  int a;
+  int32_t extra = -1;
+  if (rl == SV_RULE_GREEDY) {
+    // Rule 1: accept while x_i == argmax p_i; additional token argmax p_{a+1}
+    const bool acc = lane < mb && x == rr[lane].argmax;
+    const uint64_t rej = ~(uint64_t)__ballot(acc);
+    a = rej == 0 ? kWave : __builtin_ctzll(rej);
+    a = a < mb ? a : mb;
+    extra = rr[a].argmax;
+    if (lane == 0) jobs[b] = Job{kJobNone, a, 0, 0, 0.0};
+  } else {
+    // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i))
+    double u_acc = 1.0, u_add = 0.0;
+    verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc, &u_add);
+    const double ratio = px / qx;
+    const bool acc = lane < mb && u_acc < (ratio < 1.0 ? ratio : 1.0);
+    const uint64_t rej = ~(uint64_t)__ballot(acc);
+    a = rej == 0 ? kWave : __builtin_ctzll(rej);
+    a = a < mb ? a : mb;
+    if (lane == 0) {
+      double ua, ud;
+      verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+      jobs[b] = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
+    }
+  }
+  if (lane == 0) accepted_len[b] = a;
+  for (int j = lane; j <= M; j += kWave) {
+    int32_t v = -1;
+    if (j < a) v = x;  // j < a <= 64 means j == lane
+    else if (j == a && rl == SV_RULE_GREEDY) v = extra;
+    else if (j == a) v = -1;  // written by the sampling kernel
+    out[j] = v;
+  }
+  for (int j = lane; j < M; j += kWave) {
+    const bool have = rl == SV_RULE_SPECULATIVE && j < mb;
+    if (p_tok) p_tok[(size_t)b * M + j] = have ? px : -1.0;
+    if (q_tok) q_tok[(size_t)b * M + j] = have ? qx : -1.0;
+  }
+}
+
+constexpr int kSampleNT = 256;
+constexpr int kSampleE = 8;  // consecutive tokens per thread per chunk
+
+template <class Tr>
+struct SampleRow {
+  const typename Tr::elem_t* row;
+  RowRec r;
+  __device__ double prob(int y) const {
+    const uint32_t u = Tr::bits(row[y]);
+    const uint32_t k = Tr::key(u);
+    const bool member = k > r.kcut || (k == r.kcut && y <= r.idcut);
+    return member ? weight64(Tr::value(u), r.lmax, r.scale) / r.zsum : 0.0;
+  }
+};
+
+// Inclusive-to-exclusive block scan of binary64 values (fixed order).
+__device__ double block_exclusive_scan(double v, double* wsum, double* total) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  double inc = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += t;
+  }
+  double exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = 0.0;
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wid] = inc;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSampleNT / kWave; ++w) {
+    if (w < wid) base += wsum[w];
+    tot += wsum[w];
+  }
+  *total = tot;
+  return base + exc;
+}
+
+// Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2: additional token from
+// norm(max(0, p_j - q_j)) at the first rejection j, or from p_{m+1}; the
+// smallest id whose running mass exceeds u * S.
+template <class Tr>
+__global__ __launch_bounds__(kSampleNT) void k_sample(
+    const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
+    int B, int M, int V, const RowRec* __restrict__ rows, const Job* __restrict__ jobs,
+    int32_t* __restrict__ out_tokens) {
+  __shared__ double wsum[kSampleNT / kWave];
+  __shared__ double red[kSampleNT / kWave];
+  __shared__ int32_t ired[kSampleNT / kWave];
+  const int b = blockIdx.x;
+  if (b >= B) return;
+  const Job job = jobs[b];
+  if (job.kind == kJobNone) return;
+  const int R = 2 * M + 1;
+  SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow]};
+  SampleRow<Tr> Q{P.row, P.r};
+  bool resid = job.kind == kJobResidual;
+  if (resid) Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
+                               rows[(size_t)b * R + M + 1 + job.drow]};
+
+  auto weight = [&](int y) -> double {
+    const double p = P.prob(y);
+    if (!resid) return p;
+    const double d = p - Q.prob(y);
+    return d > 0.0 ? d : 0.0;
+  };
+
+  // pass 1: total mass S and the last id with mass
+  double S = 0.0;
+  int32_t last = -1;
+  for (int y = threadIdx.x; y < V; y += kSampleNT) {
+    const double w = weight(y);
+    S += w;
+    if (w > 0.0) last = y;
+  }
+  S = block_reduce<kSampleNT>(S, OpAdd(), red);
+  last = block_reduce<kSampleNT>(last, OpMax(), ired);
+  if (resid && S == 0.0) {  // residual without mass (rounding only): draw from p
+    resid = false;
+    S = 0.0;
+    last = -1;
+    for (int y = threadIdx.x; y < V; y += kSampleNT) {
+      const double w = weight(y);
+      S += w;
+      if (w > 0.0) last = y;
+    }
+    S = block_reduce<kSampleNT>(S, OpAdd(), red);
+    last = block_reduce<kSampleNT>(last, OpMax(), ired);
+  }
+  const double tgt = job.u * S;
+
+  // pass 2: chunks of kSampleNT * kSampleE ids in order
+  double running = 0.0;
+  int32_t pick = -1;
+  for (int c0 = 0; c0 < V && pick < 0; c0 += kSampleNT * kSampleE) {
+    const int y0 = c0 + threadIdx.x * kSampleE;
+    double w[kSampleE];
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < kSampleE; ++e) {
+      w[e] = (y0 + e < V) ? weight(y0 + e) : 0.0;
+      s += w[e];
+    }
+    double total;
+    const double base = running + block_exclusive_scan(s, wsum, &total);
+    double acc = base;
+    int32_t mine = -1;
+#pragma unroll
+    for (int e = 0; e < kSampleE; ++e) {
+      acc += w[e];
+      if (mine < 0 && acc > tgt) mine = y0 + e;
+    }
+    // the first thread (in id order) whose running mass passes the target
+    const int32_t cand = mine >= 0 ? mine : 0x7FFFFFFF;
+    const int32_t first = block_reduce<kSampleNT>(cand, OpMin(), ired);
+    if (first != 0x7FFFFFFF) pick = first;
+    running += total;
+  }
+  if (pick < 0) pick = last;
+  if (threadIdx.x == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = pick;
+}
+
+}  // namespace
+
+void launch_validate(const LaunchArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_validate, dim3((a.B + 255) / 256), dim3(256), 0, st, a.tokens, a.m, a.rule,
+                     a.sampling, a.B, a.M, a.V, a.draft != nullptr ? 1 : 0, a.sess_status);
+}
+
+void launch_finalize(const LaunchArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize, dim3(a.B), dim3(kWave), 0, st, a.tokens, a.m, a.rule, a.sampling,
+                     a.B, a.M, a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens,
+                     a.p_tok, a.q_tok, a.jobs);
+}
+
+void launch_sample(const LaunchArgs& a, hipStream_t st) {
+  if (a.dtype == SV_BF16) {
+    hipLaunchKernelGGL(k_sample<Bf16>, dim3(a.B), dim3(kSampleNT), 0, st,
+                       (const uint16_t*)a.target, (const uint16_t*)a.draft, a.B, a.M, a.V, a.rows,
+                       a.jobs, a.out_tokens);
+  } else {
+    hipLaunchKernelGGL(k_sample<F32>, dim3(a.B), dim3(kSampleNT), 0, st,
+                       (const uint32_t*)a.target, (const uint32_t*)a.draft, a.B, a.M, a.V, a.rows,
+                       a.jobs, a.out_tokens);
+  }
+}
+
+}  // namespace sv

@@ -233,7 +233,12 @@ def make(name: str, device="cpu", sessions: int | None = None, draft_top_n: int 
 
 def to_numpy(w: Workload, sessions=None):
     """Host copies (bf16 as uint16 bits) of a workload, optionally a session slice."""
-    sl = slice(None) if sessions is None else sessions
+    if sessions is None:
+        sl = slice(None)
+        sl_np = slice(None)
+    else:
+        sl_np = np.asarray(torch.as_tensor(sessions).cpu().numpy(), dtype=np.int64)
+        sl = torch.as_tensor(sl_np, device=w.target.device)
 
     def rows(t):
         if t is None:
@@ -248,7 +253,7 @@ def to_numpy(w: Workload, sessions=None):
         tokens=w.tokens[sl].cpu().numpy().astype(np.int32),
         m=w.m[sl].cpu().numpy().astype(np.int32),
         rule=w.rule[sl].cpu().numpy().astype(np.int32),
-        sampling=w.sampling[sl].copy(), seed=w.seed, round=w.round,
+        sampling=w.sampling[sl_np].copy(), seed=w.seed, round=w.round,
     )
 
 
