@@ -2,7 +2,8 @@
 //
 // sv_verify checks its scalar arguments on the host, carves the caller's
 // workspace and enqueues the kernels on the caller's stream:
-//   validate -> row profiles -> finalize (acceptance) -> sample (extra token).
+//   validate -> row profiles (single-pass top-k kernel, then the generic
+//   kernel for every other row) -> finalize (acceptance) -> sample.
 // It never synchronises and never allocates.
 #include <limits.h>
 
@@ -83,6 +84,7 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   (void)hipGetLastError();  // report only errors raised by the launches below
   sv::launch_validate(a, st);
   if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
+  sv::launch_rows_topk(a, st);
   sv::launch_rows_generic(a, st);
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
   sv::launch_finalize(a, st);

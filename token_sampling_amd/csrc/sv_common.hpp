@@ -47,6 +47,7 @@ static_assert(sizeof(Job) == 24, "Job layout");
 // ---------------------------------------------------------------- element traits
 struct Bf16 {
   using elem_t = uint16_t;
+  static constexpr int32_t kDtype = SV_BF16;
   static constexpr uint32_t kSign = 0x8000u;
   static constexpr uint32_t kInfKey = 0x8000u + 0x7F80u;  // key(+inf)
   static constexpr uint32_t kNegInfKey = 0x8000u - 0x7F80u;  // key(-inf)
@@ -64,6 +65,7 @@ struct Bf16 {
 
 struct F32 {
   using elem_t = uint32_t;
+  static constexpr int32_t kDtype = SV_FP32;
   static constexpr uint32_t kSign = 0x80000000u;
   static constexpr uint32_t kInfKey = 0x80000000u + 0x7F800000u;
   static constexpr uint32_t kNegInfKey = 0x80000000u - 0x7F800000u;

@@ -27,6 +27,19 @@ struct LaunchArgs {
   Job* jobs;            // [B]
 };
 
+// Row status written by a specialised row kernel that could not finish a row;
+// the generic kernel then computes that row.
+constexpr int32_t kRowFallback = 1;
+
+// Rows whose support lies among the 64 best tokens go to the single-pass
+// top-k kernel (bf16 only): greedy rows, temperature-0 rows, 1 <= top_k <= 64.
+__host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule,
+                                                     const sv_sampling& s) {
+  if (dtype != SV_BF16) return false;
+  if (rule == SV_RULE_GREEDY || s.temperature_milli == 0) return true;
+  return s.top_k >= 1 && s.top_k <= 64;
+}
+
 struct WorkspaceLayout {
   size_t rows_off, status_off, jobs_off, total;
 };
@@ -34,6 +47,7 @@ struct WorkspaceLayout {
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
 
 void launch_validate(const LaunchArgs& a, hipStream_t st);
+void launch_rows_topk(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
 void launch_sample(const LaunchArgs& a, hipStream_t st);

@@ -209,12 +209,14 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
   const bool is_target = slot <= M;
   const int i = is_target ? slot + 1 : slot - M;  // 1-based position
   if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
+  const sv_sampling smp = sampling[b];
+  RowRec* rec = rows + (size_t)b * R + slot;
+  if (row_uses_topk_kernel(Tr::kDtype, rl, smp) && rec->status != kRowFallback) return;
   const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
   const typename Tr::elem_t* row =
       is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
                 : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
-  const sv_sampling smp = sampling[b];
-  profile_generic<Tr>(row, V, smp, rl == SV_RULE_GREEDY, x, rows + (size_t)b * R + slot, &sm);
+  profile_generic<Tr>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, &sm);
 }
 
 }  // namespace
