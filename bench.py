@@ -83,6 +83,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--sessions", type=int, default=None,
+                    help="diagnostic only: the workload's first N sessions instead of all")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -104,7 +106,7 @@ def main():
     torch.cuda.set_device(dev)
 
     log(f"[bench] building workload {args.workload}")
-    w = W.make(args.workload, device="cuda")
+    w = W.make(args.workload, device="cuda", sessions=args.sessions)
     smp = w.sampling_tensor(dev)
     B, M, V = w.B, w.M, w.V
     P = w.positions()

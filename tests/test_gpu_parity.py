@@ -204,3 +204,49 @@ def test_workload_full_size_sampled_sessions(name, sessions):
     parity.compare(g, o, f"{name}-sampled")
     parity.log(f"[workload] {name}: mean accepted {a[a >= 0].mean():.3f}, "
                f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")
+
+
+def test_topk_kernel_edge_cases():
+    """Rows handled by the single-pass top-k path (greedy, T = 0, top_k <= 64),
+    with an odd vocabulary so that rows start at every alignment."""
+    parity.log("[case] top-k path edge cases, V=4999")
+    B, M, V = 14, 3, 4999
+    rng = np.random.default_rng(61)
+    t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
+    d = (t[:, :M] + rng.normal(0, 0.7, size=(B, M, V))).astype(np.float32)
+    s = oracle.make_sampling(B, 900, 20, 1000)
+    rule = np.full(B, 2, np.int32)
+    m = np.full(B, M, np.int32)
+    t[0] = 1.5; d[0] = 1.5; s[0]["top_k"] = 50                   # every token tied
+    t[1] -= 30.0; d[1] -= 30.0; s[1]["top_k"] = 40                # all negative (key mode)
+    t[5][:, rng.random(V) < 0.7] = -np.inf                          # -inf masks
+    d[5][:, rng.random(V) < 0.7] = -np.inf
+    s[5]["top_k"] = 10
+    s[6]["temperature_milli"] = 0                                   # T = 0 with max ties
+    t[6, :, 100] = t[6].max() + 3; t[6, :, 2000] = t[6, :, 100]
+    d[6, :, 50] = d[6].max() + 3; d[6, :, 4000] = d[6, :, 50]
+    rule[7] = 1                                                     # greedy, +-0 at the top
+    t[7] = -np.abs(t[7]) - 1.0; t[7, :, 333] = -0.0; t[7, :, 444] = 0.0
+    s[8]["top_k"] = 64; s[8]["top_p_milli"] = 500
+    s[9]["top_k"] = 1
+    t[10] = -np.inf; d[10] = -np.inf                                # three finite tokens, k = 5
+    for j in (5, 77, 4998):
+        t[10, :, j] = rng.normal(); d[10, :, j] = rng.normal()
+    s[10]["top_k"] = 5
+    s[11]["top_k"] = 64; s[11]["temperature_milli"] = 250
+    s[12]["top_k"] = 7; s[12]["top_p_milli"] = 0
+    s[13]["top_k"] = 33; s[13]["top_p_milli"] = 990
+    tb, db = oracle.bf16_bits(t), oracle.bf16_bits(d)
+    tb[2, 1, 1234] = 0xFFC1          # negative NaN inside a raw-mode row
+    tb[3, 0, 17] = 0x7FC3            # positive NaN
+    db[4, 2, 4000] = 0x7F80          # +inf in a draft row
+    h = dict(target=tb, draft=db, tokens=np.zeros((B, M), np.int32), m=m, rule=rule,
+             sampling=s, seed=9, round=4)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    for b in (2, 3, 4):  # tokens of the sessions with bad rows: any in range
+        h["tokens"][b] = rng.integers(0, V, size=M)
+    h["tokens"][6] = np.argmax(oracle.bf16_to_float(db[6]), axis=-1)
+    o = parity.run_oracle(h)
+    assert (o["accepted_len"][[2, 3, 4]] == oracle.S_BAD_LOGITS).all()
+    g = parity.run_gpu(h)
+    parity.compare(g, o, "topk-edges")

@@ -23,6 +23,11 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
   L.jobs_off = off;
   off = align_up(off + (size_t)B * sizeof(Job), 256);
+  const size_t slots = (size_t)B * (2 * (size_t)M + 1);
+  L.supid_off = off;
+  off = align_up(off + slots * kSupMax * sizeof(int32_t), 256);
+  L.supp_off = off;
+  off = align_up(off + slots * kSupMax * sizeof(double), 256);
   L.total = off;
   return L;
 }
@@ -79,6 +84,8 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   a.rows = (sv::RowRec*)(ws + L.rows_off);
   a.sess_status = (int32_t*)(ws + L.status_off);
   a.jobs = (sv::Job*)(ws + L.jobs_off);
+  a.sup_id = (int32_t*)(ws + L.supid_off);
+  a.sup_p = (double*)(ws + L.supp_off);
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below

@@ -20,13 +20,17 @@ constexpr int kWave = 64;
 // the row kernel.  The profile's support is {y : key(y) > kcut} plus the
 // tokens with key(y) == kcut and y <= idcut; every member has the weight
 // 2^((l_y - lmax) * scale), and the normaliser of the support is zsum.
+// When nsup > 0 the support is also listed (ids ascending, with p(y)) in the
+// workspace's support arrays, and the additional token is drawn from that
+// list instead of the logits row.
+constexpr int kSupMax = 64;
 struct RowRec {
   int32_t status;  // 0, or SV_S_BAD_LOGITS
   int32_t argmax;  // smallest id attaining the largest logit
   uint32_t kcut;   // key of the last token of the support (in profile order)
   int32_t idcut;   // its token id
   float lmax;      // largest logit
-  uint32_t pad;
+  int32_t nsup;    // entries of the listed support (0: not listed)
   double scale;    // log2(e) * 1000 / temperature_milli; 0 when T = 0
   double zsum;     // mass of the support
   double ptok;     // probability of the drafted token; -1 for the bonus row

@@ -25,6 +25,8 @@ struct LaunchArgs {
   RowRec* rows;         // [B, 2M+1]: target rows 1..M+1, then draft rows 1..M
   int32_t* sess_status; // [B]
   Job* jobs;            // [B]
+  int32_t* sup_id;      // [B, 2M+1, kSupMax] listed supports (ids ascending)
+  double* sup_p;        // [B, 2M+1, kSupMax] their probabilities
 };
 
 // Row status written by a specialised row kernel that could not finish a row;
@@ -41,7 +43,7 @@ __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule
 }
 
 struct WorkspaceLayout {
-  size_t rows_off, status_off, jobs_off, total;
+  size_t rows_off, status_off, jobs_off, supid_off, supp_off, total;
 };
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);

@@ -74,7 +74,7 @@ __device__ void profile_generic(const typename Tr::elem_t* row, int V, const sv_
   RowRec r;
   r.status = bad ? SV_S_BAD_LOGITS : 0;
   r.argmax = amax;
-  r.pad = 0;
+  r.nsup = 0;
   r.lmax = Tr::value(Tr::unkey(kmax));
   r.ptok = -1.0;
 

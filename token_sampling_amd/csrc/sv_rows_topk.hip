@@ -1,6 +1,7 @@
 // sv_rows_topk.hip -- one wave64 streams one bf16 logits row in a single pass
 // and keeps an exact candidate set for the top-k tokens; then it applies
-// temperature and top-p on those candidates (SDCP Sec. 4.1).
+// temperature and top-p on those candidates (SDCP Sec. 4.1) and writes the
+// row's support, sorted by token id, for the acceptance and sampling steps.
 //
 // Handles rows whose support lies inside the k best tokens with k <= 64: greedy
 // rows and temperature-0 rows (k = 1) and rows with 1 <= top_k <= 64.
@@ -9,6 +10,13 @@
 // -mag(x) if x < 0  (so -0 and +0 tie), computed two logits at a time with
 // packed 16-bit instructions.  The profile order (logit desc, id asc) is the
 // order of the 48-bit composite  (key + 0x8000) << 32 | ~id  (larger first).
+// Positions outside the row (alignment head, tail of the last tile) are read
+// as -inf, and -inf never enters the candidates (it has probability zero).
+// Raw mode: when the first tile already shows k lanes holding a positive
+// logit, every token of the support is positive, and for positive values the
+// raw bf16 bits read as a signed 16-bit integer equal the key (negative values
+// read as negative integers and never pass a positive threshold).  Such rows
+// skip the key transform after their first tile.
 //
 // Candidate filter: a wave keeps, in its own LDS region, a superset of the k
 // best (key, id) pairs seen so far.  On the first tile the k-th largest lane
@@ -25,14 +33,30 @@ namespace sv {
 
 namespace {
 
-constexpr int kVec = 4;                    // 16-byte loads per lane per tile
-constexpr int kTile = kWave * kVec * 8;    // bf16 logits per tile (4096)
+#ifndef SV_TOPK_VEC
+#define SV_TOPK_VEC 2
+#endif
+#ifndef SV_TOPK_NBUF
+#define SV_TOPK_NBUF 4
+#endif
+constexpr int kVec = SV_TOPK_VEC;          // 16-byte loads per lane per tile
+constexpr int kNBuf = SV_TOPK_NBUF;        // tiles in the load ring (kNBuf - 1 in flight)
+constexpr int kTile = kWave * kVec * 8;    // bf16 logits per tile
 constexpr int kCap = 256;                  // candidate entries per wave
 constexpr int kWavesPerBlock = 4;          // independent rows per workgroup
+constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
+constexpr uint32_t kNegInfPair = 0xFF80FF80u;
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Element reads from ext-vector values go through a scalar first: this
+// compiler reads element 0 when __builtin_bit_cast is applied to an element.
+__device__ inline uint32_t elem(const u32x4& v, int d) {
+  const uint32_t w = v[d];
+  return w;
+}
 
 __device__ inline uint32_t key_pair(uint32_t x) {
   const s16x2 v = __builtin_bit_cast(s16x2, x);
@@ -48,6 +72,12 @@ __device__ inline uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                 __builtin_bit_cast(u16x2, b)));
 }
+// sign bits (0x8000 per half) of the halves whose key is below te
+__device__ inline uint32_t below_pair(uint32_t k, uint32_t te2) {
+  const s16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(s16x2, k),
+                                                __builtin_bit_cast(s16x2, te2));
+  return __builtin_bit_cast(uint32_t, d) & 0x80008000u;
+}
 __device__ inline int lo16(uint32_t k) { return (int)(short)(k & 0xFFFFu); }
 __device__ inline int hi16(uint32_t k) { return (int)(short)(k >> 16); }
 
@@ -60,24 +90,18 @@ __device__ inline float key_value(int key) {  // signed key -> bf16 value
   const uint32_t bits = key >= 0 ? (uint32_t)key : (0x8000u | (uint32_t)(-key));
   return __uint_as_float(bits << 16);
 }
-
-__device__ inline int wave_excl_scan(int v, int* total) {
-  const int lane = __lane_id();
-  int inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int t = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += t;
-  }
-  *total = __shfl(inc, kWave - 1, kWave);
-  return inc - v;
+__device__ inline int popc64(uint64_t m) { return __builtin_popcountll(m); }
+__device__ inline int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-__device__ inline int popc64(uint64_t m) { return __builtin_popcountll(m); }
+struct Cut {
+  int n;    // entries left
+  int kth;  // k-th best key (valid when n == k)
+};
 
 // Cut the region reg[0..n) to its k best entries (k <= 64, n <= kCap).
-// Returns the new count (min(n, k)); *kth receives the k-th best key if n >= k.
-__device__ __noinline__ int region_cut(uint64_t* reg, int n, int k, int* kth) {
+__device__ __noinline__ Cut region_cut(uint64_t* reg, int n, int k) {
   const int lane = __lane_id();
   uint64_t e[kCap / kWave];
 #pragma unroll
@@ -86,15 +110,12 @@ __device__ __noinline__ int region_cut(uint64_t* reg, int n, int k, int* kth) {
     e[i] = j < n ? reg[j] : 0ull;
   }
   if (n <= k) {
-    if (n == k) {
-      int mn = 0x7FFFFFFF;
+    int mn = 0x7FFFFFFF;
 #pragma unroll
-      for (int i = 0; i < kCap / kWave; ++i)
-        if (e[i]) mn = min(mn, comp_key(e[i]));
-      for (int off = kWave / 2; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off, kWave));
-      *kth = mn;
-    }
-    return n;
+    for (int i = 0; i < kCap / kWave; ++i)
+      if (e[i]) mn = min(mn, comp_key(e[i]));
+    for (int off = kWave / 2; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off, kWave));
+    return Cut{n, mn};
   }
   // k-th largest biased key (key + 0x8000), bit by bit
   uint32_t t = 0;
@@ -131,71 +152,89 @@ __device__ __noinline__ int region_cut(uint64_t* reg, int n, int k, int* kth) {
     const uint32_t hk = (uint32_t)(e[i] >> 32);
     const bool keep = e[i] != 0 && (hk > t || (hk == t && (uint32_t)e[i] >= lowcut));
     const uint64_t mask = __ballot(keep);
-    if (keep) reg[base + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = e[i];
+    if (keep) reg[base + lanes_below(mask)] = e[i];
     base += popc64(mask);
   }
-  *kth = (int)t - 0x8000;
-  return base;  // == k
+  return Cut{base, (int)t - 0x8000};
 }
 
-struct WaveState {
-  uint64_t* reg;    // this wave's LDS region
-  int n;            // entries in the region
-  int k;            // tokens the support may hold
-  int thr;          // candidates need key >= thr (or > thr when strict)
-  bool strict;      // the threshold is the exact k-th best key of a cut
-  bool overflow;    // the row is left to the generic kernel
-  uint32_t magmax;  // largest |x| bit pattern seen (NaN detection), packed pair
-};
-
-template <bool kFull>
-__device__ inline void load_tile(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec) {
+// Load one tile (kVec 16-byte vectors per lane).  Positions outside the row
+// read as -inf; only the tiles that touch the row's ends pay for the masks.
+__device__ inline void load_tile(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec,
+                                 int head, int V) {
   const int lane = __lane_id();
+  const int g0 = tile * (kTile / 8);
+  if ((tile > 0 || head == 0) && 8 * (g0 + kTile / 8) <= head + V) {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) v[j] = __builtin_nontemporal_load(vbase + g0 + j * kWave + lane);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
-    const int g = tile * (kTile / 8) + j * kWave + lane;
-    if (kFull) {
-      v[j] = __builtin_nontemporal_load(vbase + g);
-    } else {
-      v[j] = (u32x4)(0u);
-      if (g < nvec) v[j] = __builtin_nontemporal_load(vbase + g);
+    const int g = g0 + j * kWave + lane;
+    u32x4 w = (u32x4)(kNegInfPair);
+    if (g < nvec) w = __builtin_nontemporal_load(vbase + g);
+    const int p0 = 8 * g;  // position of the vector's first logit
+    if (p0 < head || p0 + 8 > head + V) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int p = p0 + 2 * d;
+        uint32_t x = elem(w, d);
+        if (p < head || p >= head + V) x = (x & 0xFFFF0000u) | 0xFF80u;
+        if (p + 1 < head || p + 1 >= head + V) x = (x & 0x0000FFFFu) | 0xFF800000u;
+        w[d] = x;
+      }
     }
+    v[j] = w;
   }
 }
 
-__device__ inline void load_tile_any(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec) {
-  if ((tile + 1) * (kTile / 8) <= nvec) load_tile<true>(v, vbase, tile, nvec);
-  else load_tile<false>(v, vbase, tile, nvec);
-}
-
-// keys of one loaded tile, in place; positions outside the row (boundary
-// tiles only) get key -32768.  Returns the lane's largest key.
-template <bool kInterior>
-__device__ inline int tile_keys(u32x4 (&v)[kVec], int tile, int head, int V, uint32_t& magmax) {
-  const int lane = __lane_id();
-  const int tile_pos = tile * kTile;
+// keys of one loaded tile, in place; returns the lane's largest key
+__device__ inline int tile_keys(u32x4 (&v)[kVec], uint32_t& magmax) {
   uint32_t m = 0x80008000u;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const uint32_t x = v[j][d];
-      uint32_t k = key_pair(x);
-      uint32_t mg = x & 0x7FFF7FFFu;
-      if (!kInterior) {
-        const int p = tile_pos + (j * kWave + lane) * 8 + 2 * d;
-        const bool vlo = p >= head && p < head + V;
-        const bool vhi = p + 1 >= head && p + 1 < head + V;
-        k = (vlo ? (k & 0xFFFFu) : 0x8000u) | (vhi ? (k & 0xFFFF0000u) : 0x80000000u);
-        mg = (vlo ? (mg & 0xFFFFu) : 0u) | (vhi ? (mg & 0xFFFF0000u) : 0u);
-      }
+      const uint32_t x = elem(v[j], d);
+      const uint32_t k = key_pair(x);
       v[j][d] = k;
       m = max_i16x2(m, k);
-      magmax = max_u16x2(magmax, mg);
+      magmax = max_u16x2(magmax, x & 0x7FFF7FFFu);
     }
   }
   return max(lo16(m), hi16(m));
+}
+
+// tokens of this lane with key >= te.  Written as the sign of (te - 1) - key
+// so that it shares no subexpression with the insertion loop (sharing keeps
+// sixteen masks alive across it).
+// raw mode: lane maximum of the raw bits as signed 16-bit integers, and the
+// largest raw bit pattern as unsigned (above 0xFF80 only for a negative NaN)
+__device__ inline int tile_raw(const u32x4 (&v)[kVec], uint32_t& umax) {
+  uint32_t m = 0x80008000u;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t x = elem(v[j], d);
+      m = max_i16x2(m, x);
+      umax = max_u16x2(umax, x);
+    }
+  }
+  return max(lo16(m), hi16(m));
+}
+
+__device__ inline int count_ge(const u32x4 (&v)[kVec], int te) {
+  const s16x2 tm1 = (s16x2)((short)(te - 1));
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < kVec * 4; ++q) {
+    const s16x2 d = __builtin_elementwise_sub_sat(tm1, __builtin_bit_cast(s16x2, elem(v[q >> 2], q & 3)));
+    const uint32_t sg = __builtin_bit_cast(uint32_t, d);
+    n += (int)(sg >> 15 & 1u) + (int)(sg >> 31);
+  }
+  return n;
 }
 
 // k-th largest of the 64 lane values (k <= 64), as a signed 16-bit key
@@ -209,72 +248,67 @@ __device__ inline int wave_kth_largest(int v, int k) {
   return (int)t - 0x8000;
 }
 
-__device__ inline int count_ge(const u32x4 (&v)[kVec], int te) {
-  // tokens of this lane with key >= te, counted on packed pairs
-  const s16x2 t2 = (s16x2)((short)te);
-  s16x2 acc = (s16x2)((short)0);
-#pragma unroll
-  for (int q = 0; q < kVec * 4; ++q) {
-    // copy the element to a scalar first: __builtin_bit_cast applied directly
-    // to an ext-vector element reads element 0 with this compiler
-    const uint32_t w = v[q >> 2][q & 3];
-    const s16x2 kq = __builtin_bit_cast(s16x2, w);
-    acc += __builtin_elementwise_sub_sat(kq, t2) >> 15;  // -1 where key < te
-  }
-  return 2 * kVec * 4 + acc.x + acc.y;
-}
+struct WaveState {
+  int n;            // entries in the region
+  int thr;          // candidates need key >= thr (or > thr when strict)
+  bool strict;      // the threshold is the exact k-th best key of a cut
+  bool overflow;    // the row is left to the generic kernel
+  bool raw;         // raw mode (see the file comment)
+  uint32_t magmax;  // largest |x| bit pattern seen in key mode, packed pair
+  uint32_t umax;    // largest raw bit pattern seen in raw mode, packed pair
+};
 
 // One tile: keys in place, the first-tile bound, then candidate insertion one
 // dword (two logits per lane) at a time.
-template <bool kInterior>
-__device__ inline void tile_process(WaveState& s, u32x4 (&v)[kVec], int tile, int head, int V) {
+__device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&v)[kVec], int tile,
+                                    int head) {
   const int lane = __lane_id();
-  const int tile_pos = tile * kTile;
-  const int lm = tile_keys<kInterior>(v, tile, head, V, s.magmax);
-  if (tile == 0) s.thr = wave_kth_largest(lm, s.k);
-  // valid keys are >= -0x7FFF; positions outside the row hold -0x8000
-  int te = max(s.strict ? s.thr + 1 : s.thr, -0x7FFF);
+  int lm;
+  if (tile == 0) {
+    uint32_t u0 = 0;
+    const int lm_raw = tile_raw(v, u0);
+    lm = tile_keys(v, s.magmax);
+    const int t_raw = wave_kth_largest(lm_raw, k);
+    s.raw = t_raw > 0;
+    s.thr = s.raw ? t_raw : wave_kth_largest(lm, k);
+  } else if (s.raw) {
+    lm = tile_raw(v, s.umax);
+  } else {
+    lm = tile_keys(v, s.magmax);
+  }
+  int te = max(s.strict ? s.thr + 1 : s.thr, kMinKey);
   const uint64_t lanes = __ballot(lm >= te);
   if (!lanes) return;
   if (s.n + popc64(lanes) * (kVec * 8) > kCap) {
     int c = lm >= te ? count_ge(v, te) : 0;
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    if (s.n + c > kCap && s.n >= k) {
+      const Cut ct = region_cut(reg, s.n, k);
+      s.n = ct.n;
+      s.thr = ct.kth;
+      s.strict = true;
+      te = max(ct.kth + 1, kMinKey);
+      c = lm >= te ? count_ge(v, te) : 0;
+      for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    }
     if (s.n + c > kCap) {
-      if (s.n >= s.k) {
-        int kth;
-        s.n = region_cut(s.reg, s.n, s.k, &kth);
-        s.thr = kth;
-        s.strict = true;
-        te = max(kth + 1, -0x7FFF);
-        c = lm >= te ? count_ge(v, te) : 0;
-        for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
-      }
-      if (s.n + c > kCap) {
-        s.overflow = true;
-        return;
-      }
+      s.overflow = true;
+      return;
     }
   }
-  // sign bits of the saturated difference key - te mark the tokens below te
-  const s16x2 te2 = (s16x2)((short)te);
+  const uint32_t te2 = (uint32_t)(uint16_t)te * 0x10001u;
+  const int base_pos = tile * kTile + lane * 8 - head;
 #pragma unroll
   for (int q = 0; q < kVec * 4; ++q) {
-    __builtin_amdgcn_sched_barrier(0);
-    const uint32_t kq = v[q >> 2][q & 3];
-    const uint32_t below =
-        __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(s16x2, kq), te2)) &
-        0x80008000u;
-    const bool plo = (below & 0x8000u) == 0, phi = (below >> 31) == 0;
+    const uint32_t kq = elem(v[q >> 2], q & 3);
+    const uint32_t bl = below_pair(kq, te2);
+    const bool plo = (bl & 0x8000u) == 0, phi = (bl >> 31) == 0;
     const uint64_t mlo = __ballot(plo), mhi = __ballot(phi);
     if (mlo | mhi) {
-      const int p = tile_pos + ((q >> 2) * kWave + lane) * 8 + 2 * (q & 3) - head;
+      const int p = base_pos + (q >> 2) * (kWave * 8) + 2 * (q & 3);
       const int nlo = popc64(mlo);
-      const int rlo = __builtin_amdgcn_mbcnt_hi((uint32_t)(mlo >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mlo, 0));
-      const int rhi = __builtin_amdgcn_mbcnt_hi((uint32_t)(mhi >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mhi, 0));
-      if (plo) s.reg[s.n + rlo] = composite(lo16(kq), (uint32_t)p);
-      if (phi) s.reg[s.n + nlo + rhi] = composite(hi16(kq), (uint32_t)(p + 1));
+      if (plo) reg[s.n + lanes_below(mlo)] = composite(lo16(kq), (uint32_t)p);
+      if (phi) reg[s.n + nlo + lanes_below(mhi)] = composite(hi16(kq), (uint32_t)(p + 1));
       s.n += nlo + popc64(mhi);
     }
   }
@@ -288,13 +322,33 @@ __device__ inline uint64_t wave_sort_desc(uint64_t x) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const uint64_t y = __shfl_xor(x, stride, kWave);
-      const bool up = (lane & size) == 0;         // this block sorts descending
-      const bool lower = (lane & stride) == 0;    // I hold the first slot
-      const bool take_max = (lower == up);
-      x = take_max ? (x > y ? x : y) : (x < y ? x : y);
+      const bool up = (lane & size) == 0;       // this block sorts descending
+      const bool lower = (lane & stride) == 0;  // I hold the first slot
+      x = (lower == up) ? (x > y ? x : y) : (x < y ? x : y);
     }
   }
   return x;
+}
+
+// bitonic sort by ascending 32-bit key, carrying a binary64 payload
+__device__ inline void wave_sort_asc(uint32_t& key, double& val) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t ok = __shfl_xor(key, stride, kWave);
+      const double ov = __shfl_xor(val, stride, kWave);
+      const bool up = (lane & size) == 0;       // this block sorts ascending
+      const bool lower = (lane & stride) == 0;
+      const bool take_small = (lower == up);
+      const bool swap = take_small ? (ok < key) : (ok > key);
+      if (swap) {
+        key = ok;
+        val = ov;
+      }
+    }
+  }
 }
 
 __device__ inline double wave_incl_scan_f64(double v) {
@@ -308,73 +362,93 @@ __device__ inline double wave_incl_scan_f64(double v) {
 }
 
 // The row's profile from its candidates: exactly the k best, sorted (one per
-// lane), then the BAD_LOGITS checks, temperature and top-p (SDCP Sec. 4.1).
-__device__ __noinline__ void row_finish(WaveState& s, int k, bool one_hot, const sv_sampling& smp,
-                                        int32_t x, RowRec* rec) {
+// lane), then the BAD_LOGITS checks, temperature and top-p (SDCP Sec. 4.1);
+// the support is written sorted by id with its probabilities.
+__device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_t magmax_pair,
+                                        uint32_t umax_pair, bool one_hot, uint32_t t_milli, uint32_t p_milli, int32_t x,
+                                        RowRec* rec, int32_t* sup_id, double* sup_p) {
   const int lane = __lane_id();
-  int kth;
-  const int n = region_cut(s.reg, s.n, k, &kth);
-  uint64_t e = lane < n ? s.reg[lane] : 0ull;
+  const int n = region_cut(reg, n_reg, k).n;
+  uint64_t e = lane < n ? reg[lane] : 0ull;
   e = wave_sort_desc(e);
 
-  uint32_t mm = s.magmax;
-  for (int off = kWave / 2; off > 0; off >>= 1) mm = max_u16x2(mm, __shfl_xor(mm, off, kWave));
+  uint32_t mm = magmax_pair, um = umax_pair;
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    mm = max_u16x2(mm, __shfl_xor(mm, off, kWave));
+    um = max_u16x2(um, __shfl_xor(um, off, kWave));
+  }
   const int magmax = max((int)(mm & 0xFFFFu), (int)(mm >> 16));
+  const int umax = max((int)(um & 0xFFFFu), (int)(um >> 16));
   const uint64_t top = __shfl(e, 0, kWave);
   const int kmax = comp_key(top);
   // NaN anywhere, +inf at the top, or no finite logit at all
-  const bool bad = magmax > 0x7F80 || kmax >= 0x7F80 || kmax <= -0x7F80;
+  const bool bad = magmax > 0x7F80 || umax > 0xFF80 || n == 0 || kmax >= 0x7F80;
 
   RowRec r;
   r.status = bad ? SV_S_BAD_LOGITS : 0;
   r.argmax = (int32_t)comp_id(top);
-  r.pad = 0;
+  r.nsup = 0;
   r.lmax = key_value(kmax);
   r.ptok = -1.0;
-  if (bad || one_hot) {
-    r.kcut = (uint32_t)(kmax + 0x8000);
-    r.idcut = r.argmax;
+  if (bad) {
+    r.kcut = 0;
+    r.idcut = 0;
     r.scale = 0.0;
     r.zsum = 1.0;
-    if (x >= 0 && !bad) r.ptok = (x == r.argmax) ? 1.0 : 0.0;
-  } else {
-    // top-k: the candidates that are finite (at most k of them); weights
-    // exp((l - lmax) / T); top-p on the renormalised top-k distribution
-    const double scale = 1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli;
-    const bool live = lane < n && comp_key(e) > -0x7F80;
-    const int kept = popc64(__ballot(live));
-    const double w = live ? exp2(((double)key_value(comp_key(e)) - (double)r.lmax) * scale) : 0.0;
-    const double C = wave_incl_scan_f64(w);
-    const double Zk = __shfl(C, kept - 1, kWave);
-    int cut = kept;
-    if (smp.top_p_milli < 1000) {
-      const double tgt = (double)smp.top_p_milli * Zk;
-      const uint64_t hit = __ballot(live && 1000.0 * C >= tgt);
-      cut = hit ? __builtin_ctzll(hit) + 1 : kept;
-    }
-    const double zsum = __shfl(C, cut - 1, kWave);
-    const uint64_t last = __shfl(e, cut - 1, kWave);
-    r.kcut = (uint32_t)(comp_key(last) + 0x8000);
-    r.idcut = (int32_t)comp_id(last);
-    r.scale = scale;
-    r.zsum = zsum;
-    if (x >= 0) {
-      const uint64_t hitx = __ballot(lane < cut && comp_id(e) == (uint32_t)x);
-      const int jx = hitx ? __builtin_ctzll(hitx) : 0;
-      const double wx = __shfl(w, jx, kWave);
-      r.ptok = hitx ? wx / zsum : 0.0;
-    }
+    if (lane == 0) *rec = r;
+    return;
+  }
+  // weights exp((l - lmax) / T) of the top-k (one-hot: the argmax, weight 1)
+  const double scale = one_hot ? 0.0 : 1.4426950408889634074 * 1000.0 / (double)t_milli;
+  const bool live = lane < (one_hot ? 1 : n);
+  const int kept = popc64(__ballot(live));
+  const double w = live ? exp2(((double)key_value(comp_key(e)) - (double)r.lmax) * scale) : 0.0;
+  const double C = wave_incl_scan_f64(w);
+  const double Zk = __shfl(C, kept - 1, kWave);
+  int cut = kept;
+  if (!one_hot && p_milli < 1000) {  // shortest prefix with 1000 * C >= P * Z_k
+    const double tgt = (double)p_milli * Zk;
+    const uint64_t hit = __ballot(live && 1000.0 * C >= tgt);
+    cut = hit ? __builtin_ctzll(hit) + 1 : kept;
+  }
+  const double zsum = __shfl(C, cut - 1, kWave);
+  const uint64_t last = __shfl(e, cut - 1, kWave);
+  r.kcut = (uint32_t)(comp_key(last) + 0x8000);
+  r.idcut = (int32_t)comp_id(last);
+  r.scale = scale;
+  r.zsum = zsum;
+  r.nsup = cut;
+  if (x >= 0) {
+    const uint64_t hitx = __ballot(lane < cut && comp_id(e) == (uint32_t)x);
+    const int jx = hitx ? __builtin_ctzll(hitx) : 0;
+    const double wx = __shfl(w, jx, kWave);
+    r.ptok = hitx ? wx / zsum : 0.0;
+  }
+  // the support in ascending id order, with p(y) = w(y) / Z'
+  uint32_t sid = lane < cut ? comp_id(e) : 0xFFFFFFFFu;
+  double sp = lane < cut ? w / zsum : 0.0;
+  wave_sort_asc(sid, sp);
+  if (lane < cut) {
+    sup_id[lane] = (int32_t)sid;
+    sup_p[lane] = sp;
   }
   if (lane == 0) *rec = r;
 }
 
-__global__ __launch_bounds__(kWave * kWavesPerBlock) void k_rows_topk(
+#ifndef SV_TOPK_WAVES_PER_EU
+#define SV_TOPK_WAVES_PER_EU 5
+#endif
+__global__ __launch_bounds__(kWave * kWavesPerBlock)
+__attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
-    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows) {
+    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows,
+    int32_t* __restrict__ sup_id, double* __restrict__ sup_p) {
   __shared__ uint64_t region[kWavesPerBlock][kCap];
-  const int wave = threadIdx.x / kWave;
+  // the wave index is uniform across the wave: keep it (and everything
+  // derived from it, such as the row address) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = __lane_id();
   const int R = 2 * M + 1;
   const long slot_g = (long)blockIdx.x * kWavesPerBlock + wave;
@@ -394,6 +468,7 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_rows_topk(
   const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
                                   : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
   RowRec* rec = rows + (size_t)b * R + slot;
+  uint64_t* reg = region[wave];
 
   // 16-byte aligned window over the row: positions [head, head + V) are the row
   const int head = (int)(((uintptr_t)row & 15u) >> 1);
@@ -403,28 +478,28 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_rows_topk(
   const int ntiles = (npos + kTile - 1) / kTile;
 
   WaveState s;
-  s.reg = region[wave];
   s.n = 0;
-  s.k = k;
   s.thr = -0x8000;
   s.strict = false;
   s.overflow = false;
+  s.raw = false;
   s.magmax = 0;
+  s.umax = 0;
 
-  // tiles fully inside the row take the unmasked path
-  const int t_first_full = (head + kTile - 1) / kTile;
-  const int t_end_full = (head + V) / kTile;
-  u32x4 va[kVec], vb[kVec];
-  load_tile_any(va, vbase, 0, nvec);
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load_tile_any(vb, vbase, t + 1, nvec);
-    if (t >= t_first_full && t < t_end_full) tile_process<true>(s, va, t, head, V);
-    else tile_process<false>(s, va, t, head, V);
-    if (t + 1 >= ntiles || s.overflow) break;
-    if (t + 2 < ntiles) load_tile_any(va, vbase, t + 2, nvec);
-    if (t + 1 >= t_first_full && t + 1 < t_end_full) tile_process<true>(s, vb, t + 1, head, V);
-    else tile_process<false>(s, vb, t + 1, head, V);
-    if (s.overflow) break;
+  // ring of kNBuf tiles: while one is processed the next kNBuf - 1 are in flight
+  u32x4 ring[kNBuf][kVec];
+#pragma unroll
+  for (int u = 0; u < kNBuf - 1; ++u)
+    if (u < ntiles) load_tile(ring[u], vbase, u, nvec, head, V);
+  for (int t = 0; t < ntiles && !s.overflow; t += kNBuf) {
+#pragma unroll
+    for (int u = 0; u < kNBuf; ++u) {
+      const int tt = t + u;
+      if (tt >= ntiles || s.overflow) break;
+      if (tt + kNBuf - 1 < ntiles)
+        load_tile(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec, head, V);
+      tile_process(s, reg, k, ring[u], tt, head);
+    }
   }
   if (s.overflow) {
     if (lane == 0) {
@@ -434,7 +509,9 @@ __global__ __launch_bounds__(kWave * kWavesPerBlock) void k_rows_topk(
     }
     return;
   }
-  row_finish(s, k, one_hot, smp, x, rec);
+  const size_t so = ((size_t)b * R + slot) * kSupMax;
+  row_finish(reg, s.n, k, s.magmax, s.umax, one_hot, smp.temperature_milli, smp.top_p_milli, x, rec,
+             sup_id + so, sup_p + so);
 }
 
 }  // namespace
@@ -445,7 +522,7 @@ void launch_rows_topk(const LaunchArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((slots + kWavesPerBlock - 1) / kWavesPerBlock);
   hipLaunchKernelGGL(k_rows_topk, dim3(grid), dim3(kWave * kWavesPerBlock), 0, st,
                      (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
-                     a.sampling, a.sess_status, a.B, a.M, a.V, a.rows);
+                     a.sampling, a.sess_status, a.B, a.M, a.V, a.rows, a.sup_id, a.sup_p);
 }
 
 }  // namespace sv

@@ -42,6 +42,52 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ to
   sess_status[b] = st;
 }
 
+// Inverse CDF over a listed support (ids ascending): the additional token is
+// the smallest id whose running mass exceeds u * S (the largest id with mass
+// if rounding leaves none).  With a q list the weights are the residual
+// max(0, p - q); a residual without mass falls back to p.  One wave; lane j
+// holds entry j.
+__device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
+                               const int32_t* qid_g, const double* qp_g, int nq, double u,
+                               int32_t* q_id, double* q_p) {
+  const int lane = __lane_id();
+  const int32_t y = lane < np ? p_id[lane] : 0x7FFFFFFF;
+  const double p = lane < np ? p_pr[lane] : 0.0;
+  double w = p;
+  if (qid_g) {
+    if (lane < nq) {
+      q_id[lane] = qid_g[lane];
+      q_p[lane] = qp_g[lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // q(y): binary search of y in the q list
+    int lo = 0, hi = nq;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (q_id[mid] < y) lo = mid + 1;
+      else hi = mid;
+    }
+    const double q = (lane < np && lo < nq && q_id[lo] == y) ? q_p[lo] : 0.0;
+    const double d = p - q;
+    w = d > 0.0 ? d : 0.0;
+    double S = w;
+    for (int off = kWave / 2; off > 0; off >>= 1) S += __shfl_xor(S, off, kWave);
+    if (S == 0.0) w = p;  // rounding only
+  }
+  double C = w;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(C, off, kWave);
+    if (lane >= off) C += t;
+  }
+  const double S = __shfl(C, kWave - 1, kWave);
+  const double tgt = u * S;
+  const uint64_t hit = __ballot(lane < np && C > tgt);
+  const uint64_t pos = __ballot(lane < np && w > 0.0);
+  const int j = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
+  return __shfl(y, j, kWave);
+}
+
 // SDCP Sec. 6.4.  Lane i examines position i+1.
 __global__ __launch_bounds__(kWave) void k_finalize(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
@@ -49,7 +95,9 @@ __global__ __launch_bounds__(kWave) void k_finalize(
     uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
     const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
-    Job* __restrict__ jobs) {
+    Job* __restrict__ jobs, const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p) {
+  __shared__ int32_t q_id[kSupMax];
+  __shared__ double q_p[kSupMax];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   if (b >= B) return;
@@ -110,9 +158,20 @@ __global__ __launch_bounds__(kWave) void k_finalize(
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
-    if (lane == 0) {
-      double ua, ud;
-      verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+    double ua, ud;
+    verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+    // additional token: residual at the first rejection, else the bonus row;
+    // drawn here when the rows' supports are listed, else by the sampler
+    const RowRec& P = rr[a];
+    const RowRec* Q = a < mb ? &rr[M + 1 + a] : nullptr;
+    if (P.nsup > 0 && (Q == nullptr || Q->nsup > 0)) {
+      extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
+                          sup_p + ((size_t)b * R + a) * kSupMax, P.nsup,
+                          Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                          Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                          Q ? Q->nsup : 0, ud, q_id, q_p);
+      if (lane == 0) jobs[b] = Job{kJobNone, a, 0, 0, 0.0};
+    } else if (lane == 0) {
       jobs[b] = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
     }
   }
@@ -120,8 +179,7 @@ __global__ __launch_bounds__(kWave) void k_finalize(
   for (int j = lane; j <= M; j += kWave) {
     int32_t v = -1;
     if (j < a) v = x;  // j < a <= 64 means j == lane
-    else if (j == a && rl == SV_RULE_GREEDY) v = extra;
-    else if (j == a) v = -1;  // written by the sampling kernel
+    else if (j == a) v = extra;  // -1: written by the sampling kernel
     out[j] = v;
   }
   for (int j = lane; j < M; j += kWave) {
@@ -264,7 +322,7 @@ void launch_validate(const LaunchArgs& a, hipStream_t st) {
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_finalize, dim3(a.B), dim3(kWave), 0, st, a.tokens, a.m, a.rule, a.sampling,
                      a.B, a.M, a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens,
-                     a.p_tok, a.q_tok, a.jobs);
+                     a.p_tok, a.q_tok, a.jobs, a.sup_id, a.sup_p);
 }
 
 void launch_sample(const LaunchArgs& a, hipStream_t st) {
