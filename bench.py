@@ -7,11 +7,11 @@ the acceptance kernel and the additional-token sampler.
 
 Prints ONE JSON line:
   value        verified positions per second, P = sum_b (m_b + 1) per step
-  roofline     the row-profile kernels: algorithmic bytes per launch (each
-               row a session's rule reads, once) / their average duration
-               measured with hipEvents recorded on the launch stream, against
-               the 8 TB/s HBM peak; traffic = counter-measured HBM bytes per
-               launch when known for the current kernels (else null)
+  roofline     the dominant row kernel: algorithmic bytes per launch (each
+               row it handles, once) / its average duration measured with
+               hipEvents recorded on the launch stream, against the 8 TB/s HBM
+               peak; traffic = counter-measured HBM bytes per launch when known
+               for the current kernel revision (else null)
   cpu_baseline the oracle (plain single-threaded C, binary64) on this host,
                on a bounded sample of the same workload's sessions
 Default workload: B=256, M=8, V=128256, bf16, T=0.7, top_k=50, top_p=0.9.
@@ -31,10 +31,14 @@ METRIC = "verified positions/sec (B*(M+1)/s) + achieved HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b256_topk_topp"
 
-# Counter-measured HBM traffic per launch of the row kernels (bytes), keyed by
-# (workload, kernel revision); filled from rocprofv3 FETCH_SIZE/WRITE_SIZE runs.
-KERNEL_REVISION = "rows-generic-v1"
-MEASURED_TRAFFIC = {}
+# Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
+# by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs and valid only for the revision they were taken on.
+KERNEL_REVISION = "topk-ring6-prio"
+MEASURED_TRAFFIC = {
+    # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
+    ("b256_topk_topp", "k_rows_topk", "topk-ring6-prio"): 1_119_484_928,
+}
 
 
 def log(msg):
@@ -85,6 +89,10 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--sessions", type=int, default=None,
                     help="diagnostic only: the workload's first N sessions instead of all")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain elementwise copy kernel "
+                         "(1 GiB read, 1 GiB written) three times, to calibrate HBM "
+                         "byte counters under a profiler")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -110,7 +118,6 @@ def main():
     smp = w.sampling_tensor(dev)
     B, M, V = w.B, w.M, w.V
     P = w.positions()
-    alg_bytes = w.algorithmic_bytes()
     ws = torch.empty(sv.workspace_bytes(B, M, V), dtype=torch.uint8, device=dev)
     out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
            "out_tokens": torch.empty((B, M + 1), dtype=torch.int32, device=dev)}
@@ -125,7 +132,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
-    row_ev = [(sv.HipEvent(), sv.HipEvent()) for _ in range(args.steps)]
+    row_ev = [(sv.HipEvent(), sv.HipEvent(), sv.HipEvent()) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -135,14 +142,29 @@ def main():
     stop.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    rows_ms = [a.elapsed_ms(b) for a, b in row_ev]
     ms_per_step = total_ms / args.steps
-    rows_avg_ms = sum(rows_ms) / len(rows_ms)
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, row kernels {rows_avg_ms:.4f} ms")
+    topk_ms = sum(a.elapsed_ms(b) for a, b, _ in row_ev) / args.steps
+    other_ms = sum(b.elapsed_ms(c) for _, b, c in row_ev) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, top-k row kernel {topk_ms:.4f} ms, "
+        f"other row kernel {other_ms:.4f} ms")
+
+    # the dominant kernel: the row kernel that takes longer; its algorithmic
+    # bytes are the rows it handles
+    split = w.row_bytes_by_kernel()
+    kname, kms, kbytes = (("k_rows_topk", topk_ms, split["topk"]) if topk_ms >= other_ms
+                          else ("k_rows_generic", other_ms, split["other"]))
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 x (1 GiB read + 1 GiB written)")
 
     a = out["accepted_len"].cpu()
-    achieved = alg_bytes / (rows_avg_ms * 1e-3) / 1e9
-    traffic = MEASURED_TRAFFIC.get((args.workload, KERNEL_REVISION))
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    traffic = MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
     result = {
         "metric": METRIC,
         "value": P / (ms_per_step * 1e-3),
@@ -159,14 +181,15 @@ def main():
         "config": {
             "workload": args.workload, "B": B, "M": M, "V": V,
             "logits": "bf16" if w.target.dtype == torch.bfloat16 else "fp32",
-            "positions_per_step": P, "algorithmic_bytes_per_step": alg_bytes,
+            "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(),
             "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "kernel": "row-profile kernels", "ms_per_launch": rows_avg_ms,
+            "kernel": kname, "ms_per_launch": kms, "algorithmic_bytes_per_launch": kbytes,
+            "row_kernels_ms": {"k_rows_topk": topk_ms, "k_rows_generic": other_ms},
         },
     }
     if args.cpu_budget > 0:

@@ -66,13 +66,15 @@ typedef struct sv_sampling {
  *    speculative-sampling sessions with p_i(x_i) and q_i(x_i) for i <= m[b]
  *    (every position, also past the first rejection); -1 elsewhere and for
  *    greedy or failed sessions.
- *  rows_start, rows_stop: hipEvent_t handles recorded on the launch stream
- *    immediately before and after the row-profile kernels (the step's
- *    dominant, HBM-streaming part), for timing it. */
+ *  rows_start, rows_mid, rows_stop: hipEvent_t handles recorded on the
+ *    launch stream immediately before the row-profile kernels (the step's
+ *    HBM-streaming part), between the single-pass top-k kernel and the
+ *    kernel for the other rows, and after them, for timing each. */
 typedef struct sv_probe {
   double *p_tok;
   double *q_tok;
   void *rows_start;
+  void *rows_mid;
   void *rows_stop;
 } sv_probe;
 

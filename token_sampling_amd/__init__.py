@@ -50,7 +50,8 @@ class SvError(RuntimeError):
 
 class _Probe(ctypes.Structure):
     _fields_ = [("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
-                ("rows_start", ctypes.c_void_p), ("rows_stop", ctypes.c_void_p)]
+                ("rows_start", ctypes.c_void_p), ("rows_mid", ctypes.c_void_p),
+                ("rows_stop", ctypes.c_void_p)]
 
 
 class HipEvent:
@@ -67,6 +68,7 @@ class HipEvent:
             h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
             h.hipEventDestroy.argtypes = [ctypes.c_void_p]
             HipEvent._hip = h
+        self._destroy = HipEvent._hip.hipEventDestroy  # kept for interpreter shutdown
         self.handle = ctypes.c_void_p()
         rc = HipEvent._hip.hipEventCreate(ctypes.byref(self.handle))
         if rc != 0:
@@ -81,8 +83,8 @@ class HipEvent:
         return float(ms.value)
 
     def __del__(self):
-        if HipEvent._hip is not None and self.handle:
-            HipEvent._hip.hipEventDestroy(self.handle)
+        if self.handle:
+            self._destroy(self.handle)
 
 
 _lib = None
@@ -165,7 +167,8 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     make_sampling).  Returns a dict with accepted_len [B] and out_tokens
     [B, M+1] (int32), plus p_tok and q_tok [B, M] float64 if probe.  The call
     is asynchronous on ``stream`` (default: torch's current stream).
-    row_events: optional (HipEvent, HipEvent) recorded around the row kernels.
+    row_events: optional (start, stop) or (start, mid, stop) HipEvents recorded
+        around the row kernels, mid between the top-k kernel and the other.
     """
     import torch
 
@@ -209,9 +212,14 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
             out["q_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
     pr = None
     if "p_tok" in out or row_events is not None:
-        ev0, ev1 = (row_events[0].handle, row_events[1].handle) if row_events else (None, None)
+        evs = [None, None, None]
+        if row_events is not None:
+            if len(row_events) == 2:
+                evs = [row_events[0].handle, None, row_events[1].handle]
+            else:
+                evs = [e.handle for e in row_events]
         pr = ctypes.byref(_Probe(out["p_tok"].data_ptr() if "p_tok" in out else None,
-                                 out["q_tok"].data_ptr() if "q_tok" in out else None, ev0, ev1))
+                                 out["q_tok"].data_ptr() if "q_tok" in out else None, *evs))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     rc = lib().sv_verify(

@@ -92,6 +92,7 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   sv::launch_validate(a, st);
   if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
   sv::launch_rows_topk(a, st);
+  if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
   sv::launch_rows_generic(a, st);
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
   sv::launch_finalize(a, st);

@@ -37,19 +37,22 @@ namespace {
 #define SV_TOPK_VEC 2
 #endif
 #ifndef SV_TOPK_NBUF
-#define SV_TOPK_NBUF 4
+#define SV_TOPK_NBUF 6
 #endif
 constexpr int kVec = SV_TOPK_VEC;          // 16-byte loads per lane per tile
 constexpr int kNBuf = SV_TOPK_NBUF;        // tiles in the load ring (kNBuf - 1 in flight)
 constexpr int kTile = kWave * kVec * 8;    // bf16 logits per tile
 constexpr int kCap = 256;                  // candidate entries per wave
-constexpr int kWavesPerBlock = 4;          // independent rows per workgroup
+#ifndef SV_TOPK_WPB
+#define SV_TOPK_WPB 1
+#endif
+constexpr int kWavesPerBlock = SV_TOPK_WPB;  // independent rows per workgroup
 constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
-constexpr uint32_t kNegInfPair = 0xFF80FF80u;
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
 // Element reads from ext-vector values go through a scalar first: this
 // compiler reads element 0 when __builtin_bit_cast is applied to an element.
@@ -72,12 +75,6 @@ __device__ inline uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                 __builtin_bit_cast(u16x2, b)));
 }
-// sign bits (0x8000 per half) of the halves whose key is below te
-__device__ inline uint32_t below_pair(uint32_t k, uint32_t te2) {
-  const s16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(s16x2, k),
-                                                __builtin_bit_cast(s16x2, te2));
-  return __builtin_bit_cast(uint32_t, d) & 0x80008000u;
-}
 __device__ inline int lo16(uint32_t k) { return (int)(short)(k & 0xFFFFu); }
 __device__ inline int hi16(uint32_t k) { return (int)(short)(k >> 16); }
 
@@ -96,55 +93,62 @@ __device__ inline int lanes_below(uint64_t m) {
 }
 
 struct Cut {
-  int n;    // entries left
+  int n;    // entries left (all non-empty)
   int kth;  // k-th best key (valid when n == k)
 };
 
-// Cut the region reg[0..n) to its k best entries (k <= 64, n <= kCap).
-__device__ __noinline__ Cut region_cut(uint64_t* reg, int n, int k) {
+// Cut the region reg[0..n) to its k best entries (k <= 64, n <= kCap) and
+// compact them to the front; empty entries (0) are dropped.  An odd count is
+// followed by one empty entry so that pair stores stay 16-byte aligned.
+__device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, int k) {
   const int lane = __lane_id();
   uint64_t e[kCap / kWave];
+  int live = 0;
 #pragma unroll
   for (int i = 0; i < kCap / kWave; ++i) {
     const int j = i * kWave + lane;
     e[i] = j < n ? reg[j] : 0ull;
+    live += popc64(__ballot(e[i] != 0));
   }
-  if (n <= k) {
+  // keep entries with biased key (key + 0x8000) > t, or == t with low word >= lowcut;
+  // every non-empty entry has a biased key above 0, so t = 0 keeps them all
+  uint32_t t = 0, lowcut = 0;
+  int kth = -0x8000;
+  if (live > k) {
+    for (int bit = 15; bit >= 0; --bit) {  // k-th largest biased key, bit by bit
+      const uint32_t cand = t | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < kCap / kWave; ++i) cnt += popc64(__ballot((uint32_t)(e[i] >> 32) >= cand));
+      if (cnt >= k) t = cand;
+    }
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kCap / kWave; ++i) {
+      gt += popc64(__ballot((uint32_t)(e[i] >> 32) > t));
+      eq += popc64(__ballot((uint32_t)(e[i] >> 32) == t));
+    }
+    const int need = k - gt;  // ties kept at key t, smallest ids first
+    if (eq > need) {
+      uint32_t u = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = u | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kCap / kWave; ++i)
+          cnt += popc64(__ballot((uint32_t)(e[i] >> 32) == t && (uint32_t)e[i] >= cand));
+        if (cnt >= need) u = cand;
+      }
+      lowcut = u;
+    }
+    kth = (int)t - 0x8000;
+  } else if (live == k) {
     int mn = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kCap / kWave; ++i)
       if (e[i]) mn = min(mn, comp_key(e[i]));
     for (int off = kWave / 2; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off, kWave));
-    return Cut{n, mn};
-  }
-  // k-th largest biased key (key + 0x8000), bit by bit
-  uint32_t t = 0;
-  for (int bit = 15; bit >= 0; --bit) {
-    const uint32_t cand = t | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < kCap / kWave; ++i) cnt += popc64(__ballot((uint32_t)(e[i] >> 32) >= cand));
-    if (cnt >= k) t = cand;
-  }
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int i = 0; i < kCap / kWave; ++i) {
-    gt += popc64(__ballot((uint32_t)(e[i] >> 32) > t));
-    eq += popc64(__ballot(e[i] != 0 && (uint32_t)(e[i] >> 32) == t));
-  }
-  const int need = k - gt;  // ties kept at key t, smallest ids first
-  uint32_t lowcut = 0;      // keep ties whose low word (~id) >= lowcut
-  if (eq > need) {
-    uint32_t u = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = u | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int i = 0; i < kCap / kWave; ++i)
-        cnt += popc64(__ballot(e[i] != 0 && (uint32_t)(e[i] >> 32) == t && (uint32_t)e[i] >= cand));
-      if (cnt >= need) u = cand;
-    }
-    lowcut = u;
+    kth = mn;
   }
   int base = 0;
 #pragma unroll
@@ -155,37 +159,39 @@ __device__ __noinline__ Cut region_cut(uint64_t* reg, int n, int k) {
     if (keep) reg[base + lanes_below(mask)] = e[i];
     base += popc64(mask);
   }
-  return Cut{base, (int)t - 0x8000};
+  if ((base & 1) && lane == 0) reg[base] = 0ull;
+  return Cut{base, kth};
 }
 
-// Load one tile (kVec 16-byte vectors per lane).  Positions outside the row
-// read as -inf; only the tiles that touch the row's ends pay for the masks.
-__device__ inline void load_tile(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec,
-                                 int head, int V) {
+// Issue the loads of one tile (kVec 16-byte vectors per lane).  Every call
+// issues the same loads on every path, so the compiler's wait counts stay
+// exact across the ring; lanes past the row's last vector read that vector
+// again and are masked when the tile is consumed.
+__device__ inline void load_tile(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec) {
   const int lane = __lane_id();
   const int g0 = tile * (kTile / 8);
-  if ((tile > 0 || head == 0) && 8 * (g0 + kTile / 8) <= head + V) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) v[j] = __builtin_nontemporal_load(vbase + g0 + j * kWave + lane);
-    return;
-  }
+  for (int j = 0; j < kVec; ++j)
+    v[j] = __builtin_nontemporal_load(vbase + min(g0 + j * kWave + lane, nvec - 1));
+}
+
+// Positions outside the row [head, head + V) read as -inf; only the tiles
+// that touch the row's ends call this.
+__device__ inline void mask_tile(u32x4 (&v)[kVec], int tile, int head, int V) {
+  const int lane = __lane_id();
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
-    const int g = g0 + j * kWave + lane;
-    u32x4 w = (u32x4)(kNegInfPair);
-    if (g < nvec) w = __builtin_nontemporal_load(vbase + g);
-    const int p0 = 8 * g;  // position of the vector's first logit
+    const int p0 = 8 * (tile * (kTile / 8) + j * kWave + lane);  // first logit of the vector
     if (p0 < head || p0 + 8 > head + V) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const int p = p0 + 2 * d;
-        uint32_t x = elem(w, d);
+        uint32_t x = elem(v[j], d);
         if (p < head || p >= head + V) x = (x & 0xFFFF0000u) | 0xFF80u;
         if (p + 1 < head || p + 1 >= head + V) x = (x & 0x0000FFFFu) | 0xFF800000u;
-        w[d] = x;
+        v[j][d] = x;
       }
     }
-    v[j] = w;
   }
 }
 
@@ -206,9 +212,6 @@ __device__ inline int tile_keys(u32x4 (&v)[kVec], uint32_t& magmax) {
   return max(lo16(m), hi16(m));
 }
 
-// tokens of this lane with key >= te.  Written as the sign of (te - 1) - key
-// so that it shares no subexpression with the insertion loop (sharing keeps
-// sixteen masks alive across it).
 // raw mode: lane maximum of the raw bits as signed 16-bit integers, and the
 // largest raw bit pattern as unsigned (above 0xFF80 only for a negative NaN)
 __device__ inline int tile_raw(const u32x4 (&v)[kVec], uint32_t& umax) {
@@ -225,14 +228,14 @@ __device__ inline int tile_raw(const u32x4 (&v)[kVec], uint32_t& umax) {
   return max(lo16(m), hi16(m));
 }
 
-__device__ inline int count_ge(const u32x4 (&v)[kVec], int te) {
-  const s16x2 tm1 = (s16x2)((short)(te - 1));
+// region slots this lane's tile needs at threshold te: two per dword
+// holding a key >= te (the pair insertion below)
+__device__ inline int slots_ge(const u32x4 (&v)[kVec], int te) {
   int n = 0;
 #pragma unroll
   for (int q = 0; q < kVec * 4; ++q) {
-    const s16x2 d = __builtin_elementwise_sub_sat(tm1, __builtin_bit_cast(s16x2, elem(v[q >> 2], q & 3)));
-    const uint32_t sg = __builtin_bit_cast(uint32_t, d);
-    n += (int)(sg >> 15 & 1u) + (int)(sg >> 31);
+    const uint32_t kq = elem(v[q >> 2], q & 3);
+    n += max(lo16(kq), hi16(kq)) >= te ? 2 : 0;
   }
   return n;
 }
@@ -249,7 +252,7 @@ __device__ inline int wave_kth_largest(int v, int k) {
 }
 
 struct WaveState {
-  int n;            // entries in the region
+  int n;            // region slots in use (even; empty entries are 0)
   int thr;          // candidates need key >= thr (or > thr when strict)
   bool strict;      // the threshold is the exact k-th best key of a cut
   bool overflow;    // the row is left to the generic kernel
@@ -259,10 +262,14 @@ struct WaveState {
 };
 
 // One tile: keys in place, the first-tile bound, then candidate insertion one
-// dword (two logits per lane) at a time.
+// dword (two logits per lane) at a time.  A lane whose dword holds a key at or
+// above the threshold stores both halves as a pair of region entries, the
+// half below the threshold as an empty entry: one ballot per dword.
 __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&v)[kVec], int tile,
-                                    int head) {
+                                    int head, int V) {
+  if (s.overflow) return;
   const int lane = __lane_id();
+  if ((tile == 0 && head > 0) || (tile + 1) * kTile > head + V) mask_tile(v, tile, head, V);
   int lm;
   if (tile == 0) {
     uint32_t u0 = 0;
@@ -280,15 +287,15 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
   const uint64_t lanes = __ballot(lm >= te);
   if (!lanes) return;
   if (s.n + popc64(lanes) * (kVec * 8) > kCap) {
-    int c = lm >= te ? count_ge(v, te) : 0;
+    int c = lm >= te ? slots_ge(v, te) : 0;
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     if (s.n + c > kCap && s.n >= k) {
       const Cut ct = region_cut(reg, s.n, k);
-      s.n = ct.n;
+      s.n = __builtin_amdgcn_readfirstlane((ct.n + 1) & ~1);
       s.thr = ct.kth;
       s.strict = true;
       te = max(ct.kth + 1, kMinKey);
-      c = lm >= te ? count_ge(v, te) : 0;
+      c = lm >= te ? slots_ge(v, te) : 0;
       for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     }
     if (s.n + c > kCap) {
@@ -296,20 +303,22 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
       return;
     }
   }
-  const uint32_t te2 = (uint32_t)(uint16_t)te * 0x10001u;
   const int base_pos = tile * kTile + lane * 8 - head;
 #pragma unroll
   for (int q = 0; q < kVec * 4; ++q) {
     const uint32_t kq = elem(v[q >> 2], q & 3);
-    const uint32_t bl = below_pair(kq, te2);
-    const bool plo = (bl & 0x8000u) == 0, phi = (bl >> 31) == 0;
-    const uint64_t mlo = __ballot(plo), mhi = __ballot(phi);
-    if (mlo | mhi) {
-      const int p = base_pos + (q >> 2) * (kWave * 8) + 2 * (q & 3);
-      const int nlo = popc64(mlo);
-      if (plo) reg[s.n + lanes_below(mlo)] = composite(lo16(kq), (uint32_t)p);
-      if (phi) reg[s.n + nlo + lanes_below(mhi)] = composite(hi16(kq), (uint32_t)(p + 1));
-      s.n += nlo + popc64(mhi);
+    const int klo = lo16(kq), khi = hi16(kq);
+    const bool hit = max(klo, khi) >= te;
+    const uint64_t mk = __ballot(hit);
+    if (mk) {
+      if (hit) {
+        const uint32_t p = (uint32_t)(base_pos + (q >> 2) * (kWave * 8) + 2 * (q & 3));
+        u64x2 pr;
+        pr[0] = klo >= te ? composite(klo, p) : 0ull;
+        pr[1] = khi >= te ? composite(khi, p + 1) : 0ull;
+        *(u64x2*)(reg + s.n + 2 * lanes_below(mk)) = pr;
+      }
+      s.n += 2 * popc64(mk);
     }
   }
 }
@@ -435,8 +444,33 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   if (lane == 0) *rec = r;
 }
 
+// Issue priority from the work a wave has left: a SIMD's arbiter serves the
+// highest priority first and the oldest wave among equals, so with equal
+// priorities the oldest wave streams its row well ahead of the others, the
+// others finish late and the memory system runs short of requests at the
+// end.  Waves with more of their row left ask for a higher priority.
+#ifndef SV_TOPK_PRIO
+#define SV_TOPK_PRIO 1
+#endif
+__device__ inline void set_priority(int left, int total) {
+#if SV_TOPK_PRIO == 1
+  if (2 * left > total) __builtin_amdgcn_s_setprio(3);
+  else if (4 * left > total) __builtin_amdgcn_s_setprio(2);
+  else if (8 * left > total) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+#elif SV_TOPK_PRIO == 2
+  if (4 * left > 3 * total) __builtin_amdgcn_s_setprio(3);
+  else if (2 * left > total) __builtin_amdgcn_s_setprio(2);
+  else if (4 * left > total) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+#else
+  (void)left;
+  (void)total;
+#endif
+}
+
 #ifndef SV_TOPK_WAVES_PER_EU
-#define SV_TOPK_WAVES_PER_EU 5
+#define SV_TOPK_WAVES_PER_EU 6
 #endif
 __global__ __launch_bounds__(kWave * kWavesPerBlock)
 __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
@@ -445,7 +479,7 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
     const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p) {
-  __shared__ uint64_t region[kWavesPerBlock][kCap];
+  __shared__ __align__(16) uint64_t region[kWavesPerBlock][kCap];
   // the wave index is uniform across the wave: keep it (and everything
   // derived from it, such as the row address) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -486,19 +520,26 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
   s.magmax = 0;
   s.umax = 0;
 
-  // ring of kNBuf tiles: while one is processed the next kNBuf - 1 are in flight
+  // ring of kNBuf tiles: while one is processed the next kNBuf - 1 are in
+  // flight.  The loop runs whole rounds of kNBuf tiles with no exit inside a
+  // round, so each ring slot keeps its registers; tiles past the row's end
+  // read as -inf (their loads re-read the row's last vector).
   u32x4 ring[kNBuf][kVec];
+  // the first kNBuf - 1 tiles are issued in ring order (kept by the
+  // scheduling barriers), as the steady state issues them
 #pragma unroll
-  for (int u = 0; u < kNBuf - 1; ++u)
-    if (u < ntiles) load_tile(ring[u], vbase, u, nvec, head, V);
-  for (int t = 0; t < ntiles && !s.overflow; t += kNBuf) {
+  for (int u = 0; u < kNBuf - 1; ++u) {
+    load_tile(ring[u], vbase, u, nvec);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nround = (ntiles + kNBuf - 1) / kNBuf;
+  for (int r = 0; r < nround && !s.overflow; ++r) {
+    set_priority(nround - r, nround);
 #pragma unroll
     for (int u = 0; u < kNBuf; ++u) {
-      const int tt = t + u;
-      if (tt >= ntiles || s.overflow) break;
-      if (tt + kNBuf - 1 < ntiles)
-        load_tile(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec, head, V);
-      tile_process(s, reg, k, ring[u], tt, head);
+      const int tt = r * kNBuf + u;
+      load_tile(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec);
+      tile_process(s, reg, k, ring[u], tt, head, V);
     }
   }
   if (s.overflow) {
@@ -526,3 +567,4 @@ void launch_rows_topk(const LaunchArgs& a, hipStream_t st) {
 }
 
 }  // namespace sv
+

@@ -89,6 +89,20 @@ class Workload:
         small = self.B * (4 * self.M + 4 + 4 + 24 + 4 + 4 * (self.M + 1))
         return rows * self.V * s + small
 
+    def row_bytes_by_kernel(self) -> dict:
+        """Row bytes read by each row kernel: the single-pass top-k kernel takes
+        bf16 rows whose support lies among the 64 best tokens (greedy rules,
+        temperature 0, 1 <= top_k <= 64); the other kernel takes the rest."""
+        m = self.m.to("cpu").to(torch.int64).numpy()
+        rule = self.rule.to("cpu").to(torch.int64).numpy()
+        s = self.sampling
+        bf16 = self.target.dtype == torch.bfloat16
+        topk_rule = (rule == 1) | (s["temperature_milli"] == 0) | ((s["top_k"] >= 1) & (s["top_k"] <= 64))
+        per_session = (m + 1) + m * (rule == 2)
+        row = self.V * self.target.element_size()
+        topk = int(per_session[topk_rule].sum()) * row if bf16 else 0
+        return {"topk": topk, "other": int(per_session.sum()) * row - topk}
+
 
 def _to_storage(x32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
     return x32.to(dtype)  # round to nearest even for bf16
