@@ -28,14 +28,16 @@ struct RowRec {
   int32_t status;  // 0, or SV_S_BAD_LOGITS
   int32_t argmax;  // smallest id attaining the largest logit
   uint32_t kcut;   // key of the last token of the support (in profile order)
-  int32_t idcut;   // its token id
+  int32_t idcut;   // its token id (< 0: not resolved, see ntie)
   float lmax;      // largest logit
   int32_t nsup;    // entries of the listed support (0: not listed)
   double scale;    // log2(e) * 1000 / temperature_milli; 0 when T = 0
   double zsum;     // mass of the support
   double ptok;     // probability of the drafted token; -1 for the bonus row
+  int32_t ntie;    // idcut < 0: the support keeps the ntie smallest ids at key kcut
+  int32_t pad;
 };
-static_assert(sizeof(RowRec) == 48, "RowRec layout");
+static_assert(sizeof(RowRec) == 56, "RowRec layout");
 
 // Per-session draw left for the sampling kernel.
 enum JobKind : int32_t { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };

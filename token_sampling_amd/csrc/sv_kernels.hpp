@@ -42,6 +42,15 @@ __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule
   return s.top_k >= 1 && s.top_k <= 64;
 }
 
+// Rows whose support is not limited to a few best tokens go to the one-pass
+// dense kernel (bf16 only): temperature > 0 with top-k off (top_k = 0 or
+// top_k >= V), with or without top-p.
+__host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rule,
+                                                      const sv_sampling& s, int32_t V) {
+  if (dtype != SV_BF16 || row_uses_topk_kernel(dtype, rule, s)) return false;
+  return s.top_k == 0 || s.top_k >= (uint32_t)V;
+}
+
 struct WorkspaceLayout {
   size_t rows_off, status_off, jobs_off, supid_off, supp_off, total;
 };
@@ -50,6 +59,7 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
 
 void launch_validate(const LaunchArgs& a, hipStream_t st);
 void launch_rows_topk(const LaunchArgs& a, hipStream_t st);
+void launch_rows_dense(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
 void launch_sample(const LaunchArgs& a, hipStream_t st);

@@ -1,0 +1,310 @@
+// sv_rows_dense.hip -- one pass over a bf16 logits row for the profiles whose
+// support is not limited to a few best tokens: temperature alone, or
+// temperature then top-p, with top-k off (SDCP Sec. 4.1).
+//
+// One wave64 streams one row through a ring of 1 KiB tiles (as the top-k
+// kernel does) and computes, in that single pass:
+//  - the largest logit and the smallest id holding it (the argmax);
+//  - Z = sum over the row of 2^((l - lmax) * scale), scale = log2(e) / T.  Each
+//    lane keeps a running maximum m and its sum relative to m: a tile's 16
+//    weights 2^((l - m) * scale) are summed in binary32 and added to the
+//    lane's binary64 sum, which is rescaled when m rises; the lanes combine in
+//    binary64 in a fixed order.  A NaN anywhere makes Z NaN.
+//  - with top-p: a count histogram of the kWin keys at and below the running
+//    maximum, in LDS, indexed by key mod kWin.  When the maximum rises, the
+//    bins of the keys that leave the window are cleared for the keys that
+//    enter; the window's bottom only rises, so every token whose key lies in
+//    the final window has been counted.  After the pass the walk from the top
+//    accumulates binary64 masses count * w(key) until 1000 * C >= P * Z: that
+//    gives the cut key kc and the number j of its tokens that stay (those with
+//    the j smallest ids, profile order being logit desc, id asc).  A cut below
+//    the window leaves the row to the generic kernel.
+//  - the drafted token's rank among the tokens of its key with smaller ids (its
+//    key's bin just before its tile, plus the earlier tokens of that tile): it
+//    is in the support iff its key is above kc, or equal to kc with rank < j.
+// The cut is recorded as (kc, j); the sampling kernel turns j into a cut id
+// when it needs one.
+#include "sv_kernels.hpp"
+#include "sv_stream.hpp"
+
+namespace sv {
+
+namespace {
+
+using namespace stream;
+
+constexpr int kVec = 2;                  // 16-byte loads per lane per tile
+#ifndef SV_DENSE_NBUF
+#define SV_DENSE_NBUF 6
+#endif
+constexpr int kNBuf = SV_DENSE_NBUF;     // tiles in the load ring (kNBuf - 1 in flight)
+constexpr int kTile = kWave * kVec * 8;  // bf16 logits per tile
+constexpr int kWin = 1024;               // keys in the top-p histogram window
+constexpr int kPerLane = kWin / kWave;   // bins per lane in the walk
+constexpr int kNegInfKey = -0x7F80;
+
+// signed key of a bf16 value (the order of the logits; +0 and -0 are equal)
+__device__ inline int skey_of(float f) {
+  const uint32_t h = __float_as_uint(f) >> 16;
+  const int mag = (int)(h & 0x7FFFu);
+  return (h & 0x8000u) ? -mag : mag;
+}
+__device__ inline float value_of(int key) {
+  const uint32_t bits = key >= 0 ? (uint32_t)key : (0x8000u | (uint32_t)(-key));
+  return __uint_as_float(bits << 16);
+}
+
+struct LaneSum {
+  float m;       // running maximum of this lane's logits (-inf: none finite yet)
+  double s;      // sum of 2^((l - m) * scale) over this lane's logits so far
+  float best;    // largest logit seen by this lane
+  int best_pos;  // window position of its first occurrence
+};
+
+struct Hist {
+  uint32_t* bin;  // kWin counts, index = key mod kWin
+  int anchor;     // largest key seen (the window is [anchor - kWin + 1, anchor])
+  int kx;         // key of the drafted token (when it has one)
+  int rank_x;     // tokens with key kx and a smaller id
+};
+
+// One 16-byte vector (8 logits) of a tile: binary32 values, the lane's maximum,
+// argmax, running sum, then (top-p rows) the histogram window and the drafted
+// token's rank.  p0 is the window position of the vector's first logit.
+__device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v, int p0, int px,
+                                 float scale_f, double scale) {
+  float f[8];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t x = elem(v, d);
+    f[2 * d] = __uint_as_float(x << 16);
+    f[2 * d + 1] = __uint_as_float(x & 0xFFFF0000u);
+  }
+  float lmv = f[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
+
+  if (lmv > L.best) {  // a new lane maximum: its first position in the vector
+    int e0 = 7;
+#pragma unroll
+    for (int e = 7; e >= 0; --e)
+      if (f[e] == lmv) e0 = e;
+    L.best = lmv;
+    L.best_pos = p0 + e0;
+  }
+  if (lmv > L.m) {
+    L.s = L.m == -__builtin_huge_valf() ? 0.0 : L.s * exp2(((double)L.m - (double)lmv) * scale);
+    L.m = lmv;
+  }
+  // a lane without a finite logit so far only holds -inf (weight 0) or NaN
+  const float mm = L.m == -__builtin_huge_valf() ? 0.0f : L.m;
+  float ts = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ts += __builtin_amdgcn_exp2f((f[e] - mm) * scale_f);
+  L.s += (double)ts;
+
+  if (!top_p) return;
+  // window anchor: the largest key so far (wave-uniform)
+  int tk = skey_of(lmv);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
+  if (tk > H.anchor) {
+    const int lane = __lane_id();
+    const int d = tk - H.anchor;  // keys anchor+1 .. tk take the bins of the keys leaving
+    for (int i = lane; i < kWin; i += kWave)
+      if (d >= kWin || ((i - (H.anchor + 1)) & (kWin - 1)) < d) H.bin[i] = 0u;
+    H.anchor = tk;
+  }
+  const int lo = H.anchor - (kWin - 1);
+  // the drafted token's rank: tokens of its key counted before this vector of
+  // the tile, plus the tokens of this vector (in every lane) at smaller ids
+  if (__ballot(px >= p0 && px < p0 + 8)) {
+    int before = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) before += (p0 + e < px && skey_of(f[e]) == H.kx) ? 1 : 0;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) before += __shfl_xor(before, off, kWave);
+    H.rank_x = (H.kx >= lo ? (int)H.bin[H.kx & (kWin - 1)] : 0) + before;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int k = skey_of(f[e]);
+    if (k >= lo && k > kNegInfKey) atomicAdd(&H.bin[k & (kWin - 1)], 1u);
+  }
+}
+
+#ifndef SV_DENSE_WAVES_PER_EU
+#define SV_DENSE_WAVES_PER_EU 4
+#endif
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_WAVES_PER_EU))) void k_rows_dense(
+    const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
+    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows) {
+  __shared__ uint32_t bins[kWin];
+  const int lane = __lane_id();
+  const int R = 2 * M + 1;
+  const int slot_g = blockIdx.x;
+  const int b = slot_g / R;
+  const int slot = slot_g - b * R;
+  if (b >= B || sess_status[b] != 0) return;
+  const int mb = m[b];
+  const int rl = rule[b];
+  const bool is_target = slot <= M;
+  const int i = is_target ? slot + 1 : slot - M;
+  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
+  const sv_sampling smp = sampling[b];
+  if (!row_uses_dense_kernel(SV_BF16, rl, smp, V)) return;
+  const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
+                                  : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
+  const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
+  const bool top_p = smp.top_p_milli < 1000;
+  const double scale = 1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli;
+  const float scale_f = (float)scale;
+  RowRec* rec = rows + (size_t)slot_g;
+
+  // 16-byte aligned window over the row: positions [head, head + V) are the row
+  const int head = (int)(((uintptr_t)row & 15u) >> 1);
+  const u32x4* vbase = (const u32x4*)(row - head);
+  const int npos = head + V;
+  const int nvec = (npos + 7) / 8;
+  const int ntiles = (npos + kTile - 1) / kTile;
+  const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
+
+  LaneSum L{-__builtin_huge_valf(), 0.0, -__builtin_huge_valf(), 0x7FFFFFFF};
+  Hist H{bins, -0x10000, x >= 0 ? skey_of(xval) : 0, 0};
+  const int px = x >= 0 ? x + head : -1;
+
+  u32x4 ring[kNBuf][kVec];
+#pragma unroll
+  for (int u = 0; u < kNBuf - 1; ++u) {
+    load_tile<kVec>(ring[u], vbase, u, nvec - 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nround = (ntiles + kNBuf - 1) / kNBuf;
+  for (int r = 0; r < nround; ++r) {
+    set_priority(nround - r, nround);
+#pragma unroll
+    for (int u = 0; u < kNBuf; ++u) {
+      const int tt = r * kNBuf + u;
+      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec - 1);
+      if ((tt == 0 && head > 0) || (tt + 1) * kTile > npos) mask_tile<kVec>(ring[u], tt, head, npos);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j)
+        dense_vec(L, H, top_p, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px, scale_f, scale);
+    }
+  }
+
+  // lanes combined in a fixed order: maximum, Z, argmax
+  float lmax = L.m;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, kWave));
+  double z = L.m == -__builtin_huge_valf() ? (L.s != L.s ? L.s : 0.0)
+                                            : L.s * exp2(((double)L.m - (double)lmax) * scale);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
+  int bpos = L.best == lmax ? L.best_pos : 0x7FFFFFFF;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) bpos = min(bpos, __shfl_xor(bpos, off, kWave));
+
+  RowRec rr{};
+  rr.argmax = bpos - head;
+  rr.lmax = lmax;
+  rr.scale = scale;
+  rr.ptok = -1.0;
+  const bool bad = !(z == z) || lmax == __builtin_huge_valf() || lmax == -__builtin_huge_valf();
+  if (bad) {
+    rr.status = SV_S_BAD_LOGITS;
+    rr.argmax = 0;
+    rr.zsum = 1.0;
+    if (lane == 0) *rec = rr;
+    return;
+  }
+  const double wx = x >= 0 ? weight64(xval, lmax, scale) : 0.0;
+  if (!top_p) {  // the support is every finite logit
+    rr.kcut = Bf16::kNegInfKey + 1;
+    rr.idcut = 0x7FFFFFFF;
+    rr.zsum = z;
+    if (x >= 0) rr.ptok = wx / z;
+    if (lane == 0) *rec = rr;
+    return;
+  }
+
+  // the walk from the top: lane q holds the bins of keys anchor - kPerLane*q - e
+  const double tgt = (double)smp.top_p_milli * z;  // stop at 1000 * C >= tgt
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) {
+    const int k = H.anchor - kPerLane * lane - e;
+    const uint32_t c = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
+    if (c) part += (double)c * weight64(value_of(k), lmax, scale);
+  }
+  double incl = part;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  const uint64_t hit = __ballot(1000.0 * incl >= tgt);
+  if (!hit) {  // the cut lies below the window
+    if (lane == 0) {
+      RowRec fb{};
+      fb.status = kRowFallback;
+      *rec = fb;
+    }
+    return;
+  }
+  const int q = __builtin_ctzll(hit);
+  int kc = 0, j = 0;
+  double c_above = 0.0, wc = 0.0;
+  if (lane == q) {
+    double c = incl - part;
+    for (int e = 0; e < kPerLane; ++e) {
+      const int k = H.anchor - kPerLane * lane - e;
+      const uint32_t cnt = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
+      if (!cnt) continue;
+      const double w = weight64(value_of(k), lmax, scale);
+      // this lane's last key with tokens, all kept, unless a key below crosses
+      kc = k;
+      j = (int)cnt;
+      c_above = c;
+      wc = w;
+      if (1000.0 * (c + (double)cnt * w) >= tgt) {
+        // the smallest j with 1000 * (c + j * w) >= tgt
+        int jj = (int)ceil((tgt / 1000.0 - c) / w);
+        jj = max(1, min((int)cnt, jj));
+        while (jj > 1 && 1000.0 * (c + (double)(jj - 1) * w) >= tgt) --jj;
+        while (jj < (int)cnt && 1000.0 * (c + (double)jj * w) < tgt) ++jj;
+        j = jj;
+        break;
+      }
+      c += (double)cnt * w;
+    }
+  }
+  kc = __shfl(kc, q, kWave);
+  j = __shfl(j, q, kWave);
+  c_above = __shfl(c_above, q, kWave);
+  wc = __shfl(wc, q, kWave);
+  const double zsum = c_above + (double)j * wc;
+  rr.kcut = (uint32_t)(kc + 0x8000);
+  rr.idcut = -1;
+  rr.ntie = j;
+  rr.zsum = zsum;
+  if (x >= 0) {
+    const bool member = H.kx > kc || (H.kx == kc && H.rank_x < j);
+    rr.ptok = member ? wx / zsum : 0.0;
+  }
+  if (lane == 0) *rec = rr;
+}
+
+}  // namespace
+
+void launch_rows_dense(const LaunchArgs& a, hipStream_t st) {
+  if (a.dtype != SV_BF16) return;
+  const unsigned grid = (unsigned)((size_t)a.B * (2 * a.M + 1));
+  hipLaunchKernelGGL(k_rows_dense, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
+                     (const uint16_t*)a.draft, a.tokens, a.m, a.rule, a.sampling, a.sess_status,
+                     a.B, a.M, a.V, a.rows);
+}
+
+}  // namespace sv

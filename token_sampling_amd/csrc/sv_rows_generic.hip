@@ -72,6 +72,8 @@ __device__ void profile_generic(const typename Tr::elem_t* row, int V, const sv_
   amax = block_reduce<kNT>(amax, OpMin(), sm->i32);
 
   RowRec r;
+  r.ntie = 0;
+  r.pad = 0;
   r.status = bad ? SV_S_BAD_LOGITS : 0;
   r.argmax = amax;
   r.nsup = 0;
@@ -211,7 +213,9 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
   if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
   const sv_sampling smp = sampling[b];
   RowRec* rec = rows + (size_t)b * R + slot;
-  if (row_uses_topk_kernel(Tr::kDtype, rl, smp) && rec->status != kRowFallback) return;
+  if ((row_uses_topk_kernel(Tr::kDtype, rl, smp) || row_uses_dense_kernel(Tr::kDtype, rl, smp, V)) &&
+      rec->status != kRowFallback)
+    return;
   const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
   const typename Tr::elem_t* row =
       is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V

@@ -28,10 +28,13 @@
 // entries; adversarial rows such as ascending logits or tiny vocabularies) is
 // left to the generic kernel (status kRowFallback).
 #include "sv_kernels.hpp"
+#include "sv_stream.hpp"
 
 namespace sv {
 
 namespace {
+
+using namespace stream;
 
 #ifndef SV_TOPK_VEC
 #define SV_TOPK_VEC 2
@@ -49,34 +52,7 @@ constexpr int kCap = 256;                  // candidate entries per wave
 constexpr int kWavesPerBlock = SV_TOPK_WPB;  // independent rows per workgroup
 constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
 
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-
-// Element reads from ext-vector values go through a scalar first: this
-// compiler reads element 0 when __builtin_bit_cast is applied to an element.
-__device__ inline uint32_t elem(const u32x4& v, int d) {
-  const uint32_t w = v[d];
-  return w;
-}
-
-__device__ inline uint32_t key_pair(uint32_t x) {
-  const s16x2 v = __builtin_bit_cast(s16x2, x);
-  const s16x2 mag = v & (s16x2)(0x7FFF);
-  const s16x2 s = v >> 15;  // 0 or -1 per half
-  return __builtin_bit_cast(uint32_t, (s16x2)((mag ^ s) - s));
-}
-__device__ inline uint32_t max_i16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, a),
-                                                                __builtin_bit_cast(s16x2, b)));
-}
-__device__ inline uint32_t max_u16x2(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
-}
-__device__ inline int lo16(uint32_t k) { return (int)(short)(k & 0xFFFFu); }
-__device__ inline int hi16(uint32_t k) { return (int)(short)(k >> 16); }
 
 __device__ inline uint64_t composite(int key, uint32_t id) {
   return ((uint64_t)(uint32_t)(key + 0x8000) << 32) | (uint64_t)(0xFFFFFFFFu - id);
@@ -87,11 +63,6 @@ __device__ inline float key_value(int key) {  // signed key -> bf16 value
   const uint32_t bits = key >= 0 ? (uint32_t)key : (0x8000u | (uint32_t)(-key));
   return __uint_as_float(bits << 16);
 }
-__device__ inline int popc64(uint64_t m) { return __builtin_popcountll(m); }
-__device__ inline int lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-}
-
 struct Cut {
   int n;    // entries left (all non-empty)
   int kth;  // k-th best key (valid when n == k)
@@ -161,38 +132,6 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
   }
   if ((base & 1) && lane == 0) reg[base] = 0ull;
   return Cut{base, kth};
-}
-
-// Issue the loads of one tile (kVec 16-byte vectors per lane).  Every call
-// issues the same loads on every path, so the compiler's wait counts stay
-// exact across the ring; lanes past the row's last vector read that vector
-// again and are masked when the tile is consumed.
-__device__ inline void load_tile(u32x4 (&v)[kVec], const u32x4* vbase, int tile, int nvec) {
-  const int lane = __lane_id();
-  const int g0 = tile * (kTile / 8);
-#pragma unroll
-  for (int j = 0; j < kVec; ++j)
-    v[j] = __builtin_nontemporal_load(vbase + min(g0 + j * kWave + lane, nvec - 1));
-}
-
-// Positions outside the row [head, head + V) read as -inf; only the tiles
-// that touch the row's ends call this.
-__device__ inline void mask_tile(u32x4 (&v)[kVec], int tile, int head, int V) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int j = 0; j < kVec; ++j) {
-    const int p0 = 8 * (tile * (kTile / 8) + j * kWave + lane);  // first logit of the vector
-    if (p0 < head || p0 + 8 > head + V) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int p = p0 + 2 * d;
-        uint32_t x = elem(v[j], d);
-        if (p < head || p >= head + V) x = (x & 0xFFFF0000u) | 0xFF80u;
-        if (p + 1 < head || p + 1 >= head + V) x = (x & 0x0000FFFFu) | 0xFF800000u;
-        v[j][d] = x;
-      }
-    }
-  }
 }
 
 // keys of one loaded tile, in place; returns the lane's largest key
@@ -269,7 +208,7 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
                                     int head, int V) {
   if (s.overflow) return;
   const int lane = __lane_id();
-  if ((tile == 0 && head > 0) || (tile + 1) * kTile > head + V) mask_tile(v, tile, head, V);
+  if ((tile == 0 && head > 0) || (tile + 1) * kTile > head + V) mask_tile<kVec>(v, tile, head, head + V);
   int lm;
   if (tile == 0) {
     uint32_t u0 = 0;
@@ -394,6 +333,8 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   const bool bad = magmax > 0x7F80 || umax > 0xFF80 || n == 0 || kmax >= 0x7F80;
 
   RowRec r;
+  r.ntie = 0;
+  r.pad = 0;
   r.status = bad ? SV_S_BAD_LOGITS : 0;
   r.argmax = (int32_t)comp_id(top);
   r.nsup = 0;
@@ -442,31 +383,6 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
     sup_p[lane] = sp;
   }
   if (lane == 0) *rec = r;
-}
-
-// Issue priority from the work a wave has left: a SIMD's arbiter serves the
-// highest priority first and the oldest wave among equals, so with equal
-// priorities the oldest wave streams its row well ahead of the others, the
-// others finish late and the memory system runs short of requests at the
-// end.  Waves with more of their row left ask for a higher priority.
-#ifndef SV_TOPK_PRIO
-#define SV_TOPK_PRIO 1
-#endif
-__device__ inline void set_priority(int left, int total) {
-#if SV_TOPK_PRIO == 1
-  if (2 * left > total) __builtin_amdgcn_s_setprio(3);
-  else if (4 * left > total) __builtin_amdgcn_s_setprio(2);
-  else if (8 * left > total) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-#elif SV_TOPK_PRIO == 2
-  if (4 * left > 3 * total) __builtin_amdgcn_s_setprio(3);
-  else if (2 * left > total) __builtin_amdgcn_s_setprio(2);
-  else if (4 * left > total) __builtin_amdgcn_s_setprio(1);
-  else __builtin_amdgcn_s_setprio(0);
-#else
-  (void)left;
-  (void)total;
-#endif
 }
 
 #ifndef SV_TOPK_WAVES_PER_EU
@@ -529,7 +445,7 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
   // scheduling barriers), as the steady state issues them
 #pragma unroll
   for (int u = 0; u < kNBuf - 1; ++u) {
-    load_tile(ring[u], vbase, u, nvec);
+    load_tile<kVec>(ring[u], vbase, u, nvec - 1);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int nround = (ntiles + kNBuf - 1) / kNBuf;
@@ -538,7 +454,7 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
 #pragma unroll
     for (int u = 0; u < kNBuf; ++u) {
       const int tt = r * kNBuf + u;
-      load_tile(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec);
+      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec - 1);
       tile_process(s, reg, k, ring[u], tt, head, V);
     }
   }

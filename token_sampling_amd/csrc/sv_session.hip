@@ -228,6 +228,38 @@ __device__ double block_exclusive_scan(double v, double* wsum, double* total) {
   return base + exc;
 }
 
+// A row that records its cut as (kcut, ntie) keeps the ntie smallest ids among
+// the tokens with key kcut: the id of the ntie-th of them, found by counting
+// in id order (chunks of kSampleNT * kSampleE ids, block scans of the counts).
+template <class Tr>
+__device__ int32_t resolve_idcut(const typename Tr::elem_t* row, int V, uint32_t kcut, int ntie,
+                                 double* wsum, int32_t* ired) {
+  double running = 0.0;
+  for (int c0 = 0; c0 < V; c0 += kSampleNT * kSampleE) {
+    const int y0 = c0 + threadIdx.x * kSampleE;
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < kSampleE; ++e)
+      cnt += (y0 + e < V && Tr::key(Tr::bits(row[y0 + e])) == kcut) ? 1 : 0;
+    double total;
+    const double before = running + block_exclusive_scan((double)cnt, wsum, &total);
+    int32_t mine = 0x7FFFFFFF;
+    if (before < ntie && before + cnt >= ntie) {
+      int seen = (int)before;
+      for (int e = 0; e < kSampleE; ++e) {
+        if (y0 + e < V && Tr::key(Tr::bits(row[y0 + e])) == kcut && ++seen == ntie) {
+          mine = y0 + e;
+          break;
+        }
+      }
+    }
+    const int32_t first = block_reduce<kSampleNT>(mine, OpMin(), ired);
+    if (first != 0x7FFFFFFF) return first;
+    running += total;
+  }
+  return 0x7FFFFFFF;  // fewer ties than ntie: keep them all
+}
+
 // Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2: additional token from
 // norm(max(0, p_j - q_j)) at the first rejection j, or from p_{m+1}; the
 // smallest id whose running mass exceeds u * S.
@@ -249,6 +281,8 @@ __global__ __launch_bounds__(kSampleNT) void k_sample(
   bool resid = job.kind == kJobResidual;
   if (resid) Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
                                rows[(size_t)b * R + M + 1 + job.drow]};
+  if (P.r.idcut < 0) P.r.idcut = resolve_idcut<Tr>(P.row, V, P.r.kcut, P.r.ntie, wsum, ired);
+  if (resid && Q.r.idcut < 0) Q.r.idcut = resolve_idcut<Tr>(Q.row, V, Q.r.kcut, Q.r.ntie, wsum, ired);
 
   auto weight = [&](int y) -> double {
     const double p = P.prob(y);
