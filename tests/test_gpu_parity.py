@@ -250,3 +250,66 @@ def test_topk_kernel_edge_cases():
     assert (o["accepted_len"][[2, 3, 4]] == oracle.S_BAD_LOGITS).all()
     g = parity.run_gpu(h)
     parity.compare(g, o, "topk-edges")
+
+
+def test_dense_kernel_edge_cases():
+    """Rows handled by the one-pass dense path (temperature, optional top-p,
+    top-k off): a maximum that rises tile after tile, heavy ties at the cut,
+    drafted tokens on both sides of a tied cut, a cut below the histogram
+    window (generic fallback), all-negative rows, masks, bad logits; an odd
+    vocabulary of five tiles so that rows start at every alignment."""
+    parity.log("[case] dense path edge cases, V=5003")
+    B, M, V = 14, 3, 5003
+    rng = np.random.default_rng(73)
+    t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
+    d = (t[:, :M] + rng.normal(0, 0.7, size=(B, M, V))).astype(np.float32)
+    s = oracle.make_sampling(B, 1000, 0, 900)
+    rule = np.full(B, 2, np.int32)
+    m = np.full(B, M, np.int32)
+    ramp = np.linspace(-5.0, 20.0, V, dtype=np.float32)             # 0: rising maximum
+    t[0] = ramp + rng.normal(0, 0.3, size=(M + 1, V)); d[0] = t[0, :M] + rng.normal(0, 0.3, (M, V))
+    t[1] = rng.integers(0, 4, size=(M + 1, V)); d[1] = t[1, :M]     # 1: ties, identical draft
+    s[1]["top_p_milli"] = 500
+    t[2] = rng.integers(0, 3, size=(M + 1, V)) * 0.5; d[2] = t[2, :M]  # 2, 3: tied cut, chosen x
+    t[3] = t[2]; d[3] = d[2]
+    s[2]["top_p_milli"] = s[3]["top_p_milli"] = 700
+    s[4]["temperature_milli"] = 100_000                              # 4: cut far below the top
+    t[5] = -np.abs(t[5]) - 5.0; d[5] = -np.abs(d[5]) - 5.0           # 5: all negative
+    s[5]["top_p_milli"] = 800
+    t[6][:, rng.random(V) < 0.7] = -np.inf                           # 6: -inf masks
+    d[6][:, rng.random(V) < 0.7] = -np.inf
+    s[6]["top_p_milli"] = 950
+    s[10]["top_p_milli"] = 999; s[10]["temperature_milli"] = 500     # 10: nearly the full row
+    s[11]["top_p_milli"] = 1000; s[11]["temperature_milli"] = 250    # 11: untruncated, peaked
+    t[11, :, 42] += 12.0; d[11, :, 42] += 12.0
+    t[12] = -np.inf; d[12] = -np.inf; t[12, :, 3000] = 1.0; d[12, :, 3000] = 2.0  # 12: one finite
+    s[12]["top_p_milli"] = 1000
+    s[13]["top_k"] = V; s[13]["top_p_milli"] = 600                   # 13: top_k >= V is off
+    t[13] = rng.integers(0, 5, size=(M + 1, V)); d[13] = rng.permutation(t[13, :M].ravel()).reshape(M, V)
+    tb, db = oracle.bf16_bits(t), oracle.bf16_bits(d)
+    tb[7, 1, 2500] = 0x7FC3          # 7: positive NaN in a target row
+    db[8, 2, 17] = 0xFFC1            # 8: negative NaN in a draft row
+    tb[9, 3, 4000] = 0x7F80          # 9: +inf in the bonus row
+    h = dict(target=tb, draft=db, tokens=np.zeros((B, M), np.int32), m=m, rule=rule,
+             sampling=s, seed=13, round=2)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    for b in (7, 8, 9):
+        h["tokens"][b] = rng.integers(0, V, size=M)
+    # sessions 2 and 3: drafted tokens at a tied cut key (draft == target rows)
+    for i in range(M):
+        st, p, _ = oracle.profile(tb[2, i], 1000, 0, 700)
+        assert st == 0
+        ids = np.nonzero(p > 0)[0]
+        kc = oracle.bf16_to_float(tb[2, i])[ids].min()            # the cut key's value
+        tied = np.nonzero(oracle.bf16_to_float(tb[2, i]) == kc)[0]
+        kept = [y for y in tied if p[y] > 0]
+        dropped = [y for y in tied if p[y] == 0]
+        assert kept and dropped, "the cut must split a tied key"
+        h["tokens"][2, i] = kept[-1] if i != 1 else kept[0]   # the last and the first kept tie
+        h["tokens"][3, i] = dropped[0]                         # the first tie left out: q(x) = 0
+    o = parity.run_oracle(h)
+    assert (o["accepted_len"][[7, 8, 9]] == oracle.S_BAD_LOGITS).all()
+    assert o["accepted_len"][3] == oracle.S_BAD_PROPOSAL
+    assert o["accepted_len"][1] == M                               # identical rows: all accepted
+    g = parity.run_gpu(h)
+    parity.compare(g, o, "dense-edges")
