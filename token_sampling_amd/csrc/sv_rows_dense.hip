@@ -4,12 +4,18 @@
 //
 // One wave64 streams one row through a ring of 1 KiB tiles (as the top-k
 // kernel does) and computes, in that single pass:
-//  - the largest logit and the smallest id holding it (the argmax);
-//  - Z = sum over the row of 2^((l - lmax) * scale), scale = log2(e) / T.  Each
-//    lane keeps a running maximum m and its sum relative to m: a tile's 16
-//    weights 2^((l - m) * scale) are summed in binary32 and added to the
-//    lane's binary64 sum, which is rescaled when m rises; the lanes combine in
-//    binary64 in a fixed order.  A NaN anywhere makes Z NaN.
+//  - the largest logit lmax;
+//  - Z = sum over the row of 2^((l - lmax) * s), s = log2(e) / T rounded to
+//    binary32; the whole row (Z, the histogram masses, the drafted token's
+//    probability, the sampler's weights) uses this same s, so its profile is
+//    the softmax at a temperature within half a binary32 ulp of T.  Each lane
+//    keeps an integer exponent offset q and its sum of 2^(l*s - q) (one fma
+//    and one exp2 per logit); a vector's 8 terms are summed in binary32 and
+//    added to the lane's binary64 sum.  q is set at the lane's first finite
+//    logit and moves up (by an exact power-of-two rescale of the sum) only
+//    when a logit exceeds it by 32 octaves, so terms stay below 2^32; the
+//    lanes combine in binary64 in a fixed order.
+//    A NaN anywhere makes Z NaN; +inf makes it NaN or infinite.
 //  - with top-p: a count histogram of the kWin keys at and below the running
 //    maximum, in LDS, indexed by key mod kWin.  When the maximum rises, the
 //    bins of the keys that leave the window are cleared for the keys that
@@ -20,10 +26,11 @@
 //    the j smallest ids, profile order being logit desc, id asc).  A cut below
 //    the window leaves the row to the generic kernel.
 //  - the drafted token's rank among the tokens of its key with smaller ids (its
-//    key's bin just before its tile, plus the earlier tokens of that tile): it
-//    is in the support iff its key is above kc, or equal to kc with rank < j.
+//    key's bin just before its vector, plus the earlier tokens of that vector):
+//    it is in the support iff its key is above kc, or equal to kc with rank < j.
 // The cut is recorded as (kc, j); the sampling kernel turns j into a cut id
-// when it needs one.
+// when it needs one.  The argmax is not computed: no rule reads it for these
+// profiles (greedy and temperature-0 rows take the top-k kernel).
 #include "sv_kernels.hpp"
 #include "sv_stream.hpp"
 
@@ -35,7 +42,7 @@ using namespace stream;
 
 constexpr int kVec = 2;                  // 16-byte loads per lane per tile
 #ifndef SV_DENSE_NBUF
-#define SV_DENSE_NBUF 6
+#define SV_DENSE_NBUF 4
 #endif
 constexpr int kNBuf = SV_DENSE_NBUF;     // tiles in the load ring (kNBuf - 1 in flight)
 constexpr int kTile = kWave * kVec * 8;  // bf16 logits per tile
@@ -55,24 +62,28 @@ __device__ inline float value_of(int key) {
 }
 
 struct LaneSum {
-  float m;       // running maximum of this lane's logits (-inf: none finite yet)
-  double s;      // sum of 2^((l - m) * scale) over this lane's logits so far
-  float best;    // largest logit seen by this lane
-  int best_pos;  // window position of its first occurrence
+  float mv;  // this lane's largest logit so far (-inf: none finite yet)
+  float q;   // exponent offset: an integer, at most 32 below mv * s
+  float vt;  // logits above vt move q up (-inf until the first finite logit)
+  double s;  // sum of 2^(l * s - q) over this lane's logits so far
+  bool ovf;  // a logit too large for binary32 exponents: the row falls back
 };
 
 struct Hist {
-  uint32_t* bin;  // kWin counts, index = key mod kWin
-  int anchor;     // largest key seen (the window is [anchor - kWin + 1, anchor])
-  int kx;         // key of the drafted token (when it has one)
-  int rank_x;     // tokens with key kx and a smaller id
+  uint32_t* bin;    // kWin counts, index = key mod kWin
+  int anchor;       // largest key seen (the window is [anchor - kWin + 1, anchor])
+  float anchor_v;   // its value
+  float lo_v;       // value of the window's lowest key (never -inf)
+  int kx;           // key of the drafted token (when it has one)
+  int rank_x;       // tokens with key kx and a smaller id
 };
 
-// One 16-byte vector (8 logits) of a tile: binary32 values, the lane's maximum,
-// argmax, running sum, then (top-p rows) the histogram window and the drafted
-// token's rank.  p0 is the window position of the vector's first logit.
+// One 16-byte vector (8 logits) of a tile: the lane's maximum and running sum,
+// then (top-p rows) the histogram window and the drafted token's rank.  p0 is
+// the window position of the vector's first logit; xvec says (wave-uniform)
+// whether the drafted token lies in this vector of the wave.
 __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v, int p0, int px,
-                                 float scale_f, double scale) {
+                                 bool xvec, float scale_f, double scale) {
   float f[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -83,42 +94,36 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v
   float lmv = f[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
-
-  if (lmv > L.best) {  // a new lane maximum: its first position in the vector
-    int e0 = 7;
-#pragma unroll
-    for (int e = 7; e >= 0; --e)
-      if (f[e] == lmv) e0 = e;
-    L.best = lmv;
-    L.best_pos = p0 + e0;
+  L.mv = fmaxf(L.mv, lmv);
+  if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or 32 octaves up
+    const float qn = ceilf(lmv * scale_f);
+    L.ovf |= !(qn < 0x1p22f);
+    // a power-of-two rescale is exact; NaN from earlier logits stays NaN
+    L.s = L.vt == -__builtin_huge_valf() ? (L.s != L.s ? L.s : 0.0) : ldexp(L.s, (int)(L.q - qn));
+    L.q = qn;
+    L.vt = (qn + 32.0f) / scale_f;
   }
-  if (lmv > L.m) {
-    L.s = L.m == -__builtin_huge_valf() ? 0.0 : L.s * exp2(((double)L.m - (double)lmv) * scale);
-    L.m = lmv;
-  }
-  // a lane without a finite logit so far only holds -inf (weight 0) or NaN
-  const float mm = L.m == -__builtin_huge_valf() ? 0.0f : L.m;
   float ts = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ts += __builtin_amdgcn_exp2f((f[e] - mm) * scale_f);
+  for (int e = 0; e < 8; ++e) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], scale_f, -L.q));
   L.s += (double)ts;
 
   if (!top_p) return;
-  // window anchor: the largest key so far (wave-uniform)
-  int tk = skey_of(lmv);
+  if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
+    int tk = skey_of(lmv);
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
-  if (tk > H.anchor) {
+    for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
     const int lane = __lane_id();
     const int d = tk - H.anchor;  // keys anchor+1 .. tk take the bins of the keys leaving
     for (int i = lane; i < kWin; i += kWave)
       if (d >= kWin || ((i - (H.anchor + 1)) & (kWin - 1)) < d) H.bin[i] = 0u;
     H.anchor = tk;
+    H.anchor_v = value_of(tk);
+    H.lo_v = value_of(max(tk - (kWin - 1), kNegInfKey + 1));
   }
   const int lo = H.anchor - (kWin - 1);
-  // the drafted token's rank: tokens of its key counted before this vector of
-  // the tile, plus the tokens of this vector (in every lane) at smaller ids
-  if (__ballot(px >= p0 && px < p0 + 8)) {
+  if (xvec) {  // the drafted token's rank: its key's bin before this vector, plus
+               // this vector's tokens (in every lane) of that key at smaller ids
     int before = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) before += (p0 + e < px && skey_of(f[e]) == H.kx) ? 1 : 0;
@@ -126,15 +131,19 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v
     for (int off = kWave / 2; off > 0; off >>= 1) before += __shfl_xor(before, off, kWave);
     H.rank_x = (H.kx >= lo ? (int)H.bin[H.kx & (kWin - 1)] : 0) + before;
   }
+  if (lo > 0) {  // a window of positive keys: the key is the upper half of the bits
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int k = skey_of(f[e]);
-    if (k >= lo && k > kNegInfKey) atomicAdd(&H.bin[k & (kWin - 1)], 1u);
+    for (int e = 0; e < 8; ++e)
+      if (f[e] >= H.lo_v) atomicAdd(&H.bin[(__float_as_uint(f[e]) >> 16) & (kWin - 1)], 1u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (f[e] >= H.lo_v) atomicAdd(&H.bin[skey_of(f[e]) & (kWin - 1)], 1u);
   }
 }
 
 #ifndef SV_DENSE_WAVES_PER_EU
-#define SV_DENSE_WAVES_PER_EU 4
+#define SV_DENSE_WAVES_PER_EU 5
 #endif
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_WAVES_PER_EU))) void k_rows_dense(
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft,
@@ -159,8 +168,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_
                                   : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
   const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
   const bool top_p = smp.top_p_milli < 1000;
-  const double scale = 1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli;
-  const float scale_f = (float)scale;
+  // the row's scale: log2(e) / T rounded to binary32, used everywhere below
+  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
+  const double scale = (double)scale_f;
   RowRec* rec = rows + (size_t)slot_g;
 
   // 16-byte aligned window over the row: positions [head, head + V) are the row
@@ -171,9 +181,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_
   const int ntiles = (npos + kTile - 1) / kTile;
   const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
 
-  LaneSum L{-__builtin_huge_valf(), 0.0, -__builtin_huge_valf(), 0x7FFFFFFF};
-  Hist H{bins, -0x10000, x >= 0 ? skey_of(xval) : 0, 0};
+  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
+  Hist H{bins, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), x >= 0 ? skey_of(xval) : 0, 0};
   const int px = x >= 0 ? x + head : -1;
+  const int xv = px >= 0 ? px / (kWave * 8) : -1;  // the drafted token's vector index in the row
 
   u32x4 ring[kNBuf][kVec];
 #pragma unroll
@@ -191,31 +202,37 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_
       if ((tt == 0 && head > 0) || (tt + 1) * kTile > npos) mask_tile<kVec>(ring[u], tt, head, npos);
 #pragma unroll
       for (int j = 0; j < kVec; ++j)
-        dense_vec(L, H, top_p, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px, scale_f, scale);
+        dense_vec(L, H, top_p, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
+                  tt * kVec + j == xv, scale_f, scale);
     }
   }
 
-  // lanes combined in a fixed order: maximum, Z, argmax
-  float lmax = L.m;
+  // lanes combined in a fixed order: maximum and Z (relative to lmax * s)
+  float lmax = L.mv;
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, kWave));
-  double z = L.m == -__builtin_huge_valf() ? (L.s != L.s ? L.s : 0.0)
-                                            : L.s * exp2(((double)L.m - (double)lmax) * scale);
+  const double ref = (double)lmax * scale;  // exact: both factors are binary32
+  double z = L.vt == -__builtin_huge_valf() ? L.s : L.s * exp2((double)L.q - ref);
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
-  int bpos = L.best == lmax ? L.best_pos : 0x7FFFFFFF;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) bpos = min(bpos, __shfl_xor(bpos, off, kWave));
+  if (__ballot(L.ovf)) {  // logits beyond binary32 exponent range: the generic kernel
+    if (lane == 0) {
+      RowRec fb{};
+      fb.status = kRowFallback;
+      *rec = fb;
+    }
+    return;
+  }
 
   RowRec rr{};
-  rr.argmax = bpos - head;
+  rr.argmax = -1;
   rr.lmax = lmax;
   rr.scale = scale;
   rr.ptok = -1.0;
-  const bool bad = !(z == z) || lmax == __builtin_huge_valf() || lmax == -__builtin_huge_valf();
+  const bool bad = !(z == z) || z == __builtin_huge_val() || lmax == __builtin_huge_valf() ||
+                   lmax == -__builtin_huge_valf();
   if (bad) {
     rr.status = SV_S_BAD_LOGITS;
-    rr.argmax = 0;
     rr.zsum = 1.0;
     if (lane == 0) *rec = rr;
     return;
