@@ -58,6 +58,7 @@ struct Bf16 {
   static constexpr uint32_t kInfKey = 0x8000u + 0x7F80u;  // key(+inf)
   static constexpr uint32_t kNegInfKey = 0x8000u - 0x7F80u;  // key(-inf)
   static constexpr int kKeyBits = 16;
+  static constexpr uint32_t kNegInfBits = 0xFF80u;
   __device__ static inline uint32_t bits(elem_t e) { return e; }
   __device__ static inline float value(uint32_t u) { return __uint_as_float(u << 16); }
   __device__ static inline uint32_t key(uint32_t u) {
@@ -76,6 +77,7 @@ struct F32 {
   static constexpr uint32_t kInfKey = 0x80000000u + 0x7F800000u;
   static constexpr uint32_t kNegInfKey = 0x80000000u - 0x7F800000u;
   static constexpr int kKeyBits = 32;
+  static constexpr uint32_t kNegInfBits = 0xFF800000u;
   __device__ static inline uint32_t bits(elem_t e) { return e; }
   __device__ static inline float value(uint32_t u) { return __uint_as_float(u); }
   __device__ static inline uint32_t key(uint32_t u) {

@@ -189,36 +189,65 @@ __global__ __launch_bounds__(kWave) void k_finalize(
   }
 }
 
-constexpr int kSampleNT = 256;
-constexpr int kSampleE = 8;  // consecutive tokens per thread per chunk
+constexpr int kSampleNT = 1024;                  // threads per session
+constexpr int kSampleE = 4;                      // consecutive tokens per thread per group
+constexpr int kGroup = kSampleNT * kSampleE;     // ids per group
+constexpr int kMaxChunks = kSampleNT;            // chunks of whole groups, one per thread
+constexpr int kLut = 2048;                       // probabilities tabled per row (by key)
 
+// One row's profile as the sampler sees it: p(y) = w(y) / Z' on the support.
+// A row whose cut is recorded as (kcut, ntie) keeps the ntie smallest ids among
+// the tokens of key kcut; the sampler counts those ties in id order.  The
+// probabilities of the kLut keys below the row's largest key are tabled in
+// LDS (a top-p support lies there); other keys evaluate the weight.
 template <class Tr>
 struct SampleRow {
   const typename Tr::elem_t* row;
   RowRec r;
-  __device__ double prob(int y) const {
-    const uint32_t u = Tr::bits(row[y]);
+  uint32_t ktop;      // key of the row's largest logit
+  const double* lut;  // lut[ktop - k] = p of key k, for ktop - kLut < k <= ktop
+  __device__ bool tie_mode() const { return r.idcut < 0; }
+  // probability of token y with bits u; rank = ties of key kcut before y (tie mode)
+  __device__ double prob(int y, uint32_t u, int rank) const {
     const uint32_t k = Tr::key(u);
-    const bool member = k > r.kcut || (k == r.kcut && y <= r.idcut);
-    return member ? weight64(Tr::value(u), r.lmax, r.scale) / r.zsum : 0.0;
+    const bool member = k > r.kcut || (k == r.kcut && (r.idcut >= 0 ? y <= r.idcut : rank < r.ntie));
+    if (!member) return 0.0;
+    if (ktop - k < (uint32_t)kLut) return lut[ktop - k];
+    return weight64(Tr::value(u), r.lmax, r.scale) / r.zsum;
   }
 };
 
-// Inclusive-to-exclusive block scan of binary64 values (fixed order).
-__device__ double block_exclusive_scan(double v, double* wsum, double* total) {
+// Fill a row's table: p of the keys ktop, ktop - 1, ... (keys at or below
+// -inf get 0).  Entries are the same expression the direct path evaluates.
+template <class Tr>
+__device__ void fill_lut(SampleRow<Tr>& S, double* lut) {
+  S.ktop = Tr::key(__float_as_uint(S.r.lmax) >> (32 - Tr::kKeyBits));
+  S.lut = lut;
+  for (int i = threadIdx.x; i < kLut; i += blockDim.x) {
+    const long k = (long)S.ktop - i;
+    double p = 0.0;
+    if (k > (long)Tr::kNegInfKey)
+      p = weight64(Tr::value(Tr::unkey((uint32_t)k)), S.r.lmax, S.r.scale) / S.r.zsum;
+    lut[i] = p;
+  }
+}
+
+// Block-wide exclusive scan in thread order (fixed combination order).
+template <typename T>
+__device__ T block_exclusive_scan(T v, T* wsum, T* total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  double inc = v;
+  T inc = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(inc, off, kWave);
+    const T t = __shfl_up(inc, off, kWave);
     if (lane >= off) inc += t;
   }
-  double exc = __shfl_up(inc, 1, kWave);
-  if (lane == 0) exc = 0.0;
+  T exc = __shfl_up(inc, 1, kWave);
+  if (lane == 0) exc = T(0);
   __syncthreads();
   if (lane == kWave - 1) wsum[wid] = inc;
   __syncthreads();
-  double base = 0.0, tot = 0.0;
+  T base = T(0), tot = T(0);
 #pragma unroll
   for (int w = 0; w < kSampleNT / kWave; ++w) {
     if (w < wid) base += wsum[w];
@@ -228,121 +257,168 @@ __device__ double block_exclusive_scan(double v, double* wsum, double* total) {
   return base + exc;
 }
 
-// A row that records its cut as (kcut, ntie) keeps the ntie smallest ids among
-// the tokens with key kcut: the id of the ntie-th of them, found by counting
-// in id order (chunks of kSampleNT * kSampleE ids, block scans of the counts).
+struct SampleSmem {
+  double lut_p[kLut];             // p of the keys below p's largest key
+  double lut_q[kLut];             // q of the keys below q's largest key
+  double chunk_mass[kMaxChunks];  // mass of each chunk
+  uint32_t ties_p[kMaxChunks];    // ties of p's cut key before each chunk
+  uint32_t ties_q[kMaxChunks];    // ties of q's cut key before each chunk
+  double dsum[kSampleNT / kWave];
+  uint32_t usum[kSampleNT / kWave];
+  int32_t ired[kSampleNT / kWave];
+  double base;
+};
+
+// Weights of this thread's kSampleE tokens of a group (ids y0 ..): the residual
+// max(0, p - q) or p.  tp, tq: ties of each row's cut key before the group;
+// on return they count the group's ties too.
 template <class Tr>
-__device__ int32_t resolve_idcut(const typename Tr::elem_t* row, int V, uint32_t kcut, int ntie,
-                                 double* wsum, int32_t* ired) {
-  double running = 0.0;
-  for (int c0 = 0; c0 < V; c0 += kSampleNT * kSampleE) {
-    const int y0 = c0 + threadIdx.x * kSampleE;
-    int cnt = 0;
+__device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bool resid, bool ties,
+                              int y0, int V, uint32_t& tp, uint32_t& tq, double (&w)[kSampleE],
+                              SampleSmem& sm) {
+  uint32_t up[kSampleE], uq[kSampleE];
 #pragma unroll
-    for (int e = 0; e < kSampleE; ++e)
-      cnt += (y0 + e < V && Tr::key(Tr::bits(row[y0 + e])) == kcut) ? 1 : 0;
-    double total;
-    const double before = running + block_exclusive_scan((double)cnt, wsum, &total);
-    int32_t mine = 0x7FFFFFFF;
-    if (before < ntie && before + cnt >= ntie) {
-      int seen = (int)before;
-      for (int e = 0; e < kSampleE; ++e) {
-        if (y0 + e < V && Tr::key(Tr::bits(row[y0 + e])) == kcut && ++seen == ntie) {
-          mine = y0 + e;
-          break;
-        }
-      }
-    }
-    const int32_t first = block_reduce<kSampleNT>(mine, OpMin(), ired);
-    if (first != 0x7FFFFFFF) return first;
-    running += total;
+  for (int e = 0; e < kSampleE; ++e) {
+    const bool in = y0 + e < V;
+    up[e] = in ? Tr::bits(P.row[y0 + e]) : Tr::kNegInfBits;
+    uq[e] = (in && resid) ? Tr::bits(Q.row[y0 + e]) : Tr::kNegInfBits;
   }
-  return 0x7FFFFFFF;  // fewer ties than ntie: keep them all
+  int rp[kSampleE], rq[kSampleE];
+#pragma unroll
+  for (int e = 0; e < kSampleE; ++e) rp[e] = rq[e] = 0;
+  if (ties) {  // ranks among the cut keys' ties, in id order (group counts < 2^16)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < kSampleE; ++e) {
+      mine += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1u : 0u;
+      mine += (resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 0x10000u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan<uint32_t>(mine, sm.usum, &tot);
+    int cp = (int)(tp + (before & 0xFFFFu)), cq = (int)(tq + (before >> 16));
+#pragma unroll
+    for (int e = 0; e < kSampleE; ++e) {
+      rp[e] = cp;
+      rq[e] = cq;
+      cp += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1 : 0;
+      cq += (resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 1 : 0;
+    }
+    tp += tot & 0xFFFFu;
+    tq += tot >> 16;
+  }
+#pragma unroll
+  for (int e = 0; e < kSampleE; ++e) {
+    const double p = P.prob(y0 + e, up[e], rp[e]);
+    if (!resid) {
+      w[e] = p;
+    } else {
+      const double d = p - Q.prob(y0 + e, uq[e], rq[e]);
+      w[e] = d > 0.0 ? d : 0.0;
+    }
+  }
 }
 
 // Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2: additional token from
 // norm(max(0, p_j - q_j)) at the first rejection j, or from p_{m+1}; the
-// smallest id whose running mass exceeds u * S.
+// smallest id whose running mass exceeds u * S.  One workgroup per session.
+// One pass in id order records the mass of each chunk (a run of whole groups
+// of kGroup ids) and the cut keys' tie counts before it; a scan over the
+// chunk masses finds the chunk holding u * S, and from there the groups are
+// weighed again until the token is found.
 template <class Tr>
 __global__ __launch_bounds__(kSampleNT) void k_sample(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
     int B, int M, int V, const RowRec* __restrict__ rows, const Job* __restrict__ jobs,
     int32_t* __restrict__ out_tokens) {
-  __shared__ double wsum[kSampleNT / kWave];
-  __shared__ double red[kSampleNT / kWave];
-  __shared__ int32_t ired[kSampleNT / kWave];
+  __shared__ SampleSmem sm;
   const int b = blockIdx.x;
   if (b >= B) return;
   const Job job = jobs[b];
   if (job.kind == kJobNone) return;
   const int R = 2 * M + 1;
-  SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow]};
-  SampleRow<Tr> Q{P.row, P.r};
+  SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow],
+                  0, nullptr};
+  SampleRow<Tr> Q = P;
   bool resid = job.kind == kJobResidual;
   if (resid) Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
-                               rows[(size_t)b * R + M + 1 + job.drow]};
-  if (P.r.idcut < 0) P.r.idcut = resolve_idcut<Tr>(P.row, V, P.r.kcut, P.r.ntie, wsum, ired);
-  if (resid && Q.r.idcut < 0) Q.r.idcut = resolve_idcut<Tr>(Q.row, V, Q.r.kcut, Q.r.ntie, wsum, ired);
+                               rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
+  fill_lut<Tr>(P, sm.lut_p);
+  fill_lut<Tr>(Q, sm.lut_q);
+  __syncthreads();
+  const int ngroups = (V + kGroup - 1) / kGroup;
+  const int G = (ngroups + kMaxChunks - 1) / kMaxChunks;  // groups per chunk
+  const int nchunks = (ngroups + G - 1) / G;
 
-  auto weight = [&](int y) -> double {
-    const double p = P.prob(y);
-    if (!resid) return p;
-    const double d = p - Q.prob(y);
-    return d > 0.0 ? d : 0.0;
-  };
-
-  // pass 1: total mass S and the last id with mass
-  double S = 0.0;
+  // the pass: every chunk's mass in id order, and the last id with mass
   int32_t last = -1;
-  for (int y = threadIdx.x; y < V; y += kSampleNT) {
-    const double w = weight(y);
-    S += w;
-    if (w > 0.0) last = y;
-  }
-  S = block_reduce<kSampleNT>(S, OpAdd(), red);
-  last = block_reduce<kSampleNT>(last, OpMax(), ired);
-  if (resid && S == 0.0) {  // residual without mass (rounding only): draw from p
-    resid = false;
-    S = 0.0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool ties = P.tie_mode() || (resid && Q.tie_mode());
+    uint32_t tp = 0, tq = 0;
     last = -1;
-    for (int y = threadIdx.x; y < V; y += kSampleNT) {
-      const double w = weight(y);
-      S += w;
-      if (w > 0.0) last = y;
+    for (int c = 0; c < nchunks; ++c) {
+      if (threadIdx.x == 0) {
+        sm.ties_p[c] = tp;
+        sm.ties_q[c] = tq;
+      }
+      double sw = 0.0;
+      for (int g = c * G; g < min((c + 1) * G, ngroups); ++g) {
+        const int y0 = g * kGroup + threadIdx.x * kSampleE;
+        double w[kSampleE];
+        group_weights<Tr>(P, Q, resid, ties, y0, V, tp, tq, w, sm);
+#pragma unroll
+        for (int e = 0; e < kSampleE; ++e) {
+          sw += w[e];
+          if (w[e] > 0.0) last = y0 + e;
+        }
+      }
+      const double cm = block_reduce<kSampleNT>(sw, OpAdd(), sm.dsum);
+      if (threadIdx.x == 0) sm.chunk_mass[c] = cm;
     }
-    S = block_reduce<kSampleNT>(S, OpAdd(), red);
-    last = block_reduce<kSampleNT>(last, OpMax(), ired);
+    last = block_reduce<kSampleNT>(last, OpMax(), sm.ired);
+    if (!resid || last >= 0) break;
+    resid = false;  // residual without mass (rounding only): draw from p
   }
-  const double tgt = job.u * S;
 
-  // pass 2: chunks of kSampleNT * kSampleE ids in order
-  double running = 0.0;
-  int32_t pick = -1;
-  for (int c0 = 0; c0 < V && pick < 0; c0 += kSampleNT * kSampleE) {
-    const int y0 = c0 + threadIdx.x * kSampleE;
-    double w[kSampleE];
-    double s = 0.0;
+  // prefix over the chunk masses: thread c holds chunk c
+  __syncthreads();
+  const double cm = (int)threadIdx.x < nchunks ? sm.chunk_mass[threadIdx.x] : 0.0;
+  double S;
+  const double before = block_exclusive_scan<double>(cm, sm.dsum, &S);
+  const double tgt = job.u * S;
+  const int32_t mine_c = ((int)threadIdx.x < nchunks && before + cm > tgt) ? (int32_t)threadIdx.x : 0x7FFFFFFF;
+  const int32_t cstar = block_reduce<kSampleNT>(mine_c, OpMin(), sm.ired);
+  int32_t pick = last;
+  if (cstar != 0x7FFFFFFF) {
+    __syncthreads();
+    if ((int)threadIdx.x == cstar) sm.base = before;
+    __syncthreads();
+    double run = sm.base;
+    const bool ties = P.tie_mode() || (resid && Q.tie_mode());
+    uint32_t tp = sm.ties_p[cstar], tq = sm.ties_q[cstar];
+    // the chunk holding u * S; rounding may move the point into a later chunk
+    for (int g = cstar * G; g < ngroups; ++g) {
+      const int y0 = g * kGroup + threadIdx.x * kSampleE;
+      double w[kSampleE];
+      group_weights<Tr>(P, Q, resid, ties, y0, V, tp, tq, w, sm);
+      double sw = 0.0;
 #pragma unroll
-    for (int e = 0; e < kSampleE; ++e) {
-      w[e] = (y0 + e < V) ? weight(y0 + e) : 0.0;
-      s += w[e];
-    }
-    double total;
-    const double base = running + block_exclusive_scan(s, wsum, &total);
-    double acc = base;
-    int32_t mine = -1;
+      for (int e = 0; e < kSampleE; ++e) sw += w[e];
+      double gtot;
+      double a = run + block_exclusive_scan<double>(sw, sm.dsum, &gtot);
+      int32_t mine = 0x7FFFFFFF;
 #pragma unroll
-    for (int e = 0; e < kSampleE; ++e) {
-      acc += w[e];
-      if (mine < 0 && acc > tgt) mine = y0 + e;
+      for (int e = 0; e < kSampleE; ++e) {
+        a += w[e];
+        if (mine == 0x7FFFFFFF && a > tgt) mine = y0 + e;
+      }
+      const int32_t first = block_reduce<kSampleNT>(mine, OpMin(), sm.ired);
+      if (first != 0x7FFFFFFF) {
+        pick = first;
+        break;
+      }
+      run += gtot;
     }
-    // the first thread (in id order) whose running mass passes the target
-    const int32_t cand = mine >= 0 ? mine : 0x7FFFFFFF;
-    const int32_t first = block_reduce<kSampleNT>(cand, OpMin(), ired);
-    if (first != 0x7FFFFFFF) pick = first;
-    running += total;
   }
-  if (pick < 0) pick = last;
   if (threadIdx.x == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = pick;
 }
 
