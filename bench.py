@@ -34,10 +34,10 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "topk-ring6-prio"
+KERNEL_REVISION = "topk-ring6-prio-bound4"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
-    ("b256_topk_topp", "k_rows_topk", "topk-ring6-prio"): 1_119_484_928,
+    ("b256_topk_topp", "k_rows_topk", "topk-ring6-prio-bound4"): 1_119_558_656,
 }
 
 

@@ -12,15 +12,16 @@
 // order of the 48-bit composite  (key + 0x8000) << 32 | ~id  (larger first).
 // Positions outside the row (alignment head, tail of the last tile) are read
 // as -inf, and -inf never enters the candidates (it has probability zero).
-// Raw mode: when the first tile already shows k lanes holding a positive
-// logit, every token of the support is positive, and for positive values the
-// raw bf16 bits read as a signed 16-bit integer equal the key (negative values
-// read as negative integers and never pass a positive threshold).  Such rows
-// skip the key transform after their first tile.
+// Raw mode: when the first tiles already show k (lane, tile) maxima holding a
+// positive logit, every token of the support is positive, and for positive
+// values the raw bf16 bits read as a signed 16-bit integer equal the key
+// (negative values read as negative integers and never pass a positive
+// threshold).  Such rows skip the key transform.
 //
 // Candidate filter: a wave keeps, in its own LDS region, a superset of the k
-// best (key, id) pairs seen so far.  On the first tile the k-th largest lane
-// maximum bounds the k-th best key from below, so keys below it never enter.
+// best (key, id) pairs seen so far.  Before the first tile is processed, the
+// k-th largest of the lane maxima of the first four tiles (all in the load
+// ring) bounds the k-th best key from below, so keys below it never enter.
 // Before a tile that could overflow the region, the region is cut to exactly
 // its k best and the threshold rises to the k-th best key; from then on a
 // token must beat that key strictly (later tiles hold larger ids, which lose
@@ -51,6 +52,11 @@ constexpr int kCap = 256;                  // candidate entries per wave
 #endif
 constexpr int kWavesPerBlock = SV_TOPK_WPB;  // independent rows per workgroup
 constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
+#ifndef SV_TOPK_BOUND_TILES
+#define SV_TOPK_BOUND_TILES 4
+#endif
+constexpr int kBoundTiles = SV_TOPK_BOUND_TILES;  // tiles behind the first bound
+static_assert(kBoundTiles <= kNBuf - 1, "the first bound's tiles are all in the ring");
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
@@ -179,15 +185,38 @@ __device__ inline int slots_ge(const u32x4 (&v)[kVec], int te) {
   return n;
 }
 
-// k-th largest of the 64 lane values (k <= 64), as a signed 16-bit key
-__device__ inline int wave_kth_largest(int v, int k) {
+// k-th largest of the N * 64 values held N per lane (k <= 64), as a signed
+// 16-bit key
+template <int N>
+__device__ inline int wave_kth_largest_n(const int (&v)[N], int k) {
   uint32_t t = 0;
-  const uint32_t b = (uint32_t)(v + 0x8000);
   for (int bit = 15; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
-    if (popc64(__ballot(b >= cand)) >= k) t = cand;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) cnt += popc64(__ballot((uint32_t)(v[i] + 0x8000) >= cand));
+    if (cnt >= k) t = cand;
   }
   return (int)t - 0x8000;
+}
+
+// lane maxima of one tile without changing it: raw bits as signed 16-bit
+// integers, and keys
+__device__ inline int lane_max_raw(const u32x4 (&v)[kVec]) {
+  uint32_t m = 0x80008000u;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m = max_i16x2(m, elem(v[j], d));
+  return max(lo16(m), hi16(m));
+}
+__device__ inline int lane_max_key(const u32x4 (&v)[kVec]) {
+  uint32_t m = 0x80008000u;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) m = max_i16x2(m, key_pair(elem(v[j], d)));
+  return max(lo16(m), hi16(m));
 }
 
 struct WaveState {
@@ -210,14 +239,7 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
   const int lane = __lane_id();
   if ((tile == 0 && head > 0) || (tile + 1) * kTile > head + V) mask_tile<kVec>(v, tile, head, head + V);
   int lm;
-  if (tile == 0) {
-    uint32_t u0 = 0;
-    const int lm_raw = tile_raw(v, u0);
-    lm = tile_keys(v, s.magmax);
-    const int t_raw = wave_kth_largest(lm_raw, k);
-    s.raw = t_raw > 0;
-    s.thr = s.raw ? t_raw : wave_kth_largest(lm, k);
-  } else if (s.raw) {
+  if (s.raw) {
     lm = tile_raw(v, s.umax);
   } else {
     lm = tile_keys(v, s.magmax);
@@ -447,6 +469,26 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
   for (int u = 0; u < kNBuf - 1; ++u) {
     load_tile<kVec>(ring[u], vbase, u, nvec - 1);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  // the first bound: among the first kBoundTiles tiles, the k-th largest of
+  // their lane maxima (k distinct tokens reach it, so the row's k-th best key
+  // is at least that); raw mode when it is positive in raw bits
+  {
+#pragma unroll
+    for (int u = 0; u < kBoundTiles; ++u)
+      if ((u == 0 && head > 0) || (u + 1) * kTile > head + V) mask_tile<kVec>(ring[u], u, head, head + V);
+    int lmv[kBoundTiles];
+#pragma unroll
+    for (int u = 0; u < kBoundTiles; ++u) lmv[u] = lane_max_raw(ring[u]);
+    const int t_raw = wave_kth_largest_n<kBoundTiles>(lmv, k);
+    s.raw = t_raw > 0;
+    if (s.raw) {
+      s.thr = t_raw;
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBoundTiles; ++u) lmv[u] = lane_max_key(ring[u]);
+      s.thr = wave_kth_largest_n<kBoundTiles>(lmv, k);
+    }
   }
   const int nround = (ntiles + kNBuf - 1) / kNBuf;
   for (int r = 0; r < nround && !s.overflow; ++r) {
