@@ -4,7 +4,7 @@
 // workspace and enqueues the kernels on the caller's stream:
 //   validate -> row profiles (single-pass top-k kernel, one-pass dense
 //   kernel, then the generic kernel for every other row) -> finalize
-//   (acceptance) -> sample.
+//   (acceptance, and the additional token's draw).
 // It never synchronises and never allocates.
 #include <limits.h>
 
@@ -22,8 +22,6 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + (size_t)B * (2 * (size_t)M + 1) * sizeof(RowRec), 256);
   L.status_off = off;
   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
-  L.jobs_off = off;
-  off = align_up(off + (size_t)B * sizeof(Job), 256);
   const size_t slots = (size_t)B * (2 * (size_t)M + 1);
   L.supid_off = off;
   off = align_up(off + slots * kSupMax * sizeof(int32_t), 256);
@@ -84,7 +82,6 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   char* ws = (char*)workspace;
   a.rows = (sv::RowRec*)(ws + L.rows_off);
   a.sess_status = (int32_t*)(ws + L.status_off);
-  a.jobs = (sv::Job*)(ws + L.jobs_off);
   a.sup_id = (int32_t*)(ws + L.supid_off);
   a.sup_p = (double*)(ws + L.supp_off);
 
@@ -98,7 +95,6 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   sv::launch_rows_generic(a, st);
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
   sv::launch_finalize(a, st);
-  sv::launch_sample(a, st);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
   return SV_OK;
 }

@@ -39,7 +39,7 @@ struct RowRec {
 };
 static_assert(sizeof(RowRec) == 56, "RowRec layout");
 
-// Per-session draw left for the sampling kernel.
+// Per-session draw left for the whole workgroup after the acceptance wave.
 enum JobKind : int32_t { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };
 struct Job {
   int32_t kind;

@@ -24,7 +24,6 @@ struct LaunchArgs {
   // workspace carve-up
   RowRec* rows;         // [B, 2M+1]: target rows 1..M+1, then draft rows 1..M
   int32_t* sess_status; // [B]
-  Job* jobs;            // [B]
   int32_t* sup_id;      // [B, 2M+1, kSupMax] listed supports (ids ascending)
   double* sup_p;        // [B, 2M+1, kSupMax] their probabilities
 };
@@ -52,7 +51,7 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
 }
 
 struct WorkspaceLayout {
-  size_t rows_off, status_off, jobs_off, supid_off, supp_off, total;
+  size_t rows_off, status_off, supid_off, supp_off, total;
 };
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
@@ -62,6 +61,5 @@ void launch_rows_topk(const LaunchArgs& a, hipStream_t st);
 void launch_rows_dense(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
-void launch_sample(const LaunchArgs& a, hipStream_t st);
 
 }  // namespace sv

@@ -11,6 +11,8 @@
 //          1000 * (mass(key > kp) + c * w(kp)) >= P * Z_k;
 //   the c-th smallest id among the ties is the cut id, by a bitwise search.
 // Masses are binary64 sums of binary64 weights.
+#include <algorithm>
+
 #include "sv_kernels.hpp"
 
 namespace sv {
@@ -195,6 +197,32 @@ __device__ void profile_generic(const typename Tr::elem_t* row, int V, const sv_
   if (threadIdx.x == 0) *rec = r;
 }
 
+// Does row slot slot_g need this kernel?  Rows of the other row kernels only
+// when they handed the row back.
+template <class Tr>
+__device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
+                            const sv_sampling* sampling, const int32_t* sess_status, int M, int V,
+                            const RowRec* rows) {
+  const int R = 2 * M + 1;
+  const int b = slot_g / R;
+  const int slot = slot_g - b * R;
+  if (sess_status[b] != 0) return false;
+  const int mb = m[b];
+  const int rl = rule[b];
+  const bool is_target = slot <= M;
+  const int i = is_target ? slot + 1 : slot - M;  // 1-based position
+  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return false;
+  const sv_sampling smp = sampling[b];
+  if (row_uses_topk_kernel(Tr::kDtype, rl, smp) || row_uses_dense_kernel(Tr::kDtype, rl, smp, V))
+    return rows[slot_g].status == kRowFallback;
+  return true;
+}
+
+// A grid of at most kMaxBlocks workgroups scans the row slots: each workgroup
+// takes an equal share of consecutive slots, kNT at a time; each thread checks
+// one slot, the slots that need this kernel are listed in LDS, and the
+// workgroup profiles them one after another.
+constexpr int kMaxBlocks = 1024;
 template <class Tr>
 __global__ __launch_bounds__(kNT) void k_rows_generic(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
@@ -202,31 +230,53 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
     const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows) {
   __shared__ Smem sm;
+  __shared__ int32_t todo[kNT];
+  __shared__ int32_t wave_cnt[kNT / kWave];
   const int R = 2 * M + 1;
-  const int b = blockIdx.x / R;
-  const int slot = blockIdx.x - b * R;
-  if (b >= B || sess_status[b] != 0) return;
-  const int mb = m[b];
-  const int rl = rule[b];
-  const bool is_target = slot <= M;
-  const int i = is_target ? slot + 1 : slot - M;  // 1-based position
-  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
-  const sv_sampling smp = sampling[b];
-  RowRec* rec = rows + (size_t)b * R + slot;
-  if ((row_uses_topk_kernel(Tr::kDtype, rl, smp) || row_uses_dense_kernel(Tr::kDtype, rl, smp, V)) &&
-      rec->status != kRowFallback)
-    return;
-  const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
-  const typename Tr::elem_t* row =
-      is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
-                : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
-  profile_generic<Tr>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, &sm);
+  const int slots = B * R;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  // this workgroup's slots: an equal share, so that few rows spread over many groups
+  const int per = (slots + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int end = min(slots, ((int)blockIdx.x + 1) * per);
+  for (int base = (int)blockIdx.x * per; base < end; base += kNT) {
+    const int slot_g = base + (int)threadIdx.x;
+    const bool need = slot_g < end &&
+                      generic_row<Tr>(slot_g, m, rule, sampling, sess_status, M, V, rows);
+    const uint64_t mask = __ballot(need);
+    __syncthreads();  // the previous round's list is consumed
+    if (lane == 0) wave_cnt[wid] = __builtin_popcountll(mask);
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kNT / kWave; ++w) {
+      before += w < wid ? wave_cnt[w] : 0;
+      total += wave_cnt[w];
+    }
+    if (need)
+      todo[before + __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0))] = slot_g;
+    __syncthreads();
+    for (int t = 0; t < total; ++t) {
+      const int sg = todo[t];
+      const int b = sg / R;
+      const int slot = sg - b * R;
+      const bool is_target = slot <= M;
+      const int i = is_target ? slot + 1 : slot - M;
+      const int mb = m[b];
+      const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
+      const typename Tr::elem_t* row =
+          is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
+                    : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
+      profile_generic<Tr>(row, V, sampling[b], rule[b] == SV_RULE_GREEDY, x, rows + sg, &sm);
+    }
+  }
 }
 
 }  // namespace
 
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)a.B * (2 * a.M + 1));
+  const size_t slots = (size_t)a.B * (2 * a.M + 1);
+  const unsigned grid = (unsigned)std::min<size_t>(slots, kMaxBlocks);
   if (a.dtype == SV_BF16) {
     hipLaunchKernelGGL(k_rows_generic<Bf16>, dim3(grid), dim3(kNT), 0, st,
                        (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,

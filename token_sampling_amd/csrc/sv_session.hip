@@ -88,20 +88,20 @@ __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
   return __shfl(y, j, kWave);
 }
 
-// SDCP Sec. 6.4.  Lane i examines position i+1.
-__global__ __launch_bounds__(kWave) void k_finalize(
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
-    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M,
-    uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
-    const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
-    int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
-    Job* __restrict__ jobs, const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p) {
-  __shared__ int32_t q_id[kSupMax];
-  __shared__ double q_p[kSupMax];
-  const int b = blockIdx.x;
+// SDCP Sec. 6.4, for session b, by one wave: lane i examines position i+1.
+// Writes accepted_len, out_tokens and the probes; returns the draw left for
+// the whole workgroup (kJobNone when the extra token is already written).
+__device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
+                                const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
+                                const sv_sampling* __restrict__ sampling, int M, uint64_t seed,
+                                uint32_t round, const int32_t* __restrict__ sess_status,
+                                const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
+                                int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
+                                double* __restrict__ q_tok, const int32_t* __restrict__ sup_id,
+                                const double* __restrict__ sup_p, int32_t* q_id, double* q_p) {
   const int lane = threadIdx.x;
-  if (b >= B) return;
   const int R = 2 * M + 1;
+  Job job{kJobNone, 0, 0, 0, 0.0};
   const RowRec* rr = rows + (size_t)b * R;
   int32_t* out = out_tokens + (size_t)b * (M + 1);
   int st = sess_status[b];
@@ -127,16 +127,13 @@ __global__ __launch_bounds__(kWave) void k_finalize(
   }
 
   if (st < 0) {
-    if (lane == 0) {
-      accepted_len[b] = st;
-      jobs[b] = Job{kJobNone, 0, 0, 0, 0.0};
-    }
+    if (lane == 0) accepted_len[b] = st;
     for (int j = lane; j <= M; j += kWave) out[j] = -1;
     for (int j = lane; j < M; j += kWave) {
       if (p_tok) p_tok[(size_t)b * M + j] = -1.0;
       if (q_tok) q_tok[(size_t)b * M + j] = -1.0;
     }
-    return;
+    return job;
   }
 
   int a;
@@ -148,7 +145,6 @@ __global__ __launch_bounds__(kWave) void k_finalize(
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
     extra = rr[a].argmax;
-    if (lane == 0) jobs[b] = Job{kJobNone, a, 0, 0, 0.0};
   } else {
     // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i))
     double u_acc = 1.0, u_add = 0.0;
@@ -170,9 +166,8 @@ __global__ __launch_bounds__(kWave) void k_finalize(
                           Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
                           Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
                           Q ? Q->nsup : 0, ud, q_id, q_p);
-      if (lane == 0) jobs[b] = Job{kJobNone, a, 0, 0, 0.0};
-    } else if (lane == 0) {
-      jobs[b] = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
+    } else {
+      job = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
     }
   }
   if (lane == 0) accepted_len[b] = a;
@@ -187,6 +182,7 @@ __global__ __launch_bounds__(kWave) void k_finalize(
     if (p_tok) p_tok[(size_t)b * M + j] = have ? px : -1.0;
     if (q_tok) q_tok[(size_t)b * M + j] = have ? qx : -1.0;
   }
+  return job;
 }
 
 constexpr int kSampleNT = 1024;                  // threads per session
@@ -325,15 +321,31 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bo
 // of kGroup ids) and the cut keys' tie counts before it; a scan over the
 // chunk masses finds the chunk holding u * S, and from there the groups are
 // weighed again until the token is found.
+// One workgroup per session: its first wave takes the acceptance decisions
+// (finalize_session); a draw from rows without listed supports then takes
+// the whole workgroup.
 template <class Tr>
-__global__ __launch_bounds__(kSampleNT) void k_sample(
+__global__ __launch_bounds__(kSampleNT) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
-    int B, int M, int V, const RowRec* __restrict__ rows, const Job* __restrict__ jobs,
-    int32_t* __restrict__ out_tokens) {
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M, int V,
+    uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
+    const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
+    const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p) {
   __shared__ SampleSmem sm;
+  __shared__ int32_t q_id[kSupMax];
+  __shared__ double q_p[kSupMax];
+  __shared__ Job job_s;
   const int b = blockIdx.x;
   if (b >= B) return;
-  const Job job = jobs[b];
+  if (threadIdx.x < kWave) {
+    const Job j = finalize_session(b, tokens, m, rule, sampling, M, seed, round, sess_status, rows,
+                                   accepted_len, out_tokens, p_tok, q_tok, sup_id, sup_p, q_id, q_p);
+    if (threadIdx.x == 0) job_s = j;
+  }
+  __syncthreads();
+  const Job job = job_s;
   if (job.kind == kJobNone) return;
   const int R = 2 * M + 1;
   SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow],
@@ -430,20 +442,16 @@ void launch_validate(const LaunchArgs& a, hipStream_t st) {
 }
 
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize, dim3(a.B), dim3(kWave), 0, st, a.tokens, a.m, a.rule, a.sampling,
-                     a.B, a.M, a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens,
-                     a.p_tok, a.q_tok, a.jobs, a.sup_id, a.sup_p);
-}
-
-void launch_sample(const LaunchArgs& a, hipStream_t st) {
   if (a.dtype == SV_BF16) {
-    hipLaunchKernelGGL(k_sample<Bf16>, dim3(a.B), dim3(kSampleNT), 0, st,
-                       (const uint16_t*)a.target, (const uint16_t*)a.draft, a.B, a.M, a.V, a.rows,
-                       a.jobs, a.out_tokens);
+    hipLaunchKernelGGL(k_finalize<Bf16>, dim3(a.B), dim3(kSampleNT), 0, st,
+                       (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
+                       a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
+                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p);
   } else {
-    hipLaunchKernelGGL(k_sample<F32>, dim3(a.B), dim3(kSampleNT), 0, st,
-                       (const uint32_t*)a.target, (const uint32_t*)a.draft, a.B, a.M, a.V, a.rows,
-                       a.jobs, a.out_tokens);
+    hipLaunchKernelGGL(k_finalize<F32>, dim3(a.B), dim3(kSampleNT), 0, st,
+                       (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
+                       a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
+                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p);
   }
 }
 
