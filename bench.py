@@ -2,8 +2,9 @@
 """Benchmark of the verifier acceptance step (libspecverify) on one MI355X.
 
 A step is one sv_verify call over one batch of synthetic logits already
-resident in HBM: validation, the row-profile kernels (the HBM-streaming part),
-the acceptance kernel and the additional-token sampler.
+resident in HBM: the single-pass row kernel (session checks and the row
+profiles, the HBM-streaming part), the generic row kernel, and the
+per-session kernel (acceptance and the additional token).
 
 Prints ONE JSON line:
   value        verified positions per second, P = sum_b (m_b + 1) per step
@@ -34,10 +35,10 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "topk-ring6-prio-bound4"
+KERNEL_REVISION = "stream-v1"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
-    ("b256_topk_topp", "k_rows_topk", "topk-ring6-prio-bound4"): 1_119_558_656,
+    ("b256_topk_topp", "k_rows_stream", "stream-v1"): 1_119_476_736,
 }
 
 
@@ -143,16 +144,16 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    topk_ms = sum(a.elapsed_ms(b) for a, b, _ in row_ev) / args.steps
-    other_ms = sum(b.elapsed_ms(c) for _, b, c in row_ev) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, top-k row kernel {topk_ms:.4f} ms, "
-        f"other row kernel {other_ms:.4f} ms")
+    stream_ms = sum(a.elapsed_ms(b) for a, b, _ in row_ev) / args.steps
+    generic_ms = sum(b.elapsed_ms(c) for _, b, c in row_ev) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, single-pass row kernel "
+        f"{stream_ms:.4f} ms, generic row kernel {generic_ms:.4f} ms")
 
     # the dominant kernel: the row kernel that takes longer; its algorithmic
     # bytes are the rows it handles
     split = w.row_bytes_by_kernel()
-    kname, kms, kbytes = (("k_rows_topk", topk_ms, split["topk"]) if topk_ms >= other_ms
-                          else ("k_rows_generic", other_ms, split["other"]))
+    kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
+                          else ("k_rows_generic", generic_ms, split["generic"]))
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -189,7 +190,7 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "kernel": kname, "ms_per_launch": kms, "algorithmic_bytes_per_launch": kbytes,
-            "row_kernels_ms": {"k_rows_topk": topk_ms, "k_rows_generic": other_ms},
+            "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_generic": generic_ms},
         },
     }
     if args.cpu_budget > 0:

@@ -2,8 +2,8 @@
 //
 // sv_verify checks its scalar arguments on the host, carves the caller's
 // workspace and enqueues the kernels on the caller's stream:
-//   validate -> row profiles (single-pass top-k kernel, one-pass dense
-//   kernel, then the generic kernel for every other row) -> finalize
+//   single-pass row kernel (session statuses, then each row by the top-k or
+//   the dense path) -> generic row kernel (every other row) -> finalize
 //   (acceptance, and the additional token's draw).
 // It never synchronises and never allocates.
 #include <limits.h>
@@ -87,11 +87,9 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
-  sv::launch_validate(a, st);
   if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
-  sv::launch_rows_topk(a, st);
+  sv::launch_rows_stream(a, st);
   if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
-  sv::launch_rows_dense(a, st);
   sv::launch_rows_generic(a, st);
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
   sv::launch_finalize(a, st);

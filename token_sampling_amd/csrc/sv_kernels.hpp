@@ -23,7 +23,7 @@ struct LaunchArgs {
   double* q_tok;  // may be null
   // workspace carve-up
   RowRec* rows;         // [B, 2M+1]: target rows 1..M+1, then draft rows 1..M
-  int32_t* sess_status; // [B]
+  int32_t* sess_status; // [B], written by the single-pass row kernel
   int32_t* sup_id;      // [B, 2M+1, kSupMax] listed supports (ids ascending)
   double* sup_p;        // [B, 2M+1, kSupMax] their probabilities
 };
@@ -32,8 +32,9 @@ struct LaunchArgs {
 // the generic kernel then computes that row.
 constexpr int32_t kRowFallback = 1;
 
-// Rows whose support lies among the 64 best tokens go to the single-pass
-// top-k kernel (bf16 only): greedy rows, temperature-0 rows, 1 <= top_k <= 64.
+// Rows whose support lies among the 64 best tokens take the single-pass
+// kernel's top-k path (bf16 only): greedy rows, temperature-0 rows,
+// 1 <= top_k <= 64.
 __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule,
                                                      const sv_sampling& s) {
   if (dtype != SV_BF16) return false;
@@ -41,9 +42,9 @@ __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule
   return s.top_k >= 1 && s.top_k <= 64;
 }
 
-// Rows whose support is not limited to a few best tokens go to the one-pass
-// dense kernel (bf16 only): temperature > 0 with top-k off (top_k = 0 or
-// top_k >= V), with or without top-p.
+// Rows whose support is not limited to a few best tokens take the single-pass
+// kernel's dense path (bf16 only): temperature > 0 with top-k off (top_k = 0
+// or top_k >= V), with or without top-p.
 __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rule,
                                                       const sv_sampling& s, int32_t V) {
   if (dtype != SV_BF16 || row_uses_topk_kernel(dtype, rule, s)) return false;
@@ -56,9 +57,7 @@ struct WorkspaceLayout {
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
 
-void launch_validate(const LaunchArgs& a, hipStream_t st);
-void launch_rows_topk(const LaunchArgs& a, hipStream_t st);
-void launch_rows_dense(const LaunchArgs& a, hipStream_t st);
+void launch_rows_stream(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
 

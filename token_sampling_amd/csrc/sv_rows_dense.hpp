@@ -1,4 +1,4 @@
-// sv_rows_dense.hip -- one pass over a bf16 logits row for the profiles whose
+// sv_rows_dense.hpp -- one pass over a bf16 logits row for the profiles whose
 // support is not limited to a few best tokens: temperature alone, or
 // temperature then top-p, with top-k off (SDCP Sec. 4.1).
 //
@@ -31,12 +31,13 @@
 // The cut is recorded as (kc, j); the sampling kernel turns j into a cut id
 // when it needs one.  The argmax is not computed: no rule reads it for these
 // profiles (greedy and temperature-0 rows take the top-k kernel).
+#pragma once
+
 #include "sv_kernels.hpp"
 #include "sv_stream.hpp"
 
 namespace sv {
-
-namespace {
+namespace dense {
 
 using namespace stream;
 
@@ -142,36 +143,16 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v
   }
 }
 
-#ifndef SV_DENSE_WAVES_PER_EU
-#define SV_DENSE_WAVES_PER_EU 5
-#endif
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_WAVES_PER_EU))) void k_rows_dense(
-    const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
-    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
-    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows) {
-  __shared__ uint32_t bins[kWin];
+// The profile of one row of the dense class, by one wave: temperature > 0,
+// top-k off, with or without top-p.  bins is the wave's LDS histogram of kWin
+// counts.
+__device__ __attribute__((always_inline)) inline void row_profile(
+    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
   const int lane = __lane_id();
-  const int R = 2 * M + 1;
-  const int slot_g = blockIdx.x;
-  const int b = slot_g / R;
-  const int slot = slot_g - b * R;
-  if (b >= B || sess_status[b] != 0) return;
-  const int mb = m[b];
-  const int rl = rule[b];
-  const bool is_target = slot <= M;
-  const int i = is_target ? slot + 1 : slot - M;
-  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
-  const sv_sampling smp = sampling[b];
-  if (!row_uses_dense_kernel(SV_BF16, rl, smp, V)) return;
-  const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
-                                  : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
-  const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
   const bool top_p = smp.top_p_milli < 1000;
   // the row's scale: log2(e) / T rounded to binary32, used everywhere below
   const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
   const double scale = (double)scale_f;
-  RowRec* rec = rows + (size_t)slot_g;
 
   // 16-byte aligned window over the row: positions [head, head + V) are the row
   const int head = (int)(((uintptr_t)row & 15u) >> 1);
@@ -314,14 +295,5 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_DENSE_
   if (lane == 0) *rec = rr;
 }
 
-}  // namespace
-
-void launch_rows_dense(const LaunchArgs& a, hipStream_t st) {
-  if (a.dtype != SV_BF16) return;
-  const unsigned grid = (unsigned)((size_t)a.B * (2 * a.M + 1));
-  hipLaunchKernelGGL(k_rows_dense, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
-                     (const uint16_t*)a.draft, a.tokens, a.m, a.rule, a.sampling, a.sess_status,
-                     a.B, a.M, a.V, a.rows);
-}
-
+}  // namespace dense
 }  // namespace sv

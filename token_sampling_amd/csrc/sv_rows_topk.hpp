@@ -28,12 +28,13 @@
 // ties).  A tile that would overflow the region even after a cut (at most 256
 // entries; adversarial rows such as ascending logits or tiny vocabularies) is
 // left to the generic kernel (status kRowFallback).
+#pragma once
+
 #include "sv_kernels.hpp"
 #include "sv_stream.hpp"
 
 namespace sv {
-
-namespace {
+namespace topk {
 
 using namespace stream;
 
@@ -47,10 +48,6 @@ constexpr int kVec = SV_TOPK_VEC;          // 16-byte loads per lane per tile
 constexpr int kNBuf = SV_TOPK_NBUF;        // tiles in the load ring (kNBuf - 1 in flight)
 constexpr int kTile = kWave * kVec * 8;    // bf16 logits per tile
 constexpr int kCap = 256;                  // candidate entries per wave
-#ifndef SV_TOPK_WPB
-#define SV_TOPK_WPB 1
-#endif
-constexpr int kWavesPerBlock = SV_TOPK_WPB;  // independent rows per workgroup
 constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
 #ifndef SV_TOPK_BOUND_TILES
 #define SV_TOPK_BOUND_TILES 4
@@ -407,41 +404,13 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   if (lane == 0) *rec = r;
 }
 
-#ifndef SV_TOPK_WAVES_PER_EU
-#define SV_TOPK_WAVES_PER_EU 6
-#endif
-__global__ __launch_bounds__(kWave * kWavesPerBlock)
-__attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
-    const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
-    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
-    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows,
-    int32_t* __restrict__ sup_id, double* __restrict__ sup_p) {
-  __shared__ __align__(16) uint64_t region[kWavesPerBlock][kCap];
-  // the wave index is uniform across the wave: keep it (and everything
-  // derived from it, such as the row address) in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+// The profile of one row of the top-k class, by one wave: rows whose support
+// lies among the k <= 64 best tokens (k = 1 for one-hot profiles).  reg is
+// the wave's LDS region of kCap entries; sup_id, sup_p its listed support.
+__device__ __attribute__((always_inline)) inline void row_profile(
+    const uint16_t* row, int V, int k, bool one_hot, const sv_sampling& smp, int32_t x, RowRec* rec,
+    int32_t* sup_id, double* sup_p, uint64_t* reg) {
   const int lane = __lane_id();
-  const int R = 2 * M + 1;
-  const long slot_g = (long)blockIdx.x * kWavesPerBlock + wave;
-  const int b = (int)(slot_g / R);
-  const int slot = (int)(slot_g - (long)b * R);
-  if (b >= B || sess_status[b] != 0) return;
-  const int mb = m[b];
-  const int rl = rule[b];
-  const bool is_target = slot <= M;
-  const int i = is_target ? slot + 1 : slot - M;
-  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
-  const sv_sampling smp = sampling[b];
-  if (!row_uses_topk_kernel(SV_BF16, rl, smp)) return;
-  const bool one_hot = rl == SV_RULE_GREEDY || smp.temperature_milli == 0;
-  const int k = one_hot ? 1 : (int)smp.top_k;
-  const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
-  const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
-                                  : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
-  RowRec* rec = rows + (size_t)b * R + slot;
-  uint64_t* reg = region[wave];
-
   // 16-byte aligned window over the row: positions [head, head + V) are the row
   const int head = (int)(((uintptr_t)row & 15u) >> 1);
   const u32x4* vbase = (const u32x4*)(row - head);
@@ -508,21 +477,9 @@ __attribute__((amdgpu_waves_per_eu(SV_TOPK_WAVES_PER_EU))) void k_rows_topk(
     }
     return;
   }
-  const size_t so = ((size_t)b * R + slot) * kSupMax;
   row_finish(reg, s.n, k, s.magmax, s.umax, one_hot, smp.temperature_milli, smp.top_p_milli, x, rec,
-             sup_id + so, sup_p + so);
+             sup_id, sup_p);
 }
 
-}  // namespace
-
-void launch_rows_topk(const LaunchArgs& a, hipStream_t st) {
-  if (a.dtype != SV_BF16) return;
-  const size_t slots = (size_t)a.B * (2 * a.M + 1);
-  const unsigned grid = (unsigned)((slots + kWavesPerBlock - 1) / kWavesPerBlock);
-  hipLaunchKernelGGL(k_rows_topk, dim3(grid), dim3(kWave * kWavesPerBlock), 0, st,
-                     (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
-                     a.sampling, a.sess_status, a.B, a.M, a.V, a.rows, a.sup_id, a.sup_p);
-}
-
+}  // namespace topk
 }  // namespace sv
-

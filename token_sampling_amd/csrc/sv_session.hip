@@ -1,46 +1,15 @@
-// sv_session.hip -- per-session kernels of libspecverify:
-//   validate  (one thread per session): argument checks that need no logits;
-//   finalize  (one wave64 per session, lane i = position i+1): the acceptance
-//             rule with a 64-bit ballot for the first rejection;
-//   sample    (one workgroup per session): the additional token as an inverse
-//             CDF over ascending token ids.
+// sv_session.hip -- the per-session kernel of libspecverify, one workgroup
+// per session:
+//   its first wave (lane i = position i+1) takes the acceptance rule, with a
+//   64-bit ballot for the first rejection, and draws the additional token
+//   from listed supports;
+//   the whole workgroup draws the additional token, as an inverse CDF over
+//   ascending token ids, when the rows have no listed support.
 #include "sv_kernels.hpp"
 
 namespace sv {
 
 namespace {
-
-// SDCP Table 2 / Sec. 6.3: statuses decidable before any logit is read.
-__global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ tokens,
-                                                  const int32_t* __restrict__ m,
-                                                  const int32_t* __restrict__ rule,
-                                                  const sv_sampling* __restrict__ sampling,
-                                                  int B, int M, int V, int has_draft,
-                                                  int32_t* __restrict__ sess_status) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  const int mb = m[b];
-  const int rl = rule[b];
-  const sv_sampling s = sampling[b];
-  int32_t st = 0;
-  if (mb < 1 || mb > M) {
-    st = SV_S_LIMIT;
-  } else if ((rl != SV_RULE_GREEDY && rl != SV_RULE_SPECULATIVE) || s.reserved != 0 ||
-             s.top_p_milli > 1000) {
-    st = SV_S_BAD_PROFILE;
-  } else if (rl == SV_RULE_SPECULATIVE && !has_draft) {
-    st = SV_S_Q_UNAVAILABLE;
-  } else {
-    for (int i = 0; i < mb; ++i) {
-      const int32_t x = tokens[(size_t)b * M + i];
-      if (x < 0 || x >= V) {
-        st = SV_S_BAD_PROPOSAL;
-        break;
-      }
-    }
-  }
-  sess_status[b] = st;
-}
 
 // Inverse CDF over a listed support (ids ascending): the additional token is
 // the smallest id whose running mass exceeds u * S (the largest id with mass
@@ -435,11 +404,6 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
 }
 
 }  // namespace
-
-void launch_validate(const LaunchArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_validate, dim3((a.B + 255) / 256), dim3(256), 0, st, a.tokens, a.m, a.rule,
-                     a.sampling, a.B, a.M, a.V, a.draft != nullptr ? 1 : 0, a.sess_status);
-}
 
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
   if (a.dtype == SV_BF16) {

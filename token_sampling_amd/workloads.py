@@ -90,18 +90,21 @@ class Workload:
         return rows * self.V * s + small
 
     def row_bytes_by_kernel(self) -> dict:
-        """Row bytes read by each row kernel: the single-pass top-k kernel takes
-        bf16 rows whose support lies among the 64 best tokens (greedy rules,
-        temperature 0, 1 <= top_k <= 64); the other kernel takes the rest."""
+        """Row bytes read by each row kernel: the single-pass kernel takes bf16
+        rows of the top-k class (greedy rules, temperature 0, 1 <= top_k <= 64)
+        and of the dense class (temperature > 0 with top-k off); the generic
+        kernel takes the rest."""
         m = self.m.to("cpu").to(torch.int64).numpy()
         rule = self.rule.to("cpu").to(torch.int64).numpy()
         s = self.sampling
         bf16 = self.target.dtype == torch.bfloat16
-        topk_rule = (rule == 1) | (s["temperature_milli"] == 0) | ((s["top_k"] >= 1) & (s["top_k"] <= 64))
+        T, k = s["temperature_milli"], s["top_k"]
+        topk_class = (rule == 1) | (T == 0) | ((k >= 1) & (k <= 64))
+        dense_class = ~topk_class & ((k == 0) | (k >= self.V))
         per_session = (m + 1) + m * (rule == 2)
         row = self.V * self.target.element_size()
-        topk = int(per_session[topk_rule].sum()) * row if bf16 else 0
-        return {"topk": topk, "other": int(per_session.sum()) * row - topk}
+        stream = int(per_session[topk_class | dense_class].sum()) * row if bf16 else 0
+        return {"stream": stream, "generic": int(per_session.sum()) * row - stream}
 
 
 def _to_storage(x32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
