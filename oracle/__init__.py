@@ -98,6 +98,20 @@ def lib():
             ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp, dp,
         ]
         L.ov_verify.restype = ctypes.c_int
+        L.ov_verify_sdcp.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i32p, i32p, i32p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            i32p, i32p, dp, dp, dp, dp, dp, dp,
+        ]
+        L.ov_verify_sdcp.restype = ctypes.c_int
+        L.ov_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
+        L.ov_sha256.restype = None
+        L.ov_hmac_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p,
+                                     ctypes.c_size_t, ctypes.c_char_p]
+        L.ov_hmac_sha256.restype = None
+        L.ov_sdcp_uniform.argtypes = [ctypes.c_uint64, ctypes.c_char_p, ctypes.c_uint32,
+                                      ctypes.c_uint32, ctypes.c_int]
+        L.ov_sdcp_uniform.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -163,6 +177,48 @@ def residual_pick(p, q, u):
 
 
 # ------------------------------------------------------------- batched step
+# SDCP per-session inputs of the verifier's uniforms (Sec. 6.4): the 16-octet
+# session id, the profile's seed and the round (32 bytes, 8-aligned).
+SDCP_SESSION_DTYPE = np.dtype(
+    [("id", np.uint8, (16,)), ("seed", np.uint64), ("round", np.uint32), ("reserved", np.uint32)],
+    align=True)
+assert SDCP_SESSION_DTYPE.itemsize == 32
+
+
+def sha256(msg: bytes) -> bytes:
+    """SHA-256 (FIPS 180-4) of msg, by the oracle's own implementation."""
+    out = ctypes.create_string_buffer(32)
+    lib().ov_sha256(msg, len(msg), out)
+    return out.raw
+
+
+def hmac_sha256(key: bytes, msg: bytes) -> bytes:
+    """HMAC-SHA-256 (RFC 2104) by the oracle's own implementation."""
+    out = ctypes.create_string_buffer(32)
+    lib().ov_hmac_sha256(key, len(key), msg, len(msg), out)
+    return out.raw
+
+
+def sdcp_uniform(seed: int, session: bytes, round_: int, i: int, purpose: int) -> float:
+    """SDCP Sec. 6.4 verifier value for position i (purpose 0 or 1)."""
+    assert len(session) == 16
+    return lib().ov_sdcp_uniform(seed, session, round_, i, purpose)
+
+
+def make_sdcp_sessions(B, seed=0, round_=1, ids=None):
+    """SDCP session records: ids [B, 16] uint8 (default: b in the last 8
+    octets, big-endian), one seed and round for all (or arrays [B])."""
+    s = np.zeros(B, dtype=SDCP_SESSION_DTYPE)
+    if ids is None:
+        for b in range(B):
+            s[b]["id"][8:] = np.frombuffer(int(b).to_bytes(8, "big"), dtype=np.uint8)
+    else:
+        s["id"] = np.asarray(ids, dtype=np.uint8).reshape(B, 16)
+    s["seed"] = seed
+    s["round"] = round_
+    return s
+
+
 def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_key=None):
     s = np.zeros(B, dtype=SAMPLING_DTYPE)
     s["temperature_milli"] = temperature_milli
@@ -172,14 +228,16 @@ def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_
     return s
 
 
-def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=True):
+def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=True,
+           sdcp_sessions=None):
     """Run the oracle over a batch.
 
     target: [B, M+1, V] uint16 (bf16 bits) or float32; draft: [B, M, V] of the
     same dtype, or None.  tokens [B, M] int32, m [B] int32, rule [B] int32,
     sampling [B] of ``SAMPLING_DTYPE``.  Returns a dict with accepted_len,
     out_tokens, p_tok, q_tok and (if diagnostics) d_acc, d_topp_t, d_topp_d,
-    d_cdf.
+    d_cdf.  With sdcp_sessions ([B] of ``SDCP_SESSION_DTYPE``) the uniforms are
+    SDCP's HMAC-SHA-256 values and seed, round_ are ignored.
     """
     target = np.ascontiguousarray(target)
     _, dt = _as_row(target[..., :1].reshape(-1)[:1]) if target.size else (None, BF16)
@@ -208,13 +266,17 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     def opt(name):
         return _ptr(out[name], ctypes.c_double) if name in out else ctypes.cast(None, dp)
 
-    rc = lib().ov_verify(
-        target.ctypes.data, None if draft is None else draft.ctypes.data, dt,
-        _ptr(tokens, ctypes.c_int32), _ptr(m, ctypes.c_int32), _ptr(rule, ctypes.c_int32),
-        sampling.ctypes.data, B, M, V, seed, round_,
-        _ptr(out["accepted_len"], ctypes.c_int32), _ptr(out["out_tokens"], ctypes.c_int32),
-        opt("p_tok"), opt("q_tok"), opt("d_acc"), opt("d_topp_t"), opt("d_topp_d"), opt("d_cdf"),
-    )
+    outs = (_ptr(out["accepted_len"], ctypes.c_int32), _ptr(out["out_tokens"], ctypes.c_int32),
+            opt("p_tok"), opt("q_tok"), opt("d_acc"), opt("d_topp_t"), opt("d_topp_d"),
+            opt("d_cdf"))
+    common = (target.ctypes.data, None if draft is None else draft.ctypes.data, dt,
+              _ptr(tokens, ctypes.c_int32), _ptr(m, ctypes.c_int32), _ptr(rule, ctypes.c_int32),
+              sampling.ctypes.data)
+    if sdcp_sessions is None:
+        rc = lib().ov_verify(*common, B, M, V, seed, round_, *outs)
+    else:
+        sess = np.ascontiguousarray(sdcp_sessions, dtype=SDCP_SESSION_DTYPE).reshape(B)
+        rc = lib().ov_verify_sdcp(*common, sess.ctypes.data, B, M, V, *outs)
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")
     return out

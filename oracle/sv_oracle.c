@@ -25,12 +25,20 @@
  *          when every proposal is accepted).
  *  [PHX]   Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *          1, 2, 3", SC'11 -- the Philox4x64 counter-based generator.
+ *  [SHS]   FIPS 180-4, Secure Hash Standard, Sec. 4.1.2, 4.2.2, 5, 6.2 --
+ *          SHA-256 (the hash the SDCP text names, via RFC 6234).
+ *  [HMAC]  RFC 2104 -- HMAC, with SHA-256 (64-octet blocks).
  *
  * Readings taken where the pages are silent (each listed in the design notes):
- *  - the verifier's uniforms come from Philox4x64-10 keyed by (seed,
- *    session_key) at counter (round, i, 0, 0); word 0 gives the acceptance
- *    uniform and word 1 the additional-token uniform, each as its top 53 bits
- *    times 2^-53 (the SDCP text derives them from HMAC-SHA-256 instead);
+ *  - ov_verify: the verifier's uniforms come from Philox4x64-10 keyed by
+ *    (seed, session_key) at counter (round, i, 0, 0); word 0 gives the
+ *    acceptance uniform and word 1 the additional-token uniform, each as its
+ *    top 53 bits times 2^-53;
+ *  - ov_verify_sdcp: the uniforms of SDCP Sec. 6.4 itself: HMAC-SHA-256 keyed
+ *    with the session's seed (8 octets, network order) over "SDCP-VERIFY-1" ||
+ *    0x00 || session id (16 octets) || uint32(round) || uint32(i) ||
+ *    uint8(purpose); the first 53 bits of the MAC (most significant first)
+ *    times 2^-53;
  *  - q_i is the same sampling profile applied to the draft logits row i;
  *  - top-k keeps exactly k tokens in the order (logit desc, id asc);
  *  - top-p keeps the shortest non-empty prefix of that order whose mass C
@@ -109,6 +117,156 @@ double ov_uniform(uint64_t seed, uint64_t session_key, uint32_t round, uint32_t 
   ov_philox4x64_10(ctr, key, o);
   uint64_t word = purpose == 0 ? o[0] : o[1];
   return ldexp((double)(word >> 11), -53);
+}
+
+/* ------------------------------------------------------------------------ */
+/* SHA-256 [SHS].  The round constants are the first 32 bits of the          */
+/* fractional parts of the cube roots of the first 64 primes, the initial    */
+/* hash value those of the square roots of the first 8 primes [SHS Sec.      */
+/* 4.2.2, 5.3.3]; both are derived here from that definition.                */
+/* ------------------------------------------------------------------------ */
+static uint32_t SHA_K[64], SHA_H0[8];
+static int sha_ready = 0;
+
+static uint32_t frac32(double x) { return (uint32_t)ldexp(x - floor(x), 32); }
+
+static void sha_init_constants(void) {
+  if (sha_ready) return;
+  int primes[64], n = 0;
+  for (int c = 2; n < 64; ++c) {
+    int prime = 1;
+    for (int d = 2; d * d <= c; ++d)
+      if (c % d == 0) { prime = 0; break; }
+    if (prime) primes[n++] = c;
+  }
+  for (int i = 0; i < 64; ++i) SHA_K[i] = frac32(cbrt((double)primes[i]));
+  for (int i = 0; i < 8; ++i) SHA_H0[i] = frac32(sqrt((double)primes[i]));
+  sha_ready = 1;
+}
+
+static uint32_t rotr(uint32_t x, int r) { return (x >> r) | (x << (32 - r)); }
+
+/* one 64-octet block into the hash state [SHS Sec. 6.2.2] */
+static void sha256_block(uint32_t h[8], const uint8_t blk[64]) {
+  uint32_t w[64];
+  for (int t = 0; t < 16; ++t)
+    w[t] = (uint32_t)blk[4 * t] << 24 | (uint32_t)blk[4 * t + 1] << 16 |
+           (uint32_t)blk[4 * t + 2] << 8 | (uint32_t)blk[4 * t + 3];
+  for (int t = 16; t < 64; ++t) {
+    const uint32_t s0 = rotr(w[t - 15], 7) ^ rotr(w[t - 15], 18) ^ (w[t - 15] >> 3);
+    const uint32_t s1 = rotr(w[t - 2], 17) ^ rotr(w[t - 2], 19) ^ (w[t - 2] >> 10);
+    w[t] = s1 + w[t - 7] + s0 + w[t - 16];
+  }
+  uint32_t a = h[0], b = h[1], c = h[2], d = h[3], e = h[4], f = h[5], g = h[6], k = h[7];
+  for (int t = 0; t < 64; ++t) {
+    const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+    const uint32_t ch = (e & f) ^ (~e & g);
+    const uint32_t T1 = k + S1 + ch + SHA_K[t] + w[t];
+    const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+    const uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
+    const uint32_t T2 = S0 + maj;
+    k = g; g = f; f = e; e = d + T1; d = c; c = b; b = a; a = T1 + T2;
+  }
+  h[0] += a; h[1] += b; h[2] += c; h[3] += d; h[4] += e; h[5] += f; h[6] += g; h[7] += k;
+}
+
+/* SHA-256 of msg[0..len): padding with 0x80, zeros and the 64-bit bit length
+ * [SHS Sec. 5.1.1], then the blocks in order; the digest is the state words
+ * big-endian [SHS Sec. 6.2.2]. */
+void ov_sha256(const uint8_t *msg, size_t len, uint8_t out[32]) {
+  sha_init_constants();
+  uint32_t h[8];
+  memcpy(h, SHA_H0, sizeof h);
+  size_t done = 0;
+  while (len - done >= 64) {
+    sha256_block(h, msg + done);
+    done += 64;
+  }
+  uint8_t tail[128];
+  memset(tail, 0, sizeof tail);
+  const size_t r = len - done;
+  memcpy(tail, msg + done, r);
+  tail[r] = 0x80;
+  const size_t tl = r + 1 + 8 <= 64 ? 64 : 128;
+  const uint64_t bits = (uint64_t)len * 8u;
+  for (int i = 0; i < 8; ++i) tail[tl - 1 - i] = (uint8_t)(bits >> (8 * i));
+  sha256_block(h, tail);
+  if (tl == 128) sha256_block(h, tail + 64);
+  for (int i = 0; i < 8; ++i) {
+    out[4 * i] = (uint8_t)(h[i] >> 24);
+    out[4 * i + 1] = (uint8_t)(h[i] >> 16);
+    out[4 * i + 2] = (uint8_t)(h[i] >> 8);
+    out[4 * i + 3] = (uint8_t)h[i];
+  }
+}
+
+/* HMAC-SHA-256 [HMAC]: H((K ^ opad) || H((K ^ ipad) || text)), the key padded
+ * with zeros to the 64-octet block (keys longer than a block are hashed
+ * first). */
+void ov_hmac_sha256(const uint8_t *key, size_t klen, const uint8_t *msg, size_t len,
+                    uint8_t out[32]) {
+  uint8_t k0[64];
+  memset(k0, 0, sizeof k0);
+  if (klen > 64)
+    ov_sha256(key, klen, k0);
+  else
+    memcpy(k0, key, klen);
+  uint8_t *inner = (uint8_t *)malloc(64 + len);
+  for (int i = 0; i < 64; ++i) inner[i] = k0[i] ^ 0x36;
+  memcpy(inner + 64, msg, len);
+  uint8_t ih[32];
+  ov_sha256(inner, 64 + len, ih);
+  free(inner);
+  uint8_t outer[64 + 32];
+  for (int i = 0; i < 64; ++i) outer[i] = k0[i] ^ 0x5c;
+  memcpy(outer + 64, ih, 32);
+  ov_sha256(outer, sizeof outer, out);
+}
+
+/* SDCP Sec. 6.4: the verifier's value for position i and purpose (0 =
+ * acceptance test, 1 = additional token): HMAC-SHA-256 keyed with the seed
+ * as eight octets in network byte order, over "SDCP-VERIFY-1" || 0x00 ||
+ * session || uint32(round) || uint32(i) || uint8(purpose); the first 53 bits
+ * of the result divided by 2^53. */
+double ov_sdcp_uniform(uint64_t seed, const uint8_t session[16], uint32_t round, uint32_t i,
+                       int purpose) {
+  uint8_t key[8], msg[13 + 1 + 16 + 4 + 4 + 1];
+  for (int j = 0; j < 8; ++j) key[j] = (uint8_t)(seed >> (56 - 8 * j));
+  size_t n = 0;
+  memcpy(msg + n, "SDCP-VERIFY-1", 13);
+  n += 13;
+  msg[n++] = 0x00;
+  memcpy(msg + n, session, 16);
+  n += 16;
+  for (int j = 0; j < 4; ++j) msg[n++] = (uint8_t)(round >> (24 - 8 * j));
+  for (int j = 0; j < 4; ++j) msg[n++] = (uint8_t)(i >> (24 - 8 * j));
+  msg[n++] = (uint8_t)purpose;
+  uint8_t mac[32];
+  ov_hmac_sha256(key, sizeof key, msg, n, mac);
+  uint64_t w = 0;
+  for (int j = 0; j < 8; ++j) w = w << 8 | mac[j];
+  return ldexp((double)(w >> 11), -53);
+}
+
+/* SDCP per-session inputs of the uniforms (the same 32-octet layout as the
+ * library's record): session id, seed, round. */
+typedef struct {
+  uint8_t id[16];
+  uint64_t seed;
+  uint32_t round;
+  uint32_t reserved;
+} ov_sdcp_session;
+
+/* Where a session's uniforms come from. */
+typedef struct {
+  uint64_t seed, session_key;  /* Philox */
+  uint32_t round;
+  const ov_sdcp_session *sdcp; /* non-NULL: SDCP Sec. 6.4 */
+} ov_rng;
+
+static double rng_uniform(const ov_rng *g, uint32_t i, int purpose) {
+  if (g->sdcp) return ov_sdcp_uniform(g->sdcp->seed, g->sdcp->id, g->sdcp->round, i, purpose);
+  return ov_uniform(g->seed, g->session_key, g->round, i, purpose);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -310,7 +468,7 @@ static void set_if(double *arr, int64_t idx, double v) {
  */
 static int verify_session(int64_t b, const void *target, const void *draft, int dtype,
                           const int32_t *x, int m, int rule, const ov_sampling *s, int M, int V,
-                          uint64_t seed, uint32_t round, int32_t *out, double *p_tok,
+                          const ov_rng *g, int32_t *out, double *p_tok,
                           double *q_tok, double *d_acc, double *d_topp_t, double *d_topp_d,
                           double *d_cdf, ov_scratch *sc) {
   /* SDCP Sec. 6.2 / Table 2 "sdcp-limit": 1 <= M <= m_max (<= 64) */
@@ -381,7 +539,7 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
 
     const double ratio = px / qx[i - 1];
     const double acc = ratio < 1.0 ? ratio : 1.0;
-    const double u = ov_uniform(seed, s->session_key, round, (uint32_t)i, 0);
+    const double u = rng_uniform(g, (uint32_t)i, 0);
     set_if(d_acc, b * (int64_t)M + i - 1, fabs(u - acc));
     if (u < acc) {
       out[i - 1] = x[i - 1];
@@ -392,7 +550,7 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
     profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
     double dc;
     out[i - 1] = residual_pick(sc->p, sc->q, V,
-                               ov_uniform(seed, s->session_key, round, (uint32_t)i, 1), sc->w, &dc);
+                               rng_uniform(g, (uint32_t)i, 1), sc->w, &dc);
     set_if(d_cdf, b, dc);
     a = i - 1;
     decided = 1;
@@ -403,7 +561,7 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
     load_row(target, dtype, trow0 + m, V, sc->l);
     profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
     set_if(d_topp_t, b * (int64_t)(M + 1) + m, dt);
-    out[m] = inverse_cdf(sc->p, V, ov_uniform(seed, s->session_key, round, (uint32_t)(m + 1), 1), &dc);
+    out[m] = inverse_cdf(sc->p, V, rng_uniform(g, (uint32_t)(m + 1), 1), &dc);
     set_if(d_cdf, b, dc);
   }
   return a;
@@ -420,9 +578,10 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
  * d_topp_t [B, M+1], d_topp_d, d_cdf [B].
  * Returns OV_OK or OV_ERR_*.
  */
-int ov_verify(const void *target, const void *draft, int dtype, const int32_t *tokens,
+static int verify_batch(const void *target, const void *draft, int dtype, const int32_t *tokens,
               const int32_t *m, const int32_t *rule, const ov_sampling *sampling, int64_t B,
-              int M, int V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+              int M, int V, uint64_t seed, uint32_t round, const ov_sdcp_session *sdcp,
+              int32_t *accepted_len,
               int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
               double *d_topp_t, double *d_topp_d, double *d_cdf) {
   if (!target || !tokens || !m || !rule || !sampling || !accepted_len || !out_tokens)
@@ -453,8 +612,9 @@ int ov_verify(const void *target, const void *draft, int dtype, const int32_t *t
     for (int j = 0; j <= M; ++j) set_if(d_topp_t, b * (int64_t)(M + 1) + j, INFINITY);
     set_if(d_cdf, b, INFINITY);
 
+    const ov_rng g = {seed, sampling[b].session_key, round, sdcp ? &sdcp[b] : NULL};
     int a = verify_session(b, target, draft, dtype, tokens + b * (int64_t)M, m[b], rule[b],
-                           &sampling[b], M, V, seed, round, out, p_tok, q_tok, d_acc, d_topp_t,
+                           &sampling[b], M, V, &g, out, p_tok, q_tok, d_acc, d_topp_t,
                            d_topp_d, d_cdf, &sc);
     accepted_len[b] = a;
     if (a < 0) { /* a failed session emits nothing; its diagnostics are kept */
@@ -467,4 +627,25 @@ int ov_verify(const void *target, const void *draft, int dtype, const int32_t *t
   }
   free(sc.l); free(sc.p); free(sc.q); free(sc.w); free(sc.ent);
   return OV_OK;
+}
+
+int ov_verify(const void *target, const void *draft, int dtype, const int32_t *tokens,
+              const int32_t *m, const int32_t *rule, const ov_sampling *sampling, int64_t B,
+              int M, int V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+              int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
+              double *d_topp_t, double *d_topp_d, double *d_cdf) {
+  return verify_batch(target, draft, dtype, tokens, m, rule, sampling, B, M, V, seed, round, NULL,
+                      accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d, d_cdf);
+}
+
+/* The same batched step with the uniforms of SDCP Sec. 6.4 (HMAC-SHA-256);
+ * sessions[B] give each session's id, seed and round. */
+int ov_verify_sdcp(const void *target, const void *draft, int dtype, const int32_t *tokens,
+                   const int32_t *m, const int32_t *rule, const ov_sampling *sampling,
+                   const ov_sdcp_session *sessions, int64_t B, int M, int V,
+                   int32_t *accepted_len, int32_t *out_tokens, double *p_tok, double *q_tok,
+                   double *d_acc, double *d_topp_t, double *d_topp_d, double *d_cdf) {
+  if (!sessions) return OV_ERR_ARG;
+  return verify_batch(target, draft, dtype, tokens, m, rule, sampling, B, M, V, 0, 0, sessions,
+                      accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d, d_cdf);
 }
