@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the verifier acceptance step (libspecverify) on one MI355X.
 
-A step is one sv_verify call over one batch of synthetic logits already
-resident in HBM: the single-pass row kernel (session checks and the row
+A step is one sv_verify call (sv_verify_sdcp with --sdcp) over one batch of
+synthetic logits already resident in HBM: the single-pass row kernel (session checks and the row
 profiles, the HBM-streaming part), the generic row kernel, and the
 per-session kernel (acceptance and the additional token).
 
@@ -35,7 +35,7 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "stream-v1"
+KERNEL_REVISION = "stream-v2"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
     ("b256_topk_topp", "k_rows_stream", "stream-v1"): 1_119_476_736,
@@ -46,12 +46,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
-    """Time the oracle on the first sessions of the workload (bounded sample)."""
+def cpu_baseline(w, budget_s: float, sdcp_raw=None):
+    """Time the oracle on the first sessions of the workload (bounded sample).
+    sdcp_raw: the [B, 32] session records (numpy uint8) when SDCP values are used."""
     import numpy as np
 
     import oracle
     from token_sampling_amd import workloads as W
+
+    sdcp = None if sdcp_raw is None else \
+        np.ascontiguousarray(sdcp_raw).view(oracle.SDCP_SESSION_DTYPE).reshape(-1)
 
     oracle.lib()
     n = 1
@@ -63,7 +67,8 @@ def cpu_baseline(w, budget_s: float):
         h = W.to_numpy(w, sessions=idx)
         t0 = time.perf_counter()
         oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
-                      h["seed"], h["round"], diagnostics=False)
+                      h["seed"], h["round"], diagnostics=False,
+                      sdcp_sessions=None if sdcp is None else sdcp[idx])
         dt = time.perf_counter() - t0
         elapsed += dt
         positions += int((np.asarray(h["m"], dtype=np.int64) + 1).sum())
@@ -94,6 +99,9 @@ def main():
                     help="after the timed steps, run a plain elementwise copy kernel "
                          "(1 GiB read, 1 GiB written) three times, to calibrate HBM "
                          "byte counters under a profiler")
+    ap.add_argument("--sdcp", action="store_true",
+                    help="time sv_verify_sdcp: the SDCP HMAC-SHA-256 verifier values from "
+                         "per-session records (seeded random ids and seeds) instead of Philox")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,10 +131,16 @@ def main():
     out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
            "out_tokens": torch.empty((B, M + 1), dtype=torch.int32, device=dev)}
     stream = torch.cuda.current_stream(dev)
+    sdcp = None
+    if args.sdcp:
+        import numpy as np
+
+        ids = np.random.default_rng(w.seed & 0xFFFFFFFF).integers(0, 256, (B, 16), dtype=np.uint8)
+        sdcp = sv.make_sdcp_sessions(B, seed=w.seed, round_=w.round, session_ids=ids, device=dev)
 
     def step(ev=None):
         sv.verify(w.target, w.draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
-                  workspace=ws, out=out, stream=stream, row_events=ev)
+                  workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp)
 
     for _ in range(args.warmup):
         step()
@@ -165,7 +179,7 @@ def main():
 
     a = out["accepted_len"].cpu()
     achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
+    traffic = None if args.sdcp else MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
     result = {
         "metric": METRIC,
         "value": P / (ms_per_step * 1e-3),
@@ -182,6 +196,7 @@ def main():
         "config": {
             "workload": args.workload, "B": B, "M": M, "V": V,
             "logits": "bf16" if w.target.dtype == torch.bfloat16 else "fp32",
+            "uniforms": "sdcp-hmac-sha256" if args.sdcp else "philox4x64-10",
             "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(),
             "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),
@@ -195,7 +210,8 @@ def main():
     }
     if args.cpu_budget > 0:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(
+            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy())
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

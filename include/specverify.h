@@ -23,10 +23,11 @@
  *
  * Readings where the pages are silent (the library implements exactly these):
  *  - draft distribution q_i = the same profile applied to draft logits row i;
- *  - uniforms: Philox4x64-10 (Salmon et al., SC'11) with key (seed,
- *    session_key) and counter (round, i, 0, 0), i = 1-based position; word 0
- *    >> 11 times 2^-53 is the acceptance uniform, word 1 the additional-token
- *    uniform (the draft derives them from HMAC-SHA-256 instead);
+ *  - uniforms of sv_verify: Philox4x64-10 (Salmon et al., SC'11) with key
+ *    (seed, session_key) and counter (round, i, 0, 0), i = 1-based position;
+ *    word 0 >> 11 times 2^-53 is the acceptance uniform, word 1 the
+ *    additional-token uniform.  sv_verify_sdcp takes the draft's own values
+ *    instead (HMAC-SHA-256, Sec. 6.4; see sv_sdcp_session);
  *  - top-k keeps exactly k tokens in the order (logit desc, id asc); top_k = 0
  *    or >= the number of finite logits is "off";
  *  - top-p keeps the shortest non-empty prefix of that order whose mass C
@@ -50,6 +51,8 @@ extern "C" {
 #define SV_VERSION 1
 #define SV_M_MAX 64          /* SDCP Sec. 4.1: m_max <= 64 */
 #define SV_V_MAX (1 << 24)   /* largest vocabulary accepted */
+#define SV_B_MAX (1 << 21)   /* most sessions per call */
+#define SV_SLOTS_MAX (1 << 25) /* most row slots B * (2M + 1) per call */
 
 /* Per-session sampling profile (SDCP Sec. 4.1 "sampling"), 24 bytes,
  * 8-byte aligned; passed as a DEVICE array [B]. */
@@ -78,10 +81,24 @@ typedef struct sv_probe {
   void *rows_stop;
 } sv_probe;
 
+/* Per-session inputs of the SDCP verifier values (Sec. 6.4), 32 bytes, 8-byte
+ * aligned; passed to sv_verify_sdcp as a DEVICE array [B].  The value for
+ * 1-based position i and purpose (0 = acceptance test, 1 = additional token)
+ * is HMAC-SHA-256 keyed with seed as eight octets in network byte order, over
+ * "SDCP-VERIFY-1" || 0x00 || session_id || uint32(round) || uint32(i) ||
+ * uint8(purpose) (integers in network byte order); the first 53 bits of the
+ * MAC, most significant first, divided by 2^53. */
+typedef struct sv_sdcp_session {
+  uint8_t session_id[16]; /* the session's 16-octet identifier */
+  uint64_t seed;          /* the sampling profile's seed (Sec. 4.1) */
+  uint32_t round;         /* the round being verified (numbered from 1) */
+  uint32_t reserved;      /* ignored; set to 0 */
+} sv_sdcp_session;
+
 enum { SV_RULE_GREEDY = 1, SV_RULE_SPECULATIVE = 2 }; /* SDCP Sec. 10.2.2 */
 enum { SV_BF16 = 0, SV_FP32 = 1 };                   /* logits element type */
 
-/* Call-level return codes of sv_verify. */
+/* Call-level return codes of sv_verify and sv_verify_sdcp. */
 enum {
   SV_OK = 0,
   SV_ERR_ARG = -1,       /* null pointer, bad size or dtype, size overflow */
@@ -117,7 +134,8 @@ size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V);
  *   draft_tokens  [B, M] int32: x_i = draft_tokens[b, i-1]; entries i > m[b]
  *                 are ignored.
  *   m [B], rule [B] int32; sampling [B] sv_sampling.
- *   B >= 1, 1 <= M <= 64, 1 <= V <= SV_V_MAX; a session uses rows
+ *   1 <= B <= SV_B_MAX, 1 <= M <= 64, B * (2M + 1) <= SV_SLOTS_MAX,
+ *   1 <= V <= SV_V_MAX; a session uses rows
  *   1..m[b]+1 of the target and, for rule 2, rows 1..m[b] of the draft.
  *   seed, round: the generator key and counter for this call (SDCP rounds are
  *   numbered from 1; any value is accepted).
@@ -143,6 +161,22 @@ int sv_verify(const void *target_logits, const void *draft_logits, int32_t dtype
               const sv_sampling *sampling, int32_t B, int32_t M, int32_t V, uint64_t seed,
               uint32_t round, int32_t *accepted_len, int32_t *out_tokens, void *workspace,
               size_t workspace_bytes, const sv_probe *probe, void *stream);
+
+/*
+ * sv_verify with the verifier values of SDCP Sec. 6.4 itself: each session's
+ * acceptance tests and additional-token draw take the HMAC-SHA-256 values of
+ * sessions[b] (a DEVICE array [B] of sv_sdcp_session, caller-owned, not
+ * aliased with any output) in place of the Philox values of (seed, round);
+ * sampling[b].session_key is not used.  Every other argument, output, status
+ * and return code is as for sv_verify; the workspace size is the same.
+ * sessions == NULL returns SV_ERR_ARG.  A session's result depends only on
+ * its own rows, tokens, m, rule, sampling and sessions records.
+ */
+int sv_verify_sdcp(const void *target_logits, const void *draft_logits, int32_t dtype,
+                   const int32_t *draft_tokens, const int32_t *m, const int32_t *rule,
+                   const sv_sampling *sampling, const sv_sdcp_session *sessions, int32_t B,
+                   int32_t M, int32_t V, int32_t *accepted_len, int32_t *out_tokens,
+                   void *workspace, size_t workspace_bytes, const sv_probe *probe, void *stream);
 
 /* Text for an sv_verify return code; never NULL. */
 const char *sv_strerror(int code);

@@ -40,20 +40,40 @@ def sampling_bytes(s, device="cuda"):
     return torch.from_numpy(raw.copy()).to(device)
 
 
+def sdcp_bytes(sess, device="cuda"):
+    """[B] records of oracle.SDCP_SESSION_DTYPE as the library's 32-byte records."""
+    raw = np.ascontiguousarray(sess, dtype=oracle.SDCP_SESSION_DTYPE).view(np.uint8).reshape(len(sess), 32)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
 def run_gpu(h, probe=True, device="cuda"):
+    """h["sdcp"] (optional): [B] oracle.SDCP_SESSION_DTYPE records -> sv_verify_sdcp."""
     t = to_device(h["target"], device)
     d = to_device(h["draft"], device)
+    sess = h.get("sdcp")
     out = sv.verify(t, d, to_device(np.asarray(h["tokens"], np.int32), device),
                     to_device(np.asarray(h["m"], np.int32), device),
                     to_device(np.asarray(h["rule"], np.int32), device),
-                    sampling_bytes(h["sampling"], device), h["seed"], h["round"], probe=probe)
+                    sampling_bytes(h["sampling"], device), h["seed"], h["round"], probe=probe,
+                    sdcp_sessions=None if sess is None else sdcp_bytes(sess, device))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
 def run_oracle(h, diagnostics=True):
     return oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
-                         h["seed"], h["round"], diagnostics=diagnostics)
+                         h["seed"], h["round"], diagnostics=diagnostics,
+                         sdcp_sessions=h.get("sdcp"))
+
+
+def random_sdcp_sessions(B, rng):
+    """Random 16-octet ids, 64-bit seeds and rounds per session."""
+    s = np.zeros(B, dtype=oracle.SDCP_SESSION_DTYPE)
+    s["id"] = rng.integers(0, 256, size=(B, 16), dtype=np.uint8)
+    s["seed"] = rng.integers(0, 1 << 63, size=B, dtype=np.uint64) * np.uint64(2) + \
+        rng.integers(0, 2, size=B, dtype=np.uint64)
+    s["round"] = rng.integers(1, 1 << 32, size=B, dtype=np.uint64).astype(np.uint32)
+    return s
 
 
 def session_near_tie(o, b):

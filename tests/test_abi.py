@@ -34,7 +34,8 @@ def svlib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"sv_verify", "sv_workspace_bytes", "sv_strerror", "sv_status_str", "sv_version"} <= names
+    assert {"sv_verify", "sv_verify_sdcp", "sv_workspace_bytes", "sv_strerror", "sv_status_str",
+            "sv_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(svlib):
@@ -63,6 +64,11 @@ def test_workspace_bytes_bounds(svlib):
     assert svlib.workspace_bytes(4, 4, (1 << 24) + 1) == 0
     # grows with the batch
     assert svlib.workspace_bytes(512, 8, 1000) > svlib.workspace_bytes(256, 8, 1000)
+    # SV_B_MAX = 2^21 sessions, SV_SLOTS_MAX = 2^25 row slots B * (2M + 1)
+    assert svlib.workspace_bytes(1 << 21, 1, 10) > 0
+    assert svlib.workspace_bytes((1 << 21) + 1, 1, 10) == 0
+    assert svlib.workspace_bytes(1 << 19, 31, 10) > 0  # 2^19 * 63 slots
+    assert svlib.workspace_bytes(1 << 19, 32, 10) == 0  # 2^19 * 65 slots
 
 
 def test_verify_rejects_bad_arguments_on_the_host(svlib):
@@ -88,6 +94,35 @@ def test_verify_rejects_bad_arguments_on_the_host(svlib):
     assert call(M=65) == svlib.ERR_ARG
     assert call(V=0) == svlib.ERR_ARG
     assert call(dtype=7) == svlib.ERR_ARG
+    assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
+
+
+def test_sdcp_session_record_layout(svlib):
+    """sv_sdcp_session: id[16] at 0, seed at 16, round at 24, reserved at 28."""
+    d = svlib.SDCP_SESSION_DTYPE
+    assert d.itemsize == 32
+    assert [d.fields[n][1] for n in ("session_id", "seed", "round", "reserved")] == [0, 16, 24, 28]
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    body = re.search(r"typedef struct sv_sdcp_session \{(.*?)\} sv_sdcp_session;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(u?int\d+_t)\s+(\w+)(\[\d+\])?;", body)
+    assert fields == [("uint8_t", "session_id", "[16]"), ("uint64_t", "seed", ""),
+                      ("uint32_t", "round", ""), ("uint32_t", "reserved", "")]
+
+
+def test_verify_sdcp_rejects_bad_arguments_on_the_host(svlib):
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+    ws = svlib.workspace_bytes(2, 2, 10)
+
+    def call(sess=fake, target=fake, B=2, M=2, wsb=ws):
+        return L.sv_verify_sdcp(target, None, 0, fake, fake, fake, fake, sess, B, M, 10, fake,
+                                fake, fake, wsb, None, None)
+
+    assert call(sess=None) == svlib.ERR_ARG
+    assert call(target=None) == svlib.ERR_ARG
+    assert call(B=0) == svlib.ERR_ARG
+    assert call(M=65) == svlib.ERR_ARG
     assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
 
 

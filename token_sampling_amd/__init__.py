@@ -41,7 +41,14 @@ SAMPLING_DTYPE = np.dtype(
      ("reserved", "<u4"), ("session_key", "<u8")],
     align=True,
 )
-EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_strerror", "sv_status_str", "sv_version")
+# SDCP Sec. 6.4 inputs of the verifier values: 16-octet session id, the
+# profile's seed, the round (32 bytes, 8-aligned; sv_sdcp_session).
+SDCP_SESSION_DTYPE = np.dtype(
+    [("session_id", np.uint8, (16,)), ("seed", "<u8"), ("round", "<u4"), ("reserved", "<u4")],
+    align=True,
+)
+EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_strerror", "sv_status_str",
+            "sv_version")
 
 
 class SvError(RuntimeError):
@@ -107,6 +114,14 @@ def lib():
             ctypes.POINTER(_Probe), ctypes.c_void_p,
         ]
         L.sv_verify.restype = ctypes.c_int
+        L.sv_verify_sdcp.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify_sdcp.restype = ctypes.c_int
         L.sv_strerror.argtypes = [ctypes.c_int]
         L.sv_strerror.restype = ctypes.c_char_p
         L.sv_status_str.argtypes = [ctypes.c_int]
@@ -143,6 +158,27 @@ def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_
     return torch.from_numpy(raw.copy()).to(device)
 
 
+def make_sdcp_sessions(B, seed, round_, session_ids=None, device="cuda"):
+    """Pack per-session SDCP value inputs into the [B] x 32-byte device array.
+
+    seed and round_ are scalars or length-B sequences; session_ids is a
+    [B, 16] array of octets (default: b as the last eight octets, big-endian).
+    """
+    import torch
+
+    s = np.zeros(B, dtype=SDCP_SESSION_DTYPE)
+    if session_ids is None:
+        ids = np.zeros((B, 16), dtype=np.uint8)
+        ids[:, 8:] = np.arange(B, dtype=">u8").view(np.uint8).reshape(B, 8)
+    else:
+        ids = np.asarray(session_ids, dtype=np.uint8).reshape(B, 16)
+    s["session_id"] = ids
+    s["seed"] = seed
+    s["round"] = round_
+    raw = np.ascontiguousarray(s).view(np.uint8).reshape(B, 32)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
 def _check(t, name, dtype, shape, device):
     import torch
 
@@ -159,8 +195,8 @@ def _check(t, name, dtype, shape, device):
 
 
 def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, probe: bool = False,
-           workspace=None, out=None, stream=None, row_events=None):
-    """sv_verify on torch tensors (all on one GPU device).
+           workspace=None, out=None, stream=None, row_events=None, sdcp_sessions=None):
+    """sv_verify (or sv_verify_sdcp) on torch tensors (all on one GPU device).
 
     target [B, M+1, V] bf16/fp32, draft [B, M, V] same dtype or None, tokens
     [B, M] int32, m [B] int32, rule [B] int32, sampling [B, 24] uint8 (see
@@ -168,7 +204,9 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     [B, M+1] (int32), plus p_tok and q_tok [B, M] float64 if probe.  The call
     is asynchronous on ``stream`` (default: torch's current stream).
     row_events: optional (start, stop) or (start, mid, stop) HipEvents recorded
-        around the row kernels, mid between the top-k kernel and the other.
+        around the row kernels, mid between the single-pass kernel and the other.
+    sdcp_sessions: optional [B, 32] uint8 device array (see make_sdcp_sessions);
+        then the SDCP Sec. 6.4 values are used and seed, round_ are ignored.
     """
     import torch
 
@@ -194,6 +232,10 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     _check(sampling, "sampling", None, None, dev)
     if sampling.numel() * sampling.element_size() != 24 * B:
         raise ValueError("sampling must hold B 24-byte records")
+    if sdcp_sessions is not None:
+        _check(sdcp_sessions, "sdcp_sessions", None, None, dev)
+        if sdcp_sessions.numel() * sdcp_sessions.element_size() != 32 * B:
+            raise ValueError("sdcp_sessions must hold B 32-byte records")
 
     need = workspace_bytes(B, M, V)
     if need == 0:
@@ -222,14 +264,16 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
                                  out["q_tok"].data_ptr() if "q_tok" in out else None, *evs))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    rc = lib().sv_verify(
-        target.data_ptr(), None if draft is None else draft.data_ptr(), dt,
-        tokens.data_ptr(), m.data_ptr(), rule.data_ptr(), sampling.data_ptr(),
-        B, M, V, seed, round_,
-        out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
-        stream.cuda_stream,
-    )
+    common = (target.data_ptr(), None if draft is None else draft.data_ptr(), dt,
+              tokens.data_ptr(), m.data_ptr(), rule.data_ptr(), sampling.data_ptr())
+    tail = (out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
+            stream.cuda_stream)
+    if sdcp_sessions is None:
+        rc = lib().sv_verify(*common, B, M, V, seed, round_, *tail)
+    else:
+        rc = lib().sv_verify_sdcp(*common, sdcp_sessions.data_ptr(), B, M, V, *tail)
     if rc != OK:
-        raise SvError(f"sv_verify failed: {strerror(rc)} ({rc})")
+        name = "sv_verify" if sdcp_sessions is None else "sv_verify_sdcp"
+        raise SvError(f"{name} failed: {strerror(rc)} ({rc})")
     return out

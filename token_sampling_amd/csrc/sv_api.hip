@@ -1,11 +1,12 @@
 // sv_api.hip -- the C ABI of libspecverify (declared in include/specverify.h).
 //
-// sv_verify checks its scalar arguments on the host, carves the caller's
-// workspace and enqueues the kernels on the caller's stream:
+// sv_verify and sv_verify_sdcp check their scalar arguments on the host, carve
+// the caller's workspace and enqueue the kernels on the caller's stream:
 //   single-pass row kernel (session statuses, then each row by the top-k or
 //   the dense path) -> generic row kernel (every other row) -> finalize
 //   (acceptance, and the additional token's draw).
-// It never synchronises and never allocates.
+// With SDCP values the single-pass kernel's first workgroups also compute them.
+// Neither call synchronises or allocates.
 #include <limits.h>
 
 #include "sv_kernels.hpp"
@@ -27,6 +28,8 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + slots * kSupMax * sizeof(int32_t), 256);
   L.supp_off = off;
   off = align_up(off + slots * kSupMax * sizeof(double), 256);
+  L.unif_off = off;
+  off = align_up(off + slots * sizeof(double), 256);
   L.total = off;
   return L;
 }
@@ -34,9 +37,12 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
 static bool sizes_ok(int32_t B, int32_t M, int32_t V, int32_t dtype) {
   if (B < 1 || M < 1 || M > SV_M_MAX || V < 1 || V > SV_V_MAX) return false;
   if (dtype != SV_BF16 && dtype != SV_FP32) return false;
-  // one workgroup per row slot; element counts must fit a signed 64-bit index
+  // launches: one wave per row slot (plus one per 64 SDCP values) and 1024
+  // work-items per session must stay within a 32-bit work-item count;
+  // element counts must fit a signed 64-bit index
+  if (B > SV_B_MAX) return false;
   const unsigned long long slots = (unsigned long long)B * (2ull * (unsigned)M + 1ull);
-  if (slots > (unsigned long long)INT_MAX) return false;
+  if (slots > (unsigned long long)SV_SLOTS_MAX) return false;
   const unsigned long long elems = (unsigned long long)B * ((unsigned)M + 1ull) * (unsigned)V;
   if (elems > (unsigned long long)(LLONG_MAX / 4)) return false;
   return true;
@@ -49,20 +55,24 @@ extern "C" size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V) {
   return sv::workspace_layout(B, M, V).total;
 }
 
-extern "C" int sv_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
-                         const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
-                         const sv_sampling* sampling, int32_t B, int32_t M, int32_t V,
-                         uint64_t seed, uint32_t round, int32_t* accepted_len,
-                         int32_t* out_tokens, void* workspace, size_t workspace_bytes,
-                         const sv_probe* probe, void* stream) {
+namespace sv {
+
+// Shared by both entry points: sdcp == null takes the Philox values from
+// (seed, round); otherwise the SDCP Sec. 6.4 values of each session's record.
+static int verify_impl(const void* target_logits, const void* draft_logits, int32_t dtype,
+                       const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
+                       const sv_sampling* sampling, const sv_sdcp_session* sdcp, int32_t B,
+                       int32_t M, int32_t V, uint64_t seed, uint32_t round,
+                       int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                       size_t workspace_bytes, const sv_probe* probe, void* stream) {
   if (!target_logits || !draft_tokens || !m || !rule || !sampling || !accepted_len ||
       !out_tokens || !workspace)
     return SV_ERR_ARG;
-  if (!sv::sizes_ok(B, M, V, dtype)) return SV_ERR_ARG;
-  const sv::WorkspaceLayout L = sv::workspace_layout(B, M, V);
+  if (!sizes_ok(B, M, V, dtype)) return SV_ERR_ARG;
+  const WorkspaceLayout L = workspace_layout(B, M, V);
   if (workspace_bytes < L.total) return SV_ERR_WORKSPACE;
 
-  sv::LaunchArgs a;
+  LaunchArgs a;
   a.target = target_logits;
   a.draft = draft_logits;
   a.dtype = dtype;
@@ -80,21 +90,48 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
   a.p_tok = probe ? probe->p_tok : nullptr;
   a.q_tok = probe ? probe->q_tok : nullptr;
   char* ws = (char*)workspace;
-  a.rows = (sv::RowRec*)(ws + L.rows_off);
+  a.rows = (RowRec*)(ws + L.rows_off);
   a.sess_status = (int32_t*)(ws + L.status_off);
   a.sup_id = (int32_t*)(ws + L.supid_off);
   a.sup_p = (double*)(ws + L.supp_off);
+  a.sdcp = sdcp;
+  a.unif = sdcp ? (double*)(ws + L.unif_off) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
   if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
-  sv::launch_rows_stream(a, st);
+  launch_rows_stream(a, st);
   if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
-  sv::launch_rows_generic(a, st);
+  launch_rows_generic(a, st);
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
-  sv::launch_finalize(a, st);
+  launch_finalize(a, st);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
   return SV_OK;
+}
+
+}  // namespace sv
+
+extern "C" int sv_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                         const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
+                         const sv_sampling* sampling, int32_t B, int32_t M, int32_t V,
+                         uint64_t seed, uint32_t round, int32_t* accepted_len,
+                         int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                         const sv_probe* probe, void* stream) {
+  return sv::verify_impl(target_logits, draft_logits, dtype, draft_tokens, m, rule, sampling,
+                         nullptr, B, M, V, seed, round, accepted_len, out_tokens, workspace,
+                         workspace_bytes, probe, stream);
+}
+
+extern "C" int sv_verify_sdcp(const void* target_logits, const void* draft_logits,
+                              int32_t dtype, const int32_t* draft_tokens, const int32_t* m,
+                              const int32_t* rule, const sv_sampling* sampling,
+                              const sv_sdcp_session* sessions, int32_t B, int32_t M, int32_t V,
+                              int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                              size_t workspace_bytes, const sv_probe* probe, void* stream) {
+  if (!sessions) return SV_ERR_ARG;
+  return sv::verify_impl(target_logits, draft_logits, dtype, draft_tokens, m, rule, sampling,
+                         sessions, B, M, V, 0, 0, accepted_len, out_tokens, workspace,
+                         workspace_bytes, probe, stream);
 }
 
 extern "C" const char* sv_strerror(int code) {

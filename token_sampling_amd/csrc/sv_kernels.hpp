@@ -26,6 +26,10 @@ struct LaunchArgs {
   int32_t* sess_status; // [B], written by the single-pass row kernel
   int32_t* sup_id;      // [B, 2M+1, kSupMax] listed supports (ids ascending)
   double* sup_p;        // [B, 2M+1, kSupMax] their probabilities
+  // SDCP Sec. 6.4 verifier values (null: Philox from seed, round)
+  const sv_sdcp_session* sdcp;  // [B] per-session seed, id and round
+  double* unif;                 // [B, 2M+1]: j < M acceptance value of position j+1,
+                                // j >= M additional-token value of position j-M+1
 };
 
 // Row status written by a specialised row kernel that could not finish a row;
@@ -52,7 +56,7 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
 }
 
 struct WorkspaceLayout {
-  size_t rows_off, status_off, supid_off, supp_off, total;
+  size_t rows_off, status_off, supid_off, supp_off, unif_off, total;
 };
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);

@@ -67,7 +67,8 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
                                 const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
                                 int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
                                 double* __restrict__ q_tok, const int32_t* __restrict__ sup_id,
-                                const double* __restrict__ sup_p, int32_t* q_id, double* q_p) {
+                                const double* __restrict__ sup_p, const double* __restrict__ unif,
+                                int32_t* q_id, double* q_p) {
   const int lane = threadIdx.x;
   const int R = 2 * M + 1;
   Job job{kJobNone, 0, 0, 0, 0.0};
@@ -115,16 +116,20 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     a = a < mb ? a : mb;
     extra = rr[a].argmax;
   } else {
-    // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i))
+    // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i)); the values
+    // are SDCP's (computed by the row kernel into unif) or Philox's
+    const double* uv = unif ? unif + (size_t)b * R : nullptr;
     double u_acc = 1.0, u_add = 0.0;
-    verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc, &u_add);
+    if (uv) u_acc = lane < mb ? uv[lane] : 1.0;
+    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc, &u_add);
     const double ratio = px / qx;
     const bool acc = lane < mb && u_acc < (ratio < 1.0 ? ratio : 1.0);
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
     double ua, ud;
-    verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+    if (uv) ud = uv[M + a];
+    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
     // additional token: residual at the first rejection, else the bonus row;
     // drawn here when the rows' supports are listed, else by the sampler
     const RowRec& P = rr[a];
@@ -301,7 +306,8 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
     uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
     const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
-    const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p) {
+    const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p,
+    const double* __restrict__ unif) {
   __shared__ SampleSmem sm;
   __shared__ int32_t q_id[kSupMax];
   __shared__ double q_p[kSupMax];
@@ -310,7 +316,8 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
   if (b >= B) return;
   if (threadIdx.x < kWave) {
     const Job j = finalize_session(b, tokens, m, rule, sampling, M, seed, round, sess_status, rows,
-                                   accepted_len, out_tokens, p_tok, q_tok, sup_id, sup_p, q_id, q_p);
+                                   accepted_len, out_tokens, p_tok, q_tok, sup_id, sup_p, unif,
+                                   q_id, q_p);
     if (threadIdx.x == 0) job_s = j;
   }
   __syncthreads();
@@ -410,12 +417,14 @@ void launch_finalize(const LaunchArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_finalize<Bf16>, dim3(a.B), dim3(kSampleNT), 0, st,
                        (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
                        a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
-                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p);
+                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p,
+                       a.unif);
   } else {
     hipLaunchKernelGGL(k_finalize<F32>, dim3(a.B), dim3(kSampleNT), 0, st,
                        (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
                        a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
-                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p);
+                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p,
+                       a.unif);
   }
 }
 
