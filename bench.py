@@ -38,7 +38,7 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 KERNEL_REVISION = "stream-v2"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
-    ("b256_topk_topp", "k_rows_stream", "stream-v1"): 1_119_476_736,
+    ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
 }
 
 
