@@ -104,6 +104,12 @@ def lib():
             i32p, i32p, dp, dp, dp, dp, dp, dp,
         ]
         L.ov_verify_sdcp.restype = ctypes.c_int
+        L.ov_verify_qrows.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, i32p, i32p, i32p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp,
+        ]
+        L.ov_verify_qrows.restype = ctypes.c_int
         L.ov_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
         L.ov_sha256.restype = None
         L.ov_hmac_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p,
@@ -229,7 +235,7 @@ def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_
 
 
 def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=True,
-           sdcp_sessions=None):
+           sdcp_sessions=None, q_rows=None):
     """Run the oracle over a batch.
 
     target: [B, M+1, V] uint16 (bf16 bits) or float32; draft: [B, M, V] of the
@@ -237,7 +243,9 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     sampling [B] of ``SAMPLING_DTYPE``.  Returns a dict with accepted_len,
     out_tokens, p_tok, q_tok and (if diagnostics) d_acc, d_topp_t, d_topp_d,
     d_cdf.  With sdcp_sessions ([B] of ``SDCP_SESSION_DTYPE``) the uniforms are
-    SDCP's HMAC-SHA-256 values and seed, round_ are ignored.
+    SDCP's HMAC-SHA-256 values and seed, round_ are ignored.  With q_rows
+    ([B, M, V] float32 probabilities, SDCP's q_rows) the draft distributions
+    are those rows and draft must be None; d_topp_d is then not computed.
     """
     target = np.ascontiguousarray(target)
     _, dt = _as_row(target[..., :1].reshape(-1)[:1]) if target.size else (None, BF16)
@@ -246,6 +254,10 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     if draft is not None:
         draft = np.ascontiguousarray(draft)
         assert draft.dtype == target.dtype and draft.shape == (B, M, V)
+    if q_rows is not None:
+        assert draft is None, "give draft logits or q_rows, not both"
+        q_rows = np.ascontiguousarray(q_rows, dtype=np.float32)
+        assert q_rows.shape == (B, M, V)
     tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, M)
     m = np.ascontiguousarray(m, dtype=np.int32).reshape(B)
     rule = np.ascontiguousarray(rule, dtype=np.int32).reshape(B)
@@ -272,7 +284,17 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     common = (target.ctypes.data, None if draft is None else draft.ctypes.data, dt,
               _ptr(tokens, ctypes.c_int32), _ptr(m, ctypes.c_int32), _ptr(rule, ctypes.c_int32),
               sampling.ctypes.data)
-    if sdcp_sessions is None:
+    sess = None
+    if sdcp_sessions is not None:
+        sess = np.ascontiguousarray(sdcp_sessions, dtype=SDCP_SESSION_DTYPE).reshape(B)
+    if q_rows is not None:
+        no_d_topp_d = outs[:6] + outs[7:]
+        rc = lib().ov_verify_qrows(target.ctypes.data, dt, q_rows.ctypes.data, *common[3:],
+                                   None if sess is None else sess.ctypes.data, B, M, V, seed,
+                                   round_, *no_d_topp_d)
+        if "d_topp_d" in out:
+            out["d_topp_d"][:] = np.inf
+    elif sdcp_sessions is None:
         rc = lib().ov_verify(*common, B, M, V, seed, round_, *outs)
     else:
         sess = np.ascontiguousarray(sdcp_sessions, dtype=SDCP_SESSION_DTYPE).reshape(B)

@@ -39,7 +39,14 @@
  *    0x00 || session id (16 octets) || uint32(round) || uint32(i) ||
  *    uint8(purpose); the first 53 bits of the MAC (most significant first)
  *    times 2^-53;
- *  - q_i is the same sampling profile applied to the draft logits row i;
+ *  - ov_verify, ov_verify_sdcp: q_i is the same sampling profile applied to
+ *    the draft logits row i;
+ *  - ov_verify_qrows: q_i is the published q_rows row (SDCP Sec. 5.2), binary32
+ *    values widened exactly and used as given (no profile, no
+ *    renormalisation).  q_i(x_i) must be a positive finite number, checked at
+ *    every position before any draw (else BAD_PROPOSAL); the residual reads
+ *    q_i(y) only where p_i(y) > 0, and an entry read there that is negative,
+ *    NaN or infinite makes the session fail with BAD_PROPOSAL;
  *  - top-k keeps exactly k tokens in the order (logit desc, id asc);
  *  - top-p keeps the shortest non-empty prefix of that order whose mass C
  *    satisfies 1000*C >= top_p_milli * Z_k (Z_k = mass after top-k);
@@ -466,8 +473,9 @@ static void set_if(double *arr, int64_t idx, double v) {
  * One session.  Returns a = accepted count (>= 0) or a negative status; on
  * success writes out[0..a] (a accepted tokens, then the additional token).
  */
-static int verify_session(int64_t b, const void *target, const void *draft, int dtype,
-                          const int32_t *x, int m, int rule, const ov_sampling *s, int M, int V,
+static int verify_session(int64_t b, const void *target, const void *draft, const float *qrows,
+                          int dtype, const int32_t *x, int m, int rule, const ov_sampling *s,
+                          int M, int V,
                           const ov_rng *g, int32_t *out, double *p_tok,
                           double *q_tok, double *d_acc, double *d_topp_t, double *d_topp_d,
                           double *d_cdf, ov_scratch *sc) {
@@ -477,7 +485,7 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
       s->top_p_milli > 1000)
     return OV_S_BAD_PROFILE;
   /* SDCP Sec. 6.3 step 5: no q rows for a rule that needs them */
-  if (rule == OV_RULE_SPECULATIVE && draft == NULL) return OV_S_Q_UNAVAILABLE;
+  if (rule == OV_RULE_SPECULATIVE && draft == NULL && qrows == NULL) return OV_S_Q_UNAVAILABLE;
   for (int i = 0; i < m; ++i)
     if (x[i] < 0 || x[i] >= V) return OV_S_BAD_PROPOSAL;
 
@@ -489,7 +497,7 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
     load_row(target, dtype, trow0 + i - 1, V, sc->l);
     if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
   }
-  if (rule == OV_RULE_SPECULATIVE)
+  if (rule == OV_RULE_SPECULATIVE && qrows == NULL)
     for (int i = 1; i <= m; ++i) {
       load_row(draft, dtype, drow0 + i - 1, V, sc->l);
       if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
@@ -515,15 +523,22 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
    * checked before any random value is drawn. */
   double qx[64];
   for (int i = 1; i <= m; ++i) {
-    double dt;
-    load_row(draft, dtype, drow0 + i - 1, V, sc->l);
-    profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
-    set_if(d_topp_d, b * (int64_t)M + i - 1, dt);
-    qx[i - 1] = sc->q[x[i - 1]];
+    if (qrows) {
+      /* SDCP Sec. 5.2: q_i is the published row itself (binary32) */
+      qx[i - 1] = (double)qrows[(drow0 + i - 1) * (int64_t)V + x[i - 1]];
+    } else {
+      double dt;
+      load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+      profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+      set_if(d_topp_d, b * (int64_t)M + i - 1, dt);
+      qx[i - 1] = sc->q[x[i - 1]];
+    }
     set_if(q_tok, b * (int64_t)M + i - 1, qx[i - 1]);
   }
+  /* a published q_i(x_i) must be a positive number: zero, negative, NaN or
+   * infinite values are all unusable proposals */
   for (int i = 0; i < m; ++i)
-    if (qx[i] == 0.0) return OV_S_BAD_PROPOSAL;
+    if (!(qx[i] > 0.0) || isinf(qx[i])) return OV_S_BAD_PROPOSAL;
 
   /* Rule 2, positions in order: accept x_i if u < min(1, p_i(x_i)/q_i(x_i)). */
   int a = m, decided = 0;
@@ -546,8 +561,24 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
       continue;
     }
     /* first rejection: additional token from norm(max(0, p_i - q_i)) */
-    load_row(draft, dtype, drow0 + i - 1, V, sc->l);
-    profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+    if (qrows) {
+      /* the residual reads q_i(y) only where p_i(y) > 0 (elsewhere its weight
+       * is zero for any probability q_i(y)); an entry read there must be a
+       * finite non-negative number */
+      const float *qr = qrows + (drow0 + i - 1) * (int64_t)V;
+      for (int y = 0; y < V; ++y) {
+        if (sc->p[y] > 0.0) {
+          const double qy = (double)qr[y];
+          if (!(qy >= 0.0) || isinf(qy)) return OV_S_BAD_PROPOSAL;
+          sc->q[y] = qy;
+        } else {
+          sc->q[y] = 0.0;
+        }
+      }
+    } else {
+      load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+      profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+    }
     double dc;
     out[i - 1] = residual_pick(sc->p, sc->q, V,
                                rng_uniform(g, (uint32_t)i, 1), sc->w, &dc);
@@ -578,7 +609,8 @@ static int verify_session(int64_t b, const void *target, const void *draft, int 
  * d_topp_t [B, M+1], d_topp_d, d_cdf [B].
  * Returns OV_OK or OV_ERR_*.
  */
-static int verify_batch(const void *target, const void *draft, int dtype, const int32_t *tokens,
+static int verify_batch(const void *target, const void *draft, const float *qrows, int dtype,
+              const int32_t *tokens,
               const int32_t *m, const int32_t *rule, const ov_sampling *sampling, int64_t B,
               int M, int V, uint64_t seed, uint32_t round, const ov_sdcp_session *sdcp,
               int32_t *accepted_len,
@@ -613,7 +645,7 @@ static int verify_batch(const void *target, const void *draft, int dtype, const 
     set_if(d_cdf, b, INFINITY);
 
     const ov_rng g = {seed, sampling[b].session_key, round, sdcp ? &sdcp[b] : NULL};
-    int a = verify_session(b, target, draft, dtype, tokens + b * (int64_t)M, m[b], rule[b],
+    int a = verify_session(b, target, draft, qrows, dtype, tokens + b * (int64_t)M, m[b], rule[b],
                            &sampling[b], M, V, &g, out, p_tok, q_tok, d_acc, d_topp_t,
                            d_topp_d, d_cdf, &sc);
     accepted_len[b] = a;
@@ -634,8 +666,9 @@ int ov_verify(const void *target, const void *draft, int dtype, const int32_t *t
               int M, int V, uint64_t seed, uint32_t round, int32_t *accepted_len,
               int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
               double *d_topp_t, double *d_topp_d, double *d_cdf) {
-  return verify_batch(target, draft, dtype, tokens, m, rule, sampling, B, M, V, seed, round, NULL,
-                      accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d, d_cdf);
+  return verify_batch(target, draft, NULL, dtype, tokens, m, rule, sampling, B, M, V, seed, round,
+                      NULL, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
+                      d_cdf);
 }
 
 /* The same batched step with the uniforms of SDCP Sec. 6.4 (HMAC-SHA-256);
@@ -646,6 +679,21 @@ int ov_verify_sdcp(const void *target, const void *draft, int dtype, const int32
                    int32_t *accepted_len, int32_t *out_tokens, double *p_tok, double *q_tok,
                    double *d_acc, double *d_topp_t, double *d_topp_d, double *d_cdf) {
   if (!sessions) return OV_ERR_ARG;
-  return verify_batch(target, draft, dtype, tokens, m, rule, sampling, B, M, V, 0, 0, sessions,
-                      accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d, d_cdf);
+  return verify_batch(target, draft, NULL, dtype, tokens, m, rule, sampling, B, M, V, 0, 0,
+                      sessions, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
+                      d_cdf);
+}
+
+/* The batched step with the draft distributions given as SDCP q_rows (Sec.
+ * 5.2): qrows [B, M, V] binary32 probabilities, row i of session b at
+ * qrows[b, i-1, :], used as published (no profile, no renormalisation).
+ * sessions: SDCP values per session, or NULL for Philox from (seed, round). */
+int ov_verify_qrows(const void *target, int dtype, const float *qrows, const int32_t *tokens,
+                    const int32_t *m, const int32_t *rule, const ov_sampling *sampling,
+                    const ov_sdcp_session *sessions, int64_t B, int M, int V, uint64_t seed,
+                    uint32_t round, int32_t *accepted_len, int32_t *out_tokens, double *p_tok,
+                    double *q_tok, double *d_acc, double *d_topp_t, double *d_cdf) {
+  return verify_batch(target, NULL, qrows, dtype, tokens, m, rule, sampling, B, M, V, seed, round,
+                      sessions, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, NULL,
+                      d_cdf);
 }
