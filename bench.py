@@ -46,9 +46,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s: float, sdcp_raw=None):
+def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None):
     """Time the oracle on the first sessions of the workload (bounded sample).
-    sdcp_raw: the [B, 32] session records (numpy uint8) when SDCP values are used."""
+    sdcp_raw: the [B, 32] session records (numpy uint8) when SDCP values are used;
+    q_rows: the [B, M, V] published draft rows (device tensor) in q-rows mode."""
     import numpy as np
 
     import oracle
@@ -65,10 +66,14 @@ def cpu_baseline(w, budget_s: float, sdcp_raw=None):
     while done_sessions < w.B and elapsed < budget_s:
         idx = list(range(done_sessions, min(w.B, done_sessions + n)))
         h = W.to_numpy(w, sessions=idx)
+        qh = None
+        if q_rows is not None:
+            qh = q_rows[idx[0]:idx[-1] + 1].cpu().numpy()
+            h["draft"] = None
         t0 = time.perf_counter()
         oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
                       h["seed"], h["round"], diagnostics=False,
-                      sdcp_sessions=None if sdcp is None else sdcp[idx])
+                      sdcp_sessions=None if sdcp is None else sdcp[idx], q_rows=qh)
         dt = time.perf_counter() - t0
         elapsed += dt
         positions += int((np.asarray(h["m"], dtype=np.int64) + 1).sum())
@@ -102,6 +107,9 @@ def main():
     ap.add_argument("--sdcp", action="store_true",
                     help="time sv_verify_sdcp: the SDCP HMAC-SHA-256 verifier values from "
                          "per-session records (seeded random ids and seeds) instead of Philox")
+    ap.add_argument("--qrows", action="store_true",
+                    help="time sv_verify_qrows: draft distributions as published binary32 rows "
+                         "(the synthetic drafter's own distribution) instead of draft logits")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -138,9 +146,13 @@ def main():
         ids = np.random.default_rng(w.seed & 0xFFFFFFFF).integers(0, 256, (B, 16), dtype=np.uint8)
         sdcp = sv.make_sdcp_sessions(B, seed=w.seed, round_=w.round, session_ids=ids, device=dev)
 
+    q_rows = w.drafter_q_rows() if args.qrows else None
+    draft = None if args.qrows else w.draft
+
     def step(ev=None):
-        sv.verify(w.target, w.draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
-                  workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp)
+        sv.verify(w.target, draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
+                  workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp,
+                  q_rows=q_rows)
 
     for _ in range(args.warmup):
         step()
@@ -165,7 +177,7 @@ def main():
 
     # the dominant kernel: the row kernel that takes longer; its algorithmic
     # bytes are the rows it handles
-    split = w.row_bytes_by_kernel()
+    split = w.row_bytes_by_kernel(q_rows=args.qrows)
     kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
                           else ("k_rows_generic", generic_ms, split["generic"]))
     if args.copy_calibration:
@@ -179,7 +191,8 @@ def main():
 
     a = out["accepted_len"].cpu()
     achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = None if args.sdcp else MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
+    traffic = None if (args.sdcp or args.qrows) else \
+        MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
     result = {
         "metric": METRIC,
         "value": P / (ms_per_step * 1e-3),
@@ -197,7 +210,8 @@ def main():
             "workload": args.workload, "B": B, "M": M, "V": V,
             "logits": "bf16" if w.target.dtype == torch.bfloat16 else "fp32",
             "uniforms": "sdcp-hmac-sha256" if args.sdcp else "philox4x64-10",
-            "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(),
+            "draft": "q_rows fp32" if args.qrows else "logits",
+            "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(q_rows=args.qrows),
             "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),
         },
@@ -211,7 +225,7 @@ def main():
     if args.cpu_budget > 0:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(
-            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy())
+            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

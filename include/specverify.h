@@ -98,7 +98,7 @@ typedef struct sv_sdcp_session {
 enum { SV_RULE_GREEDY = 1, SV_RULE_SPECULATIVE = 2 }; /* SDCP Sec. 10.2.2 */
 enum { SV_BF16 = 0, SV_FP32 = 1 };                   /* logits element type */
 
-/* Call-level return codes of sv_verify and sv_verify_sdcp. */
+/* Call-level return codes of sv_verify, sv_verify_sdcp and sv_verify_qrows. */
 enum {
   SV_OK = 0,
   SV_ERR_ARG = -1,       /* null pointer, bad size or dtype, size overflow */
@@ -177,6 +177,31 @@ int sv_verify_sdcp(const void *target_logits, const void *draft_logits, int32_t 
                    const sv_sampling *sampling, const sv_sdcp_session *sessions, int32_t B,
                    int32_t M, int32_t V, int32_t *accepted_len, int32_t *out_tokens,
                    void *workspace, size_t workspace_bytes, const sv_probe *probe, void *stream);
+
+/*
+ * sv_verify with the draft distributions given as SDCP q_rows (Sec. 5.2):
+ * q_rows [B, M, V] binary32 DEVICE array (caller-owned), row i of session b at
+ * q_rows[b, i-1, :], the distribution x_i was drawn from.  The rows are used as
+ * published: no profile, no renormalisation, values widened exactly to
+ * binary64.  No draft logits are read.  q_rows may be NULL when no session uses
+ * rule 2 (a rule-2 session then fails with SV_S_Q_UNAVAILABLE).
+ * Reads: q_i(x_i) at every position i <= m[b], checked before any draw (Sec.
+ * 6.3 step 5): a value that is not a positive finite number fails the session
+ * with SV_S_BAD_PROPOSAL.  At the first rejection, the residual max(0, p - q)
+ * reads q(y) only where p(y) > 0 (its weight is zero elsewhere); an entry read
+ * there that is negative, NaN or infinite fails the session with
+ * SV_S_BAD_PROPOSAL (found only when that row is the residual's).  Other
+ * entries are never read.  The probe's q_tok holds the widened q_i(x_i).
+ * sessions: SDCP value records as for sv_verify_sdcp, or NULL for the Philox
+ * values of (seed, round) as for sv_verify.  Every other argument, output,
+ * status and return code is as for sv_verify; the workspace size is the same.
+ */
+int sv_verify_qrows(const void *target_logits, int32_t dtype, const float *q_rows,
+                    const int32_t *draft_tokens, const int32_t *m, const int32_t *rule,
+                    const sv_sampling *sampling, const sv_sdcp_session *sessions, int32_t B,
+                    int32_t M, int32_t V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    const sv_probe *probe, void *stream);
 
 /* Text for an sv_verify return code; never NULL. */
 const char *sv_strerror(int code);

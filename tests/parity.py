@@ -47,15 +47,18 @@ def sdcp_bytes(sess, device="cuda"):
 
 
 def run_gpu(h, probe=True, device="cuda"):
-    """h["sdcp"] (optional): [B] oracle.SDCP_SESSION_DTYPE records -> sv_verify_sdcp."""
+    """h["sdcp"] (optional): [B] oracle.SDCP_SESSION_DTYPE records -> sv_verify_sdcp;
+    h["q_rows"] (optional): [B, M, V] float32 published draft rows -> sv_verify_qrows."""
     t = to_device(h["target"], device)
     d = to_device(h["draft"], device)
+    q = h.get("q_rows")
     sess = h.get("sdcp")
     out = sv.verify(t, d, to_device(np.asarray(h["tokens"], np.int32), device),
                     to_device(np.asarray(h["m"], np.int32), device),
                     to_device(np.asarray(h["rule"], np.int32), device),
                     sampling_bytes(h["sampling"], device), h["seed"], h["round"], probe=probe,
-                    sdcp_sessions=None if sess is None else sdcp_bytes(sess, device))
+                    sdcp_sessions=None if sess is None else sdcp_bytes(sess, device),
+                    q_rows=None if q is None else to_device(np.asarray(q, np.float32), device))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -63,7 +66,7 @@ def run_gpu(h, probe=True, device="cuda"):
 def run_oracle(h, diagnostics=True):
     return oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
                          h["seed"], h["round"], diagnostics=diagnostics,
-                         sdcp_sessions=h.get("sdcp"))
+                         sdcp_sessions=h.get("sdcp"), q_rows=h.get("q_rows"))
 
 
 def random_sdcp_sessions(B, rng):

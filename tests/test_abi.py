@@ -34,8 +34,8 @@ def svlib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"sv_verify", "sv_verify_sdcp", "sv_workspace_bytes", "sv_strerror", "sv_status_str",
-            "sv_version"} <= names
+    assert {"sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_workspace_bytes", "sv_strerror",
+            "sv_status_str", "sv_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(svlib):
@@ -123,6 +123,26 @@ def test_verify_sdcp_rejects_bad_arguments_on_the_host(svlib):
     assert call(target=None) == svlib.ERR_ARG
     assert call(B=0) == svlib.ERR_ARG
     assert call(M=65) == svlib.ERR_ARG
+    assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
+
+
+def test_verify_qrows_rejects_bad_arguments_on_the_host(svlib):
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+    ws = svlib.workspace_bytes(2, 2, 10)
+
+    def call(target=fake, tokens=fake, dtype=0, B=2, M=2, V=10, wsb=ws, wsp=fake):
+        # q_rows and sessions may be NULL; no kernel is reached in these calls
+        return L.sv_verify_qrows(target, dtype, None, tokens, fake, fake, fake, None, B, M, V, 0,
+                                 1, fake, fake, wsp, wsb, None, None)
+
+    assert call(target=None) == svlib.ERR_ARG
+    assert call(tokens=None) == svlib.ERR_ARG
+    assert call(wsp=None) == svlib.ERR_ARG
+    assert call(dtype=3) == svlib.ERR_ARG
+    assert call(B=0) == svlib.ERR_ARG
+    assert call(M=65) == svlib.ERR_ARG
+    assert call(V=0) == svlib.ERR_ARG
     assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
 
 

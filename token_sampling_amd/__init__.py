@@ -47,8 +47,8 @@ SDCP_SESSION_DTYPE = np.dtype(
     [("session_id", np.uint8, (16,)), ("seed", "<u8"), ("round", "<u4"), ("reserved", "<u4")],
     align=True,
 )
-EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_strerror", "sv_status_str",
-            "sv_version")
+EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_strerror",
+            "sv_status_str", "sv_version")
 
 
 class SvError(RuntimeError):
@@ -122,6 +122,14 @@ def lib():
             ctypes.POINTER(_Probe), ctypes.c_void_p,
         ]
         L.sv_verify_sdcp.restype = ctypes.c_int
+        L.sv_verify_qrows.argtypes = [
+            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify_qrows.restype = ctypes.c_int
         L.sv_strerror.argtypes = [ctypes.c_int]
         L.sv_strerror.restype = ctypes.c_char_p
         L.sv_status_str.argtypes = [ctypes.c_int]
@@ -195,8 +203,10 @@ def _check(t, name, dtype, shape, device):
 
 
 def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, probe: bool = False,
-           workspace=None, out=None, stream=None, row_events=None, sdcp_sessions=None):
-    """sv_verify (or sv_verify_sdcp) on torch tensors (all on one GPU device).
+           workspace=None, out=None, stream=None, row_events=None, sdcp_sessions=None,
+           q_rows=None):
+    """sv_verify, sv_verify_sdcp or sv_verify_qrows on torch tensors (all on one
+    GPU device).
 
     target [B, M+1, V] bf16/fp32, draft [B, M, V] same dtype or None, tokens
     [B, M] int32, m [B] int32, rule [B] int32, sampling [B, 24] uint8 (see
@@ -207,6 +217,8 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
         around the row kernels, mid between the single-pass kernel and the other.
     sdcp_sessions: optional [B, 32] uint8 device array (see make_sdcp_sessions);
         then the SDCP Sec. 6.4 values are used and seed, round_ are ignored.
+    q_rows: optional [B, M, V] float32 draft distributions (SDCP q_rows) in place
+        of draft logits (draft must then be None): sv_verify_qrows.
     """
     import torch
 
@@ -232,6 +244,10 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     _check(sampling, "sampling", None, None, dev)
     if sampling.numel() * sampling.element_size() != 24 * B:
         raise ValueError("sampling must hold B 24-byte records")
+    if q_rows is not None:
+        if draft is not None:
+            raise ValueError("give draft logits or q_rows, not both")
+        _check(q_rows, "q_rows", torch.float32, (B, M, V), dev)
     if sdcp_sessions is not None:
         _check(sdcp_sessions, "sdcp_sessions", None, None, dev)
         if sdcp_sessions.numel() * sdcp_sessions.element_size() != 32 * B:
@@ -269,11 +285,17 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     tail = (out["accepted_len"].data_ptr(), out["out_tokens"].data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
             stream.cuda_stream)
-    if sdcp_sessions is None:
+    sess = None if sdcp_sessions is None else sdcp_sessions.data_ptr()
+    if q_rows is not None:
+        name = "sv_verify_qrows"
+        rc = lib().sv_verify_qrows(target.data_ptr(), dt, q_rows.data_ptr(), *common[3:], sess,
+                                   B, M, V, seed, round_, *tail)
+    elif sdcp_sessions is None:
+        name = "sv_verify"
         rc = lib().sv_verify(*common, B, M, V, seed, round_, *tail)
     else:
-        rc = lib().sv_verify_sdcp(*common, sdcp_sessions.data_ptr(), B, M, V, *tail)
+        name = "sv_verify_sdcp"
+        rc = lib().sv_verify_sdcp(*common, sess, B, M, V, *tail)
     if rc != OK:
-        name = "sv_verify" if sdcp_sessions is None else "sv_verify_sdcp"
         raise SvError(f"{name} failed: {strerror(rc)} ({rc})")
     return out

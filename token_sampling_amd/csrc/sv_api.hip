@@ -59,8 +59,8 @@ namespace sv {
 
 // Shared by both entry points: sdcp == null takes the Philox values from
 // (seed, round); otherwise the SDCP Sec. 6.4 values of each session's record.
-static int verify_impl(const void* target_logits, const void* draft_logits, int32_t dtype,
-                       const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
+static int verify_impl(const void* target_logits, const void* draft_logits, const float* q_rows,
+                       int32_t dtype, const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
                        const sv_sampling* sampling, const sv_sdcp_session* sdcp, int32_t B,
                        int32_t M, int32_t V, uint64_t seed, uint32_t round,
                        int32_t* accepted_len, int32_t* out_tokens, void* workspace,
@@ -75,6 +75,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, int3
   LaunchArgs a;
   a.target = target_logits;
   a.draft = draft_logits;
+  a.qrows = q_rows;
   a.dtype = dtype;
   a.tokens = draft_tokens;
   a.m = m;
@@ -117,9 +118,9 @@ extern "C" int sv_verify(const void* target_logits, const void* draft_logits, in
                          uint64_t seed, uint32_t round, int32_t* accepted_len,
                          int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                          const sv_probe* probe, void* stream) {
-  return sv::verify_impl(target_logits, draft_logits, dtype, draft_tokens, m, rule, sampling,
-                         nullptr, B, M, V, seed, round, accepted_len, out_tokens, workspace,
-                         workspace_bytes, probe, stream);
+  return sv::verify_impl(target_logits, draft_logits, nullptr, dtype, draft_tokens, m, rule,
+                         sampling, nullptr, B, M, V, seed, round, accepted_len, out_tokens,
+                         workspace, workspace_bytes, probe, stream);
 }
 
 extern "C" int sv_verify_sdcp(const void* target_logits, const void* draft_logits,
@@ -129,8 +130,19 @@ extern "C" int sv_verify_sdcp(const void* target_logits, const void* draft_logit
                               int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                               size_t workspace_bytes, const sv_probe* probe, void* stream) {
   if (!sessions) return SV_ERR_ARG;
-  return sv::verify_impl(target_logits, draft_logits, dtype, draft_tokens, m, rule, sampling,
-                         sessions, B, M, V, 0, 0, accepted_len, out_tokens, workspace,
+  return sv::verify_impl(target_logits, draft_logits, nullptr, dtype, draft_tokens, m, rule,
+                         sampling, sessions, B, M, V, 0, 0, accepted_len, out_tokens, workspace,
+                         workspace_bytes, probe, stream);
+}
+
+extern "C" int sv_verify_qrows(const void* target_logits, int32_t dtype, const float* q_rows,
+                               const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
+                               const sv_sampling* sampling, const sv_sdcp_session* sessions,
+                               int32_t B, int32_t M, int32_t V, uint64_t seed, uint32_t round,
+                               int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                               size_t workspace_bytes, const sv_probe* probe, void* stream) {
+  return sv::verify_impl(target_logits, nullptr, q_rows, dtype, draft_tokens, m, rule, sampling,
+                         sessions, B, M, V, seed, round, accepted_len, out_tokens, workspace,
                          workspace_bytes, probe, stream);
 }
 

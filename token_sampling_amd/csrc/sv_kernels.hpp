@@ -8,7 +8,8 @@ namespace sv {
 
 struct LaunchArgs {
   const void* target;
-  const void* draft;  // may be null
+  const void* draft;   // draft logits, or null (no draft logits are read)
+  const float* qrows;  // SDCP q_rows [B, M, V] in place of draft logits, or null
   int32_t dtype;
   const int32_t* tokens;
   const int32_t* m;

@@ -202,7 +202,7 @@ __device__ void profile_generic(const typename Tr::elem_t* row, int V, const sv_
 template <class Tr>
 __device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
                             const sv_sampling* sampling, const int32_t* sess_status, int M, int V,
-                            const RowRec* rows) {
+                            const RowRec* rows, bool draft_logits) {
   const int R = 2 * M + 1;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
@@ -211,7 +211,9 @@ __device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
   const int rl = rule[b];
   const bool is_target = slot <= M;
   const int i = is_target ? slot + 1 : slot - M;  // 1-based position
-  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return false;
+  // draft rows are profiled only when draft logits are given (not with q rows)
+  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb || !draft_logits))
+    return false;
   const sv_sampling smp = sampling[b];
   if (row_uses_topk_kernel(Tr::kDtype, rl, smp) || row_uses_dense_kernel(Tr::kDtype, rl, smp, V))
     return rows[slot_g].status == kRowFallback;
@@ -241,7 +243,8 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
   for (int base = (int)blockIdx.x * per; base < end; base += kNT) {
     const int slot_g = base + (int)threadIdx.x;
     const bool need = slot_g < end &&
-                      generic_row<Tr>(slot_g, m, rule, sampling, sess_status, M, V, rows);
+                      generic_row<Tr>(slot_g, m, rule, sampling, sess_status, M, V, rows,
+                                      draft != nullptr);
     const uint64_t mask = __ballot(need);
     __syncthreads();  // the previous round's list is consumed
     if (lane == 0) wave_cnt[wid] = __builtin_popcountll(mask);

@@ -94,7 +94,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
   const int rl = rule[b];
   const bool is_target = slot <= M;
   const int i = is_target ? slot + 1 : slot - M;  // 1-based position
-  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb)) return;
+  // draft rows are profiled only when draft logits are given (not with q rows)
+  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb || draft == nullptr))
+    return;
   const sv_sampling smp = sampling[b];
   const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
   const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
@@ -118,7 +120,7 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
                      (const uint16_t*)a.draft, a.dtype, a.tokens, a.m, a.rule, a.sampling,
-                     a.draft != nullptr ? 1 : 0, a.B, a.M, a.V, a.sess_status, a.rows, a.sup_id,
+                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V, a.sess_status, a.rows, a.sup_id,
                      a.sup_p, a.sdcp, a.unif, n_value_blocks);
 }
 

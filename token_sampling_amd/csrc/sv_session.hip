@@ -13,33 +13,43 @@ namespace {
 
 // Inverse CDF over a listed support (ids ascending): the additional token is
 // the smallest id whose running mass exceeds u * S (the largest id with mass
-// if rounding leaves none).  With a q list the weights are the residual
-// max(0, p - q); a residual without mass falls back to p.  One wave; lane j
-// holds entry j.
+// if rounding leaves none).  With a q list (qid_g) or a published q row (qrow)
+// the weights are the residual max(0, p - q), zero where p is zero; a residual
+// without mass falls back to p.  A published row is read only at the listed ids
+// with p > 0, and *bad is set if such an entry is not a finite non-negative
+// number.  One wave; lane j holds entry j.
 __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
-                               const int32_t* qid_g, const double* qp_g, int nq, double u,
-                               int32_t* q_id, double* q_p) {
+                               const int32_t* qid_g, const double* qp_g, int nq,
+                               const float* qrow, double u, int32_t* q_id, double* q_p,
+                               bool* bad) {
   const int lane = __lane_id();
   const int32_t y = lane < np ? p_id[lane] : 0x7FFFFFFF;
   const double p = lane < np ? p_pr[lane] : 0.0;
   double w = p;
-  if (qid_g) {
-    if (lane < nq) {
+  if (qid_g || qrow) {
+    double q = 0.0;
+    if (qrow) {
+      const bool read = lane < np && p > 0.0;
+      q = read ? (double)qrow[y] : 0.0;
+      if (__any(read && !(q >= 0.0 && q < INFINITY))) *bad = true;
+    } else {
+      if (lane < nq) {
       q_id[lane] = qid_g[lane];
       q_p[lane] = qp_g[lane];
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    // q(y): binary search of y in the q list
-    int lo = 0, hi = nq;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (q_id[mid] < y) lo = mid + 1;
-      else hi = mid;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      // q(y): binary search of y in the q list
+      int lo = 0, hi = nq;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (q_id[mid] < y) lo = mid + 1;
+        else hi = mid;
+      }
+      q = (lane < np && lo < nq && q_id[lo] == y) ? q_p[lo] : 0.0;
     }
-    const double q = (lane < np && lo < nq && q_id[lo] == y) ? q_p[lo] : 0.0;
     const double d = p - q;
-    w = d > 0.0 ? d : 0.0;
+    w = (p > 0.0 && d > 0.0) ? d : 0.0;
     double S = w;
     for (int off = kWave / 2; off > 0; off >>= 1) S += __shfl_xor(S, off, kWave);
     if (S == 0.0) w = p;  // rounding only
@@ -57,12 +67,32 @@ __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
   return __shfl(y, j, kWave);
 }
 
+// A failed session's outputs, by one wave: status, no tokens, no probes.  The
+// per-session kernel's first wave writes these and the session's other
+// outputs with the same lane-to-address mapping, so a later failure
+// overwrites them in each lane's program order.
+__device__ void write_failed(int b, int st, int M, int32_t* __restrict__ accepted_len,
+                             int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
+                             double* __restrict__ q_tok) {
+  const int lane = threadIdx.x;
+  int32_t* out = out_tokens + (size_t)b * (M + 1);
+  if (lane == 0) accepted_len[b] = st;
+  for (int j = lane; j <= M; j += kWave) out[j] = -1;
+  for (int j = lane; j < M; j += kWave) {
+    if (p_tok) p_tok[(size_t)b * M + j] = -1.0;
+    if (q_tok) q_tok[(size_t)b * M + j] = -1.0;
+  }
+}
+
 // SDCP Sec. 6.4, for session b, by one wave: lane i examines position i+1.
+// With published q rows (qrows != null) q_i(x_i) is read from them and no
+// draft row record exists.
 // Writes accepted_len, out_tokens and the probes; returns the draw left for
 // the whole workgroup (kJobNone when the extra token is already written).
 __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
                                 const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
-                                const sv_sampling* __restrict__ sampling, int M, uint64_t seed,
+                                const sv_sampling* __restrict__ sampling, int M, int V,
+                                const float* __restrict__ qrows, uint64_t seed,
                                 uint32_t round, const int32_t* __restrict__ sess_status,
                                 const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
                                 int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
@@ -83,26 +113,23 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
   if (st == 0) {
     bool bad = false;
     for (int j = lane; j <= mb; j += kWave) bad |= rr[j].status != 0;
-    if (rl == SV_RULE_SPECULATIVE && lane < mb) bad |= rr[M + 1 + lane].status != 0;
+    if (rl == SV_RULE_SPECULATIVE && !qrows && lane < mb) bad |= rr[M + 1 + lane].status != 0;
     if (__any(bad)) st = SV_S_BAD_LOGITS;
   }
   // Sec. 6.3 step 5: q_i(x_i) != 0 at every position, before any draw
+  // (x is in [0, V) once the session's checks passed); a q value that is not a
+  // positive finite number (only a published row can hold one) is unusable
   double qx = 1.0, px = -1.0;
   if (st == 0 && rl == SV_RULE_SPECULATIVE) {
     if (lane < mb) {
-      qx = rr[M + 1 + lane].ptok;
+      qx = qrows ? (double)qrows[((size_t)b * M + lane) * (size_t)V + x] : rr[M + 1 + lane].ptok;
       px = rr[lane].ptok;
     }
-    if (__any(lane < mb && qx == 0.0)) st = SV_S_BAD_PROPOSAL;
+    if (__any(lane < mb && !(qx > 0.0 && qx < INFINITY))) st = SV_S_BAD_PROPOSAL;
   }
 
   if (st < 0) {
-    if (lane == 0) accepted_len[b] = st;
-    for (int j = lane; j <= M; j += kWave) out[j] = -1;
-    for (int j = lane; j < M; j += kWave) {
-      if (p_tok) p_tok[(size_t)b * M + j] = -1.0;
-      if (q_tok) q_tok[(size_t)b * M + j] = -1.0;
-    }
+    write_failed(b, st, M, accepted_len, out_tokens, p_tok, q_tok);
     return job;
   }
 
@@ -133,13 +160,19 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     // additional token: residual at the first rejection, else the bonus row;
     // drawn here when the rows' supports are listed, else by the sampler
     const RowRec& P = rr[a];
-    const RowRec* Q = a < mb ? &rr[M + 1 + a] : nullptr;
+    const RowRec* Q = (a < mb && !qrows) ? &rr[M + 1 + a] : nullptr;
+    const float* qrow = (a < mb && qrows) ? qrows + ((size_t)b * M + a) * (size_t)V : nullptr;
     if (P.nsup > 0 && (Q == nullptr || Q->nsup > 0)) {
+      bool bad = false;
       extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
                           sup_p + ((size_t)b * R + a) * kSupMax, P.nsup,
                           Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
                           Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
-                          Q ? Q->nsup : 0, ud, q_id, q_p);
+                          Q ? Q->nsup : 0, qrow, ud, q_id, q_p, &bad);
+      if (bad) {  // an unusable entry of the published residual row
+        write_failed(b, SV_S_BAD_PROPOSAL, M, accepted_len, out_tokens, p_tok, q_tok);
+        return job;
+      }
     } else {
       job = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
     }
@@ -240,18 +273,21 @@ struct SampleSmem {
 };
 
 // Weights of this thread's kSampleE tokens of a group (ids y0 ..): the residual
-// max(0, p - q) or p.  tp, tq: ties of each row's cut key before the group;
-// on return they count the group's ties too.
-template <class Tr>
-__device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bool resid, bool ties,
-                              int y0, int V, uint32_t& tp, uint32_t& tq, double (&w)[kSampleE],
-                              SampleSmem& sm) {
+// max(0, p - q) (zero where p is zero) or p.  q comes from the draft row's
+// profile Q, or (kQ) from the published q row qrow, whose entries where p > 0
+// must be finite and non-negative (else bad is set).  tp, tq: ties of each
+// row's cut key before the group; on return they count the group's ties too.
+template <class Tr, bool kQ>
+__device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, const float* qrow,
+                              bool resid, bool ties, int y0, int V, uint32_t& tp, uint32_t& tq,
+                              double (&w)[kSampleE], bool& bad, SampleSmem& sm) {
   uint32_t up[kSampleE], uq[kSampleE];
 #pragma unroll
   for (int e = 0; e < kSampleE; ++e) {
     const bool in = y0 + e < V;
     up[e] = in ? Tr::bits(P.row[y0 + e]) : Tr::kNegInfBits;
-    uq[e] = (in && resid) ? Tr::bits(Q.row[y0 + e]) : Tr::kNegInfBits;
+    if constexpr (kQ) uq[e] = (in && resid) ? __float_as_uint(qrow[y0 + e]) : 0u;
+    else uq[e] = (in && resid) ? Tr::bits(Q.row[y0 + e]) : Tr::kNegInfBits;
   }
   int rp[kSampleE], rq[kSampleE];
 #pragma unroll
@@ -261,7 +297,7 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bo
 #pragma unroll
     for (int e = 0; e < kSampleE; ++e) {
       mine += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1u : 0u;
-      mine += (resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 0x10000u : 0u;
+      mine += (!kQ && resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 0x10000u : 0u;
     }
     uint32_t tot;
     const uint32_t before = block_exclusive_scan<uint32_t>(mine, sm.usum, &tot);
@@ -271,7 +307,7 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bo
       rp[e] = cp;
       rq[e] = cq;
       cp += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1 : 0;
-      cq += (resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 1 : 0;
+      cq += (!kQ && resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 1 : 0;
     }
     tp += tot & 0xFFFFu;
     tq += tot >> 16;
@@ -282,8 +318,15 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bo
     if (!resid) {
       w[e] = p;
     } else {
-      const double d = p - Q.prob(y0 + e, uq[e], rq[e]);
-      w[e] = d > 0.0 ? d : 0.0;
+      double q;
+      if constexpr (kQ) {
+        q = (double)__uint_as_float(uq[e]);
+        bad |= p > 0.0 && !(q >= 0.0 && q < INFINITY);
+      } else {
+        q = Q.prob(y0 + e, uq[e], rq[e]);
+      }
+      const double d = p - q;
+      w[e] = (p > 0.0 && d > 0.0) ? d : 0.0;
     }
   }
 }
@@ -298,10 +341,10 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, bo
 // One workgroup per session: its first wave takes the acceptance decisions
 // (finalize_session); a draw from rows without listed supports then takes
 // the whole workgroup.
-template <class Tr>
+template <class Tr, bool kQ>
 __global__ __launch_bounds__(kSampleNT) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const float* __restrict__ qrows, const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M, int V,
     uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
     const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
@@ -315,7 +358,8 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
   const int b = blockIdx.x;
   if (b >= B) return;
   if (threadIdx.x < kWave) {
-    const Job j = finalize_session(b, tokens, m, rule, sampling, M, seed, round, sess_status, rows,
+    const Job j = finalize_session(b, tokens, m, rule, sampling, M, V, kQ ? qrows : nullptr, seed,
+                                   round, sess_status, rows,
                                    accepted_len, out_tokens, p_tok, q_tok, sup_id, sup_p, unif,
                                    q_id, q_p);
     if (threadIdx.x == 0) job_s = j;
@@ -327,11 +371,15 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
   SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow],
                   0, nullptr};
   SampleRow<Tr> Q = P;
+  const float* qrow = nullptr;
   bool resid = job.kind == kJobResidual;
-  if (resid) Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
-                               rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
+  if (resid) {
+    if constexpr (kQ) qrow = qrows + ((size_t)b * M + job.drow) * (size_t)V;
+    else Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
+                           rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
+  }
   fill_lut<Tr>(P, sm.lut_p);
-  fill_lut<Tr>(Q, sm.lut_q);
+  if (!kQ) fill_lut<Tr>(Q, sm.lut_q);
   __syncthreads();
   const int ngroups = (V + kGroup - 1) / kGroup;
   const int G = (ngroups + kMaxChunks - 1) / kMaxChunks;  // groups per chunk
@@ -339,8 +387,9 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
 
   // the pass: every chunk's mass in id order, and the last id with mass
   int32_t last = -1;
+  bool bad = false;
   for (int attempt = 0; attempt < 2; ++attempt) {
-    const bool ties = P.tie_mode() || (resid && Q.tie_mode());
+    const bool ties = P.tie_mode() || (!kQ && resid && Q.tie_mode());
     uint32_t tp = 0, tq = 0;
     last = -1;
     for (int c = 0; c < nchunks; ++c) {
@@ -352,7 +401,7 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
       for (int g = c * G; g < min((c + 1) * G, ngroups); ++g) {
         const int y0 = g * kGroup + threadIdx.x * kSampleE;
         double w[kSampleE];
-        group_weights<Tr>(P, Q, resid, ties, y0, V, tp, tq, w, sm);
+        group_weights<Tr, kQ>(P, Q, qrow, resid, ties, y0, V, tp, tq, w, bad, sm);
 #pragma unroll
         for (int e = 0; e < kSampleE; ++e) {
           sw += w[e];
@@ -363,6 +412,15 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
       if (threadIdx.x == 0) sm.chunk_mass[c] = cm;
     }
     last = block_reduce<kSampleNT>(last, OpMax(), sm.ired);
+    if (kQ && resid && attempt == 0) {
+      // an unusable entry of the published residual row fails the session; the
+      // first wave rewrites its outputs as it wrote them
+      if (block_reduce<kSampleNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0) {
+        if (threadIdx.x < kWave)
+          write_failed(b, SV_S_BAD_PROPOSAL, M, accepted_len, out_tokens, p_tok, q_tok);
+        return;
+      }
+    }
     if (!resid || last >= 0) break;
     resid = false;  // residual without mass (rounding only): draw from p
   }
@@ -381,13 +439,13 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
     if ((int)threadIdx.x == cstar) sm.base = before;
     __syncthreads();
     double run = sm.base;
-    const bool ties = P.tie_mode() || (resid && Q.tie_mode());
+    const bool ties = P.tie_mode() || (!kQ && resid && Q.tie_mode());
     uint32_t tp = sm.ties_p[cstar], tq = sm.ties_q[cstar];
     // the chunk holding u * S; rounding may move the point into a later chunk
     for (int g = cstar * G; g < ngroups; ++g) {
       const int y0 = g * kGroup + threadIdx.x * kSampleE;
       double w[kSampleE];
-      group_weights<Tr>(P, Q, resid, ties, y0, V, tp, tq, w, sm);
+      group_weights<Tr, kQ>(P, Q, qrow, resid, ties, y0, V, tp, tq, w, bad, sm);
       double sw = 0.0;
 #pragma unroll
       for (int e = 0; e < kSampleE; ++e) sw += w[e];
@@ -412,19 +470,23 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
 
 }  // namespace
 
+template <class Tr, bool kQ>
+static void launch_finalize_t(const LaunchArgs& a, hipStream_t st) {
+  using E = typename Tr::elem_t;
+  hipLaunchKernelGGL((k_finalize<Tr, kQ>), dim3(a.B), dim3(kSampleNT), 0, st, (const E*)a.target,
+                     (const E*)a.draft, a.qrows, a.tokens, a.m, a.rule, a.sampling, a.B, a.M, a.V,
+                     a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens, a.p_tok,
+                     a.q_tok, a.sup_id, a.sup_p, a.unif);
+}
+
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
+  const bool q = a.qrows != nullptr;
   if (a.dtype == SV_BF16) {
-    hipLaunchKernelGGL(k_finalize<Bf16>, dim3(a.B), dim3(kSampleNT), 0, st,
-                       (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
-                       a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
-                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p,
-                       a.unif);
+    if (q) launch_finalize_t<Bf16, true>(a, st);
+    else launch_finalize_t<Bf16, false>(a, st);
   } else {
-    hipLaunchKernelGGL(k_finalize<F32>, dim3(a.B), dim3(kSampleNT), 0, st,
-                       (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
-                       a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
-                       a.accepted_len, a.out_tokens, a.p_tok, a.q_tok, a.sup_id, a.sup_p,
-                       a.unif);
+    if (q) launch_finalize_t<F32, true>(a, st);
+    else launch_finalize_t<F32, false>(a, st);
   }
 }
 

@@ -17,6 +17,12 @@ Gumbel-max at temperature T, among the ids of its ``draft_top_n`` largest draft
 logits (``torch.topk``); such a proposal can fall outside the verifier's
 nucleus, and the verifier then reports it as a bad proposal.  Greedy (rule 1)
 sessions of the ragged workload propose the draft argmax.
+
+Published draft rows.  ``Workload.drafter_q_rows`` returns, as SDCP q_rows, the
+distribution the synthetic drafter actually drew each token from: softmax at
+temperature T over its top-n draft logits (or over all of them when the
+profile is untruncated).  It is the drafter's arithmetic, not the verifier's
+profile (no top-k / top-p cut of the session's profile is applied).
 """
 from __future__ import annotations
 
@@ -74,26 +80,50 @@ class Workload:
         raw = np.ascontiguousarray(self.sampling).view(np.uint8).reshape(self.B, 24)
         return torch.from_numpy(raw.copy()).to(device)
 
+    def drafter_q_rows(self, draft_top_n: int = 8, chunk_sessions: int = 16) -> torch.Tensor:
+        """[B, M, V] float32 rows: the synthetic drafter's distribution for each
+        drafted position (what it publishes as q_rows).  Rows of greedy
+        sessions are filled the same way; rule 1 never reads them."""
+        B, M, V = self.B, self.M, self.V
+        T = float(self.sampling["temperature_milli"][0]) / 1000.0
+        untruncated = (int(self.sampling["top_k"][0]) == 0 and
+                       int(self.sampling["top_p_milli"][0]) >= 1000)
+        q = torch.zeros((B, M, V), dtype=torch.float32, device=self.draft.device)
+        for s0 in range(0, B, chunk_sessions):
+            d = self.draft[s0:s0 + chunk_sessions].float()
+            if untruncated or draft_top_n >= V:
+                q[s0:s0 + chunk_sessions] = torch.softmax(d / T, dim=-1)
+            else:
+                vals, ids = torch.topk(d, draft_top_n, dim=-1)
+                q[s0:s0 + chunk_sessions].scatter_(-1, ids, torch.softmax(vals / T, dim=-1))
+            del d
+        return q
+
     def positions(self) -> int:
         """P = sum_b (m_b + 1): verified positions in one step."""
         m = self.m.to("cpu").to(torch.int64)
         return int((m + 1).sum())
 
-    def algorithmic_bytes(self) -> int:
+    def algorithmic_bytes(self, q_rows: bool = False) -> int:
         """Bytes the step must move: each row a session's rule reads, once,
-        plus the small per-session arrays and the outputs."""
+        plus the small per-session arrays and the outputs.  With q_rows the
+        draft side is q_i(x_i) (4 B per drafted position) and, at most once
+        per session, the residual's row (not counted: it depends on the draws)."""
         m = self.m.to("cpu").to(torch.int64)
         rule = self.rule.to("cpu").to(torch.int64)
-        rows = int((m + 1).sum() + (m * (rule == 2)).sum())
+        draft_rows = 0 if q_rows else int((m * (rule == 2)).sum())
+        rows = int((m + 1).sum()) + draft_rows
         s = self.target.element_size()
         small = self.B * (4 * self.M + 4 + 4 + 24 + 4 + 4 * (self.M + 1))
+        if q_rows:
+            small += 4 * int((m * (rule == 2)).sum())
         return rows * self.V * s + small
 
-    def row_bytes_by_kernel(self) -> dict:
+    def row_bytes_by_kernel(self, q_rows: bool = False) -> dict:
         """Row bytes read by each row kernel: the single-pass kernel takes bf16
         rows of the top-k class (greedy rules, temperature 0, 1 <= top_k <= 64)
         and of the dense class (temperature > 0 with top-k off); the generic
-        kernel takes the rest."""
+        kernel takes the rest.  With q_rows no draft row is profiled."""
         m = self.m.to("cpu").to(torch.int64).numpy()
         rule = self.rule.to("cpu").to(torch.int64).numpy()
         s = self.sampling
@@ -101,7 +131,7 @@ class Workload:
         T, k = s["temperature_milli"], s["top_k"]
         topk_class = (rule == 1) | (T == 0) | ((k >= 1) & (k <= 64))
         dense_class = ~topk_class & ((k == 0) | (k >= self.V))
-        per_session = (m + 1) + m * (rule == 2)
+        per_session = (m + 1) + (0 if q_rows else m * (rule == 2))
         row = self.V * self.target.element_size()
         stream = int(per_session[topk_class | dense_class].sum()) * row if bf16 else 0
         return {"stream": stream, "generic": int(per_session.sum()) * row - stream}
