@@ -110,6 +110,13 @@ def lib():
             ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp,
         ]
         L.ov_verify_qrows.restype = ctypes.c_int
+        L.ov_commit.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i32p, i32p, i32p,
+                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, i32p, i32p]
+        L.ov_commit.restype = ctypes.c_int
+        L.ov_prefix_digest.argtypes = [ctypes.c_char_p, i32p, ctypes.c_uint32, ctypes.c_char_p]
+        L.ov_prefix_digest.restype = None
+        L.ov_contract_digest.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
+        L.ov_contract_digest.restype = None
         L.ov_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
         L.ov_sha256.restype = None
         L.ov_hmac_sha256.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p,
@@ -302,6 +309,78 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     if rc != 0:
         raise ValueError(f"oracle rejected the call (code {rc})")
     return out
+
+
+# ------------------------------------------------------------- commit step
+# SDCP Sec. 6.5.2 actions
+ACT_CONTINUE, ACT_REDUCE, ACT_SWITCH, ACT_SELF_DECODE, ACT_FINISH, ACT_FAIL = range(6)
+
+CONTRACT_DTYPE = np.dtype(
+    [("m_max", "<u4"), ("max_new", "<u4"), ("low_rounds", "<u4"), ("low_ratio", "<u4"),
+     ("n_stop", "<u4"), ("stop", "<i4", (8,)), ("n_fallback", "<u4"), ("fallback", "u1", (8,))],
+    align=True)
+assert CONTRACT_DTYPE.itemsize == 64
+
+STATE_DTYPE = np.dtype(
+    [("digest", "u1", (32,)), ("n", "<u4"), ("m_cap", "<u4"), ("c", "<u4"), ("g", "<u4"),
+     ("j", "<u4"), ("reserved", "<u4", (3,))],
+    align=True)
+assert STATE_DTYPE.itemsize == 64
+
+
+def make_contracts(B, m_max=8, max_new=256, low_rounds=3, low_ratio=0, stop=(2,),
+                   fallback=(ACT_REDUCE, ACT_SWITCH, ACT_SELF_DECODE, ACT_FAIL)):
+    c = np.zeros(B, dtype=CONTRACT_DTYPE)
+    c["m_max"], c["max_new"], c["low_rounds"], c["low_ratio"] = m_max, max_new, low_rounds, low_ratio
+    c["n_stop"] = len(stop)
+    c["stop"][:, :len(stop)] = stop
+    c["n_fallback"] = len(fallback)
+    c["fallback"][:, :len(fallback)] = fallback
+    return c
+
+
+def make_states(B, digest=b"\0" * 32, n=0, m_cap=8):
+    s = np.zeros(B, dtype=STATE_DTYPE)
+    s["digest"] = np.frombuffer(bytes(digest), dtype=np.uint8)
+    s["n"], s["m_cap"] = n, m_cap
+    return s
+
+
+def prefix_digest(contract_digest: bytes, prompt) -> bytes:
+    """d[0] of SDCP Sec. 4.2."""
+    p = np.ascontiguousarray(prompt, dtype=np.int32)
+    out = ctypes.create_string_buffer(32)
+    lib().ov_prefix_digest(bytes(contract_digest), _ptr(p, ctypes.c_int32), p.shape[0], out)
+    return out.raw
+
+
+def contract_digest(cbor: bytes) -> bytes:
+    """contract_digest of SDCP Sec. 4.1 over a deterministic CBOR encoding."""
+    out = ctypes.create_string_buffer(32)
+    lib().ov_contract_digest(bytes(cbor), len(cbor), out)
+    return out.raw
+
+
+def commit(contracts, states, m, accepted_len, out_tokens, self_decode_ok=None):
+    """The commit step (SDCP Sec. 6.3 steps 6-8, 6.5) for one round.  states is
+    updated in place; returns (out_tokens truncated, emitted_len, action)."""
+    contracts = np.ascontiguousarray(contracts, dtype=CONTRACT_DTYPE)
+    assert states.dtype == STATE_DTYPE and states.flags["C_CONTIGUOUS"]
+    B = states.shape[0]
+    out = np.array(out_tokens, dtype=np.int32, copy=True).reshape(B, -1)
+    M = out.shape[1] - 1
+    m = np.ascontiguousarray(m, dtype=np.int32).reshape(B)
+    a = np.ascontiguousarray(accepted_len, dtype=np.int32).reshape(B)
+    ok = None if self_decode_ok is None else np.ascontiguousarray(self_decode_ok, dtype=np.uint8)
+    emitted = np.zeros(B, dtype=np.int32)
+    action = np.zeros(B, dtype=np.int32)
+    rc = lib().ov_commit(contracts.ctypes.data, states.ctypes.data, _ptr(m, ctypes.c_int32),
+                         _ptr(a, ctypes.c_int32), _ptr(out, ctypes.c_int32),
+                         None if ok is None else ok.ctypes.data, B, M,
+                         _ptr(emitted, ctypes.c_int32), _ptr(action, ctypes.c_int32))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the call (code {rc})")
+    return out, emitted, action
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:

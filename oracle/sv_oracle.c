@@ -55,7 +55,13 @@
  *    finite logit, makes the session fail with status BAD_LOGITS;
  *  - the inverse CDF walks token ids in ascending order and returns the first
  *    y whose running sum exceeds u*S;
- *  - an all-zero residual (reachable only through rounding) falls back to p_i.
+ *  - an all-zero residual (reachable only through rounding) falls back to p_i;
+ *  - ov_commit (SDCP Sec. 6.3 steps 6-8, 6.5): a session whose acceptance step
+ *    failed commits nothing and keeps its state; the proposal length M of the
+ *    low-round test is the session's m; m_cap is restored by one after every
+ *    round that is not low (the text's example of a gradual restore), up to
+ *    m_max; finish takes precedence over the escalation's action when a stop
+ *    token was committed or max_new was reached.
  *
  * All floating-point arithmetic is IEEE binary64.
  */
@@ -696,4 +702,160 @@ int ov_verify_qrows(const void *target, int dtype, const float *qrows, const int
   return verify_batch(target, NULL, qrows, dtype, tokens, m, rule, sampling, B, M, V, seed, round,
                       sessions, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, NULL,
                       d_cdf);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The verifier's commit step around the acceptance step [SDCP Sec. 4.2,    */
+/* 6.3 steps 6-8, 6.5]: truncation, the committed-prefix digest chain, the  */
+/* low-round counters with the fallback ladder, and m_cap.                   */
+/* ------------------------------------------------------------------------ */
+enum { OV_ACT_CONTINUE = 0, OV_ACT_REDUCE = 1, OV_ACT_SWITCH = 2, OV_ACT_SELF_DECODE = 3,
+       OV_ACT_FINISH = 4, OV_ACT_FAIL = 5 };
+
+/* The contract members the commit step reads [SDCP Sec. 4.1] (the same
+ * 64-octet layout as the library's record). */
+typedef struct {
+  uint32_t m_max, max_new, low_rounds, low_ratio; /* low_ratio 0 = absent */
+  uint32_t n_stop;
+  int32_t stop[8];
+  uint32_t n_fallback;
+  uint8_t fallback[8];
+} ov_contract;
+
+/* Per-session verifier state (the same 64-octet layout as the library's). */
+typedef struct {
+  uint8_t digest[32]; /* d[n] */
+  uint32_t n;         /* committed output tokens */
+  uint32_t m_cap;
+  uint32_t c, g, j;   /* Sec. 6.5.2 counters */
+  uint32_t reserved[3];
+} ov_state;
+
+/* [SDCP Sec. 4.2] d[0] over the domain separator, the contract digest, the
+ * prompt length and the prompt tokens (each uint32, network byte order). */
+void ov_prefix_digest(const uint8_t contract_digest[32], const int32_t *prompt, uint32_t P,
+                      uint8_t out[32]) {
+  const size_t len = 14 + 32 + 4 + 4 * (size_t)P;
+  uint8_t *msg = (uint8_t *)malloc(len);
+  memcpy(msg, "SDCP-PREFIX-1", 13);
+  msg[13] = 0x00;
+  memcpy(msg + 14, contract_digest, 32);
+  size_t n = 46;
+  for (int k = 0; k < 4; ++k) msg[n++] = (uint8_t)(P >> (24 - 8 * k));
+  for (uint32_t t = 0; t < P; ++t)
+    for (int k = 0; k < 4; ++k) msg[n++] = (uint8_t)((uint32_t)prompt[t] >> (24 - 8 * k));
+  ov_sha256(msg, len, out);
+  free(msg);
+}
+
+/* [SDCP Sec. 4.1] contract_digest over the domain separator and the contract's
+ * deterministic CBOR encoding (given). */
+void ov_contract_digest(const uint8_t *cbor, size_t len, uint8_t out[32]) {
+  uint8_t *msg = (uint8_t *)malloc(16 + len);
+  memcpy(msg, "SDCP-CONTRACT-1", 15);
+  msg[15] = 0x00;
+  memcpy(msg + 16, cbor, len);
+  ov_sha256(msg, 16 + len, out);
+  free(msg);
+}
+
+/*
+ * One round's commit for B sessions, after the acceptance step:
+ *   accepted_len [B]  a (>= 0), or a negative status: such a session commits
+ *                     nothing, its state is left as it is and its action is -1;
+ *   out_tokens [B, M+1]  the a+1 emitted tokens, then -1; truncated in place
+ *                     after the first stop token and at max_new [Sec. 6.3
+ *                     step 6]: entries past the committed ones become -1;
+ *   m [B]             the proposal lengths;
+ *   self_decode_ok [B] 1 where self_decode is permitted this round (the
+ *                     contract has self_load and the load does not exceed it),
+ *                     or NULL (never permitted).
+ * Outputs: emitted_len [B] tokens committed; action [B]; state updated.
+ * Per session, in the order of the text:
+ *   commit [Sec. 6.3 step 7]: n += e; d[n+k] = SHA-256(d[n+k-1] || uint32(o_k));
+ *   low round [Sec. 6.5.2]: 100*a < low_ratio*m, or a == 0 when low_ratio is 0;
+ *   counters: low -> c += 1, g = 0; else c = 0, g += 1 and, when g reaches R,
+ *     j = 0; when c reaches R the entry j of the fallback list is applied,
+ *     self_decode skipped where not permitted, j advanced past every entry
+ *     applied or skipped, then c = 0; no entry left -> fail; otherwise
+ *     continue;
+ *   m_cap [Sec. 6.5.1, 6.5.2]: reduce halves it (at least 1); after a round
+ *     that is not low it is restored by one, up to m_max (the text's example
+ *     of a gradual restore);
+ *   finish [Sec. 6.5.2]: when a stop token was committed or n reached
+ *     max_new, the action is finish.
+ */
+int ov_commit(const ov_contract *contract, ov_state *state, const int32_t *m,
+              const int32_t *accepted_len, int32_t *out_tokens, const uint8_t *self_decode_ok,
+              int64_t B, int M, int32_t *emitted_len, int32_t *action) {
+  if (!contract || !state || !m || !accepted_len || !out_tokens || !emitted_len || !action ||
+      B < 1 || M < 1 || M > 64)
+    return OV_ERR_ARG;
+  for (int64_t b = 0; b < B; ++b) {
+    const ov_contract *k = &contract[b];
+    ov_state *s = &state[b];
+    int32_t *out = out_tokens + b * (int64_t)(M + 1);
+    const int32_t a = accepted_len[b];
+    if (a < 0) {
+      emitted_len[b] = 0;
+      action[b] = -1;
+      continue;
+    }
+    /* truncation: after the first stop token, and at max_new */
+    int e = a + 1, finished = 0;
+    for (int t = 0; t < e; ++t) {
+      int is_stop = 0;
+      for (uint32_t q = 0; q < k->n_stop && q < 8; ++q)
+        if (out[t] == k->stop[q]) is_stop = 1;
+      if (is_stop) {
+        e = t + 1;
+        finished = 1;
+        break;
+      }
+    }
+    const uint32_t room = s->n >= k->max_new ? 0u : k->max_new - s->n;
+    if ((uint32_t)e >= room) {
+      e = (int)room;
+      finished = 1;
+    }
+    for (int t = e; t <= M; ++t) out[t] = -1;
+    /* commit: extend the digest chain by every committed token */
+    for (int t = 0; t < e; ++t) {
+      uint8_t msg[36];
+      memcpy(msg, s->digest, 32);
+      for (int q = 0; q < 4; ++q) msg[32 + q] = (uint8_t)((uint32_t)out[t] >> (24 - 8 * q));
+      ov_sha256(msg, 36, s->digest);
+    }
+    s->n += (uint32_t)e;
+    /* control */
+    const int low = k->low_ratio > 0 ? (100LL * a < (long long)k->low_ratio * m[b]) : (a == 0);
+    int act = OV_ACT_CONTINUE;
+    if (low) {
+      s->c += 1;
+      s->g = 0;
+    } else {
+      s->c = 0;
+      s->g += 1;
+      if (s->g == k->low_rounds) s->j = 0;
+    }
+    if (s->c == k->low_rounds) {
+      int applied = 0;
+      while (s->j < k->n_fallback && s->j < 8) {
+        const int entry = k->fallback[s->j];
+        s->j += 1;
+        if (entry == OV_ACT_SELF_DECODE && !(self_decode_ok && self_decode_ok[b])) continue;
+        act = entry;
+        applied = 1;
+        break;
+      }
+      if (!applied) act = OV_ACT_FAIL;
+      s->c = 0;
+    }
+    if (act == OV_ACT_REDUCE) s->m_cap = s->m_cap / 2 > 1 ? s->m_cap / 2 : 1;
+    if (!low && s->m_cap < k->m_max) s->m_cap += 1;
+    if (finished) act = OV_ACT_FINISH;
+    emitted_len[b] = e;
+    action[b] = act;
+  }
+  return OV_OK;
 }
