@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--qrows", action="store_true",
                     help="time sv_verify_qrows: draft distributions as published binary32 rows "
                          "(the synthetic drafter's own distribution) instead of draft logits")
+    ap.add_argument("--commit", action="store_true",
+                    help="add the commit step (sv_commit: truncation, digest chain, counters) "
+                         "to every step, with per-session state carried across steps")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -149,10 +152,21 @@ def main():
     q_rows = w.drafter_q_rows() if args.qrows else None
     draft = None if args.qrows else w.draft
 
+    contracts = states = cres = None
+    if args.commit:
+        contracts = sv.make_contracts(B, m_max=M, max_new=1 << 30, low_rounds=3, stop=(),
+                                      device=dev)
+        states = sv.make_states(B, m_cap=M, device=dev)
+        cres = {"emitted_len": torch.empty(B, dtype=torch.int32, device=dev),
+                "action": torch.empty(B, dtype=torch.int32, device=dev)}
+
     def step(ev=None):
         sv.verify(w.target, draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
                   workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp,
                   q_rows=q_rows)
+        if args.commit:
+            sv.commit(contracts, states, w.m, out["accepted_len"], out["out_tokens"],
+                      stream=stream, out=cres)
 
     for _ in range(args.warmup):
         step()
@@ -211,6 +225,7 @@ def main():
             "logits": "bf16" if w.target.dtype == torch.bfloat16 else "fp32",
             "uniforms": "sdcp-hmac-sha256" if args.sdcp else "philox4x64-10",
             "draft": "q_rows fp32" if args.qrows else "logits",
+            "commit_step": bool(args.commit),
             "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(q_rows=args.qrows),
             "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),

@@ -203,6 +203,89 @@ int sv_verify_qrows(const void *target_logits, int32_t dtype, const float *q_row
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_probe *probe, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The verifier's commit step (SDCP Sec. 4.2, Sec. 6.3 steps 6-8, Sec. 6.5).
+ * ------------------------------------------------------------------------- */
+#define SV_STOP_MAX 8     /* stop tokens per contract */
+#define SV_FALLBACK_MAX 8 /* fallback list entries per contract */
+
+/* Verdict actions, SDCP Sec. 6.5.2. */
+enum {
+  SV_ACT_CONTINUE = 0,
+  SV_ACT_REDUCE = 1,
+  SV_ACT_SWITCH = 2,
+  SV_ACT_SELF_DECODE = 3,
+  SV_ACT_FINISH = 4,
+  SV_ACT_FAIL = 5
+};
+
+/* The contract members the commit step reads (SDCP Sec. 4.1), 64 bytes,
+ * 4-byte aligned; a DEVICE array [B]. */
+typedef struct sv_contract {
+  uint32_t m_max;      /* largest M (1..64); m_cap is restored up to it */
+  uint32_t max_new;    /* most output tokens of the session */
+  uint32_t low_rounds; /* R >= 1 */
+  uint32_t low_ratio;  /* percent, 0..100; 0 = absent */
+  uint32_t n_stop;     /* stop tokens used: min(n_stop, SV_STOP_MAX) */
+  int32_t stop[SV_STOP_MAX];
+  uint32_t n_fallback; /* entries used: min(n_fallback, SV_FALLBACK_MAX) */
+  uint8_t fallback[SV_FALLBACK_MAX]; /* SV_ACT_REDUCE, _SWITCH, _SELF_DECODE, _FAIL */
+} sv_contract;
+
+/* A session's verifier state, 64 bytes, 4-byte aligned; a DEVICE array [B]
+ * that sv_commit reads and updates.  Initially: digest = d[0] (see
+ * sv_prefix_digest), n = 0, m_cap = the first round's limit, c = g = j = 0. */
+typedef struct sv_session_state {
+  uint8_t digest[32];   /* d[n] (Sec. 4.2) */
+  uint32_t n;           /* committed output tokens */
+  uint32_t m_cap;       /* the verdict's speculation limit (Sec. 6.5.1) */
+  uint32_t c, g, j;     /* low-round counters (Sec. 6.5.2) */
+  uint32_t reserved[3]; /* not used */
+} sv_session_state;
+
+/*
+ * One round's commit for B sessions, enqueued on stream after the acceptance
+ * step of the same round.  DEVICE arrays: contracts [B], states [B] (updated),
+ * m [B] (the proposal lengths), accepted_len [B] and out_tokens [B, M+1] as
+ * written by sv_verify / sv_verify_sdcp / sv_verify_qrows, self_decode_ok [B]
+ * (1 where self_decode is permitted this round: the contract has self_load and
+ * the verifier's load does not exceed it) or NULL (never permitted).
+ * Outputs: emitted_len [B], action [B] (SV_ACT_*); out_tokens truncated in
+ * place (entries past the committed ones become -1).  Per session:
+ *  - accepted_len outside [0, M] (a failed session): nothing is committed, the
+ *    state is unchanged, emitted_len = 0, action = -1;
+ *  - truncation (Sec. 6.3 step 6): the a+1 emitted tokens end after the first
+ *    stop token, and at max_new committed tokens in all;
+ *  - commit (Sec. 6.3 step 7, Sec. 4.2): n += e and
+ *    d[n+k] = SHA-256(d[n+k-1] || uint32(o_k)) for each committed token;
+ *  - control (Sec. 6.5.2): the round is low if 100*a < low_ratio*m, or a == 0
+ *    when low_ratio is 0; low -> c += 1, g = 0; else c = 0, g += 1 and j = 0
+ *    when g reaches R.  When c reaches R, fallback entry j is applied (a
+ *    self_decode that is not permitted is skipped), j advances past every entry
+ *    applied or skipped, c = 0; with no entry left the action is fail;
+ *    otherwise continue.  reduce sets m_cap = max(1, m_cap / 2); after a round
+ *    that is not low m_cap is restored by one up to m_max (the gradual restore
+ *    of Sec. 6.5.1).  When a stop token was committed or max_new was reached,
+ *    the action is finish.
+ * Calls that overlap on the same states race.  Returns SV_OK, SV_ERR_ARG
+ * (null pointer, B or M out of range) or SV_ERR_DEVICE.
+ */
+int sv_commit(const sv_contract *contracts, sv_session_state *states, const int32_t *m,
+              const int32_t *accepted_len, int32_t *out_tokens, const uint8_t *self_decode_ok,
+              int32_t B, int32_t M, int32_t *emitted_len, int32_t *action, void *stream);
+
+/* d[0] of SDCP Sec. 4.2: SHA-256("SDCP-PREFIX-1" || 0x00 || contract_digest ||
+ * uint32(P) || uint32(prompt[0]) || ... ), integers in network byte order.
+ * HOST memory: contract_digest[32], prompt[P], out[32].  Runs on the host.
+ * Returns SV_OK or SV_ERR_ARG. */
+int sv_prefix_digest(const uint8_t *contract_digest, const int32_t *prompt, uint32_t P,
+                     uint8_t *out);
+
+/* contract_digest of SDCP Sec. 4.1: SHA-256("SDCP-CONTRACT-1" || 0x00 || cbor),
+ * over the contract's deterministic CBOR encoding supplied by the caller.
+ * HOST memory; runs on the host.  Returns SV_OK or SV_ERR_ARG. */
+int sv_contract_digest(const uint8_t *cbor, size_t len, uint8_t *out);
+
 /* Text for an sv_verify return code; never NULL. */
 const char *sv_strerror(int code);
 

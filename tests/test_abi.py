@@ -34,8 +34,9 @@ def svlib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_workspace_bytes", "sv_strerror",
-            "sv_status_str", "sv_version"} <= names
+    assert {"sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_commit", "sv_prefix_digest",
+            "sv_contract_digest", "sv_workspace_bytes", "sv_strerror", "sv_status_str",
+            "sv_version"} <= names
 
 
 def test_library_exports_every_declared_symbol(svlib):
@@ -144,6 +145,61 @@ def test_verify_qrows_rejects_bad_arguments_on_the_host(svlib):
     assert call(M=65) == svlib.ERR_ARG
     assert call(V=0) == svlib.ERR_ARG
     assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
+
+
+def header_struct_fields(name):
+    text = open(os.path.join(ROOT, "include", "specverify.h")).read()
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return re.findall(r"(u?int\d+_t)\s+([\w, ]+?)(\[\w+\])?;", body)
+
+
+def test_commit_record_layouts(svlib):
+    assert svlib.CONTRACT_DTYPE.itemsize == 64 and svlib.STATE_DTYPE.itemsize == 64
+    assert header_struct_fields("sv_contract") == [
+        ("uint32_t", "m_max", ""), ("uint32_t", "max_new", ""), ("uint32_t", "low_rounds", ""),
+        ("uint32_t", "low_ratio", ""), ("uint32_t", "n_stop", ""), ("int32_t", "stop", "[SV_STOP_MAX]"),
+        ("uint32_t", "n_fallback", ""), ("uint8_t", "fallback", "[SV_FALLBACK_MAX]")]
+    assert header_struct_fields("sv_session_state") == [
+        ("uint8_t", "digest", "[32]"), ("uint32_t", "n", ""), ("uint32_t", "m_cap", ""),
+        ("uint32_t", "c, g, j", ""), ("uint32_t", "reserved", "[3]")]
+    d = svlib.CONTRACT_DTYPE
+    assert [d.fields[f][1] for f in ("m_max", "n_stop", "stop", "n_fallback", "fallback")] == \
+        [0, 16, 20, 52, 56]
+    d = svlib.STATE_DTYPE
+    assert [d.fields[f][1] for f in ("digest", "n", "m_cap", "c", "g", "j")] == \
+        [0, 32, 36, 40, 44, 48]
+
+
+def test_host_digests_reproduce_appendix_a(svlib):
+    """The library's host SHA-256 (sv_contract_digest, sv_prefix_digest) against
+    the contract digest and d[0] printed in SDCP Appendix A."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "sdcp_appendix_a_digests.json")))
+    cd = svlib.contract_digest(bytes.fromhex(g["contract_cbor_hex"]))
+    assert cd.hex() == g["contract_digest"]
+    assert svlib.prefix_digest(cd, g["prompt"]).hex() == g["d"][0]
+    import hashlib
+    for n in (0, 1, 55, 56, 63, 64, 119, 120, 1000):
+        msg = bytes((3 * i) & 0xFF for i in range(n))
+        assert svlib.contract_digest(msg) == hashlib.sha256(b"SDCP-CONTRACT-1\x00" + msg).digest()
+
+
+def test_commit_rejects_bad_arguments_on_the_host(svlib):
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+
+    def call(contracts=fake, states=fake, B=3, M=4, emitted=fake):
+        return L.sv_commit(contracts, states, fake, fake, fake, None, B, M, emitted, fake, None)
+
+    assert call(contracts=None) == svlib.ERR_ARG
+    assert call(states=None) == svlib.ERR_ARG
+    assert call(emitted=None) == svlib.ERR_ARG
+    assert call(B=0) == svlib.ERR_ARG
+    assert call(M=0) == svlib.ERR_ARG
+    assert call(M=65) == svlib.ERR_ARG
+    assert L.sv_prefix_digest(None, None, 0, ctypes.create_string_buffer(32)) == svlib.ERR_ARG
+    assert L.sv_contract_digest(b"", 0, None) == svlib.ERR_ARG
 
 
 def test_product_path_does_not_import_the_oracle():

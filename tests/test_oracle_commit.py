@@ -105,7 +105,7 @@ def test_failed_session_commits_nothing():
     s = oracle.make_states(2, digest=b"\x22" * 32, n=7, m_cap=5)
     s["c"], s["g"], s["j"] = 1, 0, 2
     before = s.copy()
-    res, e, act = run(k, s, [3, 3], [-1, -3], [[-1] * 4, [-1] * 4])
+    res, e, act = run(k, s, [3, 3], [-1, 4], [[-1] * 4, [5] * 4])  # a = 4 > M = 3
     assert e.tolist() == [0, 0] and act.tolist() == [-1, -1]
     assert s.tobytes() == before.tobytes()
 

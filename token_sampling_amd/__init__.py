@@ -47,8 +47,22 @@ SDCP_SESSION_DTYPE = np.dtype(
     [("session_id", np.uint8, (16,)), ("seed", "<u8"), ("round", "<u4"), ("reserved", "<u4")],
     align=True,
 )
-EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_strerror",
-            "sv_status_str", "sv_version")
+# SDCP Sec. 6.5.2 actions and the commit step's records (sv_contract,
+# sv_session_state, 64 bytes each).
+ACT_CONTINUE, ACT_REDUCE, ACT_SWITCH, ACT_SELF_DECODE, ACT_FINISH, ACT_FAIL = range(6)
+CONTRACT_DTYPE = np.dtype(
+    [("m_max", "<u4"), ("max_new", "<u4"), ("low_rounds", "<u4"), ("low_ratio", "<u4"),
+     ("n_stop", "<u4"), ("stop", "<i4", (8,)), ("n_fallback", "<u4"), ("fallback", "u1", (8,))],
+    align=True,
+)
+STATE_DTYPE = np.dtype(
+    [("digest", "u1", (32,)), ("n", "<u4"), ("m_cap", "<u4"), ("c", "<u4"), ("g", "<u4"),
+     ("j", "<u4"), ("reserved", "<u4", (3,))],
+    align=True,
+)
+EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_commit",
+            "sv_prefix_digest", "sv_contract_digest", "sv_strerror", "sv_status_str",
+            "sv_version")
 
 
 class SvError(RuntimeError):
@@ -130,6 +144,15 @@ def lib():
             ctypes.POINTER(_Probe), ctypes.c_void_p,
         ]
         L.sv_verify_qrows.restype = ctypes.c_int
+        L.sv_commit.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_void_p, ctypes.c_void_p,
+                                                         ctypes.c_void_p]
+        L.sv_commit.restype = ctypes.c_int
+        L.sv_prefix_digest.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_uint32,
+                                       ctypes.c_char_p]
+        L.sv_prefix_digest.restype = ctypes.c_int
+        L.sv_contract_digest.argtypes = [ctypes.c_char_p, ctypes.c_size_t, ctypes.c_char_p]
+        L.sv_contract_digest.restype = ctypes.c_int
         L.sv_strerror.argtypes = [ctypes.c_int]
         L.sv_strerror.restype = ctypes.c_char_p
         L.sv_status_str.argtypes = [ctypes.c_int]
@@ -185,6 +208,97 @@ def make_sdcp_sessions(B, seed, round_, session_ids=None, device="cuda"):
     s["round"] = round_
     raw = np.ascontiguousarray(s).view(np.uint8).reshape(B, 32)
     return torch.from_numpy(raw.copy()).to(device)
+
+
+def make_contracts(B, m_max=8, max_new=256, low_rounds=3, low_ratio=0, stop=(),
+                   fallback=(ACT_REDUCE, ACT_SWITCH, ACT_SELF_DECODE, ACT_FAIL), device="cuda"):
+    """Pack per-session contract members (SDCP Sec. 4.1) into [B, 64] device bytes.
+    Every argument is a scalar (or a sequence, for stop and fallback) shared by
+    all sessions, or a list of B of them."""
+    import torch
+
+    c = np.zeros(B, dtype=CONTRACT_DTYPE)
+    c["m_max"], c["max_new"], c["low_rounds"], c["low_ratio"] = m_max, max_new, low_rounds, low_ratio
+    per = [stop] * B if len(stop) == 0 or np.isscalar(stop[0]) else stop
+    for b, st in enumerate(per):
+        c["n_stop"][b] = len(st)
+        c["stop"][b, :min(len(st), 8)] = list(st)[:8]
+    per = [fallback] * B if len(fallback) == 0 or np.isscalar(fallback[0]) else fallback
+    for b, fb in enumerate(per):
+        c["n_fallback"][b] = len(fb)
+        c["fallback"][b, :min(len(fb), 8)] = list(fb)[:8]
+    raw = np.ascontiguousarray(c).view(np.uint8).reshape(B, 64)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def make_states(B, digest=b"\0" * 32, n=0, m_cap=8, device="cuda"):
+    """Initial per-session states ([B, 64] device bytes): digest d[n] (32 bytes,
+    or a [B, 32] array), n committed tokens, m_cap, counters zero."""
+    import torch
+
+    s = np.zeros(B, dtype=STATE_DTYPE)
+    s["digest"] = np.asarray(np.frombuffer(digest, np.uint8) if isinstance(digest, bytes)
+                             else digest, dtype=np.uint8)
+    s["n"], s["m_cap"] = n, m_cap
+    raw = np.ascontiguousarray(s).view(np.uint8).reshape(B, 64)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def states_numpy(states):
+    """Host copy of device state records as a STATE_DTYPE array."""
+    raw = states.cpu().numpy().astype(np.uint8, copy=False)
+    return raw.reshape(-1, 64).copy().view(STATE_DTYPE).reshape(-1)
+
+
+def prefix_digest(contract_digest: bytes, prompt) -> bytes:
+    """d[0] of SDCP Sec. 4.2 (host)."""
+    p = np.ascontiguousarray(prompt, dtype=np.int32)
+    out = ctypes.create_string_buffer(32)
+    rc = lib().sv_prefix_digest(bytes(contract_digest), p.ctypes.data, p.shape[0], out)
+    if rc != OK:
+        raise SvError(f"sv_prefix_digest failed ({rc})")
+    return out.raw
+
+
+def contract_digest(cbor: bytes) -> bytes:
+    """contract_digest of SDCP Sec. 4.1 over a deterministic CBOR encoding (host)."""
+    out = ctypes.create_string_buffer(32)
+    rc = lib().sv_contract_digest(bytes(cbor), len(cbor), out)
+    if rc != OK:
+        raise SvError(f"sv_contract_digest failed ({rc})")
+    return out.raw
+
+
+def commit(contracts, states, m, accepted_len, out_tokens, self_decode_ok=None, stream=None,
+           out=None):
+    """sv_commit on device tensors: contracts [B, 64] and states [B, 64] uint8
+    (see make_contracts / make_states), m and accepted_len [B] int32, out_tokens
+    [B, M+1] int32 (truncated in place), self_decode_ok [B] uint8 or None.
+    Returns dict(emitted_len, action), both [B] int32."""
+    import torch
+
+    dev = out_tokens.device
+    B, M1 = out_tokens.shape
+    for t, name, dt in ((contracts, "contracts", torch.uint8), (states, "states", torch.uint8)):
+        _check(t, name, dt, (B, 64), dev)
+    _check(m, "m", torch.int32, (B,), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (B,), dev)
+    _check(out_tokens, "out_tokens", torch.int32, (B, M1), dev)
+    if self_decode_ok is not None:
+        _check(self_decode_ok, "self_decode_ok", torch.uint8, (B,), dev)
+    if out is None:
+        out = {"emitted_len": torch.empty(B, dtype=torch.int32, device=dev),
+               "action": torch.empty(B, dtype=torch.int32, device=dev)}
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = lib().sv_commit(contracts.data_ptr(), states.data_ptr(), m.data_ptr(),
+                         accepted_len.data_ptr(), out_tokens.data_ptr(),
+                         None if self_decode_ok is None else self_decode_ok.data_ptr(), B, M1 - 1,
+                         out["emitted_len"].data_ptr(), out["action"].data_ptr(),
+                         stream.cuda_stream)
+    if rc != OK:
+        raise SvError(f"sv_commit failed: {strerror(rc)} ({rc})")
+    return out
 
 
 def _check(t, name, dtype, shape, device):

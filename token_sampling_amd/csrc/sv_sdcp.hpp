@@ -23,30 +23,36 @@ namespace sv {
 namespace sdcp {
 
 // FIPS 180-4 Sec. 4.2.2: the first 32 bits of the fractional parts of the cube
-// roots of the first 64 primes.
-__constant__ const uint32_t kK[64] = {
-    0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u,
-    0xab1c5ed5u, 0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u, 0x80deb1feu,
-    0x9bdc06a7u, 0xc19bf174u, 0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u, 0x240ca1ccu, 0x2de92c6fu,
-    0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau, 0x983e5152u, 0xa831c66du, 0xb00327c8u, 0xbf597fc7u,
-    0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u, 0x14292967u, 0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu,
-    0x53380d13u, 0x650a7354u, 0x766a0abbu, 0x81c2c92eu, 0x92722c85u, 0xa2bfe8a1u, 0xa81a664bu,
-    0xc24b8b70u, 0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u, 0x19a4c116u,
-    0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu, 0x682e6ff3u,
-    0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u,
-    0xc67178f2u};
+// roots of the first 64 primes (one literal table for the device copy in
+// constant memory and the host copy).
+#define SV_SHA256_K                                                                           \
+  0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u,   \
+      0xab1c5ed5u, 0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u,           \
+      0x80deb1feu, 0x9bdc06a7u, 0xc19bf174u, 0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u,           \
+      0x240ca1ccu, 0x2de92c6fu, 0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau, 0x983e5152u,           \
+      0xa831c66du, 0xb00327c8u, 0xbf597fc7u, 0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u,           \
+      0x14292967u, 0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu, 0x53380d13u, 0x650a7354u,           \
+      0x766a0abbu, 0x81c2c92eu, 0x92722c85u, 0xa2bfe8a1u, 0xa81a664bu, 0xc24b8b70u,           \
+      0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u, 0x19a4c116u,           \
+      0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu,           \
+      0x682e6ff3u, 0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau,           \
+      0xa4506cebu, 0xbef9a3f7u, 0xc67178f2u
+__constant__ const uint32_t kK[64] = {SV_SHA256_K};
+static const uint32_t kKHost[64] = {SV_SHA256_K};
 
 // FIPS 180-4 Sec. 5.3.3: the first 32 bits of the fractional parts of the
 // square roots of the first 8 primes.
-constexpr uint32_t kH0[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
-                             0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
+#define SV_SHA256_H0 \
+  0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au, 0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u
+constexpr uint32_t kH0[8] = {SV_SHA256_H0};
 
-__device__ inline uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+__host__ __device__ inline uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
 
-// One compression of a 16-word block into the state h (FIPS 180-4 Sec. 6.2.2).
-// The schedule is kept as a 16-word window that rolls every 16 rounds; the
-// rounds run in four groups of sixteen so every window index is static.
-__device__ inline void compress(uint32_t h[8], uint32_t w[16]) {
+// One compression of a 16-word block into the state h (FIPS 180-4 Sec. 6.2.2),
+// with the round constants K (kK on the device, kKHost on the host).  The
+// schedule is kept as a 16-word window that rolls every 16 rounds; the rounds
+// run in four groups of sixteen so every window index is static.
+__host__ __device__ inline void compress_k(uint32_t h[8], uint32_t w[16], const uint32_t* K) {
   uint32_t a = h[0], b = h[1], c = h[2], d = h[3], e = h[4], f = h[5], g = h[6], k = h[7];
 #pragma unroll 1
   for (int grp = 0; grp < 4; ++grp) {
@@ -60,7 +66,7 @@ __device__ inline void compress(uint32_t h[8], uint32_t w[16]) {
       }
       const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
       const uint32_t ch = (e & f) ^ (~e & g);
-      const uint32_t t1 = k + S1 + ch + kK[grp * 16 + t] + w[t];
+      const uint32_t t1 = k + S1 + ch + K[grp * 16 + t] + w[t];
       const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
       const uint32_t mj = (a & b) ^ (a & c) ^ (b & c);
       k = g;
@@ -81,6 +87,30 @@ __device__ inline void compress(uint32_t h[8], uint32_t w[16]) {
   h[5] += f;
   h[6] += g;
   h[7] += k;
+}
+
+__device__ inline void compress(uint32_t h[8], uint32_t w[16]) { compress_k(h, w, kK); }
+
+// SHA-256 of a message in host memory (FIPS 180-4 Sec. 5.1.1 padding).
+inline void sha256_host(const uint8_t* msg, size_t len, uint8_t out[32]) {
+  uint32_t h[8] = {SV_SHA256_H0};
+  const size_t total = (len + 9 + 63) / 64 * 64;  // message, 0x80, 64-bit length
+  for (size_t off = 0; off < total; off += 64) {
+    uint8_t blk[64];
+    for (int i = 0; i < 64; ++i) {
+      const size_t p = off + (size_t)i;
+      blk[i] = p < len ? msg[p] : (p == len ? 0x80 : 0);
+    }
+    if (off + 64 == total)
+      for (int i = 0; i < 8; ++i) blk[56 + i] = (uint8_t)(((uint64_t)len * 8) >> (56 - 8 * i));
+    uint32_t w[16];
+    for (int t = 0; t < 16; ++t)
+      w[t] = (uint32_t)blk[4 * t] << 24 | (uint32_t)blk[4 * t + 1] << 16 |
+             (uint32_t)blk[4 * t + 2] << 8 | blk[4 * t + 3];
+    compress_k(h, w, kKHost);
+  }
+  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < 4; ++j) out[4 * i + j] = (uint8_t)(h[i] >> (24 - 8 * j));
 }
 
 // The state after hashing one block of the key xor pad (pad = 0x36 or 0x5c
