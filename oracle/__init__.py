@@ -27,6 +27,7 @@ BF16 = 0
 FP32 = 1
 RULE_GREEDY = 1
 RULE_SPECULATIVE = 2
+RULE_RELAXED = 192  # private use: accept while p_i(x_i) > 0
 S_BAD_PROPOSAL = -1
 S_LIMIT = -2
 S_Q_UNAVAILABLE = -3

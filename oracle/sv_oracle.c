@@ -56,6 +56,9 @@
  *  - the inverse CDF walks token ids in ascending order and returns the first
  *    y whose running sum exceeds u*S;
  *  - an all-zero residual (reachable only through rounding) falls back to p_i;
+ *  - rule 192 (private use, the relaxed rule): accept x_i while p_i(x_i) > 0;
+ *    the additional token is drawn from p_{a+1} with the purpose-1 value of
+ *    position a+1; no draft row or q is read;
  *  - ov_commit (SDCP Sec. 6.3 steps 6-8, 6.5): a session whose acceptance step
  *    failed commits nothing and keeps its state; the proposal length M of the
  *    low-round test is the session's m; m_cap is restored by one after every
@@ -71,7 +74,10 @@
 #include <string.h>
 
 enum { OV_BF16 = 0, OV_FP32 = 1 };
-enum { OV_RULE_GREEDY = 1, OV_RULE_SPECULATIVE = 2 };
+/* rules: SDCP Sec. 10.2.2 (1, 2); 192 is a private-use value (192-255) for the
+ * relaxed rule the textbook describes (accept a token the target's profile
+ * could sample), which does not preserve the target distribution */
+enum { OV_RULE_GREEDY = 1, OV_RULE_SPECULATIVE = 2, OV_RULE_RELAXED = 192 };
 enum {
   OV_OK = 0,
   OV_ERR_ARG = -1,
@@ -487,7 +493,8 @@ static int verify_session(int64_t b, const void *target, const void *draft, cons
                           double *d_cdf, ov_scratch *sc) {
   /* SDCP Sec. 6.2 / Table 2 "sdcp-limit": 1 <= M <= m_max (<= 64) */
   if (m < 1 || m > M) return OV_S_LIMIT;
-  if ((rule != OV_RULE_GREEDY && rule != OV_RULE_SPECULATIVE) || s->reserved != 0 ||
+  if ((rule != OV_RULE_GREEDY && rule != OV_RULE_SPECULATIVE && rule != OV_RULE_RELAXED) ||
+      s->reserved != 0 ||
       s->top_p_milli > 1000)
     return OV_S_BAD_PROFILE;
   /* SDCP Sec. 6.3 step 5: no q rows for a rule that needs them */
@@ -508,6 +515,34 @@ static int verify_session(int64_t b, const void *target, const void *draft, cons
       load_row(draft, dtype, drow0 + i - 1, V, sc->l);
       if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
     }
+
+  if (rule == OV_RULE_RELAXED) {
+    /* Relaxed rule (textbook, "Speculative decoding": accept a token that is
+     * in the target's top-k): x_i is accepted while p_i(x_i) > 0, i.e. while
+     * the target's profile (temperature, top-k, top-p) could sample it; the
+     * additional token is drawn from p_{a+1} with the purpose-1 value of
+     * position a+1.  The probe holds p_i(x_i) at every position. */
+    int a = -1;
+    for (int i = 1; i <= m; ++i) {
+      double dt;
+      load_row(target, dtype, trow0 + i - 1, V, sc->l);
+      profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+      set_if(d_topp_t, b * (int64_t)(M + 1) + i - 1, dt);
+      const double px = sc->p[x[i - 1]];
+      set_if(p_tok, b * (int64_t)M + i - 1, px);
+      if (a < 0 && !(px > 0.0)) a = i - 1;
+      if (a < 0) out[i - 1] = x[i - 1];
+      if (a >= 0 && !p_tok) break;
+    }
+    if (a < 0) a = m;
+    double dt, dc;
+    load_row(target, dtype, trow0 + a, V, sc->l);
+    profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+    set_if(d_topp_t, b * (int64_t)(M + 1) + a, dt);
+    out[a] = inverse_cdf(sc->p, V, rng_uniform(g, (uint32_t)(a + 1), 1), &dc);
+    set_if(d_cdf, b, dc);
+    return a;
+  }
 
   if (rule == OV_RULE_GREEDY) {
     /* SDCP Sec. 6.4 Rule 1: accept x_i while it equals argmax p_i (the argmax
@@ -761,8 +796,9 @@ void ov_contract_digest(const uint8_t *cbor, size_t len, uint8_t out[32]) {
 
 /*
  * One round's commit for B sessions, after the acceptance step:
- *   accepted_len [B]  a (>= 0), or a negative status: such a session commits
- *                     nothing, its state is left as it is and its action is -1;
+ *   accepted_len [B]  a in [0, M], else (a negative status, or out of range)
+ *                     the session commits nothing, its state is left as it is
+ *                     and its action is -1;
  *   out_tokens [B, M+1]  the a+1 emitted tokens, then -1; truncated in place
  *                     after the first stop token and at max_new [Sec. 6.3
  *                     step 6]: entries past the committed ones become -1;
@@ -796,7 +832,7 @@ int ov_commit(const ov_contract *contract, ov_state *state, const int32_t *m,
     ov_state *s = &state[b];
     int32_t *out = out_tokens + b * (int64_t)(M + 1);
     const int32_t a = accepted_len[b];
-    if (a < 0) {
+    if (a < 0 || a > M) {
       emitted_len[b] = 0;
       action[b] = -1;
       continue;
