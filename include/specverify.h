@@ -95,7 +95,15 @@ typedef struct sv_sdcp_session {
   uint32_t reserved;      /* ignored; set to 0 */
 } sv_sdcp_session;
 
-enum { SV_RULE_GREEDY = 1, SV_RULE_SPECULATIVE = 2 }; /* SDCP Sec. 10.2.2 */
+/* Acceptance rules: 1 and 2 are SDCP's (Sec. 6.4, registry Sec. 10.2.2).  192,
+ * from the registry's private-use range (192-255), is the relaxed rule of the
+ * textbook chapter ("Speculative decoding": accept a token in the target's
+ * top-k, no longer sampling from p): x_i is accepted while p_i(x_i) > 0, i.e.
+ * while the target's profile could sample it (with top-k alone, membership of
+ * the target's top-k); the additional token is drawn from p_{a+1} with the
+ * purpose-1 value of position a+1; no draft row or q is read; the probe's
+ * p_tok holds p_i(x_i) at every position and q_tok is -1. */
+enum { SV_RULE_GREEDY = 1, SV_RULE_SPECULATIVE = 2, SV_RULE_RELAXED = 192 };
 enum { SV_BF16 = 0, SV_FP32 = 1 };                   /* logits element type */
 
 /* Call-level return codes of sv_verify, sv_verify_sdcp and sv_verify_qrows. */
@@ -111,7 +119,7 @@ enum {
  * Checked in this order. */
 enum {
   SV_S_LIMIT = -2,         /* m[b] outside [1, M]          (sdcp-limit) */
-  SV_S_BAD_PROFILE = -4,   /* rule not 1/2, top_p_milli > 1000, reserved != 0 */
+  SV_S_BAD_PROFILE = -4,   /* rule not 1, 2 or 192, top_p_milli > 1000, reserved != 0 */
   SV_S_Q_UNAVAILABLE = -3, /* rule 2 and draft_logits == NULL (sdcp-q-unavailable) */
   SV_S_BAD_PROPOSAL = -1,  /* a token outside [0, V); or, after the logits check,
                               q_i(x_i) == 0 for some i <= m[b] (sdcp-bad-proposal) */

@@ -26,6 +26,7 @@ BF16 = 0
 FP32 = 1
 RULE_GREEDY = 1
 RULE_SPECULATIVE = 2
+RULE_RELAXED = 192  # private use: accept while p_i(x_i) > 0
 OK = 0
 ERR_ARG = -1
 ERR_DEVICE = -2

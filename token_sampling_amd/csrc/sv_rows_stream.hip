@@ -32,7 +32,8 @@ __device__ inline int session_status(int b, const int32_t* tokens, const int32_t
   const int rl = rule[b];
   const sv_sampling s = sampling[b];
   if (mb < 1 || mb > M) return SV_S_LIMIT;
-  if ((rl != SV_RULE_GREEDY && rl != SV_RULE_SPECULATIVE) || s.reserved != 0 || s.top_p_milli > 1000)
+  if ((rl != SV_RULE_GREEDY && rl != SV_RULE_SPECULATIVE && rl != SV_RULE_RELAXED) ||
+      s.reserved != 0 || s.top_p_milli > 1000)
     return SV_S_BAD_PROFILE;
   if (rl == SV_RULE_SPECULATIVE && !has_draft) return SV_S_Q_UNAVAILABLE;
   const int32_t x = lane < mb ? tokens[(size_t)b * M + lane] : 0;
@@ -43,7 +44,8 @@ __device__ inline int session_status(int b, const int32_t* tokens, const int32_t
 // Verifier value g of the [B, 2M+1] table: j = g mod (2M+1) < M is the
 // acceptance value of position j+1, j >= M the additional-token value of
 // position j-M+1.  Only speculative-sampling sessions with a valid m use
-// them, and only at positions up to m (acceptance) or m+1 (additional token).
+// them (and relaxed-rule sessions, their additional-token values), and only at
+// positions up to m (acceptance) or m+1 (additional token).
 __device__ inline void sdcp_value(int64_t g, const sv_sdcp_session* __restrict__ sessions,
                                   const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
                                   int B, int M, double* __restrict__ unif) {
@@ -54,7 +56,9 @@ __device__ inline void sdcp_value(int64_t g, const sv_sdcp_session* __restrict__
   const uint32_t purpose = j < M ? 0u : 1u;
   const int pos = j < M ? j + 1 : j - M + 1;
   const int mb = m[b];
-  if (rule[b] != SV_RULE_SPECULATIVE || mb < 1 || mb > M || pos > mb + (int)purpose) return;
+  const int rl = rule[b];
+  if (rl != SV_RULE_SPECULATIVE && !(rl == SV_RULE_RELAXED && purpose == 1)) return;
+  if (mb < 1 || mb > M || pos > mb + (int)purpose) return;
   const uint2* rec = (const uint2*)(sessions + b);  // 32 bytes, 8-byte aligned
   const uint2 id01 = rec[0], id23 = rec[1], sd = rec[2], rd = rec[3];
   const uint32_t id[4] = {__builtin_bswap32(id01.x), __builtin_bswap32(id01.y),

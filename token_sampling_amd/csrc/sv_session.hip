@@ -127,6 +127,7 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     }
     if (__any(lane < mb && !(qx > 0.0 && qx < INFINITY))) st = SV_S_BAD_PROPOSAL;
   }
+  if (st == 0 && rl == SV_RULE_RELAXED && lane < mb) px = rr[lane].ptok;
 
   if (st < 0) {
     write_failed(b, st, M, accepted_len, out_tokens, p_tok, q_tok);
@@ -142,6 +143,26 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
     extra = rr[a].argmax;
+  } else if (rl == SV_RULE_RELAXED) {
+    // relaxed rule (private use 192): accept x_i while p_i(x_i) > 0; the
+    // additional token is drawn from p_{a+1} with the purpose-1 value of
+    // position a+1, from the listed support or by the whole workgroup
+    const bool acc = lane < mb && px > 0.0;
+    const uint64_t rej = ~(uint64_t)__ballot(acc);
+    a = rej == 0 ? kWave : __builtin_ctzll(rej);
+    a = a < mb ? a : mb;
+    double ua, ud;
+    if (unif) ud = unif[(size_t)b * R + M + a];
+    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+    const RowRec& P = rr[a];
+    if (P.nsup > 0) {
+      bool bad = false;
+      extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
+                          sup_p + ((size_t)b * R + a) * kSupMax, P.nsup, nullptr, nullptr, 0,
+                          nullptr, ud, q_id, q_p, &bad);
+    } else {
+      job = Job{kJobBonus, a, a, -1, ud};
+    }
   } else {
     // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i)); the values
     // are SDCP's (computed by the row kernel into unif) or Philox's
@@ -185,9 +206,10 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     out[j] = v;
   }
   for (int j = lane; j < M; j += kWave) {
-    const bool have = rl == SV_RULE_SPECULATIVE && j < mb;
-    if (p_tok) p_tok[(size_t)b * M + j] = have ? px : -1.0;
-    if (q_tok) q_tok[(size_t)b * M + j] = have ? qx : -1.0;
+    const bool have_p = (rl == SV_RULE_SPECULATIVE || rl == SV_RULE_RELAXED) && j < mb;
+    const bool have_q = rl == SV_RULE_SPECULATIVE && j < mb;
+    if (p_tok) p_tok[(size_t)b * M + j] = have_p ? px : -1.0;
+    if (q_tok) q_tok[(size_t)b * M + j] = have_q ? qx : -1.0;
   }
   return job;
 }
