@@ -313,3 +313,22 @@ def test_dense_kernel_edge_cases():
     assert o["accepted_len"][1] == M                               # identical rows: all accepted
     g = parity.run_gpu(h)
     parity.compare(g, o, "dense-edges")
+
+
+@pytest.mark.parametrize("split", ["1", "2", "4"])
+def test_split_rows_each_factor(split, monkeypatch):
+    """The single-pass kernel with each top-k-class row streamed by 1, 2 or 4
+    waves (forced through SV_ROWS_SPLIT), on top-k, one-hot and dense profiles,
+    a vocabulary of one tile (waves with empty parts), and rows that overflow
+    the candidate region (handed to the generic kernel)."""
+    monkeypatch.setenv("SV_ROWS_SPLIT", split)
+    parity.log(f"[case] split={split}")
+    for seed, B, M, V in ((111, 24, 5, 20000), (112, 12, 3, 300), (113, 8, 2, 4097)):
+        h = mixed_case(seed, B, M, V, "bf16")
+        if seed == 113:  # ascending logits: many candidates in every part of the row
+            ramp = np.linspace(-4, 4, V, dtype=np.float32)
+            h["target"][0] = oracle.bf16_bits(np.broadcast_to(ramp, (M + 1, V)))
+            h["sampling"][0]["top_k"] = 64
+            h["sampling"][0]["temperature_milli"] = 1000
+        g = parity.run_gpu(h)
+        parity.compare(g, parity.run_oracle(h), f"split{split}-{seed}")

@@ -13,6 +13,8 @@
 // With SDCP verifier values (Sec. 6.4) the grid starts with extra workgroups
 // that compute them, one value per lane; they depend on no logits, so they
 // run while the row waves stream.
+#include <stdlib.h>
+
 #include "sv_kernels.hpp"
 #include "sv_rows_dense.hpp"
 #include "sv_rows_topk.hpp"
@@ -116,10 +118,137 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
   }
 }
 
+// The same row slots with each top-k-class row split over S waves of one
+// workgroup, for launches with few rows: one wave alone needs about 90 us for
+// a 128K-logit top-50 row (57 us of it streaming with ten tiles in flight, the
+// rest candidate insertion), so a few long rows leave the chip idle.  Wave w streams tiles
+// [w T / S, (w + 1) T / S) with its own first bound (a bound from any part of
+// the row bounds the row's k-th best), cuts its region to its k best, and wave
+// 0 merges the S lists (at most S * 64 <= kCap entries) and finishes the row.
+// Dense-class rows are profiled by one wave of the workgroup alone.
+template <int S>
+__global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
+    const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
+    int B, int M, int V, int32_t* __restrict__ sess_status, RowRec* __restrict__ rows,
+    int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
+    const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks) {
+  static_assert(S * kSupMax <= topk::kCap, "the merged lists fit one region");
+  constexpr int kWords = (S * topk::kCap > kLdsWords ? S * topk::kCap : kLdsWords);
+  __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or the dense histogram
+  __shared__ int cnt_s[S], ovf_s[S];
+  __shared__ uint32_t mm_s[S], um_s[S];
+  const int lane = __lane_id();
+  const int wid = (int)threadIdx.x / kWave;
+  if ((int)blockIdx.x < n_value_blocks) {
+    sdcp_value((int64_t)blockIdx.x * (S * kWave) + threadIdx.x, sessions, m, rule, B, M, unif);
+    return;
+  }
+  const int R = 2 * M + 1;
+  const int slot_g = blockIdx.x - n_value_blocks;
+  const int b = slot_g / R;
+  const int slot = slot_g - b * R;
+  if (b >= B) return;
+  const int st = session_status(b, tokens, m, rule, sampling, M, V, has_draft != 0);
+  if (wid == 0 && slot == 0 && lane == 0) sess_status[b] = st;
+  if (st != 0 || dtype != SV_BF16) return;
+  const int mb = m[b];
+  const int rl = rule[b];
+  const bool is_target = slot <= M;
+  const int i = is_target ? slot + 1 : slot - M;  // 1-based position
+  if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb || draft == nullptr))
+    return;
+  const sv_sampling smp = sampling[b];
+  const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
+  const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
+                                  : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
+  RowRec* rec = rows + (size_t)slot_g;
+  if (row_uses_topk_kernel(SV_BF16, rl, smp)) {
+    const bool one_hot = rl == SV_RULE_GREEDY || smp.temperature_milli == 0;
+    const int k = one_hot ? 1 : (int)smp.top_k;
+    const int T = topk::row_tiles(row, V);
+    uint64_t* reg = lds + wid * topk::kCap;
+    topk::WaveState s;
+    topk::chunk_scan(row, V, k, wid * T / S, (wid + 1) * T / S, s, reg);
+    const int n = s.overflow ? 0 : topk::region_cut(reg, s.n, k).n;
+    uint32_t mm = s.magmax, um = s.umax;
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      mm = stream::max_u16x2(mm, __shfl_xor(mm, off, kWave));
+      um = stream::max_u16x2(um, __shfl_xor(um, off, kWave));
+    }
+    if (lane == 0) {
+      cnt_s[wid] = n;
+      ovf_s[wid] = s.overflow ? 1 : 0;
+      mm_s[wid] = mm;
+      um_s[wid] = um;
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    int ovf = 0, total = cnt_s[0];
+    uint32_t mmax = mm_s[0], umax = um_s[0];
+#pragma unroll
+    for (int w = 1; w < S; ++w) {
+      ovf |= ovf_s[w];
+      mmax = stream::max_u16x2(mmax, mm_s[w]);
+      umax = stream::max_u16x2(umax, um_s[w]);
+      const int c = cnt_s[w];
+      if (lane < c) reg[total + lane] = lds[w * topk::kCap + lane];
+      total += c;
+    }
+    ovf |= ovf_s[0];
+    if (ovf) {  // a part overflowed its region: the generic kernel takes the row
+      if (lane == 0) {
+        RowRec r{};
+        r.status = kRowFallback;
+        *rec = r;
+      }
+      return;
+    }
+    const size_t so = (size_t)slot_g * kSupMax;
+    topk::row_finish(reg, total, k, lane == 0 ? mmax : 0u, lane == 0 ? umax : 0u, one_hot,
+                     smp.temperature_milli, smp.top_p_milli, x, rec, sup_id + so, sup_p + so);
+  } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
+    // one wave, chosen by the slot, so that dense rows spread over the SIMDs
+    if (wid == slot_g % S) dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+  }
+}
+
 }  // namespace
+
+// Waves per top-k-class row.  Measured on b256 rows (bf16, V = 128256): a
+// part of a row costs more than its share, since every part starts with a
+// low threshold and inserts many candidates, so splitting pays only while the
+// launch has under about one row per SIMD: 4 waves per row below 1024 rows
+// (272 rows: 91 -> 59 us; 768 rows: 104 -> 91 us), 1 above (2304 rows: 120 us
+// with 1 wave, 132 us with 2).  SV_ROWS_SPLIT (1, 2 or 4) overrides the choice.
+static int rows_split_factor(const LaunchArgs& a) {
+  const char* env = getenv("SV_ROWS_SPLIT");
+  if (env) {
+    const int s = atoi(env);
+    if (s == 1 || s == 2 || s == 4) return s;
+  }
+  const size_t rows = (size_t)a.B * (a.M + 1) + (a.draft ? (size_t)a.B * a.M : 0);
+  return rows < 1024 ? 4 : 1;
+}
+
+template <int S>
+static void launch_split(const LaunchArgs& a, hipStream_t st, size_t slots) {
+  const int per_block = S * kWave;
+  const int n_value_blocks = a.sdcp ? (int)((slots + per_block - 1) / per_block) : 0;
+  const unsigned grid = (unsigned)(slots + n_value_blocks);
+  hipLaunchKernelGGL((k_rows_split<S>), dim3(grid), dim3(per_block), 0, st,
+                     (const uint16_t*)a.target, (const uint16_t*)a.draft, a.dtype, a.tokens, a.m,
+                     a.rule, a.sampling, (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B,
+                     a.M, a.V, a.sess_status, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
+                     n_value_blocks);
+}
 
 void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   const size_t slots = (size_t)a.B * (2 * a.M + 1);
+  const int split = rows_split_factor(a);
+  if (split == 2) return launch_split<2>(a, st, slots);
+  if (split == 4) return launch_split<4>(a, st, slots);
   const int n_value_blocks = a.sdcp ? (int)((slots + kWave - 1) / kWave) : 0;
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,

@@ -230,11 +230,13 @@ struct WaveState {
 // dword (two logits per lane) at a time.  A lane whose dword holds a key at or
 // above the threshold stores both halves as a pair of region entries, the
 // half below the threshold as an empty entry: one ballot per dword.
+// Positions outside the window [lo, hi) (the row, or a chunk of it) read as
+// -inf; ids are positions minus head.
 __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&v)[kVec], int tile,
-                                    int head, int V) {
+                                    int head, int lo, int hi) {
   if (s.overflow) return;
   const int lane = __lane_id();
-  if ((tile == 0 && head > 0) || (tile + 1) * kTile > head + V) mask_tile<kVec>(v, tile, head, head + V);
+  if (tile * kTile < lo || (tile + 1) * kTile > hi) mask_tile<kVec>(v, tile, lo, hi);
   int lm;
   if (s.raw) {
     lm = tile_raw(v, s.umax);
@@ -404,21 +406,28 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   if (lane == 0) *rec = r;
 }
 
-// The profile of one row of the top-k class, by one wave: rows whose support
-// lies among the k <= 64 best tokens (k = 1 for one-hot profiles).  reg is
-// the wave's LDS region of kCap entries; sup_id, sup_p its listed support.
-__device__ __attribute__((always_inline)) inline void row_profile(
-    const uint16_t* row, int V, int k, bool one_hot, const sv_sampling& smp, int32_t x, RowRec* rec,
-    int32_t* sup_id, double* sup_p, uint64_t* reg) {
-  const int lane = __lane_id();
-  // 16-byte aligned window over the row: positions [head, head + V) are the row
-  const int head = (int)(((uintptr_t)row & 15u) >> 1);
+// Tiles of a row in the 16-byte aligned window over it: positions
+// [head, head + V) are the row.
+__device__ inline int row_head(const uint16_t* row) { return (int)(((uintptr_t)row & 15u) >> 1); }
+__device__ inline int row_tiles(const uint16_t* row, int V) {
+  return (row_head(row) + V + kTile - 1) / kTile;
+}
+
+// Stream tiles [t0, t1) of one row into the wave's candidate region reg (a
+// superset of that chunk's k best is left there, s.n entries, unless
+// s.overflow).  Loads past the chunk re-read its last vector; an empty chunk
+// (t1 <= t0) loads nothing.
+__device__ __attribute__((always_inline)) inline void chunk_scan(const uint16_t* row, int V, int k,
+                                                                 int t0, int t1, WaveState& s,
+                                                                 uint64_t* reg) {
+  const int head = row_head(row);
   const u32x4* vbase = (const u32x4*)(row - head);
   const int npos = head + V;
   const int nvec = (npos + 7) / 8;
-  const int ntiles = (npos + kTile - 1) / kTile;
+  const int lo = max(head, t0 * kTile), hi = min(npos, t1 * kTile);
+  const int gmax = min(nvec, (t1 * kTile) / 8) - 1;  // last vector of the chunk
+  const int ntiles = t1 - t0;
 
-  WaveState s;
   s.n = 0;
   s.thr = -0x8000;
   s.strict = false;
@@ -426,6 +435,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
   s.raw = false;
   s.magmax = 0;
   s.umax = 0;
+  if (ntiles <= 0) return;  // gmax would be below the row
 
   // ring of kNBuf tiles: while one is processed the next kNBuf - 1 are in
   // flight.  The loop runs whole rounds of kNBuf tiles with no exit inside a
@@ -436,7 +446,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
   // scheduling barriers), as the steady state issues them
 #pragma unroll
   for (int u = 0; u < kNBuf - 1; ++u) {
-    load_tile<kVec>(ring[u], vbase, u, nvec - 1);
+    load_tile<kVec>(ring[u], vbase, t0 + u, gmax);
     __builtin_amdgcn_sched_barrier(0);
   }
   // the first bound: among the first kBoundTiles tiles, the k-th largest of
@@ -445,7 +455,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
   {
 #pragma unroll
     for (int u = 0; u < kBoundTiles; ++u)
-      if ((u == 0 && head > 0) || (u + 1) * kTile > head + V) mask_tile<kVec>(ring[u], u, head, head + V);
+      if ((t0 + u) * kTile < lo || (t0 + u + 1) * kTile > hi) mask_tile<kVec>(ring[u], t0 + u, lo, hi);
     int lmv[kBoundTiles];
 #pragma unroll
     for (int u = 0; u < kBoundTiles; ++u) lmv[u] = lane_max_raw(ring[u]);
@@ -464,11 +474,22 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     set_priority(nround - r, nround);
 #pragma unroll
     for (int u = 0; u < kNBuf; ++u) {
-      const int tt = r * kNBuf + u;
-      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec - 1);
-      tile_process(s, reg, k, ring[u], tt, head, V);
+      const int tt = t0 + r * kNBuf + u;
+      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, gmax);
+      tile_process(s, reg, k, ring[u], tt, head, lo, hi);
     }
   }
+}
+
+// The profile of one row of the top-k class, by one wave: rows whose support
+// lies among the k <= 64 best tokens (k = 1 for one-hot profiles).  reg is
+// the wave's LDS region of kCap entries; sup_id, sup_p its listed support.
+__device__ __attribute__((always_inline)) inline void row_profile(
+    const uint16_t* row, int V, int k, bool one_hot, const sv_sampling& smp, int32_t x, RowRec* rec,
+    int32_t* sup_id, double* sup_p, uint64_t* reg) {
+  const int lane = __lane_id();
+  WaveState s;
+  chunk_scan(row, V, k, 0, row_tiles(row, V), s, reg);
   if (s.overflow) {
     if (lane == 0) {
       RowRec r{};
