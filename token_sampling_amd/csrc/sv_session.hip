@@ -215,9 +215,9 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
 }
 
 constexpr int kSampleNT = 1024;                  // threads per session
-constexpr int kSampleE = 4;                      // consecutive tokens per thread per group
-constexpr int kGroup = kSampleNT * kSampleE;     // ids per group
-constexpr int kMaxChunks = kSampleNT;            // chunks of whole groups, one per thread
+constexpr int kSampleWaves = kSampleNT / kWave;  // waves per session
+constexpr int kSub = kWave * 4;                  // ids per sub-block: 4 consecutive per lane
+constexpr int kMaxGroups = kSampleNT;            // groups of whole sub-blocks (one per thread)
 constexpr int kLut = 2048;                       // probabilities tabled per row (by key)
 
 // One row's profile as the sampler sees it: p(y) = w(y) / Z' on the support.
@@ -283,61 +283,86 @@ __device__ T block_exclusive_scan(T v, T* wsum, T* total) {
 }
 
 struct SampleSmem {
-  double lut_p[kLut];             // p of the keys below p's largest key
-  double lut_q[kLut];             // q of the keys below q's largest key
-  double chunk_mass[kMaxChunks];  // mass of each chunk
-  uint32_t ties_p[kMaxChunks];    // ties of p's cut key before each chunk
-  uint32_t ties_q[kMaxChunks];    // ties of q's cut key before each chunk
-  double dsum[kSampleNT / kWave];
-  uint32_t usum[kSampleNT / kWave];
-  int32_t ired[kSampleNT / kWave];
+  double lut_p[kLut];         // p of the keys below p's largest key
+  double lut_q[kLut];         // q of the keys below q's largest key
+  double mass[kMaxGroups];    // weight of each group
+  uint64_t ties[kMaxGroups];  // the cut keys' ties in each group (p low word, q high), then before it
+  double dsum[kSampleWaves];
+  uint64_t usum[kSampleWaves];
+  int32_t ired[kSampleWaves];
   double base;
 };
 
-// Weights of this thread's kSampleE tokens of a group (ids y0 ..): the residual
-// max(0, p - q) (zero where p is zero) or p.  q comes from the draft row's
-// profile Q, or (kQ) from the published q row qrow, whose entries where p > 0
-// must be finite and non-negative (else bad is set).  tp, tq: ties of each
-// row's cut key before the group; on return they count the group's ties too.
+// The draw of one session's additional token: weights w(y) = max(0, p(y) -
+// q(y)) (zero where p is zero) for the residual, or p(y); the smallest id
+// whose running weight exceeds u * S.
 template <class Tr, bool kQ>
-__device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, const float* qrow,
-                              bool resid, bool ties, int y0, int V, uint32_t& tp, uint32_t& tq,
-                              double (&w)[kSampleE], bool& bad, SampleSmem& sm) {
-  uint32_t up[kSampleE], uq[kSampleE];
+struct Draw {
+  SampleRow<Tr> P, Q;  // Q unused with kQ
+  const float* qrow;   // the published q row (kQ)
+  bool resid;
+  int V;
+};
+
+// Bits of this lane's 4 consecutive ids of the sub-block starting at y0.
+template <class Tr, bool kQ>
+__device__ inline void sub_load(const Draw<Tr, kQ>& d, int y0, uint32_t (&up)[4],
+                                uint32_t (&uq)[4]) {
+  const int y = y0 + 4 * __lane_id();
 #pragma unroll
-  for (int e = 0; e < kSampleE; ++e) {
-    const bool in = y0 + e < V;
-    up[e] = in ? Tr::bits(P.row[y0 + e]) : Tr::kNegInfBits;
-    if constexpr (kQ) uq[e] = (in && resid) ? __float_as_uint(qrow[y0 + e]) : 0u;
-    else uq[e] = (in && resid) ? Tr::bits(Q.row[y0 + e]) : Tr::kNegInfBits;
+  for (int e = 0; e < 4; ++e) {
+    const bool in = y + e < d.V;
+    up[e] = in ? Tr::bits(d.P.row[y + e]) : Tr::kNegInfBits;
+    if constexpr (kQ) uq[e] = (in && d.resid) ? __float_as_uint(d.qrow[y + e]) : 0u;
+    else uq[e] = (in && d.resid) ? Tr::bits(d.Q.row[y + e]) : Tr::kNegInfBits;
   }
-  int rp[kSampleE], rq[kSampleE];
+}
+
+// Which of the 4 ids hold a cut key whose ties are kept by rank: bit e for p,
+// bit 4 + e for q.
+template <class Tr, bool kQ>
+__device__ inline uint32_t sub_tie_bits(const Draw<Tr, kQ>& d, const uint32_t (&up)[4],
+                                        const uint32_t (&uq)[4]) {
+  uint32_t f = 0;
 #pragma unroll
-  for (int e = 0; e < kSampleE; ++e) rp[e] = rq[e] = 0;
-  if (ties) {  // ranks among the cut keys' ties, in id order (group counts < 2^16)
-    uint32_t mine = 0;
-#pragma unroll
-    for (int e = 0; e < kSampleE; ++e) {
-      mine += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1u : 0u;
-      mine += (!kQ && resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 0x10000u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t before = block_exclusive_scan<uint32_t>(mine, sm.usum, &tot);
-    int cp = (int)(tp + (before & 0xFFFFu)), cq = (int)(tq + (before >> 16));
-#pragma unroll
-    for (int e = 0; e < kSampleE; ++e) {
-      rp[e] = cp;
-      rq[e] = cq;
-      cp += (P.tie_mode() && Tr::key(up[e]) == P.r.kcut) ? 1 : 0;
-      cq += (!kQ && resid && Q.tie_mode() && Tr::key(uq[e]) == Q.r.kcut) ? 1 : 0;
-    }
-    tp += tot & 0xFFFFu;
-    tq += tot >> 16;
+  for (int e = 0; e < 4; ++e) {
+    if (d.P.tie_mode() && Tr::key(up[e]) == d.P.r.kcut) f |= 1u << e;
+    if (!kQ && d.resid && d.Q.tie_mode() && Tr::key(uq[e]) == d.Q.r.kcut) f |= 16u << e;
   }
+  return f;
+}
+
+// Exclusive prefix over the wave's lanes of a small count (0..7), and the
+// wave total, from one ballot per bit.
+__device__ inline int wave_excl_small(int c, int* total) {
+  int r = 0, t = 0;
 #pragma unroll
-  for (int e = 0; e < kSampleE; ++e) {
-    const double p = P.prob(y0 + e, up[e], rp[e]);
-    if (!resid) {
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t bm = __ballot((c >> bit) & 1);
+    r += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0)) << bit;
+    t += __builtin_popcountll(bm) << bit;
+  }
+  *total = t;
+  return r;
+}
+
+// Weights of this lane's 4 ids of a sub-block.  rp, rq: the cut keys' ties
+// before the sub-block (wave-uniform); on return they count its ties too.
+template <class Tr, bool kQ>
+__device__ inline void sub_weights(const Draw<Tr, kQ>& d, int y0, const uint32_t (&up)[4],
+                                   const uint32_t (&uq)[4], uint32_t& rp, uint32_t& rq,
+                                   double (&w)[4], bool& bad) {
+  const uint32_t f = sub_tie_bits<Tr, kQ>(d, up, uq);
+  int tp, tq;
+  const int bp = wave_excl_small(__builtin_popcount(f & 15u), &tp);
+  const int bq = wave_excl_small(__builtin_popcount(f >> 4), &tq);
+  int cp = (int)rp + bp, cq = (int)rq + bq;
+  const int y = y0 + 4 * __lane_id();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double p = d.P.prob(y + e, up[e], cp);
+    if (!d.resid) {
       w[e] = p;
     } else {
       double q;
@@ -345,24 +370,51 @@ __device__ void group_weights(const SampleRow<Tr>& P, const SampleRow<Tr>& Q, co
         q = (double)__uint_as_float(uq[e]);
         bad |= p > 0.0 && !(q >= 0.0 && q < INFINITY);
       } else {
-        q = Q.prob(y0 + e, uq[e], rq[e]);
+        q = d.Q.prob(y + e, uq[e], cq);
       }
-      const double d = p - q;
-      w[e] = (p > 0.0 && d > 0.0) ? d : 0.0;
+      const double df = p - q;
+      w[e] = (p > 0.0 && df > 0.0) ? df : 0.0;
     }
+    cp += (f >> e) & 1u;
+    cq += (f >> (4 + e)) & 1u;
   }
+  rp += (uint32_t)tp;
+  rq += (uint32_t)tq;
+}
+
+// Calls fn(y0, up, uq) for the sub-blocks of [lo, hi) in order (lo and hi on
+// sub-block boundaries, or hi = V).  (Loading four sub-blocks ahead measured
+// slower: the registers it needs push the kernel to its limit.)
+template <class Tr, bool kQ, class F>
+__device__ inline void stream_subs(const Draw<Tr, kQ>& d, int lo, int hi, F&& fn) {
+  for (int y0 = lo; y0 < hi; y0 += kSub) {
+    uint32_t up[4], uq[4];
+    sub_load<Tr, kQ>(d, y0, up, uq);
+    fn(y0, up, uq);
+  }
+}
+
+__device__ inline double wave_incl_scan(double v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
 }
 
 // Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2: additional token from
 // norm(max(0, p_j - q_j)) at the first rejection j, or from p_{m+1}; the
-// smallest id whose running mass exceeds u * S.  One workgroup per session.
-// One pass in id order records the mass of each chunk (a run of whole groups
-// of kGroup ids) and the cut keys' tie counts before it; a scan over the
-// chunk masses finds the chunk holding u * S, and from there the groups are
-// weighed again until the token is found.
-// One workgroup per session: its first wave takes the acceptance decisions
-// (finalize_session); a draw from rows without listed supports then takes
-// the whole workgroup.
+// smallest id whose running weight exceeds u * S.  One workgroup per session:
+// its first wave takes the acceptance decisions (finalize_session); a draw
+// from rows without listed supports then takes the whole workgroup.
+// The row is cut into at most kMaxGroups groups of whole sub-blocks; each wave
+// owns a run of consecutive groups and streams them with no workgroup barrier:
+// a first pass counts the cut keys' ties per group when they are kept by rank
+// (a workgroup scan then gives each group its ties before it), a second pass
+// weighs every group; a scan over the group weights finds the group holding
+// u * S, which one wave weighs again with a wave scan.
 template <class Tr, bool kQ>
 __global__ __launch_bounds__(kSampleNT) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
@@ -390,51 +442,82 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
   const Job job = job_s;
   if (job.kind == kJobNone) return;
   const int R = 2 * M + 1;
-  SampleRow<Tr> P{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V, rows[(size_t)b * R + job.trow],
-                  0, nullptr};
-  SampleRow<Tr> Q = P;
-  const float* qrow = nullptr;
-  bool resid = job.kind == kJobResidual;
-  if (resid) {
-    if constexpr (kQ) qrow = qrows + ((size_t)b * M + job.drow) * (size_t)V;
-    else Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
-                           rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
+  Draw<Tr, kQ> d;
+  d.P = SampleRow<Tr>{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V,
+                      rows[(size_t)b * R + job.trow], 0, nullptr};
+  d.Q = d.P;
+  d.qrow = nullptr;
+  d.resid = job.kind == kJobResidual;
+  d.V = V;
+  if (d.resid) {
+    if constexpr (kQ) d.qrow = qrows + ((size_t)b * M + job.drow) * (size_t)V;
+    else d.Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
+                             rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
   }
-  fill_lut<Tr>(P, sm.lut_p);
-  if (!kQ) fill_lut<Tr>(Q, sm.lut_q);
-  __syncthreads();
-  const int ngroups = (V + kGroup - 1) / kGroup;
-  const int G = (ngroups + kMaxChunks - 1) / kMaxChunks;  // groups per chunk
-  const int nchunks = (ngroups + G - 1) / G;
+  fill_lut<Tr>(d.P, sm.lut_p);
+  if (!kQ) fill_lut<Tr>(d.Q, sm.lut_q);
 
-  // the pass: every chunk's mass in id order, and the last id with mass
+  // groups: at most kMaxGroups runs of Lg ids (whole sub-blocks); wave w owns
+  // groups [g0, g1)
+  const int nsub = (V + kSub - 1) / kSub;
+  const int sub_per_group = (nsub + kMaxGroups - 1) / kMaxGroups;
+  const int Lg = sub_per_group * kSub;
+  const int ng = (V + Lg - 1) / Lg;
+  const int wid = (int)threadIdx.x / kWave, lane = __lane_id();
+  const int g0 = wid * ng / kSampleWaves, g1 = (wid + 1) * ng / kSampleWaves;
+  const bool ties = d.P.tie_mode() || (!kQ && d.resid && d.Q.tie_mode());
+
+  // the ties of each group, then of all groups before it
+  const int lo = g0 * Lg, hi = min(g1 * Lg, V);  // this wave's ids
+  if (ties) {
+    uint32_t cp = 0, cq = 0;
+    stream_subs<Tr, kQ>(d, lo, hi, [&](int y0, const uint32_t(&up)[4], const uint32_t(&uq)[4]) {
+      const uint32_t f = sub_tie_bits<Tr, kQ>(d, up, uq);
+      cp += __builtin_popcount(f & 15u);
+      cq += __builtin_popcount(f >> 4);
+      const int g = y0 / Lg;
+      if (y0 + kSub >= min((g + 1) * Lg, V)) {  // the group's last sub-block
+        const uint64_t c = wave_reduce((uint64_t)cp | ((uint64_t)cq << 32), OpAdd());
+        if (lane == 0) sm.ties[g] = c;
+        cp = cq = 0;
+      }
+    });
+    __syncthreads();
+    uint64_t tot;
+    const uint64_t c = (int)threadIdx.x < ng ? sm.ties[threadIdx.x] : 0ull;
+    const uint64_t before = block_exclusive_scan<uint64_t>(c, sm.usum, &tot);
+    if ((int)threadIdx.x < ng) sm.ties[threadIdx.x] = before;
+  }
+  __syncthreads();  // tables and tie counts are ready
+
+  // every group's weight, and the last id with weight
   int32_t last = -1;
   bool bad = false;
   for (int attempt = 0; attempt < 2; ++attempt) {
-    const bool ties = P.tie_mode() || (!kQ && resid && Q.tie_mode());
-    uint32_t tp = 0, tq = 0;
     last = -1;
-    for (int c = 0; c < nchunks; ++c) {
-      if (threadIdx.x == 0) {
-        sm.ties_p[c] = tp;
-        sm.ties_q[c] = tq;
+    uint32_t rp = 0, rq = 0;
+    double acc = 0.0;
+    stream_subs<Tr, kQ>(d, lo, hi, [&](int y0, const uint32_t(&up)[4], const uint32_t(&uq)[4]) {
+      const int g = y0 / Lg;
+      if (ties && y0 == g * Lg) {  // the ties before the group
+        rp = (uint32_t)sm.ties[g];
+        rq = (uint32_t)(sm.ties[g] >> 32);
       }
-      double sw = 0.0;
-      for (int g = c * G; g < min((c + 1) * G, ngroups); ++g) {
-        const int y0 = g * kGroup + threadIdx.x * kSampleE;
-        double w[kSampleE];
-        group_weights<Tr, kQ>(P, Q, qrow, resid, ties, y0, V, tp, tq, w, bad, sm);
+      double w[4];
+      sub_weights<Tr, kQ>(d, y0, up, uq, rp, rq, w, bad);
 #pragma unroll
-        for (int e = 0; e < kSampleE; ++e) {
-          sw += w[e];
-          if (w[e] > 0.0) last = y0 + e;
-        }
+      for (int e = 0; e < 4; ++e) {
+        acc += w[e];
+        if (w[e] > 0.0) last = y0 + 4 * lane + e;
       }
-      const double cm = block_reduce<kSampleNT>(sw, OpAdd(), sm.dsum);
-      if (threadIdx.x == 0) sm.chunk_mass[c] = cm;
-    }
+      if (y0 + kSub >= min((g + 1) * Lg, V)) {  // the group's last sub-block
+        const double gm = wave_reduce(acc, OpAdd());
+        if (lane == 0) sm.mass[g] = gm;
+        acc = 0.0;
+      }
+    });
     last = block_reduce<kSampleNT>(last, OpMax(), sm.ired);
-    if (kQ && resid && attempt == 0) {
+    if (kQ && d.resid && attempt == 0) {
       // an unusable entry of the published residual row fails the session; the
       // first wave rewrites its outputs as it wrote them
       if (block_reduce<kSampleNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0) {
@@ -443,51 +526,57 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
         return;
       }
     }
-    if (!resid || last >= 0) break;
-    resid = false;  // residual without mass (rounding only): draw from p
+    if (!d.resid || last >= 0) break;
+    d.resid = false;  // residual without mass (rounding only): draw from p
+    __syncthreads();  // the group weights are written again
   }
 
-  // prefix over the chunk masses: thread c holds chunk c
+  // the group holding u * S (thread g holds group g)
   __syncthreads();
-  const double cm = (int)threadIdx.x < nchunks ? sm.chunk_mass[threadIdx.x] : 0.0;
+  const double gm = (int)threadIdx.x < ng ? sm.mass[threadIdx.x] : 0.0;
   double S;
-  const double before = block_exclusive_scan<double>(cm, sm.dsum, &S);
+  const double before = block_exclusive_scan<double>(gm, sm.dsum, &S);
   const double tgt = job.u * S;
-  const int32_t mine_c = ((int)threadIdx.x < nchunks && before + cm > tgt) ? (int32_t)threadIdx.x : 0x7FFFFFFF;
-  const int32_t cstar = block_reduce<kSampleNT>(mine_c, OpMin(), sm.ired);
+  const int32_t mine_g = ((int)threadIdx.x < ng && before + gm > tgt) ? (int32_t)threadIdx.x : 0x7FFFFFFF;
+  const int32_t gstar = block_reduce<kSampleNT>(mine_g, OpMin(), sm.ired);
+  if (gstar == 0x7FFFFFFF) {
+    if (threadIdx.x == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = last;
+    return;
+  }
+  if ((int)threadIdx.x == gstar) sm.base = before;
+  __syncthreads();
+  if (wid != 0) return;
+  // the first wave weighs the group again, sub-block by sub-block, and goes on
+  // past it if rounding moved the point
+  double run = sm.base;
   int32_t pick = last;
-  if (cstar != 0x7FFFFFFF) {
-    __syncthreads();
-    if ((int)threadIdx.x == cstar) sm.base = before;
-    __syncthreads();
-    double run = sm.base;
-    const bool ties = P.tie_mode() || (!kQ && resid && Q.tie_mode());
-    uint32_t tp = sm.ties_p[cstar], tq = sm.ties_q[cstar];
-    // the chunk holding u * S; rounding may move the point into a later chunk
-    for (int g = cstar * G; g < ngroups; ++g) {
-      const int y0 = g * kGroup + threadIdx.x * kSampleE;
-      double w[kSampleE];
-      group_weights<Tr, kQ>(P, Q, qrow, resid, ties, y0, V, tp, tq, w, bad, sm);
-      double sw = 0.0;
-#pragma unroll
-      for (int e = 0; e < kSampleE; ++e) sw += w[e];
-      double gtot;
-      double a = run + block_exclusive_scan<double>(sw, sm.dsum, &gtot);
+  bool found = false;
+  for (int g = gstar; g < ng && !found; ++g) {
+    uint32_t rp = ties ? (uint32_t)sm.ties[g] : 0u, rq = ties ? (uint32_t)(sm.ties[g] >> 32) : 0u;
+    for (int y0 = g * Lg; y0 < min((g + 1) * Lg, V); y0 += kSub) {
+      uint32_t up[4], uq[4];
+      sub_load<Tr, kQ>(d, y0, up, uq);
+      double w[4];
+      sub_weights<Tr, kQ>(d, y0, up, uq, rp, rq, w, bad);
+      const double ls = (w[0] + w[1]) + (w[2] + w[3]);
+      const double incl = wave_incl_scan(ls);
+      double a = run + (incl - ls);
       int32_t mine = 0x7FFFFFFF;
 #pragma unroll
-      for (int e = 0; e < kSampleE; ++e) {
+      for (int e = 0; e < 4; ++e) {
         a += w[e];
-        if (mine == 0x7FFFFFFF && a > tgt) mine = y0 + e;
+        if (mine == 0x7FFFFFFF && a > tgt) mine = y0 + 4 * lane + e;
       }
-      const int32_t first = block_reduce<kSampleNT>(mine, OpMin(), sm.ired);
+      const int32_t first = wave_reduce(mine, OpMin());
       if (first != 0x7FFFFFFF) {
         pick = first;
+        found = true;
         break;
       }
-      run += gtot;
+      run += __shfl(incl, kWave - 1, kWave);
     }
   }
-  if (threadIdx.x == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = pick;
+  if (lane == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = pick;
 }
 
 }  // namespace
