@@ -315,6 +315,87 @@ def test_dense_kernel_edge_cases():
     parity.compare(g, o, "dense-edges")
 
 
+def test_dense_topk_above_64_edge_cases():
+    """Rows with 64 < top_k < V, which the one-pass dense path cuts from its
+    histogram window: top-k alone and top-k then top-p, ties split at the
+    top-k cut with drafted tokens on both sides of it, all-negative rows, a
+    rising maximum, -inf masks leaving fewer than K finite tokens, and a
+    window holding fewer than K tokens (the generic fallback)."""
+    parity.log("[case] dense path, top_k above 64, V=5003")
+    B, M, V = 12, 3, 5003
+    rng = np.random.default_rng(74)
+    t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
+    d = (t[:, :M] + rng.normal(0, 0.7, size=(B, M, V))).astype(np.float32)
+    s = oracle.make_sampling(B, 1000, 100, 1000)
+    rule = np.full(B, 2, np.int32)
+    m = np.full(B, M, np.int32)
+    s[1]["top_k"] = 65                                                # 1: just above 64
+    s[2]["top_k"] = 1000; s[2]["top_p_milli"] = 900                  # 2: top-p inside top-k
+    s[3]["top_k"] = 300; s[3]["top_p_milli"] = 999                   # 3: top-p reaches top-k's cut
+    t[4] = rng.integers(0, 6, size=(M + 1, V)); d[4] = t[4, :M]      # 4, 5: ties at the top-k cut
+    t[5] = t[4]; d[5] = d[4]
+    s[4]["top_k"] = s[5]["top_k"] = 1500
+    t[6] = -np.abs(t[6]) - 5.0; d[6] = -np.abs(d[6]) - 5.0           # 6: all negative
+    s[6]["top_k"] = 200; s[6]["top_p_milli"] = 800
+    ramp = np.linspace(-5.0, 20.0, V, dtype=np.float32)              # 7: rising maximum
+    t[7] = ramp + rng.normal(0, 0.3, size=(M + 1, V)); d[7] = t[7, :M] + rng.normal(0, 0.3, (M, V))
+    s[7]["top_k"] = 400
+    t[8][:, rng.random(V) < 0.99] = -np.inf                          # 8: fewer finite than K
+    d[8][:, rng.random(V) < 0.99] = -np.inf
+    s[8]["top_k"] = 2000
+    s[9]["top_k"] = 4000                                             # 9: window < K: fallback
+    s[10]["top_k"] = V - 1; s[10]["top_p_milli"] = 950               # 10: V - 1
+    s[11]["top_k"] = 129; s[11]["temperature_milli"] = 200           # 11: peaked
+    t[11, :, 42] += 6.0; d[11, :, 42] += 6.0
+    tb, db = oracle.bf16_bits(t), oracle.bf16_bits(d)
+    h = dict(target=tb, draft=db, tokens=np.zeros((B, M), np.int32), m=m, rule=rule,
+             sampling=s, seed=14, round=3)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    # sessions 4 and 5: drafted tokens at the tied top-k cut (draft == target rows)
+    for i in range(M):
+        st, p, _ = oracle.profile(tb[4, i], 1000, 1500, 1000)
+        assert st == 0 and (p > 0).sum() == 1500
+        vals = oracle.bf16_to_float(tb[4, i])
+        ids = np.nonzero(p > 0)[0]
+        tied = np.nonzero(vals == vals[ids].min())[0]
+        kept = [y for y in tied if p[y] > 0]
+        dropped = [y for y in tied if p[y] == 0]
+        assert kept and dropped, "the top-k cut must split a tied key"
+        h["tokens"][4, i] = kept[-1] if i != 1 else kept[0]
+        h["tokens"][5, i] = dropped[0]                            # q(x) = 0: bad proposal
+    o = parity.run_oracle(h)
+    assert o["accepted_len"][5] == oracle.S_BAD_PROPOSAL
+    assert o["accepted_len"][4] == M
+    g = parity.run_gpu(h)
+    parity.compare(g, o, "dense-topk-edges")
+
+
+@pytest.mark.parametrize("top_k,top_p", [(100, 1000), (1000, 900), (5000, 950)])
+def test_full_size_top_k_above_64(top_k, top_p):
+    """The B=256, V=128256 rows under top_k above 64, oracle on sampled
+    sessions.  The drafted tokens were drawn under top_k = 50 and top_p = 0.9;
+    with another cut some fall outside q's support (a bad proposal)."""
+    parity.log(f"[case] b256 rows at top_k={top_k} top_p={top_p}, oracle on sampled sessions")
+    import token_sampling_amd as sv
+    w = W.make("b256_topk_topp", device="cuda")
+    w.sampling["top_k"] = top_k
+    w.sampling["top_p_milli"] = top_p
+    out = sv.verify(w.target, w.draft, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"),
+                    w.seed, w.round, probe=True)
+    torch.cuda.synchronize()
+    g_all = {k: v.cpu().numpy() for k, v in out.items()}
+    a = g_all["accepted_len"]
+    assert np.all((a >= 0) | (a == oracle.S_BAD_PROPOSAL))
+    # a session the profile turns into a bad proposal is among those checked
+    bad = np.nonzero(a < 0)[0]
+    idx = np.array(sorted({0, 101, 255} | set(bad[:1].tolist())))
+    sub = W.to_numpy(w, sessions=torch.as_tensor(idx, device="cuda"))
+    del w, out
+    torch.cuda.empty_cache()
+    o = parity.run_oracle(sub)
+    parity.compare({k: v[idx] for k, v in g_all.items()}, o, f"b256-top_k{top_k}")
+
+
 @pytest.mark.parametrize("split", ["1", "2", "4"])
 def test_split_rows_each_factor(split, monkeypatch):
     """The single-pass kernel with each top-k-class row streamed by 1, 2 or 4

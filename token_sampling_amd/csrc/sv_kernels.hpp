@@ -47,13 +47,13 @@ __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule
   return s.top_k >= 1 && s.top_k <= 64;
 }
 
-// Rows whose support is not limited to a few best tokens take the single-pass
-// kernel's dense path (bf16 only): temperature > 0 with top-k off (top_k = 0
-// or top_k >= V), with or without top-p.
+// Every other bf16 row takes the single-pass kernel's dense path: temperature
+// > 0 with top-k off (top_k = 0 or top_k >= V) or above 64, with or without
+// top-p.
 __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rule,
                                                       const sv_sampling& s, int32_t V) {
-  if (dtype != SV_BF16 || row_uses_topk_kernel(dtype, rule, s)) return false;
-  return s.top_k == 0 || s.top_k >= (uint32_t)V;
+  (void)V;
+  return dtype == SV_BF16 && !row_uses_topk_kernel(dtype, rule, s);
 }
 
 struct WorkspaceLayout {

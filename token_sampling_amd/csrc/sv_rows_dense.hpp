@@ -1,6 +1,6 @@
 // sv_rows_dense.hpp -- one pass over a bf16 logits row for the profiles whose
 // support is not limited to a few best tokens: temperature alone, or
-// temperature then top-p, with top-k off (SDCP Sec. 4.1).
+// temperature with top-k above 64 and/or top-p (SDCP Sec. 4.1).
 //
 // One wave64 streams one row through a ring of 1 KiB tiles (as the top-k
 // kernel does) and computes, in that single pass:
@@ -16,15 +16,19 @@
 //    when a logit exceeds it by 32 octaves, so terms stay below 2^32; the
 //    lanes combine in binary64 in a fixed order.
 //    A NaN anywhere makes Z NaN; +inf makes it NaN or infinite.
-//  - with top-p: a count histogram of the kWin keys at and below the running
-//    maximum, in LDS, indexed by key mod kWin.  When the maximum rises, the
-//    bins of the keys that leave the window are cleared for the keys that
-//    enter; the window's bottom only rises, so every token whose key lies in
-//    the final window has been counted.  After the pass the walk from the top
-//    accumulates binary64 masses count * w(key) until 1000 * C >= P * Z: that
-//    gives the cut key kc and the number j of its tokens that stay (those with
-//    the j smallest ids, profile order being logit desc, id asc).  A cut below
-//    the window leaves the row to the generic kernel.
+//  - with top-k or top-p: a count histogram of the kWin keys at and below the
+//    running maximum, in LDS, indexed by key mod kWin.  When the maximum
+//    rises, the bins of the keys that leave the window are cleared for the
+//    keys that enter; the window's bottom only rises, so every token whose key
+//    lies in the final window has been counted.  After the pass, top-k counts
+//    K tokens down from the top: the key where the count reaches K keeps the
+//    K - (tokens above it) smallest ids, and Z_k is the sum of the kept
+//    counts times their keys' weights.  Top-p then walks the kept masses from
+//    the top until 1000 * C >= P * Z_k (Z_k = Z without top-k).  Either gives
+//    the cut key kc and the number j of its tokens that stay (those with the j
+//    smallest ids, profile order being logit desc, id asc).  A cut below the
+//    window (fewer than K tokens in it, or top-p's mass not reached) leaves
+//    the row to the generic kernel.
 //  - the drafted token's rank among the tokens of its key with smaller ids (its
 //    key's bin just before its vector, plus the earlier tokens of that vector):
 //    it is in the support iff its key is above kc, or equal to kc with rank < j.
@@ -80,10 +84,10 @@ struct Hist {
 };
 
 // One 16-byte vector (8 logits) of a tile: the lane's maximum and running sum,
-// then (top-p rows) the histogram window and the drafted token's rank.  p0 is
+// then (top-k and top-p rows) the histogram window and the drafted token's rank.  p0 is
 // the window position of the vector's first logit; xvec says (wave-uniform)
 // whether the drafted token lies in this vector of the wave.
-__device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v, int p0, int px,
+__device__ inline void dense_vec(LaneSum& L, Hist& H, bool hist, const u32x4& v, int p0, int px,
                                  bool xvec, float scale_f, double scale) {
   float f[8];
 #pragma unroll
@@ -109,7 +113,7 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v
   for (int e = 0; e < 8; ++e) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], scale_f, -L.q));
   L.s += (double)ts;
 
-  if (!top_p) return;
+  if (!hist) return;
   if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
     int tk = skey_of(lmv);
 #pragma unroll
@@ -144,12 +148,14 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool top_p, const u32x4& v
 }
 
 // The profile of one row of the dense class, by one wave: temperature > 0,
-// top-k off, with or without top-p.  bins is the wave's LDS histogram of kWin
-// counts.
+// top-k off or above 64, with or without top-p.  bins is the wave's LDS
+// histogram of kWin counts.
 __device__ __attribute__((always_inline)) inline void row_profile(
     const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
   const int lane = __lane_id();
   const bool top_p = smp.top_p_milli < 1000;
+  const bool top_k = smp.top_k > 0 && smp.top_k < (uint32_t)V;
+  const bool hist = top_p || top_k;  // the histogram window is kept
   // the row's scale: log2(e) / T rounded to binary32, used everywhere below
   const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
   const double scale = (double)scale_f;
@@ -183,7 +189,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
       if ((tt == 0 && head > 0) || (tt + 1) * kTile > npos) mask_tile<kVec>(ring[u], tt, head, npos);
 #pragma unroll
       for (int j = 0; j < kVec; ++j)
-        dense_vec(L, H, top_p, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
+        dense_vec(L, H, hist, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
                   tt * kVec + j == xv, scale_f, scale);
     }
   }
@@ -219,7 +225,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     return;
   }
   const double wx = x >= 0 ? weight64(xval, lmax, scale) : 0.0;
-  if (!top_p) {  // the support is every finite logit
+  if (!hist) {  // the support is every finite logit
     rr.kcut = Bf16::kNegInfKey + 1;
     rr.idcut = 0x7FFFFFFF;
     rr.zsum = z;
@@ -228,62 +234,115 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     return;
   }
 
-  // the walk from the top: lane q holds the bins of keys anchor - kPerLane*q - e
-  const double tgt = (double)smp.top_p_milli * z;  // stop at 1000 * C >= tgt
-  double part = 0.0;
+  // the window's counts: lane q holds the bins of keys anchor - kPerLane*q - e
+  uint32_t cnt[kPerLane];
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) {
     const int k = H.anchor - kPerLane * lane - e;
-    const uint32_t c = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
-    if (c) part += (double)c * weight64(value_of(k), lmax, scale);
+    cnt[e] = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
   }
+  int kc = 0, j = 0;  // the cut: key kc keeps its j smallest ids
+  // top-k: the first K tokens of the order, counted from the top.  Counts
+  // after the cut are cleared, so that the masses below are those of the kept
+  // tokens.
+  if (top_k) {
+    const uint32_t K = smp.top_k;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) tot += cnt[e];
+    uint32_t cincl = tot;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t t = __shfl_up(cincl, off, kWave);
+      if (lane >= off) cincl += t;
+    }
+    const uint64_t hitk = __ballot(cincl >= K);
+    if (!hitk) {  // fewer than K tokens in the window
+      if (lane == 0) {
+        RowRec fb{};
+        fb.status = kRowFallback;
+        *rec = fb;
+      }
+      return;
+    }
+    const int qk = __builtin_ctzll(hitk);
+    uint32_t above = __shfl(cincl - tot, qk, kWave);  // tokens in the lanes before qk
+#pragma unroll
+    for (int e = 0; e < kPerLane; ++e) {
+      // every lane walks lane qk's counts (wave-uniform): the cut is the last
+      // key that keeps a token
+      const uint32_t c = __shfl(cnt[e], qk, kWave);
+      const uint32_t keep = above >= K ? 0u : (K - above < c ? K - above : c);
+      if (keep) {
+        kc = H.anchor - kPerLane * qk - e;
+        j = (int)keep;
+      }
+      if (lane == qk) cnt[e] = keep;
+      above += c;
+    }
+    if (lane > qk) {
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) cnt[e] = 0u;
+    }
+  }
+
+  // masses of the kept counts, summed from the top
+  double part = 0.0;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e)
+    if (cnt[e]) part += (double)cnt[e] * weight64(value_of(H.anchor - kPerLane * lane - e), lmax, scale);
   double incl = part;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const double t = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += t;
   }
-  const uint64_t hit = __ballot(1000.0 * incl >= tgt);
-  if (!hit) {  // the cut lies below the window
-    if (lane == 0) {
-      RowRec fb{};
-      fb.status = kRowFallback;
-      *rec = fb;
-    }
-    return;
-  }
-  const int q = __builtin_ctzll(hit);
-  int kc = 0, j = 0;
-  double c_above = 0.0, wc = 0.0;
-  if (lane == q) {
-    double c = incl - part;
-    for (int e = 0; e < kPerLane; ++e) {
-      const int k = H.anchor - kPerLane * lane - e;
-      const uint32_t cnt = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
-      if (!cnt) continue;
-      const double w = weight64(value_of(k), lmax, scale);
-      // this lane's last key with tokens, all kept, unless a key below crosses
-      kc = k;
-      j = (int)cnt;
-      c_above = c;
-      wc = w;
-      if (1000.0 * (c + (double)cnt * w) >= tgt) {
-        // the smallest j with 1000 * (c + j * w) >= tgt
-        int jj = (int)ceil((tgt / 1000.0 - c) / w);
-        jj = max(1, min((int)cnt, jj));
-        while (jj > 1 && 1000.0 * (c + (double)(jj - 1) * w) >= tgt) --jj;
-        while (jj < (int)cnt && 1000.0 * (c + (double)jj * w) < tgt) ++jj;
-        j = jj;
-        break;
+  // Z_k: the mass of the top-k set (the last lane's prefix), else the row's Z
+  double zsum = top_k ? __shfl(incl, kWave - 1, kWave) : z;
+
+  if (top_p) {  // over the top-k distribution: stop at 1000 * C >= P * Z_k
+    const double tgt = (double)smp.top_p_milli * zsum;
+    const uint64_t hit = __ballot(1000.0 * incl >= tgt);
+    if (!hit) {  // the cut lies below the window (never with top-k: C reaches Z_k)
+      if (lane == 0) {
+        RowRec fb{};
+        fb.status = kRowFallback;
+        *rec = fb;
       }
-      c += (double)cnt * w;
+      return;
     }
+    const int q = __builtin_ctzll(hit);
+    double c_above = 0.0, wc = 0.0;
+    if (lane == q) {
+      double c = incl - part;
+#pragma unroll
+      for (int e = 0; e < kPerLane; ++e) {
+        if (!cnt[e]) continue;
+        const int k = H.anchor - kPerLane * lane - e;
+        const double w = weight64(value_of(k), lmax, scale);
+        // this lane's last key with tokens, all kept, unless a key below crosses
+        kc = k;
+        j = (int)cnt[e];
+        c_above = c;
+        wc = w;
+        if (1000.0 * (c + (double)cnt[e] * w) >= tgt) {
+          // the smallest j with 1000 * (c + j * w) >= tgt
+          int jj = (int)ceil((tgt / 1000.0 - c) / w);
+          jj = max(1, min((int)cnt[e], jj));
+          while (jj > 1 && 1000.0 * (c + (double)(jj - 1) * w) >= tgt) --jj;
+          while (jj < (int)cnt[e] && 1000.0 * (c + (double)jj * w) < tgt) ++jj;
+          j = jj;
+          break;
+        }
+        c += (double)cnt[e] * w;
+      }
+    }
+    kc = __shfl(kc, q, kWave);
+    j = __shfl(j, q, kWave);
+    c_above = __shfl(c_above, q, kWave);
+    wc = __shfl(wc, q, kWave);
+    zsum = c_above + (double)j * wc;
   }
-  kc = __shfl(kc, q, kWave);
-  j = __shfl(j, q, kWave);
-  c_above = __shfl(c_above, q, kWave);
-  wc = __shfl(wc, q, kWave);
-  const double zsum = c_above + (double)j * wc;
   rr.kcut = (uint32_t)(kc + 0x8000);
   rr.idcut = -1;
   rr.ntie = j;

@@ -2,10 +2,10 @@
 // streams the row once and computes its profile (SDCP Sec. 4.1) by the path
 // its profile needs:
 //   top-k class (greedy, temperature 0, 1 <= top_k <= 64): topk::row_profile;
-//   dense class (temperature > 0, top-k off, with or without top-p):
-//     dense::row_profile.
-// Rows of other profiles, and rows a path hands back, are left to the
-// generic kernel.  Each wave also takes its session's statuses that need no
+//   dense class (temperature > 0, top-k off or above 64, with or without
+//     top-p): dense::row_profile.
+// Rows of other dtypes, and rows a path hands back, are left to the generic
+// kernel.  Each wave also takes its session's statuses that need no
 // logits (SDCP Table 2, Sec. 6.3 step 5: limit, profile, q availability,
 // drafted tokens in range); the wave of a session's first row slot records
 // them for the kernels that follow.

@@ -120,21 +120,19 @@ class Workload:
         return rows * self.V * s + small
 
     def row_bytes_by_kernel(self, q_rows: bool = False) -> dict:
-        """Row bytes read by each row kernel: the single-pass kernel takes bf16
-        rows of the top-k class (greedy rules, temperature 0, 1 <= top_k <= 64)
-        and of the dense class (temperature > 0 with top-k off); the generic
-        kernel takes the rest.  With q_rows no draft row is profiled."""
+        """Row bytes read by each row kernel: the single-pass kernel takes every
+        bf16 row (the top-k class: greedy rules, temperature 0, 1 <= top_k <=
+        64; the dense class: the rest), the generic kernel the fp32 rows and
+        the bf16 rows a path hands back (not counted here: that depends on the
+        logits).  With q_rows no draft row is profiled."""
         m = self.m.to("cpu").to(torch.int64).numpy()
         rule = self.rule.to("cpu").to(torch.int64).numpy()
-        s = self.sampling
         bf16 = self.target.dtype == torch.bfloat16
-        T, k = s["temperature_milli"], s["top_k"]
-        topk_class = (rule == 1) | (T == 0) | ((k >= 1) & (k <= 64))
-        dense_class = ~topk_class & ((k == 0) | (k >= self.V))
         per_session = (m + 1) + (0 if q_rows else m * (rule == 2))
         row = self.V * self.target.element_size()
-        stream = int(per_session[topk_class | dense_class].sum()) * row if bf16 else 0
-        return {"stream": stream, "generic": int(per_session.sum()) * row - stream}
+        total = int(per_session.sum()) * row
+        stream = total if bf16 else 0
+        return {"stream": stream, "generic": total - stream}
 
 
 def _to_storage(x32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
