@@ -9,6 +9,8 @@
 // Neither call synchronises or allocates.
 #include <limits.h>
 
+#include <atomic>
+
 #include "sv_kernels.hpp"
 
 namespace sv {
@@ -16,7 +18,6 @@ namespace sv {
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
-  (void)V;
   WorkspaceLayout L;
   size_t off = 0;
   L.rows_off = off;
@@ -30,6 +31,12 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + slots * kSupMax * sizeof(double), 256);
   L.unif_off = off;
   off = align_up(off + slots * sizeof(double), 256);
+  L.chunk_off = off;
+  off = align_up(off + (size_t)B * (((size_t)V + kGroup - 1) / kGroup) * sizeof(GroupRec), 256);
+  L.ctr_off = off;
+  off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+  L.flag_off = off;
+  off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
   L.total = off;
   return L;
 }
@@ -56,6 +63,15 @@ extern "C" size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V) {
 }
 
 namespace sv {
+
+// A value per call for the rows' draw flags (never 0, so that a cleared
+// workspace matches no call).
+static uint32_t next_draw_token() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  if (t == 0) t = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return t;
+}
 
 // Shared by both entry points: sdcp == null takes the Philox values from
 // (seed, round); otherwise the SDCP Sec. 6.4 values of each session's record.
@@ -97,6 +113,13 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   a.sup_p = (double*)(ws + L.supp_off);
   a.sdcp = sdcp;
   a.unif = sdcp ? (double*)(ws + L.unif_off) : nullptr;
+  a.groups = (GroupRec*)(ws + L.chunk_off);
+  a.draw_ctr = (uint32_t*)(ws + L.ctr_off);
+  const DrawChunks dc = draw_chunks(B, V);
+  a.draw_C = dc.C;
+  a.draw_gw = dc.gw;
+  a.draw_flag = (uint32_t*)(ws + L.flag_off);
+  a.draw_token = next_draw_token();
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below

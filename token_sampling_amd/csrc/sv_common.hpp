@@ -163,5 +163,9 @@ struct OpMin {
   template <typename T>
   __device__ T operator()(T a, T b) const { return a < b ? a : b; }
 };
+struct OpOr {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a | b; }
+};
 
 }  // namespace sv

@@ -31,7 +31,57 @@ struct LaunchArgs {
   const sv_sdcp_session* sdcp;  // [B] per-session seed, id and round
   double* unif;                 // [B, 2M+1]: j < M acceptance value of position j+1,
                                 // j >= M additional-token value of position j-M+1
+  // the draw from rows without listed supports: each session's row is cut
+  // into groups of kGroup ids, recorded by draw_C workgroups per session,
+  // draw_gw groups per wave
+  struct GroupRec* groups;  // [B, ceil(V / kGroup)]
+  uint32_t* draw_ctr;       // [B] workgroups finished; cleared by the single-pass row kernel
+  int32_t draw_C, draw_gw;
+  // draw_flag[b] == draw_token: a row of session b has no listed support (set by
+  // the row kernels of this call); only then do a session's extra draw
+  // workgroups have work.  A value left by an earlier call that equals the
+  // token costs them an acceptance pass, nothing more.
+  uint32_t* draw_flag;  // [B]
+  uint32_t draw_token;
 };
+
+// Ids per group record of the draw.
+constexpr int kGroup = 2048;
+
+// What one group of ids leaves for the draw's last workgroup.  The cut
+// keys' ties kept by rank (rows cut by the dense path) all weigh the same,
+// so the group's weights are recorded for both cases, kept and left out, and
+// the session's tie counts decide which case holds where (only a group
+// holding a row's cut needs its ties ranked).  Residual draws: weights
+// max(0, p - q) where p > 0; p ties / q ties are tokens of the cut key of p /
+// of q in a row cut by rank.  Stored as six 64-bit words.
+struct GroupRec {
+  double a;    // weight of the tokens that are ties of neither row
+  double bp;   // residual: weight of the p ties (not q ties), all kept
+  double cq1;  // residual: weight of the q ties (not p ties), all kept
+  double cq0;  // residual: the same tokens with no q tie kept (their p)
+  double ap;   // residual: p of the tokens that are not p ties (a draw from p)
+  uint32_t ties;     // p ties | q ties << 16
+  uint32_t npq_bad;  // tokens that are both | published q unusable << 16 (bit
+                     // 0 where p > 0 outside the p ties, bit 1 at a p tie)
+};
+static_assert(sizeof(GroupRec) == 48, "GroupRec layout");
+
+// Workgroups per session for the draw: about 1024 in all (B * C), each
+// wave taking gw whole groups.
+struct DrawChunks {
+  int32_t C, gw;
+};
+__host__ __device__ inline DrawChunks draw_chunks(int32_t B, int32_t V) {
+  const long long G = ((long long)V + kGroup - 1) / kGroup;
+  long long C = (1024 + (long long)B - 1) / B;
+  const long long cmax = (G + 3) / 4;
+  if (C > cmax) C = cmax;
+  if (C < 1) C = 1;
+  const long long gw = (G + 4 * C - 1) / (4 * C);
+  C = (G + 4 * gw - 1) / (4 * gw);
+  return DrawChunks{(int32_t)C, (int32_t)gw};
+}
 
 // Row status written by a specialised row kernel that could not finish a row;
 // the generic kernel then computes that row.
@@ -57,7 +107,7 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
 }
 
 struct WorkspaceLayout {
-  size_t rows_off, status_off, supid_off, supp_off, unif_off, total;
+  size_t rows_off, status_off, supid_off, supp_off, unif_off, chunk_off, ctr_off, flag_off, total;
 };
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);

@@ -230,7 +230,8 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
-    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows) {
+    const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows,
+    uint32_t* __restrict__ draw_flag, uint32_t draw_token) {
   __shared__ Smem sm;
   __shared__ int32_t todo[kNT];
   __shared__ int32_t wave_cnt[kNT / kWave];
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
     const bool need = slot_g < end &&
                       generic_row<Tr>(slot_g, m, rule, sampling, sess_status, M, V, rows,
                                       draft != nullptr);
+    if (need) draw_flag[slot_g / R] = draw_token;  // a row without a listed support
     const uint64_t mask = __ballot(need);
     __syncthreads();  // the previous round's list is consumed
     if (lane == 0) wave_cnt[wid] = __builtin_popcountll(mask);
@@ -283,11 +285,13 @@ void launch_rows_generic(const LaunchArgs& a, hipStream_t st) {
   if (a.dtype == SV_BF16) {
     hipLaunchKernelGGL(k_rows_generic<Bf16>, dim3(grid), dim3(kNT), 0, st,
                        (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
-                       a.sampling, a.sess_status, a.B, a.M, a.V, a.rows);
+                       a.sampling, a.sess_status, a.B, a.M, a.V, a.rows, a.draw_flag,
+                       a.draw_token);
   } else {
     hipLaunchKernelGGL(k_rows_generic<F32>, dim3(grid), dim3(kNT), 0, st,
                        (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
-                       a.sampling, a.sess_status, a.B, a.M, a.V, a.rows);
+                       a.sampling, a.sess_status, a.B, a.M, a.V, a.rows, a.draw_flag,
+                       a.draw_token);
   }
 }
 

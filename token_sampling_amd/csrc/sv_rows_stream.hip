@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
-    int B, int M, int V, int32_t* __restrict__ sess_status, RowRec* __restrict__ rows,
+    int B, int M, int V, int32_t* __restrict__ sess_status, uint32_t* __restrict__ draw_ctr,
+    uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks) {
   __shared__ __align__(16) uint64_t lds[kLdsWords];  // top-k region or dense histogram
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
   const int slot = slot_g - b * R;
   if (b >= B) return;
   const int st = session_status(b, tokens, m, rule, sampling, M, V, has_draft != 0);
-  if (slot == 0 && lane == 0) sess_status[b] = st;
+  if (slot == 0 && lane == 0) {
+    sess_status[b] = st;
+    draw_ctr[b] = 0u;  // the draw's chunk counter, for the per-session kernel
+  }
   if (st != 0 || dtype != SV_BF16) return;
   const int mb = m[b];
   const int rl = rule[b];
@@ -114,6 +118,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
     const size_t so = (size_t)slot_g * kSupMax;
     topk::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
   } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
+    if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
     dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
   }
 }
@@ -131,7 +136,8 @@ __global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_ST
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
-    int B, int M, int V, int32_t* __restrict__ sess_status, RowRec* __restrict__ rows,
+    int B, int M, int V, int32_t* __restrict__ sess_status, uint32_t* __restrict__ draw_ctr,
+    uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks) {
   static_assert(S * kSupMax <= topk::kCap, "the merged lists fit one region");
@@ -151,7 +157,10 @@ __global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_ST
   const int slot = slot_g - b * R;
   if (b >= B) return;
   const int st = session_status(b, tokens, m, rule, sampling, M, V, has_draft != 0);
-  if (wid == 0 && slot == 0 && lane == 0) sess_status[b] = st;
+  if (wid == 0 && slot == 0 && lane == 0) {
+    sess_status[b] = st;
+    draw_ctr[b] = 0u;
+  }
   if (st != 0 || dtype != SV_BF16) return;
   const int mb = m[b];
   const int rl = rule[b];
@@ -210,7 +219,10 @@ __global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_ST
                      smp.temperature_milli, smp.top_p_milli, x, rec, sup_id + so, sup_p + so);
   } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
     // one wave, chosen by the slot, so that dense rows spread over the SIMDs
-    if (wid == slot_g % S) dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+    if (wid == slot_g % S) {
+      if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
+      dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+    }
   }
 }
 
@@ -240,7 +252,7 @@ static void launch_split(const LaunchArgs& a, hipStream_t st, size_t slots) {
   hipLaunchKernelGGL((k_rows_split<S>), dim3(grid), dim3(per_block), 0, st,
                      (const uint16_t*)a.target, (const uint16_t*)a.draft, a.dtype, a.tokens, a.m,
                      a.rule, a.sampling, (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B,
-                     a.M, a.V, a.sess_status, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
+                     a.M, a.V, a.sess_status, a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
                      n_value_blocks);
 }
 
@@ -253,7 +265,8 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
                      (const uint16_t*)a.draft, a.dtype, a.tokens, a.m, a.rule, a.sampling,
-                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V, a.sess_status, a.rows, a.sup_id,
+                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V, a.sess_status,
+                     a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id,
                      a.sup_p, a.sdcp, a.unif, n_value_blocks);
 }
 

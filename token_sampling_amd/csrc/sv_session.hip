@@ -1,15 +1,18 @@
-// sv_session.hip -- the per-session kernel of libspecverify, one workgroup
-// per session:
-//   its first wave (lane i = position i+1) takes the acceptance rule, with a
-//   64-bit ballot for the first rejection, and draws the additional token
-//   from listed supports;
-//   the whole workgroup draws the additional token, as an inverse CDF over
-//   ascending token ids, when the rows have no listed support.
+// sv_session.hip -- the per-session kernel of libspecverify.  A session
+// takes C workgroups (one per chunk of its vocabulary):
+//   the first wave of each takes the acceptance rule (lane i = position i+1,
+//   a 64-bit ballot for the first rejection); chunk 0's workgroup draws the
+//   additional token from listed supports and writes the session's outputs;
+//   when the rows have no listed support, the additional token is an inverse
+//   CDF over ascending token ids: each workgroup weighs its chunk, and the
+//   session's last workgroup picks the token and writes the outputs.
 #include "sv_kernels.hpp"
 
 namespace sv {
 
 namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Inverse CDF over a listed support (ids ascending): the additional token is
 // the smallest id whose running mass exceeds u * S (the largest id with mass
@@ -71,7 +74,7 @@ __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
 // per-session kernel's first wave writes these and the session's other
 // outputs with the same lane-to-address mapping, so a later failure
 // overwrites them in each lane's program order.
-__device__ void write_failed(int b, int st, int M, int32_t* __restrict__ accepted_len,
+__device__ __attribute__((always_inline)) void write_failed(int b, int st, int M, int32_t* __restrict__ accepted_len,
                              int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
                              double* __restrict__ q_tok) {
   const int lane = threadIdx.x;
@@ -84,30 +87,47 @@ __device__ void write_failed(int b, int st, int M, int32_t* __restrict__ accepte
   }
 }
 
+// One session's acceptance verdict, held by the lanes of one wave (lane i:
+// position i+1).
+struct Verdict {
+  int st;         // 0, or the session's failure status
+  int a;          // accepted drafted tokens
+  int rl, mb;     // rule, drafted tokens
+  int32_t x;      // this lane's drafted token (-1 past m)
+  double px, qx;  // this lane's p_i(x_i) and q_i(x_i)
+  int32_t extra;  // the additional token, when already drawn
+  Job job;        // the draw left to the chunked sampler (kJobNone: none)
+};
+
 // SDCP Sec. 6.4, for session b, by one wave: lane i examines position i+1.
 // With published q rows (qrows != null) q_i(x_i) is read from them and no
-// draft row record exists.
-// Writes accepted_len, out_tokens and the probes; returns the draw left for
-// the whole workgroup (kJobNone when the extra token is already written).
-__device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
-                                const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
-                                const sv_sampling* __restrict__ sampling, int M, int V,
-                                const float* __restrict__ qrows, uint64_t seed,
-                                uint32_t round, const int32_t* __restrict__ sess_status,
-                                const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
-                                int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
-                                double* __restrict__ q_tok, const int32_t* __restrict__ sup_id,
-                                const double* __restrict__ sup_p, const double* __restrict__ unif,
-                                int32_t* q_id, double* q_p) {
+// draft row record exists.  Writes nothing.  A draw from listed supports is
+// taken here when listed is set; otherwise such a session only reports that
+// no chunked draw is left (job kind none).
+__device__ __attribute__((always_inline)) Verdict accept_session(int b, const int32_t* __restrict__ tokens,
+                                  const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
+                                  const sv_sampling* __restrict__ sampling, int M, int V,
+                                  const float* __restrict__ qrows, uint64_t seed, uint32_t round,
+                                  const int32_t* __restrict__ sess_status,
+                                  const RowRec* __restrict__ rows,
+                                  const int32_t* __restrict__ sup_id,
+                                  const double* __restrict__ sup_p,
+                                  const double* __restrict__ unif, bool listed, int32_t* q_id,
+                                  double* q_p) {
   const int lane = threadIdx.x;
   const int R = 2 * M + 1;
-  Job job{kJobNone, 0, 0, 0, 0.0};
+  Verdict v;
+  v.job = Job{kJobNone, 0, 0, 0, 0.0};
+  v.a = 0;
+  v.extra = -1;
   const RowRec* rr = rows + (size_t)b * R;
-  int32_t* out = out_tokens + (size_t)b * (M + 1);
   int st = sess_status[b];
   const int mb = m[b];
   const int rl = rule[b];
+  v.rl = rl;
+  v.mb = mb;
   const int32_t x = (st == 0 && lane < mb) ? tokens[(size_t)b * M + lane] : -1;
+  v.x = x;
 
   // every row the rule reads must be usable (target rows 1..m+1, draft rows 1..m)
   if (st == 0) {
@@ -128,25 +148,23 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     if (__any(lane < mb && !(qx > 0.0 && qx < INFINITY))) st = SV_S_BAD_PROPOSAL;
   }
   if (st == 0 && rl == SV_RULE_RELAXED && lane < mb) px = rr[lane].ptok;
-
-  if (st < 0) {
-    write_failed(b, st, M, accepted_len, out_tokens, p_tok, q_tok);
-    return job;
-  }
+  v.px = px;
+  v.qx = qx;
+  v.st = st;
+  if (st < 0) return v;
 
   int a;
-  int32_t extra = -1;
   if (rl == SV_RULE_GREEDY) {
     // Rule 1: accept while x_i == argmax p_i; additional token argmax p_{a+1}
     const bool acc = lane < mb && x == rr[lane].argmax;
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
-    extra = rr[a].argmax;
+    v.extra = rr[a].argmax;
   } else if (rl == SV_RULE_RELAXED) {
     // relaxed rule (private use 192): accept x_i while p_i(x_i) > 0; the
     // additional token is drawn from p_{a+1} with the purpose-1 value of
-    // position a+1, from the listed support or by the whole workgroup
+    // position a+1, from the listed support or by the chunked sampler
     const bool acc = lane < mb && px > 0.0;
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
@@ -156,12 +174,14 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
     const RowRec& P = rr[a];
     if (P.nsup > 0) {
-      bool bad = false;
-      extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
-                          sup_p + ((size_t)b * R + a) * kSupMax, P.nsup, nullptr, nullptr, 0,
-                          nullptr, ud, q_id, q_p, &bad);
+      if (listed) {
+        bool bad = false;
+        v.extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
+                              sup_p + ((size_t)b * R + a) * kSupMax, P.nsup, nullptr, nullptr, 0,
+                              nullptr, ud, q_id, q_p, &bad);
+      }
     } else {
-      job = Job{kJobBonus, a, a, -1, ud};
+      v.job = Job{kJobBonus, a, a, -1, ud};
     }
   } else {
     // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i)); the values
@@ -179,87 +199,471 @@ __device__ Job finalize_session(int b, const int32_t* __restrict__ tokens,
     if (uv) ud = uv[M + a];
     else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
     // additional token: residual at the first rejection, else the bonus row;
-    // drawn here when the rows' supports are listed, else by the sampler
+    // drawn here when the rows' supports are listed, else by the chunks
     const RowRec& P = rr[a];
     const RowRec* Q = (a < mb && !qrows) ? &rr[M + 1 + a] : nullptr;
     const float* qrow = (a < mb && qrows) ? qrows + ((size_t)b * M + a) * (size_t)V : nullptr;
     if (P.nsup > 0 && (Q == nullptr || Q->nsup > 0)) {
-      bool bad = false;
-      extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
-                          sup_p + ((size_t)b * R + a) * kSupMax, P.nsup,
-                          Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
-                          Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
-                          Q ? Q->nsup : 0, qrow, ud, q_id, q_p, &bad);
-      if (bad) {  // an unusable entry of the published residual row
-        write_failed(b, SV_S_BAD_PROPOSAL, M, accepted_len, out_tokens, p_tok, q_tok);
-        return job;
+      if (listed) {
+        bool bad = false;
+        v.extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
+                              sup_p + ((size_t)b * R + a) * kSupMax, P.nsup,
+                              Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                              Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                              Q ? Q->nsup : 0, qrow, ud, q_id, q_p, &bad);
+        if (bad) v.st = SV_S_BAD_PROPOSAL;  // an unusable entry of the published residual row
       }
     } else {
-      job = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
+      v.job = a < mb ? Job{kJobResidual, a, a, a, ud} : Job{kJobBonus, a, mb, -1, ud};
     }
   }
-  if (lane == 0) accepted_len[b] = a;
-  for (int j = lane; j <= M; j += kWave) {
-    int32_t v = -1;
-    if (j < a) v = x;  // j < a <= 64 means j == lane
-    else if (j == a) v = extra;  // -1: written by the sampling kernel
-    out[j] = v;
-  }
-  for (int j = lane; j < M; j += kWave) {
-    const bool have_p = (rl == SV_RULE_SPECULATIVE || rl == SV_RULE_RELAXED) && j < mb;
-    const bool have_q = rl == SV_RULE_SPECULATIVE && j < mb;
-    if (p_tok) p_tok[(size_t)b * M + j] = have_p ? px : -1.0;
-    if (q_tok) q_tok[(size_t)b * M + j] = have_q ? qx : -1.0;
-  }
-  return job;
+  v.a = a;
+  return v;
 }
 
-constexpr int kSampleNT = 1024;                  // threads per session
-constexpr int kSampleWaves = kSampleNT / kWave;  // waves per session
-constexpr int kSub = kWave * 4;                  // ids per sub-block: 4 consecutive per lane
-constexpr int kMaxGroups = kSampleNT;            // groups of whole sub-blocks (one per thread)
-constexpr int kLut = 2048;                       // probabilities tabled per row (by key)
+// A session's outputs from its verdict and additional token, by one wave.
+__device__ __attribute__((always_inline)) void write_verdict(int b, const Verdict& v, int32_t extra, int M,
+                              int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+                              double* __restrict__ p_tok, double* __restrict__ q_tok) {
+  if (v.st < 0) {
+    write_failed(b, v.st, M, accepted_len, out_tokens, p_tok, q_tok);
+    return;
+  }
+  const int lane = threadIdx.x;
+  int32_t* out = out_tokens + (size_t)b * (M + 1);
+  if (lane == 0) accepted_len[b] = v.a;
+  for (int j = lane; j <= M; j += kWave) {
+    int32_t t = -1;
+    if (j < v.a) t = v.x;  // j < a <= 64 means j == lane
+    else if (j == v.a) t = extra;
+    out[j] = t;
+  }
+  for (int j = lane; j < M; j += kWave) {
+    const bool have_p = (v.rl == SV_RULE_SPECULATIVE || v.rl == SV_RULE_RELAXED) && j < v.mb;
+    const bool have_q = v.rl == SV_RULE_SPECULATIVE && j < v.mb;
+    if (p_tok) p_tok[(size_t)b * M + j] = have_p ? v.px : -1.0;
+    if (q_tok) q_tok[(size_t)b * M + j] = have_q ? v.qx : -1.0;
+  }
+}
 
-// One row's profile as the sampler sees it: p(y) = w(y) / Z' on the support.
-// A row whose cut is recorded as (kcut, ntie) keeps the ntie smallest ids among
-// the tokens of key kcut; the sampler counts those ties in id order.  The
-// probabilities of the kLut keys below the row's largest key are tabled in
-// LDS (a top-p support lies there); other keys evaluate the weight.
+// ------------------------------------------------------------ chunked draw
+// Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2 (and the relaxed
+// rule's draw from p): the additional token is the smallest id whose running
+// weight exceeds u * S, over ascending ids, with weights max(0, p - q) (zero
+// where p is zero) for the residual, or p.  A session's row is cut into groups
+// of kGroup ids; C workgroups per session each take a run of groups, each
+// wave a run inside it, and record every group (GroupRec).  The session's
+// last workgroup to finish adds the records up, finds the group holding
+// u * S and weighs that group again id by id.
+
+constexpr int kDrawNT = 256;                 // threads per workgroup
+constexpr int kDrawWaves = kDrawNT / kWave;
+constexpr int kPer = 8;                      // consecutive ids per lane per step
+constexpr int kWStep = kWave * kPer;         // ids per wave step
+constexpr int kSteps = kGroup / kWStep;      // wave steps per group
+constexpr int kTab = 256;
+static_assert(kSteps == 4, "the load ring holds one group");
+
+// Weights in binary64 by Tang's table-driven method (P. T. P. Tang, "Table-
+// driven implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989), base 2: with x = (l - lmax) * scale and
+// 256 x = n + f (n integer, 0 <= f < 1),
+//   2^x = 2^(n >> 8) * 2^((n & 255) / 256) * 2^(f / 256),
+// the middle factor (divided by the row's Z) tabled per row, the last a
+// degree-5 Taylor polynomial in f (truncation below 6e-19 relative).
+constexpr double kT1 = 0.69314718055994530942 / 256.0;  // ln 2 / 256
+constexpr double kT2 = kT1 * kT1 / 2.0;
+constexpr double kT3 = kT2 * kT1 / 3.0;
+constexpr double kT4 = kT3 * kT1 / 4.0;
+constexpr double kT5 = kT4 * kT1 / 5.0;
+
+// One row as the draw sees it: p(y) = w(y) / Z on the support.  A row whose
+// cut is recorded as (kcut, ntie) keeps the ntie smallest ids among the tokens
+// of key kcut (its ties, ranked in id order); other members are decided by
+// key (and id, when the cut id is known).
 template <class Tr>
-struct SampleRow {
+struct DrawRow {
   const typename Tr::elem_t* row;
-  RowRec r;
-  uint32_t ktop;      // key of the row's largest logit
-  const double* lut;  // lut[ktop - k] = p of key k, for ktop - kLut < k <= ktop
-  __device__ bool tie_mode() const { return r.idcut < 0; }
-  // probability of token y with bits u; rank = ties of key kcut before y (tie mode)
-  __device__ double prob(int y, uint32_t u, int rank) const {
+  const double* tab;  // tab[i] = 2^(i / 256) / Z
+  double s256, c256;  // 256 * scale and 256 * scale * lmax (both exact)
+  double wcut;        // p of each tie (tie mode)
+  uint32_t kcut;
+  int32_t idcut;
+  uint32_t ntie;      // ties kept (tie mode), else 0
+  bool vec;           // 16-byte aligned row: vector loads
+  __device__ bool tie(uint32_t k) const { return idcut < 0 && k == kcut; }
+  __device__ bool fixed_member(uint32_t k, int y) const {
+    return k > kcut || (k == kcut && idcut >= 0 && y <= idcut);
+  }
+  __device__ double w(float l) const {
+    // t = 256 (l - lmax) scale, from exact products rounded once (as rounding
+    // (l - lmax) * scale, an exact difference, and scaling by 256); far below
+    // the binary64 range the integer part saturates and ldexp gives 0
+    const double t = __builtin_fma((double)l, s256, -c256);
+    const double n = floor(t);
+    const double f = t - n;
+    const int ni = (int)n;
+    double p = __builtin_fma(kT5, f, kT4);
+    p = __builtin_fma(p, f, kT3);
+    p = __builtin_fma(p, f, kT2);
+    p = __builtin_fma(p, f, kT1);
+    p = __builtin_fma(p, f, 1.0);
+    return ldexp(tab[ni & (kTab - 1)] * p, ni >> 8);
+  }
+  // p of a token that is not a tie
+  __device__ double p_fixed(uint32_t u, int y) const {
     const uint32_t k = Tr::key(u);
-    const bool member = k > r.kcut || (k == r.kcut && (r.idcut >= 0 ? y <= r.idcut : rank < r.ntie));
-    if (!member) return 0.0;
-    if (ktop - k < (uint32_t)kLut) return lut[ktop - k];
-    return weight64(Tr::value(u), r.lmax, r.scale) / r.zsum;
+    return fixed_member(k, y) ? w(Tr::value(u)) : 0.0;
   }
 };
 
-// Fill a row's table: p of the keys ktop, ktop - 1, ... (keys at or below
-// -inf get 0).  Entries are the same expression the direct path evaluates.
-template <class Tr>
-__device__ void fill_lut(SampleRow<Tr>& S, double* lut) {
-  S.ktop = Tr::key(__float_as_uint(S.r.lmax) >> (32 - Tr::kKeyBits));
-  S.lut = lut;
-  for (int i = threadIdx.x; i < kLut; i += blockDim.x) {
-    const long k = (long)S.ktop - i;
-    double p = 0.0;
-    if (k > (long)Tr::kNegInfKey)
-      p = weight64(Tr::value(Tr::unkey((uint32_t)k)), S.r.lmax, S.r.scale) / S.r.zsum;
-    lut[i] = p;
+// 8 consecutive elements' raw bits.
+template <int kBytes>
+struct Raw8;
+template <>
+struct Raw8<2> {
+  u32x4 v;
+  __device__ uint32_t get(int e) const {
+    const uint32_t d = v[e >> 1];
+    return (e & 1) ? d >> 16 : d & 0xFFFFu;
+  }
+};
+template <>
+struct Raw8<4> {
+  u32x4 v[2];
+  __device__ uint32_t get(int e) const {
+    const uint32_t d = v[e >> 2][e & 3];
+    return d;
+  }
+};
+
+// Elements y .. y+7 of a row (fill past V).  Vector loads where the row is
+// 16-byte aligned and the 8 elements lie inside it.
+template <class E>
+__device__ inline void load8(const E* row, int y, int V, bool vec, uint32_t fill,
+                             Raw8<sizeof(E)>& r) {
+  if (vec && y + kPer <= V) {
+    const u32x4* p = (const u32x4*)(row + y);
+    if constexpr (sizeof(E) == 2) r.v = p[0];
+    else {
+      r.v[0] = p[0];
+      r.v[1] = p[1];
+    }
+  } else if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = y + 2 * d < V ? (uint32_t)row[y + 2 * d] : fill;
+      const uint32_t hi = y + 2 * d + 1 < V ? (uint32_t)row[y + 2 * d + 1] : fill;
+      r.v[d] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) r.v[e >> 2][e & 3] = y + e < V ? (uint32_t)row[y + e] : fill;
   }
 }
 
+template <class Tr, bool kQ>
+struct DrawCtx {
+  using RawP = Raw8<sizeof(typename Tr::elem_t)>;
+  using RawQ = Raw8<kQ ? 4 : sizeof(typename Tr::elem_t)>;
+  DrawRow<Tr> P, Q;    // Q: draft row (residual, !kQ)
+  const float* qrow;   // published q row (residual, kQ)
+  bool qvec;
+  int V;
+  __device__ void load(int y, bool resid, RawP& rp, RawQ& rq) const {
+    load8(P.row, y, V, P.vec, Tr::kNegInfBits, rp);
+    if (resid) {
+      if constexpr (kQ) load8((const uint32_t*)qrow, y, V, qvec, 0u, rq);
+      else load8(Q.row, y, V, Q.vec, Tr::kNegInfBits, rq);
+    }
+  }
+};
+
+// A group's weights with the ties of each cut both kept and left out (see
+// GroupRec), summed over one lane's ids.
+struct GroupAcc {
+  double a, bp, cq1, cq0, ap;
+  uint32_t np, nq, npq, bad;
+};
+
+template <class Tr, bool kQ>
+__device__ inline void weigh8(const DrawCtx<Tr, kQ>& d, bool resid, int y,
+                              const typename DrawCtx<Tr, kQ>::RawP& pr,
+                              const typename DrawCtx<Tr, kQ>::RawQ& qr, GroupAcc& s) {
+  // Selects rather than branches per lane; the branches below test ballots
+  // (one value for the whole wave), so no lane masks are set up per token.
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const uint32_t up = pr.get(e), kp = Tr::key(up);
+    const bool tp = d.P.tie(kp);
+    const bool mp = !tp && d.P.fixed_member(kp, y + e);
+    bool tq = false, mq = false;
+    const uint32_t uq = resid ? qr.get(e) : 0u;
+    if constexpr (!kQ) {
+      if (resid) {
+        const uint32_t kq = Tr::key(uq);
+        tq = d.Q.tie(kq);
+        mq = !tq && d.Q.fixed_member(kq, y + e);
+      }
+    }
+    // no member or tie of either row at this position in the whole wave: the
+    // tokens add nothing (most tokens of a truncated row)
+    if (!__builtin_amdgcn_ballot_w64(mp || tp || mq || tq)) continue;
+    double pv = 0.0;
+    if (__builtin_amdgcn_ballot_w64(mp)) {
+      const double w = d.P.w(Tr::value(up));
+      pv = mp ? w : 0.0;
+    }
+    if (!resid) {
+      s.a += pv;
+      s.np += tp ? 1u : 0u;
+      continue;
+    }
+    double qv = 0.0;
+    bool qbad = false;
+    if constexpr (kQ) {
+      qv = (double)__uint_as_float(uq);
+      qbad = !(qv >= 0.0 && qv < INFINITY);
+    } else if (__builtin_amdgcn_ballot_w64(mq)) {
+      const double w = d.Q.w(Tr::value(uq));
+      qv = mq ? w : 0.0;
+    }
+    const bool plain = !tp && !tq;
+    const double df = pv - qv;
+    s.a += (plain && pv > 0.0 && df > 0.0) ? df : 0.0;
+    s.ap += tp ? 0.0 : pv;
+    if (kQ && plain && pv > 0.0 && qbad) s.bad |= 1u;
+    if (__builtin_amdgcn_ballot_w64(tp || tq)) {  // ties: rows cut by rank only
+      const double dp = d.P.wcut - qv;   // a tie of p (not of q), kept
+      s.bp += (tp && !tq && d.P.wcut > 0.0 && dp > 0.0) ? dp : 0.0;
+      const double dq = pv - d.Q.wcut;   // a tie of q (not of p), kept
+      s.cq1 += (!tp && tq && pv > 0.0 && dq > 0.0) ? dq : 0.0;
+      s.cq0 += (!tp && tq) ? pv : 0.0;
+      s.np += tp ? 1u : 0u;
+      s.nq += tq ? 1u : 0u;
+      s.npq += (tp && tq) ? 1u : 0u;
+      if (kQ && tp && qbad) s.bad |= 2u;
+    }
+  }
+}
+
+// Group records cross workgroups as six 64-bit words in device-scope atomics
+// (the session's workgroups may run on different L2 caches): lane i of the
+// wave stores word i of the wave-uniform sums.
+__device__ inline void store_group(GroupRec* rec, const GroupAcc& s) {
+  const int lane = __lane_id();
+  const double dv = lane == 0 ? s.a : lane == 1 ? s.bp : lane == 2 ? s.cq1 : lane == 3 ? s.cq0 : s.ap;
+  uint64_t w = (uint64_t)__double_as_longlong(dv);
+  if (lane == 5)
+    w = (uint64_t)(s.np | (s.nq << 16)) | ((uint64_t)(s.npq | (s.bad << 16)) << 32);
+  if (lane < 6) __hip_atomic_store((uint64_t*)rec + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline GroupAcc decode_group(const uint64_t (&w)[6]) {
+  GroupAcc r;
+  r.a = __longlong_as_double((long long)w[0]);
+  r.bp = __longlong_as_double((long long)w[1]);
+  r.cq1 = __longlong_as_double((long long)w[2]);
+  r.cq0 = __longlong_as_double((long long)w[3]);
+  r.ap = __longlong_as_double((long long)w[4]);
+  r.np = (uint32_t)w[5] & 0xFFFFu;
+  r.nq = (uint32_t)w[5] >> 16;
+  r.npq = (uint32_t)(w[5] >> 32) & 0xFFFFu;
+  r.bad = (uint32_t)(w[5] >> 48);
+  return r;
+}
+__device__ inline GroupAcc load_group(const GroupRec* rec) {
+  uint64_t w[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i)
+    w[i] = __hip_atomic_load((const uint64_t*)rec + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return decode_group(w);
+}
+
+// One wave records groups [g0, g1): steps of 8 ids per lane through a ring of
+// kSteps loads, two steps ahead.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid, int g0, int g1,
+                              GroupRec* __restrict__ recs) {
+  if (g0 >= g1) return;
+  const int lane = __lane_id();
+  const int nk = (g1 - g0) * kSteps;
+  const int ybase = g0 * kGroup + lane * kPer;
+  typename DrawCtx<Tr, kQ>::RawP p[kSteps];
+  typename DrawCtx<Tr, kQ>::RawQ q[kSteps];
+  d.load(ybase, resid, p[0], q[0]);
+  d.load(ybase + kWStep, resid, p[1], q[1]);
+  for (int k = 0; k < nk; k += kSteps) {
+    GroupAcc s{};
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const int kk = k + u;
+      if (kk + 2 < nk) d.load(ybase + (kk + 2) * kWStep, resid, p[(u + 2) % kSteps], q[(u + 2) % kSteps]);
+      weigh8<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s);
+    }
+    s.a = wave_reduce(s.a, OpAdd());
+    s.bp = wave_reduce(s.bp, OpAdd());
+    s.cq1 = wave_reduce(s.cq1, OpAdd());
+    s.cq0 = wave_reduce(s.cq0, OpAdd());
+    s.ap = wave_reduce(s.ap, OpAdd());
+    s.np = wave_reduce(s.np, OpAdd());
+    s.nq = wave_reduce(s.nq, OpAdd());
+    s.npq = wave_reduce(s.npq, OpAdd());
+    s.bad = wave_reduce(s.bad, OpOr());
+    store_group(recs + g0 + k / kSteps, s);
+  }
+}
+
+// Exclusive prefix over the wave's lanes of a count in 0..15, and the wave
+// total, from one ballot per bit.
+__device__ inline uint32_t wave_excl_count(uint32_t c, uint32_t* total) {
+  uint32_t r = 0, t = 0;
+#pragma unroll
+  for (int bit = 0; bit < 4; ++bit) {
+    const uint64_t bm = __ballot((c >> bit) & 1u);
+    r += (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0)) << bit;
+    t += (uint32_t)__builtin_popcountll(bm) << bit;
+  }
+  *total = t;
+  return r;
+}
+
+// Group g weighed id by id by one wave, ties ranked: rp, rq are the ties of p
+// and q before the group.  Returns the group's weight and tie counts, the last
+// id with weight, whether an unusable published q entry was read where p > 0,
+// and (find) the first id at which base + running weight exceeds tgt.
+struct ScanRes {
+  double total;
+  int32_t first;  // INT32_MAX: not in this group
+  int32_t lastpos;
+  uint32_t np, nq;
+  bool bad;
+};
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, kQ>& d, bool resid, int g, uint32_t rp,
+                              uint32_t rq, double base, double tgt, bool find) {
+  const int lane = __lane_id();
+  const int ybase = g * kGroup + lane * kPer;
+  typename DrawCtx<Tr, kQ>::RawP pc, pn;
+  typename DrawCtx<Tr, kQ>::RawQ qc, qn;
+  d.load(ybase, resid, pc, qc);
+  ScanRes res{0.0, INT32_MAX, -1, 0u, 0u, false};
+  double run = base;
+  bool bad = false;
+  int32_t lastpos = -1;
+#pragma unroll 1
+  for (int s = 0; s < kSteps; ++s) {
+    const int y = ybase + s * kWStep;
+    if (s + 1 < kSteps) d.load(y + kWStep, resid, pn, qn);
+    uint32_t fp = 0, fq = 0;  // which of the 8 ids are ties of p, of q
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (d.P.tie(Tr::key(pc.get(e)))) fp |= 1u << e;
+      if constexpr (!kQ)
+        if (resid && d.Q.tie(Tr::key(qc.get(e)))) fq |= 1u << e;
+    }
+    uint32_t tp, tq;
+    uint32_t cp = rp + wave_excl_count(__builtin_popcount(fp), &tp);
+    uint32_t cq = rq + wave_excl_count(__builtin_popcount(fq), &tq);
+    double w[kPer];
+    double ls = 0.0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      double pv;
+      if ((fp >> e) & 1u) pv = cp++ < d.P.ntie ? d.P.wcut : 0.0;
+      else pv = d.P.p_fixed(pc.get(e), y + e);
+      double wt = pv;
+      if (resid) {
+        double qv;
+        if constexpr (kQ) {
+          qv = (double)__uint_as_float(qc.get(e));
+          bad |= pv > 0.0 && !(qv >= 0.0 && qv < INFINITY);
+        } else {
+          if ((fq >> e) & 1u) qv = cq++ < d.Q.ntie ? d.Q.wcut : 0.0;
+          else qv = d.Q.p_fixed(qc.get(e), y + e);
+        }
+        const double df = pv - qv;
+        wt = (pv > 0.0 && df > 0.0) ? df : 0.0;
+      }
+      w[e] = wt;
+      ls += wt;
+      if (wt > 0.0) lastpos = y + e;
+    }
+    // running weight over the lanes in id order
+    double incl = ls;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const double t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    // the exclusive prefix as incl - ls: a shift of incl by one lane whose
+    // result only the lanes above 0 read was moved by this compiler into a
+    // branch without lane 0, where the shift then reads 0 for lane 1
+    const double excl = incl - ls;
+    const double tot = __shfl(incl, kWave - 1, kWave);
+    if (find && res.first == INT32_MAX) {
+      double acc = run + excl;
+      int32_t mine = INT32_MAX;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        acc += w[e];
+        if (mine == INT32_MAX && acc > tgt) mine = y + e;
+      }
+      res.first = wave_reduce(mine, OpMin());
+    }
+    run += tot;
+    res.total += tot;
+    rp += tp;
+    rq += tq;
+    res.np += tp;
+    res.nq += tq;
+    pc = pn;
+    qc = qn;
+  }
+  res.lastpos = wave_reduce(lastpos, OpMax());
+  res.bad = __any(bad);
+  return res;
+}
+
+// A group's weight from its record: the ties of p kept (sp = 1), left out
+// (sp = 0); likewise for q.  kept: ties of p kept (draws from p).
+__device__ inline double group_mass(const GroupAcc& r, bool resid, int sp, int sq, uint32_t kept,
+                                    double Pk, double Qk) {
+  if (!resid) return r.a + (double)kept * Pk;
+  double m = r.a + (sp ? r.bp : 0.0) + (sq ? r.cq1 : r.cq0);
+  if (r.npq) {
+    const double df = Pk - Qk;
+    m += (double)r.npq * (sp ? (sq ? ((Pk > 0.0 && df > 0.0) ? df : 0.0) : Pk) : 0.0);
+  }
+  return m;
+}
+
+constexpr int kLdsGroups = 512;  // group records staged in LDS for the pick
+
+struct DrawSmem {
+  uint64_t grec[kLdsGroups][6];
+  double tab_p[kTab];
+  double tab_q[kTab];
+  double dscan[kDrawWaves];
+  uint64_t uscan[kDrawWaves];
+  int32_t ired[kDrawWaves];
+  int32_t sg[2];            // groups holding the cut of p, of q (-1: none)
+  uint32_t stp[2], stq[2];  // their ties before them
+  double smass[2];          // their weights, ties ranked
+  int32_t sbad[2];
+  int32_t gstar;            // the group holding u * S, its weight before, ties before
+  double gbase;
+  uint32_t gtp, gtq;
+  uint32_t ltp, ltq;        // ties before the last group with weight
+  int32_t q_id[kSupMax];
+  double q_p[kSupMax];
+  Job job;
+  uint32_t last;
+};
+
 // Block-wide exclusive scan in thread order (fixed combination order).
-template <typename T>
-__device__ T block_exclusive_scan(T v, T* wsum, T* total) {
+template <int NT, typename T>
+__device__ __attribute__((always_inline)) T block_exclusive_scan(T v, T* wsum, T* total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   T inc = v;
 #pragma unroll
@@ -267,14 +671,13 @@ __device__ T block_exclusive_scan(T v, T* wsum, T* total) {
     const T t = __shfl_up(inc, off, kWave);
     if (lane >= off) inc += t;
   }
-  T exc = __shfl_up(inc, 1, kWave);
-  if (lane == 0) exc = T(0);
+  const T exc = inc - v;  // not a one-lane shift: see group_scan
   __syncthreads();
   if (lane == kWave - 1) wsum[wid] = inc;
   __syncthreads();
   T base = T(0), tot = T(0);
 #pragma unroll
-  for (int w = 0; w < kSampleNT / kWave; ++w) {
+  for (int w = 0; w < NT / kWave; ++w) {
     if (w < wid) base += wsum[w];
     tot += wsum[w];
   }
@@ -282,141 +685,15 @@ __device__ T block_exclusive_scan(T v, T* wsum, T* total) {
   return base + exc;
 }
 
-struct SampleSmem {
-  double lut_p[kLut];         // p of the keys below p's largest key
-  double lut_q[kLut];         // q of the keys below q's largest key
-  double mass[kMaxGroups];    // weight of each group
-  uint64_t ties[kMaxGroups];  // the cut keys' ties in each group (p low word, q high), then before it
-  double dsum[kSampleWaves];
-  uint64_t usum[kSampleWaves];
-  int32_t ired[kSampleWaves];
-  double base;
-};
-
-// The draw of one session's additional token: weights w(y) = max(0, p(y) -
-// q(y)) (zero where p is zero) for the residual, or p(y); the smallest id
-// whose running weight exceeds u * S.
+// The kernel: workgroup (b, c) = blockIdx.x = b * C + c; wave w of chunk c
+// records groups [(4c + w) * gw, (4c + w + 1) * gw).  Every workgroup's first
+// wave takes session b's acceptance rule; chunk 0's workgroup writes the
+// outputs of a session left with no whole-row draw.  With such a draw, the
+// last workgroup to finish (a counter per session, cleared by the single-pass
+// row kernel; C = 1 needs none) picks the token and writes all the session's
+// outputs.
 template <class Tr, bool kQ>
-struct Draw {
-  SampleRow<Tr> P, Q;  // Q unused with kQ
-  const float* qrow;   // the published q row (kQ)
-  bool resid;
-  int V;
-};
-
-// Bits of this lane's 4 consecutive ids of the sub-block starting at y0.
-template <class Tr, bool kQ>
-__device__ inline void sub_load(const Draw<Tr, kQ>& d, int y0, uint32_t (&up)[4],
-                                uint32_t (&uq)[4]) {
-  const int y = y0 + 4 * __lane_id();
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const bool in = y + e < d.V;
-    up[e] = in ? Tr::bits(d.P.row[y + e]) : Tr::kNegInfBits;
-    if constexpr (kQ) uq[e] = (in && d.resid) ? __float_as_uint(d.qrow[y + e]) : 0u;
-    else uq[e] = (in && d.resid) ? Tr::bits(d.Q.row[y + e]) : Tr::kNegInfBits;
-  }
-}
-
-// Which of the 4 ids hold a cut key whose ties are kept by rank: bit e for p,
-// bit 4 + e for q.
-template <class Tr, bool kQ>
-__device__ inline uint32_t sub_tie_bits(const Draw<Tr, kQ>& d, const uint32_t (&up)[4],
-                                        const uint32_t (&uq)[4]) {
-  uint32_t f = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (d.P.tie_mode() && Tr::key(up[e]) == d.P.r.kcut) f |= 1u << e;
-    if (!kQ && d.resid && d.Q.tie_mode() && Tr::key(uq[e]) == d.Q.r.kcut) f |= 16u << e;
-  }
-  return f;
-}
-
-// Exclusive prefix over the wave's lanes of a small count (0..7), and the
-// wave total, from one ballot per bit.
-__device__ inline int wave_excl_small(int c, int* total) {
-  int r = 0, t = 0;
-#pragma unroll
-  for (int bit = 0; bit < 3; ++bit) {
-    const uint64_t bm = __ballot((c >> bit) & 1);
-    r += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0)) << bit;
-    t += __builtin_popcountll(bm) << bit;
-  }
-  *total = t;
-  return r;
-}
-
-// Weights of this lane's 4 ids of a sub-block.  rp, rq: the cut keys' ties
-// before the sub-block (wave-uniform); on return they count its ties too.
-template <class Tr, bool kQ>
-__device__ inline void sub_weights(const Draw<Tr, kQ>& d, int y0, const uint32_t (&up)[4],
-                                   const uint32_t (&uq)[4], uint32_t& rp, uint32_t& rq,
-                                   double (&w)[4], bool& bad) {
-  const uint32_t f = sub_tie_bits<Tr, kQ>(d, up, uq);
-  int tp, tq;
-  const int bp = wave_excl_small(__builtin_popcount(f & 15u), &tp);
-  const int bq = wave_excl_small(__builtin_popcount(f >> 4), &tq);
-  int cp = (int)rp + bp, cq = (int)rq + bq;
-  const int y = y0 + 4 * __lane_id();
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const double p = d.P.prob(y + e, up[e], cp);
-    if (!d.resid) {
-      w[e] = p;
-    } else {
-      double q;
-      if constexpr (kQ) {
-        q = (double)__uint_as_float(uq[e]);
-        bad |= p > 0.0 && !(q >= 0.0 && q < INFINITY);
-      } else {
-        q = d.Q.prob(y + e, uq[e], cq);
-      }
-      const double df = p - q;
-      w[e] = (p > 0.0 && df > 0.0) ? df : 0.0;
-    }
-    cp += (f >> e) & 1u;
-    cq += (f >> (4 + e)) & 1u;
-  }
-  rp += (uint32_t)tp;
-  rq += (uint32_t)tq;
-}
-
-// Calls fn(y0, up, uq) for the sub-blocks of [lo, hi) in order (lo and hi on
-// sub-block boundaries, or hi = V).  (Loading four sub-blocks ahead measured
-// slower: the registers it needs push the kernel to its limit.)
-template <class Tr, bool kQ, class F>
-__device__ inline void stream_subs(const Draw<Tr, kQ>& d, int lo, int hi, F&& fn) {
-  for (int y0 = lo; y0 < hi; y0 += kSub) {
-    uint32_t up[4], uq[4];
-    sub_load<Tr, kQ>(d, y0, up, uq);
-    fn(y0, up, uq);
-  }
-}
-
-__device__ inline double wave_incl_scan(double v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
-
-// Textbook "The acceptance rule" / SDCP Sec. 6.4 Rule 2: additional token from
-// norm(max(0, p_j - q_j)) at the first rejection j, or from p_{m+1}; the
-// smallest id whose running weight exceeds u * S.  One workgroup per session:
-// its first wave takes the acceptance decisions (finalize_session); a draw
-// from rows without listed supports then takes the whole workgroup.
-// The row is cut into at most kMaxGroups groups of whole sub-blocks; each wave
-// owns a run of consecutive groups and streams them with no workgroup barrier:
-// a first pass counts the cut keys' ties per group when they are kept by rank
-// (a workgroup scan then gives each group its ties before it), a second pass
-// weighs every group; a scan over the group weights finds the group holding
-// u * S, which one wave weighs again with a wave scan.
-template <class Tr, bool kQ>
-__global__ __launch_bounds__(kSampleNT) void k_finalize(
+__global__ __launch_bounds__(kDrawNT) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
     const float* __restrict__ qrows, const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M, int V,
@@ -424,159 +701,259 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
     const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
     int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
     const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p,
-    const double* __restrict__ unif) {
-  __shared__ SampleSmem sm;
-  __shared__ int32_t q_id[kSupMax];
-  __shared__ double q_p[kSupMax];
-  __shared__ Job job_s;
-  const int b = blockIdx.x;
+    const double* __restrict__ unif, GroupRec* __restrict__ groups, uint32_t* __restrict__ ctr,
+    const uint32_t* __restrict__ draw_flag, uint32_t draw_token, int C, int gw) {
+  __shared__ DrawSmem sm;
+  const int b = (int)blockIdx.x / C;
+  const int c = (int)blockIdx.x - b * C;
   if (b >= B) return;
-  if (threadIdx.x < kWave) {
-    const Job j = finalize_session(b, tokens, m, rule, sampling, M, V, kQ ? qrows : nullptr, seed,
-                                   round, sess_status, rows,
-                                   accepted_len, out_tokens, p_tok, q_tok, sup_id, sup_p, unif,
-                                   q_id, q_p);
-    if (threadIdx.x == 0) job_s = j;
+  const int t = threadIdx.x;
+  const int lane = t & (kWave - 1), wid = t / kWave;
+  // only chunk 0 has work in sessions that draw no token from whole rows
+  if (c > 0 && (draw_flag[b] != draw_token || rule[b] == SV_RULE_GREEDY || sess_status[b] != 0))
+    return;
+  Verdict v{};
+  if (t < kWave) {
+    v = accept_session(b, tokens, m, rule, sampling, M, V, kQ ? qrows : nullptr, seed, round,
+                       sess_status, rows, sup_id, sup_p, unif, c == 0, sm.q_id, sm.q_p);
+    if (v.st < 0 || v.job.kind == kJobNone) {
+      if (c == 0) write_verdict(b, v, v.extra, M, accepted_len, out_tokens, p_tok, q_tok);
+      v.job.kind = kJobNone;
+    }
+    if (t == 0) sm.job = v.job;
   }
   __syncthreads();
-  const Job job = job_s;
+  const Job job = sm.job;
   if (job.kind == kJobNone) return;
+
   const int R = 2 * M + 1;
-  Draw<Tr, kQ> d;
-  d.P = SampleRow<Tr>{target + ((size_t)b * (M + 1) + job.trow) * (size_t)V,
-                      rows[(size_t)b * R + job.trow], 0, nullptr};
-  d.Q = d.P;
-  d.qrow = nullptr;
-  d.resid = job.kind == kJobResidual;
-  d.V = V;
-  if (d.resid) {
-    if constexpr (kQ) d.qrow = qrows + ((size_t)b * M + job.drow) * (size_t)V;
-    else d.Q = SampleRow<Tr>{draft + ((size_t)b * M + job.drow) * (size_t)V,
-                             rows[(size_t)b * R + M + 1 + job.drow], 0, nullptr};
+  const int G = (V + kGroup - 1) / kGroup;
+  bool resid = job.kind == kJobResidual;
+  auto make_row = [&](const typename Tr::elem_t* row, const RowRec& r, double* tab) {
+    DrawRow<Tr> D;
+    D.row = row;
+    D.tab = tab;
+    D.s256 = r.scale * 256.0;
+    D.c256 = (double)r.lmax * D.s256;
+    D.kcut = r.kcut;
+    D.idcut = r.idcut;
+    D.ntie = r.idcut < 0 ? (uint32_t)r.ntie : 0u;
+    D.wcut = weight64(Tr::value(Tr::unkey(r.kcut)), r.lmax, r.scale) / r.zsum;
+    D.vec = ((uintptr_t)row & 15u) == 0;
+    tab[t] = exp2((double)t / (double)kTab) / r.zsum;  // one entry per thread
+    return D;
+  };
+  const DrawRow<Tr> Prow = make_row(target + ((size_t)b * (M + 1) + job.trow) * (size_t)V,
+                                    rows[(size_t)b * R + job.trow], sm.tab_p);
+  DrawRow<Tr> Qrow = Prow;
+  Qrow.idcut = 0;  // no q ties unless a draft row is read
+  Qrow.ntie = 0;
+  const float* qrow = nullptr;
+  if (resid) {
+    if constexpr (kQ) qrow = qrows + ((size_t)b * M + job.drow) * (size_t)V;
+    else Qrow = make_row(draft + ((size_t)b * M + job.drow) * (size_t)V,
+                         rows[(size_t)b * R + M + 1 + job.drow], sm.tab_q);
   }
-  fill_lut<Tr>(d.P, sm.lut_p);
-  if (!kQ) fill_lut<Tr>(d.Q, sm.lut_q);
+  const DrawCtx<Tr, kQ> d{Prow, Qrow, qrow, ((uintptr_t)qrow & 15u) == 0, V};
+  __syncthreads();  // tables ready
 
-  // groups: at most kMaxGroups runs of Lg ids (whole sub-blocks); wave w owns
-  // groups [g0, g1)
-  const int nsub = (V + kSub - 1) / kSub;
-  const int sub_per_group = (nsub + kMaxGroups - 1) / kMaxGroups;
-  const int Lg = sub_per_group * kSub;
-  const int ng = (V + Lg - 1) / Lg;
-  const int wid = (int)threadIdx.x / kWave, lane = __lane_id();
-  const int g0 = wid * ng / kSampleWaves, g1 = (wid + 1) * ng / kSampleWaves;
-  const bool ties = d.P.tie_mode() || (!kQ && d.resid && d.Q.tie_mode());
-
-  // the ties of each group, then of all groups before it
-  const int lo = g0 * Lg, hi = min(g1 * Lg, V);  // this wave's ids
-  if (ties) {
-    uint32_t cp = 0, cq = 0;
-    stream_subs<Tr, kQ>(d, lo, hi, [&](int y0, const uint32_t(&up)[4], const uint32_t(&uq)[4]) {
-      const uint32_t f = sub_tie_bits<Tr, kQ>(d, up, uq);
-      cp += __builtin_popcount(f & 15u);
-      cq += __builtin_popcount(f >> 4);
-      const int g = y0 / Lg;
-      if (y0 + kSub >= min((g + 1) * Lg, V)) {  // the group's last sub-block
-        const uint64_t c = wave_reduce((uint64_t)cp | ((uint64_t)cq << 32), OpAdd());
-        if (lane == 0) sm.ties[g] = c;
-        cp = cq = 0;
-      }
-    });
+  // this wave's groups, then (several chunks) the session's counter
+  GroupRec* recs = groups + (size_t)b * G;
+  {
+    const int g0 = (4 * c + wid) * gw;
+    record_groups<Tr, kQ>(d, resid, min(g0, G), min(g0 + gw, G), recs);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's records are stored
+  __syncthreads();
+  if (C > 1) {
+    if (t == 0) {
+      const uint32_t done =
+          __hip_atomic_fetch_add(&ctr[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = done == (uint32_t)(C - 1);
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      sm.last = last ? 1u : 0u;
+    }
     __syncthreads();
-    uint64_t tot;
-    const uint64_t c = (int)threadIdx.x < ng ? sm.ties[threadIdx.x] : 0ull;
-    const uint64_t before = block_exclusive_scan<uint64_t>(c, sm.usum, &tot);
-    if ((int)threadIdx.x < ng) sm.ties[threadIdx.x] = before;
+    if (!sm.last) return;
   }
-  __syncthreads();  // tables and tie counts are ready
 
-  // every group's weight, and the last id with weight
-  int32_t last = -1;
-  bool bad = false;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    last = -1;
-    uint32_t rp = 0, rq = 0;
-    double acc = 0.0;
-    stream_subs<Tr, kQ>(d, lo, hi, [&](int y0, const uint32_t(&up)[4], const uint32_t(&uq)[4]) {
-      const int g = y0 / Lg;
-      if (ties && y0 == g * Lg) {  // the ties before the group
-        rp = (uint32_t)sm.ties[g];
-        rq = (uint32_t)(sm.ties[g] >> 32);
-      }
-      double w[4];
-      sub_weights<Tr, kQ>(d, y0, up, uq, rp, rq, w, bad);
+  // ---- the session's last workgroup: thread t adds up groups [ga, gb)
+  const int ga = (int)((long long)t * G / kDrawNT), gb = (int)((long long)(t + 1) * G / kDrawNT);
+  // the records, staged in LDS when they fit (else read where they are)
+  const bool staged = G <= kLdsGroups;
+  if (staged) {
+    for (int i = t; i < G * 6; i += kDrawNT)
+      sm.grec[i / 6][i % 6] = __hip_atomic_load((const uint64_t*)(recs + i / 6) + i % 6,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+  auto rec = [&](int g) -> GroupAcc {
+    if (staged) {
+      uint64_t w[6];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc += w[e];
-        if (w[e] > 0.0) last = y0 + 4 * lane + e;
+      for (int i = 0; i < 6; ++i) w[i] = sm.grec[g][i];
+      return decode_group(w);
+    }
+    return load_group(recs + g);
+  };
+  const uint32_t jp = d.P.ntie, jq = d.Q.ntie;
+  const double Pk = d.P.wcut, Qk = kQ ? 0.0 : d.Q.wcut;
+  // a group's ties: all kept (1), none (0), or the cut falls inside it (2)
+  auto state = [](uint32_t before, uint32_t n, uint32_t j) -> int {
+    return before + n <= j ? 1 : (before >= j ? 0 : 2);
+  };
+  auto kept = [](int s, uint32_t before, uint32_t n, uint32_t j) -> uint32_t {
+    return s == 1 ? n : (s == 0 ? 0u : j - before);
+  };
+  if (t == 0) sm.sg[0] = sm.sg[1] = -1;
+  uint32_t lp = 0, lq = 0;
+  for (int g = ga; g < gb; ++g) {
+    const GroupAcc r = rec(g);
+    lp += r.np;
+    lq += r.nq;
+  }
+  uint64_t ttot;
+  const uint64_t tb = block_exclusive_scan<kDrawNT, uint64_t>((uint64_t)lp | ((uint64_t)lq << 32),
+                                                             sm.uscan, &ttot);
+  const uint32_t tp0 = (uint32_t)tb, tq0 = (uint32_t)(tb >> 32);
+  if (resid) {  // the groups holding a cut: their weights need the ties ranked
+    uint32_t tp = tp0, tq = tq0;
+    for (int g = ga; g < gb; ++g) {
+      const GroupAcc r = rec(g);
+      if (state(tp, r.np, jp) == 2) {
+        sm.sg[0] = g;
+        sm.stp[0] = tp;
+        sm.stq[0] = tq;
       }
-      if (y0 + kSub >= min((g + 1) * Lg, V)) {  // the group's last sub-block
-        const double gm = wave_reduce(acc, OpAdd());
-        if (lane == 0) sm.mass[g] = gm;
-        acc = 0.0;
+      if (state(tq, r.nq, jq) == 2) {
+        sm.sg[1] = g;
+        sm.stp[1] = tp;
+        sm.stq[1] = tq;
       }
-    });
-    last = block_reduce<kSampleNT>(last, OpMax(), sm.ired);
-    if (kQ && d.resid && attempt == 0) {
-      // an unusable entry of the published residual row fails the session; the
-      // first wave rewrites its outputs as it wrote them
-      if (block_reduce<kSampleNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0) {
-        if (threadIdx.x < kWave)
-          write_failed(b, SV_S_BAD_PROPOSAL, M, accepted_len, out_tokens, p_tok, q_tok);
-        return;
+      tp += r.np;
+      tq += r.nq;
+    }
+  }
+  __syncthreads();
+  if (wid < 2) {
+    const int g = sm.sg[wid];
+    if (g >= 0 && !(wid == 1 && g == sm.sg[0])) {
+      const ScanRes sr = group_scan<Tr, kQ>(d, true, g, sm.stp[wid], sm.stq[wid], 0.0, 0.0, false);
+      if (lane == 0) {
+        sm.smass[wid] = sr.total;
+        sm.sbad[wid] = sr.bad ? 1 : 0;
       }
     }
-    if (!d.resid || last >= 0) break;
-    d.resid = false;  // residual without mass (rounding only): draw from p
-    __syncthreads();  // the group weights are written again
   }
-
-  // the group holding u * S (thread g holds group g)
   __syncthreads();
-  const double gm = (int)threadIdx.x < ng ? sm.mass[threadIdx.x] : 0.0;
-  double S;
-  const double before = block_exclusive_scan<double>(gm, sm.dsum, &S);
-  const double tgt = job.u * S;
-  const int32_t mine_g = ((int)threadIdx.x < ng && before + gm > tgt) ? (int32_t)threadIdx.x : 0x7FFFFFFF;
-  const int32_t gstar = block_reduce<kSampleNT>(mine_g, OpMin(), sm.ired);
-  if (gstar == 0x7FFFFFFF) {
-    if (threadIdx.x == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = last;
+  // every group's weight (the ranked weights for the cut groups)
+  auto mass_of = [&](int g, const GroupAcc& r, uint32_t tp, uint32_t tq, bool rs, bool* badp) -> double {
+    const int sp = state(tp, r.np, jp), sq = rs ? state(tq, r.nq, jq) : 1;
+    if (!rs) return (resid ? r.ap : r.a) + (double)kept(sp, tp, r.np, jp) * Pk;
+    if (g == sm.sg[0] || g == sm.sg[1]) {
+      const int k = g == sm.sg[0] ? 0 : 1;
+      if (badp) *badp |= sm.sbad[k] != 0;
+      return sm.smass[k];
+    }
+    if (badp) *badp |= (r.bad & 1u) || ((r.bad & 2u) && sp == 1 && Pk > 0.0);
+    return group_mass(r, true, sp, sq, 0u, Pk, Qk);
+  };
+  double loc = 0.0;
+  bool bad = false;
+  {
+    uint32_t tp = tp0, tq = tq0;
+    for (int g = ga; g < gb; ++g) {
+      const GroupAcc r = rec(g);
+      loc += mass_of(g, r, tp, tq, resid, &bad);
+      tp += r.np;
+      tq += r.nq;
+    }
+  }
+  if (kQ && resid && block_reduce<kDrawNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0) {
+    // an unusable entry of the published residual row fails the session
+    if (t < kWave) write_failed(b, SV_S_BAD_PROPOSAL, M, accepted_len, out_tokens, p_tok, q_tok);
     return;
   }
-  if ((int)threadIdx.x == gstar) sm.base = before;
-  __syncthreads();
-  if (wid != 0) return;
-  // the first wave weighs the group again, sub-block by sub-block, and goes on
-  // past it if rounding moved the point
-  double run = sm.base;
-  int32_t pick = last;
-  bool found = false;
-  for (int g = gstar; g < ng && !found; ++g) {
-    uint32_t rp = ties ? (uint32_t)sm.ties[g] : 0u, rq = ties ? (uint32_t)(sm.ties[g] >> 32) : 0u;
-    for (int y0 = g * Lg; y0 < min((g + 1) * Lg, V); y0 += kSub) {
-      uint32_t up[4], uq[4];
-      sub_load<Tr, kQ>(d, y0, up, uq);
-      double w[4];
-      sub_weights<Tr, kQ>(d, y0, up, uq, rp, rq, w, bad);
-      const double ls = (w[0] + w[1]) + (w[2] + w[3]);
-      const double incl = wave_incl_scan(ls);
-      double a = run + (incl - ls);
-      int32_t mine = 0x7FFFFFFF;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a += w[e];
-        if (mine == 0x7FFFFFFF && a > tgt) mine = y0 + 4 * lane + e;
-      }
-      const int32_t first = wave_reduce(mine, OpMin());
-      if (first != 0x7FFFFFFF) {
-        pick = first;
+  double S;
+  double before = block_exclusive_scan<kDrawNT, double>(loc, sm.dscan, &S);
+  bool rs = resid;
+  if (resid && S == 0.0) {  // residual without mass (rounding only): draw from p
+    rs = false;
+    loc = 0.0;
+    uint32_t tp = tp0, tq = tq0;
+    for (int g = ga; g < gb; ++g) {
+      const GroupAcc r = rec(g);
+      loc += mass_of(g, r, tp, tq, false, nullptr);
+      tp += r.np;
+      tq += r.nq;
+    }
+    before = block_exclusive_scan<kDrawNT, double>(loc, sm.dscan, &S);
+  }
+  const double tgt = job.u * S;
+  // the group holding u * S, and the last group with weight
+  if (t == 0) sm.gstar = -1;
+  const int owner = block_reduce<kDrawNT>((gb > ga && before + loc > tgt) ? t : INT32_MAX,
+                                          OpMin(), sm.ired);
+  int lastg = -1;
+  {
+    uint32_t tp = tp0, tq = tq0;
+    double run = before;
+    bool found = false;
+    for (int g = ga; g < gb; ++g) {
+      const GroupAcc r = rec(g);
+      const double mg = mass_of(g, r, tp, tq, rs, nullptr);
+      if (t == owner && !found && run + mg > tgt) {
         found = true;
-        break;
+        sm.gstar = g;
+        sm.gbase = run;
+        sm.gtp = tp;
+        sm.gtq = tq;
       }
-      run += __shfl(incl, kWave - 1, kWave);
+      if (mg > 0.0) lastg = g;
+      run += mg;
+      tp += r.np;
+      tq += r.nq;
+    }
+    // rounding kept the point past this range's groups: on from the next one
+    if (t == owner && !found && gb < G) {
+      sm.gstar = gb;
+      sm.gbase = run;
+      sm.gtp = tp;
+      sm.gtq = tq;
     }
   }
-  if (lane == 0) out_tokens[(size_t)b * (M + 1) + job.pos] = pick;
+  const int lg = block_reduce<kDrawNT>(lastg, OpMax(), sm.ired);
+  if (lg >= 0 && lastg == lg) {  // this thread's range holds it: its ties before
+    uint32_t tp = tp0, tq = tq0;
+    for (int g = ga; g < lg; ++g) {
+      const GroupAcc r = rec(g);
+      tp += r.np;
+      tq += r.nq;
+    }
+    sm.ltp = tp;
+    sm.ltq = tq;
+  }
+  __syncthreads();
+  if (wid != 0) return;
+  // the first wave weighs the group again id by id, on past it if rounding
+  // moved the point, else takes the largest id with weight
+  int32_t pick = INT32_MAX;
+  if (sm.gstar >= 0) {
+    double run = sm.gbase;
+    uint32_t tp = sm.gtp, tq = sm.gtq;
+    for (int g = sm.gstar; g < G && pick == INT32_MAX; ++g) {
+      const ScanRes sr = group_scan<Tr, kQ>(d, rs, g, tp, tq, run, tgt, true);
+      pick = sr.first;
+      run += sr.total;
+      tp += sr.np;
+      tq += sr.nq;
+    }
+  }
+  if (pick == INT32_MAX) {
+    pick = -1;
+    if (lg >= 0) pick = group_scan<Tr, kQ>(d, rs, lg, sm.ltp, sm.ltq, 0.0, 0.0, false).lastpos;
+  }
+  write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
 }
 
 }  // namespace
@@ -584,10 +961,12 @@ __global__ __launch_bounds__(kSampleNT) void k_finalize(
 template <class Tr, bool kQ>
 static void launch_finalize_t(const LaunchArgs& a, hipStream_t st) {
   using E = typename Tr::elem_t;
-  hipLaunchKernelGGL((k_finalize<Tr, kQ>), dim3(a.B), dim3(kSampleNT), 0, st, (const E*)a.target,
+  const unsigned grid = (unsigned)((size_t)a.B * (size_t)a.draw_C);
+  hipLaunchKernelGGL((k_finalize<Tr, kQ>), dim3(grid), dim3(kDrawNT), 0, st, (const E*)a.target,
                      (const E*)a.draft, a.qrows, a.tokens, a.m, a.rule, a.sampling, a.B, a.M, a.V,
                      a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens, a.p_tok,
-                     a.q_tok, a.sup_id, a.sup_p, a.unif);
+                     a.q_tok, a.sup_id, a.sup_p, a.unif, a.groups, a.draw_ctr, a.draw_flag,
+                     a.draw_token, a.draw_C, a.draw_gw);
 }
 
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
