@@ -35,10 +35,11 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "stream-v2"
+KERNEL_REVISION = "stream-v3"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
     ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
+    ("b256_topk_topp", "k_rows_stream", "stream-v3"): 1_119_487_488,
 }
 
 
