@@ -261,21 +261,29 @@ constexpr int kDrawWaves = kDrawNT / kWave;
 constexpr int kPer = 8;                      // consecutive ids per lane per step
 constexpr int kWStep = kWave * kPer;         // ids per wave step
 constexpr int kSteps = kGroup / kWStep;      // wave steps per group
-constexpr int kTab = 256;
+constexpr int kTabBits = 9;                // 2^(i / kTab) tabled per row
+constexpr int kTab = 1 << kTabBits;
+constexpr int kDeg = 4;                    // degree of the polynomial for 2^(f / kTab)
 static_assert(kSteps == 4, "the load ring holds one group");
 
 // Weights in binary64 by Tang's table-driven method (P. T. P. Tang, "Table-
 // driven implementation of the exponential function in IEEE floating-point
 // arithmetic", ACM TOMS 15(2), 1989), base 2: with x = (l - lmax) * scale and
-// 256 x = n + f (n integer, 0 <= f < 1),
-//   2^x = 2^(n >> 8) * 2^((n & 255) / 256) * 2^(f / 256),
-// the middle factor (divided by the row's Z) tabled per row, the last a
-// degree-5 Taylor polynomial in f (truncation below 6e-19 relative).
-constexpr double kT1 = 0.69314718055994530942 / 256.0;  // ln 2 / 256
-constexpr double kT2 = kT1 * kT1 / 2.0;
-constexpr double kT3 = kT2 * kT1 / 3.0;
-constexpr double kT4 = kT3 * kT1 / 4.0;
-constexpr double kT5 = kT4 * kT1 / 5.0;
+// kTab x = n + f (n integer, 0 <= f < 1),
+//   2^x = 2^(n >> kTabBits) * 2^((n & (kTab - 1)) / kTab) * 2^(f / kTab),
+// the middle factor (divided by the row's Z) tabled per row, the last the
+// Taylor polynomial of exp(f ln2 / kTab) to degree kDeg (with kTab = 512 and
+// degree 4 the truncation is below 4e-17 relative; measured faster than 256
+// entries and degree 5, and than 16 to 64 entries with degrees 8 to 6).
+struct TaylorCoef {
+  double c[kDeg + 1];
+  constexpr TaylorCoef() : c() {
+    const double r = 0.69314718055994530942 / kTab;  // ln 2 / kTab
+    c[0] = 1.0;
+    for (int n = 1; n <= kDeg; ++n) c[n] = c[n - 1] * r / n;
+  }
+};
+constexpr TaylorCoef kTaylor;
 
 // One row as the draw sees it: p(y) = w(y) / Z on the support.  A row whose
 // cut is recorded as (kcut, ntie) keeps the ntie smallest ids among the tokens
@@ -285,7 +293,7 @@ template <class Tr>
 struct DrawRow {
   const typename Tr::elem_t* row;
   const double* tab;  // tab[i] = 2^(i / 256) / Z
-  double s256, c256;  // 256 * scale and 256 * scale * lmax (both exact)
+  double sk, ck;      // kTab * scale and kTab * scale * lmax (both exact)
   double wcut;        // p of each tie (tie mode)
   uint32_t kcut;
   int32_t idcut;
@@ -296,19 +304,17 @@ struct DrawRow {
     return k > kcut || (k == kcut && idcut >= 0 && y <= idcut);
   }
   __device__ double w(float l) const {
-    // t = 256 (l - lmax) scale, from exact products rounded once (as rounding
-    // (l - lmax) * scale, an exact difference, and scaling by 256); far below
+    // t = kTab (l - lmax) scale, from exact products rounded once (as rounding
+    // (l - lmax) * scale, an exact difference, and scaling by kTab); far below
     // the binary64 range the integer part saturates and ldexp gives 0
-    const double t = __builtin_fma((double)l, s256, -c256);
+    const double t = __builtin_fma((double)l, sk, -ck);
     const double n = floor(t);
     const double f = t - n;
     const int ni = (int)n;
-    double p = __builtin_fma(kT5, f, kT4);
-    p = __builtin_fma(p, f, kT3);
-    p = __builtin_fma(p, f, kT2);
-    p = __builtin_fma(p, f, kT1);
-    p = __builtin_fma(p, f, 1.0);
-    return ldexp(tab[ni & (kTab - 1)] * p, ni >> 8);
+    double p = kTaylor.c[kDeg];
+#pragma unroll
+    for (int i = kDeg - 1; i >= 0; --i) p = __builtin_fma(p, f, kTaylor.c[i]);
+    return ldexp(tab[ni & (kTab - 1)] * p, ni >> kTabBits);
   }
   // p of a token that is not a tie
   __device__ double p_fixed(uint32_t u, int y) const {
@@ -733,14 +739,14 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
     DrawRow<Tr> D;
     D.row = row;
     D.tab = tab;
-    D.s256 = r.scale * 256.0;
-    D.c256 = (double)r.lmax * D.s256;
+    D.sk = r.scale * (double)kTab;
+    D.ck = (double)r.lmax * D.sk;
     D.kcut = r.kcut;
     D.idcut = r.idcut;
     D.ntie = r.idcut < 0 ? (uint32_t)r.ntie : 0u;
     D.wcut = weight64(Tr::value(Tr::unkey(r.kcut)), r.lmax, r.scale) / r.zsum;
     D.vec = ((uintptr_t)row & 15u) == 0;
-    tab[t] = exp2((double)t / (double)kTab) / r.zsum;  // one entry per thread
+    for (int i = t; i < kTab; i += kDrawNT) tab[i] = exp2((double)i / (double)kTab) / r.zsum;
     return D;
   };
   const DrawRow<Tr> Prow = make_row(target + ((size_t)b * (M + 1) + job.trow) * (size_t)V,
