@@ -486,7 +486,7 @@ __device__ inline GroupAcc load_group(const GroupRec* rec) {
 }
 
 // One wave records groups [g0, g1): steps of 8 ids per lane through a ring of
-// kSteps loads, two steps ahead.
+// kSteps loads, three steps ahead.
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid, int g0, int g1,
                               GroupRec* __restrict__ recs) {
@@ -498,12 +498,13 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
   typename DrawCtx<Tr, kQ>::RawQ q[kSteps];
   d.load(ybase, resid, p[0], q[0]);
   d.load(ybase + kWStep, resid, p[1], q[1]);
+  d.load(ybase + 2 * kWStep, resid, p[2], q[2]);
   for (int k = 0; k < nk; k += kSteps) {
     GroupAcc s{};
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int kk = k + u;
-      if (kk + 2 < nk) d.load(ybase + (kk + 2) * kWStep, resid, p[(u + 2) % kSteps], q[(u + 2) % kSteps]);
+      if (kk + 3 < nk) d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
       weigh8<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s);
     }
     s.a = wave_reduce(s.a, OpAdd());
@@ -534,103 +535,6 @@ __device__ inline uint32_t wave_excl_count(uint32_t c, uint32_t* total) {
   return r;
 }
 
-// Group g weighed id by id by one wave, ties ranked: rp, rq are the ties of p
-// and q before the group.  Returns the group's weight and tie counts, the last
-// id with weight, whether an unusable published q entry was read where p > 0,
-// and (find) the first id at which base + running weight exceeds tgt.
-struct ScanRes {
-  double total;
-  int32_t first;  // INT32_MAX: not in this group
-  int32_t lastpos;
-  uint32_t np, nq;
-  bool bad;
-};
-template <class Tr, bool kQ>
-__device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, kQ>& d, bool resid, int g, uint32_t rp,
-                              uint32_t rq, double base, double tgt, bool find) {
-  const int lane = __lane_id();
-  const int ybase = g * kGroup + lane * kPer;
-  typename DrawCtx<Tr, kQ>::RawP pc, pn;
-  typename DrawCtx<Tr, kQ>::RawQ qc, qn;
-  d.load(ybase, resid, pc, qc);
-  ScanRes res{0.0, INT32_MAX, -1, 0u, 0u, false};
-  double run = base;
-  bool bad = false;
-  int32_t lastpos = -1;
-#pragma unroll 1
-  for (int s = 0; s < kSteps; ++s) {
-    const int y = ybase + s * kWStep;
-    if (s + 1 < kSteps) d.load(y + kWStep, resid, pn, qn);
-    uint32_t fp = 0, fq = 0;  // which of the 8 ids are ties of p, of q
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      if (d.P.tie(Tr::key(pc.get(e)))) fp |= 1u << e;
-      if constexpr (!kQ)
-        if (resid && d.Q.tie(Tr::key(qc.get(e)))) fq |= 1u << e;
-    }
-    uint32_t tp, tq;
-    uint32_t cp = rp + wave_excl_count(__builtin_popcount(fp), &tp);
-    uint32_t cq = rq + wave_excl_count(__builtin_popcount(fq), &tq);
-    double w[kPer];
-    double ls = 0.0;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      double pv;
-      if ((fp >> e) & 1u) pv = cp++ < d.P.ntie ? d.P.wcut : 0.0;
-      else pv = d.P.p_fixed(pc.get(e), y + e);
-      double wt = pv;
-      if (resid) {
-        double qv;
-        if constexpr (kQ) {
-          qv = (double)__uint_as_float(qc.get(e));
-          bad |= pv > 0.0 && !(qv >= 0.0 && qv < INFINITY);
-        } else {
-          if ((fq >> e) & 1u) qv = cq++ < d.Q.ntie ? d.Q.wcut : 0.0;
-          else qv = d.Q.p_fixed(qc.get(e), y + e);
-        }
-        const double df = pv - qv;
-        wt = (pv > 0.0 && df > 0.0) ? df : 0.0;
-      }
-      w[e] = wt;
-      ls += wt;
-      if (wt > 0.0) lastpos = y + e;
-    }
-    // running weight over the lanes in id order
-    double incl = ls;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const double t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
-    // the exclusive prefix as incl - ls: a shift of incl by one lane whose
-    // result only the lanes above 0 read was moved by this compiler into a
-    // branch without lane 0, where the shift then reads 0 for lane 1
-    const double excl = incl - ls;
-    const double tot = __shfl(incl, kWave - 1, kWave);
-    if (find && res.first == INT32_MAX) {
-      double acc = run + excl;
-      int32_t mine = INT32_MAX;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        acc += w[e];
-        if (mine == INT32_MAX && acc > tgt) mine = y + e;
-      }
-      res.first = wave_reduce(mine, OpMin());
-    }
-    run += tot;
-    res.total += tot;
-    rp += tp;
-    rq += tq;
-    res.np += tp;
-    res.nq += tq;
-    pc = pn;
-    qc = qn;
-  }
-  res.lastpos = wave_reduce(lastpos, OpMax());
-  res.bad = __any(bad);
-  return res;
-}
-
 // A group's weight from its record: the ties of p kept (sp = 1), left out
 // (sp = 0); likewise for q.  kept: ties of p kept (draws from p).
 __device__ inline double group_mass(const GroupAcc& r, bool resid, int sp, int sq, uint32_t kept,
@@ -653,6 +557,8 @@ struct DrawSmem {
   double dscan[kDrawWaves];
   uint64_t uscan[kDrawWaves];
   int32_t ired[kDrawWaves];
+  uint32_t wties[kDrawWaves];  // group scans: ties of each wave's step
+  double wsum[kDrawWaves];     // group scans: weight of each wave's step
   int32_t sg[2];            // groups holding the cut of p, of q (-1: none)
   uint32_t stp[2], stq[2];  // their ties before them
   double smass[2];          // their weights, ties ranked
@@ -689,6 +595,116 @@ __device__ __attribute__((always_inline)) T block_exclusive_scan(T v, T* wsum, T
   }
   *total = tot;
   return base + exc;
+}
+
+struct ScanRes {
+  double total;
+  int32_t first;  // INT32_MAX: not in this group
+  int32_t lastpos;
+  uint32_t np, nq;
+  bool bad;
+};
+
+// Group g weighed id by id by the whole workgroup, ties ranked: wave w takes
+// the group's step w (512 ids), the waves exchange their tie counts and
+// weights through LDS.  rp, rq are the ties of p and q before the group.
+// Returns the group's weight and tie counts, the last id with weight, whether
+// an unusable published q entry was read where p > 0, and (find) the first id
+// at which base + running weight exceeds tgt.  All threads call it.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                             int g, uint32_t rp, uint32_t rq,
+                                                             double base, double tgt, bool find,
+                                                             DrawSmem& sm) {
+  const int lane = __lane_id(), wid = (int)threadIdx.x / kWave;
+  const int y = g * kGroup + wid * kWStep + lane * kPer;
+  typename DrawCtx<Tr, kQ>::RawP pr;
+  typename DrawCtx<Tr, kQ>::RawQ qr;
+  d.load(y, resid, pr, qr);
+  uint32_t fp = 0, fq = 0;  // which of the 8 ids are ties of p, of q
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if (d.P.tie(Tr::key(pr.get(e)))) fp |= 1u << e;
+    if constexpr (!kQ)
+      if (resid && d.Q.tie(Tr::key(qr.get(e)))) fq |= 1u << e;
+  }
+  uint32_t tpw, tqw;
+  const uint32_t ep = wave_excl_count(__builtin_popcount(fp), &tpw);
+  const uint32_t eq = wave_excl_count(__builtin_popcount(fq), &tqw);
+  __syncthreads();  // the previous scan's exchange is read
+  if (lane == 0) sm.wties[wid] = tpw | (tqw << 16);  // at most 512 each
+  __syncthreads();
+  uint32_t bp = 0, bq = 0, np = 0, nq = 0;
+#pragma unroll
+  for (int w = 0; w < kDrawWaves; ++w) {
+    const uint32_t v = sm.wties[w];
+    if (w < wid) {
+      bp += v & 0xFFFFu;
+      bq += v >> 16;
+    }
+    np += v & 0xFFFFu;
+    nq += v >> 16;
+  }
+  uint32_t cp = rp + bp + ep, cq = rq + bq + eq;
+  double w8[kPer];
+  double ls = 0.0;
+  bool bad = false;
+  int32_t lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    double pv;
+    if ((fp >> e) & 1u) pv = cp++ < d.P.ntie ? d.P.wcut : 0.0;
+    else pv = d.P.p_fixed(pr.get(e), y + e);
+    double wt = pv;
+    if (resid) {
+      double qv;
+      if constexpr (kQ) {
+        qv = (double)__uint_as_float(qr.get(e));
+        bad |= pv > 0.0 && !(qv >= 0.0 && qv < INFINITY);
+      } else {
+        if ((fq >> e) & 1u) qv = cq++ < d.Q.ntie ? d.Q.wcut : 0.0;
+        else qv = d.Q.p_fixed(qr.get(e), y + e);
+      }
+      const double df = pv - qv;
+      wt = (pv > 0.0 && df > 0.0) ? df : 0.0;
+    }
+    w8[e] = wt;
+    ls += wt;
+    if (wt > 0.0) lastpos = y + e;
+  }
+  // running weight over the lanes in id order; the exclusive prefix as
+  // incl - ls (see block_exclusive_scan)
+  double incl = ls;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  const double excl = incl - ls;
+  const double wtot = __shfl(incl, kWave - 1, kWave);
+  if (lane == 0) sm.wsum[wid] = wtot;
+  __syncthreads();
+  double before = 0.0, total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kDrawWaves; ++w) {
+    const double v = sm.wsum[w];
+    if (w < wid) before += v;
+    total += v;
+  }
+  ScanRes res{total, INT32_MAX, -1, np, nq, false};
+  if (find) {
+    double acc = base + before + excl;
+    int32_t mine = INT32_MAX;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      acc += w8[e];
+      if (mine == INT32_MAX && acc > tgt) mine = y + e;
+    }
+    res.first = block_reduce<kDrawNT>(mine, OpMin(), sm.ired);
+  }
+  res.lastpos = block_reduce<kDrawNT>(lastpos, OpMax(), sm.ired);
+  res.bad = block_reduce<kDrawNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0;
+  return res;
 }
 
 // The kernel: workgroup (b, c) = blockIdx.x = b * C + c; wave w of chunk c
@@ -841,13 +857,13 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
     }
   }
   __syncthreads();
-  if (wid < 2) {
-    const int g = sm.sg[wid];
-    if (g >= 0 && !(wid == 1 && g == sm.sg[0])) {
-      const ScanRes sr = group_scan<Tr, kQ>(d, true, g, sm.stp[wid], sm.stq[wid], 0.0, 0.0, false);
-      if (lane == 0) {
-        sm.smass[wid] = sr.total;
-        sm.sbad[wid] = sr.bad ? 1 : 0;
+  for (int k = 0; k < 2; ++k) {
+    const int g = sm.sg[k];
+    if (g >= 0 && !(k == 1 && g == sm.sg[0])) {
+      const ScanRes sr = group_scan<Tr, kQ>(d, true, g, sm.stp[k], sm.stq[k], 0.0, 0.0, false, sm);
+      if (t == 0) {
+        sm.smass[k] = sr.total;
+        sm.sbad[k] = sr.bad ? 1 : 0;
       }
     }
   }
@@ -940,15 +956,15 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
     sm.ltq = tq;
   }
   __syncthreads();
-  if (wid != 0) return;
-  // the first wave weighs the group again id by id, on past it if rounding
-  // moved the point, else takes the largest id with weight
+  // the group holding u * S weighed again id by id, on past it if rounding
+  // moved the point, else the largest id with weight
   int32_t pick = INT32_MAX;
-  if (sm.gstar >= 0) {
+  const int gstar = sm.gstar;
+  if (gstar >= 0) {
     double run = sm.gbase;
     uint32_t tp = sm.gtp, tq = sm.gtq;
-    for (int g = sm.gstar; g < G && pick == INT32_MAX; ++g) {
-      const ScanRes sr = group_scan<Tr, kQ>(d, rs, g, tp, tq, run, tgt, true);
+    for (int g = gstar; g < G && pick == INT32_MAX; ++g) {
+      const ScanRes sr = group_scan<Tr, kQ>(d, rs, g, tp, tq, run, tgt, true, sm);
       pick = sr.first;
       run += sr.total;
       tp += sr.np;
@@ -957,9 +973,10 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   }
   if (pick == INT32_MAX) {
     pick = -1;
-    if (lg >= 0) pick = group_scan<Tr, kQ>(d, rs, lg, sm.ltp, sm.ltq, 0.0, 0.0, false).lastpos;
+    if (lg >= 0)
+      pick = group_scan<Tr, kQ>(d, rs, lg, sm.ltp, sm.ltq, 0.0, 0.0, false, sm).lastpos;
   }
-  write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
+  if (wid == 0) write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
 }
 
 }  // namespace
