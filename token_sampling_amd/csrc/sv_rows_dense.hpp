@@ -27,8 +27,8 @@
 //    the top until 1000 * C >= P * Z_k (Z_k = Z without top-k).  Either gives
 //    the cut key kc and the number j of its tokens that stay (those with the j
 //    smallest ids, profile order being logit desc, id asc).  A cut below the
-//    window (fewer than K tokens in it, or top-p's mass not reached) leaves
-//    the row to the generic kernel.
+//    window (fewer than K tokens in it, or top-p's mass not reached) hands
+//    the row back: the caller profiles it exactly.
 //  - the drafted token's rank among the tokens of its key with smaller ids (its
 //    key's bin just before its vector, plus the earlier tokens of that vector):
 //    it is in the support iff its key is above kc, or equal to kc with rank < j.
@@ -150,7 +150,7 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool hist, const u32x4& v,
 // The profile of one row of the dense class, by one wave: temperature > 0,
 // top-k off or above 64, with or without top-p.  bins is the wave's LDS
 // histogram of kWin counts.
-__device__ __attribute__((always_inline)) inline void row_profile(
+__device__ __attribute__((always_inline)) inline bool row_profile(
     const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
   const int lane = __lane_id();
   const bool top_p = smp.top_p_milli < 1000;
@@ -202,13 +202,8 @@ __device__ __attribute__((always_inline)) inline void row_profile(
   double z = L.vt == -__builtin_huge_valf() ? L.s : L.s * exp2((double)L.q - ref);
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
-  if (__ballot(L.ovf)) {  // logits beyond binary32 exponent range: the generic kernel
-    if (lane == 0) {
-      RowRec fb{};
-      fb.status = kRowFallback;
-      *rec = fb;
-    }
-    return;
+  if (__ballot(L.ovf)) {  // logits beyond binary32 exponent range: handed back
+    return true;
   }
 
   RowRec rr{};
@@ -222,7 +217,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     rr.status = SV_S_BAD_LOGITS;
     rr.zsum = 1.0;
     if (lane == 0) *rec = rr;
-    return;
+    return false;
   }
   const double wx = x >= 0 ? weight64(xval, lmax, scale) : 0.0;
   if (!hist) {  // the support is every finite logit
@@ -231,7 +226,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     rr.zsum = z;
     if (x >= 0) rr.ptok = wx / z;
     if (lane == 0) *rec = rr;
-    return;
+    return false;
   }
 
   // the window's counts: lane q holds the bins of keys anchor - kPerLane*q - e
@@ -258,12 +253,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     }
     const uint64_t hitk = __ballot(cincl >= K);
     if (!hitk) {  // fewer than K tokens in the window
-      if (lane == 0) {
-        RowRec fb{};
-        fb.status = kRowFallback;
-        *rec = fb;
-      }
-      return;
+      return true;
     }
     const int qk = __builtin_ctzll(hitk);
     uint32_t above = __shfl(cincl - tot, qk, kWave);  // tokens in the lanes before qk
@@ -304,12 +294,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     const double tgt = (double)smp.top_p_milli * zsum;
     const uint64_t hit = __ballot(1000.0 * incl >= tgt);
     if (!hit) {  // the cut lies below the window (never with top-k: C reaches Z_k)
-      if (lane == 0) {
-        RowRec fb{};
-        fb.status = kRowFallback;
-        *rec = fb;
-      }
-      return;
+      return true;
     }
     const int q = __builtin_ctzll(hit);
     double c_above = 0.0, wc = 0.0;
@@ -352,6 +337,7 @@ __device__ __attribute__((always_inline)) inline void row_profile(
     rr.ptok = member ? wx / zsum : 0.0;
   }
   if (lane == 0) *rec = rr;
+  return false;
 }
 
 }  // namespace dense

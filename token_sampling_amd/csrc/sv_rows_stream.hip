@@ -4,8 +4,10 @@
 //   top-k class (greedy, temperature 0, 1 <= top_k <= 64): topk::row_profile;
 //   dense class (temperature > 0, top-k off or above 64, with or without
 //     top-p): dense::row_profile.
-// Rows of other dtypes, and rows a path hands back, are left to the generic
-// kernel.  Each wave also takes its session's statuses that need no
+// A row a path hands back (a top-k region that overflows, a cut below the
+// dense histogram's window, logits beyond binary32 exponent range) is profiled
+// exactly by the same wave (sv_rows_exact.hpp).  fp32 rows are left to the
+// generic kernel.  Each wave also takes its session's statuses that need no
 // logits (SDCP Table 2, Sec. 6.3 step 5: limit, profile, q availability,
 // drafted tokens in range); the wave of a session's first row slot records
 // them for the kernels that follow.
@@ -17,6 +19,7 @@
 
 #include "sv_kernels.hpp"
 #include "sv_rows_dense.hpp"
+#include "sv_rows_exact.hpp"
 #include "sv_rows_topk.hpp"
 #include "sv_sdcp.hpp"
 
@@ -112,14 +115,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
   const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
                                   : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
   RowRec* rec = rows + (size_t)slot_g;
+  bool back;
   if (row_uses_topk_kernel(SV_BF16, rl, smp)) {
     const bool one_hot = rl == SV_RULE_GREEDY || smp.temperature_milli == 0;
     const int k = one_hot ? 1 : (int)smp.top_k;
     const size_t so = (size_t)slot_g * kSupMax;
-    topk::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
-  } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
+    back = topk::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
+  } else {
     if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
-    dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+    back = dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+  }
+  if (back) {  // the exact profile, by this wave
+    if (lane == 0) draw_flag[b] = draw_token;
+    exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
   }
 }
 
@@ -206,12 +214,9 @@ __global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_ST
       total += c;
     }
     ovf |= ovf_s[0];
-    if (ovf) {  // a part overflowed its region: the generic kernel takes the row
-      if (lane == 0) {
-        RowRec r{};
-        r.status = kRowFallback;
-        *rec = r;
-      }
+    if (ovf) {  // a part overflowed its region: the exact profile, by this wave
+      if (lane == 0) draw_flag[b] = draw_token;
+      exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
       return;
     }
     const size_t so = (size_t)slot_g * kSupMax;
@@ -221,7 +226,8 @@ __global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_ST
     // one wave, chosen by the slot, so that dense rows spread over the SIMDs
     if (wid == slot_g % S) {
       if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
-      dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+      if (dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds))
+        exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
     }
   }
 }

@@ -27,7 +27,7 @@
 // token must beat that key strictly (later tiles hold larger ids, which lose
 // ties).  A tile that would overflow the region even after a cut (at most 256
 // entries; adversarial rows such as ascending logits or tiny vocabularies) is
-// left to the generic kernel (status kRowFallback).
+// handed back: the caller profiles the row exactly (sv_rows_exact.hpp).
 #pragma once
 
 #include "sv_kernels.hpp"
@@ -220,7 +220,7 @@ struct WaveState {
   int n;            // region slots in use (even; empty entries are 0)
   int thr;          // candidates need key >= thr (or > thr when strict)
   bool strict;      // the threshold is the exact k-th best key of a cut
-  bool overflow;    // the row is left to the generic kernel
+  bool overflow;    // the row is handed back to the exact profile
   bool raw;         // raw mode (see the file comment)
   uint32_t magmax;  // largest |x| bit pattern seen in key mode, packed pair
   uint32_t umax;    // largest raw bit pattern seen in raw mode, packed pair
@@ -484,22 +484,15 @@ __device__ __attribute__((always_inline)) inline void chunk_scan(const uint16_t*
 // The profile of one row of the top-k class, by one wave: rows whose support
 // lies among the k <= 64 best tokens (k = 1 for one-hot profiles).  reg is
 // the wave's LDS region of kCap entries; sup_id, sup_p its listed support.
-__device__ __attribute__((always_inline)) inline void row_profile(
+__device__ __attribute__((always_inline)) inline bool row_profile(
     const uint16_t* row, int V, int k, bool one_hot, const sv_sampling& smp, int32_t x, RowRec* rec,
     int32_t* sup_id, double* sup_p, uint64_t* reg) {
-  const int lane = __lane_id();
   WaveState s;
   chunk_scan(row, V, k, 0, row_tiles(row, V), s, reg);
-  if (s.overflow) {
-    if (lane == 0) {
-      RowRec r{};
-      r.status = kRowFallback;
-      *rec = r;
-    }
-    return;
-  }
+  if (s.overflow) return true;  // handed back: the caller profiles it exactly
   row_finish(reg, s.n, k, s.magmax, s.umax, one_hot, smp.temperature_milli, smp.top_p_milli, x, rec,
              sup_id, sup_p);
+  return false;
 }
 
 }  // namespace topk

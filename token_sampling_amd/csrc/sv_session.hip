@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   const int c = (int)blockIdx.x - b * C;
   if (b >= B) return;
   const int t = threadIdx.x;
-  const int lane = t & (kWave - 1), wid = t / kWave;
+  const int wid = t / kWave;
   // only chunk 0 has work in sessions that draw no token from whole rows
   if (c > 0 && (draw_flag[b] != draw_token || rule[b] == SV_RULE_GREEDY || sess_status[b] != 0))
     return;
