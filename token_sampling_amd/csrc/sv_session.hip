@@ -346,8 +346,8 @@ struct Raw8<4> {
 // Elements y .. y+7 of a row (fill past V).  Vector loads where the row is
 // 16-byte aligned and the 8 elements lie inside it.
 template <class E>
-__device__ inline void load8(const E* row, int y, int V, bool vec, uint32_t fill,
-                             Raw8<sizeof(E)>& r) {
+__device__ __attribute__((always_inline)) void load8(const E* row, int y, int V, bool vec,
+                                                     uint32_t fill, Raw8<sizeof(E)>& r) {
   if (vec && y + kPer <= V) {
     const u32x4* p = (const u32x4*)(row + y);
     if constexpr (sizeof(E) == 2) r.v = p[0];
@@ -376,7 +376,7 @@ struct DrawCtx {
   const float* qrow;   // published q row (residual, kQ)
   bool qvec;
   int V;
-  __device__ void load(int y, bool resid, RawP& rp, RawQ& rq) const {
+  __device__ __attribute__((always_inline)) void load(int y, bool resid, RawP& rp, RawQ& rq) const {
     load8(P.row, y, V, P.vec, Tr::kNegInfBits, rp);
     if (resid) {
       if constexpr (kQ) load8((const uint32_t*)qrow, y, V, qvec, 0u, rq);
@@ -385,6 +385,21 @@ struct DrawCtx {
   }
 };
 
+// Exclusive prefix over the wave's lanes of a count in 0..15, and the wave
+// total, from one ballot per bit.
+__device__ inline uint32_t wave_excl_count(uint32_t c, uint32_t* total) {
+  uint32_t r = 0, t = 0;
+#pragma unroll
+  for (int bit = 0; bit < 4; ++bit) {
+    const uint64_t bm = __ballot((c >> bit) & 1u);
+    r += (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0)) << bit;
+    t += (uint32_t)__builtin_popcountll(bm) << bit;
+  }
+  *total = t;
+  return r;
+}
+
 // A group's weights with the ties of each cut both kept and left out (see
 // GroupRec), summed over one lane's ids.
 struct GroupAcc {
@@ -392,65 +407,126 @@ struct GroupAcc {
   uint32_t np, nq, npq, bad;
 };
 
+// One token's share of its group (see GroupAcc).  Selects rather than
+// branches per lane; the branches test ballots (one value for the whole
+// wave), so no lane masks are set up per token.
 template <class Tr, bool kQ>
-__device__ inline void weigh8(const DrawCtx<Tr, kQ>& d, bool resid, int y,
-                              const typename DrawCtx<Tr, kQ>::RawP& pr,
-                              const typename DrawCtx<Tr, kQ>::RawQ& qr, GroupAcc& s) {
-  // Selects rather than branches per lane; the branches below test ballots
-  // (one value for the whole wave), so no lane masks are set up per token.
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const uint32_t up = pr.get(e), kp = Tr::key(up);
-    const bool tp = d.P.tie(kp);
-    const bool mp = !tp && d.P.fixed_member(kp, y + e);
-    bool tq = false, mq = false;
-    const uint32_t uq = resid ? qr.get(e) : 0u;
-    if constexpr (!kQ) {
-      if (resid) {
-        const uint32_t kq = Tr::key(uq);
-        tq = d.Q.tie(kq);
-        mq = !tq && d.Q.fixed_member(kq, y + e);
-      }
-    }
-    // no member or tie of either row at this position in the whole wave: the
-    // tokens add nothing (most tokens of a truncated row)
-    if (!__builtin_amdgcn_ballot_w64(mp || tp || mq || tq)) continue;
-    double pv = 0.0;
-    if (__builtin_amdgcn_ballot_w64(mp)) {
-      const double w = d.P.w(Tr::value(up));
-      pv = mp ? w : 0.0;
-    }
-    if (!resid) {
-      s.a += pv;
-      s.np += tp ? 1u : 0u;
-      continue;
-    }
-    double qv = 0.0;
-    bool qbad = false;
-    if constexpr (kQ) {
-      qv = (double)__uint_as_float(uq);
-      qbad = !(qv >= 0.0 && qv < INFINITY);
-    } else if (__builtin_amdgcn_ballot_w64(mq)) {
-      const double w = d.Q.w(Tr::value(uq));
-      qv = mq ? w : 0.0;
-    }
-    const bool plain = !tp && !tq;
-    const double df = pv - qv;
-    s.a += (plain && pv > 0.0 && df > 0.0) ? df : 0.0;
-    s.ap += tp ? 0.0 : pv;
-    if (kQ && plain && pv > 0.0 && qbad) s.bad |= 1u;
-    if (__builtin_amdgcn_ballot_w64(tp || tq)) {  // ties: rows cut by rank only
-      const double dp = d.P.wcut - qv;   // a tie of p (not of q), kept
-      s.bp += (tp && !tq && d.P.wcut > 0.0 && dp > 0.0) ? dp : 0.0;
-      const double dq = pv - d.Q.wcut;   // a tie of q (not of p), kept
-      s.cq1 += (!tp && tq && pv > 0.0 && dq > 0.0) ? dq : 0.0;
-      s.cq0 += (!tp && tq) ? pv : 0.0;
-      s.np += tp ? 1u : 0u;
-      s.nq += tq ? 1u : 0u;
-      s.npq += (tp && tq) ? 1u : 0u;
-      if (kQ && tp && qbad) s.bad |= 2u;
+__device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                          uint32_t up, uint32_t uq, int y,
+                                                          GroupAcc s) {
+  const uint32_t kp = Tr::key(up);
+  const bool tp = d.P.tie(kp);
+  const bool mp = !tp && d.P.fixed_member(kp, y);
+  bool tq = false, mq = false;
+  if constexpr (!kQ) {
+    if (resid) {
+      const uint32_t kq = Tr::key(uq);
+      tq = d.Q.tie(kq);
+      mq = !tq && d.Q.fixed_member(kq, y);
     }
   }
+  // no member or tie of either row in the whole wave: nothing to add
+  if (!__builtin_amdgcn_ballot_w64(mp || tp || mq || tq)) return s;
+  double pv = 0.0;
+  if (__builtin_amdgcn_ballot_w64(mp)) {
+    const double w = d.P.w(Tr::value(up));
+    pv = mp ? w : 0.0;
+  }
+  if (!resid) {
+    s.a += pv;
+    s.np += tp ? 1u : 0u;
+    return s;
+  }
+  double qv = 0.0;
+  bool qbad = false;
+  if constexpr (kQ) {
+    qv = (double)__uint_as_float(uq);
+    qbad = !(qv >= 0.0 && qv < INFINITY);
+  } else if (__builtin_amdgcn_ballot_w64(mq)) {
+    const double w = d.Q.w(Tr::value(uq));
+    qv = mq ? w : 0.0;
+  }
+  const bool plain = !tp && !tq;
+  const double df = pv - qv;
+  s.a += (plain && pv > 0.0 && df > 0.0) ? df : 0.0;
+  s.ap += tp ? 0.0 : pv;
+  if (kQ && plain && pv > 0.0 && qbad) s.bad |= 1u;
+  if (__builtin_amdgcn_ballot_w64(tp || tq)) {  // ties: rows cut by rank only
+    const double dp = d.P.wcut - qv;   // a tie of p (not of q), kept
+    s.bp += (tp && !tq && d.P.wcut > 0.0 && dp > 0.0) ? dp : 0.0;
+    const double dq = pv - d.Q.wcut;   // a tie of q (not of p), kept
+    s.cq1 += (!tp && tq && pv > 0.0 && dq > 0.0) ? dq : 0.0;
+    s.cq0 += (!tp && tq) ? pv : 0.0;
+    s.np += tp ? 1u : 0u;
+    s.nq += tq ? 1u : 0u;
+    s.npq += (tp && tq) ? 1u : 0u;
+    if (kQ && tp && qbad) s.bad |= 2u;
+  }
+  return s;
+}
+
+// A lane's 8 ids of one step, in place: rows where most ids are members.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) void weigh8(const DrawCtx<Tr, kQ>& d, bool resid, int y,
+                                                      const typename DrawCtx<Tr, kQ>::RawP& pr,
+                                                      const typename DrawCtx<Tr, kQ>::RawQ& qr,
+                                                      GroupAcc& s) {
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) s = weigh1<Tr, kQ>(d, resid, pr.get(e), resid ? qr.get(e) : 0u, y + e, s);
+}
+
+// Which of a lane's 8 ids are at or above a row's cut key: only those can be
+// members or ties; the others add nothing.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) uint32_t need_bits(
+    const DrawCtx<Tr, kQ>& d, bool resid, const typename DrawCtx<Tr, kQ>::RawP& pr,
+    const typename DrawCtx<Tr, kQ>::RawQ& qr) {
+  uint32_t need = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    bool n = Tr::key(pr.get(e)) >= d.P.kcut;
+    if constexpr (!kQ)
+      if (resid) n |= Tr::key(qr.get(e)) >= d.Q.kcut;
+    need |= n ? 1u << e : 0u;
+  }
+  return need;
+}
+
+// The wave's 512 ids of one step, compacted: the ids that need weighing are
+// queued in LDS in id order and weighed 64 at a time, so that a position
+// whose lanes mostly hold non-members does not cost a full wave's binary64
+// work.  qu holds the wave's queue: p bits, q bits, ids.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
+    const DrawCtx<Tr, kQ>& d, bool resid, int y, const typename DrawCtx<Tr, kQ>::RawP& pr,
+    const typename DrawCtx<Tr, kQ>::RawQ& qr, GroupAcc s, uint32_t* qu) {
+  const int lane = __lane_id();
+  const uint32_t need = need_bits<Tr, kQ>(d, resid, pr, qr);
+  uint32_t total;
+  uint32_t j = wave_excl_count(__builtin_popcount(need), &total);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if ((need >> e) & 1u) {
+      qu[j] = pr.get(e);
+      qu[kWStep + j] = resid ? qr.get(e) : 0u;
+      qu[2 * kWStep + j] = (uint32_t)(y + e);
+      ++j;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (uint32_t r = 0; r < total; r += kWave) {
+    const uint32_t i = r + (uint32_t)lane;
+    const bool valid = i < total;
+    // past the queue: -inf bits, neither a member nor a tie of either row
+    const uint32_t up = valid ? qu[i] : Tr::kNegInfBits;
+    const uint32_t uq = valid ? qu[kWStep + i] : (kQ ? 0u : Tr::kNegInfBits);
+    const int yy = valid ? (int)qu[2 * kWStep + i] : 0;
+    s = weigh1<Tr, kQ>(d, resid, up, uq, yy, s);
+  }
+  __builtin_amdgcn_wave_barrier();
+  return s;
 }
 
 // Group records cross workgroups as six 64-bit words in device-scope atomics
@@ -486,11 +562,17 @@ __device__ inline GroupAcc load_group(const GroupRec* rec) {
 }
 
 // One wave records groups [g0, g1): steps of 8 ids per lane through a ring of
-// kSteps loads, three steps ahead.
-template <class Tr, bool kQ>
-__device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid, int g0, int g1,
-                              GroupRec* __restrict__ recs) {
-  if (g0 >= g1) return;
+// kSteps loads, three steps ahead.  For a row cut to a support, the wave
+// weighs queued ids when its first step has 16 to 128 ids to weigh, else in
+// place (a queue of more rounds measured slower: the 8 unrolled positions
+// overlap their binary64 chains; with fewer, in place skips the empty
+// positions anyway).  The two loops are kept apart so that each has its own
+// registers.
+template <class Tr, bool kQ, bool kQueued>
+__device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                           int g0, int g1,
+                                                           GroupRec* __restrict__ recs,
+                                                           uint32_t* qu) {
   const int lane = __lane_id();
   const int nk = (g1 - g0) * kSteps;
   const int ybase = g0 * kGroup + lane * kPer;
@@ -505,7 +587,8 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
     for (int u = 0; u < kSteps; ++u) {
       const int kk = k + u;
       if (kk + 3 < nk) d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
-      weigh8<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s);
+      if constexpr (kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s, qu);
+      else weigh8<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s);
     }
     s.a = wave_reduce(s.a, OpAdd());
     s.bp = wave_reduce(s.bp, OpAdd());
@@ -520,19 +603,23 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
   }
 }
 
-// Exclusive prefix over the wave's lanes of a count in 0..15, and the wave
-// total, from one ballot per bit.
-__device__ inline uint32_t wave_excl_count(uint32_t c, uint32_t* total) {
-  uint32_t r = 0, t = 0;
-#pragma unroll
-  for (int bit = 0; bit < 4; ++bit) {
-    const uint64_t bm = __ballot((c >> bit) & 1u);
-    r += (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
-                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0)) << bit;
-    t += (uint32_t)__builtin_popcountll(bm) << bit;
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                             int g0, int g1, bool sparse,
+                                                             GroupRec* __restrict__ recs,
+                                                             uint32_t* qu) {
+  if (g0 >= g1) return;
+  bool queued = false;
+  if (sparse) {  // the first step's ids to weigh, over the wave
+    typename DrawCtx<Tr, kQ>::RawP p0;
+    typename DrawCtx<Tr, kQ>::RawQ q0;
+    d.load(g0 * kGroup + __lane_id() * kPer, resid, p0, q0);
+    uint32_t total;
+    (void)wave_excl_count(__builtin_popcount(need_bits<Tr, kQ>(d, resid, p0, q0)), &total);
+    queued = total >= 16 && total <= 2 * kWave;
   }
-  *total = t;
-  return r;
+  if (queued) record_loop<Tr, kQ, true>(d, resid, g0, g1, recs, qu);
+  else record_loop<Tr, kQ, false>(d, resid, g0, g1, recs, qu);
 }
 
 // A group's weight from its record: the ties of p kept (sp = 1), left out
@@ -551,7 +638,10 @@ __device__ inline double group_mass(const GroupAcc& r, bool resid, int sp, int s
 constexpr int kLdsGroups = 512;  // group records staged in LDS for the pick
 
 struct DrawSmem {
-  uint64_t grec[kLdsGroups][6];
+  union {
+    uint64_t grec[kLdsGroups][6];             // the pick: staged group records
+    uint32_t queue[kDrawWaves][3 * kWStep];  // the records: each wave's queue
+  };
   double tab_p[kTab];
   double tab_q[kTab];
   double dscan[kDrawWaves];
@@ -783,7 +873,10 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   GroupRec* recs = groups + (size_t)b * G;
   {
     const int g0 = (4 * c + wid) * gw;
-    record_groups<Tr, kQ>(d, resid, min(g0, G), min(g0 + gw, G), recs);
+    // rows cut to a support (top-k, top-p) weigh their members only;
+    // untruncated rows, where every id is a member, weigh in place
+    const bool sparse = !(d.P.kcut == Tr::kNegInfKey + 1 && d.P.idcut >= 0);
+    record_groups<Tr, kQ>(d, resid, min(g0, G), min(g0 + gw, G), sparse, recs, sm.queue[wid]);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's records are stored
   __syncthreads();
