@@ -35,11 +35,12 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "stream-v3"
+KERNEL_REVISION = "stream-v4"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
     ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
     ("b256_topk_topp", "k_rows_stream", "stream-v3"): 1_119_487_488,
+    ("b256_topk_topp", "k_rows_stream", "stream-v4"): 1_119_499_072,
 }
 
 
@@ -174,7 +175,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
-    row_ev = [(sv.HipEvent(), sv.HipEvent(), sv.HipEvent()) for _ in range(args.steps)]
+    # bf16 rows are all taken by the single-pass kernel: two events bracket it;
+    # fp32 rows go to the generic kernel: a third event between the two
+    bf16 = w.target.dtype == torch.bfloat16
+    row_ev = [tuple(sv.HipEvent() for _ in range(2 if bf16 else 3)) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -185,8 +189,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
-    stream_ms = sum(a.elapsed_ms(b) for a, b, _ in row_ev) / args.steps
-    generic_ms = sum(b.elapsed_ms(c) for _, b, c in row_ev) / args.steps
+    stream_ms = sum(e[0].elapsed_ms(e[1]) for e in row_ev) / args.steps
+    generic_ms = 0.0 if bf16 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, single-pass row kernel "
         f"{stream_ms:.4f} ms, generic row kernel {generic_ms:.4f} ms")
 
