@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
       const typename Tr::elem_t* row =
           is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
                     : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
-      exact::profile_row<Tr, kNT>(row, V, sampling[b], rule[b] == SV_RULE_GREEDY, x, rows + sg, &sm);
+      exact::profile_row<Tr, kNT>(row, V, sampling[b], rule[b] == SV_RULE_GREEDY, x, rows + sg,
+                                  &sm);
     }
   }
 }

@@ -78,7 +78,8 @@ constexpr int kLdsWords = (topk::kCap * 8 > dense::kWin * 4 ? topk::kCap * 8 : d
 #ifndef SV_STREAM_WAVES_PER_EU
 #define SV_STREAM_WAVES_PER_EU 5
 #endif
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
+__global__ __launch_bounds__(kWave)
+__attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM
 // 0 merges the S lists (at most S * 64 <= kCap entries) and finishes the row.
 // Dense-class rows are profiled by one wave of the workgroup alone.
 template <int S>
-__global__ __launch_bounds__(S * kWave) __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
+__global__ __launch_bounds__(S * kWave)
+__attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
@@ -258,7 +260,8 @@ static void launch_split(const LaunchArgs& a, hipStream_t st, size_t slots) {
   hipLaunchKernelGGL((k_rows_split<S>), dim3(grid), dim3(per_block), 0, st,
                      (const uint16_t*)a.target, (const uint16_t*)a.draft, a.dtype, a.tokens, a.m,
                      a.rule, a.sampling, (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B,
-                     a.M, a.V, a.sess_status, a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
+                     a.M, a.V, a.sess_status, a.draw_ctr, a.draw_flag, a.draw_token, a.rows,
+                     a.sup_id, a.sup_p, a.sdcp, a.unif,
                      n_value_blocks);
 }
 
@@ -271,7 +274,8 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
                      (const uint16_t*)a.draft, a.dtype, a.tokens, a.m, a.rule, a.sampling,
-                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V, a.sess_status,
+                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V,
+                     a.sess_status,
                      a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id,
                      a.sup_p, a.sdcp, a.unif, n_value_blocks);
 }

@@ -74,9 +74,9 @@ __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
 // per-session kernel's first wave writes these and the session's other
 // outputs with the same lane-to-address mapping, so a later failure
 // overwrites them in each lane's program order.
-__device__ __attribute__((always_inline)) void write_failed(int b, int st, int M, int32_t* __restrict__ accepted_len,
-                             int32_t* __restrict__ out_tokens, double* __restrict__ p_tok,
-                             double* __restrict__ q_tok) {
+__device__ __attribute__((always_inline)) void write_failed(
+    int b, int st, int M, int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+    double* __restrict__ p_tok, double* __restrict__ q_tok) {
   const int lane = threadIdx.x;
   int32_t* out = out_tokens + (size_t)b * (M + 1);
   if (lane == 0) accepted_len[b] = st;
@@ -104,16 +104,13 @@ struct Verdict {
 // draft row record exists.  Writes nothing.  A draw from listed supports is
 // taken here when listed is set; otherwise such a session only reports that
 // no chunked draw is left (job kind none).
-__device__ __attribute__((always_inline)) Verdict accept_session(int b, const int32_t* __restrict__ tokens,
-                                  const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
-                                  const sv_sampling* __restrict__ sampling, int M, int V,
-                                  const float* __restrict__ qrows, uint64_t seed, uint32_t round,
-                                  const int32_t* __restrict__ sess_status,
-                                  const RowRec* __restrict__ rows,
-                                  const int32_t* __restrict__ sup_id,
-                                  const double* __restrict__ sup_p,
-                                  const double* __restrict__ unif, bool listed, int32_t* q_id,
-                                  double* q_p) {
+__device__ __attribute__((always_inline)) Verdict accept_session(
+    int b, const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int M, int V,
+    const float* __restrict__ qrows, uint64_t seed, uint32_t round,
+    const int32_t* __restrict__ sess_status, const RowRec* __restrict__ rows,
+    const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p,
+    const double* __restrict__ unif, bool listed, int32_t* q_id, double* q_p) {
   const int lane = threadIdx.x;
   const int R = 2 * M + 1;
   Verdict v;
@@ -189,7 +186,9 @@ __device__ __attribute__((always_inline)) Verdict accept_session(int b, const in
     const double* uv = unif ? unif + (size_t)b * R : nullptr;
     double u_acc = 1.0, u_add = 0.0;
     if (uv) u_acc = lane < mb ? uv[lane] : 1.0;
-    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc, &u_add);
+    else
+      verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc,
+                        &u_add);
     const double ratio = px / qx;
     const bool acc = lane < mb && u_acc < (ratio < 1.0 ? ratio : 1.0);
     const uint64_t rej = ~(uint64_t)__ballot(acc);
@@ -222,9 +221,9 @@ __device__ __attribute__((always_inline)) Verdict accept_session(int b, const in
 }
 
 // A session's outputs from its verdict and additional token, by one wave.
-__device__ __attribute__((always_inline)) void write_verdict(int b, const Verdict& v, int32_t extra, int M,
-                              int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-                              double* __restrict__ p_tok, double* __restrict__ q_tok) {
+__device__ __attribute__((always_inline)) void write_verdict(
+    int b, const Verdict& v, int32_t extra, int M, int32_t* __restrict__ accepted_len,
+    int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok) {
   if (v.st < 0) {
     write_failed(b, v.st, M, accepted_len, out_tokens, p_tok, q_tok);
     return;
@@ -261,9 +260,9 @@ constexpr int kDrawWaves = kDrawNT / kWave;
 constexpr int kPer = 8;                      // consecutive ids per lane per step
 constexpr int kWStep = kWave * kPer;         // ids per wave step
 constexpr int kSteps = kGroup / kWStep;      // wave steps per group
-constexpr int kTabBits = 9;                // 2^(i / kTab) tabled per row
+constexpr int kTabBits = 9;                  // 2^(i / kTab) tabled per row
 constexpr int kTab = 1 << kTabBits;
-constexpr int kDeg = 4;                    // degree of the polynomial for 2^(f / kTab)
+constexpr int kDeg = 4;                      // degree of the polynomial for 2^(f / kTab)
 static_assert(kSteps == 4, "the load ring holds one group");
 
 // Weights in binary64 by Tang's table-driven method (P. T. P. Tang, "Table-
@@ -292,7 +291,7 @@ constexpr TaylorCoef kTaylor;
 template <class Tr>
 struct DrawRow {
   const typename Tr::elem_t* row;
-  const double* tab;  // tab[i] = 2^(i / 256) / Z
+  const double* tab;  // tab[i] = 2^(i / kTab) / Z
   double sk, ck;      // kTab * scale and kTab * scale * lmax (both exact)
   double wcut;        // p of each tie (tie mode)
   uint32_t kcut;
@@ -472,7 +471,8 @@ __device__ __attribute__((always_inline)) void weigh8(const DrawCtx<Tr, kQ>& d, 
                                                       const typename DrawCtx<Tr, kQ>::RawQ& qr,
                                                       GroupAcc& s) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) s = weigh1<Tr, kQ>(d, resid, pr.get(e), resid ? qr.get(e) : 0u, y + e, s);
+  for (int e = 0; e < kPer; ++e)
+    s = weigh1<Tr, kQ>(d, resid, pr.get(e), resid ? qr.get(e) : 0u, y + e, s);
 }
 
 // Which of a lane's 8 ids are at or above a row's cut key: only those can be
@@ -534,11 +534,13 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
 // wave stores word i of the wave-uniform sums.
 __device__ inline void store_group(GroupRec* rec, const GroupAcc& s) {
   const int lane = __lane_id();
-  const double dv = lane == 0 ? s.a : lane == 1 ? s.bp : lane == 2 ? s.cq1 : lane == 3 ? s.cq0 : s.ap;
+  const double dv =
+      lane == 0 ? s.a : lane == 1 ? s.bp : lane == 2 ? s.cq1 : lane == 3 ? s.cq0 : s.ap;
   uint64_t w = (uint64_t)__double_as_longlong(dv);
   if (lane == 5)
     w = (uint64_t)(s.np | (s.nq << 16)) | ((uint64_t)(s.npq | (s.bad << 16)) << 32);
-  if (lane < 6) __hip_atomic_store((uint64_t*)rec + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane < 6)
+    __hip_atomic_store((uint64_t*)rec + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline GroupAcc decode_group(const uint64_t (&w)[6]) {
   GroupAcc r;
@@ -586,9 +588,11 @@ __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int kk = k + u;
-      if (kk + 3 < nk) d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
-      if constexpr (kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s, qu);
-      else weigh8<Tr, kQ>(d, resid, ybase + kk * kWStep, p[u], q[u], s);
+      if (kk + 3 < nk)
+        d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
+      const int y = ybase + kk * kWStep;
+      if constexpr (kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, y, p[u], q[u], s, qu);
+      else weigh8<Tr, kQ>(d, resid, y, p[u], q[u], s);
     }
     s.a = wave_reduce(s.a, OpAdd());
     s.bp = wave_reduce(s.bp, OpAdd());
@@ -807,7 +811,8 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
 template <class Tr, bool kQ>
 __global__ __launch_bounds__(kDrawNT) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
-    const float* __restrict__ qrows, const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
+    const float* __restrict__ qrows, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int B, int M, int V,
     uint64_t seed, uint32_t round, const int32_t* __restrict__ sess_status,
     const RowRec* __restrict__ rows, int32_t* __restrict__ accepted_len,
@@ -840,7 +845,7 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
 
   const int R = 2 * M + 1;
   const int G = (V + kGroup - 1) / kGroup;
-  bool resid = job.kind == kJobResidual;
+  const bool resid = job.kind == kJobResidual;
   auto make_row = [&](const typename Tr::elem_t* row, const RowRec& r, double* tab) {
     DrawRow<Tr> D;
     D.row = row;
@@ -962,7 +967,8 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   }
   __syncthreads();
   // every group's weight (the ranked weights for the cut groups)
-  auto mass_of = [&](int g, const GroupAcc& r, uint32_t tp, uint32_t tq, bool rs, bool* badp) -> double {
+  auto mass_of = [&](int g, const GroupAcc& r, uint32_t tp, uint32_t tq, bool rs,
+                     bool* badp) -> double {
     const int sp = state(tp, r.np, jp), sq = rs ? state(tq, r.nq, jq) : 1;
     if (!rs) return (resid ? r.ap : r.a) + (double)kept(sp, tp, r.np, jp) * Pk;
     if (g == sm.sg[0] || g == sm.sg[1]) {
