@@ -111,6 +111,12 @@ def lib():
             ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp,
         ]
         L.ov_verify_qrows.restype = ctypes.c_int
+        L.ov_verify_early.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, i32p, i32p, i32p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_uint64, ctypes.c_uint32, i32p, i32p, dp, dp, dp, dp, dp, dp,
+        ]
+        L.ov_verify_early.restype = ctypes.c_int
         L.ov_commit.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i32p, i32p, i32p,
                                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, i32p, i32p]
         L.ov_commit.restype = ctypes.c_int
@@ -243,7 +249,7 @@ def make_sampling(B, temperature_milli=1000, top_k=0, top_p_milli=1000, session_
 
 
 def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=True,
-           sdcp_sessions=None, q_rows=None):
+           sdcp_sessions=None, q_rows=None, early=False):
     """Run the oracle over a batch.
 
     target: [B, M+1, V] uint16 (bf16 bits) or float32; draft: [B, M, V] of the
@@ -254,6 +260,10 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     SDCP's HMAC-SHA-256 values and seed, round_ are ignored.  With q_rows
     ([B, M, V] float32 probabilities, SDCP's q_rows) the draft distributions
     are those rows and draft must be None; d_topp_d is then not computed.
+    With early=True positions are examined in order and each row is read only
+    when its position is reached (``ov_verify_early``): a problem in a row
+    after the deciding position changes nothing, and the probes and
+    diagnostics hold values only up to that position.
     """
     target = np.ascontiguousarray(target)
     _, dt = _as_row(target[..., :1].reshape(-1)[:1]) if target.size else (None, BF16)
@@ -295,7 +305,12 @@ def verify(target, draft, tokens, m, rule, sampling, seed, round_, diagnostics=T
     sess = None
     if sdcp_sessions is not None:
         sess = np.ascontiguousarray(sdcp_sessions, dtype=SDCP_SESSION_DTYPE).reshape(B)
-    if q_rows is not None:
+    if early:
+        rc = lib().ov_verify_early(target.ctypes.data, common[1],
+                                   None if q_rows is None else q_rows.ctypes.data, *common[2:],
+                                   None if sess is None else sess.ctypes.data, B, M, V, seed,
+                                   round_, *outs)
+    elif q_rows is not None:
         no_d_topp_d = outs[:6] + outs[7:]
         rc = lib().ov_verify_qrows(target.ctypes.data, dt, q_rows.ctypes.data, *common[3:],
                                    None if sess is None else sess.ctypes.data, B, M, V, seed,

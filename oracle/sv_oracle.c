@@ -640,6 +640,116 @@ static int verify_session(int64_t b, const void *target, const void *draft, cons
 }
 
 /*
+ * The same session with positions examined in order, each row read only when
+ * its position is reached (textbook "The acceptance rule": the proposals are
+ * checked one after another and the first rejection ends the round).  This
+ * departs from verify_session, which follows SDCP Sec. 6.3 step 5 and checks
+ * every row and every q_i(x_i) before any decision.
+ * Position i reads target row i, and for rule 2 draft row i (or the published
+ * q_i(x_i)); a bad row there fails the session with BAD_LOGITS, then an
+ * unusable q_i(x_i) with BAD_PROPOSAL; then the position's test.  Rows after
+ * the deciding position are never read, so a problem there changes nothing.
+ * With every proposal accepted, row m+1 is read for the additional token.
+ * The session checks that read no logits (limit, profile, q availability,
+ * drafted tokens in range) come first, as in verify_session.  Where every
+ * row is usable and every q_i(x_i) positive, the verdict is verify_session's.
+ */
+static int verify_session_early(int64_t b, const void *target, const void *draft,
+                                const float *qrows, int dtype, const int32_t *x, int m, int rule,
+                                const ov_sampling *s, int M, int V, const ov_rng *g, int32_t *out,
+                                double *p_tok, double *q_tok, double *d_acc, double *d_topp_t,
+                                double *d_topp_d, double *d_cdf, ov_scratch *sc) {
+  if (m < 1 || m > M) return OV_S_LIMIT;
+  if ((rule != OV_RULE_GREEDY && rule != OV_RULE_SPECULATIVE && rule != OV_RULE_RELAXED) ||
+      s->reserved != 0 || s->top_p_milli > 1000)
+    return OV_S_BAD_PROFILE;
+  if (rule == OV_RULE_SPECULATIVE && draft == NULL && qrows == NULL) return OV_S_Q_UNAVAILABLE;
+  for (int i = 0; i < m; ++i)
+    if (x[i] < 0 || x[i] >= V) return OV_S_BAD_PROPOSAL;
+
+  const int64_t trow0 = b * (int64_t)(M + 1);
+  const int64_t drow0 = b * (int64_t)M;
+  for (int i = 1; i <= m; ++i) {
+    double dt;
+    load_row(target, dtype, trow0 + i - 1, V, sc->l);
+    if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
+    if (rule == OV_RULE_GREEDY) {
+      /* Rule 1 at position i: the additional token at a mismatch is argmax p_i */
+      const int y = row_argmax(sc->l, V);
+      out[i - 1] = y;
+      if (x[i - 1] != y) return i - 1;
+      continue;
+    }
+    profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+    set_if(d_topp_t, b * (int64_t)(M + 1) + i - 1, dt);
+    const double px = sc->p[x[i - 1]];
+    if (rule == OV_RULE_RELAXED) {
+      set_if(p_tok, b * (int64_t)M + i - 1, px);
+      if (px > 0.0) {
+        out[i - 1] = x[i - 1];
+        continue;
+      }
+      double dc;
+      out[i - 1] = inverse_cdf(sc->p, V, rng_uniform(g, (uint32_t)i, 1), &dc);
+      set_if(d_cdf, b, dc);
+      return i - 1;
+    }
+    /* Rule 2 at position i: q_i(x_i), checked before the position's test */
+    double qx;
+    if (qrows) {
+      qx = (double)qrows[(drow0 + i - 1) * (int64_t)V + x[i - 1]];
+    } else {
+      load_row(draft, dtype, drow0 + i - 1, V, sc->l);
+      if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
+      profile_row(sc->l, V, s, sc->q, &dt, sc->ent);
+      set_if(d_topp_d, b * (int64_t)M + i - 1, dt);
+      qx = sc->q[x[i - 1]];
+    }
+    set_if(q_tok, b * (int64_t)M + i - 1, qx);
+    set_if(p_tok, b * (int64_t)M + i - 1, px);
+    if (!(qx > 0.0) || isinf(qx)) return OV_S_BAD_PROPOSAL;
+    const double ratio = px / qx;
+    const double acc = ratio < 1.0 ? ratio : 1.0;
+    const double u = rng_uniform(g, (uint32_t)i, 0);
+    set_if(d_acc, b * (int64_t)M + i - 1, fabs(u - acc));
+    if (u < acc) {
+      out[i - 1] = x[i - 1];
+      continue;
+    }
+    if (qrows) {
+      /* the published residual row, read where p_i > 0 (as in verify_session) */
+      const float *qr = qrows + (drow0 + i - 1) * (int64_t)V;
+      for (int y = 0; y < V; ++y) {
+        if (sc->p[y] > 0.0) {
+          const double qy = (double)qr[y];
+          if (!(qy >= 0.0) || isinf(qy)) return OV_S_BAD_PROPOSAL;
+          sc->q[y] = qy;
+        } else {
+          sc->q[y] = 0.0;
+        }
+      }
+    }
+    double dc;
+    out[i - 1] = residual_pick(sc->p, sc->q, V, rng_uniform(g, (uint32_t)i, 1), sc->w, &dc);
+    set_if(d_cdf, b, dc);
+    return i - 1;
+  }
+  /* every proposal accepted: row m+1 gives the additional token */
+  double dt, dc;
+  load_row(target, dtype, trow0 + m, V, sc->l);
+  if (row_is_bad(sc->l, V)) return OV_S_BAD_LOGITS;
+  if (rule == OV_RULE_GREEDY) {
+    out[m] = row_argmax(sc->l, V);
+    return m;
+  }
+  profile_row(sc->l, V, s, sc->p, &dt, sc->ent);
+  set_if(d_topp_t, b * (int64_t)(M + 1) + m, dt);
+  out[m] = inverse_cdf(sc->p, V, rng_uniform(g, (uint32_t)(m + 1), 1), &dc);
+  set_if(d_cdf, b, dc);
+  return m;
+}
+
+/*
  * The batched step over B sessions (same layout as the GPU entry point):
  *   target   [B, M+1, V]  dtype (bf16 bits as uint16, or float32)
  *   draft    [B, M,   V]  dtype, or NULL
@@ -654,7 +764,7 @@ static int verify_batch(const void *target, const void *draft, const float *qrow
               const int32_t *tokens,
               const int32_t *m, const int32_t *rule, const ov_sampling *sampling, int64_t B,
               int M, int V, uint64_t seed, uint32_t round, const ov_sdcp_session *sdcp,
-              int32_t *accepted_len,
+              int early, int32_t *accepted_len,
               int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
               double *d_topp_t, double *d_topp_d, double *d_cdf) {
   if (!target || !tokens || !m || !rule || !sampling || !accepted_len || !out_tokens)
@@ -686,9 +796,9 @@ static int verify_batch(const void *target, const void *draft, const float *qrow
     set_if(d_cdf, b, INFINITY);
 
     const ov_rng g = {seed, sampling[b].session_key, round, sdcp ? &sdcp[b] : NULL};
-    int a = verify_session(b, target, draft, qrows, dtype, tokens + b * (int64_t)M, m[b], rule[b],
-                           &sampling[b], M, V, &g, out, p_tok, q_tok, d_acc, d_topp_t,
-                           d_topp_d, d_cdf, &sc);
+    int a = (early ? verify_session_early : verify_session)(
+        b, target, draft, qrows, dtype, tokens + b * (int64_t)M, m[b], rule[b], &sampling[b], M,
+        V, &g, out, p_tok, q_tok, d_acc, d_topp_t, d_topp_d, d_cdf, &sc);
     accepted_len[b] = a;
     if (a < 0) { /* a failed session emits nothing; its diagnostics are kept */
       for (int j = 0; j <= M; ++j) out[j] = -1;
@@ -708,7 +818,7 @@ int ov_verify(const void *target, const void *draft, int dtype, const int32_t *t
               int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
               double *d_topp_t, double *d_topp_d, double *d_cdf) {
   return verify_batch(target, draft, NULL, dtype, tokens, m, rule, sampling, B, M, V, seed, round,
-                      NULL, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
+                      NULL, 0, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
                       d_cdf);
 }
 
@@ -721,7 +831,7 @@ int ov_verify_sdcp(const void *target, const void *draft, int dtype, const int32
                    double *d_acc, double *d_topp_t, double *d_topp_d, double *d_cdf) {
   if (!sessions) return OV_ERR_ARG;
   return verify_batch(target, draft, NULL, dtype, tokens, m, rule, sampling, B, M, V, 0, 0,
-                      sessions, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
+                      sessions, 0, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, d_topp_d,
                       d_cdf);
 }
 
@@ -735,8 +845,24 @@ int ov_verify_qrows(const void *target, int dtype, const float *qrows, const int
                     uint32_t round, int32_t *accepted_len, int32_t *out_tokens, double *p_tok,
                     double *q_tok, double *d_acc, double *d_topp_t, double *d_cdf) {
   return verify_batch(target, NULL, qrows, dtype, tokens, m, rule, sampling, B, M, V, seed, round,
-                      sessions, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, NULL,
+                      sessions, 0, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t, NULL,
                       d_cdf);
+}
+
+/* The batched step with positions examined in order and each row read only
+ * when its position is reached (verify_session_early).  Draft distributions
+ * from draft logits (draft) or published q_rows (qrows), at most one of them;
+ * uniforms from SDCP Sec. 6.4 records (sessions) or Philox (seed, round). */
+int ov_verify_early(const void *target, const void *draft, const float *qrows, int dtype,
+                    const int32_t *tokens, const int32_t *m, const int32_t *rule,
+                    const ov_sampling *sampling, const ov_sdcp_session *sessions, int64_t B,
+                    int M, int V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+                    int32_t *out_tokens, double *p_tok, double *q_tok, double *d_acc,
+                    double *d_topp_t, double *d_topp_d, double *d_cdf) {
+  if (draft && qrows) return OV_ERR_ARG;
+  return verify_batch(target, draft, qrows, dtype, tokens, m, rule, sampling, B, M, V, seed,
+                      round, sessions, 1, accepted_len, out_tokens, p_tok, q_tok, d_acc, d_topp_t,
+                      d_topp_d, d_cdf);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -66,7 +66,8 @@ def run_gpu(h, probe=True, device="cuda"):
 def run_oracle(h, diagnostics=True):
     return oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
                          h["seed"], h["round"], diagnostics=diagnostics,
-                         sdcp_sessions=h.get("sdcp"), q_rows=h.get("q_rows"))
+                         sdcp_sessions=h.get("sdcp"), q_rows=h.get("q_rows"),
+                         early=h.get("early") is not None)
 
 
 def random_sdcp_sessions(B, rng):
