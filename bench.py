@@ -35,7 +35,7 @@ DEFAULT_WORKLOAD = "b256_topk_topp"
 # Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
 # by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "stream-v4"
+KERNEL_REVISION = "stream-v5"
 MEASURED_TRAFFIC = {
     # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
     ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--qrows", action="store_true",
                     help="time sv_verify_qrows: draft distributions as published binary32 rows "
                          "(the synthetic drafter's own distribution) instead of draft logits")
+    ap.add_argument("--early", type=int, default=None, metavar="W",
+                    help="time sv_verify_early: positions read in order, in windows of W, 2W, "
+                         "4W, ... positions, each only for the sessions still undecided")
     ap.add_argument("--commit", action="store_true",
                     help="add the commit step (sv_commit: truncation, digest chain, counters) "
                          "to every step, with per-session state carried across steps")
@@ -165,7 +168,7 @@ def main():
     def step(ev=None):
         sv.verify(w.target, draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
                   workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp,
-                  q_rows=q_rows)
+                  q_rows=q_rows, early=args.early)
         if args.commit:
             sv.commit(contracts, states, w.m, out["accepted_len"], out["out_tokens"],
                       stream=stream, out=cres)
@@ -176,9 +179,11 @@ def main():
     log(f"[bench] warmup done ({args.warmup} steps)")
 
     # bf16 rows are all taken by the single-pass kernel: two events bracket it;
-    # fp32 rows go to the generic kernel: a third event between the two
+    # fp32 rows go to the generic kernel: a third event between the two.  Read
+    # in order, two events bracket all the windows' row and advance kernels.
     bf16 = w.target.dtype == torch.bfloat16
-    row_ev = [tuple(sv.HipEvent() for _ in range(2 if bf16 else 3)) for _ in range(args.steps)]
+    n_ev = 2 if (bf16 or args.early) else 3
+    row_ev = [tuple(sv.HipEvent() for _ in range(n_ev)) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -190,7 +195,7 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
     stream_ms = sum(e[0].elapsed_ms(e[1]) for e in row_ev) / args.steps
-    generic_ms = 0.0 if bf16 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
+    generic_ms = 0.0 if n_ev == 2 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, single-pass row kernel "
         f"{stream_ms:.4f} ms, generic row kernel {generic_ms:.4f} ms")
 
@@ -199,6 +204,24 @@ def main():
     split = w.row_bytes_by_kernel(q_rows=args.qrows)
     kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
                           else ("k_rows_generic", generic_ms, split["generic"]))
+    a = out["accepted_len"].cpu()
+    if args.early:
+        # read in order, the rows a session needs are its first a+1 target rows
+        # and (rule 2 with draft logits) as many draft rows; failed sessions are
+        # counted as reading nothing
+        import numpy as np
+
+        an = a.numpy().astype(np.int64)
+        ok = an >= 0
+        e = an + 1
+        mm = w.m.cpu().numpy().astype(np.int64)
+        r2 = w.rule.cpu().numpy() == sv.RULE_SPECULATIVE
+        rows_needed = e[ok].sum()
+        if not args.qrows:
+            rows_needed += np.minimum(e, mm)[ok & r2].sum()
+        kname = "row kernels, all windows"
+        kms = stream_ms + generic_ms
+        kbytes = int(rows_needed) * V * w.target.element_size()
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -208,9 +231,8 @@ def main():
         del src, dst
         log("[bench] copy calibration: 3 x (1 GiB read + 1 GiB written)")
 
-    a = out["accepted_len"].cpu()
     achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = None if (args.sdcp or args.qrows) else \
+    traffic = None if (args.sdcp or args.qrows or args.early) else \
         MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
     result = {
         "metric": METRIC,
@@ -231,6 +253,7 @@ def main():
             "uniforms": "sdcp-hmac-sha256" if args.sdcp else "philox4x64-10",
             "draft": "q_rows fp32" if args.qrows else "logits",
             "commit_step": bool(args.commit),
+            "reading": f"in order, first window {args.early}" if args.early else "every row",
             "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(q_rows=args.qrows),
             "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),

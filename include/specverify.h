@@ -211,6 +211,40 @@ int sv_verify_qrows(const void *target_logits, int32_t dtype, const float *q_row
                     int32_t *out_tokens, void *workspace, size_t workspace_bytes,
                     const sv_probe *probe, void *stream);
 
+/*
+ * The acceptance step read in order (textbook "Inference: KV Cache, Batching,
+ * Speculative Decoding", "The acceptance rule": the proposals are checked one
+ * after another and the first rejection ends the round).  Position i reads
+ * target row i and, for rule 2, draft row i (or q_rows' q_i(x_i)); a
+ * session's rows after the position that ends its round are never read.  The
+ * rows are read in windows of positions: window0 positions first
+ * (1..window0), then 2 window0, 4 window0, ... (at most 128), the last one
+ * ending at M+1, each window only for the sessions still undecided; fewer
+ * windows cost fewer launches, smaller ones read fewer rows.
+ * Statuses follow the order: the first position (1-based i <= m[b] + 1)
+ * with a bad target or draft row fails the session with SV_S_BAD_LOGITS, one
+ * with an unusable q_i(x_i) with SV_S_BAD_PROPOSAL, and a rejection ends the
+ * round; problems in rows after that position are not seen.  This departs
+ * from sv_verify, which checks every row and every q_i(x_i) before any
+ * decision (SDCP Sec. 6.3 step 5); where every row of a session is usable and
+ * every q_i(x_i) positive, the two give the same result.  The probes hold
+ * p_i(x_i), q_i(x_i) for the positions up to the one ending the round, -1
+ * after it.
+ * draft_logits or q_rows (at most one of them, both DEVICE arrays laid out
+ * as for sv_verify and sv_verify_qrows) gives rule 2's draft distributions;
+ * sessions: SDCP value records as for sv_verify_sdcp, or NULL for the Philox
+ * values of (seed, round).  1 <= window0 <= 65.  Every other argument, output,
+ * status and return code is as for sv_verify; the workspace size is the same.
+ * Returns SV_ERR_ARG for window0 out of range or both draft sources given.
+ */
+int sv_verify_early(const void *target_logits, const void *draft_logits, const float *q_rows,
+                    int32_t dtype, const int32_t *draft_tokens, const int32_t *m,
+                    const int32_t *rule, const sv_sampling *sampling,
+                    const sv_sdcp_session *sessions, int32_t B, int32_t M, int32_t V,
+                    uint64_t seed, uint32_t round, int32_t window0, int32_t *accepted_len,
+                    int32_t *out_tokens, void *workspace, size_t workspace_bytes,
+                    const sv_probe *probe, void *stream);
+
 /* ---------------------------------------------------------------------------
  * The verifier's commit step (SDCP Sec. 4.2, Sec. 6.3 steps 6-8, Sec. 6.5).
  * ------------------------------------------------------------------------- */

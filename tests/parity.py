@@ -58,7 +58,8 @@ def run_gpu(h, probe=True, device="cuda"):
                     to_device(np.asarray(h["rule"], np.int32), device),
                     sampling_bytes(h["sampling"], device), h["seed"], h["round"], probe=probe,
                     sdcp_sessions=None if sess is None else sdcp_bytes(sess, device),
-                    q_rows=None if q is None else to_device(np.asarray(q, np.float32), device))
+                    q_rows=None if q is None else to_device(np.asarray(q, np.float32), device),
+                    early=h.get("early"))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 

@@ -1,0 +1,169 @@
+"""GPU parity of the in-order reading (sv_verify_early): a session's positions
+are examined one after another and its rows after the position that ends its
+round are never read (textbook "The acceptance rule"); the library reads the
+rows in windows of positions, each window only for the sessions still
+undecided.  The oracle's in-order reading (ov_verify_early) is the reference.
+
+Cases: mixed profiles and rules in both dtypes with several first windows;
+NaN rows after the deciding position (never read) and at or before it
+(BAD_LOGITS); SDCP values and published q rows; m = 64 sessions that accept
+every position (the additional token's row is position 65); the workloads in
+full or, at full size, the same result as sv_verify for every session whose
+rows are all usable and the oracle on sampled sessions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import parity
+from tests.test_gpu_parity import mixed_case
+from token_sampling_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_sampling_amd as sv
+    sv.lib()
+    yield
+
+
+def set_nan(arr, idx):
+    if arr.dtype == np.uint16:
+        arr[idx] = BF16_NAN
+    else:
+        arr[idx] = np.nan
+
+
+@pytest.mark.parametrize("window", [1, 2, 5])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_mixed_profiles_in_order(dtype, window):
+    parity.log(f"[case] in-order mixed dtype={dtype} window={window}")
+    h = mixed_case(61, 28, 6, 2500, dtype)
+    h["early"] = window
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-mixed-{dtype}-{window}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_rows_after_the_end_are_not_read(dtype):
+    """NaN in every row after each session's deciding position: the in-order
+    result is the oracle's on the clean rows; NaN in a row at or before it
+    fails the session."""
+    parity.log(f"[case] in-order NaN rows dtype={dtype}")
+    h = mixed_case(62, 30, 7, 3000, dtype)
+    clean = parity.run_oracle(h)
+    a = clean["accepted_len"]
+    rng = np.random.default_rng(9)
+    c = dict(h)
+    c["target"], c["draft"] = h["target"].copy(), h["draft"].copy()
+    before = []
+    for b in range(len(a)):
+        if a[b] < 0:
+            continue
+        e = int(a[b]) + 1  # 1-based deciding position
+        set_nan(c["target"], (b, slice(e, None)))
+        set_nan(c["draft"], (b, slice(e, None)))
+        if b % 4 == 1:  # a NaN at or before the deciding position
+            j = int(rng.integers(1, e + 1))
+            set_nan(c["target"], (b, j - 1, int(rng.integers(0, c["target"].shape[2]))))
+            before.append(b)
+    c["early"] = 1
+    o = parity.run_oracle(c)
+    for b in range(len(a)):
+        if a[b] >= 0 and b not in before:
+            assert o["accepted_len"][b] == a[b] and np.array_equal(o["out_tokens"][b],
+                                                                  clean["out_tokens"][b])
+    assert all(o["accepted_len"][b] == oracle.S_BAD_LOGITS for b in before) and before
+    for window in (1, 3):
+        c["early"] = window
+        parity.compare(parity.run_gpu(c), o, f"early-nan-{dtype}-{window}")
+
+
+@pytest.mark.parametrize("window", [1, 4])
+def test_sdcp_values_and_q_rows_in_order(window):
+    parity.log(f"[case] in-order SDCP values and q rows window={window}")
+    h = mixed_case(63, 24, 5, 4000)
+    rng = np.random.default_rng(10)
+    h["sdcp"] = parity.random_sdcp_sessions(24, rng)
+    h["early"] = window
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-sdcp-{window}")
+    d = oracle.bf16_to_float(h["draft"]).astype(np.float64)
+    q = np.exp(d - d.max(axis=-1, keepdims=True))
+    q /= q.sum(axis=-1, keepdims=True)
+    h["q_rows"] = q.astype(np.float32)
+    h["draft"] = None
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-qrows-{window}")
+
+
+def test_every_position_accepted_at_m_64():
+    """m = 64 with the draft equal to the target: every proposal is accepted
+    and the additional token comes from row 65; a NaN there fails the
+    session, a NaN in row 64 of a session rejecting earlier does not."""
+    parity.log("[case] in-order m=64 full acceptance")
+    B, M, V = 6, 64, 300
+    rng = np.random.default_rng(12)
+    t = rng.normal(0, 1, size=(B, M + 1, V)).astype(np.float32)
+    d = t[:, :M].copy()
+    d[4] += rng.normal(0, 3, size=(M, V)).astype(np.float32)  # rejects early
+    h = dict(target=oracle.bf16_bits(t), draft=oracle.bf16_bits(d),
+             tokens=np.zeros((B, M), np.int32), m=np.full(B, M, np.int32),
+             rule=np.array([2, 2, 1, 192, 2, 2], np.int32),
+             sampling=oracle.make_sampling(B, 1000, 0, 1000), seed=3, round=4)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    o = parity.run_oracle(h)
+    assert (o["accepted_len"][[0, 1, 5]] == M).all()
+    set_nan(h["target"], (1, M, 7))                      # row 65 of a full acceptance
+    set_nan(h["target"], (4, M - 1, 3))                  # row 64 of an early rejection
+    h["early"] = 1
+    o = parity.run_oracle(h)
+    assert o["accepted_len"][1] == oracle.S_BAD_LOGITS
+    assert 0 <= o["accepted_len"][4] < M - 1
+    for window in (1, 65):
+        h["early"] = window
+        parity.compare(parity.run_gpu(h), o, f"early-m64-{window}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "b64"])
+def test_workload_in_order_in_full(name):
+    parity.log(f"[case] in-order workload {name} (all sessions)")
+    h = W.to_numpy(W.make(name, device="cuda"))
+    h["early"] = 1
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-{name}")
+
+
+@pytest.mark.parametrize("name,sessions", [("b256_topk_topp", (0, 77, 255)),
+                                           ("ragged", (3, 200, 511)),
+                                           ("large", (0, 1023))])
+def test_workload_full_size_in_order(name, sessions):
+    """At full size: every session whose SDCP reading succeeds gets the same
+    result in order (rows are all usable there), a bad proposal either stays
+    one or is not reached; sampled sessions against the oracle."""
+    parity.log(f"[case] in-order workload {name} full size, oracle on sessions {sessions}")
+    import token_sampling_amd as sv
+    w = W.make(name, device="cuda")
+    args = (w.target, w.draft, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"), w.seed, w.round)
+    full = {k: v.cpu().numpy() for k, v in sv.verify(*args).items()}
+    out = sv.verify(*args, probe=True, early=1)
+    torch.cuda.synchronize()
+    g_all = {k: v.cpu().numpy() for k, v in out.items()}
+    a_full, a = full["accepted_len"], g_all["accepted_len"]
+    ok = a_full >= 0
+    assert np.array_equal(a[ok], a_full[ok])
+    assert np.array_equal(g_all["out_tokens"][ok], full["out_tokens"][ok])
+    assert np.all((a_full[~ok] == oracle.S_BAD_PROPOSAL) & ((a[~ok] == oracle.S_BAD_PROPOSAL)
+                                                           | (a[~ok] >= 0)))
+    idx = np.array(sessions)
+    sub = W.to_numpy(w, sessions=torch.as_tensor(idx, device="cuda"))
+    del w, out, args
+    torch.cuda.empty_cache()
+    sub["early"] = 1
+    o = parity.run_oracle(sub)
+    parity.compare({k: v[idx] for k, v in g_all.items()}, o, f"early-{name}-sampled")
+    parity.log(f"[workload] {name} in order: mean accepted {a[a >= 0].mean():.3f}, "
+               f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")

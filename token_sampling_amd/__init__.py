@@ -61,7 +61,8 @@ STATE_DTYPE = np.dtype(
      ("j", "<u4"), ("reserved", "<u4", (3,))],
     align=True,
 )
-EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_commit",
+EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows",
+            "sv_verify_early", "sv_commit",
             "sv_prefix_digest", "sv_contract_digest", "sv_strerror", "sv_status_str",
             "sv_version")
 
@@ -145,6 +146,14 @@ def lib():
             ctypes.POINTER(_Probe), ctypes.c_void_p,
         ]
         L.sv_verify_qrows.restype = ctypes.c_int
+        L.sv_verify_early.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify_early.restype = ctypes.c_int
         L.sv_commit.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_int32,
                                                          ctypes.c_void_p, ctypes.c_void_p,
                                                          ctypes.c_void_p]
@@ -319,9 +328,9 @@ def _check(t, name, dtype, shape, device):
 
 def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, probe: bool = False,
            workspace=None, out=None, stream=None, row_events=None, sdcp_sessions=None,
-           q_rows=None):
-    """sv_verify, sv_verify_sdcp or sv_verify_qrows on torch tensors (all on one
-    GPU device).
+           q_rows=None, early=None):
+    """sv_verify, sv_verify_sdcp, sv_verify_qrows or sv_verify_early on torch
+    tensors (all on one GPU device).
 
     target [B, M+1, V] bf16/fp32, draft [B, M, V] same dtype or None, tokens
     [B, M] int32, m [B] int32, rule [B] int32, sampling [B, 24] uint8 (see
@@ -334,6 +343,9 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
         then the SDCP Sec. 6.4 values are used and seed, round_ are ignored.
     q_rows: optional [B, M, V] float32 draft distributions (SDCP q_rows) in place
         of draft logits (draft must then be None): sv_verify_qrows.
+    early: the first window (1..65 positions) of the in-order reading,
+        sv_verify_early (with either draft source and either value source); None:
+        every row is read.
     """
     import torch
 
@@ -401,7 +413,12 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
             stream.cuda_stream)
     sess = None if sdcp_sessions is None else sdcp_sessions.data_ptr()
-    if q_rows is not None:
+    if early is not None:
+        name = "sv_verify_early"
+        rc = lib().sv_verify_early(target.data_ptr(), common[1],
+                                   None if q_rows is None else q_rows.data_ptr(), dt,
+                                   *common[3:], sess, B, M, V, seed, round_, int(early), *tail)
+    elif q_rows is not None:
         name = "sv_verify_qrows"
         rc = lib().sv_verify_qrows(target.data_ptr(), dt, q_rows.data_ptr(), *common[3:], sess,
                                    B, M, V, seed, round_, *tail)

@@ -6,6 +6,8 @@
 //   the dense path) -> generic row kernel (every other row) -> finalize
 //   (acceptance, and the additional token's draw).
 // With SDCP values the single-pass kernel's first workgroups also compute them.
+// sv_verify_early enqueues the row kernels once per window of positions, each
+// followed by the advance kernel, and the finalize after the last window.
 // Neither call synchronises or allocates.
 #include <limits.h>
 
@@ -37,6 +39,8 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
   L.flag_off = off;
   off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
+  L.decided_off = off;
+  off = align_up(off + (size_t)B * sizeof(int32_t), 256);
   L.total = off;
   return L;
 }
@@ -73,14 +77,19 @@ static uint32_t next_draw_token() {
   return t;
 }
 
-// Shared by both entry points: sdcp == null takes the Philox values from
+// Shared by the entry points: sdcp == null takes the Philox values from
 // (seed, round); otherwise the SDCP Sec. 6.4 values of each session's record.
+// window0 == 0 reads every row of a session (the SDCP reading); window0 >= 1
+// reads them in order, in windows of window0, 2 window0, 4 window0, ...
+// positions, each window only for the sessions its predecessors left
+// undecided.
 static int verify_impl(const void* target_logits, const void* draft_logits, const float* q_rows,
                        int32_t dtype, const int32_t* draft_tokens, const int32_t* m, const int32_t* rule,
                        const sv_sampling* sampling, const sv_sdcp_session* sdcp, int32_t B,
                        int32_t M, int32_t V, uint64_t seed, uint32_t round,
                        int32_t* accepted_len, int32_t* out_tokens, void* workspace,
-                       size_t workspace_bytes, const sv_probe* probe, void* stream) {
+                       size_t workspace_bytes, const sv_probe* probe, void* stream,
+                       int32_t window0 = 0) {
   if (!target_logits || !draft_tokens || !m || !rule || !sampling || !accepted_len ||
       !out_tokens || !workspace)
     return SV_ERR_ARG;
@@ -120,13 +129,32 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   a.draw_gw = dc.gw;
   a.draw_flag = (uint32_t*)(ws + L.flag_off);
   a.draw_token = next_draw_token();
+  a.decided = window0 > 0 ? (int32_t*)(ws + L.decided_off) : nullptr;
+  a.win_lo = 1;
+  a.win_w = 0;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
   if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
-  launch_rows_stream(a, st);
-  if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
-  launch_rows_generic(a, st);
+  if (window0 == 0) {
+    launch_rows_stream(a, st);
+    if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
+    launch_rows_generic(a, st);
+  } else {
+    // windows of positions [lo, lo + w), w doubling, the last one ending at M+1
+    int w = window0;
+    for (int lo = 1; lo <= M + 1;) {
+      a.win_lo = lo;
+      a.win_w = w < M + 2 - lo ? w : M + 2 - lo;
+      launch_rows_stream(a, st);
+      launch_rows_generic(a, st);
+      const int hi = lo + a.win_w - 1;
+      if (hi < M + 1) launch_advance(a, st, hi);  // after the last window: the finalize
+      lo = hi + 1;
+      w = w < 64 ? 2 * w : w;
+    }
+    if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
+  }
   if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
   launch_finalize(a, st);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
@@ -167,6 +195,20 @@ extern "C" int sv_verify_qrows(const void* target_logits, int32_t dtype, const f
   return sv::verify_impl(target_logits, nullptr, q_rows, dtype, draft_tokens, m, rule, sampling,
                          sessions, B, M, V, seed, round, accepted_len, out_tokens, workspace,
                          workspace_bytes, probe, stream);
+}
+
+extern "C" int sv_verify_early(const void* target_logits, const void* draft_logits,
+                               const float* q_rows, int32_t dtype, const int32_t* draft_tokens,
+                               const int32_t* m, const int32_t* rule, const sv_sampling* sampling,
+                               const sv_sdcp_session* sessions, int32_t B, int32_t M, int32_t V,
+                               uint64_t seed, uint32_t round, int32_t window0,
+                               int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                               size_t workspace_bytes, const sv_probe* probe, void* stream) {
+  if (window0 < 1 || window0 > SV_M_MAX + 1) return SV_ERR_ARG;
+  if (draft_logits && q_rows) return SV_ERR_ARG;
+  return sv::verify_impl(target_logits, draft_logits, q_rows, dtype, draft_tokens, m, rule,
+                         sampling, sessions, B, M, V, seed, round, accepted_len, out_tokens,
+                         workspace, workspace_bytes, probe, stream, window0);
 }
 
 extern "C" const char* sv_strerror(int code) {

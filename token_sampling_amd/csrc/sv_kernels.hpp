@@ -43,6 +43,13 @@ struct LaunchArgs {
   // token costs them an acceptance pass, nothing more.
   uint32_t* draw_flag;  // [B]
   uint32_t draw_token;
+  // In-order reading (null decided: every row of a session is read).  The
+  // row kernels then read the positions win_lo .. win_lo + win_w - 1 of the
+  // sessions still undecided; decided[b] is the position (1-based) at which
+  // session b's round ends, 0 while undecided (cleared by the row kernels'
+  // first window).
+  int32_t* decided;  // [B]
+  int32_t win_lo, win_w;
 };
 
 // Ids per group record of the draw.
@@ -107,13 +114,30 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
 }
 
 struct WorkspaceLayout {
-  size_t rows_off, status_off, supid_off, supp_off, unif_off, chunk_off, ctr_off, flag_off, total;
+  size_t rows_off, status_off, supid_off, supp_off, unif_off, chunk_off, ctr_off, flag_off,
+      decided_off, total;
 };
+
+// Row slot g of the launch: every slot of every session (win_w == 0), or the
+// positions win_lo .. win_lo + win_w - 1 of each session, its target rows then
+// its draft rows.  Returns the slot in the [B, 2M+1] record array, or -1 for
+// a draft position past M.
+__device__ inline int launch_slot(int g, int M, int win_lo, int win_w) {
+  if (win_w == 0) return g;
+  const int per = 2 * win_w;
+  const int b = g / per;
+  const int k = g - b * per;
+  const bool is_target = k < win_w;
+  const int i = win_lo + (is_target ? k : k - win_w);  // 1-based position
+  if (!is_target && i > M) return -1;
+  return b * (2 * M + 1) + (is_target ? i - 1 : M + i);
+}
 
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
 
 void launch_rows_stream(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
+void launch_advance(const LaunchArgs& a, hipStream_t st, int hi);
 
 }  // namespace sv

@@ -16,10 +16,13 @@ constexpr int kNT = 256;
 
 // Does row slot slot_g need this kernel?  Rows of the other row kernels only
 // when they handed the row back.
+// With in-order reading (decided != null) only the window's positions of the
+// sessions still undecided.
 template <class Tr>
 __device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
                             const sv_sampling* sampling, const int32_t* sess_status, int M, int V,
-                            const RowRec* rows, bool draft_logits) {
+                            const RowRec* rows, bool draft_logits, const int32_t* decided,
+                            int win_lo, int win_w) {
   const int R = 2 * M + 1;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
@@ -28,6 +31,8 @@ __device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
   const int rl = rule[b];
   const bool is_target = slot <= M;
   const int i = is_target ? slot + 1 : slot - M;  // 1-based position
+  if (decided && (i < win_lo || i >= win_lo + win_w || (win_lo > 1 && decided[b] != 0)))
+    return false;
   // draft rows are profiled only when draft logits are given (not with q rows)
   if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb || !draft_logits))
     return false;
@@ -48,7 +53,8 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling,
     const int32_t* __restrict__ sess_status, int B, int M, int V, RowRec* __restrict__ rows,
-    uint32_t* __restrict__ draw_flag, uint32_t draw_token) {
+    uint32_t* __restrict__ draw_flag, uint32_t draw_token, const int32_t* __restrict__ decided,
+    int win_lo, int win_w) {
   __shared__ exact::Smem<kNT> sm;
   __shared__ int32_t todo[kNT];
   __shared__ int32_t wave_cnt[kNT / kWave];
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(kNT) void k_rows_generic(
     const int slot_g = base + (int)threadIdx.x;
     const bool need = slot_g < end &&
                       generic_row<Tr>(slot_g, m, rule, sampling, sess_status, M, V, rows,
-                                      draft != nullptr);
+                                      draft != nullptr, decided, win_lo, win_w);
     if (need) draw_flag[slot_g / R] = draw_token;  // a row without a listed support
     const uint64_t mask = __ballot(need);
     __syncthreads();  // the previous round's list is consumed
@@ -107,7 +113,7 @@ void launch_rows_generic(const LaunchArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_rows_generic<F32>, dim3(grid), dim3(kNT), 0, st,
                        (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
                        a.sampling, a.sess_status, a.B, a.M, a.V, a.rows, a.draw_flag,
-                       a.draw_token);
+                       a.draw_token, a.decided, a.win_lo, a.win_w);
   }
 }
 

@@ -86,7 +86,8 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     int B, int M, int V, int32_t* __restrict__ sess_status, uint32_t* __restrict__ draw_ctr,
     uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
-    const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks) {
+    const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
+    int32_t* __restrict__ decided, int win_lo, int win_w) {
   __shared__ __align__(16) uint64_t lds[kLdsWords];  // top-k region or dense histogram
   const int lane = __lane_id();
   if ((int)blockIdx.x < n_value_blocks) {
@@ -94,14 +95,17 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     return;
   }
   const int R = 2 * M + 1;
-  const int slot_g = blockIdx.x - n_value_blocks;
+  const int slot_g = launch_slot((int)blockIdx.x - n_value_blocks, M, win_lo, win_w);
+  if (slot_g < 0) return;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
   if (b >= B) return;
+  if (win_lo > 1 && decided[b] != 0) return;  // decided by an earlier window
   const int st = session_status(b, tokens, m, rule, sampling, M, V, has_draft != 0);
   if (slot == 0 && lane == 0) {
     sess_status[b] = st;
     draw_ctr[b] = 0u;  // the draw's chunk counter, for the per-session kernel
+    if (decided) decided[b] = 0;
   }
   if (st != 0 || dtype != SV_BF16) return;
   const int mb = m[b];
@@ -149,7 +153,8 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
     int B, int M, int V, int32_t* __restrict__ sess_status, uint32_t* __restrict__ draw_ctr,
     uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
-    const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks) {
+    const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
+    int32_t* __restrict__ decided, int win_lo, int win_w) {
   static_assert(S * kSupMax <= topk::kCap, "the merged lists fit one region");
   constexpr int kWords = (S * topk::kCap > kLdsWords ? S * topk::kCap : kLdsWords);
   __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or the dense histogram
@@ -162,14 +167,17 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
     return;
   }
   const int R = 2 * M + 1;
-  const int slot_g = blockIdx.x - n_value_blocks;
+  const int slot_g = launch_slot((int)blockIdx.x - n_value_blocks, M, win_lo, win_w);
+  if (slot_g < 0) return;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
   if (b >= B) return;
+  if (win_lo > 1 && decided[b] != 0) return;  // decided by an earlier window
   const int st = session_status(b, tokens, m, rule, sampling, M, V, has_draft != 0);
   if (wid == 0 && slot == 0 && lane == 0) {
     sess_status[b] = st;
     draw_ctr[b] = 0u;
+    if (decided) decided[b] = 0;
   }
   if (st != 0 || dtype != SV_BF16) return;
   const int mb = m[b];
@@ -248,36 +256,49 @@ static int rows_split_factor(const LaunchArgs& a) {
     const int s = atoi(env);
     if (s == 1 || s == 2 || s == 4) return s;
   }
-  const size_t rows = (size_t)a.B * (a.M + 1) + (a.draft ? (size_t)a.B * a.M : 0);
+  const int W = a.win_w == 0 ? a.M + 1 : a.win_w;  // target positions per session
+  const size_t rows = (size_t)a.B * W + (a.draft ? (size_t)a.B * (W < a.M ? W : a.M) : 0);
   return rows < 1024 ? 4 : 1;
+}
+
+// Row slots of the launch (every slot, or a window's), and the SDCP values'
+// workgroups of per_block values each (all values, in the first launch only).
+static size_t launch_slots(const LaunchArgs& a) {
+  if (a.win_w == 0) return (size_t)a.B * (2 * a.M + 1);
+  return (size_t)a.B * 2 * a.win_w;
+}
+static int value_blocks(const LaunchArgs& a, int per_block) {
+  if (!a.sdcp || a.win_lo > 1) return 0;
+  const size_t values = (size_t)a.B * (2 * a.M + 1);
+  return (int)((values + per_block - 1) / per_block);
 }
 
 template <int S>
 static void launch_split(const LaunchArgs& a, hipStream_t st, size_t slots) {
   const int per_block = S * kWave;
-  const int n_value_blocks = a.sdcp ? (int)((slots + per_block - 1) / per_block) : 0;
+  const int n_value_blocks = value_blocks(a, per_block);
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL((k_rows_split<S>), dim3(grid), dim3(per_block), 0, st,
                      (const uint16_t*)a.target, (const uint16_t*)a.draft, a.dtype, a.tokens, a.m,
                      a.rule, a.sampling, (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B,
                      a.M, a.V, a.sess_status, a.draw_ctr, a.draw_flag, a.draw_token, a.rows,
-                     a.sup_id, a.sup_p, a.sdcp, a.unif,
-                     n_value_blocks);
+                     a.sup_id, a.sup_p, a.sdcp, a.unif, n_value_blocks, a.decided, a.win_lo,
+                     a.win_w);
 }
 
 void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
-  const size_t slots = (size_t)a.B * (2 * a.M + 1);
+  const size_t slots = launch_slots(a);
   const int split = rows_split_factor(a);
   if (split == 2) return launch_split<2>(a, st, slots);
   if (split == 4) return launch_split<4>(a, st, slots);
-  const int n_value_blocks = a.sdcp ? (int)((slots + kWave - 1) / kWave) : 0;
+  const int n_value_blocks = value_blocks(a, kWave);
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
                      (const uint16_t*)a.draft, a.dtype, a.tokens, a.m, a.rule, a.sampling,
                      (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V,
                      a.sess_status,
                      a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id,
-                     a.sup_p, a.sdcp, a.unif, n_value_blocks);
+                     a.sup_p, a.sdcp, a.unif, n_value_blocks, a.decided, a.win_lo, a.win_w);
 }
 
 }  // namespace sv

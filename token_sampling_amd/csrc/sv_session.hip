@@ -93,24 +93,84 @@ struct Verdict {
   int st;         // 0, or the session's failure status
   int a;          // accepted drafted tokens
   int rl, mb;     // rule, drafted tokens
+  int np;         // positions with probe values: mb, or fewer when read in order
   int32_t x;      // this lane's drafted token (-1 past m)
   double px, qx;  // this lane's p_i(x_i) and q_i(x_i)
   int32_t extra;  // the additional token, when already drawn
   Job job;        // the draw left to the chunked sampler (kJobNone: none)
 };
 
+// What lane i of a session's wave knows of position i+1 once its rows are
+// profiled: the drafted token, p_i(x_i) and q_i(x_i) where the rule reads
+// them (-1 and 1 elsewhere), and the acceptance value of rule 2 (1 elsewhere).
+struct LanePos {
+  int32_t x;
+  double px, qx, u;
+};
+
+__device__ __attribute__((always_inline)) LanePos lane_position(
+    int b, int lane, int mb, int rl, const int32_t* __restrict__ tokens, int M, int V,
+    const float* __restrict__ qrows, const RowRec* __restrict__ rr,
+    const double* __restrict__ unif, uint64_t seed, uint64_t session_key, uint32_t round) {
+  LanePos P{-1, -1.0, 1.0, 1.0};
+  if (lane >= mb) return P;
+  P.x = tokens[(size_t)b * M + lane];  // in [0, V) once the session's checks passed
+  if (rl == SV_RULE_SPECULATIVE || rl == SV_RULE_RELAXED) P.px = rr[lane].ptok;
+  if (rl == SV_RULE_SPECULATIVE) {
+    P.qx = qrows ? (double)qrows[((size_t)b * M + lane) * (size_t)V + P.x] : rr[M + 1 + lane].ptok;
+    double ud;
+    if (unif) P.u = unif[(size_t)b * (2 * M + 1) + lane];
+    else verifier_uniforms(seed, session_key, round, (uint32_t)(lane + 1), &P.u, &ud);
+  }
+  return P;
+}
+
+// The in-order reading of a session (textbook "The acceptance rule": the
+// proposals are checked one after another, and the first rejection ends the
+// round): the first of positions 1..n (lane j: position j+1) at which the
+// round ends, as a 1-based position, or 0 if none does.  A position ends it
+// with a bad target row (or bad draft row), an unusable q_i(x_i), or a failed
+// test; position m+1 (the additional token's row) with a bad row only.
+__device__ __attribute__((always_inline)) int inorder_end(int n, int mb, int rl, bool draft_rows,
+                                                          const RowRec* __restrict__ rr, int M,
+                                                          const LanePos& P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool end = false;
+  if (lane < n) {
+    end = rr[lane].status != 0;
+    if (lane < mb) {
+      if (rl == SV_RULE_GREEDY) {
+        end |= P.x != rr[lane].argmax;
+      } else if (rl == SV_RULE_RELAXED) {
+        end |= !(P.px > 0.0);
+      } else {
+        if (draft_rows) end |= rr[M + 1 + lane].status != 0;
+        const double ratio = P.px / P.qx;
+        end |= !(P.qx > 0.0 && P.qx < INFINITY) || !(P.u < (ratio < 1.0 ? ratio : 1.0));
+      }
+    }
+  }
+  const uint64_t e = __ballot(end);
+  // position 65 (m = 64, lane 64 does not exist): its row alone
+  if (e == 0 && n > kWave && rr[kWave].status != 0) return kWave + 1;
+  return e ? __builtin_ctzll(e) + 1 : 0;
+}
+
 // SDCP Sec. 6.4, for session b, by one wave: lane i examines position i+1.
 // With published q rows (qrows != null) q_i(x_i) is read from them and no
 // draft row record exists.  Writes nothing.  A draw from listed supports is
 // taken here when listed is set; otherwise such a session only reports that
-// no chunked draw is left (job kind none).
+// no chunked draw is left (job kind none).  decided != null: the in-order
+// reading, whose rows are read up to the position decided[b] (0: up to m+1),
+// and statuses and decisions come from those rows alone.
 __device__ __attribute__((always_inline)) Verdict accept_session(
     int b, const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int M, int V,
     const float* __restrict__ qrows, uint64_t seed, uint32_t round,
     const int32_t* __restrict__ sess_status, const RowRec* __restrict__ rows,
     const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p,
-    const double* __restrict__ unif, bool listed, int32_t* q_id, double* q_p) {
+    const double* __restrict__ unif, const int32_t* __restrict__ decided, bool listed,
+    int32_t* q_id, double* q_p) {
   const int lane = threadIdx.x;
   const int R = 2 * M + 1;
   Verdict v;
@@ -123,28 +183,43 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   const int rl = rule[b];
   v.rl = rl;
   v.mb = mb;
-  const int32_t x = (st == 0 && lane < mb) ? tokens[(size_t)b * M + lane] : -1;
+  const bool draft_rows = rl == SV_RULE_SPECULATIVE && !qrows;
+  LanePos pos{-1, -1.0, 1.0, 1.0};
+  if (st == 0)
+    pos = lane_position(b, lane, mb, rl, tokens, M, V, qrows, rr, unif, seed,
+                      sampling[b].session_key, round);
+  // target rows read: 1..L (the SDCP reading: every row, m+1 of them)
+  int L = mb + 1;
+  if (st == 0 && decided) {
+    const int e = decided[b];
+    const int n = e > 0 ? e : mb + 1;
+    const int f = inorder_end(n, mb, rl, draft_rows, rr, M, pos);
+    L = f > 0 ? f : n;
+  }
+  const int np = L < mb ? L : mb;  // positions whose drafted token is examined
+  v.np = np;
+  const int32_t x = lane < np ? pos.x : -1;
   v.x = x;
 
-  // every row the rule reads must be usable (target rows 1..m+1, draft rows 1..m)
+  // every row the rule reads must be usable (target rows 1..L, draft rows 1..np)
   if (st == 0) {
     bool bad = false;
-    for (int j = lane; j <= mb; j += kWave) bad |= rr[j].status != 0;
-    if (rl == SV_RULE_SPECULATIVE && !qrows && lane < mb) bad |= rr[M + 1 + lane].status != 0;
+    for (int j = lane; j < L; j += kWave) bad |= rr[j].status != 0;
+    if (draft_rows && lane < np) bad |= rr[M + 1 + lane].status != 0;
     if (__any(bad)) st = SV_S_BAD_LOGITS;
   }
-  // Sec. 6.3 step 5: q_i(x_i) != 0 at every position, before any draw
-  // (x is in [0, V) once the session's checks passed); a q value that is not a
-  // positive finite number (only a published row can hold one) is unusable
+  // Sec. 6.3 step 5: q_i(x_i) != 0 at every position examined, before any
+  // draw; a q value that is not a positive finite number (only a published
+  // row can hold one) is unusable
   double qx = 1.0, px = -1.0;
   if (st == 0 && rl == SV_RULE_SPECULATIVE) {
-    if (lane < mb) {
-      qx = qrows ? (double)qrows[((size_t)b * M + lane) * (size_t)V + x] : rr[M + 1 + lane].ptok;
-      px = rr[lane].ptok;
+    if (lane < np) {
+      qx = pos.qx;
+      px = pos.px;
     }
-    if (__any(lane < mb && !(qx > 0.0 && qx < INFINITY))) st = SV_S_BAD_PROPOSAL;
+    if (__any(lane < np && !(qx > 0.0 && qx < INFINITY))) st = SV_S_BAD_PROPOSAL;
   }
-  if (st == 0 && rl == SV_RULE_RELAXED && lane < mb) px = rr[lane].ptok;
+  if (st == 0 && rl == SV_RULE_RELAXED && lane < np) px = pos.px;
   v.px = px;
   v.qx = qx;
   v.st = st;
@@ -153,7 +228,7 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   int a;
   if (rl == SV_RULE_GREEDY) {
     // Rule 1: accept while x_i == argmax p_i; additional token argmax p_{a+1}
-    const bool acc = lane < mb && x == rr[lane].argmax;
+    const bool acc = lane < np && x == rr[lane].argmax;
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
@@ -162,7 +237,7 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
     // relaxed rule (private use 192): accept x_i while p_i(x_i) > 0; the
     // additional token is drawn from p_{a+1} with the purpose-1 value of
     // position a+1, from the listed support or by the chunked sampler
-    const bool acc = lane < mb && px > 0.0;
+    const bool acc = lane < np && px > 0.0;
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
@@ -184,13 +259,8 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
     // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i)); the values
     // are SDCP's (computed by the row kernel into unif) or Philox's
     const double* uv = unif ? unif + (size_t)b * R : nullptr;
-    double u_acc = 1.0, u_add = 0.0;
-    if (uv) u_acc = lane < mb ? uv[lane] : 1.0;
-    else
-      verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(lane + 1), &u_acc,
-                        &u_add);
     const double ratio = px / qx;
-    const bool acc = lane < mb && u_acc < (ratio < 1.0 ? ratio : 1.0);
+    const bool acc = lane < np && pos.u < (ratio < 1.0 ? ratio : 1.0);
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
@@ -238,8 +308,8 @@ __device__ __attribute__((always_inline)) void write_verdict(
     out[j] = t;
   }
   for (int j = lane; j < M; j += kWave) {
-    const bool have_p = (v.rl == SV_RULE_SPECULATIVE || v.rl == SV_RULE_RELAXED) && j < v.mb;
-    const bool have_q = v.rl == SV_RULE_SPECULATIVE && j < v.mb;
+    const bool have_p = (v.rl == SV_RULE_SPECULATIVE || v.rl == SV_RULE_RELAXED) && j < v.np;
+    const bool have_q = v.rl == SV_RULE_SPECULATIVE && j < v.np;
     if (p_tok) p_tok[(size_t)b * M + j] = have_p ? v.px : -1.0;
     if (q_tok) q_tok[(size_t)b * M + j] = have_q ? v.qx : -1.0;
   }
@@ -819,7 +889,8 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
     int32_t* __restrict__ out_tokens, double* __restrict__ p_tok, double* __restrict__ q_tok,
     const int32_t* __restrict__ sup_id, const double* __restrict__ sup_p,
     const double* __restrict__ unif, GroupRec* __restrict__ groups, uint32_t* __restrict__ ctr,
-    const uint32_t* __restrict__ draw_flag, uint32_t draw_token, int C, int gw) {
+    const uint32_t* __restrict__ draw_flag, uint32_t draw_token, int C, int gw,
+    const int32_t* __restrict__ decided) {
   __shared__ DrawSmem sm;
   const int b = (int)blockIdx.x / C;
   const int c = (int)blockIdx.x - b * C;
@@ -832,7 +903,8 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   Verdict v{};
   if (t < kWave) {
     v = accept_session(b, tokens, m, rule, sampling, M, V, kQ ? qrows : nullptr, seed, round,
-                       sess_status, rows, sup_id, sup_p, unif, c == 0, sm.q_id, sm.q_p);
+                       sess_status, rows, sup_id, sup_p, unif, decided, c == 0, sm.q_id,
+                       sm.q_p);
     if (v.st < 0 || v.job.kind == kJobNone) {
       if (c == 0) write_verdict(b, v, v.extra, M, accepted_len, out_tokens, p_tok, q_tok);
       v.job.kind = kJobNone;
@@ -1078,7 +1150,43 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
   if (wid == 0) write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
 }
 
+// After a window of the in-order reading (positions up to hi read for every
+// undecided session): one wave per session finds the position at which its
+// round ends, if any is at or before hi, and records it in decided[b]; a
+// session whose every position through m+1 passes ends at m+1.  The next
+// window's row kernels skip decided sessions.
+constexpr int kAdvanceNT = 256;
+__global__ __launch_bounds__(kAdvanceNT) void k_advance(
+    const float* __restrict__ qrows, const int32_t* __restrict__ tokens,
+    const int32_t* __restrict__ m, const int32_t* __restrict__ rule,
+    const sv_sampling* __restrict__ sampling, int B, int M, int V, uint64_t seed, uint32_t round,
+    const int32_t* __restrict__ sess_status, const RowRec* __restrict__ rows,
+    const double* __restrict__ unif, int has_draft_logits, int hi, int32_t* __restrict__ decided) {
+  const int b = (int)blockIdx.x * (kAdvanceNT / kWave) + (int)threadIdx.x / kWave;
+  if (b >= B || decided[b] != 0 || sess_status[b] != 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int mb = m[b];
+  const int rl = rule[b];
+  const RowRec* rr = rows + (size_t)b * (2 * M + 1);
+  const LanePos pos = lane_position(b, lane, mb, rl, tokens, M, V, qrows, rr, unif, seed,
+                                    sampling[b].session_key, round);
+  const int n = hi < mb + 1 ? hi : mb + 1;
+  const int f = inorder_end(n, mb, rl, rl == SV_RULE_SPECULATIVE && has_draft_logits, rr, M, pos);
+  if (lane == 0) {
+    if (f > 0) decided[b] = f;
+    else if (hi >= mb + 1) decided[b] = mb + 1;
+  }
+}
+
 }  // namespace
+
+void launch_advance(const LaunchArgs& a, hipStream_t st, int hi) {
+  const int per = kAdvanceNT / kWave;
+  const unsigned grid = (unsigned)((a.B + per - 1) / per);
+  hipLaunchKernelGGL(k_advance, dim3(grid), dim3(kAdvanceNT), 0, st, a.qrows, a.tokens, a.m,
+                     a.rule, a.sampling, a.B, a.M, a.V, a.seed, a.round, a.sess_status, a.rows,
+                     a.unif, a.draft != nullptr ? 1 : 0, hi, a.decided);
+}
 
 template <class Tr, bool kQ>
 static void launch_finalize_t(const LaunchArgs& a, hipStream_t st) {
@@ -1088,7 +1196,7 @@ static void launch_finalize_t(const LaunchArgs& a, hipStream_t st) {
                      (const E*)a.draft, a.qrows, a.tokens, a.m, a.rule, a.sampling, a.B, a.M, a.V,
                      a.seed, a.round, a.sess_status, a.rows, a.accepted_len, a.out_tokens, a.p_tok,
                      a.q_tok, a.sup_id, a.sup_p, a.unif, a.groups, a.draw_ctr, a.draw_flag,
-                     a.draw_token, a.draw_C, a.draw_gw);
+                     a.draw_token, a.draw_C, a.draw_gw, a.decided);
 }
 
 void launch_finalize(const LaunchArgs& a, hipStream_t st) {
