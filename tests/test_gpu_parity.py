@@ -252,13 +252,16 @@ def test_topk_kernel_edge_cases():
     parity.compare(g, o, "topk-edges")
 
 
-def test_dense_kernel_edge_cases():
+@pytest.mark.parametrize("split", ["1", "4"])
+def test_dense_kernel_edge_cases(split, monkeypatch):
     """Rows handled by the one-pass dense path (temperature, optional top-p,
     top-k off): a maximum that rises tile after tile, heavy ties at the cut,
     drafted tokens on both sides of a tied cut, a cut below the histogram
     window (generic fallback), all-negative rows, masks, bad logits; an odd
-    vocabulary of five tiles so that rows start at every alignment."""
-    parity.log("[case] dense path edge cases, V=5003")
+    vocabulary of five tiles so that rows start at every alignment.  Each row
+    by one wave, or split over four (histogram windows and ranks merged)."""
+    monkeypatch.setenv("SV_ROWS_SPLIT", split)
+    parity.log(f"[case] dense path edge cases, V=5003, split={split}")
     B, M, V = 14, 3, 5003
     rng = np.random.default_rng(73)
     t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
@@ -315,13 +318,15 @@ def test_dense_kernel_edge_cases():
     parity.compare(g, o, "dense-edges")
 
 
-def test_dense_topk_above_64_edge_cases():
+@pytest.mark.parametrize("split", ["1", "4"])
+def test_dense_topk_above_64_edge_cases(split, monkeypatch):
     """Rows with 64 < top_k < V, which the one-pass dense path cuts from its
     histogram window: top-k alone and top-k then top-p, ties split at the
     top-k cut with drafted tokens on both sides of it, all-negative rows, a
     rising maximum, -inf masks leaving fewer than K finite tokens, and a
     window holding fewer than K tokens (the generic fallback)."""
-    parity.log("[case] dense path, top_k above 64, V=5003")
+    monkeypatch.setenv("SV_ROWS_SPLIT", split)
+    parity.log(f"[case] dense path, top_k above 64, V=5003, split={split}")
     B, M, V = 12, 3, 5003
     rng = np.random.default_rng(74)
     t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)

@@ -147,62 +147,195 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool hist, const u32x4& v,
   }
 }
 
-// The profile of one row of the dense class, by one wave: temperature > 0,
-// top-k off or above 64, with or without top-p.  bins is the wave's LDS
-// histogram of kWin counts.
-__device__ __attribute__((always_inline)) inline bool row_profile(
-    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
+// The row's layout for the pass: a 16-byte aligned window over the row, in
+// which positions [head, head + V) are the row.
+struct RowWin {
+  const u32x4* vbase;
+  int head, npos, nvec, ntiles;
+};
+__device__ inline RowWin row_window(const uint16_t* row, int V) {
+  RowWin W;
+  W.head = (int)(((uintptr_t)row & 15u) >> 1);
+  W.vbase = (const u32x4*)(row - W.head);
+  W.npos = W.head + V;
+  W.nvec = (W.npos + 7) / 8;
+  W.ntiles = (W.npos + kTile - 1) / kTile;
+  return W;
+}
+
+// The pass over tiles [t0, t1) of the window, by one wave: its lanes' running
+// maxima and sums (L), and with hist its histogram window (H) and, when the
+// drafted token lies in these tiles, the token's rank among the tokens of its
+// key before it in these tiles.  Positions from t1's first on read as -inf.
+__device__ __attribute__((always_inline)) inline void stream_part(const RowWin& W, int t0, int t1,
+                                                                  bool hist, int px, float scale_f,
+                                                                  double scale, LaneSum& L,
+                                                                  Hist& H) {
   const int lane = __lane_id();
-  const bool top_p = smp.top_p_milli < 1000;
-  const bool top_k = smp.top_k > 0 && smp.top_k < (uint32_t)V;
-  const bool hist = top_p || top_k;  // the histogram window is kept
-  // the row's scale: log2(e) / T rounded to binary32, used everywhere below
-  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
-  const double scale = (double)scale_f;
-
-  // 16-byte aligned window over the row: positions [head, head + V) are the row
-  const int head = (int)(((uintptr_t)row & 15u) >> 1);
-  const u32x4* vbase = (const u32x4*)(row - head);
-  const int npos = head + V;
-  const int nvec = (npos + 7) / 8;
-  const int ntiles = (npos + kTile - 1) / kTile;
-  const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
-
-  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
-  Hist H{bins, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), x >= 0 ? skey_of(xval) : 0, 0};
-  const int px = x >= 0 ? x + head : -1;
-  const int xv = px >= 0 ? px / (kWave * 8) : -1;  // the drafted token's vector index in the row
-
+  const int hi = min(W.npos, t1 * kTile);
+  const int xv = px >= 0 ? px / (kWave * 8) : -1;  // the drafted token's vector index
   u32x4 ring[kNBuf][kVec];
 #pragma unroll
   for (int u = 0; u < kNBuf - 1; ++u) {
-    load_tile<kVec>(ring[u], vbase, u, nvec - 1);
+    load_tile<kVec>(ring[u], W.vbase, t0 + u, W.nvec - 1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int nround = (ntiles + kNBuf - 1) / kNBuf;
+  const int nround = (t1 - t0 + kNBuf - 1) / kNBuf;
   for (int r = 0; r < nround; ++r) {
     set_priority(nround - r, nround);
 #pragma unroll
     for (int u = 0; u < kNBuf; ++u) {
-      const int tt = r * kNBuf + u;
-      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec - 1);
-      if ((tt == 0 && head > 0) || (tt + 1) * kTile > npos) mask_tile<kVec>(ring[u], tt, head, npos);
+      const int tt = t0 + r * kNBuf + u;
+      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], W.vbase, tt + kNBuf - 1, W.nvec - 1);
+      if ((tt == 0 && W.head > 0) || (tt + 1) * kTile > hi) mask_tile<kVec>(ring[u], tt, W.head, hi);
 #pragma unroll
       for (int j = 0; j < kVec; ++j)
         dense_vec(L, H, hist, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
                   tt * kVec + j == xv, scale_f, scale);
     }
   }
+}
 
-  // lanes combined in a fixed order: maximum and Z (relative to lmax * s)
-  float lmax = L.mv;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, kWave));
+// This wave's share of Z relative to lmax * s (lanes combined in a fixed order).
+__device__ inline double wave_z(const LaneSum& L, float lmax, double scale) {
   const double ref = (double)lmax * scale;  // exact: both factors are binary32
   double z = L.vt == -__builtin_huge_valf() ? L.s : L.s * exp2((double)L.q - ref);
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
-  if (__ballot(L.ovf)) {  // logits beyond binary32 exponent range: handed back
+  return z;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V, int32_t x, float xval, float lmax,
+                              double z, bool ovf, const Hist& H, RowRec* rec);
+
+// The profile of one row of the dense class, by one wave: temperature > 0,
+// top-k off or above 64, with or without top-p.  bins is the wave's LDS
+// histogram of kWin counts.  Returns true if the row is handed back.
+__device__ __attribute__((always_inline)) inline bool row_profile(
+    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
+  const bool hist = smp.top_p_milli < 1000 || (smp.top_k > 0 && smp.top_k < (uint32_t)V);
+  // the row's scale: log2(e) / T rounded to binary32, used everywhere below
+  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
+  const double scale = (double)scale_f;
+  const RowWin W = row_window(row, V);
+  const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
+  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
+  Hist H{bins, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), x >= 0 ? skey_of(xval) : 0, 0};
+  stream_part(W, 0, W.ntiles, hist, x >= 0 ? x + W.head : -1, scale_f, scale, L, H);
+  const float lmax = wave_max(L.mv);
+  const double z = wave_z(L, lmax, scale);
+  return finish(smp, V, x, xval, lmax, z, __ballot(L.ovf) != 0, H, rec);
+}
+
+// What each wave of a split row leaves for the merge.
+struct PartRec {
+  float lmax;
+  int anchor;  // the part's histogram window is [anchor - kWin + 1, anchor]
+  int nx;      // tokens of the drafted token's key: before it (its own part), or all
+  int ovf;
+  double z;    // the part's sum relative to the row's lmax * s
+};
+
+// The same profile with the row split over the S waves of a workgroup, for
+// launches with few rows: wave w streams tiles [w T / S, (w + 1) T / S) into
+// its own histogram window (bins + w kWin), and wave 0 merges them.  Every
+// part's window ends at its own maximum, at or below the row's, so each holds
+// every token of the keys in the row's window [A - kWin + 1, A] (A the row's
+// largest key) that lie at or below its maximum: the row's counts there are
+// the sums of those bins.  Z is the parts' sums relative to the row's maximum,
+// added in part order.  Called by every wave of the workgroup (it has
+// workgroup barriers); returns true (in wave 0) if the row is handed back.
+template <int S>
+__device__ __attribute__((always_inline)) inline bool row_profile_split(
+    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins_all,
+    PartRec* parts, int wid) {
+  const int lane = __lane_id();
+  const bool hist = smp.top_p_milli < 1000 || (smp.top_k > 0 && smp.top_k < (uint32_t)V);
+  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
+  const double scale = (double)scale_f;
+  const RowWin W = row_window(row, V);
+  const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
+  const int kx = x >= 0 ? skey_of(xval) : 0;
+  const int px = x >= 0 ? x + W.head : -1;
+  const int t0 = wid * W.ntiles / S, t1 = (wid + 1) * W.ntiles / S;
+  const bool x_here = px >= 0 && px / kTile >= t0 && px / kTile < t1;
+  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
+  Hist H{bins_all + wid * kWin, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), kx, 0};
+  stream_part(W, t0, t1, hist, x_here ? px : -1, scale_f, scale, L, H);
+  const float lm = wave_max(L.mv);
+  const bool ovf = __ballot(L.ovf) != 0;
+  // tokens of the drafted token's key: before it in its part, all of them in
+  // a part before it (when the key lies in the part's window)
+  int nx = 0;
+  if (x_here) nx = H.rank_x;
+  else if (x >= 0 && hist && kx <= H.anchor && kx > H.anchor - kWin)
+    nx = (int)H.bin[kx & (kWin - 1)];
+  if (lane == 0) {
+    parts[wid].lmax = lm;
+    parts[wid].anchor = H.anchor;
+    parts[wid].nx = nx;
+    parts[wid].ovf = ovf ? 1 : 0;
+  }
+  __syncthreads();
+  float lmax = parts[0].lmax;
+#pragma unroll
+  for (int w = 1; w < S; ++w) lmax = fmaxf(lmax, parts[w].lmax);
+  const double zw = wave_z(L, lmax, scale);
+  if (lane == 0) parts[wid].z = zw;
+  __syncthreads();  // every part's sum and histogram are complete
+  if (wid != 0) return false;
+  double z = parts[0].z;
+  int anc = parts[0].anchor, any_ovf = parts[0].ovf;
+#pragma unroll
+  for (int w = 1; w < S; ++w) {
+    z += parts[w].z;
+    anc = max(anc, parts[w].anchor);
+    any_ovf |= parts[w].ovf;
+  }
+  Hist M{bins_all, anc, value_of(anc), value_of(max(anc - (kWin - 1), kNegInfKey + 1)), kx, 0};
+  if (hist) {
+    // the row's window: bin i holds key k = anc - ((anc - i) mod kWin)
+    for (int i = lane; i < kWin; i += kWave) {
+      const int k = anc - ((anc - i) & (kWin - 1));
+      uint32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < S; ++w)
+        if (k <= parts[w].anchor) c += bins_all[w * kWin + i];
+      bins_all[i] = c;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (px >= 0) {  // the drafted token's rank: the parts before its own, then its own
+      const int tx = px / kTile;
+      for (int w = 0; w < S; ++w) {
+        M.rank_x += parts[w].nx;
+        if (tx < (w + 1) * W.ntiles / S) break;
+      }
+    }
+  }
+  return finish(smp, V, x, xval, lmax, z, any_ovf != 0, M, rec);
+}
+
+// After the pass: the row's record from its maximum, Z, the overflow flag and
+// the histogram window H (with the drafted token's key and rank).  Returns
+// true if the row is handed back.
+__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V, int32_t x, float xval, float lmax,
+                              double z, bool ovf, const Hist& H, RowRec* rec) {
+  const int lane = __lane_id();
+  const bool top_p = smp.top_p_milli < 1000;
+  const bool top_k = smp.top_k > 0 && smp.top_k < (uint32_t)V;
+  const bool hist = top_p || top_k;
+  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
+  const double scale = (double)scale_f;
+  const uint32_t* bins = H.bin;
+  if (ovf) {  // logits beyond binary32 exponent range: handed back
     return true;
   }
 

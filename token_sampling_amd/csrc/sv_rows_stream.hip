@@ -136,17 +136,21 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
   }
 }
 
-// The same row slots with each top-k-class row split over S waves of one
-// workgroup, for launches with few rows: one wave alone needs about 90 us for
-// a 128K-logit top-50 row (57 us of it streaming with ten tiles in flight, the
-// rest candidate insertion), so a few long rows leave the chip idle.  Wave w streams tiles
-// [w T / S, (w + 1) T / S) with its own first bound (a bound from any part of
-// the row bounds the row's k-th best), cuts its region to its k best, and wave
-// 0 merges the S lists (at most S * 64 <= kCap entries) and finishes the row.
-// Dense-class rows are profiled by one wave of the workgroup alone.
+// The same row slots with each row split over S waves of one workgroup, for
+// launches with few rows: one wave alone needs about 90 us for a 128K-logit
+// top-50 row (57 us of it streaming with ten tiles in flight, the rest
+// candidate insertion), so a few long rows leave the chip idle.  Wave w streams
+// tiles [w T / S, (w + 1) T / S).  Top-k class: with its own first bound (a
+// bound from any part of the row bounds the row's k-th best), it cuts its
+// region to its k best, and wave 0 merges the S lists (at most S * 64 <= kCap
+// entries) and finishes the row.  Dense class: into its own histogram window
+// and sums, which wave 0 merges (dense::row_profile_split).
+#ifndef SV_SPLIT_WAVES_PER_EU
+#define SV_SPLIT_WAVES_PER_EU 4
+#endif
 template <int S>
 __global__ __launch_bounds__(S * kWave)
-__attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
+__attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
     const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
@@ -156,8 +160,10 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
     int32_t* __restrict__ decided, int win_lo, int win_w) {
   static_assert(S * kSupMax <= topk::kCap, "the merged lists fit one region");
-  constexpr int kWords = (S * topk::kCap > kLdsWords ? S * topk::kCap : kLdsWords);
-  __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or the dense histogram
+  constexpr int kRegions = S * topk::kCap > S * dense::kWin / 2 ? S * topk::kCap : S * dense::kWin / 2;
+  constexpr int kWords = kRegions > kLdsWords ? kRegions : kLdsWords;
+  __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or S dense histograms
+  __shared__ dense::PartRec parts_s[S];
   __shared__ int cnt_s[S], ovf_s[S];
   __shared__ uint32_t mm_s[S], um_s[S];
   const int lane = __lane_id();
@@ -233,12 +239,10 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_split(
     topk::row_finish(reg, total, k, lane == 0 ? mmax : 0u, lane == 0 ? umax : 0u, one_hot,
                      smp.temperature_milli, smp.top_p_milli, x, rec, sup_id + so, sup_p + so);
   } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
-    // one wave, chosen by the slot, so that dense rows spread over the SIMDs
-    if (wid == slot_g % S) {
-      if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
-      if (dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds))
-        exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
-    }
+    // the S waves stream S parts of the row; wave 0 merges them and finishes
+    if (wid == 0 && lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
+    if (dense::row_profile_split<S>(row, V, smp, x, rec, (uint32_t*)lds, parts_s, wid))
+      exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
   }
 }
 
@@ -256,6 +260,8 @@ static int rows_split_factor(const LaunchArgs& a) {
     const int s = atoi(env);
     if (s == 1 || s == 2 || s == 4) return s;
   }
+  // windows after the first read the few sessions left undecided
+  if (a.win_w != 0 && a.win_lo > 1) return 4;
   const int W = a.win_w == 0 ? a.M + 1 : a.win_w;  // target positions per session
   const size_t rows = (size_t)a.B * W + (a.draft ? (size_t)a.B * (W < a.M ? W : a.M) : 0);
   return rows < 1024 ? 4 : 1;
