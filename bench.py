@@ -41,6 +41,7 @@ MEASURED_TRAFFIC = {
     ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
     ("b256_topk_topp", "k_rows_stream", "stream-v3"): 1_119_487_488,
     ("b256_topk_topp", "k_rows_stream", "stream-v4"): 1_119_499_072,
+    ("b256_topk_topp", "k_rows_stream", "stream-v5"): 1_119_496_295,
 }
 
 
