@@ -1,10 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the verifier acceptance step (libspecverify) on one MI355X.
 
-A step is one sv_verify call (sv_verify_sdcp with --sdcp) over one batch of
-synthetic logits already resident in HBM: the single-pass row kernel (session checks and the row
-profiles, the HBM-streaming part), the generic row kernel, and the
-per-session kernel (acceptance and the additional token).
+A step is one sv_verify call (sv_verify_sdcp with --sdcp, sv_verify_qrows with
+--qrows, sv_verify_early with --early W) over one batch of synthetic logits
+already resident in HBM: the single-pass row kernel (session checks and the row
+profiles, the HBM-streaming part), the generic row kernel, and the per-session
+kernel (acceptance and the additional token).  With --early the rows are read in
+windows of positions, and the roofline line counts the rows the sessions need
+(a+1 target rows and, for rule 2, a+1 draft rows) over the time of all the
+windows' row and advance kernels.
 
 Prints ONE JSON line:
   value        verified positions per second, P = sum_b (m_b + 1) per step
@@ -49,10 +53,11 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None):
+def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None, early=False):
     """Time the oracle on the first sessions of the workload (bounded sample).
     sdcp_raw: the [B, 32] session records (numpy uint8) when SDCP values are used;
-    q_rows: the [B, M, V] published draft rows (device tensor) in q-rows mode."""
+    q_rows: the [B, M, V] published draft rows (device tensor) in q-rows mode;
+    early: the oracle's in-order reading (rows after the deciding position unread)."""
     import numpy as np
 
     import oracle
@@ -76,7 +81,7 @@ def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None):
         t0 = time.perf_counter()
         oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
                       h["seed"], h["round"], diagnostics=False,
-                      sdcp_sessions=None if sdcp is None else sdcp[idx], q_rows=qh)
+                      sdcp_sessions=None if sdcp is None else sdcp[idx], q_rows=qh, early=early)
         dt = time.perf_counter() - t0
         elapsed += dt
         positions += int((np.asarray(h["m"], dtype=np.int64) + 1).sum())
@@ -89,7 +94,7 @@ def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None):
         "cores": 1,
         "kind": "oracle",
         "sample": f"sessions 0..{done_sessions - 1} of {w.name} (P={positions}), "
-                  f"{elapsed:.1f} s single-threaded",
+                  f"{elapsed:.1f} s single-threaded" + (", read in order" if early else ""),
     }
 
 
@@ -269,7 +274,8 @@ def main():
     if args.cpu_budget > 0:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(
-            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows)
+            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows,
+            early=bool(args.early))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -74,14 +74,18 @@ struct GroupRec {
 };
 static_assert(sizeof(GroupRec) == 48, "GroupRec layout");
 
-// Workgroups per session for the draw: about 1024 in all (B * C), each
+// Workgroups per session for the draw: about kDrawTarget in all (B * C), each
 // wave taking gw whole groups.
+#ifndef SV_DRAW_TARGET
+#define SV_DRAW_TARGET 1024
+#endif
+constexpr long long kDrawTarget = SV_DRAW_TARGET;
 struct DrawChunks {
   int32_t C, gw;
 };
 __host__ __device__ inline DrawChunks draw_chunks(int32_t B, int32_t V) {
   const long long G = ((long long)V + kGroup - 1) / kGroup;
-  long long C = (1024 + (long long)B - 1) / B;
+  long long C = (kDrawTarget + (long long)B - 1) / B;
   const long long cmax = (G + 3) / 4;
   if (C > cmax) C = cmax;
   if (C < 1) C = 1;
