@@ -252,7 +252,7 @@ def test_topk_kernel_edge_cases():
     parity.compare(g, o, "topk-edges")
 
 
-@pytest.mark.parametrize("split", ["1", "4"])
+@pytest.mark.parametrize("split", ["1", "4", "8"])
 def test_dense_kernel_edge_cases(split, monkeypatch):
     """Rows handled by the one-pass dense path (temperature, optional top-p,
     top-k off): a maximum that rises tile after tile, heavy ties at the cut,
@@ -318,7 +318,7 @@ def test_dense_kernel_edge_cases(split, monkeypatch):
     parity.compare(g, o, "dense-edges")
 
 
-@pytest.mark.parametrize("split", ["1", "4"])
+@pytest.mark.parametrize("split", ["1", "4", "8"])
 def test_dense_topk_above_64_edge_cases(split, monkeypatch):
     """Rows with 64 < top_k < V, which the one-pass dense path cuts from its
     histogram window: top-k alone and top-k then top-p, ties split at the
@@ -401,10 +401,11 @@ def test_full_size_top_k_above_64(top_k, top_p):
     parity.compare({k: v[idx] for k, v in g_all.items()}, o, f"b256-top_k{top_k}")
 
 
-@pytest.mark.parametrize("split", ["1", "2", "4"])
+@pytest.mark.parametrize("split", ["1", "2", "4", "8"])
 def test_split_rows_each_factor(split, monkeypatch):
-    """The single-pass kernel with each top-k-class row streamed by 1, 2 or 4
-    waves (forced through SV_ROWS_SPLIT), on top-k, one-hot and dense profiles,
+    """The single-pass kernel with each row streamed by 1, 2, 4 or 8 waves
+    (forced through SV_ROWS_SPLIT; top-k-class rows use at most 4), on top-k,
+    one-hot and dense profiles,
     a vocabulary of one tile (waves with empty parts), and rows that overflow
     the candidate region (handed to the generic kernel)."""
     monkeypatch.setenv("SV_ROWS_SPLIT", split)

@@ -159,7 +159,9 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
     int32_t* __restrict__ decided, int win_lo, int win_w) {
-  static_assert(S * kSupMax <= topk::kCap, "the merged lists fit one region");
+  // top-k-class rows use the first TS waves (the merged lists fit one region)
+  constexpr int TS = S < 4 ? S : 4;
+  static_assert(TS * kSupMax <= topk::kCap, "the merged lists fit one region");
   constexpr int kRegions = S * topk::kCap > S * dense::kWin / 2 ? S * topk::kCap : S * dense::kWin / 2;
   constexpr int kWords = kRegions > kLdsWords ? kRegions : kLdsWords;
   __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or S dense histograms
@@ -202,26 +204,28 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
     const int k = one_hot ? 1 : (int)smp.top_k;
     const int T = topk::row_tiles(row, V);
     uint64_t* reg = lds + wid * topk::kCap;
-    topk::WaveState s;
-    topk::chunk_scan(row, V, k, wid * T / S, (wid + 1) * T / S, s, reg);
-    const int n = s.overflow ? 0 : topk::region_cut(reg, s.n, k).n;
-    uint32_t mm = s.magmax, um = s.umax;
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      mm = stream::max_u16x2(mm, __shfl_xor(mm, off, kWave));
-      um = stream::max_u16x2(um, __shfl_xor(um, off, kWave));
-    }
-    if (lane == 0) {
-      cnt_s[wid] = n;
-      ovf_s[wid] = s.overflow ? 1 : 0;
-      mm_s[wid] = mm;
-      um_s[wid] = um;
+    if (wid < TS) {
+      topk::WaveState s;
+      topk::chunk_scan(row, V, k, wid * T / TS, (wid + 1) * T / TS, s, reg);
+      const int n = s.overflow ? 0 : topk::region_cut(reg, s.n, k).n;
+      uint32_t mm = s.magmax, um = s.umax;
+      for (int off = kWave / 2; off > 0; off >>= 1) {
+        mm = stream::max_u16x2(mm, __shfl_xor(mm, off, kWave));
+        um = stream::max_u16x2(um, __shfl_xor(um, off, kWave));
+      }
+      if (lane == 0) {
+        cnt_s[wid] = n;
+        ovf_s[wid] = s.overflow ? 1 : 0;
+        mm_s[wid] = mm;
+        um_s[wid] = um;
+      }
     }
     __syncthreads();
     if (wid != 0) return;
     int ovf = 0, total = cnt_s[0];
     uint32_t mmax = mm_s[0], umax = um_s[0];
 #pragma unroll
-    for (int w = 1; w < S; ++w) {
+    for (int w = 1; w < TS; ++w) {
       ovf |= ovf_s[w];
       mmax = stream::max_u16x2(mmax, mm_s[w]);
       umax = stream::max_u16x2(umax, um_s[w]);
@@ -253,15 +257,18 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
 // low threshold and inserts many candidates, so splitting pays only while the
 // launch has under about one row per SIMD: 4 waves per row below 1024 rows
 // (272 rows: 91 -> 59 us; 768 rows: 104 -> 91 us), 1 above (2304 rows: 120 us
-// with 1 wave, 132 us with 2).  SV_ROWS_SPLIT (1, 2 or 4) overrides the choice.
+// with 1 wave, 132 us with 2).  SV_ROWS_SPLIT (1, 2, 4 or 8) overrides the choice.
+#ifndef SV_LATE_SPLIT
+#define SV_LATE_SPLIT 4
+#endif
 static int rows_split_factor(const LaunchArgs& a) {
   const char* env = getenv("SV_ROWS_SPLIT");
   if (env) {
     const int s = atoi(env);
-    if (s == 1 || s == 2 || s == 4) return s;
+    if (s == 1 || s == 2 || s == 4 || s == 8) return s;
   }
   // windows after the first read the few sessions left undecided
-  if (a.win_w != 0 && a.win_lo > 1) return 4;
+  if (a.win_w != 0 && a.win_lo > 1) return SV_LATE_SPLIT;
   const int W = a.win_w == 0 ? a.M + 1 : a.win_w;  // target positions per session
   const size_t rows = (size_t)a.B * W + (a.draft ? (size_t)a.B * (W < a.M ? W : a.M) : 0);
   return rows < 1024 ? 4 : 1;
@@ -297,6 +304,7 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   const int split = rows_split_factor(a);
   if (split == 2) return launch_split<2>(a, st, slots);
   if (split == 4) return launch_split<4>(a, st, slots);
+  if (split == 8) return launch_split<8>(a, st, slots);
   const int n_value_blocks = value_blocks(a, kWave);
   const unsigned grid = (unsigned)(slots + n_value_blocks);
   hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,

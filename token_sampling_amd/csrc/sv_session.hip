@@ -103,17 +103,18 @@ struct Verdict {
 // What lane i of a session's wave knows of position i+1 once its rows are
 // profiled: the drafted token, p_i(x_i) and q_i(x_i) where the rule reads
 // them (-1 and 1 elsewhere), and the acceptance value of rule 2 (1 elsewhere).
+// Only positions before lim are read.
 struct LanePos {
   int32_t x;
   double px, qx, u;
 };
 
 __device__ __attribute__((always_inline)) LanePos lane_position(
-    int b, int lane, int mb, int rl, const int32_t* __restrict__ tokens, int M, int V,
+    int b, int lane, int mb, int lim, int rl, const int32_t* __restrict__ tokens, int M, int V,
     const float* __restrict__ qrows, const RowRec* __restrict__ rr,
     const double* __restrict__ unif, uint64_t seed, uint64_t session_key, uint32_t round) {
   LanePos P{-1, -1.0, 1.0, 1.0};
-  if (lane >= mb) return P;
+  if (lane >= mb || lane >= lim) return P;
   P.x = tokens[(size_t)b * M + lane];  // in [0, V) once the session's checks passed
   if (rl == SV_RULE_SPECULATIVE || rl == SV_RULE_RELAXED) P.px = rr[lane].ptok;
   if (rl == SV_RULE_SPECULATIVE) {
@@ -184,15 +185,16 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   v.rl = rl;
   v.mb = mb;
   const bool draft_rows = rl == SV_RULE_SPECULATIVE && !qrows;
+  // target rows read: 1..L (the SDCP reading: every row, m+1 of them); in
+  // order, up to the decided position (all m+1 rows if still undecided)
+  const int e = (st == 0 && decided) ? decided[b] : 0;
+  const int n = e > 0 ? e : mb + 1;
   LanePos pos{-1, -1.0, 1.0, 1.0};
   if (st == 0)
-    pos = lane_position(b, lane, mb, rl, tokens, M, V, qrows, rr, unif, seed,
-                      sampling[b].session_key, round);
-  // target rows read: 1..L (the SDCP reading: every row, m+1 of them)
+    pos = lane_position(b, lane, mb, n, rl, tokens, M, V, qrows, rr, unif, seed,
+                        sampling[b].session_key, round);
   int L = mb + 1;
   if (st == 0 && decided) {
-    const int e = decided[b];
-    const int n = e > 0 ? e : mb + 1;
     const int f = inorder_end(n, mb, rl, draft_rows, rr, M, pos);
     L = f > 0 ? f : n;
   }
@@ -1168,9 +1170,9 @@ __global__ __launch_bounds__(kAdvanceNT) void k_advance(
   const int mb = m[b];
   const int rl = rule[b];
   const RowRec* rr = rows + (size_t)b * (2 * M + 1);
-  const LanePos pos = lane_position(b, lane, mb, rl, tokens, M, V, qrows, rr, unif, seed,
-                                    sampling[b].session_key, round);
   const int n = hi < mb + 1 ? hi : mb + 1;
+  const LanePos pos = lane_position(b, lane, mb, n, rl, tokens, M, V, qrows, rr, unif, seed,
+                                    sampling[b].session_key, round);
   const int f = inorder_end(n, mb, rl, rl == SV_RULE_SPECULATIVE && has_draft_logits, rr, M, pos);
   if (lane == 0) {
     if (f > 0) decided[b] = f;
