@@ -46,6 +46,18 @@ MEASURED_TRAFFIC = {
     ("b256_topk_topp", "k_rows_stream", "stream-v3"): 1_119_487_488,
     ("b256_topk_topp", "k_rows_stream", "stream-v4"): 1_119_499_072,
     ("b256_topk_topp", "k_rows_stream", "stream-v5"): 1_119_496_295,
+    ("b64", "k_rows_split<4>", "stream-v5"): 38_273_434,
+    ("ragged", "k_rows_stream", "stream-v5"): 2_450_512_384,
+    ("large", "k_rows_stream", "stream-v5"): 34_218_138_829,
+}
+# VALU busy (rocprofv3 derived counter VALUBusy: VALU cycles over GPU-busy
+# cycles per CU, percent) of the same kernels, same keys: near 100 the kernel
+# is bound by its vector ALU work rather than by HBM.
+MEASURED_VALU_BUSY = {
+    ("b64", "k_rows_split<4>", "stream-v5"): 22.2,
+    ("b256_topk_topp", "k_rows_stream", "stream-v5"): 45.6,
+    ("ragged", "k_rows_stream", "stream-v5"): 67.0,
+    ("large", "k_rows_stream", "stream-v5"): 101.5,
 }
 
 
@@ -210,6 +222,8 @@ def main():
     split = w.row_bytes_by_kernel(q_rows=args.qrows)
     kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
                           else ("k_rows_generic", generic_ms, split["generic"]))
+    if kname == "k_rows_stream" and B * (M + 1) + (B * M if draft is not None else 0) < 1024:
+        kname = "k_rows_split<4>"  # launches under 1024 row slots split each row over 4 waves
     a = out["accepted_len"].cpu()
     if args.early:
         # read in order, the rows a session needs are its first a+1 target rows
@@ -238,8 +252,9 @@ def main():
         log("[bench] copy calibration: 3 x (1 GiB read + 1 GiB written)")
 
     achieved = kbytes / (kms * 1e-3) / 1e9
-    traffic = None if (args.sdcp or args.qrows or args.early) else \
-        MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION))
+    measured = not (args.sdcp or args.qrows or args.early or args.sessions)
+    traffic = MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION)) if measured else None
+    valu_busy = MEASURED_VALU_BUSY.get((args.workload, kname, KERNEL_REVISION)) if measured else None
     result = {
         "metric": METRIC,
         "value": P / (ms_per_step * 1e-3),
@@ -266,7 +281,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "valu_busy_pct": valu_busy,
             "kernel": kname, "ms_per_launch": kms, "algorithmic_bytes_per_launch": kbytes,
             "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_generic": generic_ms},
         },
