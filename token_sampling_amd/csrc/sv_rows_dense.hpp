@@ -35,6 +35,8 @@
 // The cut is recorded as (kc, j); the sampling kernel turns j into a cut id
 // when it needs one.  The argmax is not computed: no rule reads it for these
 // profiles (greedy and temperature-0 rows take the top-k kernel).
+// row_profile_split runs the same pass over S parts of the row, one wave per
+// part, and merges the parts' windows, sums and ranks before the cut.
 #pragma once
 
 #include "sv_kernels.hpp"

@@ -1,11 +1,14 @@
-// sv_session.hip -- the per-session kernel of libspecverify.  A session
-// takes C workgroups (one per chunk of its vocabulary):
+// sv_session.hip -- the per-session kernels of libspecverify.
+// k_finalize: a session takes C workgroups (one per chunk of its vocabulary):
 //   the first wave of each takes the acceptance rule (lane i = position i+1,
 //   a 64-bit ballot for the first rejection); chunk 0's workgroup draws the
 //   additional token from listed supports and writes the session's outputs;
 //   when the rows have no listed support, the additional token is an inverse
 //   CDF over ascending token ids: each workgroup weighs its chunk, and the
 //   session's last workgroup picks the token and writes the outputs.
+// k_advance (the in-order reading, between windows of positions): one wave
+//   per undecided session finds the position that ends its round, if the
+//   rows read so far hold it.
 #include "sv_kernels.hpp"
 
 namespace sv {
