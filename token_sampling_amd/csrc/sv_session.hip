@@ -499,8 +499,9 @@ __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>&
       mq = !tq && d.Q.fixed_member(kq, y);
     }
   }
-  // no member or tie of either row in the whole wave: nothing to add
-  if (!__builtin_amdgcn_ballot_w64(mp || tp || mq || tq)) return s;
+  // no member or tie of p and no tie of q in the whole wave: nothing to add
+  // (where p is zero, a member of q changes no weight)
+  if (!__builtin_amdgcn_ballot_w64(mp || tp || tq)) return s;
   double pv = 0.0;
   if (__builtin_amdgcn_ballot_w64(mp)) {
     const double w = d.P.w(Tr::value(up));
@@ -516,7 +517,7 @@ __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>&
   if constexpr (kQ) {
     qv = (double)__uint_as_float(uq);
     qbad = !(qv >= 0.0 && qv < INFINITY);
-  } else if (__builtin_amdgcn_ballot_w64(mq)) {
+  } else if (__builtin_amdgcn_ballot_w64(mq && (mp || tp))) {
     const double w = d.Q.w(Tr::value(uq));
     qv = mq ? w : 0.0;
   }
@@ -550,8 +551,10 @@ __device__ __attribute__((always_inline)) void weigh8(const DrawCtx<Tr, kQ>& d, 
     s = weigh1<Tr, kQ>(d, resid, pr.get(e), resid ? qr.get(e) : 0u, y + e, s);
 }
 
-// Which of a lane's 8 ids are at or above a row's cut key: only those can be
-// members or ties; the others add nothing.
+// Which of a lane's 8 ids can add to a group record: ids at or above p's cut
+// key (members or ties of p), and for a residual the ties of q (counted even
+// where p is zero).  A member of q where p is zero adds nothing: every
+// residual weight, and the p mass of q's ties, is zero there.
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) uint32_t need_bits(
     const DrawCtx<Tr, kQ>& d, bool resid, const typename DrawCtx<Tr, kQ>::RawP& pr,
@@ -561,7 +564,7 @@ __device__ __attribute__((always_inline)) uint32_t need_bits(
   for (int e = 0; e < kPer; ++e) {
     bool n = Tr::key(pr.get(e)) >= d.P.kcut;
     if constexpr (!kQ)
-      if (resid) n |= Tr::key(qr.get(e)) >= d.Q.kcut;
+      if (resid) n |= d.Q.tie(Tr::key(qr.get(e)));
     need |= n ? 1u << e : 0u;
   }
   return need;
