@@ -137,9 +137,10 @@ def test_workload_in_order_in_full(name):
     parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-{name}")
 
 
-@pytest.mark.parametrize("name,sessions", [("b256_topk_topp", (0, 77, 255)),
-                                           ("ragged", (3, 200, 511)),
-                                           ("large", (0, 1023))])
+@pytest.mark.parametrize("name,sessions", [
+    ("b256_topk_topp", (0, 17, 77, 111, 160, 255)),
+    ("ragged", (3, 77, 200, 333, 444, 511)),
+    ("large", (0, 511, 1023))])
 def test_workload_full_size_in_order(name, sessions):
     """At full size: every session whose SDCP reading succeeds gets the same
     result in order (rows are all usable there), a bad proposal either stays

@@ -182,9 +182,10 @@ def test_workload_in_full(name):
     parity.compare(g, o, name)
 
 
-@pytest.mark.parametrize("name,sessions", [("b256_topk_topp", (0, 1, 77, 255)),
-                                           ("ragged", (0, 3, 200, 511)),
-                                           ("large", (0, 1023))])
+@pytest.mark.parametrize("name,sessions", [
+    ("b256_topk_topp", (0, 1, 31, 64, 77, 100, 128, 150, 190, 200, 230, 255)),
+    ("ragged", (0, 3, 50, 100, 150, 200, 250, 300, 350, 400, 450, 511)),
+    ("large", (0, 300, 700, 1023))])
 def test_workload_full_size_sampled_sessions(name, sessions):
     parity.log(f"[case] workload {name} full size, oracle on sessions {sessions}")
     w = W.make(name, device="cuda")
