@@ -65,6 +65,56 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def cpu_baseline_threads(w, budget_s: float, threads: int, early=False):
+    """The oracle on the first sessions of the workload, run by `threads` host
+    threads at once (ctypes releases the GIL during the oracle's C call), one
+    block of sessions per call.  The sample is sized from one session's time so
+    that the parallel section takes about budget_s."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+    from token_sampling_amd import workloads as W
+
+    oracle.lib()
+
+    def run(h):
+        oracle.verify(h["target"], h["draft"], h["tokens"], h["m"], h["rule"], h["sampling"],
+                      h["seed"], h["round"], diagnostics=False, early=early)
+
+    h0 = W.to_numpy(w, sessions=[0])
+    t0 = time.perf_counter()
+    run(h0)
+    per = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(w.B, max(threads, budget_s * threads / per)))
+    blocks = np.array_split(np.arange(n), threads)
+    hs = [W.to_numpy(w, sessions=list(bl)) for bl in blocks if len(bl)]
+    positions = int(sum((np.asarray(h["m"], dtype=np.int64) + 1).sum() for h in hs))
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=len(hs)) as ex:
+        list(ex.map(run, hs))
+    elapsed = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": positions / elapsed,
+        "unit": "positions/s",
+        "cores": len(hs),
+        "kind": "oracle",
+        "sample": f"sessions 0..{n - 1} of {w.name} (P={positions}) in {len(hs)} blocks, "
+                  f"{elapsed:.1f} s on {len(hs)} host threads ({model})"
+                  + (", read in order" if early else ""),
+    }
+
+
 def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None, early=False):
     """Time the oracle on the first sessions of the workload (bounded sample).
     sdcp_raw: the [B, 32] session records (numpy uint8) when SDCP values are used;
@@ -118,6 +168,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--cpu-threads", type=int, default=1,
+                    help="host threads for the CPU baseline (1: the oracle as defined, one "
+                         "core; N: blocks of sessions on N threads at once, Philox values "
+                         "and draft logits only)")
     ap.add_argument("--sessions", type=int, default=None,
                     help="diagnostic only: the workload's first N sessions instead of all")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -288,9 +342,13 @@ def main():
     }
     if args.cpu_budget > 0:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(
-            w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows,
-            early=bool(args.early))
+        if args.cpu_threads > 1 and sdcp is None and q_rows is None:
+            result["cpu_baseline"] = cpu_baseline_threads(w, args.cpu_budget, args.cpu_threads,
+                                                          early=bool(args.early))
+        else:
+            result["cpu_baseline"] = cpu_baseline(
+                w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows,
+                early=bool(args.early))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -168,3 +168,43 @@ def test_workload_full_size_in_order(name, sessions):
     parity.compare({k: v[idx] for k, v in g_all.items()}, o, f"early-{name}-sampled")
     parity.log(f"[workload] {name} in order: mean accepted {a[a >= 0].mean():.3f}, "
                f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")
+
+
+@pytest.mark.parametrize("window", [1, 2])
+def test_unusable_published_q_in_later_windows(window):
+    """Published q rows with an unusable q_j(x_j) (NaN, zero) at a position j
+    in a later window: at or before the deciding position it fails the session
+    with BAD_PROPOSAL, after it nothing changes."""
+    parity.log(f"[case] in-order unusable q entries window={window}")
+    B, M, V = 16, 8, 3000
+    rng = np.random.default_rng(14)
+    t = rng.normal(0, 1, size=(B, M + 1, V)).astype(np.float32)
+    d = (t[:, :M] + rng.normal(0, 0.3, size=(B, M, V))).astype(np.float32)
+    q = np.exp(d.astype(np.float64) - d.max(axis=-1, keepdims=True))
+    q /= q.sum(axis=-1, keepdims=True)
+    s = oracle.make_sampling(B, 1000, 0, 1000)
+    tokens = np.zeros((B, M), np.int32)
+    for b in range(B):
+        for i in range(M):
+            tokens[b, i] = rng.choice(V, p=q[b, i])
+    h = dict(target=oracle.bf16_bits(t), draft=None, q_rows=q.astype(np.float32), tokens=tokens,
+             m=np.full(B, M, np.int32), rule=np.full(B, 2, np.int32), sampling=s, seed=21,
+             round=3, early=window)
+    clean = parity.run_oracle(h)
+    a = clean["accepted_len"]
+    assert (a >= 2).sum() >= 4, "sessions reaching later windows"
+    planted = {}
+    for b in range(B):
+        e = int(a[b]) + 1
+        j = int(rng.integers(2, M + 1))  # 1-based, past the first window
+        h["q_rows"][b, j - 1, tokens[b, j - 1]] = np.nan if b % 2 else 0.0
+        planted[b] = (j, e)
+    o = parity.run_oracle(h)
+    for b, (j, e) in planted.items():
+        if j <= min(e, M):
+            assert o["accepted_len"][b] == oracle.S_BAD_PROPOSAL, (b, j, e)
+        else:
+            assert o["accepted_len"][b] == a[b], (b, j, e)
+    assert any(j <= min(e, M) for j, e in planted.values())
+    assert any(j > min(e, M) for j, e in planted.values())
+    parity.compare(parity.run_gpu(h), o, f"early-qbad-{window}")
