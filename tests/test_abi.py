@@ -34,7 +34,8 @@ def svlib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert {"sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_commit", "sv_prefix_digest",
+    assert {"sv_verify", "sv_verify_sdcp", "sv_verify_qrows", "sv_verify_early", "sv_commit",
+            "sv_prefix_digest",
             "sv_contract_digest", "sv_workspace_bytes", "sv_strerror", "sv_status_str",
             "sv_version"} <= names
 
@@ -145,6 +146,27 @@ def test_verify_qrows_rejects_bad_arguments_on_the_host(svlib):
     assert call(M=65) == svlib.ERR_ARG
     assert call(V=0) == svlib.ERR_ARG
     assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
+
+
+def test_verify_early_rejects_bad_arguments_on_the_host(svlib):
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+    ws = svlib.workspace_bytes(2, 2, 10)
+
+    def call(target=fake, draft=None, qrows=None, window0=1, B=2, M=2, V=10, wsb=ws, wsp=fake):
+        return L.sv_verify_early(target, draft, qrows, 0, fake, fake, fake, fake, None, B, M, V,
+                                 0, 1, window0, fake, fake, wsp, wsb, None, None)
+
+    assert call(window0=0) == svlib.ERR_ARG
+    assert call(window0=66) == svlib.ERR_ARG
+    assert call(draft=fake, qrows=fake) == svlib.ERR_ARG  # one draft source at most
+    assert call(target=None) == svlib.ERR_ARG
+    assert call(wsp=None) == svlib.ERR_ARG
+    assert call(B=0) == svlib.ERR_ARG
+    assert call(M=65) == svlib.ERR_ARG
+    assert call(V=0) == svlib.ERR_ARG
+    assert call(wsb=ws - 1) == svlib.ERR_WORKSPACE
+    assert call(window0=65, wsb=ws - 1) == svlib.ERR_WORKSPACE
 
 
 def header_struct_fields(name):
