@@ -218,7 +218,7 @@ int sv_verify_qrows(const void *target_logits, int32_t dtype, const float *q_row
  * target row i and, for rule 2, draft row i (or q_rows' q_i(x_i)); a
  * session's rows after the position that ends its round are never read.  The
  * rows are read in windows of positions: window0 positions first
- * (1..window0), then 2 window0, 4 window0, ... (at most 128), the last one
+ * (1..window0), then 4 window0, 16 window0, ... positions, the last one
  * ending at M+1, each window only for the sessions still undecided; fewer
  * windows cost fewer launches, smaller ones read fewer rows.
  * Statuses follow the order: the first position (1-based i <= m[b] + 1)

@@ -68,6 +68,13 @@ extern "C" size_t sv_workspace_bytes(int32_t B, int32_t M, int32_t V) {
 
 namespace sv {
 
+// Each window of the in-order reading after the first covers kWindowGrowth
+// times the positions of the one before it.
+#ifndef SV_WINDOW_GROWTH
+#define SV_WINDOW_GROWTH 4
+#endif
+constexpr int kWindowGrowth = SV_WINDOW_GROWTH;
+
 // A value per call for the rows' draw flags (never 0, so that a cleared
 // workspace matches no call).
 static uint32_t next_draw_token() {
@@ -80,7 +87,7 @@ static uint32_t next_draw_token() {
 // Shared by the entry points: sdcp == null takes the Philox values from
 // (seed, round); otherwise the SDCP Sec. 6.4 values of each session's record.
 // window0 == 0 reads every row of a session (the SDCP reading); window0 >= 1
-// reads them in order, in windows of window0, 2 window0, 4 window0, ...
+// reads them in order, in windows of window0, 4 window0, 16 window0, ...
 // positions, each window only for the sessions its predecessors left
 // undecided.
 static int verify_impl(const void* target_logits, const void* draft_logits, const float* q_rows,
@@ -141,7 +148,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
     if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
     launch_rows_generic(a, st);
   } else {
-    // windows of positions [lo, lo + w), w doubling, the last one ending at M+1
+    // windows of positions [lo, lo + w), w growing, the last one ending at M+1
     int w = window0;
     for (int lo = 1; lo <= M + 1;) {
       a.win_lo = lo;
@@ -151,7 +158,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
       const int hi = lo + a.win_w - 1;
       if (hi < M + 1) launch_advance(a, st, hi);  // after the last window: the finalize
       lo = hi + 1;
-      w = w < 64 ? 2 * w : w;
+      w = w < 64 ? kWindowGrowth * w : w;
     }
     if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
   }
