@@ -208,3 +208,14 @@ def test_unusable_published_q_in_later_windows(window):
     assert any(j <= min(e, M) for j, e in planted.values())
     assert any(j > min(e, M) for j, e in planted.values())
     parity.compare(parity.run_gpu(h), o, f"early-qbad-{window}")
+
+
+@pytest.mark.parametrize("split", ["1", "2", "8"])
+def test_in_order_with_each_split_factor(split, monkeypatch):
+    """Every window's rows streamed by 1, 2 or 8 waves (SV_ROWS_SPLIT): the
+    same result as the oracle's in-order reading, in both dtypes' paths."""
+    monkeypatch.setenv("SV_ROWS_SPLIT", split)
+    parity.log(f"[case] in-order split={split}")
+    h = mixed_case(64, 20, 6, 5003)
+    h["early"] = 1
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-split{split}")
