@@ -643,11 +643,11 @@ __device__ inline GroupAcc load_group(const GroupRec* rec) {
 
 // One wave records groups [g0, g1): steps of 8 ids per lane through a ring of
 // kSteps loads, three steps ahead.  For a row cut to a support, the wave
-// weighs queued ids when its first step has 16 to 128 ids to weigh, else in
-// place (a queue of more rounds measured slower: the 8 unrolled positions
-// overlap their binary64 chains; with fewer, in place skips the empty
-// positions anyway).  The two loops are kept apart so that each has its own
-// registers.
+// weighs queued ids when its first step has 16 to SV_QUEUE_MAX (three rounds
+// of 64) ids to weigh, else in place (with fewer, in place skips the empty
+// positions anyway; rows with more members keep the 8 unrolled positions,
+// which overlap their binary64 chains).  The two loops are kept apart so that
+// each has its own registers.
 template <class Tr, bool kQ, bool kQueued>
 __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>& d, bool resid,
                                                            int g0, int g1,
@@ -685,6 +685,9 @@ __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>
   }
 }
 
+#ifndef SV_QUEUE_MAX
+#define SV_QUEUE_MAX (3 * kWave)
+#endif
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid,
                                                              int g0, int g1, bool sparse,
@@ -698,7 +701,7 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
     d.load(g0 * kGroup + __lane_id() * kPer, resid, p0, q0);
     uint32_t total;
     (void)wave_excl_count(__builtin_popcount(need_bits<Tr, kQ>(d, resid, p0, q0)), &total);
-    queued = total >= 16 && total <= 2 * kWave;
+    queued = total >= 16 && total <= SV_QUEUE_MAX;
   }
   if (queued) record_loop<Tr, kQ, true>(d, resid, g0, g1, recs, qu);
   else record_loop<Tr, kQ, false>(d, resid, g0, g1, recs, qu);
