@@ -85,20 +85,21 @@ def test_rows_after_the_end_are_not_read(dtype):
         parity.compare(parity.run_gpu(c), o, f"early-nan-{dtype}-{window}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("window", [1, 4])
-def test_sdcp_values_and_q_rows_in_order(window):
-    parity.log(f"[case] in-order SDCP values and q rows window={window}")
-    h = mixed_case(63, 24, 5, 4000)
+def test_sdcp_values_and_q_rows_in_order(window, dtype):
+    parity.log(f"[case] in-order SDCP values and q rows window={window} dtype={dtype}")
+    h = mixed_case(63, 24, 5, 4000, dtype)
     rng = np.random.default_rng(10)
     h["sdcp"] = parity.random_sdcp_sessions(24, rng)
     h["early"] = window
-    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-sdcp-{window}")
-    d = oracle.bf16_to_float(h["draft"]).astype(np.float64)
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-sdcp-{window}-{dtype}")
+    d = (oracle.bf16_to_float(h["draft"]) if dtype == "bf16" else h["draft"]).astype(np.float64)
     q = np.exp(d - d.max(axis=-1, keepdims=True))
     q /= q.sum(axis=-1, keepdims=True)
     h["q_rows"] = q.astype(np.float32)
     h["draft"] = None
-    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-qrows-{window}")
+    parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-qrows-{window}-{dtype}")
 
 
 def test_every_position_accepted_at_m_64():
