@@ -220,3 +220,30 @@ def test_in_order_with_each_split_factor(split, monkeypatch):
     h = mixed_case(64, 20, 6, 5003)
     h["early"] = 1
     parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-split{split}")
+
+
+def test_status_order_at_one_position():
+    """In order, a bad row and a zero q_1(x_1) at position 1 give BAD_LOGITS; a
+    zero q_1(x_1) with a bad row further on gives BAD_PROPOSAL (the SDCP
+    reading gives BAD_LOGITS there)."""
+    parity.log("[case] in-order status order")
+    h = mixed_case(65, 16, 5, 3000, "fp32")
+    base = parity.run_oracle(h)
+    a = base["accepted_len"]
+    c = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in h.items()}
+    both, first = [], []
+    for b in np.nonzero((a >= 1) & (h["rule"] == 2))[0]:
+        x1 = int(h["tokens"][b, 0])
+        c["draft"][b, 0, x1] = -np.inf  # q_1(x_1) = 0
+        if len(both) <= len(first):
+            c["target"][b, 0, 11] = np.nan
+            both.append(b)
+        else:
+            c["target"][b, int(a[b]), 11] = np.nan  # the deciding row, after position 1
+            first.append(b)
+    assert both and first
+    c["early"] = 1
+    o = parity.run_oracle(c)
+    assert all(o["accepted_len"][b] == oracle.S_BAD_LOGITS for b in both)
+    assert all(o["accepted_len"][b] == oracle.S_BAD_PROPOSAL for b in first)
+    parity.compare(parity.run_gpu(c), o, "early-status-order")

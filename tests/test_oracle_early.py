@@ -156,3 +156,28 @@ def test_greedy_in_order_is_the_argmax_prefix(ora):
         assert np.array_equal(e["out_tokens"][b, :a], tokens[b, :a])
         assert e["out_tokens"][b, a] == am[b, a]
         assert (e["out_tokens"][b, a + 1:] == -1).all()
+
+
+def test_bad_row_before_unusable_q_at_one_position(ora):
+    """At one position a bad row and an unusable q_i(x_i) together fail the
+    session with BAD_LOGITS (the row is read first); an unusable q_i(x_i)
+    alone at an earlier position than a bad row gives BAD_PROPOSAL."""
+    h = mixed_case(ora, 41)
+    f = run(ora, h, False)
+    a = f["accepted_len"]
+    checked = 0
+    for b in np.nonzero((a >= 1) & (h["rule"] == 2))[0][:8]:
+        e = int(a[b]) + 1
+        x1 = int(h["tokens"][b, 0])
+        c = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in h.items()}
+        c["target"][b, 0, 7] = np.nan                 # bad target row 1
+        c["draft"][b, 0, x1] = -np.inf                # and q_1(x_1) = 0
+        assert run(ora, c, True)["accepted_len"][b] == ora.S_BAD_LOGITS
+        c = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in h.items()}
+        c["draft"][b, 0, x1] = -np.inf                # q_1(x_1) = 0 ...
+        c["target"][b, e - 1, 7] = np.nan             # ... before a bad row at e >= 2
+        assert run(ora, c, True)["accepted_len"][b] == ora.S_BAD_PROPOSAL
+        # the SDCP reading checks every row first
+        assert run(ora, c, False)["accepted_len"][b] == ora.S_BAD_LOGITS
+        checked += 1
+    assert checked >= 3
