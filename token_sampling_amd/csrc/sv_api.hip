@@ -139,6 +139,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   a.decided = window0 > 0 ? (int32_t*)(ws + L.decided_off) : nullptr;
   a.win_lo = 1;
   a.win_w = 0;
+  a.win_index = 0;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
@@ -159,6 +160,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
       if (hi < M + 1) launch_advance(a, st, hi);  // after the last window: the finalize
       lo = hi + 1;
       w = w < 64 ? kWindowGrowth * w : w;
+      ++a.win_index;
     }
     if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
   }

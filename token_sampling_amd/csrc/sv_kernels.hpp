@@ -50,6 +50,7 @@ struct LaunchArgs {
   // first window).
   int32_t* decided;  // [B]
   int32_t win_lo, win_w;
+  int32_t win_index;  // 0 for the first window
 };
 
 // Ids per group record of the draw.

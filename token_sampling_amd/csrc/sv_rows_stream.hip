@@ -261,13 +261,20 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
 #ifndef SV_LATE_SPLIT
 #define SV_LATE_SPLIT 4
 #endif
+#ifndef SV_TAIL_SPLIT
+#define SV_TAIL_SPLIT 1
+#endif
 static int rows_split_factor(const LaunchArgs& a) {
   const char* env = getenv("SV_ROWS_SPLIT");
   if (env) {
     const int s = atoi(env);
     if (s == 1 || s == 2 || s == 4 || s == 8) return s;
   }
-  // windows after the first read the few sessions left undecided
+  // In-order windows: the second holds the few sessions the first left
+  // undecided (few rows: split); the later ones are either empty, where
+  // dispatch dominates and a one-wave workgroup costs least, or hold sessions
+  // that accept long runs, with rows enough for one wave each.
+  if (a.win_w != 0 && a.win_index >= 2) return SV_TAIL_SPLIT;
   if (a.win_w != 0 && a.win_lo > 1) return SV_LATE_SPLIT;
   const int W = a.win_w == 0 ? a.M + 1 : a.win_w;  // target positions per session
   const size_t rows = (size_t)a.B * W + (a.draft ? (size_t)a.B * (W < a.M ? W : a.M) : 0);
