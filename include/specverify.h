@@ -68,17 +68,10 @@ typedef struct sv_sampling {
  *  p_tok, q_tok: DEVICE arrays [B, M] of float64, written for
  *    speculative-sampling sessions with p_i(x_i) and q_i(x_i) for i <= m[b]
  *    (every position, also past the first rejection); -1 elsewhere and for
- *    greedy or failed sessions.
- *  rows_start, rows_mid, rows_stop: hipEvent_t handles recorded on the
- *    launch stream immediately before the row-profile kernels (the step's
- *    HBM-streaming part), between the single-pass top-k kernel and the
- *    kernel for the other rows, and after them, for timing each. */
+ *    greedy or failed sessions. */
 typedef struct sv_probe {
   double *p_tok;
   double *q_tok;
-  void *rows_start;
-  void *rows_mid;
-  void *rows_stop;
 } sv_probe;
 
 /* Per-session inputs of the SDCP verifier values (Sec. 6.4), 32 bytes, 8-byte
@@ -97,8 +90,9 @@ typedef struct sv_sdcp_session {
 
 /* Acceptance rules: 1 and 2 are SDCP's (Sec. 6.4, registry Sec. 10.2.2).  192,
  * from the registry's private-use range (192-255), is the relaxed rule of the
- * textbook chapter ("Speculative decoding": accept a token in the target's
- * top-k, no longer sampling from p): x_i is accepted while p_i(x_i) > 0, i.e.
+ * textbook chapter (section "Speculative decoding": acceptance by membership
+ * of the target's top-k, which gives up sampling exactly from p); read as:
+ * x_i is accepted while p_i(x_i) > 0, i.e.
  * while the target's profile could sample it (with top-k alone, membership of
  * the target's top-k); the additional token is drawn from p_{a+1} with the
  * purpose-1 value of position a+1; no draft row or q is read; the probe's
@@ -327,6 +321,16 @@ int sv_prefix_digest(const uint8_t *contract_digest, const int32_t *prompt, uint
  * over the contract's deterministic CBOR encoding supplied by the caller.
  * HOST memory; runs on the host.  Returns SV_OK or SV_ERR_ARG. */
 int sv_contract_digest(const uint8_t *cbor, size_t len, uint8_t *out);
+
+/* Benchmark hook, not part of the acceptance step: hipEvent_t handles that
+ * the sv_verify* calls made afterwards from the calling host thread record on
+ * their launch stream, immediately before the row-profile kernels (start),
+ * between the single-pass kernel and the kernel for the other rows (mid; read
+ * in order: after the last window's kernels), and after them (stop), once per
+ * call.  A NULL handle leaves its slot unrecorded; three NULLs turn the hook
+ * off.  The caller owns the events and keeps them alive while it is on.
+ * Returns SV_OK. */
+int sv_bench_row_events(void *start, void *mid, void *stop);
 
 /* Text for an sv_verify return code; never NULL. */
 const char *sv_strerror(int code);

@@ -8,8 +8,8 @@ Cases: mixed profiles and rules in both dtypes with several first windows;
 NaN rows after the deciding position (never read) and at or before it
 (BAD_LOGITS); SDCP values and published q rows; m = 64 sessions that accept
 every position (the additional token's row is position 65); the workloads in
-full or, at full size, the same result as sv_verify for every session whose
-rows are all usable and the oracle on sampled sessions.
+full and, at full size, the same result as sv_verify for every session whose
+rows are all usable and every session against the oracle.
 """
 import numpy as np
 import pytest
@@ -138,15 +138,13 @@ def test_workload_in_order_in_full(name):
     parity.compare(parity.run_gpu(h), parity.run_oracle(h), f"early-{name}")
 
 
-@pytest.mark.parametrize("name,sessions", [
-    ("b256_topk_topp", (0, 17, 77, 111, 160, 255)),
-    ("ragged", (3, 77, 200, 333, 444, 511)),
-    ("large", (0, 511, 1023))])
-def test_workload_full_size_in_order(name, sessions):
+@pytest.mark.parametrize("name", ["b256_topk_topp", "ragged", "large"])
+def test_workload_full_size_in_order(name):
     """At full size: every session whose SDCP reading succeeds gets the same
     result in order (rows are all usable there), a bad proposal either stays
-    one or is not reached; sampled sessions against the oracle."""
-    parity.log(f"[case] in-order workload {name} full size, oracle on sessions {sessions}")
+    one or is not reached; every session against the oracle's in-order
+    reading."""
+    parity.log(f"[case] in-order workload {name} full size, every session")
     import token_sampling_amd as sv
     w = W.make(name, device="cuda")
     args = (w.target, w.draft, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"), w.seed, w.round)
@@ -160,13 +158,10 @@ def test_workload_full_size_in_order(name, sessions):
     assert np.array_equal(g_all["out_tokens"][ok], full["out_tokens"][ok])
     assert np.all((a_full[~ok] == oracle.S_BAD_PROPOSAL) & ((a[~ok] == oracle.S_BAD_PROPOSAL)
                                                            | (a[~ok] >= 0)))
-    idx = np.array(sessions)
-    sub = W.to_numpy(w, sessions=torch.as_tensor(idx, device="cuda"))
-    del w, out, args
-    torch.cuda.empty_cache()
-    sub["early"] = 1
-    o = parity.run_oracle(sub)
-    parity.compare({k: v[idx] for k, v in g_all.items()}, o, f"early-{name}-sampled")
+    del args, out
+    o = parity.run_oracle_sessions(w, early=True)
+    rep = parity.compare(g_all, o, f"early-{name}-full")
+    assert rep["sessions"] == w.B
     parity.log(f"[workload] {name} in order: mean accepted {a[a >= 0].mean():.3f}, "
                f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")
 

@@ -4,7 +4,7 @@ oracle's q_rows mode on the same inputs, to the same bar as the other parity
 tests.  Covers the listed-support residual (q gathered at the target's listed
 support), the whole-row residual of the per-session sampler, the entries the
 rule reads and the ones it must ignore, SDCP values, and the b256 and ragged
-workloads at full size on sampled sessions."""
+workloads at full size on every session."""
 import numpy as np
 import pytest
 import torch
@@ -126,28 +126,28 @@ def test_qrows_with_sdcp_values():
     parity.compare(parity.run_gpu(h), parity.run_oracle(h), "qrows-sdcp")
 
 
-@pytest.mark.parametrize("name,sessions", [("b256_topk_topp", (0, 5, 130, 255)),
-                                           ("ragged", (1, 2, 300, 511))])
-def test_qrows_workload_full_size_sampled_sessions(name, sessions):
+@pytest.mark.parametrize("name", ["b256_topk_topp", "ragged"])
+def test_qrows_workload_full_size_every_session(name):
     """The workload's target rows with the synthetic drafter's published rows
-    (its top-8 at temperature T, the distribution its tokens were drawn from)."""
-    parity.log(f"[case] qrows workload {name} full size, oracle on sessions {sessions}")
+    (its top-8 at temperature T, the distribution its tokens were drawn from),
+    every session against the oracle."""
+    parity.log(f"[case] qrows workload {name} full size, every session")
     w = W.make(name, device="cuda")
     q = w.drafter_q_rows()
     import token_sampling_amd as sv
     out = sv.verify(w.target, None, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"), w.seed,
                     w.round, probe=True, q_rows=q)
     torch.cuda.synchronize()
-    g_all = {k: v.cpu().numpy() for k, v in out.items()}
-    a = g_all["accepted_len"]
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    a = g["accepted_len"]
     assert (a >= 0).all()  # every token was drawn from its published row
-    idx = np.array(sessions)
-    sub = W.to_numpy(w, sessions=torch.as_tensor(idx, device="cuda"))
-    sub["draft"] = None
-    sub["q_rows"] = q[torch.as_tensor(idx, device="cuda")].cpu().numpy()
-    del w, out, q
-    torch.cuda.empty_cache()
-    o = parity.run_oracle(sub)
-    g = {k: v[idx] for k, v in g_all.items()}
-    parity.compare(g, o, f"qrows-{name}-sampled")
+    del out
+
+    def with_q(ids, h):
+        h["draft"] = None
+        h["q_rows"] = q[torch.as_tensor(ids, device="cuda")].cpu().numpy()
+
+    o = parity.run_oracle_sessions(w, extra=with_q)
+    rep = parity.compare(g, o, f"qrows-{name}-full")
+    assert rep["sessions"] == w.B
     parity.log(f"[workload] {name} with q rows: mean accepted {a.mean():.3f}")

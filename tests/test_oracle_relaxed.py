@@ -1,6 +1,7 @@
 """Pins for the oracle's relaxed rule (rule 192, a private-use value of the
-SDCP rule registry, Sec. 10.2.2): the textbook's "accept if the token is in
-the target's top-k" ("Speculative decoding"), read as: accept x_i while
+SDCP rule registry, Sec. 10.2.2): relaxed acceptance by membership of the
+target's top-k (textbook "Inference: KV Cache, Batching, Speculative
+Decoding", section "Speculative decoding"), read as: accept x_i while
 p_i(x_i) > 0, then draw the additional token from p_{a+1} with the purpose-1
 value of position a+1.
 

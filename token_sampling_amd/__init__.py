@@ -64,7 +64,7 @@ STATE_DTYPE = np.dtype(
 EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows",
             "sv_verify_early", "sv_commit",
             "sv_prefix_digest", "sv_contract_digest", "sv_strerror", "sv_status_str",
-            "sv_version")
+            "sv_version", "sv_bench_row_events")
 
 
 class SvError(RuntimeError):
@@ -72,13 +72,11 @@ class SvError(RuntimeError):
 
 
 class _Probe(ctypes.Structure):
-    _fields_ = [("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p),
-                ("rows_start", ctypes.c_void_p), ("rows_mid", ctypes.c_void_p),
-                ("rows_stop", ctypes.c_void_p)]
+    _fields_ = [("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p)]
 
 
 class HipEvent:
-    """A raw hipEvent_t (for the probe's row-kernel timing slots)."""
+    """A raw hipEvent_t (for the benchmark hook's row-kernel timing slots)."""
 
     _hip = None
 
@@ -169,6 +167,8 @@ def lib():
         L.sv_status_str.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
         L.sv_version.restype = ctypes.c_int
+        L.sv_bench_row_events.argtypes = [ctypes.c_void_p] * 3
+        L.sv_bench_row_events.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -338,7 +338,8 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     [B, M+1] (int32), plus p_tok and q_tok [B, M] float64 if probe.  The call
     is asynchronous on ``stream`` (default: torch's current stream).
     row_events: optional (start, stop) or (start, mid, stop) HipEvents recorded
-        around the row kernels, mid between the single-pass kernel and the other.
+        around the row kernels, mid between the single-pass kernel and the other
+        (the library's benchmark hook, sv_bench_row_events, set for this call).
     sdcp_sessions: optional [B, 32] uint8 device array (see make_sdcp_sessions);
         then the SDCP Sec. 6.4 values are used and seed, round_ are ignored.
     q_rows: optional [B, M, V] float32 draft distributions (SDCP q_rows) in place
@@ -396,15 +397,12 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
             out["p_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
             out["q_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
     pr = None
-    if "p_tok" in out or row_events is not None:
-        evs = [None, None, None]
-        if row_events is not None:
-            if len(row_events) == 2:
-                evs = [row_events[0].handle, None, row_events[1].handle]
-            else:
-                evs = [e.handle for e in row_events]
-        pr = ctypes.byref(_Probe(out["p_tok"].data_ptr() if "p_tok" in out else None,
-                                 out["q_tok"].data_ptr() if "q_tok" in out else None, *evs))
+    if "p_tok" in out:
+        pr = ctypes.byref(_Probe(out["p_tok"].data_ptr(), out["q_tok"].data_ptr()))
+    evs = None
+    if row_events is not None:
+        evs = ([row_events[0].handle, None, row_events[1].handle] if len(row_events) == 2
+               else [e.handle for e in row_events])
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     common = (target.data_ptr(), None if draft is None else draft.data_ptr(), dt,
@@ -413,6 +411,19 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
             workspace.data_ptr(), workspace.numel() * workspace.element_size(), pr,
             stream.cuda_stream)
     sess = None if sdcp_sessions is None else sdcp_sessions.data_ptr()
+    if evs is not None:
+        lib().sv_bench_row_events(*evs)
+    try:
+        rc, name = _call(common, tail, target, q_rows, dt, sess, B, M, V, seed, round_, early)
+    finally:
+        if evs is not None:
+            lib().sv_bench_row_events(None, None, None)
+    if rc != OK:
+        raise SvError(f"{name} failed: {strerror(rc)} ({rc})")
+    return out
+
+
+def _call(common, tail, target, q_rows, dt, sess, B, M, V, seed, round_, early):
     if early is not None:
         name = "sv_verify_early"
         rc = lib().sv_verify_early(target.data_ptr(), common[1],
@@ -422,12 +433,10 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
         name = "sv_verify_qrows"
         rc = lib().sv_verify_qrows(target.data_ptr(), dt, q_rows.data_ptr(), *common[3:], sess,
                                    B, M, V, seed, round_, *tail)
-    elif sdcp_sessions is None:
+    elif sess is None:
         name = "sv_verify"
         rc = lib().sv_verify(*common, B, M, V, seed, round_, *tail)
     else:
         name = "sv_verify_sdcp"
         rc = lib().sv_verify_sdcp(*common, sess, B, M, V, *tail)
-    if rc != OK:
-        raise SvError(f"{name} failed: {strerror(rc)} ({rc})")
-    return out
+    return rc, name

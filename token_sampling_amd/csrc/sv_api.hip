@@ -75,6 +75,9 @@ namespace sv {
 #endif
 constexpr int kWindowGrowth = SV_WINDOW_GROWTH;
 
+// The benchmark hook's events (sv_bench_row_events), per host thread.
+static thread_local hipEvent_t g_row_ev[3] = {nullptr, nullptr, nullptr};
+
 // A value per call for the rows' draw flags (never 0, so that a cleared
 // workspace matches no call).
 static uint32_t next_draw_token() {
@@ -143,10 +146,10 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
-  if (probe && probe->rows_start) (void)hipEventRecord((hipEvent_t)probe->rows_start, st);
+  if (g_row_ev[0]) (void)hipEventRecord(g_row_ev[0], st);
   if (window0 == 0) {
     launch_rows_stream(a, st);
-    if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
+    if (g_row_ev[1]) (void)hipEventRecord(g_row_ev[1], st);
     launch_rows_generic(a, st);
   } else {
     // windows of positions [lo, lo + w), w growing, the last one ending at M+1
@@ -162,9 +165,9 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
       w = w < 64 ? kWindowGrowth * w : w;
       ++a.win_index;
     }
-    if (probe && probe->rows_mid) (void)hipEventRecord((hipEvent_t)probe->rows_mid, st);
+    if (g_row_ev[1]) (void)hipEventRecord(g_row_ev[1], st);
   }
-  if (probe && probe->rows_stop) (void)hipEventRecord((hipEvent_t)probe->rows_stop, st);
+  if (g_row_ev[2]) (void)hipEventRecord(g_row_ev[2], st);
   launch_finalize(a, st);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
   return SV_OK;
@@ -218,6 +221,13 @@ extern "C" int sv_verify_early(const void* target_logits, const void* draft_logi
   return sv::verify_impl(target_logits, draft_logits, q_rows, dtype, draft_tokens, m, rule,
                          sampling, sessions, B, M, V, seed, round, accepted_len, out_tokens,
                          workspace, workspace_bytes, probe, stream, window0);
+}
+
+extern "C" int sv_bench_row_events(void* start, void* mid, void* stop) {
+  sv::g_row_ev[0] = (hipEvent_t)start;
+  sv::g_row_ev[1] = (hipEvent_t)mid;
+  sv::g_row_ev[2] = (hipEvent_t)stop;
+  return SV_OK;
 }
 
 extern "C" const char* sv_strerror(int code) {

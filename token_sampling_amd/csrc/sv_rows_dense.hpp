@@ -5,16 +5,22 @@
 // One wave64 streams one row through a ring of 1 KiB tiles (as the top-k
 // kernel does) and computes, in that single pass:
 //  - the largest logit lmax;
-//  - Z = sum over the row of 2^((l - lmax) * s), s = log2(e) / T rounded to
-//    binary32; the whole row (Z, the histogram masses, the drafted token's
-//    probability, the sampler's weights) uses this same s, so its profile is
-//    the softmax at a temperature within half a binary32 ulp of T.  Each lane
-//    keeps an integer exponent offset q and its sum of 2^(l*s - q) (one fma
-//    and one exp2 per logit); a vector's 8 terms are summed in binary32 and
-//    added to the lane's binary64 sum.  q is set at the lane's first finite
-//    logit and moves up (by an exact power-of-two rescale of the sum) only
-//    when a logit exceeds it by 32 octaves, so terms stay below 2^32; the
-//    lanes combine in binary64 in a fixed order.
+//  - Z = sum over the row of 2^((l - lmax) * s), s = log2(e) / T.  Every
+//    weight, mass and probability of the row is taken in binary64 at this s
+//    (the profile is the softmax at T itself).  The one pass sums in binary32
+//    at sf, s rounded to binary32: each lane keeps an integer exponent offset
+//    q and its sum of 2^(l*sf - q) (one fma and one exp2 per logit); a
+//    vector's 8 terms are summed pairwise in binary32 and added to the lane's
+//    binary64 sum.  q is set at the lane's first finite logit and moves up (by
+//    an exact power-of-two rescale) when a logit passes it by one octave, so
+//    the rounded exponent of the lane's largest terms stays below 2 in
+//    magnitude; the lanes combine in binary64 in a fixed order.  Z then drops
+//    the scale's rounding: rows with a histogram (below) replace the window's
+//    share of the sum by its exact binary64 mass at s (the window holds the
+//    row's largest logits, the tokens below it weigh at least 2^-8 octaves
+//    less); untruncated rows also sum w * l per lane, and add the first-order
+//    term ln2 (s - sf) sum w (l - lmax) (|s - sf| <= 2^-24 s, so the second
+//    order is below 1e-11 for every term above 2^-60 of the row's largest).
 //    A NaN anywhere makes Z NaN; +inf makes it NaN or infinite.
 //  - with top-k or top-p: a count histogram of the kWin keys at and below the
 //    running maximum, in LDS, indexed by key mod kWin.  When the maximum
@@ -68,12 +74,30 @@ __device__ inline float value_of(int key) {
   return __uint_as_float(bits << 16);
 }
 
+// The row's scales: s for every binary64 weight, sf (s rounded to binary32)
+// for the one-pass sum.
+struct Scales {
+  double s;      // log2(e) * 1000 / temperature_milli
+  double d;      // s - sf (exact)
+  float sf;
+  float inv_sf;  // 1 / sf, rounded: only the lanes' offset thresholds use it
+};
+__device__ inline Scales row_scales(uint32_t t_milli) {
+  Scales c;
+  c.s = 1.4426950408889634074 * 1000.0 / (double)t_milli;
+  c.sf = (float)c.s;
+  c.d = c.s - (double)c.sf;
+  c.inv_sf = 1.0f / c.sf;
+  return c;
+}
+
 struct LaneSum {
-  float mv;  // this lane's largest logit so far (-inf: none finite yet)
-  float q;   // exponent offset: an integer, at most 32 below mv * s
-  float vt;  // logits above vt move q up (-inf until the first finite logit)
-  double s;  // sum of 2^(l * s - q) over this lane's logits so far
-  bool ovf;  // a logit too large for binary32 exponents: the row falls back
+  float mv;   // this lane's largest logit so far (-inf: none finite yet)
+  float q;    // exponent offset: an integer, at most one octave below mv * sf
+  float vt;   // logits above vt move q up (-inf until the first finite logit)
+  double s;   // sum of 2^(l * sf - q) over this lane's logits so far
+  double l1;  // untruncated rows: sum of 2^(l * sf - q) * l (the scale's correction)
+  bool ovf;   // a logit too large for binary32 exponents: the row falls back
 };
 
 struct Hist {
@@ -86,11 +110,13 @@ struct Hist {
 };
 
 // One 16-byte vector (8 logits) of a tile: the lane's maximum and running sum,
-// then (top-k and top-p rows) the histogram window and the drafted token's rank.  p0 is
-// the window position of the vector's first logit; xvec says (wave-uniform)
-// whether the drafted token lies in this vector of the wave.
-__device__ inline void dense_vec(LaneSum& L, Hist& H, bool hist, const u32x4& v, int p0, int px,
-                                 bool xvec, float scale_f, double scale) {
+// then (kHist: top-k and top-p rows) the histogram window and the drafted
+// token's rank.  p0 is the window position of the vector's first logit; xvec
+// says (wave-uniform) whether the drafted token lies in this vector of the wave.
+template <bool kHist>
+__device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist& H,
+                                                                const u32x4& v, int p0, int px,
+                                                                bool xvec, const Scales& sc) {
   float f[8];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
@@ -102,20 +128,29 @@ __device__ inline void dense_vec(LaneSum& L, Hist& H, bool hist, const u32x4& v,
 #pragma unroll
   for (int e = 1; e < 8; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
   L.mv = fmaxf(L.mv, lmv);
-  if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or 32 octaves up
-    const float qn = ceilf(lmv * scale_f);
+  if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or an octave up
+    const float qn = ceilf(lmv * sc.sf);
     L.ovf |= !(qn < 0x1p22f);
     // a power-of-two rescale is exact; NaN from earlier logits stays NaN
-    L.s = L.vt == -__builtin_huge_valf() ? (L.s != L.s ? L.s : 0.0) : ldexp(L.s, (int)(L.q - qn));
+    const bool first = L.vt == -__builtin_huge_valf();
+    L.s = first ? (L.s != L.s ? L.s : 0.0) : ldexp(L.s, (int)(L.q - qn));
+    if constexpr (!kHist) L.l1 = first ? (L.l1 != L.l1 ? L.l1 : 0.0) : ldexp(L.l1, (int)(L.q - qn));
     L.q = qn;
-    L.vt = (qn + 32.0f) / scale_f;
+    L.vt = (qn + 1.0f) * sc.inv_sf;
   }
-  float ts = 0.0f;
+  float w[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ts += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], scale_f, -L.q));
-  L.s += (double)ts;
-
-  if (!hist) return;
+  for (int e = 0; e < 8; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+  L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
+  if constexpr (!kHist) {
+    // w * l, with -inf logits (weight 0) taken as the largest negative finite
+    // value so that they add 0; a NaN logit has a NaN weight and stays NaN
+    float tl = w[0] * fmaxf(f[0], -__FLT_MAX__);
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tl = __builtin_fmaf(w[e], fmaxf(f[e], -__FLT_MAX__), tl);
+    L.l1 += (double)tl;
+    return;
+  }
   if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
     int tk = skey_of(lmv);
 #pragma unroll
@@ -166,13 +201,13 @@ __device__ inline RowWin row_window(const uint16_t* row, int V) {
 }
 
 // The pass over tiles [t0, t1) of the window, by one wave: its lanes' running
-// maxima and sums (L), and with hist its histogram window (H) and, when the
+// maxima and sums (L), and with kHist its histogram window (H) and, when the
 // drafted token lies in these tiles, the token's rank among the tokens of its
 // key before it in these tiles.  Positions from t1's first on read as -inf.
+template <bool kHist>
 __device__ __attribute__((always_inline)) inline void stream_part(const RowWin& W, int t0, int t1,
-                                                                  bool hist, int px, float scale_f,
-                                                                  double scale, LaneSum& L,
-                                                                  Hist& H) {
+                                                                  int px, const Scales& sc,
+                                                                  LaneSum& L, Hist& H) {
   const int lane = __lane_id();
   const int hi = min(W.npos, t1 * kTile);
   const int xv = px >= 0 ? px / (kWave * 8) : -1;  // the drafted token's vector index
@@ -192,19 +227,35 @@ __device__ __attribute__((always_inline)) inline void stream_part(const RowWin& 
       if ((tt == 0 && W.head > 0) || (tt + 1) * kTile > hi) mask_tile<kVec>(ring[u], tt, W.head, hi);
 #pragma unroll
       for (int j = 0; j < kVec; ++j)
-        dense_vec(L, H, hist, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
-                  tt * kVec + j == xv, scale_f, scale);
+        dense_vec<kHist>(L, H, ring[u][j], tt * kTile + j * (kWave * 8) + lane * 8, px,
+                         tt * kVec + j == xv, sc);
     }
   }
 }
 
-// This wave's share of Z relative to lmax * s (lanes combined in a fixed order).
-__device__ inline double wave_z(const LaneSum& L, float lmax, double scale) {
-  const double ref = (double)lmax * scale;  // exact: both factors are binary32
-  double z = L.vt == -__builtin_huge_valf() ? L.s : L.s * exp2((double)L.q - ref);
+__device__ inline LaneSum lane_sum_init() {
+  return LaneSum{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, 0.0, false};
+}
+
+// This wave's sums relative to lmax * sf (lanes combined in a fixed order):
+// z = sum of 2^((l - lmax) sf), and (untruncated rows) c = sum of
+// 2^((l - lmax) sf) (l - lmax), the first-order term of the scale's rounding.
+struct WaveZ {
+  double z, c;
+};
+template <bool kHist>
+__device__ inline WaveZ wave_z(const LaneSum& L, float lmax, float sf) {
+  const double ref = (double)lmax * (double)sf;  // exact: both factors are binary32
+  const bool none = L.vt == -__builtin_huge_valf();  // no finite logit in this lane
+  const double f = none ? 1.0 : exp2((double)L.q - ref);
+  double z = L.s * f;
+  double c = kHist ? 0.0 : (none ? L.l1 : (L.l1 - (double)lmax * L.s) * f);
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) z += __shfl_xor(z, off, kWave);
-  return z;
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    z += __shfl_xor(z, off, kWave);
+    c += __shfl_xor(c, off, kWave);
+  }
+  return WaveZ{z, c};
 }
 
 __device__ inline float wave_max(float v) {
@@ -213,26 +264,36 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V, int32_t x, float xval, float lmax,
-                              double z, bool ovf, const Hist& H, RowRec* rec);
+template <bool kHist>
+__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V,
+                                                             int32_t x, float xval, float lmax,
+                                                             WaveZ z, bool ovf, const Hist& H,
+                                                             RowRec* rec);
+
+__device__ inline bool row_has_hist(const sv_sampling& smp, int V) {
+  return smp.top_p_milli < 1000 || (smp.top_k > 0 && smp.top_k < (uint32_t)V);
+}
 
 // The profile of one row of the dense class, by one wave: temperature > 0,
 // top-k off or above 64, with or without top-p.  bins is the wave's LDS
 // histogram of kWin counts.  Returns true if the row is handed back.
-__device__ __attribute__((always_inline)) inline bool row_profile(
+template <bool kHist>
+__device__ __attribute__((always_inline)) inline bool row_profile_t(
     const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
-  const bool hist = smp.top_p_milli < 1000 || (smp.top_k > 0 && smp.top_k < (uint32_t)V);
-  // the row's scale: log2(e) / T rounded to binary32, used everywhere below
-  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
-  const double scale = (double)scale_f;
+  const Scales sc = row_scales(smp.temperature_milli);
   const RowWin W = row_window(row, V);
   const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
-  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
+  LaneSum L = lane_sum_init();
   Hist H{bins, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), x >= 0 ? skey_of(xval) : 0, 0};
-  stream_part(W, 0, W.ntiles, hist, x >= 0 ? x + W.head : -1, scale_f, scale, L, H);
+  stream_part<kHist>(W, 0, W.ntiles, x >= 0 ? x + W.head : -1, sc, L, H);
   const float lmax = wave_max(L.mv);
-  const double z = wave_z(L, lmax, scale);
-  return finish(smp, V, x, xval, lmax, z, __ballot(L.ovf) != 0, H, rec);
+  return finish<kHist>(smp, V, x, xval, lmax, wave_z<kHist>(L, lmax, sc.sf), __ballot(L.ovf) != 0, H,
+                       rec);
+}
+__device__ __attribute__((always_inline)) inline bool row_profile(
+    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
+  return row_has_hist(smp, V) ? row_profile_t<true>(row, V, smp, x, rec, bins)
+                              : row_profile_t<false>(row, V, smp, x, rec, bins);
 }
 
 // What each wave of a split row leaves for the merge.
@@ -241,7 +302,7 @@ struct PartRec {
   int anchor;  // the part's histogram window is [anchor - kWin + 1, anchor]
   int nx;      // tokens of the drafted token's key: before it (its own part), or all
   int ovf;
-  double z;    // the part's sum relative to the row's lmax * s
+  double z, c;  // the part's sums relative to the row's lmax * sf (see WaveZ)
 };
 
 // The same profile with the row split over the S waves of a workgroup, for
@@ -253,30 +314,28 @@ struct PartRec {
 // the sums of those bins.  Z is the parts' sums relative to the row's maximum,
 // added in part order.  Called by every wave of the workgroup (it has
 // workgroup barriers); returns true (in wave 0) if the row is handed back.
-template <int S>
-__device__ __attribute__((always_inline)) inline bool row_profile_split(
+template <int S, bool kHist>
+__device__ __attribute__((always_inline)) inline bool row_profile_split_t(
     const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins_all,
     PartRec* parts, int wid) {
   const int lane = __lane_id();
-  const bool hist = smp.top_p_milli < 1000 || (smp.top_k > 0 && smp.top_k < (uint32_t)V);
-  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
-  const double scale = (double)scale_f;
+  const Scales sc = row_scales(smp.temperature_milli);
   const RowWin W = row_window(row, V);
   const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
   const int kx = x >= 0 ? skey_of(xval) : 0;
   const int px = x >= 0 ? x + W.head : -1;
   const int t0 = wid * W.ntiles / S, t1 = (wid + 1) * W.ntiles / S;
   const bool x_here = px >= 0 && px / kTile >= t0 && px / kTile < t1;
-  LaneSum L{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, false};
+  LaneSum L = lane_sum_init();
   Hist H{bins_all + wid * kWin, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), kx, 0};
-  stream_part(W, t0, t1, hist, x_here ? px : -1, scale_f, scale, L, H);
+  stream_part<kHist>(W, t0, t1, x_here ? px : -1, sc, L, H);
   const float lm = wave_max(L.mv);
   const bool ovf = __ballot(L.ovf) != 0;
   // tokens of the drafted token's key: before it in its part, all of them in
   // a part before it (when the key lies in the part's window)
   int nx = 0;
   if (x_here) nx = H.rank_x;
-  else if (x >= 0 && hist && kx <= H.anchor && kx > H.anchor - kWin)
+  else if (x >= 0 && kHist && kx <= H.anchor && kx > H.anchor - kWin)
     nx = (int)H.bin[kx & (kWin - 1)];
   if (lane == 0) {
     parts[wid].lmax = lm;
@@ -288,20 +347,24 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split(
   float lmax = parts[0].lmax;
 #pragma unroll
   for (int w = 1; w < S; ++w) lmax = fmaxf(lmax, parts[w].lmax);
-  const double zw = wave_z(L, lmax, scale);
-  if (lane == 0) parts[wid].z = zw;
+  const WaveZ zw = wave_z<kHist>(L, lmax, sc.sf);
+  if (lane == 0) {
+    parts[wid].z = zw.z;
+    parts[wid].c = zw.c;
+  }
   __syncthreads();  // every part's sum and histogram are complete
   if (wid != 0) return false;
-  double z = parts[0].z;
+  WaveZ z{parts[0].z, parts[0].c};
   int anc = parts[0].anchor, any_ovf = parts[0].ovf;
 #pragma unroll
   for (int w = 1; w < S; ++w) {
-    z += parts[w].z;
+    z.z += parts[w].z;
+    z.c += parts[w].c;
     anc = max(anc, parts[w].anchor);
     any_ovf |= parts[w].ovf;
   }
   Hist M{bins_all, anc, value_of(anc), value_of(max(anc - (kWin - 1), kNegInfKey + 1)), kx, 0};
-  if (hist) {
+  if constexpr (kHist) {
     // the row's window: bin i holds key k = anc - ((anc - i) mod kWin)
     for (int i = lane; i < kWin; i += kWave) {
       const int k = anc - ((anc - i) & (kWin - 1));
@@ -322,20 +385,31 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split(
       }
     }
   }
-  return finish(smp, V, x, xval, lmax, z, any_ovf != 0, M, rec);
+  return finish<kHist>(smp, V, x, xval, lmax, z, any_ovf != 0, M, rec);
 }
 
-// After the pass: the row's record from its maximum, Z, the overflow flag and
-// the histogram window H (with the drafted token's key and rank).  Returns
+template <int S>
+__device__ __attribute__((always_inline)) inline bool row_profile_split(
+    const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins_all,
+    PartRec* parts, int wid) {
+  return row_has_hist(smp, V)
+             ? row_profile_split_t<S, true>(row, V, smp, x, rec, bins_all, parts, wid)
+             : row_profile_split_t<S, false>(row, V, smp, x, rec, bins_all, parts, wid);
+}
+
+// After the pass: the row's record from its maximum, the one-pass sums, the
+// overflow flag and the histogram window H (with the drafted token's key and
+// rank).  Every weight here is binary64 at the row's true scale s.  Returns
 // true if the row is handed back.
-__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V, int32_t x, float xval, float lmax,
-                              double z, bool ovf, const Hist& H, RowRec* rec) {
+template <bool kHist>
+__device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V,
+                                                             int32_t x, float xval, float lmax,
+                                                             WaveZ zc, bool ovf, const Hist& H,
+                                                             RowRec* rec) {
   const int lane = __lane_id();
   const bool top_p = smp.top_p_milli < 1000;
   const bool top_k = smp.top_k > 0 && smp.top_k < (uint32_t)V;
-  const bool hist = top_p || top_k;
-  const float scale_f = (float)(1.4426950408889634074 * 1000.0 / (double)smp.temperature_milli);
-  const double scale = (double)scale_f;
+  const Scales sc = row_scales(smp.temperature_milli);
   const uint32_t* bins = H.bin;
   if (ovf) {  // logits beyond binary32 exponent range: handed back
     return true;
@@ -344,18 +418,20 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
   RowRec rr{};
   rr.argmax = -1;
   rr.lmax = lmax;
-  rr.scale = scale;
+  rr.scale = sc.s;
   rr.ptok = -1.0;
-  const bool bad = !(z == z) || z == __builtin_huge_val() || lmax == __builtin_huge_valf() ||
-                   lmax == -__builtin_huge_valf();
+  const bool bad = !(zc.z == zc.z) || zc.z == __builtin_huge_val() || !(zc.c == zc.c) ||
+                   lmax == __builtin_huge_valf() || lmax == -__builtin_huge_valf();
   if (bad) {
     rr.status = SV_S_BAD_LOGITS;
     rr.zsum = 1.0;
     if (lane == 0) *rec = rr;
     return false;
   }
-  const double wx = x >= 0 ? weight64(xval, lmax, scale) : 0.0;
-  if (!hist) {  // the support is every finite logit
+  const double wx = x >= 0 ? weight64(xval, lmax, sc.s) : 0.0;
+  if constexpr (!kHist) {  // the support is every finite logit
+    // Z at s: the one-pass sum at sf and its first-order correction
+    const double z = zc.z + 0.69314718055994530942 * sc.d * zc.c;
     rr.kcut = Bf16::kNegInfKey + 1;
     rr.idcut = 0x7FFFFFFF;
     rr.zsum = z;
@@ -364,13 +440,29 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
     return false;
   }
 
-  // the window's counts: lane q holds the bins of keys anchor - kPerLane*q - e
+  // the window's counts: lane q holds the bins of keys anchor - kPerLane*q - e;
+  // and the window's mass at sf and at s
   uint32_t cnt[kPerLane];
+  double win_f = 0.0, win_s = 0.0;
+  const double lref = (double)lmax;
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) {
     const int k = H.anchor - kPerLane * lane - e;
     cnt[e] = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
+    if (cnt[e]) {
+      const double dl = (double)value_of(k) - lref;  // exact
+      win_f += (double)cnt[e] * exp2(dl * (double)sc.sf);
+      win_s += (double)cnt[e] * exp2(dl * sc.s);
+    }
   }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    win_f += __shfl_xor(win_f, off, kWave);
+    win_s += __shfl_xor(win_s, off, kWave);
+  }
+  // Z at s: the window's share of the one-pass sum replaced by its exact mass;
+  // the rest (tokens below the window) keeps the one-pass sum at sf
+  const double z = zc.z - win_f + win_s;
   int kc = 0, j = 0;  // the cut: key kc keeps its j smallest ids
   // top-k: the first K tokens of the order, counted from the top.  Counts
   // after the cut are cleared, so that the masses below are those of the kept
@@ -415,7 +507,7 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
   double part = 0.0;
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e)
-    if (cnt[e]) part += (double)cnt[e] * weight64(value_of(H.anchor - kPerLane * lane - e), lmax, scale);
+    if (cnt[e]) part += (double)cnt[e] * weight64(value_of(H.anchor - kPerLane * lane - e), lmax, sc.s);
   double incl = part;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -439,7 +531,7 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
       for (int e = 0; e < kPerLane; ++e) {
         if (!cnt[e]) continue;
         const int k = H.anchor - kPerLane * lane - e;
-        const double w = weight64(value_of(k), lmax, scale);
+        const double w = weight64(value_of(k), lmax, sc.s);
         // this lane's last key with tokens, all kept, unless a key below crosses
         kc = k;
         j = (int)cnt[e];
