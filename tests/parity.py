@@ -11,7 +11,9 @@ oracle measured it:
     CDF boundary around the pick, over S.
 Excused sessions and near-ties are counted by kind and reported.
 Probabilities p_i(x_i), q_i(x_i) agree within 1e-5 relative (1e-5 is the
-stated bound; callers may ask for a tighter one).
+stated bound; callers may ask for a tighter one), except in a row whose top-p
+cut the oracle found within 1e-6 of its threshold: there the support, and so
+the normaliser, may differ by the tokens at the cut (counted and reported).
 """
 from __future__ import annotations
 
@@ -233,23 +235,30 @@ def compare(g, o, label="", prob_rtol=PROB_RTOL):
     excused_ids = {e[0] for e in excused}
     max_rel = 0.0
     prob_bad = []
+    prob_at_cut = 0
     if "p_tok" in g:
         for name in ("p_tok", "q_tok"):
             gp, op = g[name], o[name]
+            dname = "d_topp_t" if name == "p_tok" else "d_topp_d"
             for b in range(B):
                 if b in excused_ids:
                     continue
                 ok_rows = op[b] >= 0
                 both = ok_rows & (op[b] > 0) & (gp[b] > 0)
-                if both.any():
-                    rel = np.abs(gp[b][both] - op[b][both]) / op[b][both]
-                    max_rel = max(max_rel, float(rel.max()))
-                    if (rel > prob_rtol).any():
-                        prob_bad.append((name, b, float(rel.max())))
+                for i in np.nonzero(both)[0]:
+                    rel = abs(gp[b, i] - op[b, i]) / op[b, i]
+                    if rel <= prob_rtol:
+                        max_rel = max(max_rel, float(rel))
+                    elif _row_delta(o, dname, b, int(i)) < NEAR_TIE:
+                        # the row's top-p cut is a near-tie: its support (so
+                        # its normaliser) may hold a token more or less
+                        prob_at_cut += 1
+                    else:
+                        max_rel = max(max_rel, float(rel))
+                        prob_bad.append((name, b, int(i), float(rel)))
                 # support membership: a difference is allowed only at a top-p cut
                 # within NEAR_TIE (that row's oracle delta)
                 for i in np.nonzero(ok_rows & ((op[b] > 0) != (gp[b] > 0)))[0]:
-                    dname = "d_topp_t" if name == "p_tok" else "d_topp_d"
                     if _row_delta(o, dname, b, int(i)) >= NEAR_TIE:
                         prob_bad.append((name, b, int(i), "support"))
                 neg_mismatch = (op[b] < 0) != (gp[b] < 0)
@@ -261,7 +270,7 @@ def compare(g, o, label="", prob_rtol=PROB_RTOL):
                mean_a=float(a[a >= 0].mean()) if (a >= 0).any() else None,
                bad_proposal=int((a == oracle.S_BAD_PROPOSAL).sum()),
                mismatches=len(mism), excused=by_kind, near_ties=near_ties(o),
-               max_prob_rel=max_rel)
+               max_prob_rel=max_rel, prob_at_near_tie_cut=prob_at_cut)
     log(f"[parity] {rep}")
     detail = [(b, d, k, int(g["accepted_len"][b]), int(o["accepted_len"][b]),
                g["out_tokens"][b].tolist(), o["out_tokens"][b].tolist()) for b, d, k in mism[:5]]

@@ -115,3 +115,17 @@ def test_probability_tolerance():
     parity.compare(g, o, "rtol-default")
     with pytest.raises(AssertionError, match="probability"):
         parity.compare(g, o, "rtol-tight", prob_rtol=2e-7)
+
+
+def test_probability_at_a_near_tie_cut_is_excused_and_counted():
+    g, o = results()
+    g["p_tok"][0, 1] *= 1 + 3e-6        # the row's support holds one token more
+    with pytest.raises(AssertionError, match="probability"):
+        parity.compare(g, o, "cut-far", prob_rtol=2e-7)
+    o["d_topp_t"][0, 1] = 4e-9          # the oracle's cut of that row is a near-tie
+    rep = parity.compare(g, o, "cut-near", prob_rtol=2e-7)
+    assert rep["prob_at_near_tie_cut"] == 1
+    o["d_topp_t"][0, 1] = 0.1
+    o["d_topp_d"][0, 1] = 4e-9          # a near-tie of the draft row excuses q only
+    with pytest.raises(AssertionError, match="probability"):
+        parity.compare(g, o, "cut-other-row", prob_rtol=2e-7)

@@ -82,12 +82,22 @@ struct Scales {
   float sf;
   float inv_sf;  // 1 / sf, rounded: only the lanes' offset thresholds use it
 };
+// Wave-uniform values kept in scalar registers.
+__device__ inline float uni(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ inline double uni(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ inline Scales row_scales(uint32_t t_milli) {
   Scales c;
-  c.s = 1.4426950408889634074 * 1000.0 / (double)t_milli;
-  c.sf = (float)c.s;
-  c.d = c.s - (double)c.sf;
-  c.inv_sf = 1.0f / c.sf;
+  c.s = uni(1.4426950408889634074 * 1000.0 / (double)t_milli);
+  c.sf = uni((float)c.s);
+  c.d = uni(c.s - (double)c.sf);
+  c.inv_sf = uni(1.0f / c.sf);
   return c;
 }
 
@@ -97,17 +107,24 @@ struct LaneSum {
   float vt;   // logits above vt move q up (-inf until the first finite logit)
   double s;   // sum of 2^(l * sf - q) over this lane's logits so far
   double l1;  // untruncated rows: sum of 2^(l * sf - q) * l (the scale's correction)
+  float dep;  // rows with a histogram: mass relative to Hist::dref of the tokens
+              // counted in bins that later left the window (this lane's bins)
   bool ovf;   // a logit too large for binary32 exponents: the row falls back
 };
 
+constexpr int kNoAnchor = -0x10000;  // no window yet (no finite logit seen)
 struct Hist {
   uint32_t* bin;    // kWin counts, index = key mod kWin
   int anchor;       // largest key seen (the window is [anchor - kWin + 1, anchor])
   float anchor_v;   // its value
   float lo_v;       // value of the window's lowest key (never -inf)
+  float dref;       // the lanes' departed masses are relative to this value
   int kx;           // key of the drafted token (when it has one)
   int rank_x;       // tokens with key kx and a smaller id
 };
+__device__ inline Hist hist_init(uint32_t* bins, int kx) {
+  return Hist{bins, kNoAnchor, -__builtin_huge_valf(), -__builtin_huge_valf(), 0.0f, kx, 0};
+}
 
 // One 16-byte vector (8 logits) of a tile: the lane's maximum and running sum,
 // then (kHist: top-k and top-p rows) the histogram window and the drafted
@@ -138,11 +155,11 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     L.q = qn;
     L.vt = (qn + 1.0f) * sc.inv_sf;
   }
-  float w[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
-  L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
   if constexpr (!kHist) {
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+    L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
     // w * l, with -inf logits (weight 0) taken as the largest negative finite
     // value so that they add 0; a NaN logit has a NaN weight and stays NaN
     float tl = w[0] * fmaxf(f[0], -__FLT_MAX__);
@@ -157,11 +174,25 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
     const int lane = __lane_id();
     const int d = tk - H.anchor;  // keys anchor+1 .. tk take the bins of the keys leaving
-    for (int i = lane; i < kWin; i += kWave)
-      if (d >= kWin || ((i - (H.anchor + 1)) & (kWin - 1)) < d) H.bin[i] = 0u;
-    H.anchor = tk;
-    H.anchor_v = value_of(tk);
-    H.lo_v = value_of(max(tk - (kWin - 1), kNegInfKey + 1));
+    const float nref = value_of(tk);
+    const bool had = H.anchor != kNoAnchor;
+    // the leaving bins' tokens are in no sum: their mass goes to dep.  They lie
+    // at least kWin keys (eight octaves of magnitude) below the new maximum, so
+    // binary32 suffices: an error of a few 1e-7 of a mass far below Z's
+    if (had) L.dep *= __builtin_amdgcn_exp2f((H.dref - nref) * sc.sf);
+    for (int i = lane; i < kWin; i += kWave) {
+      if (d >= kWin || ((i - (H.anchor + 1)) & (kWin - 1)) < d) {
+        const int ko = H.anchor - ((H.anchor - i) & (kWin - 1));  // the key leaving bin i
+        const uint32_t c = had ? H.bin[i] : 0u;
+        if (c && ko > kNegInfKey)
+          L.dep += (float)c * __builtin_amdgcn_exp2f((value_of(ko) - nref) * sc.sf);
+        H.bin[i] = 0u;
+      }
+    }
+    H.dref = uni(nref);
+    H.anchor = __builtin_amdgcn_readfirstlane(tk);
+    H.anchor_v = uni(nref);
+    H.lo_v = uni(value_of(max(tk - (kWin - 1), kNegInfKey + 1)));
   }
   const int lo = H.anchor - (kWin - 1);
   if (xvec) {  // the drafted token's rank: its key's bin before this vector, plus
@@ -173,15 +204,27 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     for (int off = kWave / 2; off > 0; off >>= 1) before += __shfl_xor(before, off, kWave);
     H.rank_x = (H.kx >= lo ? (int)H.bin[H.kx & (kWin - 1)] : 0) + before;
   }
-  if (lo > 0) {  // a window of positive keys: the key is the upper half of the bits
+  // tokens in the window are counted; the binary32 sum takes only the others
+  if (lo > 0) {
+    // a window of positive keys: the key is the upper half of the bits, and the
+    // unpacked value's low 16 bits are zero, so bits 14..25 are the bin's byte
+    // offset
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (f[e] >= H.lo_v) atomicAdd(&H.bin[(__float_as_uint(f[e]) >> 16) & (kWin - 1)], 1u);
+      if (f[e] >= H.lo_v)
+        atomicAdd((uint32_t*)((char*)H.bin + __builtin_amdgcn_ubfe(__float_as_uint(f[e]), 14, 12)), 1u);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (f[e] >= H.lo_v) atomicAdd(&H.bin[skey_of(f[e]) & (kWin - 1)], 1u);
   }
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+    w[e] = f[e] >= H.lo_v ? 0.0f : t;
+  }
+  L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
 }
 
 // The row's layout for the pass: a 16-byte aligned window over the row, in
@@ -234,28 +277,34 @@ __device__ __attribute__((always_inline)) inline void stream_part(const RowWin& 
 }
 
 __device__ inline LaneSum lane_sum_init() {
-  return LaneSum{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, 0.0, false};
+  return LaneSum{-__builtin_huge_valf(), 0.0f, -__builtin_huge_valf(), 0.0, 0.0, 0.0f, false};
 }
 
-// This wave's sums relative to lmax * sf (lanes combined in a fixed order):
-// z = sum of 2^((l - lmax) sf), and (untruncated rows) c = sum of
-// 2^((l - lmax) sf) (l - lmax), the first-order term of the scale's rounding.
+// This wave's sums relative to lmax (lanes combined in a fixed order):
+// z = sum of 2^((l - lmax) sf) over the tokens the binary32 pass summed (rows
+// with a histogram: those below the window when they were read); c
+// (untruncated rows) = sum of 2^((l - lmax) sf) (l - lmax), the first-order
+// term of the scale's rounding; dep (rows with a histogram) = the exact mass
+// at s of the tokens whose bins left the window.
 struct WaveZ {
-  double z, c;
+  double z, c, dep;
 };
 template <bool kHist>
-__device__ inline WaveZ wave_z(const LaneSum& L, float lmax, float sf) {
-  const double ref = (double)lmax * (double)sf;  // exact: both factors are binary32
+__device__ inline WaveZ wave_z(const LaneSum& L, const Hist& H, float lmax, const Scales& sc) {
+  const double ref = (double)lmax * (double)sc.sf;  // exact: both factors are binary32
   const bool none = L.vt == -__builtin_huge_valf();  // no finite logit in this lane
   const double f = none ? 1.0 : exp2((double)L.q - ref);
   double z = L.s * f;
   double c = kHist ? 0.0 : (none ? L.l1 : (L.l1 - (double)lmax * L.s) * f);
+  double dep = (kHist && L.dep != 0.0f)
+                   ? (double)L.dep * exp2(((double)H.dref - (double)lmax) * sc.s) : 0.0;
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     z += __shfl_xor(z, off, kWave);
     c += __shfl_xor(c, off, kWave);
+    dep += __shfl_xor(dep, off, kWave);
   }
-  return WaveZ{z, c};
+  return WaveZ{z, c, dep};
 }
 
 __device__ inline float wave_max(float v) {
@@ -284,11 +333,11 @@ __device__ __attribute__((always_inline)) inline bool row_profile_t(
   const RowWin W = row_window(row, V);
   const float xval = x >= 0 ? __uint_as_float((uint32_t)row[x] << 16) : 0.0f;
   LaneSum L = lane_sum_init();
-  Hist H{bins, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), x >= 0 ? skey_of(xval) : 0, 0};
+  Hist H = hist_init(bins, x >= 0 ? skey_of(xval) : 0);
   stream_part<kHist>(W, 0, W.ntiles, x >= 0 ? x + W.head : -1, sc, L, H);
   const float lmax = wave_max(L.mv);
-  return finish<kHist>(smp, V, x, xval, lmax, wave_z<kHist>(L, lmax, sc.sf), __ballot(L.ovf) != 0, H,
-                       rec);
+  return finish<kHist>(smp, V, x, xval, lmax, wave_z<kHist>(L, H, lmax, sc),
+                       __ballot(L.ovf) != 0, H, rec);
 }
 __device__ __attribute__((always_inline)) inline bool row_profile(
     const uint16_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec, uint32_t* bins) {
@@ -302,7 +351,7 @@ struct PartRec {
   int anchor;  // the part's histogram window is [anchor - kWin + 1, anchor]
   int nx;      // tokens of the drafted token's key: before it (its own part), or all
   int ovf;
-  double z, c;  // the part's sums relative to the row's lmax * sf (see WaveZ)
+  double z, c, dep;  // the part's sums relative to the row's lmax (see WaveZ)
 };
 
 // The same profile with the row split over the S waves of a workgroup, for
@@ -327,7 +376,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split_t(
   const int t0 = wid * W.ntiles / S, t1 = (wid + 1) * W.ntiles / S;
   const bool x_here = px >= 0 && px / kTile >= t0 && px / kTile < t1;
   LaneSum L = lane_sum_init();
-  Hist H{bins_all + wid * kWin, -0x10000, -__builtin_huge_valf(), -__builtin_huge_valf(), kx, 0};
+  Hist H = hist_init(bins_all + wid * kWin, kx);
   stream_part<kHist>(W, t0, t1, x_here ? px : -1, sc, L, H);
   const float lm = wave_max(L.mv);
   const bool ovf = __ballot(L.ovf) != 0;
@@ -347,33 +396,51 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split_t(
   float lmax = parts[0].lmax;
 #pragma unroll
   for (int w = 1; w < S; ++w) lmax = fmaxf(lmax, parts[w].lmax);
-  const WaveZ zw = wave_z<kHist>(L, lmax, sc.sf);
+  const WaveZ zw = wave_z<kHist>(L, H, lmax, sc);
   if (lane == 0) {
     parts[wid].z = zw.z;
     parts[wid].c = zw.c;
+    parts[wid].dep = zw.dep;
   }
   __syncthreads();  // every part's sum and histogram are complete
   if (wid != 0) return false;
-  WaveZ z{parts[0].z, parts[0].c};
+  WaveZ z{parts[0].z, parts[0].c, parts[0].dep};
   int anc = parts[0].anchor, any_ovf = parts[0].ovf;
 #pragma unroll
   for (int w = 1; w < S; ++w) {
     z.z += parts[w].z;
     z.c += parts[w].c;
+    z.dep += parts[w].dep;
     anc = max(anc, parts[w].anchor);
     any_ovf |= parts[w].ovf;
   }
-  Hist M{bins_all, anc, value_of(anc), value_of(max(anc - (kWin - 1), kNegInfKey + 1)), kx, 0};
+  Hist M = hist_init(bins_all, kx);
+  M.anchor = anc;
+  M.anchor_v = value_of(anc);
+  M.lo_v = value_of(max(anc - (kWin - 1), kNegInfKey + 1));
   if constexpr (kHist) {
-    // the row's window: bin i holds key k = anc - ((anc - i) mod kWin)
+    // the row's window: bin i holds key k = anc - ((anc - i) mod kWin).  Part
+    // w's bin i holds key kw = a_w - ((a_w - i) mod kWin) (a_w <= anc, its own
+    // anchor): the same key when kw lies in the row's window; else a key below
+    // it, whose tokens are in no sum yet and add their exact mass to dep
+    double below = 0.0;
     for (int i = lane; i < kWin; i += kWave) {
       const int k = anc - ((anc - i) & (kWin - 1));
       uint32_t c = 0;
 #pragma unroll
-      for (int w = 0; w < S; ++w)
-        if (k <= parts[w].anchor) c += bins_all[w * kWin + i];
+      for (int w = 0; w < S; ++w) {
+        const int aw = parts[w].anchor;
+        const uint32_t cw = aw == kNoAnchor ? 0u : bins_all[w * kWin + i];
+        const int kw = aw - ((aw - i) & (kWin - 1));
+        if (kw == k) c += cw;
+        else if (cw && kw > kNegInfKey)
+          below += (double)cw * exp2(((double)value_of(kw) - (double)lmax) * sc.s);
+      }
       bins_all[i] = c;
     }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) below += __shfl_xor(below, off, kWave);
+    z.dep += below;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -441,28 +508,20 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
   }
 
   // the window's counts: lane q holds the bins of keys anchor - kPerLane*q - e;
-  // and the window's mass at sf and at s
+  // and the window's exact mass at s
   uint32_t cnt[kPerLane];
-  double win_f = 0.0, win_s = 0.0;
-  const double lref = (double)lmax;
+  double win = 0.0;
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e) {
     const int k = H.anchor - kPerLane * lane - e;
     cnt[e] = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
-    if (cnt[e]) {
-      const double dl = (double)value_of(k) - lref;  // exact
-      win_f += (double)cnt[e] * exp2(dl * (double)sc.sf);
-      win_s += (double)cnt[e] * exp2(dl * sc.s);
-    }
+    if (cnt[e]) win += (double)cnt[e] * weight64(value_of(k), lmax, sc.s);
   }
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    win_f += __shfl_xor(win_f, off, kWave);
-    win_s += __shfl_xor(win_s, off, kWave);
-  }
-  // Z at s: the window's share of the one-pass sum replaced by its exact mass;
-  // the rest (tokens below the window) keeps the one-pass sum at sf
-  const double z = zc.z - win_f + win_s;
+  for (int off = kWave / 2; off > 0; off >>= 1) win += __shfl_xor(win, off, kWave);
+  // Z at s: the window's and the departed bins' exact masses, and the binary32
+  // sum of the tokens below the window when they were read
+  const double z = win + zc.dep + zc.z;
   int kc = 0, j = 0;  // the cut: key kc keeps its j smallest ids
   // top-k: the first K tokens of the order, counted from the top.  Counts
   // after the cut are cleared, so that the masses below are those of the kept
