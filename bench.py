@@ -166,6 +166,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--logits", choices=("bf16", "fp32"), default=None,
+                    help="store the workload's logits as bf16 or binary32 (default: the "
+                         "workload's own type)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=1,
@@ -211,7 +214,7 @@ def main():
     torch.cuda.set_device(dev)
 
     log(f"[bench] building workload {args.workload}")
-    w = W.make(args.workload, device="cuda", sessions=args.sessions)
+    w = W.make(args.workload, device="cuda", sessions=args.sessions, logits=args.logits)
     smp = w.sampling_tensor(dev)
     B, M, V = w.B, w.M, w.V
     P = w.positions()

@@ -95,27 +95,25 @@ __host__ __device__ inline DrawChunks draw_chunks(int32_t B, int32_t V) {
   return DrawChunks{(int32_t)C, (int32_t)gw};
 }
 
-// Row status written by a specialised row kernel that could not finish a row;
-// the generic kernel then computes that row.
-constexpr int32_t kRowFallback = 1;
-
 // Rows whose support lies among the 64 best tokens take the single-pass
-// kernel's top-k path (bf16 only): greedy rows, temperature-0 rows,
+// kernel's top-k path (bf16 or binary32): greedy rows, temperature-0 rows,
 // 1 <= top_k <= 64.
 __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule,
                                                      const sv_sampling& s) {
-  if (dtype != SV_BF16) return false;
+  (void)dtype;
   if (rule == SV_RULE_GREEDY || s.temperature_milli == 0) return true;
   return s.top_k >= 1 && s.top_k <= 64;
 }
 
-// Every other bf16 row takes the single-pass kernel's dense path: temperature
-// > 0 with top-k off (top_k = 0 or top_k >= V) or above 64, with or without
-// top-p.
+// The single-pass kernel's dense path takes every other bf16 row (temperature
+// > 0 with top-k off or above 64, with or without top-p), and the binary32
+// rows with temperature alone (top-k and top-p off); other binary32 rows take
+// the generic kernel's exact profile.
 __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rule,
                                                       const sv_sampling& s, int32_t V) {
-  (void)V;
-  return dtype == SV_BF16 && !row_uses_topk_kernel(dtype, rule, s);
+  if (row_uses_topk_kernel(dtype, rule, s)) return false;
+  if (dtype == SV_BF16) return true;
+  return s.top_p_milli >= 1000 && (s.top_k == 0 || s.top_k >= (uint32_t)V);
 }
 
 struct WorkspaceLayout {

@@ -126,6 +126,44 @@ __device__ inline Hist hist_init(uint32_t* bins, int kx) {
   return Hist{bins, kNoAnchor, -__builtin_huge_valf(), -__builtin_huge_valf(), 0.0f, kx, 0};
 }
 
+// One lane's step over kE logits: its maximum, its offset q, and (kSum: rows
+// without a histogram) its binary32 sum of 2^(l sf - q) with the sum of
+// those terms times l.  Returns the kE logits' maximum.
+template <int kE, bool kSum>
+__device__ __attribute__((always_inline)) inline float lane_step(LaneSum& L, const float (&f)[kE],
+                                                                 const Scales& sc) {
+  float lmv = f[0];
+#pragma unroll
+  for (int e = 1; e < kE; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
+  L.mv = fmaxf(L.mv, lmv);
+  if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or an octave up
+    const float qn = ceilf(lmv * sc.sf);
+    L.ovf |= !(qn < 0x1p22f);
+    // a power-of-two rescale is exact; NaN from earlier logits stays NaN
+    const bool first = L.vt == -__builtin_huge_valf();
+    L.s = first ? (L.s != L.s ? L.s : 0.0) : ldexp(L.s, (int)(L.q - qn));
+    if constexpr (kSum) L.l1 = first ? (L.l1 != L.l1 ? L.l1 : 0.0) : ldexp(L.l1, (int)(L.q - qn));
+    L.q = qn;
+    L.vt = (qn + 1.0f) * sc.inv_sf;
+  }
+  if constexpr (kSum) {
+    float w[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+    float ts;
+    if constexpr (kE == 8) ts = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+    else ts = (w[0] + w[1]) + (w[2] + w[3]);
+    L.s += (double)ts;
+    // w * l, with -inf logits (weight 0) taken as the largest negative finite
+    // value so that they add 0; a NaN logit has a NaN weight and stays NaN
+    float tl = w[0] * fmaxf(f[0], -__FLT_MAX__);
+#pragma unroll
+    for (int e = 1; e < kE; ++e) tl = __builtin_fmaf(w[e], fmaxf(f[e], -__FLT_MAX__), tl);
+    L.l1 += (double)tl;
+  }
+  return lmv;
+}
+
 // One 16-byte vector (8 logits) of a tile: the lane's maximum and running sum,
 // then (kHist: top-k and top-p rows) the histogram window and the drafted
 // token's rank.  p0 is the window position of the vector's first logit; xvec
@@ -141,33 +179,8 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     f[2 * d] = __uint_as_float(x << 16);
     f[2 * d + 1] = __uint_as_float(x & 0xFFFF0000u);
   }
-  float lmv = f[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
-  L.mv = fmaxf(L.mv, lmv);
-  if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or an octave up
-    const float qn = ceilf(lmv * sc.sf);
-    L.ovf |= !(qn < 0x1p22f);
-    // a power-of-two rescale is exact; NaN from earlier logits stays NaN
-    const bool first = L.vt == -__builtin_huge_valf();
-    L.s = first ? (L.s != L.s ? L.s : 0.0) : ldexp(L.s, (int)(L.q - qn));
-    if constexpr (!kHist) L.l1 = first ? (L.l1 != L.l1 ? L.l1 : 0.0) : ldexp(L.l1, (int)(L.q - qn));
-    L.q = qn;
-    L.vt = (qn + 1.0f) * sc.inv_sf;
-  }
-  if constexpr (!kHist) {
-    float w[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
-    L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
-    // w * l, with -inf logits (weight 0) taken as the largest negative finite
-    // value so that they add 0; a NaN logit has a NaN weight and stays NaN
-    float tl = w[0] * fmaxf(f[0], -__FLT_MAX__);
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tl = __builtin_fmaf(w[e], fmaxf(f[e], -__FLT_MAX__), tl);
-    L.l1 += (double)tl;
-    return;
-  }
+  const float lmv = lane_step<8, !kHist>(L, f, sc);
+  if constexpr (!kHist) return;
   if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
     int tk = skey_of(lmv);
 #pragma unroll
@@ -313,7 +326,7 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
-template <bool kHist>
+template <bool kHist, class Tr = Bf16>
 __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V,
                                                              int32_t x, float xval, float lmax,
                                                              WaveZ z, bool ovf, const Hist& H,
@@ -468,7 +481,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split(
 // overflow flag and the histogram window H (with the drafted token's key and
 // rank).  Every weight here is binary64 at the row's true scale s.  Returns
 // true if the row is handed back.
-template <bool kHist>
+template <bool kHist, class Tr>
 __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& smp, int V,
                                                              int32_t x, float xval, float lmax,
                                                              WaveZ zc, bool ovf, const Hist& H,
@@ -499,7 +512,7 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
   if constexpr (!kHist) {  // the support is every finite logit
     // Z at s: the one-pass sum at sf and its first-order correction
     const double z = zc.z + 0.69314718055994530942 * sc.d * zc.c;
-    rr.kcut = Bf16::kNegInfKey + 1;
+    rr.kcut = Tr::kNegInfKey + 1;
     rr.idcut = 0x7FFFFFFF;
     rr.zsum = z;
     if (x >= 0) rr.ptok = wx / z;
@@ -624,6 +637,52 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
   }
   if (lane == 0) *rec = rr;
   return false;
+}
+
+
+// A binary32 row of the dense class without a histogram (temperature alone:
+// top-k and top-p off), by one wave: one pass through a ring of 2 KiB tiles
+// (4 logits per 16-byte vector), the lanes' maxima and sums as for bf16 rows.
+// Rows with top-p or top-k above 64 take the exact profile.  Returns true if
+// the row is handed back.
+__device__ __attribute__((always_inline)) inline bool row_profile_f32_untruncated(
+    const uint32_t* row, int V, const sv_sampling& smp, int32_t x, RowRec* rec) {
+  constexpr int kT = kWave * kVec * 4;  // binary32 logits per tile
+  const Scales sc = row_scales(smp.temperature_milli);
+  const int head = (int)(((uintptr_t)row & 15u) >> 2);
+  const u32x4* vbase = (const u32x4*)(row - head);
+  const int npos = head + V;
+  const int nvec = (npos + 3) / 4;
+  const int ntiles = (npos + kT - 1) / kT;
+  const float xval = x >= 0 ? __uint_as_float(row[x]) : 0.0f;
+  LaneSum L = lane_sum_init();
+  u32x4 ring[kNBuf][kVec];
+#pragma unroll
+  for (int u = 0; u < kNBuf - 1; ++u) {
+    load_tile<kVec>(ring[u], vbase, u, nvec - 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nround = (ntiles + kNBuf - 1) / kNBuf;
+  for (int r = 0; r < nround; ++r) {
+    set_priority(nround - r, nround);
+#pragma unroll
+    for (int u = 0; u < kNBuf; ++u) {
+      const int tt = r * kNBuf + u;
+      load_tile<kVec>(ring[(u + kNBuf - 1) % kNBuf], vbase, tt + kNBuf - 1, nvec - 1);
+      if ((tt == 0 && head > 0) || (tt + 1) * kT > npos) mask_tile_f32<kVec>(ring[u], tt, head, npos);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        float f[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) f[d] = __uint_as_float(elem(ring[u][j], d));
+        (void)lane_step<4, true>(L, f, sc);
+      }
+    }
+  }
+  const float lmax = wave_max(L.mv);
+  const Hist H = hist_init(nullptr, 0);
+  return finish<false, F32>(smp, V, x, xval, lmax, wave_z<false>(L, H, lmax, sc),
+                            __ballot(L.ovf) != 0, H, rec);
 }
 
 }  // namespace dense

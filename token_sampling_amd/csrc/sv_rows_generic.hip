@@ -1,7 +1,7 @@
 // sv_rows_generic.hip -- the generic row kernel: the exact profile of
-// sv_rows_exact.hpp, one workgroup of kNT threads per row, for fp32 rows (the
-// single-pass kernel takes bf16 rows, and profiles a row it hands back
-// itself).
+// sv_rows_exact.hpp, one workgroup of kNT threads per row, for the binary32
+// rows with top-p or top-k above 64 (the single-pass kernel takes every other
+// row, and profiles a row it hands back itself).
 #include <algorithm>
 
 #include "sv_kernels.hpp"
@@ -14,8 +14,7 @@ namespace {
 constexpr int kNT = 256;
 
 
-// Does row slot slot_g need this kernel?  Rows of the other row kernels only
-// when they handed the row back.
+// Does row slot slot_g need this kernel?
 // With in-order reading (decided != null) only the window's positions of the
 // sessions still undecided.
 template <class Tr>
@@ -37,9 +36,9 @@ __device__ bool generic_row(int slot_g, const int32_t* m, const int32_t* rule,
   if (is_target ? (i > mb + 1) : (rl != SV_RULE_SPECULATIVE || i > mb || !draft_logits))
     return false;
   const sv_sampling smp = sampling[b];
-  if (row_uses_topk_kernel(Tr::kDtype, rl, smp) || row_uses_dense_kernel(Tr::kDtype, rl, smp, V))
-    return rows[slot_g].status == kRowFallback;
-  return true;
+  // the single-pass kernel's rows (a row it hands back, it profiles itself)
+  return !row_uses_topk_kernel(Tr::kDtype, rl, smp) &&
+         !row_uses_dense_kernel(Tr::kDtype, rl, smp, V);
 }
 
 // A grid of at most kMaxBlocks workgroups scans the row slots: each workgroup

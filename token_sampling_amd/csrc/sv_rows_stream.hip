@@ -6,8 +6,10 @@
 //     top-p): dense::row_profile.
 // A row a path hands back (a top-k region that overflows, a cut below the
 // dense histogram's window, logits beyond binary32 exponent range) is profiled
-// exactly by the same wave (sv_rows_exact.hpp).  fp32 rows are left to the
-// generic kernel.  Each wave also takes its session's statuses that need no
+// exactly by the same wave (sv_rows_exact.hpp).  Binary32 rows take the top-k
+// path on 32-bit keys (topk32::row_profile) or, with temperature alone, the
+// dense pass (dense::row_profile_f32_untruncated); binary32 rows with top-p or
+// top-k above 64 are left to the generic kernel.  Each wave also takes its session's statuses that need no
 // logits (SDCP Table 2, Sec. 6.3 step 5: limit, profile, q availability,
 // drafted tokens in range); the wave of a session's first row slot records
 // them for the kernels that follow.
@@ -21,6 +23,7 @@
 #include "sv_rows_dense.hpp"
 #include "sv_rows_exact.hpp"
 #include "sv_rows_topk.hpp"
+#include "sv_rows_topk32.hpp"
 #include "sv_sdcp.hpp"
 
 namespace sv {
@@ -78,9 +81,10 @@ constexpr int kLdsWords = (topk::kCap * 8 > dense::kWin * 4 ? topk::kCap * 8 : d
 #ifndef SV_STREAM_WAVES_PER_EU
 #define SV_STREAM_WAVES_PER_EU 5
 #endif
+template <class Tr>
 __global__ __launch_bounds__(kWave)
 __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
-    const uint16_t* __restrict__ target, const uint16_t* __restrict__ draft, int32_t dtype,
+    const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ m,
     const int32_t* __restrict__ rule, const sv_sampling* __restrict__ sampling, int has_draft,
     int B, int M, int V, int32_t* __restrict__ sess_status, uint32_t* __restrict__ draw_ctr,
@@ -88,6 +92,7 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
     int32_t* __restrict__ decided, int win_lo, int win_w) {
+  using E = typename Tr::elem_t;
   __shared__ __align__(16) uint64_t lds[kLdsWords];  // top-k region or dense histogram
   const int lane = __lane_id();
   if ((int)blockIdx.x < n_value_blocks) {
@@ -107,7 +112,7 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     draw_ctr[b] = 0u;  // the draw's chunk counter, for the per-session kernel
     if (decided) decided[b] = 0;
   }
-  if (st != 0 || dtype != SV_BF16) return;
+  if (st != 0) return;
   const int mb = m[b];
   const int rl = rule[b];
   const bool is_target = slot <= M;
@@ -117,22 +122,30 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     return;
   const sv_sampling smp = sampling[b];
   const int32_t x = i <= mb ? tokens[(size_t)b * M + (i - 1)] : -1;
-  const uint16_t* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
-                                  : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
+  const E* row = is_target ? target + ((size_t)b * (M + 1) + (i - 1)) * (size_t)V
+                           : draft + ((size_t)b * M + (i - 1)) * (size_t)V;
   RowRec* rec = rows + (size_t)slot_g;
   bool back;
-  if (row_uses_topk_kernel(SV_BF16, rl, smp)) {
+  if (row_uses_topk_kernel(Tr::kDtype, rl, smp)) {
     const bool one_hot = rl == SV_RULE_GREEDY || smp.temperature_milli == 0;
     const int k = one_hot ? 1 : (int)smp.top_k;
     const size_t so = (size_t)slot_g * kSupMax;
-    back = topk::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
-  } else {
+    if constexpr (Tr::kDtype == SV_BF16)
+      back = topk::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
+    else
+      back = topk32::row_profile(row, V, k, one_hot, smp, x, rec, sup_id + so, sup_p + so, lds);
+  } else if (row_uses_dense_kernel(Tr::kDtype, rl, smp, V)) {
     if (lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
-    back = dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+    if constexpr (Tr::kDtype == SV_BF16)
+      back = dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
+    else
+      back = dense::row_profile_f32_untruncated(row, V, smp, x, rec);
+  } else {
+    return;  // binary32 rows with top-p or top-k above 64: the generic kernel
   }
   if (back) {  // the exact profile, by this wave
     if (lane == 0) draw_flag[b] = draw_token;
-    exact::profile_row<Bf16, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
+    exact::profile_row<Tr, kWave>(row, V, smp, rl == SV_RULE_GREEDY, x, rec, nullptr);
   }
 }
 
@@ -240,8 +253,10 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
       return;
     }
     const size_t so = (size_t)slot_g * kSupMax;
-    topk::row_finish(reg, total, k, lane == 0 ? mmax : 0u, lane == 0 ? umax : 0u, one_hot,
-                     smp.temperature_milli, smp.top_p_milli, x, rec, sup_id + so, sup_p + so);
+    const bool nan = max((int)(mmax & 0xFFFFu), (int)(mmax >> 16)) > 0x7F80 ||
+                     max((int)(umax & 0xFFFFu), (int)(umax >> 16)) > 0xFF80;
+    topk::row_finish<topk::Key16>(reg, total, k, nan, 0x7F80, one_hot, smp.temperature_milli,
+                                  smp.top_p_milli, x, rec, sup_id + so, sup_p + so);
   } else if (row_uses_dense_kernel(SV_BF16, rl, smp, V)) {
     // the S waves stream S parts of the row; wave 0 merges them and finishes
     if (wid == 0 && lane == 0) draw_flag[b] = draw_token;  // a row without a listed support
@@ -265,6 +280,7 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
 #define SV_TAIL_SPLIT 1
 #endif
 static int rows_split_factor(const LaunchArgs& a) {
+  if (a.dtype != SV_BF16) return 1;  // binary32 rows: one wave per row
   const char* env = getenv("SV_ROWS_SPLIT");
   if (env) {
     const int s = atoi(env);
@@ -314,12 +330,19 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   if (split == 8) return launch_split<8>(a, st, slots);
   const int n_value_blocks = value_blocks(a, kWave);
   const unsigned grid = (unsigned)(slots + n_value_blocks);
-  hipLaunchKernelGGL(k_rows_stream, dim3(grid), dim3(kWave), 0, st, (const uint16_t*)a.target,
-                     (const uint16_t*)a.draft, a.dtype, a.tokens, a.m, a.rule, a.sampling,
-                     (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B, a.M, a.V,
-                     a.sess_status,
-                     a.draw_ctr, a.draw_flag, a.draw_token, a.rows, a.sup_id,
-                     a.sup_p, a.sdcp, a.unif, n_value_blocks, a.decided, a.win_lo, a.win_w);
+  const int has_draft = (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0;
+  if (a.dtype == SV_BF16)
+    hipLaunchKernelGGL(k_rows_stream<Bf16>, dim3(grid), dim3(kWave), 0, st,
+                       (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
+                       a.sampling, has_draft, a.B, a.M, a.V, a.sess_status, a.draw_ctr,
+                       a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
+                       n_value_blocks, a.decided, a.win_lo, a.win_w);
+  else
+    hipLaunchKernelGGL(k_rows_stream<F32>, dim3(grid), dim3(kWave), 0, st,
+                       (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
+                       a.sampling, has_draft, a.B, a.M, a.V, a.sess_status, a.draw_ctr,
+                       a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
+                       n_value_blocks, a.decided, a.win_lo, a.win_w);
 }
 
 }  // namespace sv

@@ -57,6 +57,19 @@ static_assert(kBoundTiles <= kNBuf - 1, "the first bound's tiles are all in the 
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 
+// Key widths of the candidate composites (key + bias) << 32 | ~id: the signed
+// 16-bit keys of bf16 rows, the signed 32-bit keys of binary32 rows.
+struct Key16 {
+  static constexpr int kBits = 16;
+  __device__ static int unbias(uint32_t t) { return (int)t - 0x8000; }
+  __device__ static uint32_t bias(int k) { return (uint32_t)(k + 0x8000); }
+};
+struct Key32 {
+  static constexpr int kBits = 32;
+  __device__ static int unbias(uint32_t t) { return (int)(t - 0x80000000u); }
+  __device__ static uint32_t bias(int k) { return (uint32_t)k + 0x80000000u; }
+};
+
 __device__ inline uint64_t composite(int key, uint32_t id) {
   return ((uint64_t)(uint32_t)(key + 0x8000) << 32) | (uint64_t)(0xFFFFFFFFu - id);
 }
@@ -74,6 +87,7 @@ struct Cut {
 // Cut the region reg[0..n) to its k best entries (k <= 64, n <= kCap) and
 // compact them to the front; empty entries (0) are dropped.  An odd count is
 // followed by one empty entry so that pair stores stay 16-byte aligned.
+template <class K = Key16>
 __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, int k) {
   const int lane = __lane_id();
   uint64_t e[kCap / kWave];
@@ -87,9 +101,9 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
   // keep entries with biased key (key + 0x8000) > t, or == t with low word >= lowcut;
   // every non-empty entry has a biased key above 0, so t = 0 keeps them all
   uint32_t t = 0, lowcut = 0;
-  int kth = -0x8000;
+  int kth = K::unbias(0);
   if (live > k) {
-    for (int bit = 15; bit >= 0; --bit) {  // k-th largest biased key, bit by bit
+    for (int bit = K::kBits - 1; bit >= 0; --bit) {  // k-th largest biased key, bit by bit
       const uint32_t cand = t | (1u << bit);
       int cnt = 0;
 #pragma unroll
@@ -115,12 +129,12 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
       }
       lowcut = u;
     }
-    kth = (int)t - 0x8000;
+    kth = K::unbias(t);
   } else if (live == k) {
     int mn = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kCap / kWave; ++i)
-      if (e[i]) mn = min(mn, comp_key(e[i]));
+      if (e[i]) mn = min(mn, K::unbias((uint32_t)(e[i] >> 32)));
     for (int off = kWave / 2; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off, kWave));
     kth = mn;
   }
@@ -184,17 +198,17 @@ __device__ inline int slots_ge(const u32x4 (&v)[kVec], int te) {
 
 // k-th largest of the N * 64 values held N per lane (k <= 64), as a signed
 // 16-bit key
-template <int N>
+template <int N, class K = Key16>
 __device__ inline int wave_kth_largest_n(const int (&v)[N], int k) {
   uint32_t t = 0;
-  for (int bit = 15; bit >= 0; --bit) {
+  for (int bit = K::kBits - 1; bit >= 0; --bit) {
     const uint32_t cand = t | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) cnt += popc64(__ballot((uint32_t)(v[i] + 0x8000) >= cand));
+    for (int i = 0; i < N; ++i) cnt += popc64(__ballot(K::bias(v[i]) >= cand));
     if (cnt >= k) t = cand;
   }
-  return (int)t - 0x8000;
+  return K::unbias(t);
 }
 
 // lane maxima of one tile without changing it: raw bits as signed 16-bit
@@ -330,28 +344,40 @@ __device__ inline double wave_incl_scan_f64(double v) {
   return v;
 }
 
+// Wave maxima of packed 16-bit pairs, as one value.
+__device__ inline int wave_pair_max(uint32_t pair) {
+  for (int off = kWave / 2; off > 0; off >>= 1) pair = max_u16x2(pair, __shfl_xor(pair, off, kWave));
+  return max((int)(pair & 0xFFFFu), (int)(pair >> 16));
+}
+
+// Key decoding of a composite, for the key width K: the signed key and its
+// logit value.
+template <class K>
+__device__ inline int ckey(uint64_t c) { return K::unbias((uint32_t)(c >> 32)); }
+template <class K>
+__device__ inline float ckey_value(int key) {
+  if constexpr (K::kBits == 16) return key_value(key);
+  else return __uint_as_float(key >= 0 ? (uint32_t)key : (0x80000000u | (uint32_t)(-key)));
+}
+
 // The row's profile from its candidates: exactly the k best, sorted (one per
 // lane), then the BAD_LOGITS checks, temperature and top-p (SDCP Sec. 4.1);
-// the support is written sorted by id with its probabilities.
-__device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_t magmax_pair,
-                                        uint32_t umax_pair, bool one_hot, uint32_t t_milli, uint32_t p_milli, int32_t x,
-                                        RowRec* rec, int32_t* sup_id, double* sup_p) {
+// the support is written sorted by id with its probabilities.  bad_seen: a
+// NaN was seen in the row (the caller's wave maxima of magnitudes and of raw
+// bits); kInfKey: the key of +inf.
+template <class K>
+__device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, bool bad_seen, int kInfKey,
+                                        bool one_hot, uint32_t t_milli, uint32_t p_milli,
+                                        int32_t x, RowRec* rec, int32_t* sup_id, double* sup_p) {
   const int lane = __lane_id();
-  const int n = region_cut(reg, n_reg, k).n;
+  const int n = region_cut<K>(reg, n_reg, k).n;
   uint64_t e = lane < n ? reg[lane] : 0ull;
   e = wave_sort_desc(e);
 
-  uint32_t mm = magmax_pair, um = umax_pair;
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    mm = max_u16x2(mm, __shfl_xor(mm, off, kWave));
-    um = max_u16x2(um, __shfl_xor(um, off, kWave));
-  }
-  const int magmax = max((int)(mm & 0xFFFFu), (int)(mm >> 16));
-  const int umax = max((int)(um & 0xFFFFu), (int)(um >> 16));
   const uint64_t top = __shfl(e, 0, kWave);
-  const int kmax = comp_key(top);
+  const int kmax = ckey<K>(top);
   // NaN anywhere, +inf at the top, or no finite logit at all
-  const bool bad = magmax > 0x7F80 || umax > 0xFF80 || n == 0 || kmax >= 0x7F80;
+  const bool bad = bad_seen || n == 0 || kmax >= kInfKey;
 
   RowRec r;
   r.ntie = 0;
@@ -359,7 +385,7 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   r.status = bad ? SV_S_BAD_LOGITS : 0;
   r.argmax = (int32_t)comp_id(top);
   r.nsup = 0;
-  r.lmax = key_value(kmax);
+  r.lmax = ckey_value<K>(kmax);
   r.ptok = -1.0;
   if (bad) {
     r.kcut = 0;
@@ -373,7 +399,7 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   const double scale = one_hot ? 0.0 : 1.4426950408889634074 * 1000.0 / (double)t_milli;
   const bool live = lane < (one_hot ? 1 : n);
   const int kept = popc64(__ballot(live));
-  const double w = live ? exp2(((double)key_value(comp_key(e)) - (double)r.lmax) * scale) : 0.0;
+  const double w = live ? exp2(((double)ckey_value<K>(ckey<K>(e)) - (double)r.lmax) * scale) : 0.0;
   const double C = wave_incl_scan_f64(w);
   const double Zk = __shfl(C, kept - 1, kWave);
   int cut = kept;
@@ -384,7 +410,7 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, uint32_
   }
   const double zsum = __shfl(C, cut - 1, kWave);
   const uint64_t last = __shfl(e, cut - 1, kWave);
-  r.kcut = (uint32_t)(comp_key(last) + 0x8000);
+  r.kcut = K::bias(ckey<K>(last));
   r.idcut = (int32_t)comp_id(last);
   r.scale = scale;
   r.zsum = zsum;
@@ -490,8 +516,9 @@ __device__ __attribute__((always_inline)) inline bool row_profile(
   WaveState s;
   chunk_scan(row, V, k, 0, row_tiles(row, V), s, reg);
   if (s.overflow) return true;  // handed back: the caller profiles it exactly
-  row_finish(reg, s.n, k, s.magmax, s.umax, one_hot, smp.temperature_milli, smp.top_p_milli, x, rec,
-             sup_id, sup_p);
+  const bool nan = wave_pair_max(s.magmax) > 0x7F80 || wave_pair_max(s.umax) > 0xFF80;
+  row_finish<Key16>(reg, s.n, k, nan, 0x7F80, one_hot, smp.temperature_milli, smp.top_p_milli, x,
+                    rec, sup_id, sup_p);
   return false;
 }
 

@@ -75,6 +75,19 @@ __device__ inline void mask_tile(u32x4 (&v)[VEC], int tile, int lo, int hi) {
   }
 }
 
+// The same for a tile of binary32 logits (4 per 16-byte vector).
+template <int VEC>
+__device__ inline void mask_tile_f32(u32x4 (&v)[VEC], int tile, int lo, int hi) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int p0 = 4 * (tile * (kWave * VEC) + j * kWave + lane);  // first logit of the vector
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      if (p0 + d < lo || p0 + d >= hi) v[j][d] = 0xFF800000u;
+  }
+}
+
 // Issue priority from the work a wave has left: a SIMD's arbiter serves the
 // highest priority first and the oldest wave among equals, so with equal
 // priorities the oldest wave streams its row well ahead of the others, the

@@ -121,17 +121,23 @@ class Workload:
 
     def row_bytes_by_kernel(self, q_rows: bool = False) -> dict:
         """Row bytes read by each row kernel: the single-pass kernel takes every
-        bf16 row (the top-k class: greedy rules, temperature 0, 1 <= top_k <=
-        64; the dense class: the rest), the generic kernel the fp32 rows and
-        the bf16 rows a path hands back (not counted here: that depends on the
-        logits).  With q_rows no draft row is profiled."""
+        bf16 row, and the binary32 rows of the top-k class (greedy rule,
+        temperature 0, 1 <= top_k <= 64) or with temperature alone; the
+        generic kernel the other binary32 rows.  Rows a path hands back are not
+        counted (that depends on the logits).  With q_rows no draft row is
+        profiled."""
         m = self.m.to("cpu").to(torch.int64).numpy()
         rule = self.rule.to("cpu").to(torch.int64).numpy()
-        bf16 = self.target.dtype == torch.bfloat16
         per_session = (m + 1) + (0 if q_rows else m * (rule == 2))
         row = self.V * self.target.element_size()
         total = int(per_session.sum()) * row
-        stream = total if bf16 else 0
+        if self.target.dtype == torch.bfloat16:
+            return {"stream": total, "generic": 0}
+        s = self.sampling
+        topk_class = (rule == 1) | (s["temperature_milli"] == 0) | \
+            ((s["top_k"] >= 1) & (s["top_k"] <= 64))
+        untruncated = (s["top_p_milli"] >= 1000) & ((s["top_k"] == 0) | (s["top_k"] >= self.V))
+        stream = int(per_session[topk_class | untruncated].sum()) * row
         return {"stream": stream, "generic": total - stream}
 
 
@@ -167,9 +173,11 @@ CONFIG_NAMES = ("tiny", "b64", "b256_topk_topp", "ragged", "large")
 
 
 def make(name: str, device="cpu", sessions: int | None = None, draft_top_n: int = 8,
-         chunk_sessions: int = 32) -> Workload:
+         chunk_sessions: int = 32, logits: str | None = None) -> Workload:
     """Build a named workload.  ``sessions`` truncates B (same rows as the
-    full workload's first sessions), for CPU-sized runs of the big shapes."""
+    full workload's first sessions), for CPU-sized runs of the big shapes.
+    ``logits`` ("bf16" or "fp32") overrides the workload's element type: the
+    same draws, stored as binary32 or rounded to bf16."""
     idx = CONFIG_NAMES.index(name)
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + idx)
@@ -190,6 +198,8 @@ def make(name: str, device="cpu", sessions: int | None = None, draft_top_n: int 
     else:
         B, M, V, dt = 1024, 64, 129280, torch.bfloat16
         T, K, P = 1000, 0, 950
+    if logits is not None:
+        dt = {"bf16": torch.bfloat16, "fp32": torch.float32}[logits]
     B_full = B
     if sessions is not None:
         B = min(B, sessions)
