@@ -36,29 +36,36 @@ METRIC = "verified positions/sec (B*(M+1)/s) + achieved HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b256_topk_topp"
 
-# Counter-measured HBM traffic per launch of the dominant kernel (bytes), keyed
-# by (workload, kernel, kernel revision); filled from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE runs and valid only for the revision they were taken on.
-KERNEL_REVISION = "stream-v5"
-MEASURED_TRAFFIC = {
-    # FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000, scaled by a 1 GiB copy kernel
-    ("b256_topk_topp", "k_rows_stream", "stream-v2"): 1_119_476_736,
-    ("b256_topk_topp", "k_rows_stream", "stream-v3"): 1_119_487_488,
-    ("b256_topk_topp", "k_rows_stream", "stream-v4"): 1_119_499_072,
-    ("b256_topk_topp", "k_rows_stream", "stream-v5"): 1_119_496_295,
-    ("b64", "k_rows_split<4>", "stream-v5"): 38_273_434,
-    ("ragged", "k_rows_stream", "stream-v5"): 2_450_512_384,
-    ("large", "k_rows_stream", "stream-v5"): 34_218_138_829,
-}
-# VALU busy (rocprofv3 derived counter VALUBusy: VALU cycles over GPU-busy
-# cycles per CU, percent) of the same kernels, same keys: near 100 the kernel
-# is bound by its vector ALU work rather than by HBM.
-MEASURED_VALU_BUSY = {
-    ("b64", "k_rows_split<4>", "stream-v5"): 22.2,
-    ("b256_topk_topp", "k_rows_stream", "stream-v5"): 45.6,
-    ("ragged", "k_rows_stream", "stream-v5"): 67.0,
-    ("large", "k_rows_stream", "stream-v5"): 101.5,
-}
+# Counter readings of the row kernels (HBM bytes per launch from rocprofv3
+# FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy; VALU busy percent), kept
+# in profiles/counters.json under a hash of the row kernels' sources: a reading
+# is reported only while the sources it was taken on are unchanged.
+COUNTERS_FILE = os.path.join(HERE, "profiles", "counters.json")
+ROW_KERNEL_SOURCES = ("sv_rows_stream.hip", "sv_rows_topk.hpp", "sv_rows_topk32.hpp",
+                      "sv_rows_dense.hpp", "sv_rows_exact.hpp", "sv_stream.hpp", "sv_common.hpp",
+                      "sv_kernels.hpp", "sv_sdcp.hpp")
+CONFIG_NAMES = ("tiny", "b64", "b256_topk_topp", "ragged", "large")
+
+
+def row_kernel_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ROW_KERNEL_SOURCES:
+        with open(os.path.join(HERE, "token_sampling_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_record(workload: str):
+    """The counters recorded for this workload under the current row-kernel
+    sources, or None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec.get(row_kernel_hash(), {}).get(workload)
 
 
 def log(msg):
@@ -160,6 +167,159 @@ def cpu_baseline(w, budget_s: float, sdcp_raw=None, q_rows=None, early=False):
     }
 
 
+def measure(w, args, sv, torch, draft, q_rows=None, sdcp=None, early=None, commit=False,
+            scrub=False):
+    """Time one workload on the GPU: W warm-up steps, then K timed steps (one
+    sv_verify* call each), then K more steps with HIP events around the row
+    kernels.  scrub: inputs small enough to stay in the 256 MB last-level
+    cache are timed step by step with a 1 GiB write between steps (outside the
+    step's events), so that every step reads its rows from HBM.  Returns the
+    step time, the row kernels' times and the last step's outputs (host)."""
+    dev = w.target.device
+    B, M, V = w.B, w.M, w.V
+    smp = w.sampling_tensor(dev)
+    ws = torch.empty(sv.workspace_bytes(B, M, V), dtype=torch.uint8, device=dev)
+    out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "out_tokens": torch.empty((B, M + 1), dtype=torch.int32, device=dev)}
+    stream = torch.cuda.current_stream(dev)
+    contracts = states = cres = None
+    if commit:
+        contracts = sv.make_contracts(B, m_max=M, max_new=1 << 30, low_rounds=3, stop=(),
+                                      device=dev)
+        states = sv.make_states(B, m_cap=M, device=dev)
+        cres = {"emitted_len": torch.empty(B, dtype=torch.int32, device=dev),
+                "action": torch.empty(B, dtype=torch.int32, device=dev)}
+
+    def step(ev=None):
+        sv.verify(w.target, draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
+                  workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp,
+                  q_rows=q_rows, early=early)
+        if commit:
+            sv.commit(contracts, states, w.m, out["accepted_len"], out["out_tokens"],
+                      stream=stream, out=cres)
+
+    junk = torch.empty(1 << 28, dtype=torch.float32, device=dev) if scrub else None
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # bf16 rows are all taken by the single-pass kernel: two events bracket it;
+    # binary32 rows may also take the generic kernel: a third event between the
+    # two.  Read in order, two events bracket all the windows' row and advance
+    # kernels.
+    n_ev = 2 if (w.target.dtype == torch.bfloat16 or early) else 3
+    row_ev = [tuple(sv.HipEvent() for _ in range(n_ev)) for _ in range(args.steps)]
+    if scrub:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for k in range(args.steps):
+            junk.fill_(float(k))
+            ev[k][0].record(stream)
+            step()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    else:
+        # the timed region: exactly K steps, with no event inside a step (an
+        # event recorded between two kernels of a step adds about 5 us to it)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(stop) / args.steps
+    for k in range(args.steps):
+        if scrub:
+            junk.fill_(float(k))
+        step(row_ev[k])
+    torch.cuda.synchronize()
+    stream_ms = sum(e[0].elapsed_ms(e[1]) for e in row_ev) / args.steps
+    generic_ms = 0.0 if n_ev == 2 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
+    del junk
+    return {"ms_per_step": ms_per_step, "stream_ms": stream_ms, "generic_ms": generic_ms,
+            "accepted_len": out["accepted_len"].cpu().numpy(),
+            "out_tokens": out["out_tokens"].cpu().numpy()}
+
+
+def roofline(w, r, qrows=False, early=False):
+    """The dominant row kernel's algorithmic rate: the bytes of the rows it
+    handles, each once, over its average duration (HIP events on the launch
+    stream)."""
+    import numpy as np
+
+    B, M = w.B, w.M
+    split = w.row_bytes_by_kernel(q_rows=qrows)
+    stream_ms, generic_ms = r["stream_ms"], r["generic_ms"]
+    kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
+                          else ("k_rows_generic", generic_ms, split["generic"]))
+    rows = B * (M + 1) + (B * M if not qrows else 0)
+    if kname == "k_rows_stream" and w.target.dtype.itemsize == 2 and rows < 1024:
+        kname = "k_rows_split<4>"  # bf16 launches under 1024 row slots split each row
+    if early:
+        # read in order, the rows a session needs are its first a+1 target rows
+        # and (rule 2 with draft logits) as many draft rows; failed sessions are
+        # counted as reading nothing
+        an = r["accepted_len"].astype(np.int64)
+        ok = an >= 0
+        e = an + 1
+        mm = w.m.cpu().numpy().astype(np.int64)
+        r2 = w.rule.cpu().numpy() == 2
+        rows_needed = e[ok].sum()
+        if not qrows:
+            rows_needed += np.minimum(e, mm)[ok & r2].sum()
+        kname = "row kernels, all windows"
+        kms = stream_ms + generic_ms
+        kbytes = int(rows_needed) * w.V * w.target.element_size()
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "kernel": kname, "ms_per_launch": kms,
+            "algorithmic_bytes_per_launch": kbytes,
+            "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_generic": generic_ms}}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def oracle_config(w, gpu, budget_1core: float):
+    """The oracle (run unchanged) on this workload: single-threaded on its first
+    sessions for about budget_1core seconds, then over every session on the
+    host's threads (at most 16; B=1024, M=64: the oracle's in-order reading,
+    which gives the same verdicts where every row is usable), with the GPU's
+    accepted_len and out_tokens compared session by session."""
+    import contextlib
+
+    from tests import parity
+
+    one = cpu_baseline(w, budget_1core) if budget_1core > 0 else None
+    early = w.name == "large"
+    threads = parity.host_threads()
+    t0 = time.perf_counter()
+    o = parity.run_oracle_sessions(w, early=early)
+    elapsed = time.perf_counter() - t0
+    with contextlib.redirect_stdout(sys.stderr):  # stdout carries the one JSON line
+        rep = parity.compare({"accepted_len": gpu["accepted_len"],
+                              "out_tokens": gpu["out_tokens"]}, o, w.name, strict=False)
+    P = w.positions()
+    return {
+        "oracle_1core_positions_per_s": None if one is None else one["value"],
+        "oracle_all_positions_per_s": P / elapsed,
+        "oracle_threads": threads,
+        "oracle_reading": "in order" if early else "every row",
+        "sessions_checked": rep["sessions"], "mismatches": rep["mismatches"],
+        "excused_by_kind": rep["excused"], "near_ties_by_kind": rep["near_ties"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +329,9 @@ def main():
     ap.add_argument("--logits", choices=("bf16", "fp32"), default=None,
                     help="store the workload's logits as bf16 or binary32 (default: the "
                          "workload's own type)")
+    ap.add_argument("--configs", choices=("all", "none"), default=None,
+                    help="also time the five workloads and check them against the oracle "
+                         "(default: all, unless a single-workload option is given)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=1,
@@ -188,8 +351,8 @@ def main():
                     help="time sv_verify_qrows: draft distributions as published binary32 rows "
                          "(the synthetic drafter's own distribution) instead of draft logits")
     ap.add_argument("--early", type=int, default=None, metavar="W",
-                    help="time sv_verify_early: positions read in order, in windows of W, 2W, "
-                         "4W, ... positions, each only for the sessions still undecided")
+                    help="time sv_verify_early: positions read in order, in windows of W, 4W, "
+                         "16W, ... positions, each only for the sessions still undecided")
     ap.add_argument("--commit", action="store_true",
                     help="add the commit step (sv_commit: truncation, digest chain, counters) "
                          "to every step, with per-session state carried across steps")
@@ -200,6 +363,9 @@ def main():
               "the verifier step shards by session with no exchange, so N GPUs run N "
               "independent copies of this single-GPU step.", file=sys.stderr)
         sys.exit(2)
+    single = (args.sdcp or args.qrows or args.early or args.commit or args.sessions or
+              args.logits or args.copy_calibration or args.workload != DEFAULT_WORKLOAD)
+    run_configs = (args.configs == "all") or (args.configs is None and not single)
 
     import torch
 
@@ -215,97 +381,21 @@ def main():
 
     log(f"[bench] building workload {args.workload}")
     w = W.make(args.workload, device="cuda", sessions=args.sessions, logits=args.logits)
-    smp = w.sampling_tensor(dev)
     B, M, V = w.B, w.M, w.V
     P = w.positions()
-    ws = torch.empty(sv.workspace_bytes(B, M, V), dtype=torch.uint8, device=dev)
-    out = {"accepted_len": torch.empty(B, dtype=torch.int32, device=dev),
-           "out_tokens": torch.empty((B, M + 1), dtype=torch.int32, device=dev)}
-    stream = torch.cuda.current_stream(dev)
     sdcp = None
     if args.sdcp:
         import numpy as np
 
         ids = np.random.default_rng(w.seed & 0xFFFFFFFF).integers(0, 256, (B, 16), dtype=np.uint8)
         sdcp = sv.make_sdcp_sessions(B, seed=w.seed, round_=w.round, session_ids=ids, device=dev)
-
     q_rows = w.drafter_q_rows() if args.qrows else None
     draft = None if args.qrows else w.draft
 
-    contracts = states = cres = None
-    if args.commit:
-        contracts = sv.make_contracts(B, m_max=M, max_new=1 << 30, low_rounds=3, stop=(),
-                                      device=dev)
-        states = sv.make_states(B, m_cap=M, device=dev)
-        cres = {"emitted_len": torch.empty(B, dtype=torch.int32, device=dev),
-                "action": torch.empty(B, dtype=torch.int32, device=dev)}
-
-    def step(ev=None):
-        sv.verify(w.target, draft, w.tokens, w.m, w.rule, smp, w.seed, w.round,
-                  workspace=ws, out=out, stream=stream, row_events=ev, sdcp_sessions=sdcp,
-                  q_rows=q_rows, early=args.early)
-        if args.commit:
-            sv.commit(contracts, states, w.m, out["accepted_len"], out["out_tokens"],
-                      stream=stream, out=cres)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-
-    # bf16 rows are all taken by the single-pass kernel: two events bracket it;
-    # fp32 rows go to the generic kernel: a third event between the two.  Read
-    # in order, two events bracket all the windows' row and advance kernels.
-    bf16 = w.target.dtype == torch.bfloat16
-    n_ev = 2 if (bf16 or args.early) else 3
-    row_ev = [tuple(sv.HipEvent() for _ in range(n_ev)) for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    # the timed region: exactly K steps, with no event inside a step (an event
-    # recorded between two kernels of a step adds about 5 us to it)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for k in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-    # then K more steps, outside the timed region, with HIP events around the
-    # row kernels for the roofline line
-    for k in range(args.steps):
-        step(row_ev[k])
-    torch.cuda.synchronize()
-    stream_ms = sum(e[0].elapsed_ms(e[1]) for e in row_ev) / args.steps
-    generic_ms = 0.0 if n_ev == 2 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, single-pass row kernel "
-        f"{stream_ms:.4f} ms, generic row kernel {generic_ms:.4f} ms")
-
-    # the dominant kernel: the row kernel that takes longer; its algorithmic
-    # bytes are the rows it handles
-    split = w.row_bytes_by_kernel(q_rows=args.qrows)
-    kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
-                          else ("k_rows_generic", generic_ms, split["generic"]))
-    if kname == "k_rows_stream" and B * (M + 1) + (B * M if draft is not None else 0) < 1024:
-        kname = "k_rows_split<4>"  # launches under 1024 row slots split each row over 4 waves
-    a = out["accepted_len"].cpu()
-    if args.early:
-        # read in order, the rows a session needs are its first a+1 target rows
-        # and (rule 2 with draft logits) as many draft rows; failed sessions are
-        # counted as reading nothing
-        import numpy as np
-
-        an = a.numpy().astype(np.int64)
-        ok = an >= 0
-        e = an + 1
-        mm = w.m.cpu().numpy().astype(np.int64)
-        r2 = w.rule.cpu().numpy() == sv.RULE_SPECULATIVE
-        rows_needed = e[ok].sum()
-        if not args.qrows:
-            rows_needed += np.minimum(e, mm)[ok & r2].sum()
-        kname = "row kernels, all windows"
-        kms = stream_ms + generic_ms
-        kbytes = int(rows_needed) * V * w.target.element_size()
+    r = measure(w, args, sv, torch, draft, q_rows=q_rows, sdcp=sdcp, early=args.early,
+                commit=args.commit)
+    log(f"[bench] {args.steps} steps: {r['ms_per_step']:.4f} ms/step, single-pass row kernel "
+        f"{r['stream_ms']:.4f} ms, generic row kernel {r['generic_ms']:.4f} ms")
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -315,18 +405,21 @@ def main():
         del src, dst
         log("[bench] copy calibration: 3 x (1 GiB read + 1 GiB written)")
 
-    achieved = kbytes / (kms * 1e-3) / 1e9
-    measured = not (args.sdcp or args.qrows or args.early or args.sessions)
-    traffic = MEASURED_TRAFFIC.get((args.workload, kname, KERNEL_REVISION)) if measured else None
-    valu_busy = MEASURED_VALU_BUSY.get((args.workload, kname, KERNEL_REVISION)) if measured else None
+    roof = roofline(w, r, qrows=args.qrows, early=args.early)
+    rec = None if (args.sdcp or args.qrows or args.early or args.sessions or args.logits) \
+        else counter_record(args.workload)
+    roof["traffic"] = rec.get("traffic") if rec else None
+    roof["valu_busy_pct"] = rec.get("valu_busy_pct") if rec else None
+    roof["counters_for_sources"] = row_kernel_hash()
+    a = r["accepted_len"]
     result = {
         "metric": METRIC,
-        "value": P / (ms_per_step * 1e-3),
+        "value": P / (r["ms_per_step"] * 1e-3),
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -339,16 +432,12 @@ def main():
             "draft": "q_rows fp32" if args.qrows else "logits",
             "commit_step": bool(args.commit),
             "reading": f"in order, first window {args.early}" if args.early else "every row",
-            "positions_per_step": P, "algorithmic_bytes_per_step": w.algorithmic_bytes(q_rows=args.qrows),
-            "mean_accepted": float(a[a >= 0].float().mean()) if (a >= 0).any() else None,
+            "positions_per_step": P,
+            "algorithmic_bytes_per_step": w.algorithmic_bytes(q_rows=args.qrows),
+            "mean_accepted": float(a[a >= 0].mean()) if (a >= 0).any() else None,
             "bad_proposals": int((a == sv.S_BAD_PROPOSAL).sum()),
         },
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "valu_busy_pct": valu_busy,
-            "kernel": kname, "ms_per_launch": kms, "algorithmic_bytes_per_launch": kbytes,
-            "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_generic": generic_ms},
-        },
+        "roofline": roof,
     }
     if args.cpu_budget > 0:
         log(f"[bench] oracle CPU baseline (~{args.cpu_budget:.0f} s)")
@@ -359,8 +448,52 @@ def main():
             result["cpu_baseline"] = cpu_baseline(
                 w, args.cpu_budget, None if sdcp is None else sdcp.cpu().numpy(), q_rows,
                 early=bool(args.early))
+            if run_configs:
+                from tests import parity
+
+                result["cpu_baseline"]["all_cores"] = cpu_baseline_threads(
+                    w, max(2.0, args.cpu_budget / 3), parity.host_threads())
     else:
         result["cpu_baseline"] = None
+
+    if run_configs:
+        configs = {}
+        del w, draft, q_rows, r
+        torch.cuda.empty_cache()
+        for name in CONFIG_NAMES:
+            log(f"[bench] config {name}")
+            wc = W.make(name, device="cuda")
+            small = wc.algorithmic_bytes() < (1 << 30)
+            rc = measure(wc, args, sv, torch, wc.draft, scrub=small)
+            roofc = roofline(wc, rc)
+            recc = counter_record(name)
+            ac = rc["accepted_len"]
+            Pc = wc.positions()
+            ent = {
+                "B": wc.B, "M": wc.M, "V": wc.V,
+                "logits": "bf16" if wc.target.dtype == torch.bfloat16 else "fp32",
+                "positions_per_step": Pc, "ms_per_step": rc["ms_per_step"],
+                "positions_per_s": Pc / (rc["ms_per_step"] * 1e-3),
+                "algorithmic_bytes_per_step": wc.algorithmic_bytes(),
+                "step_gbs": wc.algorithmic_bytes() / (rc["ms_per_step"] * 1e-3) / 1e9,
+                "step_frac": wc.algorithmic_bytes() / (rc["ms_per_step"] * 1e-3) / 1e9
+                / HBM_PEAK_GBS,
+                "cold_hbm": "1 GiB written between steps" if small else "inputs exceed the cache",
+                "row_kernel": roofc["kernel"], "row_kernel_ms": roofc["ms_per_launch"],
+                "row_kernel_gbs": roofc["achieved"], "row_kernel_frac": roofc["frac"],
+                "traffic": recc.get("traffic") if recc else None,
+                "valu_busy_pct": recc.get("valu_busy_pct") if recc else None,
+                "mean_accepted": float(ac[ac >= 0].mean()) if (ac >= 0).any() else None,
+                "bad_proposals": int((ac == sv.S_BAD_PROPOSAL).sum()),
+            }
+            if args.cpu_budget > 0:
+                ent.update(oracle_config(wc, rc, budget_1core=min(5.0, args.cpu_budget / 3)))
+            configs[name] = ent
+            log(f"[bench] {name}: {json.dumps(ent)}")
+            del wc, rc
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+        result["host"] = {"cpu_model": cpu_model(), "cpu_count": os.cpu_count()}
     print(json.dumps(result), flush=True)
 
 

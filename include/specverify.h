@@ -322,6 +322,27 @@ int sv_prefix_digest(const uint8_t *contract_digest, const int32_t *prompt, uint
  * HOST memory; runs on the host.  Returns SV_OK or SV_ERR_ARG. */
 int sv_contract_digest(const uint8_t *cbor, size_t len, uint8_t *out);
 
+/*
+ * sv_verify for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call without a workspace argument.  Its workspace is a device array
+ * inside the library, SV_NOALLOC_WORKSPACE_MAX bytes per GPU, set up on the
+ * first call on each device and held until the process ends; the call itself
+ * allocates and frees nothing.  Every call on one GPU shares that GPU's array
+ * (a later call overwrites it; the kernels need none of its contents at the
+ * start of a call), so calls that overlap on one GPU (other streams or host
+ * threads) race and must be serialised by the caller.  Arguments, outputs,
+ * statuses and return codes are those of sv_verify, plus SV_ERR_WORKSPACE
+ * when sv_workspace_bytes(B, M, V) > SV_NOALLOC_WORKSPACE_MAX, and
+ * SV_ERR_DEVICE when the array's device address cannot be obtained.
+ */
+#define SV_NOALLOC_WORKSPACE_MAX (128u << 20) /* bytes: B=1024, M=64, V=129280 needs 108 MiB */
+int sv_verify_noalloc(const void *target_logits, const void *draft_logits, int32_t dtype,
+                      const int32_t *draft_tokens, const int32_t *m, const int32_t *rule,
+                      const sv_sampling *sampling, int32_t B, int32_t M, int32_t V, uint64_t seed,
+                      uint32_t round, int32_t *accepted_len, int32_t *out_tokens,
+                      const sv_probe *probe, void *stream);
+
 /* Benchmark hook, not part of the acceptance step: hipEvent_t handles that
  * the sv_verify* calls made afterwards from the calling host thread record on
  * their launch stream, immediately before the row-profile kernels (start),

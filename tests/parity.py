@@ -221,8 +221,9 @@ def near_ties(o):
     return out
 
 
-def compare(g, o, label="", prob_rtol=PROB_RTOL):
-    """Return a report dict; raises AssertionError on an unexcused mismatch."""
+def compare(g, o, label="", prob_rtol=PROB_RTOL, strict=True):
+    """Return a report dict; raises AssertionError on an unexcused mismatch
+    (strict; otherwise the report counts them)."""
     B = o["accepted_len"].shape[0]
     mism, excused = [], []
     for b in range(B):
@@ -272,6 +273,8 @@ def compare(g, o, label="", prob_rtol=PROB_RTOL):
                mismatches=len(mism), excused=by_kind, near_ties=near_ties(o),
                max_prob_rel=max_rel, prob_at_near_tie_cut=prob_at_cut)
     log(f"[parity] {rep}")
+    if not strict:
+        return rep
     detail = [(b, d, k, int(g["accepted_len"][b]), int(o["accepted_len"][b]),
                g["out_tokens"][b].tolist(), o["out_tokens"][b].tolist()) for b, d, k in mism[:5]]
     assert not mism, (f"{label}: unexcused mismatches (session, delta of the first differing "

@@ -231,3 +231,18 @@ def test_product_path_does_not_import_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "sv_oracle" not in text and "ov_verify" not in text, path
+
+
+def test_noalloc_refuses_on_the_host(svlib):
+    """sv_verify_noalloc refuses sizes beyond its device array, and bad sizes,
+    before any device call."""
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+    B, M, V = 1 << 20, 8, 1 << 20
+    assert svlib.workspace_bytes(B, M, V) > (128 << 20)
+    assert L.sv_verify_noalloc(fake, fake, 0, fake, fake, fake, fake, B, M, V, 0, 1, fake, fake,
+                               None, None) == svlib.ERR_WORKSPACE
+    assert L.sv_verify_noalloc(fake, fake, 0, fake, fake, fake, fake, 0, M, V, 0, 1, fake, fake,
+                               None, None) == svlib.ERR_ARG
+    assert L.sv_verify_noalloc(fake, fake, 7, fake, fake, fake, fake, 4, M, 100, 0, 1, fake, fake,
+                               None, None) == svlib.ERR_ARG

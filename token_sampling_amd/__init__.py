@@ -64,7 +64,7 @@ STATE_DTYPE = np.dtype(
 EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows",
             "sv_verify_early", "sv_commit",
             "sv_prefix_digest", "sv_contract_digest", "sv_strerror", "sv_status_str",
-            "sv_version", "sv_bench_row_events")
+            "sv_version", "sv_bench_row_events", "sv_verify_noalloc")
 
 
 class SvError(RuntimeError):
@@ -169,6 +169,13 @@ def lib():
         L.sv_version.restype = ctypes.c_int
         L.sv_bench_row_events.argtypes = [ctypes.c_void_p] * 3
         L.sv_bench_row_events.restype = ctypes.c_int
+        L.sv_verify_noalloc.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 

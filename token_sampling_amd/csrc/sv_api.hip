@@ -12,6 +12,7 @@
 #include <limits.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "sv_kernels.hpp"
 
@@ -221,6 +222,58 @@ extern "C" int sv_verify_early(const void* target_logits, const void* draft_logi
   return sv::verify_impl(target_logits, draft_logits, q_rows, dtype, draft_tokens, m, rule,
                          sampling, sessions, B, M, V, seed, round, accepted_len, out_tokens,
                          workspace, workspace_bytes, probe, stream, window0);
+}
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing (sv_verify_noalloc): its workspace is
+// a file-scope device array, one per GPU, held until the process ends.  Host
+// code never uses the array's name as an address: on the first call on each
+// device, with that device current, hipGetSymbolAddress gives this device's
+// copy, kept per device and passed to the kernels like a caller's workspace.
+namespace sv {
+constexpr size_t kScratchBytes = (size_t)SV_NOALLOC_WORKSPACE_MAX;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices] = {};
+static std::mutex g_scratch_mu;
+
+// This device's copy of scratch, or null (with *rc set) if it cannot be had.
+static void* device_scratch(int* rc) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *rc = SV_ERR_DEVICE;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      *rc = SV_ERR_DEVICE;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace sv
+
+extern "C" int sv_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                 int32_t dtype, const int32_t* draft_tokens, const int32_t* m,
+                                 const int32_t* rule, const sv_sampling* sampling, int32_t B,
+                                 int32_t M, int32_t V, uint64_t seed, uint32_t round,
+                                 int32_t* accepted_len, int32_t* out_tokens, const sv_probe* probe,
+                                 void* stream) {
+  if (!target_logits || !draft_tokens || !m || !rule || !sampling || !accepted_len ||
+      !out_tokens || !sv::sizes_ok(B, M, V, dtype))
+    return SV_ERR_ARG;
+  if (sv::workspace_layout(B, M, V).total > sv::kScratchBytes) return SV_ERR_WORKSPACE;
+  int rc = SV_OK;
+  void* ws = sv::device_scratch(&rc);
+  if (!ws) return rc;
+  return sv::verify_impl(target_logits, draft_logits, nullptr, dtype, draft_tokens, m, rule,
+                         sampling, nullptr, B, M, V, seed, round, accepted_len, out_tokens, ws,
+                         sv::kScratchBytes, probe, stream);
 }
 
 extern "C" int sv_bench_row_events(void* start, void* mid, void* stop) {
