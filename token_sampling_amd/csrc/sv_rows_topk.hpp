@@ -47,8 +47,14 @@ using namespace stream;
 constexpr int kVec = SV_TOPK_VEC;          // 16-byte loads per lane per tile
 constexpr int kNBuf = SV_TOPK_NBUF;        // tiles in the load ring (kNBuf - 1 in flight)
 constexpr int kTile = kWave * kVec * 8;    // bf16 logits per tile
-constexpr int kCap = 256;                  // candidate entries per wave
+#ifndef SV_TOPK_CAP
+#define SV_TOPK_CAP 256
+#endif
+constexpr int kCap = SV_TOPK_CAP;          // candidate entries per wave
 constexpr int kMinKey = -0x7F7F;           // smallest finite key (-inf is -0x7F80)
+#ifndef SV_TOPK_LOOSE_CUT
+#define SV_TOPK_LOOSE_CUT 1  // cuts during the stream keep every tie at the k-th key
+#endif
 #ifndef SV_TOPK_BOUND_TILES
 #define SV_TOPK_BOUND_TILES 4
 #endif
@@ -87,7 +93,11 @@ struct Cut {
 // Cut the region reg[0..n) to its k best entries (k <= 64, n <= kCap) and
 // compact them to the front; empty entries (0) are dropped.  An odd count is
 // followed by one empty entry so that pair stores stay 16-byte aligned.
-template <class K = Key16>
+// kExact = false (the cuts during the stream) keeps every tie at the k-th key
+// instead of the smallest ids among them, which skips the search over ids:
+// later tokens must beat that key strictly, and a later token tied with it has
+// a larger id than k kept entries, so the k best of the row are still there.
+template <class K = Key16, bool kExact = true>
 __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, int k) {
   const int lane = __lane_id();
   uint64_t e[kCap / kWave];
@@ -103,21 +113,39 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
   uint32_t t = 0, lowcut = 0;
   int kth = K::unbias(0);
   if (live > k) {
-    for (int bit = K::kBits - 1; bit >= 0; --bit) {  // k-th largest biased key, bit by bit
+    // the k-th largest biased key lies between the smallest and the largest
+    // present, so it has their common leading bits: search the bits below
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < kCap / kWave; ++i) {
+      const uint32_t h = (uint32_t)(e[i] >> 32);
+      if (e[i]) {
+        lo = min(lo, h);
+        hi = max(hi, h);
+      }
+    }
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
+    }
+    const uint32_t diff = __builtin_amdgcn_readfirstlane(lo ^ hi);
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;
+    t = (uint32_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hi) >> (top + 1)) << (top + 1));
+    for (int bit = top; bit >= 0; --bit) {  // k-th largest biased key, bit by bit
       const uint32_t cand = t | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int i = 0; i < kCap / kWave; ++i) cnt += popc64(__ballot((uint32_t)(e[i] >> 32) >= cand));
       if (cnt >= k) t = cand;
     }
-    int gt = 0, eq = 0;
+  int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kCap / kWave; ++i) {
       gt += popc64(__ballot((uint32_t)(e[i] >> 32) > t));
       eq += popc64(__ballot((uint32_t)(e[i] >> 32) == t));
     }
     const int need = k - gt;  // ties kept at key t, smallest ids first
-    if (eq > need) {
+    if (kExact && eq > need) {
       uint32_t u = 0;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = u | (1u << bit);
@@ -264,13 +292,15 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
     int c = lm >= te ? slots_ge(v, te) : 0;
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     if (s.n + c > kCap && s.n >= k) {
-      const Cut ct = region_cut(reg, s.n, k);
-      s.n = __builtin_amdgcn_readfirstlane((ct.n + 1) & ~1);
-      s.thr = ct.kth;
-      s.strict = true;
+      Cut ct = region_cut<Key16, !SV_TOPK_LOOSE_CUT>(reg, s.n, k);
       te = max(ct.kth + 1, kMinKey);
       c = lm >= te ? slots_ge(v, te) : 0;
       for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+      // ties at the k-th key left too little room: cut to exactly k
+      if (((ct.n + 1) & ~1) + c > kCap) ct = region_cut<Key16, true>(reg, ct.n, k);
+      s.n = __builtin_amdgcn_readfirstlane((ct.n + 1) & ~1);
+      s.thr = ct.kth;
+      s.strict = true;
     }
     if (s.n + c > kCap) {
       s.overflow = true;

@@ -126,13 +126,15 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
     int c = lm >= te ? slots_ge(v, te) : 0;
     for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
     if (s.n + c > kCap && s.n >= k) {
-      const topk::Cut ct = topk::region_cut<Key32>(reg, s.n, k);
-      s.n = __builtin_amdgcn_readfirstlane(ct.n);
-      s.thr = ct.kth;
-      s.strict = true;
+      topk::Cut ct = topk::region_cut<Key32, false>(reg, s.n, k);
       te = max(ct.kth + 1, kMinKey);
       c = lm >= te ? slots_ge(v, te) : 0;
       for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+      // ties at the k-th key left too little room: cut to exactly k
+      if (ct.n + c > kCap) ct = topk::region_cut<Key32, true>(reg, ct.n, k);
+      s.n = __builtin_amdgcn_readfirstlane(ct.n);
+      s.thr = ct.kth;
+      s.strict = true;
     }
     if (s.n + c > kCap) {
       s.overflow = true;
