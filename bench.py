@@ -57,6 +57,71 @@ def row_kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_short_name(full: str) -> str:
+    import re
+
+    m = re.search(r"(k_rows_stream|k_rows_split<\d+>|k_rows_generic|k_finalize|k_advance|k_commit)",
+                  full)
+    return m.group(1) if m else ""
+
+
+def ingest_counters(root: str) -> dict:
+    """Counter passes of this benchmark, as rocprofv3 --pmc writes them: under
+    root, for each workload W, fetch_W, write_W and valu_W (FETCH_SIZE,
+    WRITE_SIZE and VALUBusy, one pass each, every run with --copy-calibration
+    for the first two).  Bytes per dispatch are scaled by what the same counter
+    reads for the calibration copy (torch.neg over 2^28 float32: 1 GiB read,
+    1 GiB written); each kernel's figure is the median over its dispatches
+    after the first.  Returns {W: {kernel: {...}}}."""
+    import csv
+    import glob
+    import statistics
+
+    def passes(kind, w):
+        files = glob.glob(os.path.join(root, f"{kind}_{w}", "**", "*counter_collection.csv"),
+                          recursive=True)
+        per = {}
+        for fn in files:
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    per.setdefault((r["Kernel_Name"], int(r["Dispatch_Id"])), 0.0)
+                    per[(r["Kernel_Name"], int(r["Dispatch_Id"]))] += float(r["Counter_Value"])
+        by_kernel = {}
+        for (name, disp), v in sorted(per.items(), key=lambda kv: kv[0][1]):
+            by_kernel.setdefault(name, []).append(v)
+        return by_kernel
+
+    out = {}
+    for w in CONFIG_NAMES:
+        fetch, write, valu = passes("fetch", w), passes("write", w), passes("valu", w)
+        if not fetch or not write:
+            continue
+
+        def copy_value(table):
+            vals = [v for name, vs in table.items() if "neg" in name.lower() for v in vs]
+            return statistics.median(vals) if vals else None
+
+        fcopy, wcopy = copy_value(fetch), copy_value(write)
+        if not fcopy or not wcopy:
+            continue
+        fscale, wscale = (1 << 20) / fcopy, (1 << 20) / wcopy
+        rec = {}
+        for name, vs in fetch.items():
+            short = kernel_short_name(name)
+            if not short:
+                continue
+            fk = statistics.median(vs[1:] or vs)
+            wk = statistics.median((write.get(name) or [0.0])[1:] or write.get(name) or [0.0])
+            ent = {"fetch_kib": fk, "write_kib": wk, "fetch_scale": fscale, "write_scale": wscale,
+                   "traffic": int(round(fk * 1024 * fscale + wk * 1024 * wscale))}
+            vv = valu.get(name)
+            if vv:
+                ent["valu_busy_pct"] = statistics.median(vv[1:] or vv)
+            rec[short] = ent
+        out[w] = rec
+    return out
+
+
 def counter_record(workload: str):
     """The counters recorded for this workload under the current row-kernel
     sources, or None."""
@@ -66,6 +131,11 @@ def counter_record(workload: str):
     except (OSError, ValueError):
         return None
     return rec.get(row_kernel_hash(), {}).get(workload)
+
+
+def counters_for(workload: str, kname: str):
+    rec = counter_record(workload)
+    return (rec or {}).get(kname)
 
 
 def log(msg):
@@ -356,7 +426,24 @@ def main():
     ap.add_argument("--commit", action="store_true",
                     help="add the commit step (sv_commit: truncation, digest chain, counters) "
                          "to every step, with per-session state carried across steps")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="read rocprofv3 counter passes under DIR (fetch_W, write_W, valu_W) and "
+                         "record them in profiles/counters.json under the current row-kernel "
+                         "sources; no GPU work")
     args = ap.parse_args()
+
+    if args.ingest_counters:
+        rec = ingest_counters(args.ingest_counters)
+        try:
+            with open(COUNTERS_FILE) as f:
+                allrec = json.load(f)
+        except (OSError, ValueError):
+            allrec = {}
+        allrec.setdefault(row_kernel_hash(), {}).update(rec)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(allrec, f, indent=1, sort_keys=True)
+        print(json.dumps({"sources": row_kernel_hash(), "workloads": sorted(rec)}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -407,7 +494,7 @@ def main():
 
     roof = roofline(w, r, qrows=args.qrows, early=args.early)
     rec = None if (args.sdcp or args.qrows or args.early or args.sessions or args.logits) \
-        else counter_record(args.workload)
+        else counters_for(args.workload, roof["kernel"])
     roof["traffic"] = rec.get("traffic") if rec else None
     roof["valu_busy_pct"] = rec.get("valu_busy_pct") if rec else None
     roof["counters_for_sources"] = row_kernel_hash()
@@ -466,7 +553,7 @@ def main():
             small = wc.algorithmic_bytes() < (1 << 30)
             rc = measure(wc, args, sv, torch, wc.draft, scrub=small)
             roofc = roofline(wc, rc)
-            recc = counter_record(name)
+            recc = counters_for(name, roofc["kernel"])
             ac = rc["accepted_len"]
             Pc = wc.positions()
             ent = {
