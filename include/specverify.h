@@ -310,6 +310,40 @@ int sv_commit(const sv_contract *contracts, sv_session_state *states, const int3
               const int32_t *accepted_len, int32_t *out_tokens, const uint8_t *self_decode_ok,
               int32_t B, int32_t M, int32_t *emitted_len, int32_t *action, void *stream);
 
+/* The commit step's arrays for sv_verify_commit (a HOST struct of DEVICE
+ * pointers): contracts [B], states [B] (read and updated), self_decode_ok [B]
+ * or NULL (never permitted); outputs emitted_len [B] and action [B].  Their
+ * meaning is sv_commit's. */
+typedef struct sv_commit_io {
+  const sv_contract *contracts;
+  sv_session_state *states;
+  const uint8_t *self_decode_ok;
+  int32_t *emitted_len;
+  int32_t *action;
+} sv_commit_io;
+
+/*
+ * One round's acceptance step and commit step in one call (SDCP Sec. 6.3
+ * steps 5-8): sv_verify (sessions == NULL: Philox values from seed and round)
+ * or sv_verify_sdcp (sessions != NULL: the Sec. 6.4 values; seed and round are
+ * ignored), then sv_commit on its verdict, with the same arguments, outputs,
+ * statuses and results, bit for bit.  The difference is only where the work
+ * runs: the commit's digest links over the drafted tokens (Sec. 4.2) do not
+ * depend on the verdict, so the row kernel's first workgroups compute them,
+ * one session per work-item, while the rows stream; after the verdict each
+ * session links at most the additional token.  These links read the states
+ * and contracts while the row kernel runs, so nothing else may write them
+ * during the call.  The workspace (sv_workspace_bytes) holds the links.
+ * Returns SV_OK, SV_ERR_ARG (as sv_verify, or a null commit pointer or
+ * member other than self_decode_ok), SV_ERR_WORKSPACE or SV_ERR_DEVICE.
+ */
+int sv_verify_commit(const void *target_logits, const void *draft_logits, int32_t dtype,
+                     const int32_t *draft_tokens, const int32_t *m, const int32_t *rule,
+                     const sv_sampling *sampling, const sv_sdcp_session *sessions, int32_t B,
+                     int32_t M, int32_t V, uint64_t seed, uint32_t round, int32_t *accepted_len,
+                     int32_t *out_tokens, const sv_commit_io *commit, void *workspace,
+                     size_t workspace_bytes, const sv_probe *probe, void *stream);
+
 /* d[0] of SDCP Sec. 4.2: SHA-256("SDCP-PREFIX-1" || 0x00 || contract_digest ||
  * uint32(P) || uint32(prompt[0]) || ... ), integers in network byte order.
  * HOST memory: contract_digest[32], prompt[P], out[32].  Runs on the host.

@@ -60,6 +60,18 @@ int main() {
                            nullptr, nullptr) == SV_ERR_WORKSPACE);
   EXPECT(sv_verify_noalloc(f, f, 9, fi, fi, fi, fs, 4, 4, 100, 0, 1, fo, fo, nullptr, nullptr) ==
          SV_ERR_ARG);
+  {
+    sv_commit_io io = {(const sv_contract*)f, (sv_session_state*)f, nullptr, fo, fo};
+    EXPECT(sv_verify_commit(f, f, SV_BF16, fi, fi, fi, fs, nullptr, 4, 4, 100, 0, 1, fo, fo,
+                            nullptr, f, ws, nullptr, nullptr) == SV_ERR_ARG);
+    EXPECT(sv_verify_commit(f, f, SV_BF16, fi, fi, fi, fs, nullptr, 0, 4, 100, 0, 1, fo, fo, &io,
+                            f, ws, nullptr, nullptr) == SV_ERR_ARG);
+    EXPECT(sv_verify_commit(f, f, SV_BF16, fi, fi, fi, fs, nullptr, 4, 4, 100, 0, 1, fo, fo, &io,
+                            f, 16, nullptr, nullptr) == SV_ERR_WORKSPACE);
+    io.action = nullptr;
+    EXPECT(sv_verify_commit(f, f, SV_BF16, fi, fi, fi, fs, nullptr, 4, 4, 100, 0, 1, fo, fo, &io,
+                            f, ws, nullptr, nullptr) == SV_ERR_ARG);
+  }
   EXPECT(sv_commit(nullptr, nullptr, fi, fi, fo, nullptr, 4, 4, fo, fo, nullptr) == SV_ERR_ARG);
   EXPECT(sv_commit((const sv_contract*)f, (sv_session_state*)f, fi, fi, fo, nullptr, 4, 65, fo, fo,
                    nullptr) == SV_ERR_ARG);

@@ -246,3 +246,28 @@ def test_noalloc_refuses_on_the_host(svlib):
                                None, None) == svlib.ERR_ARG
     assert L.sv_verify_noalloc(fake, fake, 7, fake, fake, fake, fake, 4, M, 100, 0, 1, fake, fake,
                                None, None) == svlib.ERR_ARG
+
+
+def test_verify_commit_refuses_on_the_host(svlib):
+    """sv_verify_commit refuses a null commit struct or a null member (other
+    than self_decode_ok), and bad sizes, before any device call."""
+    L = svlib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the call returns first
+    B, M, V = 4, 3, 100
+    ws = svlib.workspace_bytes(B, M, V)
+
+    def call(cio, B=B, dtype=0):
+        return L.sv_verify_commit(fake, fake, dtype, fake, fake, fake, fake, None, B, M, V, 0, 1,
+                                  fake, fake, cio, fake, ws, None, None)
+
+    assert call(None) == svlib.ERR_ARG
+    full = dict(contracts=0x1000, states=0x1000, self_decode_ok=None, emitted_len=0x1000,
+                action=0x1000)
+    for k in ("contracts", "states", "emitted_len", "action"):
+        io = svlib._CommitIO(**{**full, k: None})
+        assert call(ctypes.byref(io)) == svlib.ERR_ARG, k
+    io = svlib._CommitIO(**full)
+    assert call(ctypes.byref(io), B=0) == svlib.ERR_ARG
+    assert call(ctypes.byref(io), dtype=7) == svlib.ERR_ARG
+    # the drafted tokens' links live in the workspace: B * M * 32 bytes of it
+    assert svlib.workspace_bytes(256, 8, 1000) - svlib.workspace_bytes(256, 7, 1000) >= 256 * 32

@@ -64,7 +64,7 @@ STATE_DTYPE = np.dtype(
 EXPORTED = ("sv_workspace_bytes", "sv_verify", "sv_verify_sdcp", "sv_verify_qrows",
             "sv_verify_early", "sv_commit",
             "sv_prefix_digest", "sv_contract_digest", "sv_strerror", "sv_status_str",
-            "sv_version", "sv_bench_row_events", "sv_verify_noalloc")
+            "sv_version", "sv_bench_row_events", "sv_verify_noalloc", "sv_verify_commit")
 
 
 class SvError(RuntimeError):
@@ -73,6 +73,12 @@ class SvError(RuntimeError):
 
 class _Probe(ctypes.Structure):
     _fields_ = [("p_tok", ctypes.c_void_p), ("q_tok", ctypes.c_void_p)]
+
+
+class _CommitIO(ctypes.Structure):
+    _fields_ = [("contracts", ctypes.c_void_p), ("states", ctypes.c_void_p),
+                ("self_decode_ok", ctypes.c_void_p), ("emitted_len", ctypes.c_void_p),
+                ("action", ctypes.c_void_p)]
 
 
 class HipEvent:
@@ -176,6 +182,14 @@ def lib():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Probe), ctypes.c_void_p,
         ]
         L.sv_verify_noalloc.restype = ctypes.c_int
+        L.sv_verify_commit.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64, ctypes.c_uint32,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_CommitIO),
+            ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(_Probe), ctypes.c_void_p,
+        ]
+        L.sv_verify_commit.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -335,7 +349,7 @@ def _check(t, name, dtype, shape, device):
 
 def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, probe: bool = False,
            workspace=None, out=None, stream=None, row_events=None, sdcp_sessions=None,
-           q_rows=None, early=None):
+           q_rows=None, early=None, commit=None):
     """sv_verify, sv_verify_sdcp, sv_verify_qrows or sv_verify_early on torch
     tensors (all on one GPU device).
 
@@ -354,6 +368,11 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     early: the first window (1..65 positions) of the in-order reading,
         sv_verify_early (with either draft source and either value source); None:
         every row is read.
+    commit: optional (contracts, states, self_decode_ok or None), device arrays
+        as for commit(): the acceptance step and the commit step in one call,
+        sv_verify_commit (draft logits, either value source, every row read);
+        the result then also holds emitted_len and action [B] int32, and out_tokens
+        is truncated as sv_commit truncates it.
     """
     import torch
 
@@ -388,6 +407,15 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
         if sdcp_sessions.numel() * sdcp_sessions.element_size() != 32 * B:
             raise ValueError("sdcp_sessions must hold B 32-byte records")
 
+    cio = None
+    if commit is not None:
+        if q_rows is not None or early is not None:
+            raise ValueError("commit= takes draft logits and reads every row")
+        contracts, states, self_ok = commit
+        for t, name in ((contracts, "contracts"), (states, "states")):
+            _check(t, name, torch.uint8, (B, 64), dev)
+        if self_ok is not None:
+            _check(self_ok, "self_decode_ok", torch.uint8, (B,), dev)
     need = workspace_bytes(B, M, V)
     if need == 0:
         raise SvError("sizes out of range")
@@ -403,6 +431,13 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
         if probe:
             out["p_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
             out["q_tok"] = torch.empty((B, M), dtype=torch.float64, device=dev)
+    if commit is not None:
+        for k in ("emitted_len", "action"):
+            if k not in out:
+                out[k] = torch.empty(B, dtype=torch.int32, device=dev)
+        cio = ctypes.byref(_CommitIO(contracts.data_ptr(), states.data_ptr(),
+                                     None if self_ok is None else self_ok.data_ptr(),
+                                     out["emitted_len"].data_ptr(), out["action"].data_ptr()))
     pr = None
     if "p_tok" in out:
         pr = ctypes.byref(_Probe(out["p_tok"].data_ptr(), out["q_tok"].data_ptr()))
@@ -421,7 +456,13 @@ def verify(target, draft, tokens, m, rule, sampling, seed: int, round_: int, pro
     if evs is not None:
         lib().sv_bench_row_events(*evs)
     try:
-        rc, name = _call(common, tail, target, q_rows, dt, sess, B, M, V, seed, round_, early)
+        if cio is not None:
+            name = "sv_verify_commit"
+            rc = lib().sv_verify_commit(*common, sess, B, M, V, seed, round_, tail[0], tail[1],
+                                        cio, *tail[2:])
+        else:
+            rc, name = _call(common, tail, target, q_rows, dt, sess, B, M, V, seed, round_,
+                             early)
     finally:
         if evs is not None:
             lib().sv_bench_row_events(None, None, None)

@@ -5,7 +5,9 @@
 //   single-pass row kernel (session statuses, then each row by the top-k or
 //   the dense path) -> generic row kernel (every other row) -> finalize
 //   (acceptance, and the additional token's draw).
-// With SDCP values the single-pass kernel's first workgroups also compute them.
+// With SDCP values the single-pass kernel's first workgroups also compute them;
+// sv_verify_commit adds workgroups in front of those that chain the drafted
+// tokens' digests, and the commit kernel after the finalize.
 // sv_verify_early enqueues the row kernels once per window of positions, each
 // followed by the advance kernel, and the finalize after the last window.
 // Neither call synchronises or allocates.
@@ -42,6 +44,8 @@ WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V) {
   off = align_up(off + (size_t)B * sizeof(uint32_t), 256);
   L.decided_off = off;
   off = align_up(off + (size_t)B * sizeof(int32_t), 256);
+  L.chain_off = off;
+  off = align_up(off + (size_t)B * (size_t)M * 32, 256);
   L.total = off;
   return L;
 }
@@ -100,9 +104,12 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
                        int32_t M, int32_t V, uint64_t seed, uint32_t round,
                        int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                        size_t workspace_bytes, const sv_probe* probe, void* stream,
-                       int32_t window0 = 0) {
+                       int32_t window0 = 0, const sv_commit_io* commit = nullptr) {
   if (!target_logits || !draft_tokens || !m || !rule || !sampling || !accepted_len ||
       !out_tokens || !workspace)
+    return SV_ERR_ARG;
+  if (commit && (!commit->contracts || !commit->states || !commit->emitted_len ||
+                 !commit->action))
     return SV_ERR_ARG;
   if (!sizes_ok(B, M, V, dtype)) return SV_ERR_ARG;
   const WorkspaceLayout L = workspace_layout(B, M, V);
@@ -144,6 +151,9 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   a.win_lo = 1;
   a.win_w = 0;
   a.win_index = 0;
+  a.contracts = commit ? commit->contracts : nullptr;
+  a.states = commit ? commit->states : nullptr;
+  a.chain = commit ? (uint32_t*)(ws + L.chain_off) : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   (void)hipGetLastError();  // report only errors raised by the launches below
@@ -170,6 +180,9 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   }
   if (g_row_ev[2]) (void)hipEventRecord(g_row_ev[2], st);
   launch_finalize(a, st);
+  if (commit)
+    launch_commit(commit->contracts, commit->states, m, accepted_len, out_tokens,
+                  commit->self_decode_ok, B, M, commit->emitted_len, commit->action, a.chain, st);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
   return SV_OK;
 }
@@ -222,6 +235,19 @@ extern "C" int sv_verify_early(const void* target_logits, const void* draft_logi
   return sv::verify_impl(target_logits, draft_logits, q_rows, dtype, draft_tokens, m, rule,
                          sampling, sessions, B, M, V, seed, round, accepted_len, out_tokens,
                          workspace, workspace_bytes, probe, stream, window0);
+}
+
+extern "C" int sv_verify_commit(const void* target_logits, const void* draft_logits,
+                                int32_t dtype, const int32_t* draft_tokens, const int32_t* m,
+                                const int32_t* rule, const sv_sampling* sampling,
+                                const sv_sdcp_session* sessions, int32_t B, int32_t M, int32_t V,
+                                uint64_t seed, uint32_t round, int32_t* accepted_len,
+                                int32_t* out_tokens, const sv_commit_io* commit, void* workspace,
+                                size_t workspace_bytes, const sv_probe* probe, void* stream) {
+  if (!commit) return SV_ERR_ARG;
+  return sv::verify_impl(target_logits, draft_logits, nullptr, dtype, draft_tokens, m, rule,
+                         sampling, sessions, B, M, V, seed, round, accepted_len, out_tokens,
+                         workspace, workspace_bytes, probe, stream, 0, commit);
 }
 
 // ---------------------------------------------------------------------------

@@ -8,11 +8,13 @@
 //   Sec. 6.5         control: low rounds, the counters c, g, j, the fallback
 //                    ladder, m_cap.
 // One lane per session; each lane's digest chain is one compression per
-// committed token.  Host functions give d[0] and the contract digest.
+// committed token, or, after sv_verify_commit, at most one: the links over
+// the drafted tokens were computed beside the row stream (sv_commit.hpp).
+// Host functions give d[0] and the contract digest.
 #include <string.h>
 
+#include "sv_commit.hpp"
 #include "sv_kernels.hpp"
-#include "sv_sdcp.hpp"
 
 namespace sv {
 
@@ -25,7 +27,8 @@ __global__ __launch_bounds__(kWave) void k_commit(const sv_contract* __restrict_
                                                   int32_t* __restrict__ out_tokens,
                                                   const uint8_t* __restrict__ self_decode_ok, int B,
                                                   int M, int32_t* __restrict__ emitted_len,
-                                                  int32_t* __restrict__ action) {
+                                                  int32_t* __restrict__ action,
+                                                  const uint32_t* __restrict__ chain) {
   const int b = (int)(blockIdx.x * kWave + threadIdx.x);
   if (b >= B) return;
   const int32_t a = accepted_len[b];
@@ -48,10 +51,7 @@ __global__ __launch_bounds__(kWave) void k_commit(const sv_contract* __restrict_
   bool finished = false;
   const uint32_t nstop = k.n_stop < SV_STOP_MAX ? k.n_stop : SV_STOP_MAX;
   for (int t = 0; t < e; ++t) {
-    const int32_t o = out[t];
-    bool stop = false;
-    for (uint32_t q = 0; q < nstop; ++q) stop |= o == k.stop[q];
-    if (stop) {
+    if (commit::is_stop(k, nstop, out[t])) {
       e = t + 1;
       finished = true;
       break;
@@ -63,23 +63,25 @@ __global__ __launch_bounds__(kWave) void k_commit(const sv_contract* __restrict_
     finished = true;
   }
 
-  // commit: d[n+t+1] = SHA-256(d[n+t] || uint32(o_t)), one 36-octet block each
+  // commit: d[n+t+1] = SHA-256(d[n+t] || uint32(o_t)), one 36-octet block each.
+  // With the drafted tokens' links given, d[n+t0] for t0 = min(e, a) is
+  // chain[b][t0-1] (the first a committed tokens are the accepted drafts, and
+  // t0 never exceeds the links chained: e <= a stops at max_new and at the
+  // first stop token, and e = a+1 means no stop among x_1..x_a and a < room);
+  // only the additional token, if committed, is linked here.
   uint32_t h[8];
+  int t0 = 0;
+  if (chain != nullptr) t0 = e < a ? e : a;
+  if (t0 > 0) {
+    const uint4* c = (const uint4*)(chain + ((size_t)b * M + (t0 - 1)) * 8);
+    const uint4 lo = c[0], hi = c[1];
+    h[0] = lo.x, h[1] = lo.y, h[2] = lo.z, h[3] = lo.w;
+    h[4] = hi.x, h[5] = hi.y, h[6] = hi.z, h[7] = hi.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = __builtin_bswap32(dg[i]);
-  for (int t = 0; t < e; ++t) {
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = h[i];
-    w[8] = (uint32_t)out[t];
-    w[9] = 0x80000000u;
-#pragma unroll
-    for (int i = 10; i < 15; ++i) w[i] = 0;
-    w[15] = 36 * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = sdcp::kH0[i];
-    sdcp::compress(h, w);
+    for (int i = 0; i < 8; ++i) h[i] = __builtin_bswap32(dg[i]);
   }
+  for (int t = t0; t < e; ++t) commit::link(h, out[t]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dg[i] = __builtin_bswap32(h[i]);
   for (int t = e; t <= M; ++t) out[t] = -1;
@@ -131,6 +133,15 @@ __global__ __launch_bounds__(kWave) void k_commit(const sv_contract* __restrict_
 
 }  // namespace
 
+void launch_commit(const sv_contract* contracts, sv_session_state* states, const int32_t* m,
+                   const int32_t* accepted_len, int32_t* out_tokens, const uint8_t* self_decode_ok,
+                   int B, int M, int32_t* emitted_len, int32_t* action, const uint32_t* chain,
+                   hipStream_t st) {
+  const unsigned grid = (unsigned)((B + kWave - 1) / kWave);
+  hipLaunchKernelGGL(k_commit, dim3(grid), dim3(kWave), 0, st, contracts, states, m, accepted_len,
+                     out_tokens, self_decode_ok, B, M, emitted_len, action, chain);
+}
+
 }  // namespace sv
 
 extern "C" int sv_commit(const sv_contract* contracts, sv_session_state* states, const int32_t* m,
@@ -141,10 +152,8 @@ extern "C" int sv_commit(const sv_contract* contracts, sv_session_state* states,
     return SV_ERR_ARG;
   if (B < 1 || B > SV_B_MAX || M < 1 || M > SV_M_MAX) return SV_ERR_ARG;
   (void)hipGetLastError();
-  const unsigned grid = (unsigned)((B + sv::kWave - 1) / sv::kWave);
-  hipLaunchKernelGGL(sv::k_commit, dim3(grid), dim3(sv::kWave), 0, (hipStream_t)stream,
-                     contracts, states, m, accepted_len, out_tokens, self_decode_ok, B, M,
-                     emitted_len, action);
+  sv::launch_commit(contracts, states, m, accepted_len, out_tokens, self_decode_ok, B, M,
+                    emitted_len, action, nullptr, (hipStream_t)stream);
   if (hipGetLastError() != hipSuccess) return SV_ERR_DEVICE;
   return SV_OK;
 }

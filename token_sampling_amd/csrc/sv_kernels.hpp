@@ -51,6 +51,12 @@ struct LaunchArgs {
   int32_t* decided;  // [B]
   int32_t win_lo, win_w;
   int32_t win_index;  // 0 for the first window
+  // sv_verify_commit: the first row launch's front workgroups chain the
+  // drafted tokens' digests (sv_commit.hpp) from each session's state, for the
+  // commit after the verdict (null chain: no commit)
+  const sv_contract* contracts;  // [B]
+  const sv_session_state* states;  // [B]
+  uint32_t* chain;  // [B, M] digests after the first 1..M drafted tokens, 8 words each
 };
 
 // Ids per group record of the draw.
@@ -118,7 +124,7 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
 
 struct WorkspaceLayout {
   size_t rows_off, status_off, supid_off, supp_off, unif_off, chunk_off, ctr_off, flag_off,
-      decided_off, total;
+      decided_off, chain_off, total;
 };
 
 // Row slot g of the launch: every slot of every session (win_w == 0), or the
@@ -142,5 +148,9 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st);
 void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
 void launch_advance(const LaunchArgs& a, hipStream_t st, int hi);
+void launch_commit(const sv_contract* contracts, sv_session_state* states, const int32_t* m,
+                   const int32_t* accepted_len, int32_t* out_tokens, const uint8_t* self_decode_ok,
+                   int B, int M, int32_t* emitted_len, int32_t* action, const uint32_t* chain,
+                   hipStream_t st);
 
 }  // namespace sv

@@ -19,6 +19,7 @@
 // run while the row waves stream.
 #include <stdlib.h>
 
+#include "sv_commit.hpp"
 #include "sv_kernels.hpp"
 #include "sv_rows_dense.hpp"
 #include "sv_rows_exact.hpp"
@@ -91,16 +92,26 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
-    int32_t* __restrict__ decided, int win_lo, int win_w) {
+    int32_t* __restrict__ decided, int win_lo, int win_w,
+    const sv_contract* __restrict__ contracts, const sv_session_state* __restrict__ states,
+    uint32_t* __restrict__ chain, int n_chain_blocks) {
   using E = typename Tr::elem_t;
   __shared__ __align__(16) uint64_t lds[kLdsWords];  // top-k region or dense histogram
   const int lane = __lane_id();
-  if ((int)blockIdx.x < n_value_blocks) {
-    sdcp_value((int64_t)blockIdx.x * kWave + lane, sessions, m, rule, B, M, unif);
+  const int n_front = n_chain_blocks + n_value_blocks;
+  if ((int)blockIdx.x < n_front) {
+    if ((int)blockIdx.x < n_chain_blocks) {
+      __builtin_amdgcn_s_setprio(3);
+      commit::chain_drafted((int64_t)blockIdx.x * kWave + lane, contracts, states, tokens, m, B, M,
+                            chain);
+    } else {
+      sdcp_value((int64_t)((int)blockIdx.x - n_chain_blocks) * kWave + lane, sessions, m, rule, B,
+                 M, unif);
+    }
     return;
   }
   const int R = 2 * M + 1;
-  const int slot_g = launch_slot((int)blockIdx.x - n_value_blocks, M, win_lo, win_w);
+  const int slot_g = launch_slot((int)blockIdx.x - n_front, M, win_lo, win_w);
   if (slot_g < 0) return;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
@@ -171,7 +182,9 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
     uint32_t* __restrict__ draw_flag, uint32_t draw_token, RowRec* __restrict__ rows,
     int32_t* __restrict__ sup_id, double* __restrict__ sup_p,
     const sv_sdcp_session* __restrict__ sessions, double* __restrict__ unif, int n_value_blocks,
-    int32_t* __restrict__ decided, int win_lo, int win_w) {
+    int32_t* __restrict__ decided, int win_lo, int win_w,
+    const sv_contract* __restrict__ contracts, const sv_session_state* __restrict__ states,
+    uint32_t* __restrict__ chain, int n_chain_blocks) {
   // top-k-class rows use the first TS waves (the merged lists fit one region)
   constexpr int TS = S < 4 ? S : 4;
   static_assert(TS * kSupMax <= topk::kCap, "the merged lists fit one region");
@@ -183,12 +196,20 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
   __shared__ uint32_t mm_s[S], um_s[S];
   const int lane = __lane_id();
   const int wid = (int)threadIdx.x / kWave;
-  if ((int)blockIdx.x < n_value_blocks) {
-    sdcp_value((int64_t)blockIdx.x * (S * kWave) + threadIdx.x, sessions, m, rule, B, M, unif);
+  const int n_front = n_chain_blocks + n_value_blocks;
+  if ((int)blockIdx.x < n_front) {
+    if ((int)blockIdx.x < n_chain_blocks) {
+      __builtin_amdgcn_s_setprio(3);
+      commit::chain_drafted((int64_t)blockIdx.x * (S * kWave) + threadIdx.x, contracts, states,
+                            tokens, m, B, M, chain);
+    } else {
+      sdcp_value((int64_t)((int)blockIdx.x - n_chain_blocks) * (S * kWave) + threadIdx.x,
+                 sessions, m, rule, B, M, unif);
+    }
     return;
   }
   const int R = 2 * M + 1;
-  const int slot_g = launch_slot((int)blockIdx.x - n_value_blocks, M, win_lo, win_w);
+  const int slot_g = launch_slot((int)blockIdx.x - n_front, M, win_lo, win_w);
   if (slot_g < 0) return;
   const int b = slot_g / R;
   const int slot = slot_g - b * R;
@@ -308,18 +329,25 @@ static int value_blocks(const LaunchArgs& a, int per_block) {
   const size_t values = (size_t)a.B * (2 * a.M + 1);
   return (int)((values + per_block - 1) / per_block);
 }
+// The drafted tokens' digest chains, one session per work-item (first launch
+// only).
+static int chain_blocks(const LaunchArgs& a, int per_block) {
+  if (!a.chain || a.win_lo > 1) return 0;
+  return (a.B + per_block - 1) / per_block;
+}
 
 template <int S>
 static void launch_split(const LaunchArgs& a, hipStream_t st, size_t slots) {
   const int per_block = S * kWave;
   const int n_value_blocks = value_blocks(a, per_block);
-  const unsigned grid = (unsigned)(slots + n_value_blocks);
+  const int n_chain_blocks = chain_blocks(a, per_block);
+  const unsigned grid = (unsigned)(slots + n_value_blocks + n_chain_blocks);
   hipLaunchKernelGGL((k_rows_split<S>), dim3(grid), dim3(per_block), 0, st,
                      (const uint16_t*)a.target, (const uint16_t*)a.draft, a.dtype, a.tokens, a.m,
                      a.rule, a.sampling, (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0, a.B,
                      a.M, a.V, a.sess_status, a.draw_ctr, a.draw_flag, a.draw_token, a.rows,
                      a.sup_id, a.sup_p, a.sdcp, a.unif, n_value_blocks, a.decided, a.win_lo,
-                     a.win_w);
+                     a.win_w, a.contracts, a.states, a.chain, n_chain_blocks);
 }
 
 void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
@@ -329,20 +357,23 @@ void launch_rows_stream(const LaunchArgs& a, hipStream_t st) {
   if (split == 4) return launch_split<4>(a, st, slots);
   if (split == 8) return launch_split<8>(a, st, slots);
   const int n_value_blocks = value_blocks(a, kWave);
-  const unsigned grid = (unsigned)(slots + n_value_blocks);
+  const int n_chain_blocks = chain_blocks(a, kWave);
+  const unsigned grid = (unsigned)(slots + n_value_blocks + n_chain_blocks);
   const int has_draft = (a.draft != nullptr || a.qrows != nullptr) ? 1 : 0;
   if (a.dtype == SV_BF16)
     hipLaunchKernelGGL(k_rows_stream<Bf16>, dim3(grid), dim3(kWave), 0, st,
                        (const uint16_t*)a.target, (const uint16_t*)a.draft, a.tokens, a.m, a.rule,
                        a.sampling, has_draft, a.B, a.M, a.V, a.sess_status, a.draw_ctr,
                        a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
-                       n_value_blocks, a.decided, a.win_lo, a.win_w);
+                       n_value_blocks, a.decided, a.win_lo, a.win_w, a.contracts, a.states,
+                       a.chain, n_chain_blocks);
   else
     hipLaunchKernelGGL(k_rows_stream<F32>, dim3(grid), dim3(kWave), 0, st,
                        (const uint32_t*)a.target, (const uint32_t*)a.draft, a.tokens, a.m, a.rule,
                        a.sampling, has_draft, a.B, a.M, a.V, a.sess_status, a.draw_ctr,
                        a.draw_flag, a.draw_token, a.rows, a.sup_id, a.sup_p, a.sdcp, a.unif,
-                       n_value_blocks, a.decided, a.win_lo, a.win_w);
+                       n_value_blocks, a.decided, a.win_lo, a.win_w, a.contracts, a.states,
+                       a.chain, n_chain_blocks);
 }
 
 }  // namespace sv
