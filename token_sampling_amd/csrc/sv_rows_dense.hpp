@@ -126,6 +126,14 @@ __device__ inline Hist hist_init(uint32_t* bins, int kx) {
   return Hist{bins, kNoAnchor, -__builtin_huge_valf(), -__builtin_huge_valf(), 0.0f, kx, 0};
 }
 
+// The maximum of two binary32 values, NaN if either is NaN (v_maximum on this
+// chip).  fmaxf would skip a NaN but costs a canonicalizing instruction per
+// logit; a NaN in the row makes its sums NaN and the row bad either way.
+__device__ inline float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Bits 14..25 of x in one v_bfe_u32.
+__device__ inline uint32_t bits_14_25(uint32_t x) { return __builtin_amdgcn_ubfe(x, 14, 12); }
+
 // One lane's step over kE logits: its maximum, its offset q, and (kSum: rows
 // without a histogram) its binary32 sum of 2^(l sf - q) with the sum of
 // those terms times l.  Returns the kE logits' maximum.
@@ -134,8 +142,8 @@ __device__ __attribute__((always_inline)) inline float lane_step(LaneSum& L, con
                                                                  const Scales& sc) {
   float lmv = f[0];
 #pragma unroll
-  for (int e = 1; e < kE; ++e) lmv = fmaxf(lmv, f[e]);  // NaN is skipped
-  L.mv = fmaxf(L.mv, lmv);
+  for (int e = 1; e < kE; ++e) lmv = max_nan(lmv, f[e]);
+  L.mv = max_nan(L.mv, lmv);
   if (lmv > L.vt && lmv < __builtin_huge_valf()) {  // first finite logit, or an octave up
     const float qn = ceilf(lmv * sc.sf);
     L.ovf |= !(qn < 0x1p22f);
@@ -156,9 +164,9 @@ __device__ __attribute__((always_inline)) inline float lane_step(LaneSum& L, con
     L.s += (double)ts;
     // w * l, with -inf logits (weight 0) taken as the largest negative finite
     // value so that they add 0; a NaN logit has a NaN weight and stays NaN
-    float tl = w[0] * fmaxf(f[0], -__FLT_MAX__);
+    float tl = w[0] * max_nan(f[0], -__FLT_MAX__);
 #pragma unroll
-    for (int e = 1; e < kE; ++e) tl = __builtin_fmaf(w[e], fmaxf(f[e], -__FLT_MAX__), tl);
+    for (int e = 1; e < kE; ++e) tl = __builtin_fmaf(w[e], max_nan(f[e], -__FLT_MAX__), tl);
     L.l1 += (double)tl;
   }
   return lmv;
@@ -176,19 +184,39 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const uint32_t x = elem(v, d);
-    f[2 * d] = __uint_as_float(x << 16);
-    f[2 * d + 1] = __uint_as_float(x & 0xFFFF0000u);
+    // the two bf16 halves as binary32 (byte permutes: x << 16, x & 0xFFFF0000)
+    f[2 * d] = __uint_as_float(__builtin_amdgcn_perm(0u, x, 0x01000C0Cu));
+    f[2 * d + 1] = __uint_as_float(__builtin_amdgcn_perm(0u, x, 0x03020C0Cu));
   }
-  const float lmv = lane_step<8, !kHist>(L, f, sc);
-  if constexpr (!kHist) return;
+  if constexpr (!kHist) {
+    (void)lane_step<8, true>(L, f, sc);
+    return;
+  }
+  // rows with a histogram: the offset q is the wave's, moved with the window
+  // (below), so the lanes need only their maximum here
+  float lmv = f[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) lmv = max_nan(lmv, f[e]);
+  L.mv = max_nan(L.mv, lmv);
   if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
     int tk = skey_of(lmv);
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
     const int lane = __lane_id();
     const int d = tk - H.anchor;  // keys anchor+1 .. tk take the bins of the keys leaving
-    const float nref = value_of(tk);
+    const float nref = uni(value_of(tk));
     const bool had = H.anchor != kNoAnchor;
+    // the wave's offset: q = ceil(lmax sf) keeps every term at or below 2; a
+    // power-of-two rescale of the sums is exact (NaN stays NaN).  A maximum
+    // beyond binary32 exponents (or +inf, or NaN) hands the row back.
+    const float qn = ceilf(nref * sc.sf);
+    if (qn < 0x1p22f) {
+      if (had) L.s = ldexp(L.s, (int)(L.q - qn));
+      L.q = qn;
+      L.vt = __builtin_huge_valf();  // the lane's sum is relative to the wave's q
+    } else {
+      L.ovf = true;
+    }
     // the leaving bins' tokens are in no sum: their mass goes to dep.  They lie
     // at least kWin keys (eight octaves of magnitude) below the new maximum, so
     // binary32 suffices: an error of a few 1e-7 of a mass far below Z's
@@ -217,25 +245,30 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     for (int off = kWave / 2; off > 0; off >>= 1) before += __shfl_xor(before, off, kWave);
     H.rank_x = (H.kx >= lo ? (int)H.bin[H.kx & (kWin - 1)] : 0) + before;
   }
-  // tokens in the window are counted; the binary32 sum takes only the others
+  // tokens in the window are counted; the binary32 sum takes only the others.
+  // One test per token selects both.  The count is an LDS atomic from the
+  // lanes whose token is in the window only (measured: atomics from every
+  // lane, the others into a dummy word, cost more than the branch saves).
+  float w[8];
   if (lo > 0) {
     // a window of positive keys: the key is the upper half of the bits, and the
     // unpacked value's low 16 bits are zero, so bits 14..25 are the bin's byte
     // offset
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (f[e] >= H.lo_v)
-        atomicAdd((uint32_t*)((char*)H.bin + __builtin_amdgcn_ubfe(__float_as_uint(f[e]), 14, 12)), 1u);
+    for (int e = 0; e < 8; ++e) {
+      const bool in = f[e] >= H.lo_v;
+      if (in) atomicAdd((uint32_t*)((char*)H.bin + bits_14_25(__float_as_uint(f[e]))), 1u);
+      const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+      w[e] = in ? 0.0f : t;
+    }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (f[e] >= H.lo_v) atomicAdd(&H.bin[skey_of(f[e]) & (kWin - 1)], 1u);
-  }
-  float w[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
-    w[e] = f[e] >= H.lo_v ? 0.0f : t;
+    for (int e = 0; e < 8; ++e) {
+      const bool in = f[e] >= H.lo_v;
+      if (in) atomicAdd(&H.bin[skey_of(f[e]) & (kWin - 1)], 1u);
+      const float t = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], sc.sf, -L.q));
+      w[e] = in ? 0.0f : t;
+    }
   }
   L.s += (double)(((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7])));
 }

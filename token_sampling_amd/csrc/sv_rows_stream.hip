@@ -77,7 +77,9 @@ __device__ inline void sdcp_value(int64_t g, const sv_sdcp_session* __restrict__
   unif[g] = (double)bits * 0x1p-53;
 }
 
-constexpr int kLdsWords = (topk::kCap * 8 > dense::kWin * 4 ? topk::kCap * 8 : dense::kWin * 4) / 8;
+// LDS of one wave: the top-k region, or the dense histogram
+constexpr int kDenseBytes = dense::kWin * 4;
+constexpr int kLdsWords = (topk::kCap * 8 > kDenseBytes ? topk::kCap * 8 : kDenseBytes) / 8;
 
 #ifndef SV_STREAM_WAVES_PER_EU
 #define SV_STREAM_WAVES_PER_EU 5
@@ -188,7 +190,8 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
   // top-k-class rows use the first TS waves (the merged lists fit one region)
   constexpr int TS = S < 4 ? S : 4;
   static_assert(TS * kSupMax <= topk::kCap, "the merged lists fit one region");
-  constexpr int kRegions = S * topk::kCap > S * dense::kWin / 2 ? S * topk::kCap : S * dense::kWin / 2;
+  constexpr int kHists = S * dense::kWin / 2;  // S histograms
+  constexpr int kRegions = S * topk::kCap > kHists ? S * topk::kCap : kHists;
   constexpr int kWords = kRegions > kLdsWords ? kRegions : kLdsWords;
   __shared__ __align__(16) uint64_t lds[kWords];  // S regions, or S dense histograms
   __shared__ dense::PartRec parts_s[S];
