@@ -160,7 +160,7 @@ def test_workload_full_size_in_order(name):
                                                            | (a[~ok] >= 0)))
     del args, out
     o = parity.run_oracle_sessions(w, early=True)
-    rep = parity.compare(g_all, o, f"early-{name}-full")
+    rep = parity.compare(g_all, o, f"early-{name}-full", prob_rtol=parity.DENSE_PROB_RTOL)
     assert rep["sessions"] == w.B
     parity.log(f"[workload] {name} in order: mean accepted {a[a >= 0].mean():.3f}, "
                f"bad proposals {(a == oracle.S_BAD_PROPOSAL).sum()} of {a.shape[0]}")
