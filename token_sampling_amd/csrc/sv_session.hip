@@ -443,6 +443,19 @@ __device__ __attribute__((always_inline)) void load8(const E* row, int y, int V,
   }
 }
 
+// Elements y .. y+7 by vector loads only: the row is 16-byte aligned and
+// y + 8 <= V (the caller's guarantee).
+template <class E>
+__device__ __attribute__((always_inline)) void load8_vec(const E* row, int y,
+                                                         Raw8<sizeof(E)>& r) {
+  const u32x4* p = (const u32x4*)(row + y);
+  if constexpr (sizeof(E) == 2) r.v = p[0];
+  else {
+    r.v[0] = p[0];
+    r.v[1] = p[1];
+  }
+}
+
 template <class Tr, bool kQ>
 struct DrawCtx {
   using RawP = Raw8<sizeof(typename Tr::elem_t)>;
@@ -458,6 +471,19 @@ struct DrawCtx {
       else load8(Q.row, y, V, Q.vec, Tr::kNegInfBits, rq);
     }
   }
+  // the same inside whole vectors of aligned rows: a fixed number of vector
+  // loads (kResid: the q row's too), so that a ring of them keeps its wait
+  // counts exact
+  template <bool kResid>
+  __device__ __attribute__((always_inline)) void load_vec(int y, RawP& rp, RawQ& rq) const {
+    load8_vec(P.row, y, rp);
+    if constexpr (kResid) {
+      if constexpr (kQ) load8_vec((const uint32_t*)qrow, y, rq);
+      else load8_vec(Q.row, y, rq);
+    }
+  }
+  // whole vectors can be loaded: every row read 16-byte aligned
+  __device__ bool aligned(bool resid) const { return P.vec && (!resid || (kQ ? qvec : Q.vec)); }
 };
 
 // Exclusive prefix over the wave's lanes of a count in 0..15, and the wave
@@ -649,29 +675,53 @@ __device__ inline GroupAcc load_group(const GroupRec* rec) {
 // positions anyway; rows with more members keep the 8 unrolled positions,
 // which overlap their binary64 chains).  The two loops are kept apart so that
 // each has its own registers.
-template <class Tr, bool kQ, bool kQueued>
+//
+// kSteady: groups that lie wholly inside aligned rows.  Every step then issues
+// the same vector loads (the ring's last three clamped to the wave's last
+// step), so the compiler's wait counts leave three steps in flight; with
+// loads that depend on the step (the row's end, a scalar fallback) it waits
+// for all of them at each step, and the ring drains.  kResid fixes, at
+// compile time, whether the q row is read.
+template <class Tr, bool kQ, bool kQueued, bool kSteady = false, bool kResid = false>
 __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>& d, bool resid,
                                                            int g0, int g1,
                                                            GroupRec* __restrict__ recs,
                                                            uint32_t* qu) {
+  if constexpr (kSteady) resid = kResid;
   const int lane = __lane_id();
   const int nk = (g1 - g0) * kSteps;
   const int ybase = g0 * kGroup + lane * kPer;
   typename DrawCtx<Tr, kQ>::RawP p[kSteps];
   typename DrawCtx<Tr, kQ>::RawQ q[kSteps];
-  d.load(ybase, resid, p[0], q[0]);
-  d.load(ybase + kWStep, resid, p[1], q[1]);
-  d.load(ybase + 2 * kWStep, resid, p[2], q[2]);
+  if constexpr (kSteady) {
+    // four steps ahead, each slot refilled right after it is weighed, so the
+    // loads outstanding at the loop's back edge are those of the prologue, in
+    // the same order
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      d.template load_vec<kResid>(ybase + min(u, nk - 1) * kWStep, p[u], q[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    d.load(ybase, resid, p[0], q[0]);
+    d.load(ybase + kWStep, resid, p[1], q[1]);
+    d.load(ybase + 2 * kWStep, resid, p[2], q[2]);
+  }
   for (int k = 0; k < nk; k += kSteps) {
     GroupAcc s{};
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int kk = k + u;
-      if (kk + 3 < nk)
-        d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
+      if constexpr (!kSteady)
+        if (kk + 3 < nk)
+          d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
       const int y = ybase + kk * kWStep;
       if constexpr (kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, y, p[u], q[u], s, qu);
       else weigh8<Tr, kQ>(d, resid, y, p[u], q[u], s);
+      if constexpr (kSteady) {
+        __builtin_amdgcn_sched_barrier(0);
+        d.template load_vec<kResid>(ybase + min(kk + kSteps, nk - 1) * kWStep, p[u], q[u]);
+      }
     }
     s.a = wave_reduce(s.a, OpAdd());
     s.bp = wave_reduce(s.bp, OpAdd());
@@ -704,8 +754,23 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
     (void)wave_excl_count(__builtin_popcount(need_bits<Tr, kQ>(d, resid, p0, q0)), &total);
     queued = total >= 16 && total <= SV_QUEUE_MAX;
   }
-  if (queued) record_loop<Tr, kQ, true>(d, resid, g0, g1, recs, qu);
-  else record_loop<Tr, kQ, false>(d, resid, g0, g1, recs, qu);
+  // the groups inside whole vectors of aligned rows take the steady loop; a
+  // row's last group (its end, a partial vector) the general one
+  const int gs = d.aligned(resid) ? min(g1, d.V / kGroup) : g0;
+  if (g0 < gs) {
+    if (queued) {
+      if (resid) record_loop<Tr, kQ, true, true, true>(d, resid, g0, gs, recs, qu);
+      else record_loop<Tr, kQ, true, true, false>(d, resid, g0, gs, recs, qu);
+    } else {
+      if (resid) record_loop<Tr, kQ, false, true, true>(d, resid, g0, gs, recs, qu);
+      else record_loop<Tr, kQ, false, true, false>(d, resid, g0, gs, recs, qu);
+    }
+  }
+  const int gr = max(g0, gs);
+  if (gr < g1) {
+    if (queued) record_loop<Tr, kQ, true>(d, resid, gr, g1, recs, qu);
+    else record_loop<Tr, kQ, false>(d, resid, gr, g1, recs, qu);
+  }
 }
 
 // A group's weight from its record: the ties of p kept (sp = 1), left out
