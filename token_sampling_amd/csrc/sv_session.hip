@@ -370,12 +370,20 @@ struct DrawRow {
   double sk, ck;      // kTab * scale (exact) and kTab * scale * lmax (rounded once)
   double wcut;        // p of each tie (tie mode)
   uint32_t kcut;
+  float cv;           // the value of key kcut
   int32_t idcut;
   uint32_t ntie;      // ties kept (tie mode), else 0
   bool vec;           // 16-byte aligned row: vector loads
   __device__ bool tie(uint32_t k) const { return idcut < 0 && k == kcut; }
   __device__ bool fixed_member(uint32_t k, int y) const {
     return k > kcut || (k == kcut && idcut >= 0 && y <= idcut);
+  }
+  // the same tests on values: for the logits of a row that is drawn from (no
+  // NaN) the order of the values is that of the keys, and +0 and -0 compare
+  // equal as their keys do; one compare instead of the key transform
+  __device__ bool tie_v(float f) const { return idcut < 0 && f == cv; }
+  __device__ bool fixed_v(float f, int y) const {
+    return f > cv || (f == cv && idcut >= 0 && y <= idcut);
   }
   __device__ double w(float l) const {
     // t = kTab (l - lmax) scale: l * sk is exact inside the fma and ck carries
@@ -515,15 +523,16 @@ template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>& d, bool resid,
                                                           uint32_t up, uint32_t uq, int y,
                                                           GroupAcc s) {
-  const uint32_t kp = Tr::key(up);
-  const bool tp = d.P.tie(kp);
-  const bool mp = !tp && d.P.fixed_member(kp, y);
+  const float fp = Tr::value(up);
+  const bool tp = d.P.tie_v(fp);
+  const bool mp = !tp && d.P.fixed_v(fp, y);
   bool tq = false, mq = false;
+  float fq = 0.0f;
   if constexpr (!kQ) {
     if (resid) {
-      const uint32_t kq = Tr::key(uq);
-      tq = d.Q.tie(kq);
-      mq = !tq && d.Q.fixed_member(kq, y);
+      fq = Tr::value(uq);
+      tq = d.Q.tie_v(fq);
+      mq = !tq && d.Q.fixed_v(fq, y);
     }
   }
   // no member or tie of p and no tie of q in the whole wave: nothing to add
@@ -531,7 +540,7 @@ __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>&
   if (!__builtin_amdgcn_ballot_w64(mp || tp || tq)) return s;
   double pv = 0.0;
   if (__builtin_amdgcn_ballot_w64(mp)) {
-    const double w = d.P.w(Tr::value(up));
+    const double w = d.P.w(fp);
     pv = mp ? w : 0.0;
   }
   if (!resid) {
@@ -545,7 +554,7 @@ __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>&
     qv = (double)__uint_as_float(uq);
     qbad = !(qv >= 0.0 && qv < INFINITY);
   } else if (__builtin_amdgcn_ballot_w64(mq && (mp || tp))) {
-    const double w = d.Q.w(Tr::value(uq));
+    const double w = d.Q.w(fq);
     qv = mq ? w : 0.0;
   }
   const bool plain = !tp && !tq;
@@ -589,33 +598,44 @@ __device__ __attribute__((always_inline)) uint32_t need_bits(
   uint32_t need = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    bool n = Tr::key(pr.get(e)) >= d.P.kcut;
+    bool n = Tr::value(pr.get(e)) >= d.P.cv;
     if constexpr (!kQ)
-      if (resid) n |= d.Q.tie(Tr::key(qr.get(e)));
+      if (resid) n |= d.Q.tie_v(Tr::value(qr.get(e)));
     need |= n ? 1u << e : 0u;
   }
   return need;
 }
 
 // The wave's 512 ids of one step, compacted: the ids that need weighing are
-// queued in LDS in id order and weighed 64 at a time, so that a position
-// whose lanes mostly hold non-members does not cost a full wave's binary64
-// work.  qu holds the wave's queue: p bits, q bits, ids.
+// queued in LDS and weighed 64 at a time, so that a position whose lanes
+// mostly hold non-members does not cost a full wave's binary64 work.  The
+// queue is filled one element position at a time (a ballot and its prefix
+// count per position), so it holds the ids by position, then lane; a group
+// record only sums its ids' weights and counts its ties, so their order is
+// free.  qu holds the wave's queue: p bits, q bits, ids.
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
     const DrawCtx<Tr, kQ>& d, bool resid, int y, const typename DrawCtx<Tr, kQ>::RawP& pr,
     const typename DrawCtx<Tr, kQ>::RawQ& qr, GroupAcc s, uint32_t* qu) {
   const int lane = __lane_id();
-  const uint32_t need = need_bits<Tr, kQ>(d, resid, pr, qr);
-  uint32_t total;
-  uint32_t j = wave_excl_count(__builtin_popcount(need), &total);
+  uint32_t total = 0;  // wave-uniform
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    if ((need >> e) & 1u) {
-      qu[j] = pr.get(e);
-      qu[kWStep + j] = resid ? qr.get(e) : 0u;
-      qu[2 * kWStep + j] = (uint32_t)(y + e);
-      ++j;
+    const uint32_t up = pr.get(e);
+    const uint32_t uq = resid ? qr.get(e) : 0u;
+    bool n = Tr::value(up) >= d.P.cv;  // at or above p's cut key
+    if constexpr (!kQ)
+      if (resid) n |= d.Q.tie_v(Tr::value(uq));
+    const uint64_t m = __builtin_amdgcn_ballot_w64(n);
+    if (m) {
+      const uint32_t j = total + __builtin_amdgcn_mbcnt_hi(
+                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (n) {
+        qu[j] = up;
+        qu[kWStep + j] = uq;
+        qu[2 * kWStep + j] = (uint32_t)(y + e);
+      }
+      total += (uint32_t)__builtin_popcountll(m);
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1002,6 +1022,7 @@ __global__ __launch_bounds__(kDrawNT) void k_finalize(
     D.sk = r.scale * (double)kTab;
     D.ck = (double)r.lmax * D.sk;
     D.kcut = r.kcut;
+    D.cv = Tr::value(Tr::unkey(r.kcut));
     D.idcut = r.idcut;
     D.ntie = r.idcut < 0 ? (uint32_t)r.ntie : 0u;
     D.wcut = weight64(Tr::value(Tr::unkey(r.kcut)), r.lmax, r.scale) / r.zsum;
