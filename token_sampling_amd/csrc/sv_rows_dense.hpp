@@ -221,10 +221,19 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     // at least kWin keys (eight octaves of magnitude) below the new maximum, so
     // binary32 suffices: an error of a few 1e-7 of a mass far below Z's
     if (had) L.dep *= __builtin_amdgcn_exp2f((H.dref - nref) * sc.sf);
-    for (int i = lane; i < kWin; i += kWave) {
-      if (d >= kWin || ((i - (H.anchor + 1)) & (kWin - 1)) < d) {
+    if (!had || d >= kWin) {  // every bin (the first window: clears them)
+      for (int i = lane; i < kWin; i += kWave) {
         const int ko = H.anchor - ((H.anchor - i) & (kWin - 1));  // the key leaving bin i
         const uint32_t c = had ? H.bin[i] : 0u;
+        if (c && ko > kNegInfKey)
+          L.dep += (float)c * __builtin_amdgcn_exp2f((value_of(ko) - nref) * sc.sf);
+        H.bin[i] = 0u;
+      }
+    } else {  // the d keys leaving: key anchor - (kWin - 1) + j sits in bin anchor + 1 + j
+      for (int j = lane; j < d; j += kWave) {
+        const int ko = H.anchor - (kWin - 1) + j;
+        const int i = (H.anchor + 1 + j) & (kWin - 1);
+        const uint32_t c = H.bin[i];
         if (c && ko > kNegInfKey)
           L.dep += (float)c * __builtin_amdgcn_exp2f((value_of(ko) - nref) * sc.sf);
         H.bin[i] = 0u;

@@ -42,16 +42,25 @@ __device__ inline int lanes_below(uint64_t m) {
 
 // Issue the loads of one tile (VEC 16-byte vectors per lane, 64 * VEC * 8
 // bf16 logits).  Every call issues the same loads on every path, so the
-// compiler's wait counts stay exact across a ring of tiles; vectors past gmax
-// (the last one the caller needs) re-read it and are masked when the tile is
-// consumed.
+// compiler's wait counts stay exact across a ring of tiles.  They are
+// nontemporal buffer loads over vectors [0, gmax] of vbase (vbase and gmax
+// wave-uniform): the tile's offset goes into the lane's byte offset, which
+// the buffer's range check covers (its scalar offset would not be), so a
+// vector past gmax reads as zeros without touching memory; the caller masks
+// the positions past the row when it consumes the tile.  One add per tile
+// instead of a clamp and a 64-bit address per load.
+constexpr int kBufferDword3 = 0x00020000;  // raw buffer, this chip's default format
+constexpr int kNonTemporal = 2;            // cache policy: nt
 template <int VEC>
 __device__ inline void load_tile(u32x4 (&v)[VEC], const u32x4* vbase, int tile, int gmax) {
   const int lane = __lane_id();
-  const int g0 = tile * (kWave * VEC);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (gmax + 1) * 16, kBufferDword3);
+  const int off = (tile * (kWave * VEC) + lane) * 16;
 #pragma unroll
   for (int j = 0; j < VEC; ++j)
-    v[j] = __builtin_nontemporal_load(vbase + min(g0 + j * kWave + lane, gmax));
+    v[j] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + j * kWave * 16, 0, kNonTemporal));
 }
 
 // Positions outside [lo, hi) read as -inf; only tiles that touch the window's
