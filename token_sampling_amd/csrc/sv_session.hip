@@ -381,9 +381,9 @@ struct DrawRow {
   // the same tests on values: for the logits of a row that is drawn from (no
   // NaN) the order of the values is that of the keys, and +0 and -0 compare
   // equal as their keys do; one compare instead of the key transform
-  __device__ bool tie_v(float f) const { return idcut < 0 && f == cv; }
+  __device__ bool tie_v(float f) const { return (idcut < 0) & (f == cv); }
   __device__ bool fixed_v(float f, int y) const {
-    return f > cv || (f == cv && idcut >= 0 && y <= idcut);
+    return (f > cv) | ((f == cv) & (idcut >= 0) & (y <= idcut));
   }
   __device__ double w(float l) const {
     // t = kTab (l - lmax) scale: l * sk is exact inside the fma and ck carries
@@ -516,53 +516,57 @@ struct GroupAcc {
   uint32_t np, nq, npq, bad;
 };
 
-// One token's share of its group (see GroupAcc).  Selects rather than
-// branches per lane; the branches test ballots (one value for the whole
-// wave), so no lane masks are set up per token.
+// One token's weights and classes: p's and q's weights are computed on every
+// lane and kept where the token is a member (no branch per token, so that the
+// binary64 chains and table reads of several tokens overlap).
+struct IdW {
+  double pv, qv;
+  bool tp, tq, qbad;
+};
 template <class Tr, bool kQ>
-__device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>& d, bool resid,
-                                                          uint32_t up, uint32_t uq, int y,
-                                                          GroupAcc s) {
+__device__ __attribute__((always_inline)) IdW weigh_id(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                       uint32_t up, uint32_t uq, int y) {
+  IdW r;
   const float fp = Tr::value(up);
-  const bool tp = d.P.tie_v(fp);
-  const bool mp = !tp && d.P.fixed_v(fp, y);
-  bool tq = false, mq = false;
-  float fq = 0.0f;
-  if constexpr (!kQ) {
-    if (resid) {
-      fq = Tr::value(uq);
-      tq = d.Q.tie_v(fq);
-      mq = !tq && d.Q.fixed_v(fq, y);
+  r.tp = d.P.tie_v(fp);
+  const bool mp = !r.tp & d.P.fixed_v(fp, y);
+  const double wp = d.P.w(fp);
+  r.pv = mp ? wp : 0.0;
+  r.qv = 0.0;
+  r.tq = false;
+  r.qbad = false;
+  if (resid) {
+    if constexpr (kQ) {
+      r.qv = (double)__uint_as_float(uq);
+      r.qbad = !(r.qv >= 0.0 && r.qv < INFINITY);
+    } else {
+      const float fq = Tr::value(uq);
+      r.tq = d.Q.tie_v(fq);
+      const bool mq = !r.tq & d.Q.fixed_v(fq, y);
+      const double wq = d.Q.w(fq);
+      r.qv = mq ? wq : 0.0;
     }
   }
-  // no member or tie of p and no tie of q in the whole wave: nothing to add
-  // (where p is zero, a member of q changes no weight)
-  if (!__builtin_amdgcn_ballot_w64(mp || tp || tq)) return s;
-  double pv = 0.0;
-  if (__builtin_amdgcn_ballot_w64(mp)) {
-    const double w = d.P.w(fp);
-    pv = mp ? w : 0.0;
-  }
+  return r;
+}
+
+// One token's share of its group (see GroupAcc).  Only the ties take a
+// branch, on a ballot (one value for the whole wave).
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) GroupAcc add_id(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                          double pv, double qv, bool tp, bool tq,
+                                                          bool qbad, GroupAcc s) {
   if (!resid) {
     s.a += pv;
     s.np += tp ? 1u : 0u;
     return s;
   }
-  double qv = 0.0;
-  bool qbad = false;
-  if constexpr (kQ) {
-    qv = (double)__uint_as_float(uq);
-    qbad = !(qv >= 0.0 && qv < INFINITY);
-  } else if (__builtin_amdgcn_ballot_w64(mq && (mp || tp))) {
-    const double w = d.Q.w(fq);
-    qv = mq ? w : 0.0;
-  }
-  const bool plain = !tp && !tq;
+  const bool plain = !tp & !tq;
   const double df = pv - qv;
-  s.a += (plain && pv > 0.0 && df > 0.0) ? df : 0.0;
+  s.a += (plain & (pv > 0.0) & (df > 0.0)) ? df : 0.0;
   s.ap += tp ? 0.0 : pv;
   if (kQ && plain && pv > 0.0 && qbad) s.bad |= 1u;
-  if (__builtin_amdgcn_ballot_w64(tp || tq)) {  // ties: rows cut by rank only
+  if (__builtin_amdgcn_ballot_w64(tp | tq)) {  // ties: rows cut by rank only
     const double dp = d.P.wcut - qv;   // a tie of p (not of q), kept
     s.bp += (tp && !tq && d.P.wcut > 0.0 && dp > 0.0) ? dp : 0.0;
     const double dq = pv - d.Q.wcut;   // a tie of q (not of p), kept
@@ -574,6 +578,45 @@ __device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>&
     if (kQ && tp && qbad) s.bad |= 2u;
   }
   return s;
+}
+
+// One token's share of its group, in place (see GroupAcc): the branches test
+// ballots, so a weight no lane of the wave needs is not computed.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) GroupAcc weigh1(const DrawCtx<Tr, kQ>& d, bool resid,
+                                                          uint32_t up, uint32_t uq, int y,
+                                                          GroupAcc s) {
+  const float fp = Tr::value(up);
+  const bool tp = d.P.tie_v(fp);
+  const bool mp = !tp & d.P.fixed_v(fp, y);
+  bool tq = false, mq = false;
+  float fq = 0.0f;
+  if constexpr (!kQ) {
+    if (resid) {
+      fq = Tr::value(uq);
+      tq = d.Q.tie_v(fq);
+      mq = !tq & d.Q.fixed_v(fq, y);
+    }
+  }
+  // no member or tie of p and no tie of q in the whole wave: nothing to add
+  // (where p is zero, a member of q changes no weight)
+  if (!__builtin_amdgcn_ballot_w64(mp | tp | tq)) return s;
+  double pv = 0.0, qv = 0.0;
+  bool qbad = false;
+  if (__builtin_amdgcn_ballot_w64(mp)) {
+    const double w = d.P.w(fp);
+    pv = mp ? w : 0.0;
+  }
+  if (resid) {
+    if constexpr (kQ) {
+      qv = (double)__uint_as_float(uq);
+      qbad = !(qv >= 0.0 && qv < INFINITY);
+    } else if (__builtin_amdgcn_ballot_w64(mq & (mp | tp))) {
+      const double w = d.Q.w(fq);
+      qv = mq ? w : 0.0;
+    }
+  }
+  return add_id<Tr, kQ>(d, resid, pv, qv, tp, tq, qbad, s);
 }
 
 // A lane's 8 ids of one step, in place: rows where most ids are members.
@@ -641,14 +684,36 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (uint32_t r = 0; r < total; r += kWave) {
-    const uint32_t i = r + (uint32_t)lane;
+  // rounds of 64 queued ids, two at a time; total <= kWStep and rounds start
+  // at multiples of 64 below it, so every slot read lies in the queue (slots
+  // at or past total hold stale words and are masked)
+  auto entry = [&](uint32_t i, uint32_t& up, uint32_t& uq, int& yy) {
     const bool valid = i < total;
+    up = qu[i];
+    uq = qu[kWStep + i];
+    yy = (int)qu[2 * kWStep + i];
     // past the queue: -inf bits, neither a member nor a tie of either row
-    const uint32_t up = valid ? qu[i] : Tr::kNegInfBits;
-    const uint32_t uq = valid ? qu[kWStep + i] : (kQ ? 0u : Tr::kNegInfBits);
-    const int yy = valid ? (int)qu[2 * kWStep + i] : 0;
-    s = weigh1<Tr, kQ>(d, resid, up, uq, yy, s);
+    up = valid ? up : Tr::kNegInfBits;
+    uq = valid ? uq : (kQ ? 0u : Tr::kNegInfBits);
+    yy = valid ? yy : 0;
+  };
+  uint32_t r = 0;
+  for (; r + kWave < total; r += 2 * kWave) {
+    uint32_t up0, uq0, up1, uq1;
+    int y0, y1;
+    entry(r + (uint32_t)lane, up0, uq0, y0);
+    entry(r + kWave + (uint32_t)lane, up1, uq1, y1);
+    const IdW a0 = weigh_id<Tr, kQ>(d, resid, up0, uq0, y0);
+    const IdW a1 = weigh_id<Tr, kQ>(d, resid, up1, uq1, y1);
+    s = add_id<Tr, kQ>(d, resid, a0.pv, a0.qv, a0.tp, a0.tq, a0.qbad, s);
+    s = add_id<Tr, kQ>(d, resid, a1.pv, a1.qv, a1.tp, a1.tq, a1.qbad, s);
+  }
+  for (; r < total; r += kWave) {
+    uint32_t up0, uq0;
+    int y0;
+    entry(r + (uint32_t)lane, up0, uq0, y0);
+    const IdW a0 = weigh_id<Tr, kQ>(d, resid, up0, uq0, y0);
+    s = add_id<Tr, kQ>(d, resid, a0.pv, a0.qv, a0.tp, a0.tq, a0.qbad, s);
   }
   __builtin_amdgcn_wave_barrier();
   return s;
@@ -976,7 +1041,10 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
 // row kernel; C = 1 needs none) picks the token and writes all the session's
 // outputs.
 template <class Tr, bool kQ>
-__global__ __launch_bounds__(kDrawNT) void k_finalize(
+// The LDS of four workgroups fits a CU (four waves per SIMD); bf16 rows hold
+// their registers to the same occupancy.
+__global__ __launch_bounds__(kDrawNT)
+__attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) void k_finalize(
     const typename Tr::elem_t* __restrict__ target, const typename Tr::elem_t* __restrict__ draft,
     const float* __restrict__ qrows, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ m,
