@@ -119,3 +119,77 @@ def test_more_groups_than_staged():
     h["tokens"] = parity.draw_valid_tokens(h, rng)
     o = parity.run_oracle(h)
     parity.compare(parity.run_gpu(h), o, "draw-1.1M")
+
+
+def _key_bits(k):
+    """bf16 bits of the keys k (key order = value order, +0 at 0x8000)."""
+    k = np.asarray(k, np.int64)
+    return np.where(k >= 0x8000, k - 0x8000, 0x8000 | (0x8000 - k)).astype(np.uint16)
+
+
+def _span_row(rng, V, k0, n, ties):
+    """One id at each of the n keys k0 .. k0+n-1, `ties` more ids at k0, the
+    rest -inf (no mass), in a random order."""
+    row = np.full(V, 0xFF80, np.uint16)
+    ids = rng.permutation(V)
+    row[ids[:n]] = _key_bits(k0 + np.arange(n))
+    row[ids[n:n + ties]] = _key_bits(k0)
+    return row
+
+
+def _cut_in_ties(rows, T, k0, ties):
+    """A top_p (milli) whose cut falls inside the ties at k0 for every row of
+    `rows` (same multiset of logits), and the support's span in keys."""
+    keys = lambda b: np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b).astype(np.int64)
+    for tp in range(999, 0, -1):
+        ok = True
+        for r in rows:
+            st, p, _ = oracle.profile(r, T, 0, tp)
+            k = keys(r.astype(np.int64))
+            kept_ties = int(((k == k0) & (p > 0)).sum())
+            if st != 0 or k[p > 0].min() != k0 or not 0 < kept_ties <= ties:
+                ok = False
+                break
+        if ok:
+            return tp, int(keys(rows[0].astype(np.int64)).max() - k0 + 1)
+    raise AssertionError("no top_p cuts inside the ties")
+
+
+@pytest.mark.parametrize("V", [6144, 5003])
+def test_key_table_spans(V):
+    """Rows cut by rank at a positive key with few distinct member logits take
+    their weights from per-row tables of at most 1535 keys.  Sessions: spans
+    of 1535 keys (the largest a table holds) and 1536 (one more: weighed as
+    before), 300 and 40 keys, a cut at the smallest positive bf16 value, a
+    negative cut, and a target row that fits with a draft row that does not.
+    Both residual draws (drafts permuted) and draws from p (drafts equal to
+    the targets) occur; V = 6144 gives aligned rows of whole groups, V = 5003
+    unaligned rows with a partial group."""
+    parity.log(f"[case] draw key-table spans V={V}")
+    rng = np.random.default_rng(300 + V)
+    one = 0x8000 + 0x3F80      # key of 1.0
+    cases = [  # (k0 of p, span of p, span of q, drafts equal)
+        (one, 1535, 1535, False), (one, 1536, 1536, False), (one - 128, 300, 300, True),
+        (one + 192, 40, 40, False), (0x8001, 200, 200, False), (0x8000 - 0x3F80, 300, 300, False),
+        (one, 1535, 1536, False), (one + 128, 800, 800, True)]
+    B, M, ties = len(cases), 3, 1200
+    tgt = np.zeros((B, M + 1, V), np.uint16)
+    dft = np.zeros((B, M, V), np.uint16)
+    s = oracle.make_sampling(B)
+    spans = []
+    for b, (k0, n, nq, same) in enumerate(cases):
+        vmax = float(oracle.bf16_to_float(_key_bits(k0 + max(n, nq) - 1)))
+        T = int(max(1.0, abs(vmax)) * 2000)   # milli: nearly flat weights over the span
+        tgt[b] = [_span_row(rng, V, k0, n, ties) for _ in range(M + 1)]
+        dft[b] = tgt[b, :M] if same else [_span_row(rng, V, k0, nq, ties) for _ in range(M)]
+        tp, span_p = _cut_in_ties(list(tgt[b]) + list(dft[b]), T, k0, ties + 1)
+        spans.append(span_p)
+        s[b]["temperature_milli"], s[b]["top_p_milli"] = T, tp
+    assert spans[0] == 1535 and spans[1] == 1536
+    h = dict(target=tgt, draft=dft, tokens=np.zeros((B, M), np.int32), m=np.full(B, M, np.int32),
+             rule=np.full(B, 2, np.int32), sampling=s, seed=31, round=32)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    o = parity.run_oracle(h)
+    a = o["accepted_len"]
+    assert ((a >= 0) & (a < M)).sum() >= 3 and (a == M).sum() >= 2, a
+    parity.compare(parity.run_gpu(h), o, f"draw-key-tables-{V}")

@@ -516,18 +516,19 @@ struct GroupAcc {
   uint32_t np, nq, npq, bad;
 };
 
-// One token's weights and classes: p's and q's weights are computed on every
-// lane and kept where the token is a member (no branch per token, so that the
-// binary64 chains and table reads of several tokens overlap).
+// One token's weights and classes from its binary32 logits (fp, and uq: q's
+// logit as binary32 bits, or a published q entry): p's and q's weights are
+// computed on every lane and kept where the token is a member (no branch per
+// token, so that the binary64 chains and table reads of several tokens
+// overlap).
 struct IdW {
   double pv, qv;
   bool tp, tq, qbad;
 };
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) IdW weigh_id(const DrawCtx<Tr, kQ>& d, bool resid,
-                                                       uint32_t up, uint32_t uq, int y) {
+                                                       float fp, uint32_t uq, int y) {
   IdW r;
-  const float fp = Tr::value(up);
   r.tp = d.P.tie_v(fp);
   const bool mp = !r.tp & d.P.fixed_v(fp, y);
   const double wp = d.P.w(fp);
@@ -540,7 +541,7 @@ __device__ __attribute__((always_inline)) IdW weigh_id(const DrawCtx<Tr, kQ>& d,
       r.qv = (double)__uint_as_float(uq);
       r.qbad = !(r.qv >= 0.0 && r.qv < INFINITY);
     } else {
-      const float fq = Tr::value(uq);
+      const float fq = __uint_as_float(uq);
       r.tq = d.Q.tie_v(fq);
       const bool mq = !r.tq & d.Q.fixed_v(fq, y);
       const double wq = d.Q.w(fq);
@@ -550,8 +551,25 @@ __device__ __attribute__((always_inline)) IdW weigh_id(const DrawCtx<Tr, kQ>& d,
   return r;
 }
 
-// One token's share of its group (see GroupAcc).  Only the ties take a
-// branch, on a ballot (one value for the whole wave).
+// One residual token's share of its group when no lane of the wave holds a
+// tie of either row: p is zero off its support, and a draft row's q is never
+// negative, so max(p - q, 0) is the residual.
+template <bool kQ>
+__device__ __attribute__((always_inline)) GroupAcc add_plain(double pv, double qv, bool qbad,
+                                                             GroupAcc s) {
+  const double df = pv - qv;
+  if constexpr (kQ) {
+    s.a += ((pv > 0.0) & (df > 0.0)) ? df : 0.0;
+    if (pv > 0.0 && qbad) s.bad |= 1u;
+  } else {
+    s.a += __builtin_fmax(df, 0.0);
+  }
+  s.ap += pv;
+  return s;
+}
+
+// One token's share of its group (see GroupAcc), ties included.  Only the
+// ties take a branch, on a ballot (one value for the whole wave).
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) GroupAcc add_id(const DrawCtx<Tr, kQ>& d, bool resid,
                                                           double pv, double qv, bool tp, bool tq,
@@ -630,6 +648,82 @@ __device__ __attribute__((always_inline)) void weigh8(const DrawCtx<Tr, kQ>& d, 
     s = weigh1<Tr, kQ>(d, resid, pr.get(e), resid ? qr.get(e) : 0u, y + e, s);
 }
 
+// Table mode: a bf16 row cut by rank (idcut < 0) at a key above +0, with at
+// most kKeyTab - 1 keys from the cut key to its largest logit, has few
+// distinct member logits, and a member's weight depends on its logit alone.
+// Its table holds, at entry i, the weight of the logit whose key is kcut + i
+// (entry 0, the ties, 0: they are weighed by rank), and at entry n, past the
+// largest key, 0.  For logits above +0 the binary32 bits grow with the key
+// and step by 2^16 per key, so (bits - bits(cut)) >> 13 is entry i's byte
+// offset; every logit below the cut (negative ones too: their bits lie past
+// the finite positive range, which holds bits(cut) + n 2^16) gives a larger
+// offset, clamped to entry n.
+constexpr int kKeyTab = 1536;  // entries of a row table, the zero entry included
+struct KeyTab {
+  bool on;
+  const double* t[2];  // p's and q's tables
+  uint32_t cvb[2];     // binary32 bits of each row's cut value
+  uint32_t zero[2];    // byte offset of each table's zero entry
+};
+__device__ inline double key_weight(const double* t, uint32_t bits, uint32_t cvb, uint32_t zero) {
+  const uint32_t off = min((bits - cvb) >> 13, zero);
+  return *(const double*)((const char*)t + off);
+}
+// Keys from a row's cut key to its largest logit when the row can take a
+// table (bf16 rows), else 0.
+__device__ inline int key_span(const RowRec& r) {
+  if (r.idcut >= 0 || r.kcut <= Bf16::kSign) return 0;
+  const int n = (int)Bf16::key(__float_as_uint(r.lmax) >> 16) - (int)r.kcut + 1;
+  return (n >= 1 && n <= kKeyTab - 1) ? n : 0;
+}
+
+// A lane's 8 ids of one step in table mode: the weights of p and q read from
+// the key tables (ties and non-members read 0), kTabBatch ids at a time, then
+// each id's share in id order.
+#ifndef SV_TAB_BATCH
+#define SV_TAB_BATCH 2
+#endif
+constexpr int kTabBatch = SV_TAB_BATCH;
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) void weigh8_table(
+    const DrawCtx<Tr, kQ>& d, const KeyTab& kt, bool resid,
+    const typename DrawCtx<Tr, kQ>::RawP& pr, const typename DrawCtx<Tr, kQ>::RawQ& qr,
+    GroupAcc& s) {
+#pragma unroll
+  for (int h = 0; h < kPer; h += kTabBatch) {
+    uint32_t bp[kTabBatch], bq[kTabBatch];
+    double pv[kTabBatch], qv[kTabBatch];
+#pragma unroll
+    for (int e = 0; e < kTabBatch; ++e) {
+      bp[e] = __float_as_uint(Tr::value(pr.get(h + e)));
+      pv[e] = key_weight(kt.t[0], bp[e], kt.cvb[0], kt.zero[0]);
+      if (resid) {
+        bq[e] = __float_as_uint(Tr::value(qr.get(h + e)));
+        qv[e] = key_weight(kt.t[1], bq[e], kt.cvb[1], kt.zero[1]);
+      }
+    }
+    if (!resid) {
+#pragma unroll
+      for (int e = 0; e < kTabBatch; ++e) {
+        s.a += pv[e];
+        s.np += bp[e] == kt.cvb[0] ? 1u : 0u;
+      }
+      continue;
+    }
+    bool tie = false;  // a tie of either row among the batch's ids
+#pragma unroll
+    for (int e = 0; e < kTabBatch; ++e) tie |= (bp[e] == kt.cvb[0]) | (bq[e] == kt.cvb[1]);
+    if (!__builtin_amdgcn_ballot_w64(tie)) {
+#pragma unroll
+      for (int e = 0; e < kTabBatch; ++e) s = add_plain<kQ>(pv[e], qv[e], false, s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kTabBatch; ++e)
+        s = add_id<Tr, kQ>(d, true, pv[e], qv[e], bp[e] == kt.cvb[0], bq[e] == kt.cvb[1], false, s);
+    }
+  }
+}
+
 // Which of a lane's 8 ids can add to a group record: ids at or above p's cut
 // key (members or ties of p), and for a residual the ties of q (counted even
 // where p is zero).  A member of q where p is zero adds nothing: every
@@ -655,7 +749,8 @@ __device__ __attribute__((always_inline)) uint32_t need_bits(
 // queue is filled one element position at a time (a ballot and its prefix
 // count per position), so it holds the ids by position, then lane; a group
 // record only sums its ids' weights and counts its ties, so their order is
-// free.  qu holds the wave's queue: p bits, q bits, ids.
+// free.  qu holds the wave's queue: p's logits and q's (binary32 bits;
+// a published q row's entries), ids.
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
     const DrawCtx<Tr, kQ>& d, bool resid, int y, const typename DrawCtx<Tr, kQ>::RawP& pr,
@@ -664,17 +759,24 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
   uint32_t total = 0;  // wave-uniform
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const uint32_t up = pr.get(e);
-    const uint32_t uq = resid ? qr.get(e) : 0u;
-    bool n = Tr::value(up) >= d.P.cv;  // at or above p's cut key
-    if constexpr (!kQ)
-      if (resid) n |= d.Q.tie_v(Tr::value(uq));
+    const float fp = Tr::value(pr.get(e));
+    bool n = fp >= d.P.cv;  // at or above p's cut key
+    uint32_t uq = 0u;       // q's logit as binary32 bits, or the published entry
+    if (resid) {
+      if constexpr (kQ) {
+        uq = qr.get(e);
+      } else {
+        const float fq = Tr::value(qr.get(e));
+        n |= d.Q.tie_v(fq);
+        uq = __float_as_uint(fq);
+      }
+    }
     const uint64_t m = __builtin_amdgcn_ballot_w64(n);
     if (m) {
-      const uint32_t j = total + __builtin_amdgcn_mbcnt_hi(
-                                     (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint32_t j = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, total));
       if (n) {
-        qu[j] = up;
+        qu[j] = __float_as_uint(fp);
         qu[kWStep + j] = uq;
         qu[2 * kWStep + j] = (uint32_t)(y + e);
       }
@@ -692,9 +794,9 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
     up = qu[i];
     uq = qu[kWStep + i];
     yy = (int)qu[2 * kWStep + i];
-    // past the queue: -inf bits, neither a member nor a tie of either row
-    up = valid ? up : Tr::kNegInfBits;
-    uq = valid ? uq : (kQ ? 0u : Tr::kNegInfBits);
+    // past the queue: -inf, neither a member nor a tie of either row
+    up = valid ? up : 0xFF800000u;
+    uq = valid ? uq : (kQ ? 0u : 0xFF800000u);
     yy = valid ? yy : 0;
   };
   uint32_t r = 0;
@@ -703,16 +805,21 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
     int y0, y1;
     entry(r + (uint32_t)lane, up0, uq0, y0);
     entry(r + kWave + (uint32_t)lane, up1, uq1, y1);
-    const IdW a0 = weigh_id<Tr, kQ>(d, resid, up0, uq0, y0);
-    const IdW a1 = weigh_id<Tr, kQ>(d, resid, up1, uq1, y1);
-    s = add_id<Tr, kQ>(d, resid, a0.pv, a0.qv, a0.tp, a0.tq, a0.qbad, s);
-    s = add_id<Tr, kQ>(d, resid, a1.pv, a1.qv, a1.tp, a1.tq, a1.qbad, s);
+    const IdW a0 = weigh_id<Tr, kQ>(d, resid, __uint_as_float(up0), uq0, y0);
+    const IdW a1 = weigh_id<Tr, kQ>(d, resid, __uint_as_float(up1), uq1, y1);
+    if (resid && !__builtin_amdgcn_ballot_w64(a0.tp | a0.tq | a1.tp | a1.tq)) {
+      s = add_plain<kQ>(a0.pv, a0.qv, a0.qbad, s);
+      s = add_plain<kQ>(a1.pv, a1.qv, a1.qbad, s);
+    } else {
+      s = add_id<Tr, kQ>(d, resid, a0.pv, a0.qv, a0.tp, a0.tq, a0.qbad, s);
+      s = add_id<Tr, kQ>(d, resid, a1.pv, a1.qv, a1.tp, a1.tq, a1.qbad, s);
+    }
   }
   for (; r < total; r += kWave) {
     uint32_t up0, uq0;
     int y0;
     entry(r + (uint32_t)lane, up0, uq0, y0);
-    const IdW a0 = weigh_id<Tr, kQ>(d, resid, up0, uq0, y0);
+    const IdW a0 = weigh_id<Tr, kQ>(d, resid, __uint_as_float(up0), uq0, y0);
     s = add_id<Tr, kQ>(d, resid, a0.pv, a0.qv, a0.tp, a0.tq, a0.qbad, s);
   }
   __builtin_amdgcn_wave_barrier();
@@ -767,11 +874,12 @@ __device__ inline GroupAcc load_group(const GroupRec* rec) {
 // loads that depend on the step (the row's end, a scalar fallback) it waits
 // for all of them at each step, and the ring drains.  kResid fixes, at
 // compile time, whether the q row is read.
-template <class Tr, bool kQ, bool kQueued, bool kSteady = false, bool kResid = false>
+enum RecordMode { kInPlace = 0, kQueued = 1, kTable = 2 };
+template <class Tr, bool kQ, int kMode, bool kSteady = false, bool kResid = false>
 __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>& d, bool resid,
                                                            int g0, int g1,
                                                            GroupRec* __restrict__ recs,
-                                                           uint32_t* qu) {
+                                                           uint32_t* qu, const KeyTab& kt) {
   if constexpr (kSteady) resid = kResid;
   const int lane = __lane_id();
   const int nk = (g1 - g0) * kSteps;
@@ -801,7 +909,8 @@ __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>
         if (kk + 3 < nk)
           d.load(ybase + (kk + 3) * kWStep, resid, p[(u + 3) % kSteps], q[(u + 3) % kSteps]);
       const int y = ybase + kk * kWStep;
-      if constexpr (kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, y, p[u], q[u], s, qu);
+      if constexpr (kMode == kTable) weigh8_table<Tr, kQ>(d, kt, resid, p[u], q[u], s);
+      else if constexpr (kMode == kQueued) s = weigh_step_queued<Tr, kQ>(d, resid, y, p[u], q[u], s, qu);
       else weigh8<Tr, kQ>(d, resid, y, p[u], q[u], s);
       if constexpr (kSteady) {
         __builtin_amdgcn_sched_barrier(0);
@@ -828,8 +937,20 @@ template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, kQ>& d, bool resid,
                                                              int g0, int g1, bool sparse,
                                                              GroupRec* __restrict__ recs,
-                                                             uint32_t* qu) {
+                                                             uint32_t* qu, const KeyTab& kt) {
   if (g0 >= g1) return;
+  if constexpr (std::is_same<Tr, Bf16>::value && !kQ) {
+    if (kt.on) {
+      const int gs = d.aligned(resid) ? min(g1, d.V / kGroup) : g0;
+      if (g0 < gs) {
+        if (resid) record_loop<Tr, kQ, kTable, true, true>(d, resid, g0, gs, recs, qu, kt);
+        else record_loop<Tr, kQ, kTable, true, false>(d, resid, g0, gs, recs, qu, kt);
+      }
+      const int gr = max(g0, gs);
+      if (gr < g1) record_loop<Tr, kQ, kTable>(d, resid, gr, g1, recs, qu, kt);
+      return;
+    }
+  }
   bool queued = false;
   if (sparse) {  // the first step's ids to weigh, over the wave
     typename DrawCtx<Tr, kQ>::RawP p0;
@@ -844,17 +965,17 @@ __device__ __attribute__((always_inline)) void record_groups(const DrawCtx<Tr, k
   const int gs = d.aligned(resid) ? min(g1, d.V / kGroup) : g0;
   if (g0 < gs) {
     if (queued) {
-      if (resid) record_loop<Tr, kQ, true, true, true>(d, resid, g0, gs, recs, qu);
-      else record_loop<Tr, kQ, true, true, false>(d, resid, g0, gs, recs, qu);
+      if (resid) record_loop<Tr, kQ, kQueued, true, true>(d, resid, g0, gs, recs, qu, kt);
+      else record_loop<Tr, kQ, kQueued, true, false>(d, resid, g0, gs, recs, qu, kt);
     } else {
-      if (resid) record_loop<Tr, kQ, false, true, true>(d, resid, g0, gs, recs, qu);
-      else record_loop<Tr, kQ, false, true, false>(d, resid, g0, gs, recs, qu);
+      if (resid) record_loop<Tr, kQ, kInPlace, true, true>(d, resid, g0, gs, recs, qu, kt);
+      else record_loop<Tr, kQ, kInPlace, true, false>(d, resid, g0, gs, recs, qu, kt);
     }
   }
   const int gr = max(g0, gs);
   if (gr < g1) {
-    if (queued) record_loop<Tr, kQ, true>(d, resid, gr, g1, recs, qu);
-    else record_loop<Tr, kQ, false>(d, resid, gr, g1, recs, qu);
+    if (queued) record_loop<Tr, kQ, kQueued>(d, resid, gr, g1, recs, qu, kt);
+    else record_loop<Tr, kQ, kInPlace>(d, resid, gr, g1, recs, qu, kt);
   }
 }
 
@@ -877,6 +998,7 @@ struct DrawSmem {
   union {
     uint64_t grec[kLdsGroups][6];             // the pick: staged group records
     uint32_t queue[kDrawWaves][3 * kWStep];  // the records: each wave's queue
+    double ktab[2][kKeyTab];                  // the records in table mode: p's, q's table
   };
   double tab_p[kTab];
   double tab_q[kTab];
@@ -1112,6 +1234,30 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
   const DrawCtx<Tr, kQ> d{Prow, Qrow, qrow, ((uintptr_t)qrow & 15u) == 0, V};
   __syncthreads();  // tables ready
 
+  // rows with few member logits: their key tables, from the weights above
+  KeyTab kt{};
+  if constexpr (std::is_same<Tr, Bf16>::value && !kQ) {
+    const RowRec& rp = rows[(size_t)b * R + job.trow];
+    const int np = key_span(rp);
+    const int nq = resid ? key_span(rows[(size_t)b * R + M + 1 + job.drow]) : 1;
+    if (np > 0 && nq > 0) {
+      kt.on = true;
+      const DrawRow<Tr>* row2[2] = {&d.P, &d.Q};
+      const int n2[2] = {np, nq};
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !resid) break;
+        const DrawRow<Tr>& D = *row2[r];
+        kt.t[r] = sm.ktab[r];
+        kt.cvb[r] = __float_as_uint(D.cv);
+        kt.zero[r] = (uint32_t)n2[r] * 8u;
+        for (int i = t; i <= n2[r]; i += kDrawNT)
+          sm.ktab[r][i] = (i == 0 || i == n2[r]) ? 0.0 : D.w(Tr::value(Tr::unkey(D.kcut + (uint32_t)i)));
+      }
+      __syncthreads();
+    }
+  }
+
   // this wave's groups, then (several chunks) the session's counter
   GroupRec* recs = groups + (size_t)b * G;
   {
@@ -1119,7 +1265,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     // rows cut to a support (top-k, top-p) weigh their members only;
     // untruncated rows, where every id is a member, weigh in place
     const bool sparse = !(d.P.kcut == Tr::kNegInfKey + 1 && d.P.idcut >= 0);
-    record_groups<Tr, kQ>(d, resid, min(g0, G), min(g0 + gw, G), sparse, recs, sm.queue[wid]);
+    record_groups<Tr, kQ>(d, resid, min(g0, G), min(g0 + gw, G), sparse, recs, sm.queue[wid],
+                          kt);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's records are stored
   __syncthreads();
