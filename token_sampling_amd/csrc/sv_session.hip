@@ -653,28 +653,44 @@ __device__ __attribute__((always_inline)) void weigh8(const DrawCtx<Tr, kQ>& d, 
 // distinct member logits, and a member's weight depends on its logit alone.
 // Its table holds, at entry i, the weight of the logit whose key is kcut + i
 // (entry 0, the ties, 0: they are weighed by rank), and at entry n, past the
-// largest key, 0.  For logits above +0 the binary32 bits grow with the key
-// and step by 2^16 per key, so (bits - bits(cut)) >> 13 is entry i's byte
-// offset; every logit below the cut (negative ones too: their bits lie past
-// the finite positive range, which holds bits(cut) + n 2^16) gives a larger
-// offset, clamped to entry n.
+// largest key, 0.  For logits above +0 the bf16 bits grow with the key by
+// one per key, so bits - bits(cut) is the entry; every logit below the cut
+// gives, modulo 2^16, a larger value (negative ones too: their bits lie past
+// the finite positive range, which holds bits(cut) + n), clamped to n.
 constexpr int kKeyTab = 1536;  // entries of a row table, the zero entry included
 struct KeyTab {
   bool on;
   const double* t[2];  // p's and q's tables
-  uint32_t cvb[2];     // binary32 bits of each row's cut value
-  uint32_t zero[2];    // byte offset of each table's zero entry
+  uint32_t cut2[2];    // each row's cut logit (bf16 bits) in both halves
+  uint32_t n2[2];      // each table's zero entry n in both halves
 };
-__device__ inline double key_weight(const double* t, uint32_t bits, uint32_t cvb, uint32_t zero) {
-  const uint32_t off = min((bits - cvb) >> 13, zero);
-  return *(const double*)((const char*)t + off);
-}
 // Keys from a row's cut key to its largest logit when the row can take a
 // table (bf16 rows), else 0.
 __device__ inline int key_span(const RowRec& r) {
   if (r.idcut >= 0 || r.kcut <= Bf16::kSign) return 0;
   const int n = (int)Bf16::key(__float_as_uint(r.lmax) >> 16) - (int)r.kcut + 1;
   return (n >= 1 && n <= kKeyTab - 1) ? n : 0;
+}
+
+// Table mode on the logits as they are loaded, a dword holding two bf16
+// logits (the lower id in the low half): with 16-bit halves, key - kcut is
+// bits - bits(cut) for logits above +0 (and wraps past n for the others, see
+// above), so one packed subtract and one packed minimum give both entries,
+// and the sign bit of entry - 1 marks a tie (entry 0).
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+struct PairEntries {
+  uint32_t lo, hi;  // byte offsets of the two logits' entries
+  uint32_t tie;     // 0x8000 (low) and 0x80000000 (high) for ties
+};
+__device__ inline PairEntries pair_entries(uint32_t d, uint32_t cut2, uint32_t n2) {
+  u16x2 x = __builtin_bit_cast(u16x2, d) - __builtin_bit_cast(u16x2, cut2);
+  x = __builtin_elementwise_min(x, __builtin_bit_cast(u16x2, n2));
+  const uint32_t off = __builtin_bit_cast(uint32_t, (u16x2)(x << (uint16_t)3));
+  const u16x2 xm = x - (u16x2)(uint16_t)1;
+  return PairEntries{off & 0xFFFFu, off >> 16, __builtin_bit_cast(uint32_t, xm) & 0x80008000u};
+}
+__device__ inline double table_at(const double* t, uint32_t off) {
+  return *(const double*)((const char*)t + off);
 }
 
 // A lane's 8 ids of one step in table mode: the weights of p and q read from
@@ -684,42 +700,51 @@ __device__ inline int key_span(const RowRec& r) {
 #define SV_TAB_BATCH 2
 #endif
 constexpr int kTabBatch = SV_TAB_BATCH;
+static_assert(kTabBatch % 2 == 0, "whole dwords of bf16 pairs");
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) void weigh8_table(
     const DrawCtx<Tr, kQ>& d, const KeyTab& kt, bool resid,
     const typename DrawCtx<Tr, kQ>::RawP& pr, const typename DrawCtx<Tr, kQ>::RawQ& qr,
     GroupAcc& s) {
+  static_assert(sizeof(typename Tr::elem_t) == 2, "bf16 rows");
 #pragma unroll
   for (int h = 0; h < kPer; h += kTabBatch) {
-    uint32_t bp[kTabBatch], bq[kTabBatch];
     double pv[kTabBatch], qv[kTabBatch];
+    uint32_t tp[kTabBatch / 2], tq[kTabBatch / 2];
+    uint32_t tie = 0;
 #pragma unroll
-    for (int e = 0; e < kTabBatch; ++e) {
-      bp[e] = __float_as_uint(Tr::value(pr.get(h + e)));
-      pv[e] = key_weight(kt.t[0], bp[e], kt.cvb[0], kt.zero[0]);
+    for (int j = 0; j < kTabBatch / 2; ++j) {
+      const PairEntries ep = pair_entries(pr.v[h / 2 + j], kt.cut2[0], kt.n2[0]);
+      pv[2 * j] = table_at(kt.t[0], ep.lo);
+      pv[2 * j + 1] = table_at(kt.t[0], ep.hi);
+      tp[j] = ep.tie;
+      tie |= ep.tie;
+      tq[j] = 0;
       if (resid) {
-        bq[e] = __float_as_uint(Tr::value(qr.get(h + e)));
-        qv[e] = key_weight(kt.t[1], bq[e], kt.cvb[1], kt.zero[1]);
+        const PairEntries eq = pair_entries(qr.v[h / 2 + j], kt.cut2[1], kt.n2[1]);
+        qv[2 * j] = table_at(kt.t[1], eq.lo);
+        qv[2 * j + 1] = table_at(kt.t[1], eq.hi);
+        tq[j] = eq.tie;
+        tie |= eq.tie;
       }
     }
     if (!resid) {
 #pragma unroll
-      for (int e = 0; e < kTabBatch; ++e) {
-        s.a += pv[e];
-        s.np += bp[e] == kt.cvb[0] ? 1u : 0u;
-      }
+      for (int e = 0; e < kTabBatch; ++e) s.a += pv[e];
+#pragma unroll
+      for (int j = 0; j < kTabBatch / 2; ++j) s.np += (uint32_t)__popc(tp[j]);
       continue;
     }
-    bool tie = false;  // a tie of either row among the batch's ids
-#pragma unroll
-    for (int e = 0; e < kTabBatch; ++e) tie |= (bp[e] == kt.cvb[0]) | (bq[e] == kt.cvb[1]);
-    if (!__builtin_amdgcn_ballot_w64(tie)) {
+    if (!__builtin_amdgcn_ballot_w64(tie != 0)) {
 #pragma unroll
       for (int e = 0; e < kTabBatch; ++e) s = add_plain<kQ>(pv[e], qv[e], false, s);
     } else {
 #pragma unroll
-      for (int e = 0; e < kTabBatch; ++e)
-        s = add_id<Tr, kQ>(d, true, pv[e], qv[e], bp[e] == kt.cvb[0], bq[e] == kt.cvb[1], false, s);
+      for (int e = 0; e < kTabBatch; ++e) {
+        const uint32_t bit = (e & 1) ? 0x80000000u : 0x8000u;
+        s = add_id<Tr, kQ>(d, true, pv[e], qv[e], (tp[e / 2] & bit) != 0, (tq[e / 2] & bit) != 0,
+                           false, s);
+      }
     }
   }
 }
@@ -1064,7 +1089,7 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
                                                              int g, uint32_t rp, uint32_t rq,
                                                              double base, double tgt, bool find,
                                                              DrawSmem& sm) {
-  const int lane = __lane_id(), wid = (int)threadIdx.x / kWave;
+  const int lane = __lane_id(), wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int y = g * kGroup + wid * kWStep + lane * kPer;
   typename DrawCtx<Tr, kQ>::RawP pr;
   typename DrawCtx<Tr, kQ>::RawQ qr;
@@ -1183,7 +1208,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
   const int c = (int)blockIdx.x - b * C;
   if (b >= B) return;
   const int t = threadIdx.x;
-  const int wid = t / kWave;
+  // the wave's index, as a scalar: the record loops' bounds derive from it
+  const int wid = __builtin_amdgcn_readfirstlane(t / kWave);
   // only chunk 0 has work in sessions that draw no token from whole rows
   if (c > 0 && (draw_flag[b] != draw_token || rule[b] == SV_RULE_GREEDY || sess_status[b] != 0))
     return;
@@ -1236,6 +1262,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
 
   // rows with few member logits: their key tables, from the weights above
   KeyTab kt{};
+  kt.t[0] = sm.ktab[0];  // set on every path: a constant LDS address, folded into the reads
+  kt.t[1] = sm.ktab[1];
   if constexpr (std::is_same<Tr, Bf16>::value && !kQ) {
     const RowRec& rp = rows[(size_t)b * R + job.trow];
     const int np = key_span(rp);
@@ -1248,9 +1276,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
       for (int r = 0; r < 2; ++r) {
         if (r == 1 && !resid) break;
         const DrawRow<Tr>& D = *row2[r];
-        kt.t[r] = sm.ktab[r];
-        kt.cvb[r] = __float_as_uint(D.cv);
-        kt.zero[r] = (uint32_t)n2[r] * 8u;
+        const uint32_t cut = __float_as_uint(D.cv) >> 16;
+        kt.cut2[r] = cut | (cut << 16);
+        kt.n2[r] = (uint32_t)n2[r] | ((uint32_t)n2[r] << 16);
         for (int i = t; i <= n2[r]; i += kDrawNT)
           sm.ktab[r][i] = (i == 0 || i == n2[r]) ? 0.0 : D.w(Tr::value(Tr::unkey(D.kcut + (uint32_t)i)));
       }
