@@ -852,17 +852,77 @@ __device__ __attribute__((always_inline)) GroupAcc weigh_step_queued(
 }
 
 // Group records cross workgroups as six 64-bit words in device-scope atomics
-// (the session's workgroups may run on different L2 caches): lane i of the
-// wave stores word i of the wave-uniform sums.
-__device__ inline void store_group(GroupRec* rec, const GroupAcc& s) {
+// (the session's workgroups may run on different L2 caches): word i of a
+// record is a, bp, cq1, cq0, ap (i = 0..4), and the tie counts np | nq << 16 |
+// (npq | bad << 16) << 32 (i = 5).
+// A group's sums over the wave, stored as its record (the words above).
+// The six 64-bit fields (five weights; the tie counts packed exactly into one
+// binary64 integer, each count below 2^12 and each flag count below 2^8) and
+// two empty ones are reduced by a transposed butterfly: across 32 and then 16
+// lanes a lane keeps half of its fields and takes its partner's share of
+// them (v_permlane32_swap, v_permlane16_swap: after a swap of the fields a, b
+// that the two halves keep, a + b is the pair's sum in both), across 8 lanes
+// one of its two (DPP row mirror), and the 8 lanes that hold field f add it
+// up (DPP), so lane 8f stores word f.  The order of the additions is fixed.
+__device__ inline void swap_halves(double& a, double& b, bool rows16) {
+  const uint64_t ua = (uint64_t)__double_as_longlong(a), ub = (uint64_t)__double_as_longlong(b);
+  uint32_t lo0, lo1, hi0, hi1;
+  if (rows16) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)ua, (uint32_t)ub, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
+                                                     false, false);
+    lo0 = lo[0], lo1 = lo[1], hi0 = hi[0], hi1 = hi[1];
+  } else {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
+                                                     false, false);
+    lo0 = lo[0], lo1 = lo[1], hi0 = hi[0], hi1 = hi[1];
+  }
+  a = __longlong_as_double((long long)(((uint64_t)hi0 << 32) | lo0));
+  b = __longlong_as_double((long long)(((uint64_t)hi1 << 32) | lo1));
+}
+template <int kCtrl>
+__device__ inline double dpp_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), kCtrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ inline void reduce_store_group(GroupRec* rec, const GroupAcc& s) {
+  constexpr int kRowMirror = 0x140, kHalfMirror = 0x141;
+  constexpr int kQuadSwap2 = 0x4E, kQuadSwap1 = 0xB1;  // quad_perm [2,3,0,1], [1,0,3,2]
   const int lane = __lane_id();
-  const double dv =
-      lane == 0 ? s.a : lane == 1 ? s.bp : lane == 2 ? s.cq1 : lane == 3 ? s.cq0 : s.ap;
-  uint64_t w = (uint64_t)__double_as_longlong(dv);
-  if (lane == 5)
-    w = (uint64_t)(s.np | (s.nq << 16)) | ((uint64_t)(s.npq | (s.bad << 16)) << 32);
-  if (lane < 6)
-    __hip_atomic_store((uint64_t*)rec + lane, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t c_lo = s.np | (s.nq << 12);
+  const uint32_t c_hi = s.npq | ((s.bad & 1u) << 12) | ((s.bad >> 1) << 20);
+  double v[8] = {s.a, s.bp, s.cq1, s.cq0, s.ap, (double)c_lo + (double)c_hi * 16777216.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // lanes 0-31 keep fields 0-3, lanes 32-63 fields 4-7
+    swap_halves(v[i], v[i + 4], false);
+    v[i] = v[i] + v[i + 4];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // within each half, rows 0 and 2 keep the first two
+    swap_halves(v[j], v[j + 2], true);
+    v[j] = v[j] + v[j + 2];
+  }
+  const bool up8 = (lane & 8) != 0;  // within a row, lanes 8-15 keep the second
+  const double keep = up8 ? v[1] : v[0];
+  const double x = keep + dpp_f64<kRowMirror>(up8 ? v[0] : v[1]);
+  const double x1 = x + dpp_f64<kHalfMirror>(x);
+  const double x2 = x1 + dpp_f64<kQuadSwap2>(x1);
+  const double t = x2 + dpp_f64<kQuadSwap1>(x2);  // field lane >> 3, in all 8 of its lanes
+  const int f = lane >> 3;
+  if ((lane & 7) == 0 && f < 6) {
+    uint64_t w = (uint64_t)__double_as_longlong(t);
+    if (f == 5) {
+      const uint32_t hi = (uint32_t)(t * (1.0 / 16777216.0));
+      const uint32_t lo = (uint32_t)(t - (double)hi * 16777216.0);
+      const uint32_t np = lo & 0xFFFu, nq = lo >> 12, npq = hi & 0xFFFu;
+      const uint32_t bad = (((hi >> 12) & 0xFFu) ? 1u : 0u) | ((hi >> 20) ? 2u : 0u);
+      w = (uint64_t)(np | (nq << 16)) | ((uint64_t)(npq | (bad << 16)) << 32);
+    }
+    __hip_atomic_store((uint64_t*)rec + f, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 __device__ inline GroupAcc decode_group(const uint64_t (&w)[6]) {
   GroupAcc r;
@@ -942,16 +1002,7 @@ __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>
         d.template load_vec<kResid>(ybase + min(kk + kSteps, nk - 1) * kWStep, p[u], q[u]);
       }
     }
-    s.a = wave_reduce(s.a, OpAdd());
-    s.bp = wave_reduce(s.bp, OpAdd());
-    s.cq1 = wave_reduce(s.cq1, OpAdd());
-    s.cq0 = wave_reduce(s.cq0, OpAdd());
-    s.ap = wave_reduce(s.ap, OpAdd());
-    s.np = wave_reduce(s.np, OpAdd());
-    s.nq = wave_reduce(s.nq, OpAdd());
-    s.npq = wave_reduce(s.npq, OpAdd());
-    s.bad = wave_reduce(s.bad, OpOr());
-    store_group(recs + g0 + k / kSteps, s);
+    reduce_store_group(recs + g0 + k / kSteps, s);
   }
 }
 
@@ -1030,6 +1081,7 @@ struct DrawSmem {
   double dscan[kDrawWaves];
   uint64_t uscan[kDrawWaves];
   int32_t ired[kDrawWaves];
+  int32_t red3[kDrawWaves][3];  // group scans: first crossing, last id with weight, unusable
   uint32_t wties[kDrawWaves];  // group scans: ties of each wave's step
   double wsum[kDrawWaves];     // group scans: weight of each wave's step
   int32_t sg[2];            // groups holding the cut of p, of q (-1: none)
@@ -1078,22 +1130,39 @@ struct ScanRes {
   bool bad;
 };
 
+// A thread's 8 ids of group g for group_scan, loaded ahead of it (so that
+// the loads of two groups can be in flight together).
+template <class Tr, bool kQ>
+struct ScanLoad {
+  typename DrawCtx<Tr, kQ>::RawP pr;
+  typename DrawCtx<Tr, kQ>::RawQ qr;
+};
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) ScanLoad<Tr, kQ> scan_load(const DrawCtx<Tr, kQ>& d,
+                                                                     bool resid, int g) {
+  const int lane = __lane_id(), wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  ScanLoad<Tr, kQ> L;
+  d.load(g * kGroup + wid * kWStep + lane * kPer, resid, L.pr, L.qr);
+  return L;
+}
+
 // Group g weighed id by id by the whole workgroup, ties ranked: wave w takes
-// the group's step w (512 ids), the waves exchange their tie counts and
-// weights through LDS.  rp, rq are the ties of p and q before the group.
-// Returns the group's weight and tie counts, the last id with weight, whether
-// an unusable published q entry was read where p > 0, and (find) the first id
-// at which base + running weight exceeds tgt.  All threads call it.
+// the group's step w (512 ids, loaded by scan_load), the waves exchange their
+// tie counts and weights through LDS.  rp, rq are the ties of p and q before
+// the group.  Returns the group's weight and tie counts, the last id with
+// weight, whether an unusable published q entry was read where p > 0, and
+// (find) the first id at which base + running weight exceeds tgt.  All
+// threads call it.
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, kQ>& d, bool resid,
-                                                             int g, uint32_t rp, uint32_t rq,
+                                                             int g, const ScanLoad<Tr, kQ>& L,
+                                                             uint32_t rp, uint32_t rq,
                                                              double base, double tgt, bool find,
                                                              DrawSmem& sm) {
   const int lane = __lane_id(), wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int y = g * kGroup + wid * kWStep + lane * kPer;
-  typename DrawCtx<Tr, kQ>::RawP pr;
-  typename DrawCtx<Tr, kQ>::RawQ qr;
-  d.load(y, resid, pr, qr);
+  const typename DrawCtx<Tr, kQ>::RawP& pr = L.pr;
+  const typename DrawCtx<Tr, kQ>::RawQ& qr = L.qr;
   uint32_t fp = 0, fq = 0;  // which of the 8 ids are ties of p, of q
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -1164,19 +1233,34 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
     if (w < wid) before += v;
     total += v;
   }
-  ScanRes res{total, INT32_MAX, -1, np, nq, false};
+  int32_t mine = INT32_MAX;
   if (find) {
     double acc = base + before + excl;
-    int32_t mine = INT32_MAX;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       acc += w8[e];
       if (mine == INT32_MAX && acc > tgt) mine = y + e;
     }
-    res.first = block_reduce<kDrawNT>(mine, OpMin(), sm.ired);
   }
-  res.lastpos = block_reduce<kDrawNT>(lastpos, OpMax(), sm.ired);
-  res.bad = block_reduce<kDrawNT>(bad ? 1 : 0, OpMax(), sm.ired) != 0;
+  // the first crossing, the last id with weight and the unusable entries over
+  // the workgroup, in one exchange (the previous scan's reads of sm.red3 are
+  // behind the barriers of this scan's exchanges above)
+  mine = wave_reduce(mine, OpMin());
+  lastpos = wave_reduce(lastpos, OpMax());
+  const int32_t anybad = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1 : 0;
+  if (lane == 0) {
+    sm.red3[wid][0] = mine;
+    sm.red3[wid][1] = lastpos;
+    sm.red3[wid][2] = anybad;
+  }
+  __syncthreads();
+  ScanRes res{total, INT32_MAX, -1, np, nq, false};
+#pragma unroll
+  for (int w = 0; w < kDrawWaves; ++w) {
+    res.first = min(res.first, sm.red3[w][0]);
+    res.lastpos = max(res.lastpos, sm.red3[w][1]);
+    res.bad |= sm.red3[w][2] != 0;
+  }
   return res;
 }
 
@@ -1368,13 +1452,26 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     }
   }
   __syncthreads();
-  for (int k = 0; k < 2; ++k) {
-    const int g = sm.sg[k];
-    if (g >= 0 && !(k == 1 && g == sm.sg[0])) {
-      const ScanRes sr = group_scan<Tr, kQ>(d, true, g, sm.stp[k], sm.stq[k], 0.0, 0.0, false, sm);
+  {  // the groups holding p's and q's cut, both loaded before either is weighed
+    const int ga = sm.sg[0], gq = sm.sg[1];
+    const bool has_a = ga >= 0, has_q = gq >= 0 && gq != ga;
+    ScanLoad<Tr, kQ> La{}, Lq{};
+    if (has_a) La = scan_load<Tr, kQ>(d, true, ga);
+    if (has_q) Lq = scan_load<Tr, kQ>(d, true, gq);
+    if (has_a) {
+      const ScanRes sr =
+          group_scan<Tr, kQ>(d, true, ga, La, sm.stp[0], sm.stq[0], 0.0, 0.0, false, sm);
       if (t == 0) {
-        sm.smass[k] = sr.total;
-        sm.sbad[k] = sr.bad ? 1 : 0;
+        sm.smass[0] = sr.total;
+        sm.sbad[0] = sr.bad ? 1 : 0;
+      }
+    }
+    if (has_q) {
+      const ScanRes sr =
+          group_scan<Tr, kQ>(d, true, gq, Lq, sm.stp[1], sm.stq[1], 0.0, 0.0, false, sm);
+      if (t == 0) {
+        sm.smass[1] = sr.total;
+        sm.sbad[1] = sr.bad ? 1 : 0;
       }
     }
   }
@@ -1476,7 +1573,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     double run = sm.gbase;
     uint32_t tp = sm.gtp, tq = sm.gtq;
     for (int g = gstar; g < G && pick == INT32_MAX; ++g) {
-      const ScanRes sr = group_scan<Tr, kQ>(d, rs, g, tp, tq, run, tgt, true, sm);
+      const ScanRes sr =
+          group_scan<Tr, kQ>(d, rs, g, scan_load<Tr, kQ>(d, rs, g), tp, tq, run, tgt, true, sm);
       pick = sr.first;
       run += sr.total;
       tp += sr.np;
@@ -1486,7 +1584,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
   if (pick == INT32_MAX) {
     pick = -1;
     if (lg >= 0)
-      pick = group_scan<Tr, kQ>(d, rs, lg, sm.ltp, sm.ltq, 0.0, 0.0, false, sm).lastpos;
+      pick = group_scan<Tr, kQ>(d, rs, lg, scan_load<Tr, kQ>(d, rs, lg), sm.ltp, sm.ltq, 0.0, 0.0,
+                                false, sm).lastpos;
   }
   if (wid == 0) write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
 }
