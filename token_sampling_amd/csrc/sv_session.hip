@@ -10,6 +10,7 @@
 //   per undecided session finds the position that ends its round, if the
 //   rows read so far hold it.
 #include "sv_kernels.hpp"
+#include "sv_stream.hpp"
 
 namespace sv {
 
@@ -987,6 +988,10 @@ __device__ __attribute__((always_inline)) void record_loop(const DrawCtx<Tr, kQ>
   }
   for (int k = 0; k < nk; k += kSteps) {
     GroupAcc s{};
+    // the waves of a SIMD share it by the share of their groups left (see
+    // stream::set_priority): without it the oldest waves finish first and the
+    // session whose waves came last on their SIMDs ends the kernel
+    stream::set_priority(nk - k, nk);
 #pragma unroll
     for (int u = 0; u < kSteps; ++u) {
       const int kk = k + u;
@@ -1394,7 +1399,10 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     if (!sm.last) return;
   }
 
-  // ---- the session's last workgroup: thread t adds up groups [ga, gb)
+  // ---- the session's last workgroup: the pick is the end of the session's
+  // critical path, so it takes the SIMD ahead of waves still recording
+  __builtin_amdgcn_s_setprio(3);
+  // thread t adds up groups [ga, gb)
   const int ga = (int)((long long)t * G / kDrawNT), gb = (int)((long long)(t + 1) * G / kDrawNT);
   // the records, staged in LDS when they fit (else read where they are)
   const bool staged = G <= kLdsGroups;
