@@ -128,13 +128,106 @@ __device__ inline void verifier_uniforms(uint64_t seed, uint64_t session_key, ui
   *u_add = (double)(c[1] >> 11) * 0x1p-53;
 }
 
+// ------------------------------------------------------- lane exchanges
+// The value of lane (this lane xor S), without the LDS crossbar that a
+// general shuffle (ds_bpermute) goes through: DPP within rows of 16 lanes
+// (quad permutes for 1 and 2; a rotate by 8 for 8; for 4, the rotates by 4
+// and by 12, one of which brings the partner), the permlane swaps between
+// rows for 16 and 32.  Each takes a few cycles where a shuffle waits on the
+// LDS.
+template <int kCtrl>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+}
+template <int S>
+__device__ inline uint32_t lane_xor_u32(uint32_t x) {
+  static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16 || S == 32, "xor distance");
+  const int lane = __lane_id();
+  if constexpr (S == 1) {
+    return dpp_u32<0xB1>(x);  // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return dpp_u32<0x4E>(x);  // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const uint32_t up = dpp_u32<0x120 + 12>(x), dn = dpp_u32<0x120 + 4>(x);  // row_ror
+    return (lane & 4) ? dn : up;
+  } else if constexpr (S == 8) {
+    return dpp_u32<0x120 + 8>(x);  // row_ror:8
+  } else if constexpr (S == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+template <int S, typename T>
+__device__ inline T lane_xor(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, lane_xor_u32<S>(__builtin_bit_cast(uint32_t, v)));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = lane_xor_u32<S>((uint32_t)u), hi = lane_xor_u32<S>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, lo | (hi << 32));
+  }
+}
+// The value of lane l of a 32- or 64-bit value, l the same in every lane.
+template <typename T>
+__device__ inline T lane_read(T v, int l) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  l = __builtin_amdgcn_readfirstlane(l);
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(T, lo | (hi << 32));
+  }
+}
+
 // ---------------------------------------------------------------- reductions
 // Deterministic block-wide reductions: a fixed xor-butterfly inside each
-// wave64, then the wave totals combined in wave order by every thread.
+// wave64 (distances 32, 16, ..., 1), then the wave totals combined in wave
+// order by every thread.
 template <typename T, typename Op>
 __device__ inline T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = op(v, __shfl_xor(v, off, kWave));
+  v = op(v, lane_xor<32>(v));
+  v = op(v, lane_xor<16>(v));
+  v = op(v, lane_xor<8>(v));
+  v = op(v, lane_xor<4>(v));
+  v = op(v, lane_xor<2>(v));
+  v = op(v, lane_xor<1>(v));
+  return v;
+}
+
+// Inclusive prefix sum over the wave's lanes, in lane order: within rows of
+// 16 lanes (DPP shifts by 1, 2, 4, 8), then each row's total added to the
+// rows after it (DPP row broadcasts of lanes 15 and 31).  Lanes past a row's
+// start read 0 from the shifts.
+template <int kCtrl, int kRowMask, typename T>
+__device__ inline T dpp_move(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(
+        T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask, 0xF, false));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo =
+        (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, kRowMask, 0xF, false);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl,
+                                                              kRowMask, 0xF, false);
+    return __builtin_bit_cast(T, lo | (hi << 32));
+  }
+}
+template <typename T>
+__device__ inline T wave_incl_scan(T v) {
+  v += dpp_move<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_move<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_move<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_move<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_move<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

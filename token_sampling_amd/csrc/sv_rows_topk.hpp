@@ -124,10 +124,8 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
         hi = max(hi, h);
       }
     }
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      lo = min(lo, (uint32_t)__shfl_xor((int)lo, off, kWave));
-      hi = max(hi, (uint32_t)__shfl_xor((int)hi, off, kWave));
-    }
+    lo = wave_reduce(lo, OpMin());
+    hi = wave_reduce(hi, OpMax());
     const uint32_t diff = __builtin_amdgcn_readfirstlane(lo ^ hi);
     const int top = diff ? 31 - __builtin_clz(diff) : -1;
     t = (uint32_t)(((uint64_t)__builtin_amdgcn_readfirstlane(hi) >> (top + 1)) << (top + 1));
@@ -163,7 +161,7 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
 #pragma unroll
     for (int i = 0; i < kCap / kWave; ++i)
       if (e[i]) mn = min(mn, K::unbias((uint32_t)(e[i] >> 32)));
-    for (int off = kWave / 2; off > 0; off >>= 1) mn = min(mn, __shfl_xor(mn, off, kWave));
+    mn = wave_reduce(mn, OpMin());
     kth = mn;
   }
   int base = 0;
@@ -290,12 +288,12 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
   if (!lanes) return;
   if (s.n + popc64(lanes) * (kVec * 8) > kCap) {
     int c = lm >= te ? slots_ge(v, te) : 0;
-    for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    c = wave_reduce(c, OpAdd());
     if (s.n + c > kCap && s.n >= k) {
       Cut ct = region_cut<Key16, !SV_TOPK_LOOSE_CUT>(reg, s.n, k);
       te = max(ct.kth + 1, kMinKey);
       c = lm >= te ? slots_ge(v, te) : 0;
-      for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+      c = wave_reduce(c, OpAdd());
       // ties at the k-th key left too little room: cut to exactly k
       if (((ct.n + 1) & ~1) + c > kCap) ct = region_cut<Key16, true>(reg, ct.n, k);
       s.n = __builtin_amdgcn_readfirstlane((ct.n + 1) & ~1);
@@ -327,56 +325,73 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
   }
 }
 
+// One compare-exchange stage of a bitonic sort over the wave's lanes (block
+// size `size`, distance S): the partner's value by a lane exchange; desc
+// sorts each block's first half largest first.
+template <int S>
+__device__ inline uint64_t bitonic_stage_desc(uint64_t x, int size) {
+  const int lane = __lane_id();
+  const uint64_t y = lane_xor<S>(x);
+  const bool up = (lane & size) == 0;   // this block sorts descending
+  const bool lower = (lane & S) == 0;   // I hold the first slot
+  return (lower == up) ? (x > y ? x : y) : (x < y ? x : y);
+}
+template <int S>
+__device__ inline void bitonic_stage_asc(uint32_t& key, double& val, int size) {
+  const int lane = __lane_id();
+  const uint32_t ok = lane_xor<S>(key);
+  const double ov = lane_xor<S>(val);
+  const bool up = (lane & size) == 0;  // this block sorts ascending
+  const bool lower = (lane & S) == 0;
+  const bool swap = (lower == up) ? (ok < key) : (ok > key);
+  if (swap) {
+    key = ok;
+    val = ov;
+  }
+}
+template <int S>
+__device__ inline uint64_t bitonic_merge_desc(uint64_t x, int size) {
+  x = bitonic_stage_desc<S>(x, size);
+  if constexpr (S > 1) x = bitonic_merge_desc<S / 2>(x, size);
+  return x;
+}
+template <int S>
+__device__ inline void bitonic_merge_asc(uint32_t& key, double& val, int size) {
+  bitonic_stage_asc<S>(key, val, size);
+  if constexpr (S > 1) bitonic_merge_asc<S / 2>(key, val, size);
+}
+
 // bitonic sort of one u64 per lane, largest first
 __device__ inline uint64_t wave_sort_desc(uint64_t x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t y = __shfl_xor(x, stride, kWave);
-      const bool up = (lane & size) == 0;       // this block sorts descending
-      const bool lower = (lane & stride) == 0;  // I hold the first slot
-      x = (lower == up) ? (x > y ? x : y) : (x < y ? x : y);
-    }
-  }
+  x = bitonic_merge_desc<1>(x, 2);
+  x = bitonic_merge_desc<2>(x, 4);
+  x = bitonic_merge_desc<4>(x, 8);
+  x = bitonic_merge_desc<8>(x, 16);
+  x = bitonic_merge_desc<16>(x, 32);
+  x = bitonic_merge_desc<32>(x, 64);
   return x;
 }
 
 // bitonic sort by ascending 32-bit key, carrying a binary64 payload
 __device__ inline void wave_sort_asc(uint32_t& key, double& val) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t ok = __shfl_xor(key, stride, kWave);
-      const double ov = __shfl_xor(val, stride, kWave);
-      const bool up = (lane & size) == 0;       // this block sorts ascending
-      const bool lower = (lane & stride) == 0;
-      const bool take_small = (lower == up);
-      const bool swap = take_small ? (ok < key) : (ok > key);
-      if (swap) {
-        key = ok;
-        val = ov;
-      }
-    }
-  }
+  bitonic_merge_asc<1>(key, val, 2);
+  bitonic_merge_asc<2>(key, val, 4);
+  bitonic_merge_asc<4>(key, val, 8);
+  bitonic_merge_asc<8>(key, val, 16);
+  bitonic_merge_asc<16>(key, val, 32);
+  bitonic_merge_asc<32>(key, val, 64);
 }
 
-__device__ inline double wave_incl_scan_f64(double v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
-  return v;
-}
+__device__ inline double wave_incl_scan_f64(double v) { return wave_incl_scan(v); }
 
 // Wave maxima of packed 16-bit pairs, as one value.
 __device__ inline int wave_pair_max(uint32_t pair) {
-  for (int off = kWave / 2; off > 0; off >>= 1) pair = max_u16x2(pair, __shfl_xor(pair, off, kWave));
+  pair = max_u16x2(pair, lane_xor<32>(pair));
+  pair = max_u16x2(pair, lane_xor<16>(pair));
+  pair = max_u16x2(pair, lane_xor<8>(pair));
+  pair = max_u16x2(pair, lane_xor<4>(pair));
+  pair = max_u16x2(pair, lane_xor<2>(pair));
+  pair = max_u16x2(pair, lane_xor<1>(pair));
   return max((int)(pair & 0xFFFFu), (int)(pair >> 16));
 }
 
@@ -404,7 +419,7 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, bool ba
   uint64_t e = lane < n ? reg[lane] : 0ull;
   e = wave_sort_desc(e);
 
-  const uint64_t top = __shfl(e, 0, kWave);
+  const uint64_t top = lane_read(e, 0);
   const int kmax = ckey<K>(top);
   // NaN anywhere, +inf at the top, or no finite logit at all
   const bool bad = bad_seen || n == 0 || kmax >= kInfKey;
@@ -431,15 +446,15 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, bool ba
   const int kept = popc64(__ballot(live));
   const double w = live ? exp2(((double)ckey_value<K>(ckey<K>(e)) - (double)r.lmax) * scale) : 0.0;
   const double C = wave_incl_scan_f64(w);
-  const double Zk = __shfl(C, kept - 1, kWave);
+  const double Zk = lane_read(C, kept - 1);
   int cut = kept;
   if (!one_hot && p_milli < 1000) {  // shortest prefix with 1000 * C >= P * Z_k
     const double tgt = (double)p_milli * Zk;
     const uint64_t hit = __ballot(live && 1000.0 * C >= tgt);
     cut = hit ? __builtin_ctzll(hit) + 1 : kept;
   }
-  const double zsum = __shfl(C, cut - 1, kWave);
-  const uint64_t last = __shfl(e, cut - 1, kWave);
+  const double zsum = lane_read(C, cut - 1);
+  const uint64_t last = lane_read(e, cut - 1);
   r.kcut = K::bias(ckey<K>(last));
   r.idcut = (int32_t)comp_id(last);
   r.scale = scale;
@@ -448,7 +463,7 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, bool ba
   if (x >= 0) {
     const uint64_t hitx = __ballot(lane < cut && comp_id(e) == (uint32_t)x);
     const int jx = hitx ? __builtin_ctzll(hitx) : 0;
-    const double wx = __shfl(w, jx, kWave);
+    const double wx = lane_read(w, jx);
     r.ptok = hitx ? wx / zsum : 0.0;
   }
   // the support in ascending id order, with p(y) = w(y) / Z'
