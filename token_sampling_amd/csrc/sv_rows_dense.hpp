@@ -200,8 +200,7 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
   L.mv = max_nan(L.mv, lmv);
   if (__ballot(lmv > H.anchor_v)) {  // the window moves up (wave-uniform)
     int tk = skey_of(lmv);
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) tk = max(tk, __shfl_xor(tk, off, kWave));
+    tk = wave_reduce(tk, OpMax());
     const int lane = __lane_id();
     const int d = tk - H.anchor;  // keys anchor+1 .. tk take the bins of the keys leaving
     const float nref = uni(value_of(tk));
@@ -250,8 +249,7 @@ __device__ __attribute__((always_inline)) inline void dense_vec(LaneSum& L, Hist
     int before = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) before += (p0 + e < px && skey_of(f[e]) == H.kx) ? 1 : 0;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) before += __shfl_xor(before, off, kWave);
+    before = wave_reduce(before, OpAdd());
     H.rank_x = (H.kx >= lo ? (int)H.bin[H.kx & (kWin - 1)] : 0) + before;
   }
   // tokens in the window are counted; the binary32 sum takes only the others.
@@ -353,18 +351,19 @@ __device__ inline WaveZ wave_z(const LaneSum& L, const Hist& H, float lmax, cons
   double c = kHist ? 0.0 : (none ? L.l1 : (L.l1 - (double)lmax * L.s) * f);
   double dep = (kHist && L.dep != 0.0f)
                    ? (double)L.dep * exp2(((double)H.dref - (double)lmax) * sc.s) : 0.0;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    z += __shfl_xor(z, off, kWave);
-    c += __shfl_xor(c, off, kWave);
-    dep += __shfl_xor(dep, off, kWave);
-  }
+  z = wave_reduce(z, OpAdd());
+  c = wave_reduce(c, OpAdd());
+  dep = wave_reduce(dep, OpAdd());
   return WaveZ{z, c, dep};
 }
 
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  v = fmaxf(v, lane_xor<32>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<2>(v));
+  v = fmaxf(v, lane_xor<1>(v));
   return v;
 }
 
@@ -493,8 +492,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile_split_t(
       }
       bins_all[i] = c;
     }
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) below += __shfl_xor(below, off, kWave);
+    below = wave_reduce(below, OpAdd());
     z.dep += below;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -572,8 +570,7 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
     cnt[e] = k > kNegInfKey ? bins[k & (kWin - 1)] : 0u;
     if (cnt[e]) win += (double)cnt[e] * weight64(value_of(k), lmax, sc.s);
   }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) win += __shfl_xor(win, off, kWave);
+  win = wave_reduce(win, OpAdd());
   // Z at s: the window's and the departed bins' exact masses, and the binary32
   // sum of the tokens below the window when they were read
   const double z = win + zc.dep + zc.z;
@@ -586,23 +583,18 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
     uint32_t tot = 0;
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) tot += cnt[e];
-    uint32_t cincl = tot;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const uint32_t t = __shfl_up(cincl, off, kWave);
-      if (lane >= off) cincl += t;
-    }
+    const uint32_t cincl = wave_incl_scan(tot);
     const uint64_t hitk = __ballot(cincl >= K);
     if (!hitk) {  // fewer than K tokens in the window
       return true;
     }
     const int qk = __builtin_ctzll(hitk);
-    uint32_t above = __shfl(cincl - tot, qk, kWave);  // tokens in the lanes before qk
+    uint32_t above = lane_read(cincl - tot, qk);  // tokens in the lanes before qk
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) {
       // every lane walks lane qk's counts (wave-uniform): the cut is the last
       // key that keeps a token
-      const uint32_t c = __shfl(cnt[e], qk, kWave);
+      const uint32_t c = lane_read(cnt[e], qk);
       const uint32_t keep = above >= K ? 0u : (K - above < c ? K - above : c);
       if (keep) {
         kc = H.anchor - kPerLane * qk - e;
@@ -622,14 +614,9 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
 #pragma unroll
   for (int e = 0; e < kPerLane; ++e)
     if (cnt[e]) part += (double)cnt[e] * weight64(value_of(H.anchor - kPerLane * lane - e), lmax, sc.s);
-  double incl = part;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
+  const double incl = wave_incl_scan(part);
   // Z_k: the mass of the top-k set (the last lane's prefix), else the row's Z
-  double zsum = top_k ? __shfl(incl, kWave - 1, kWave) : z;
+  double zsum = top_k ? lane_read(incl, kWave - 1) : z;
 
   if (top_p) {  // over the top-k distribution: stop at 1000 * C >= P * Z_k
     const double tgt = (double)smp.top_p_milli * zsum;
@@ -663,10 +650,10 @@ __device__ __attribute__((always_inline)) inline bool finish(const sv_sampling& 
         c += (double)cnt[e] * w;
       }
     }
-    kc = __shfl(kc, q, kWave);
-    j = __shfl(j, q, kWave);
-    c_above = __shfl(c_above, q, kWave);
-    wc = __shfl(wc, q, kWave);
+    kc = lane_read(kc, q);
+    j = lane_read(j, q);
+    c_above = lane_read(c_above, q);
+    wc = lane_read(wc, q);
     zsum = c_above + (double)j * wc;
   }
   rr.kcut = (uint32_t)(kc + 0x8000);

@@ -245,11 +245,10 @@ __attribute__((amdgpu_waves_per_eu(SV_SPLIT_WAVES_PER_EU))) void k_rows_split(
       topk::WaveState s;
       topk::chunk_scan(row, V, k, wid * T / TS, (wid + 1) * T / TS, s, reg);
       const int n = s.overflow ? 0 : topk::region_cut(reg, s.n, k).n;
-      uint32_t mm = s.magmax, um = s.umax;
-      for (int off = kWave / 2; off > 0; off >>= 1) {
-        mm = stream::max_u16x2(mm, __shfl_xor(mm, off, kWave));
-        um = stream::max_u16x2(um, __shfl_xor(um, off, kWave));
-      }
+      struct PairMax {
+        __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return stream::max_u16x2(a, b); }
+      };
+      const uint32_t mm = wave_reduce(s.magmax, PairMax()), um = wave_reduce(s.umax, PairMax());
       if (lane == 0) {
         cnt_s[wid] = n;
         ovf_s[wid] = s.overflow ? 1 : 0;

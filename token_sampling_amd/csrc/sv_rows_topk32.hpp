@@ -124,12 +124,12 @@ __device__ inline void tile_process(WaveState& s, uint64_t* reg, int k, u32x4 (&
   if (!lanes) return;
   if (s.n + popc64(lanes) * (kVec * 4) > kCap) {
     int c = lm >= te ? slots_ge(v, te) : 0;
-    for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    c = wave_reduce(c, OpAdd());
     if (s.n + c > kCap && s.n >= k) {
       topk::Cut ct = topk::region_cut<Key32, false>(reg, s.n, k);
       te = max(ct.kth + 1, kMinKey);
       c = lm >= te ? slots_ge(v, te) : 0;
-      for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+      c = wave_reduce(c, OpAdd());
       // ties at the k-th key left too little room: cut to exactly k
       if (ct.n + c > kCap) ct = topk::region_cut<Key32, true>(reg, ct.n, k);
       s.n = __builtin_amdgcn_readfirstlane(ct.n);
@@ -205,11 +205,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile(
     }
   }
   if (s.overflow) return true;
-  uint32_t mm = s.magmax, um = s.umax;
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    mm = max(mm, (uint32_t)__shfl_xor((int)mm, off, kWave));
-    um = max(um, (uint32_t)__shfl_xor((int)um, off, kWave));
-  }
+  const uint32_t mm = wave_reduce(s.magmax, OpMax()), um = wave_reduce(s.umax, OpMax());
   const bool nan = mm > 0x7F800000u || um > 0xFF800000u;
   topk::row_finish<Key32>(reg, s.n, k, nan, 0x7F800000, one_hot, smp.temperature_milli,
                           smp.top_p_milli, x, rec, sup_id, sup_p);

@@ -57,21 +57,16 @@ __device__ int32_t listed_draw(const int32_t* p_id, const double* p_pr, int np,
     }
     const double d = p - q;
     w = (p > 0.0 && d > 0.0) ? d : 0.0;
-    double S = w;
-    for (int off = kWave / 2; off > 0; off >>= 1) S += __shfl_xor(S, off, kWave);
+    const double S = wave_reduce(w, OpAdd());
     if (S == 0.0) w = p;  // rounding only
   }
-  double C = w;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(C, off, kWave);
-    if (lane >= off) C += t;
-  }
-  const double S = __shfl(C, kWave - 1, kWave);
+  const double C = wave_incl_scan(w);
+  const double S = lane_read(C, kWave - 1);
   const double tgt = u * S;
   const uint64_t hit = __ballot(lane < np && C > tgt);
   const uint64_t pos = __ballot(lane < np && w > 0.0);
   const int j = hit ? __builtin_ctzll(hit) : (pos ? 63 - __builtin_clzll(pos) : 0);
-  return __shfl(y, j, kWave);
+  return lane_read(y, j);
 }
 
 // A failed session's outputs, by one wave: status, no tokens, no probes.  The
@@ -1107,12 +1102,7 @@ struct DrawSmem {
 template <int NT, typename T>
 __device__ __attribute__((always_inline)) T block_exclusive_scan(T v, T* wsum, T* total) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  T inc = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const T t = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += t;
-  }
+  const T inc = wave_incl_scan(v);
   const T exc = inc - v;  // not a one-lane shift: see group_scan
   __syncthreads();
   if (lane == kWave - 1) wsum[wid] = inc;
@@ -1221,14 +1211,9 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
   }
   // running weight over the lanes in id order; the exclusive prefix as
   // incl - ls (see block_exclusive_scan)
-  double incl = ls;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
+  const double incl = wave_incl_scan(ls);
   const double excl = incl - ls;
-  const double wtot = __shfl(incl, kWave - 1, kWave);
+  const double wtot = lane_read(incl, kWave - 1);
   if (lane == 0) sm.wsum[wid] = wtot;
   __syncthreads();
   double before = 0.0, total = 0.0;
