@@ -136,8 +136,8 @@ __device__ inline void verifier_uniforms(uint64_t seed, uint64_t session_key, ui
 // rows for 16 and 32.  Each takes a few cycles where a shuffle waits on the
 // LDS.
 template <int kCtrl>
-__device__ inline uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+__device__ inline uint32_t dpp_u32(uint32_t x) {  // every source lane lies in the row
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
 }
 template <int S>
 __device__ inline uint32_t lane_xor_u32(uint32_t x) {

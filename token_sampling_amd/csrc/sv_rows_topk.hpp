@@ -144,8 +144,23 @@ __device__ __attribute__((always_inline)) Cut region_cut(uint64_t* reg, int n, i
     }
     const int need = k - gt;  // ties kept at key t, smallest ids first
     if (kExact && eq > need) {
-      uint32_t u = 0;
-      for (int bit = 31; bit >= 0; --bit) {
+      // the need-th largest low word among the ties lies between their
+      // smallest and largest: search only the bits below their common ones
+      uint32_t wlo = 0xFFFFFFFFu, whi = 0u;
+#pragma unroll
+      for (int i = 0; i < kCap / kWave; ++i) {
+        if ((uint32_t)(e[i] >> 32) == t) {
+          wlo = min(wlo, (uint32_t)e[i]);
+          whi = max(whi, (uint32_t)e[i]);
+        }
+      }
+      wlo = wave_reduce(wlo, OpMin());
+      whi = wave_reduce(whi, OpMax());
+      const uint32_t wdiff = __builtin_amdgcn_readfirstlane(wlo ^ whi);
+      const int wtop = wdiff ? 31 - __builtin_clz(wdiff) : -1;
+      uint32_t u =
+          (uint32_t)(((uint64_t)__builtin_amdgcn_readfirstlane(whi) >> (wtop + 1)) << (wtop + 1));
+      for (int bit = wtop; bit >= 0; --bit) {
         const uint32_t cand = u | (1u << bit);
         int cnt = 0;
 #pragma unroll
@@ -343,11 +358,11 @@ __device__ inline void bitonic_stage_asc(uint32_t& key, double& val, int size) {
   const double ov = lane_xor<S>(val);
   const bool up = (lane & size) == 0;  // this block sorts ascending
   const bool lower = (lane & S) == 0;
-  const bool swap = (lower == up) ? (ok < key) : (ok > key);
-  if (swap) {
-    key = ok;
-    val = ov;
-  }
+  // selects, not branches: the partner's pair replaces this lane's when it
+  // belongs here (the smaller key in the block's first slot when ascending)
+  const bool swap = (ok != key) & ((ok < key) == (lower == up));
+  key = swap ? ok : key;
+  val = swap ? ov : val;
 }
 template <int S>
 __device__ inline uint64_t bitonic_merge_desc(uint64_t x, int size) {
