@@ -156,6 +156,105 @@ __device__ __attribute__((always_inline)) int inorder_end(int n, int mb, int rl,
   return e ? __builtin_ctzll(e) + 1 : 0;
 }
 
+// What lane j reads of position j+1's rows, loaded at once before the
+// session's checks: every address is in bounds for any m (target rows 0..M,
+// draft rows and drafted tokens 0..M-1), so no load waits for m, the rule or
+// the status.  Lane j holds the target row record's status, argmax, listed
+// support size and p of the drafted token; below M the draft row record's
+// status, support size and q of the drafted token, and the drafted token;
+// and the verifier values of position j+1 (both words of one Philox call, or
+// the SDCP table's entries).  Position M+1 = 65 (M = 64) has no lane: the
+// callers read its row record where they need it.
+struct LaneRows {
+  int32_t ts, targ, tn;  // target row: status, argmax, nsup
+  double tp;             // target row: ptok
+  int32_t ds, dn;        // draft row: status, nsup
+  double dp;             // draft row: ptok
+  int32_t x;             // drafted token
+  double ua, ud;         // acceptance and additional-token values
+};
+__device__ __attribute__((always_inline)) LaneRows lane_rows(
+    int b, int lane, int M, const int32_t* __restrict__ tokens, const RowRec* __restrict__ rr,
+    const double* __restrict__ unif, uint64_t seed, uint64_t session_key, uint32_t round) {
+  LaneRows r{0, -1, 0, -1.0, 0, 0, 1.0, -1, 1.0, 1.0};
+  if (lane <= M) {
+    const RowRec& t = rr[lane];
+    r.ts = t.status;
+    r.targ = t.argmax;
+    r.tn = t.nsup;
+    r.tp = t.ptok;
+  }
+  if (lane < M) {
+    const RowRec& d = rr[M + 1 + lane];
+    r.ds = d.status;
+    r.dn = d.nsup;
+    r.dp = d.ptok;
+    r.x = tokens[(size_t)b * M + lane];
+  }
+  if (unif) {
+    const int R = 2 * M + 1;
+    if (lane < M) r.ua = unif[(size_t)b * R + lane];
+    if (lane <= M) r.ud = unif[(size_t)b * R + M + lane];
+  } else {
+    verifier_uniforms(seed, session_key, round, (uint32_t)(lane + 1), &r.ua, &r.ud);
+  }
+  return r;
+}
+
+// lane_position from a lane's loaded rows (see lane_position).
+__device__ __attribute__((always_inline)) LanePos lane_position_lr(
+    const LaneRows& Lr, int b, int lane, int mb, int lim, int rl, int M, int V,
+    const float* __restrict__ qrows) {
+  LanePos P{-1, -1.0, 1.0, 1.0};
+  if (lane >= mb || lane >= lim) return P;
+  P.x = Lr.x;  // in [0, V) once the session's checks passed
+  if (rl == SV_RULE_SPECULATIVE || rl == SV_RULE_RELAXED) P.px = Lr.tp;
+  if (rl == SV_RULE_SPECULATIVE) {
+    P.qx = qrows ? (double)qrows[((size_t)b * M + lane) * (size_t)V + P.x] : Lr.dp;
+    P.u = Lr.ua;
+  }
+  return P;
+}
+
+// inorder_end from a lane's loaded rows (see inorder_end).
+__device__ __attribute__((always_inline)) int inorder_end_lr(int n, int mb, int rl,
+                                                             bool draft_rows, const LaneRows& Lr,
+                                                             const RowRec* __restrict__ rr,
+                                                             const LanePos& P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  bool end = false;
+  if (lane < n) {
+    end = Lr.ts != 0;
+    if (lane < mb) {
+      if (rl == SV_RULE_GREEDY) {
+        end |= P.x != Lr.targ;
+      } else if (rl == SV_RULE_RELAXED) {
+        end |= !(P.px > 0.0);
+      } else {
+        if (draft_rows) end |= Lr.ds != 0;
+        const double ratio = P.px / P.qx;
+        end |= !(P.qx > 0.0 && P.qx < INFINITY) || !(P.u < (ratio < 1.0 ? ratio : 1.0));
+      }
+    }
+  }
+  const uint64_t e = __ballot(end);
+  // position 65 (m = 64, lane 64 does not exist): its row alone
+  if (e == 0 && n > kWave && rr[kWave].status != 0) return kWave + 1;
+  return e ? __builtin_ctzll(e) + 1 : 0;
+}
+
+// The additional token's value (purpose 1) for position a+1: lane a's, or
+// for a = 64 (position 65, no lane) the table's entry or a Philox call.
+__device__ __attribute__((always_inline)) double additional_value(
+    const LaneRows& Lr, int a, int b, int M, const double* __restrict__ unif, uint64_t seed,
+    const sv_sampling* __restrict__ sampling, uint32_t round) {
+  if (a < kWave) return lane_read(Lr.ud, a);
+  if (unif) return unif[(size_t)b * (2 * M + 1) + M + a];
+  double ua, ud;
+  verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+  return ud;
+}
+
 // SDCP Sec. 6.4, for session b, by one wave: lane i examines position i+1.
 // With published q rows (qrows != null) q_i(x_i) is read from them and no
 // draft row record exists.  Writes nothing.  A draw from listed supports is
@@ -178,6 +277,7 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   v.a = 0;
   v.extra = -1;
   const RowRec* rr = rows + (size_t)b * R;
+  const LaneRows Lr = lane_rows(b, lane, M, tokens, rr, unif, seed, sampling[b].session_key, round);
   int st = sess_status[b];
   const int mb = m[b];
   const int rl = rule[b];
@@ -189,12 +289,10 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   const int e = (st == 0 && decided) ? decided[b] : 0;
   const int n = e > 0 ? e : mb + 1;
   LanePos pos{-1, -1.0, 1.0, 1.0};
-  if (st == 0)
-    pos = lane_position(b, lane, mb, n, rl, tokens, M, V, qrows, rr, unif, seed,
-                        sampling[b].session_key, round);
+  if (st == 0) pos = lane_position_lr(Lr, b, lane, mb, n, rl, M, V, qrows);
   int L = mb + 1;
   if (st == 0 && decided) {
-    const int f = inorder_end(n, mb, rl, draft_rows, rr, M, pos);
+    const int f = inorder_end_lr(n, mb, rl, draft_rows, Lr, rr, pos);
     L = f > 0 ? f : n;
   }
   const int np = L < mb ? L : mb;  // positions whose drafted token is examined
@@ -204,9 +302,9 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
 
   // every row the rule reads must be usable (target rows 1..L, draft rows 1..np)
   if (st == 0) {
-    bool bad = false;
-    for (int j = lane; j < L; j += kWave) bad |= rr[j].status != 0;
-    if (draft_rows && lane < np) bad |= rr[M + 1 + lane].status != 0;
+    bool bad = lane < L && Lr.ts != 0;
+    if (L > kWave && lane == 0) bad |= rr[kWave].status != 0;  // row 65 (M = 64)
+    if (draft_rows && lane < np) bad |= Lr.ds != 0;
     if (__any(bad)) st = SV_S_BAD_LOGITS;
   }
   // Sec. 6.3 step 5: q_i(x_i) != 0 at every position examined, before any
@@ -229,11 +327,11 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   int a;
   if (rl == SV_RULE_GREEDY) {
     // Rule 1: accept while x_i == argmax p_i; additional token argmax p_{a+1}
-    const bool acc = lane < np && x == rr[lane].argmax;
+    const bool acc = lane < np && x == Lr.targ;
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
-    v.extra = rr[a].argmax;
+    v.extra = a < kWave ? lane_read(Lr.targ, a) : rr[a].argmax;
   } else if (rl == SV_RULE_RELAXED) {
     // relaxed rule (private use 192): accept x_i while p_i(x_i) > 0; the
     // additional token is drawn from p_{a+1} with the purpose-1 value of
@@ -242,15 +340,13 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
-    double ua, ud;
-    if (unif) ud = unif[(size_t)b * R + M + a];
-    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
-    const RowRec& P = rr[a];
-    if (P.nsup > 0) {
+    const double ud = additional_value(Lr, a, b, M, unif, seed, sampling, round);
+    const int pn = a < kWave ? lane_read(Lr.tn, a) : rr[a].nsup;
+    if (pn > 0) {
       if (listed) {
         bool bad = false;
         v.extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
-                              sup_p + ((size_t)b * R + a) * kSupMax, P.nsup, nullptr, nullptr, 0,
+                              sup_p + ((size_t)b * R + a) * kSupMax, pn, nullptr, nullptr, 0,
                               nullptr, ud, q_id, q_p, &bad);
       }
     } else {
@@ -259,28 +355,26 @@ __device__ __attribute__((always_inline)) Verdict accept_session(
   } else {
     // Rule 2: accept x_i if u_acc(i) < min(1, p_i(x_i) / q_i(x_i)); the values
     // are SDCP's (computed by the row kernel into unif) or Philox's
-    const double* uv = unif ? unif + (size_t)b * R : nullptr;
     const double ratio = px / qx;
     const bool acc = lane < np && pos.u < (ratio < 1.0 ? ratio : 1.0);
     const uint64_t rej = ~(uint64_t)__ballot(acc);
     a = rej == 0 ? kWave : __builtin_ctzll(rej);
     a = a < mb ? a : mb;
-    double ua, ud;
-    if (uv) ud = uv[M + a];
-    else verifier_uniforms(seed, sampling[b].session_key, round, (uint32_t)(a + 1), &ua, &ud);
+    const double ud = additional_value(Lr, a, b, M, unif, seed, sampling, round);
     // additional token: residual at the first rejection, else the bonus row;
     // drawn here when the rows' supports are listed, else by the chunks
-    const RowRec& P = rr[a];
-    const RowRec* Q = (a < mb && !qrows) ? &rr[M + 1 + a] : nullptr;
+    const int pn = a < kWave ? lane_read(Lr.tn, a) : rr[a].nsup;
+    const bool draft = a < mb && !qrows;  // a < mb <= 64: lane a exists
+    const int qn = draft ? lane_read(Lr.dn, a) : 0;
     const float* qrow = (a < mb && qrows) ? qrows + ((size_t)b * M + a) * (size_t)V : nullptr;
-    if (P.nsup > 0 && (Q == nullptr || Q->nsup > 0)) {
+    if (pn > 0 && (!draft || qn > 0)) {
       if (listed) {
         bool bad = false;
         v.extra = listed_draw(sup_id + ((size_t)b * R + a) * kSupMax,
-                              sup_p + ((size_t)b * R + a) * kSupMax, P.nsup,
-                              Q ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
-                              Q ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
-                              Q ? Q->nsup : 0, qrow, ud, q_id, q_p, &bad);
+                              sup_p + ((size_t)b * R + a) * kSupMax, pn,
+                              draft ? sup_id + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                              draft ? sup_p + ((size_t)b * R + M + 1 + a) * kSupMax : nullptr,
+                              qn, qrow, ud, q_id, q_p, &bad);
         if (bad) v.st = SV_S_BAD_PROPOSAL;  // an unusable entry of the published residual row
       }
     } else {
