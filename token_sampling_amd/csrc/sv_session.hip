@@ -1242,12 +1242,29 @@ __device__ __attribute__((always_inline)) ScanLoad<Tr, kQ> scan_load(const DrawC
 // weight, whether an unusable published q entry was read where p > 0, and
 // (find) the first id at which base + running weight exceeds tgt.  All
 // threads call it.
+// p (r = 0) or q (r = 1) of a token that is not a tie of that row: from the
+// row's key table when the tables are still in LDS (table mode; the same
+// binary64 weights, see weigh8_table), else computed.
+template <class Tr, bool kQ>
+__device__ __attribute__((always_inline)) double scan_weight(const DrawRow<Tr>& D,
+                                                             const KeyTab& kt, bool tabs, int r,
+                                                             uint32_t u, int y) {
+  if constexpr (std::is_same<Tr, Bf16>::value && !kQ) {
+    if (tabs) {
+      const uint32_t cut = kt.cut2[r] & 0xFFFFu, n = kt.n2[r] & 0xFFFFu;
+      return table_at(kt.t[r], min((u - cut) & 0xFFFFu, n) * 8u);
+    }
+  }
+  return D.p_fixed(u, y);
+}
+
 template <class Tr, bool kQ>
 __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, kQ>& d, bool resid,
                                                              int g, const ScanLoad<Tr, kQ>& L,
                                                              uint32_t rp, uint32_t rq,
                                                              double base, double tgt, bool find,
-                                                             DrawSmem& sm) {
+                                                             DrawSmem& sm, const KeyTab& kt,
+                                                             bool tabs) {
   const int lane = __lane_id(), wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int y = g * kGroup + wid * kWStep + lane * kPer;
   const typename DrawCtx<Tr, kQ>::RawP& pr = L.pr;
@@ -1285,7 +1302,7 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
   for (int e = 0; e < kPer; ++e) {
     double pv;
     if ((fp >> e) & 1u) pv = cp++ < d.P.ntie ? d.P.wcut : 0.0;
-    else pv = d.P.p_fixed(pr.get(e), y + e);
+    else pv = scan_weight<Tr, kQ>(d.P, kt, tabs, 0, pr.get(e), y + e);
     double wt = pv;
     if (resid) {
       double qv;
@@ -1294,7 +1311,7 @@ __device__ __attribute__((always_inline)) ScanRes group_scan(const DrawCtx<Tr, k
         bad |= pv > 0.0 && !(qv >= 0.0 && qv < INFINITY);
       } else {
         if ((fq >> e) & 1u) qv = cq++ < d.Q.ntie ? d.Q.wcut : 0.0;
-        else qv = d.Q.p_fixed(qr.get(e), y + e);
+        else qv = scan_weight<Tr, kQ>(d.Q, kt, tabs, 1, qr.get(e), y + e);
       }
       const double df = pv - qv;
       wt = (pv > 0.0 && df > 0.0) ? df : 0.0;
@@ -1484,18 +1501,31 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
   // thread t adds up groups [ga, gb)
   const int ga = (int)((long long)t * G / kDrawNT), gb = (int)((long long)(t + 1) * G / kDrawNT);
   // the records, staged in LDS when they fit (else read where they are)
+  // the records, staged in LDS when they fit (else read where they are): in
+  // table mode after the key tables' entries when there is room, so that the
+  // groups weighed again read their weights from the tables
   const bool staged = G <= kLdsGroups;
+  constexpr int kUnionBytes = (int)sizeof(sm.grec);
+  static_assert(sizeof(sm.ktab) == kUnionBytes, "the key tables fill the staging space");
+  bool tabs_kept = false;
+  if constexpr (std::is_same<Tr, Bf16>::value && !kQ) {
+    const int used = resid ? (int)sizeof(sm.ktab[0]) + 8 * ((int)(kt.n2[1] & 0xFFFFu) + 1)
+                           : 8 * ((int)(kt.n2[0] & 0xFFFFu) + 1);
+    tabs_kept = kt.on && staged && kUnionBytes - 48 * G >= used;
+  }
+  uint64_t* grec = tabs_kept ? (uint64_t*)((char*)&sm.grec[0][0] + kUnionBytes - 48 * G)
+                             : &sm.grec[0][0];
   if (staged) {
     for (int i = t; i < G * 6; i += kDrawNT)
-      sm.grec[i / 6][i % 6] = __hip_atomic_load((const uint64_t*)(recs + i / 6) + i % 6,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      grec[i] = __hip_atomic_load((const uint64_t*)(recs + i / 6) + i % 6, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
   auto rec = [&](int g) -> GroupAcc {
     if (staged) {
       uint64_t w[6];
 #pragma unroll
-      for (int i = 0; i < 6; ++i) w[i] = sm.grec[g][i];
+      for (int i = 0; i < 6; ++i) w[i] = grec[g * 6 + i];
       return decode_group(w);
     }
     return load_group(recs + g);
@@ -1547,7 +1577,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     if (has_q) Lq = scan_load<Tr, kQ>(d, true, gq);
     if (has_a) {
       const ScanRes sr =
-          group_scan<Tr, kQ>(d, true, ga, La, sm.stp[0], sm.stq[0], 0.0, 0.0, false, sm);
+          group_scan<Tr, kQ>(d, true, ga, La, sm.stp[0], sm.stq[0], 0.0, 0.0, false, sm, kt, tabs_kept);
       if (t == 0) {
         sm.smass[0] = sr.total;
         sm.sbad[0] = sr.bad ? 1 : 0;
@@ -1555,7 +1585,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     }
     if (has_q) {
       const ScanRes sr =
-          group_scan<Tr, kQ>(d, true, gq, Lq, sm.stp[1], sm.stq[1], 0.0, 0.0, false, sm);
+          group_scan<Tr, kQ>(d, true, gq, Lq, sm.stp[1], sm.stq[1], 0.0, 0.0, false, sm, kt, tabs_kept);
       if (t == 0) {
         sm.smass[1] = sr.total;
         sm.sbad[1] = sr.bad ? 1 : 0;
@@ -1661,7 +1691,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     uint32_t tp = sm.gtp, tq = sm.gtq;
     for (int g = gstar; g < G && pick == INT32_MAX; ++g) {
       const ScanRes sr =
-          group_scan<Tr, kQ>(d, rs, g, scan_load<Tr, kQ>(d, rs, g), tp, tq, run, tgt, true, sm);
+          group_scan<Tr, kQ>(d, rs, g, scan_load<Tr, kQ>(d, rs, g), tp, tq, run, tgt, true, sm, kt, tabs_kept);
       pick = sr.first;
       run += sr.total;
       tp += sr.np;
@@ -1672,7 +1702,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(typename Tr::elem_t) == 2 ? 4 : 3))) v
     pick = -1;
     if (lg >= 0)
       pick = group_scan<Tr, kQ>(d, rs, lg, scan_load<Tr, kQ>(d, rs, lg), sm.ltp, sm.ltq, 0.0, 0.0,
-                                false, sm).lastpos;
+                                false, sm, kt, tabs_kept).lastpos;
   }
   if (wid == 0) write_verdict(b, v, pick, M, accepted_len, out_tokens, p_tok, q_tok);
 }
