@@ -430,8 +430,13 @@ __device__ __noinline__ void row_finish(uint64_t* reg, int n_reg, int k, bool ba
                                         bool one_hot, uint32_t t_milli, uint32_t p_milli,
                                         int32_t x, RowRec* rec, int32_t* sup_id, double* sup_p) {
   const int lane = __lane_id();
-  const int n = region_cut<K>(reg, n_reg, k).n;
-  uint64_t e = lane < n ? reg[lane] : 0ull;
+  // the k best: a cut that keeps the ties at the k-th key, then the sort
+  // below orders them by id; only when the ties leave more than a wave's
+  // worth of entries the exact cut (a search over the ties' ids) first
+  Cut ct = region_cut<K, false>(reg, n_reg, k);
+  if (ct.n > kWave) ct = region_cut<K, true>(reg, ct.n, k);
+  const int n = ct.n < k ? ct.n : k;  // entries of the k best (all of them when fewer)
+  uint64_t e = lane < ct.n ? reg[lane] : 0ull;
   e = wave_sort_desc(e);
 
   const uint64_t top = lane_read(e, 0);
