@@ -233,7 +233,7 @@ def test_topk_kernel_edge_cases():
     """Rows handled by the single-pass top-k path (greedy, T = 0, top_k <= 64),
     with an odd vocabulary so that rows start at every alignment."""
     parity.log("[case] top-k path edge cases, V=4999")
-    B, M, V = 14, 3, 4999
+    B, M, V = 16, 3, 4999
     rng = np.random.default_rng(61)
     t = rng.normal(0, 2, size=(B, M + 1, V)).astype(np.float32)
     d = (t[:, :M] + rng.normal(0, 0.7, size=(B, M, V))).astype(np.float32)
@@ -259,6 +259,17 @@ def test_topk_kernel_edge_cases():
     s[11]["top_k"] = 64; s[11]["temperature_milli"] = 250
     s[12]["top_k"] = 7; s[12]["top_p_milli"] = 0
     s[13]["top_k"] = 33; s[13]["top_p_milli"] = 990
+    # ties at the k-th key: 10 distinct best values, then 150 (session 14) or
+    # 40 (session 15) tokens of one value, top_k 20: the final cut resolves
+    # them by a search over ids (more than a wave of entries) or by the sort
+    for b_, nt in ((14, 150), (15, 40)):
+        for r in range(M + 1):
+            ids = rng.permutation(V)
+            t[b_, r] = rng.normal(0, 1, size=V) - 6.0
+            t[b_, r, ids[:10]] = 8.0 + np.arange(10) * 0.25
+            t[b_, r, ids[10:10 + nt]] = 5.0
+        d[b_] = t[b_, :M]
+        s[b_]["top_k"] = 20
     tb, db = oracle.bf16_bits(t), oracle.bf16_bits(d)
     tb[2, 1, 1234] = 0xFFC1          # negative NaN inside a raw-mode row
     tb[3, 0, 17] = 0x7FC3            # positive NaN
