@@ -133,8 +133,10 @@ __device__ inline void verifier_uniforms(uint64_t seed, uint64_t session_key, ui
 // general shuffle (ds_bpermute) goes through: DPP within rows of 16 lanes
 // (quad permutes for 1 and 2; a rotate by 8 for 8; for 4, the rotates by 4
 // and by 12, one of which brings the partner), the permlane swaps between
-// rows for 16 and 32.  Each takes a few cycles where a shuffle waits on the
-// LDS.
+// rows for 16 and 32 (called with the value as both operands, the swap
+// leaves the partner's value in the first result in the upper rows and in
+// the second result in the lower rows).  Each takes a few cycles where a
+// shuffle waits on the LDS.  Every lane of the wave must be active.
 template <int kCtrl>
 __device__ inline uint32_t dpp_u32(uint32_t x) {  // every source lane lies in the row
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
@@ -202,9 +204,10 @@ __device__ inline T wave_reduce(T v, Op op) {
 }
 
 // Inclusive prefix sum over the wave's lanes, in lane order: within rows of
-// 16 lanes (DPP shifts by 1, 2, 4, 8), then each row's total added to the
-// rows after it (DPP row broadcasts of lanes 15 and 31).  Lanes past a row's
-// start read 0 from the shifts.
+// 16 lanes (DPP shifts by 1, 2, 4, 8; a lane whose source would lie before
+// its row's first lane adds 0), then the rows' totals carried on (lane 15
+// broadcast into rows 1 and 3, then lane 31 into rows 2 and 3).  Every lane
+// of the wave must be active.
 template <int kCtrl, int kRowMask, typename T>
 __device__ inline T dpp_move(T v) {
   static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
