@@ -99,7 +99,7 @@ int main() {
 namespace sv {
 bool launch_reached = false;
 void launch_rows_stream(const LaunchArgs&, hipStream_t) { launch_reached = true; }
-void launch_rows_generic(const LaunchArgs&, hipStream_t) { launch_reached = true; }
+void launch_rows_dense32(const LaunchArgs&, hipStream_t) { launch_reached = true; }
 void launch_finalize(const LaunchArgs&, hipStream_t) { launch_reached = true; }
 void launch_advance(const LaunchArgs&, hipStream_t, int) { launch_reached = true; }
 }  // namespace sv

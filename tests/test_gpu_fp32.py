@@ -1,11 +1,14 @@
-"""GPU parity of binary32 logits rows on the single-pass kernel: the top-k
-class (greedy, temperature 0, 1 <= top_k <= 64) on 32-bit keys and rows with
-temperature alone (one pass for the maximum and the normaliser); rows with
-top-p or top-k above 64 take the exact profile.  Edge cases use values that
-bf16 cannot tell apart (ties only in binary32 or only in bf16), denormals,
-signed zeros, NaN payloads of both signs, +inf, -inf masks and an odd
-vocabulary so that rows start at every 4-byte alignment.  The B=256, M=8,
-V=128256 top-k/top-p workload in binary32 is checked on every session."""
+"""GPU parity of binary32 logits rows: the single-pass kernel's top-k class
+(greedy, temperature 0, 1 <= top_k <= 64) on 32-bit keys and rows with
+temperature alone (one pass for the maximum and the normaliser), and the
+cut-row kernel's rows with top-p or top-k above 64 (a histogram of coarse
+keys, then a pass that lists the cut's coarse key; rows it hands back take
+the exact profile).  Edge cases use values that bf16 cannot tell apart (ties
+only in binary32 or only in bf16), denormals, signed zeros, NaN payloads of
+both signs, +inf, -inf masks and an odd vocabulary so that rows start at
+every 4-byte alignment.  The B=256, M=8, V=128256 top-k/top-p workload and
+the B=512, M=16, V=151936 ragged top-p workload in binary32 are checked on
+every session."""
 import numpy as np
 import pytest
 import torch
@@ -116,6 +119,87 @@ def test_fp32_temperature_only_edge_cases():
     assert o["accepted_len"][1] == M
     g = parity.run_gpu(h)
     parity.compare(g, o, "fp32-temperature-edges", prob_rtol=parity.DENSE_PROB_RTOL)
+
+
+def test_fp32_cut_rows_edge_cases():
+    """Rows with top-p or top-k above 64: the cut in one coarse key (1/128
+    octave) listed and settled on exact keys, top-k and top-p cutting in the
+    same or in different coarse keys, ties only in binary32, and the rows the
+    kernel hands back to the exact profile (a coarse key with more tokens than
+    its list holds, |lmax| / T beyond its precision bound, a cut below the
+    window)."""
+    parity.log("[case] fp32 cut rows (top-p, top-k above 64), V=5003")
+    B, M, V = 18, 3, 5003
+    rng, t, d = fp32_case(93, B, M, V)
+    s = oracle.make_sampling(B, 800, 0, 900)
+    rule = np.full(B, 2, np.int32)
+    m = np.full(B, M, np.int32)
+    s[1]["top_k"] = 100; s[1]["top_p_milli"] = 1000                     # 1: top-k alone
+    s[2]["top_k"] = 200; s[2]["top_p_milli"] = 950                      # 2: both
+    s[3]["top_k"] = 70; s[3]["top_p_milli"] = 500                       # 3: both, tighter
+    t[4] -= 30.0; d[4] -= 30.0; s[4]["top_p_milli"] = 950               # 4: all negative
+    # 5: 600 tokens on 8 binary32 values of one coarse key (ties only in
+    # binary32) above a low background, identical draft
+    t[5] = rng.normal(-6.0, 1.0, size=(M + 1, V)).astype(np.float32)
+    for r in range(M + 1):
+        ids = rng.choice(V, size=600, replace=False)
+        t[5, r, ids] = np.float32(1.0) + rng.integers(0, 8, size=600).astype(np.float32) * np.float32(2.0 ** -20)
+    d[5] = t[5, :M]; s[5]["top_p_milli"] = 700
+    # 6: 2000 distinct values in one coarse key: more than the list holds
+    t[6] = rng.normal(-8.0, 1.0, size=(M + 1, V)).astype(np.float32)
+    for r in range(M + 1):
+        ids = rng.choice(V, size=2000, replace=False)
+        t[6, r, ids] = np.float32(1.0) + rng.permutation(2000).astype(np.float32) * np.float32(2.0 ** -21)
+    d[6] = t[6, :M]; s[6]["top_p_milli"] = 500
+    t[7][:, rng.random(V) < 0.7] = -np.inf                              # 7: -inf masks
+    d[7][:, rng.random(V) < 0.7] = -np.inf
+    t[8] *= 40.0; d[8] *= 40.0; s[8]["temperature_milli"] = 500         # 8: |lmax| / T large
+    # 9: denormals and signed zeros of both signs around a few normal values
+    t[9] = (rng.normal(0, 1, size=(M + 1, V)) * 1e-39).astype(np.float32)
+    t[9, :, ::7] = -0.0; t[9, :, 3::7] = 0.0; t[9, :, 100:110] = 0.5
+    d[9] = t[9, :M]; s[9]["temperature_milli"] = 1000
+    ramp = np.linspace(-5.0, 30.0, V, dtype=np.float32)               # 10: a rising maximum
+    t[10] = ramp + rng.normal(0, 0.3, size=(M + 1, V)); d[10] = t[10, :M] + rng.normal(0, 0.3, (M, V))
+    s[10]["top_p_milli"] = 950
+    s[11]["top_p_milli"] = 999; s[11]["temperature_milli"] = 3000       # 11: a cut deep down
+    s[12]["top_k"] = V - 1; s[12]["top_p_milli"] = 1000                 # 12: top-k just below V
+    t[13] = -np.inf; d[13] = -np.inf; t[13, :, 4000] = 1.0; d[13, :, 4000] = 2.0  # 13: one finite
+    t[14] = rng.integers(0, 4, size=(M + 1, V)); d[14] = t[14, :M]      # 14: few values, many ties
+    s[14]["top_k"] = 300; s[14]["top_p_milli"] = 800
+    tb, db = t.copy(), d.copy()
+    tb.view(np.uint32)[15, 1, 2500] = 0x7FC00003    # 15: positive NaN
+    db.view(np.uint32)[16, 2, 17] = 0xFFC00001      # 16: negative NaN in a draft row
+    tb.view(np.uint32)[17, 3, 4000] = 0x7F800000    # 17: +inf in the bonus row
+    h = dict(target=tb, draft=db, tokens=np.zeros((B, M), np.int32), m=m, rule=rule,
+             sampling=s, seed=29, round=3)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    for b in (15, 16, 17):
+        h["tokens"][b] = rng.integers(0, V, size=M)
+    o = parity.run_oracle(h)
+    assert (o["accepted_len"][[15, 16, 17]] == oracle.S_BAD_LOGITS).all()
+    g = parity.run_gpu(h)
+    parity.compare(g, o, "fp32-cut-edges", prob_rtol=parity.DENSE_PROB_RTOL)
+
+
+@pytest.mark.parametrize("window", [None, 1])
+def test_fp32_ragged_full_size_every_session(window):
+    """The B=512, M=16, V=151936 ragged workload (top-p 0.95, 30% greedy
+    sessions) with binary32 logits, every session; also read in order
+    (windows of positions), where the cut-row kernel takes each window's
+    rows."""
+    parity.log(f"[case] ragged in fp32, full size, every session, window={window}")
+    import token_sampling_amd as sv
+    w = W.make("ragged", device="cuda", logits="fp32")
+    out = sv.verify(w.target, w.draft, w.tokens, w.m, w.rule, w.sampling_tensor("cuda"),
+                    w.seed, w.round, probe=True, early=window)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    a = g["accepted_len"]
+    assert np.all((a >= 0) | (a == oracle.S_BAD_PROPOSAL))
+    del out
+    o = parity.run_oracle_sessions(w, early=window is not None)
+    rep = parity.compare(g, o, f"fp32-ragged-full-w{window}", prob_rtol=parity.DENSE_PROB_RTOL)
+    assert rep["sessions"] == 512
 
 
 @pytest.mark.parametrize("window", [None, 1])

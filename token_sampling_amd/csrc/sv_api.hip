@@ -3,7 +3,8 @@
 // sv_verify and sv_verify_sdcp check their scalar arguments on the host, carve
 // the caller's workspace and enqueue the kernels on the caller's stream:
 //   single-pass row kernel (session statuses, then each row by the top-k or
-//   the dense path) -> generic row kernel (every other row) -> finalize
+//   the dense path) -> binary32 cut-row kernel (binary32 rows with top-p or
+//   top-k above 64) -> finalize
 //   (acceptance, and the additional token's draw).
 // With SDCP values the single-pass kernel's first workgroups also compute them;
 // sv_verify_commit adds workgroups in front of those that chain the drafted
@@ -161,7 +162,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
   if (window0 == 0) {
     launch_rows_stream(a, st);
     if (g_row_ev[1]) (void)hipEventRecord(g_row_ev[1], st);
-    launch_rows_generic(a, st);
+    launch_rows_dense32(a, st);
   } else {
     // windows of positions [lo, lo + w), w growing, the last one ending at M+1
     int w = window0;
@@ -169,7 +170,7 @@ static int verify_impl(const void* target_logits, const void* draft_logits, cons
       a.win_lo = lo;
       a.win_w = w < M + 2 - lo ? w : M + 2 - lo;
       launch_rows_stream(a, st);
-      launch_rows_generic(a, st);
+      launch_rows_dense32(a, st);
       const int hi = lo + a.win_w - 1;
       if (hi < M + 1) launch_advance(a, st, hi);  // after the last window: the finalize
       lo = hi + 1;

@@ -114,7 +114,7 @@ __host__ __device__ inline bool row_uses_topk_kernel(int32_t dtype, int32_t rule
 // The single-pass kernel's dense path takes every other bf16 row (temperature
 // > 0 with top-k off or above 64, with or without top-p), and the binary32
 // rows with temperature alone (top-k and top-p off); other binary32 rows take
-// the generic kernel's exact profile.
+// k_rows_dense32 (sv_rows_dense32.hip).
 __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rule,
                                                       const sv_sampling& s, int32_t V) {
   if (row_uses_topk_kernel(dtype, rule, s)) return false;
@@ -145,7 +145,7 @@ __device__ inline int launch_slot(int g, int M, int win_lo, int win_w) {
 WorkspaceLayout workspace_layout(int32_t B, int32_t M, int32_t V);
 
 void launch_rows_stream(const LaunchArgs& a, hipStream_t st);
-void launch_rows_generic(const LaunchArgs& a, hipStream_t st);
+void launch_rows_dense32(const LaunchArgs& a, hipStream_t st);
 void launch_finalize(const LaunchArgs& a, hipStream_t st);
 void launch_advance(const LaunchArgs& a, hipStream_t st, int hi);
 void launch_commit(const sv_contract* contracts, sv_session_state* states, const int32_t* m,

@@ -9,7 +9,7 @@
 // exactly by the same wave (sv_rows_exact.hpp).  Binary32 rows take the top-k
 // path on 32-bit keys (topk32::row_profile) or, with temperature alone, the
 // dense pass (dense::row_profile_f32_untruncated); binary32 rows with top-p or
-// top-k above 64 are left to the generic kernel.  Each wave also takes its session's statuses that need no
+// top-k above 64 are left to k_rows_dense32.  Each wave also takes its session's statuses that need no
 // logits (SDCP Table 2, Sec. 6.3 step 5: limit, profile, q availability,
 // drafted tokens in range); the wave of a session's first row slot records
 // them for the kernels that follow.
@@ -154,7 +154,7 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
     else
       back = dense::row_profile_f32_untruncated(row, V, smp, x, rec);
   } else {
-    return;  // binary32 rows with top-p or top-k above 64: the generic kernel
+    return;  // binary32 rows with top-p or top-k above 64: k_rows_dense32
   }
   if (back) {  // the exact profile, by this wave
     if (lane == 0) draw_flag[b] = draw_token;
