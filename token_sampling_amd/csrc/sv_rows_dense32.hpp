@@ -157,9 +157,12 @@ __device__ __attribute__((always_inline)) inline void pass1_vec(Lane& L, Window&
   float w[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
+    // in the window: 2^((l - r) s) relative to the bin's reference r (l - r
+    // exact: the same sign and exponent); below it: 2^(l sf - q).  Selects of
+    // operands, not of two expressions, so that no branch is taken per logit.
     const bool in = f[e] >= W.lo_v;
-    const float dl = f[e] - cref(f[e]);  // exact: same sign and exponent
-    const float ex = in ? __builtin_fmaf(dl, sc.sf, dl * df) : __builtin_fmaf(f[e], sc.sf, -L.q);
+    const float dl = f[e] - (in ? cref(f[e]) : 0.0f);
+    const float ex = __builtin_fmaf(dl, sc.sf, in ? dl * df : -L.q);
     const float t = __builtin_amdgcn_exp2f(ex);
     if (in) {
       const int i = skey_of(f[e]) & (kWin - 1);
@@ -224,11 +227,15 @@ __device__ inline List list_key(const RowWin& R, int c, int n, float lmax, const
                                 void* lds) {
   List Ls{(uint64_t*)lds, (double*)((char*)lds + kMemberCap * 8), 0};
   int k = 0;
+  // the upper 16 bits of the key's logits (either sign for key 0); c is above
+  // -inf's key, so no masked position matches
+  const uint32_t cmask = c == 0 ? 0x7FFFu : 0xFFFFu;
+  const uint32_t cbits = c >= 0 ? (uint32_t)c : (0x8000u | (uint32_t)(-c));
   stream_row(R, [&](const u32x4& v, int p0) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t bits = elem(v, e);
-      const bool hit = skey_of(__uint_as_float(bits)) == c;  // c > kNegInfKey: no masked position
+      const bool hit = ((bits >> 16) & cmask) == cbits;
       const uint64_t mk = __ballot(hit);
       if (mk) {
         const int at = k + lanes_below(mk);
