@@ -4,7 +4,8 @@
 A step is one sv_verify call (sv_verify_sdcp with --sdcp, sv_verify_qrows with
 --qrows, sv_verify_early with --early W) over one batch of synthetic logits
 already resident in HBM: the single-pass row kernel (session checks and the row
-profiles, the HBM-streaming part), the generic row kernel, and the per-session
+profiles, the HBM-streaming part), the binary32 cut-row kernel (binary32 rows
+with top-p or top-k above 64), and the per-session
 kernel (acceptance and the additional token).  With --early the rows are read in
 windows of positions, and the roofline line counts the rows the sessions need
 (a+1 target rows and, for rule 2, a+1 draft rows) over the time of all the
@@ -60,7 +61,7 @@ def row_kernel_hash() -> str:
 def kernel_short_name(full: str) -> str:
     import re
 
-    m = re.search(r"(k_rows_stream|k_rows_split<\d+>|k_rows_generic|k_finalize|k_advance|k_commit)",
+    m = re.search(r"(k_rows_stream|k_rows_split<\d+>|k_rows_dense32|k_finalize|k_advance|k_commit)",
                   full)
     return m.group(1) if m else ""
 
@@ -282,8 +283,8 @@ def measure(w, args, sv, torch, draft, q_rows=None, sdcp=None, early=None, commi
         step()
     torch.cuda.synchronize()
     # bf16 rows are all taken by the single-pass kernel: two events bracket it;
-    # binary32 rows may also take the generic kernel: a third event between the
-    # two.  Read in order, two events bracket all the windows' row and advance
+    # binary32 rows may also take the cut-row kernel: a third event between
+    # the two.  Read in order, two events bracket all the windows' row and advance
     # kernels.
     n_ev = 2 if (w.target.dtype == torch.bfloat16 or early) else 3
     row_ev = [tuple(sv.HipEvent() for _ in range(n_ev)) for _ in range(args.steps)]
@@ -315,9 +316,9 @@ def measure(w, args, sv, torch, draft, q_rows=None, sdcp=None, early=None, commi
         step(row_ev[k])
     torch.cuda.synchronize()
     stream_ms = sum(e[0].elapsed_ms(e[1]) for e in row_ev) / args.steps
-    generic_ms = 0.0 if n_ev == 2 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
+    dense32_ms = 0.0 if n_ev == 2 else sum(e[1].elapsed_ms(e[2]) for e in row_ev) / args.steps
     del junk
-    return {"ms_per_step": ms_per_step, "stream_ms": stream_ms, "generic_ms": generic_ms,
+    return {"ms_per_step": ms_per_step, "stream_ms": stream_ms, "dense32_ms": dense32_ms,
             "accepted_len": out["accepted_len"].cpu().numpy(),
             "out_tokens": out["out_tokens"].cpu().numpy()}
 
@@ -330,9 +331,9 @@ def roofline(w, r, qrows=False, early=False):
 
     B, M = w.B, w.M
     split = w.row_bytes_by_kernel(q_rows=qrows)
-    stream_ms, generic_ms = r["stream_ms"], r["generic_ms"]
-    kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= generic_ms
-                          else ("k_rows_generic", generic_ms, split["generic"]))
+    stream_ms, dense32_ms = r["stream_ms"], r["dense32_ms"]
+    kname, kms, kbytes = (("k_rows_stream", stream_ms, split["stream"]) if stream_ms >= dense32_ms
+                          else ("k_rows_dense32", dense32_ms, split["dense32"]))
     rows = B * (M + 1) + (B * M if not qrows else 0)
     if kname == "k_rows_stream" and w.target.dtype.itemsize == 2 and rows < 1024:
         kname = "k_rows_split<4>"  # bf16 launches under 1024 row slots split each row
@@ -349,13 +350,13 @@ def roofline(w, r, qrows=False, early=False):
         if not qrows:
             rows_needed += np.minimum(e, mm)[ok & r2].sum()
         kname = "row kernels, all windows"
-        kms = stream_ms + generic_ms
+        kms = stream_ms + dense32_ms
         kbytes = int(rows_needed) * w.V * w.target.element_size()
     achieved = kbytes / (kms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "kernel": kname, "ms_per_launch": kms,
             "algorithmic_bytes_per_launch": kbytes,
-            "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_generic": generic_ms}}
+            "row_kernels_ms": {"k_rows_stream": stream_ms, "k_rows_dense32": dense32_ms}}
 
 
 def cpu_model():
@@ -492,7 +493,7 @@ def main():
     r = measure(w, args, sv, torch, draft, q_rows=q_rows, sdcp=sdcp, early=args.early,
                 commit=args.commit)
     log(f"[bench] {args.steps} steps: {r['ms_per_step']:.4f} ms/step, single-pass row kernel "
-        f"{r['stream_ms']:.4f} ms, generic row kernel {r['generic_ms']:.4f} ms")
+        f"{r['stream_ms']:.4f} ms, binary32 cut-row kernel {r['dense32_ms']:.4f} ms")
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

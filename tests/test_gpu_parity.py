@@ -291,7 +291,7 @@ def test_dense_kernel_edge_cases(split, monkeypatch):
     """Rows handled by the one-pass dense path (temperature, optional top-p,
     top-k off): a maximum that rises tile after tile, heavy ties at the cut,
     drafted tokens on both sides of a tied cut, a cut below the histogram
-    window (generic fallback), all-negative rows, masks, bad logits; an odd
+    window (the exact fallback), all-negative rows, masks, bad logits; an odd
     vocabulary of five tiles so that rows start at every alignment.  Each row
     by one wave, or split over four (histogram windows and ranks merged)."""
     monkeypatch.setenv("SV_ROWS_SPLIT", split)
@@ -358,7 +358,7 @@ def test_dense_topk_above_64_edge_cases(split, monkeypatch):
     histogram window: top-k alone and top-k then top-p, ties split at the
     top-k cut with drafted tokens on both sides of it, all-negative rows, a
     rising maximum, -inf masks leaving fewer than K finite tokens, and a
-    window holding fewer than K tokens (the generic fallback)."""
+    window holding fewer than K tokens (the exact fallback)."""
     monkeypatch.setenv("SV_ROWS_SPLIT", split)
     parity.log(f"[case] dense path, top_k above 64, V=5003, split={split}")
     B, M, V = 12, 3, 5003
@@ -431,7 +431,7 @@ def test_split_rows_each_factor(split, monkeypatch):
     (forced through SV_ROWS_SPLIT; top-k-class rows use at most 4), on top-k,
     one-hot and dense profiles,
     a vocabulary of one tile (waves with empty parts), and rows that overflow
-    the candidate region (handed to the generic kernel)."""
+    the candidate region (profiled exactly by the same wave)."""
     monkeypatch.setenv("SV_ROWS_SPLIT", split)
     parity.log(f"[case] split={split}")
     for seed, B, M, V in ((111, 24, 5, 20000), (112, 12, 3, 300), (113, 8, 2, 4097)):

@@ -1,6 +1,6 @@
 """GPU parity of the relaxed rule (private-use rule 192: accept x_i while
 p_i(x_i) > 0, then draw the additional token from p_{a+1}) against the oracle,
-mixed with the other rules, on the top-k, dense and generic row paths, with
+mixed with the other rules, on the top-k, dense and binary32 cut-row paths, with
 Philox and SDCP values, with draft logits and with published q rows, and on
 the b256 workload at full size (every session)."""
 import numpy as np

@@ -123,22 +123,23 @@ class Workload:
         """Row bytes read by each row kernel: the single-pass kernel takes every
         bf16 row, and the binary32 rows of the top-k class (greedy rule,
         temperature 0, 1 <= top_k <= 64) or with temperature alone; the
-        generic kernel the other binary32 rows.  Rows a path hands back are not
-        counted (that depends on the logits).  With q_rows no draft row is
-        profiled."""
+        binary32 cut-row kernel the other binary32 rows (each counted once,
+        though it reads the cut's coarse key in a second pass).  Rows a path
+        hands back are not counted (that depends on the logits).  With q_rows
+        no draft row is profiled."""
         m = self.m.to("cpu").to(torch.int64).numpy()
         rule = self.rule.to("cpu").to(torch.int64).numpy()
         per_session = (m + 1) + (0 if q_rows else m * (rule == 2))
         row = self.V * self.target.element_size()
         total = int(per_session.sum()) * row
         if self.target.dtype == torch.bfloat16:
-            return {"stream": total, "generic": 0}
+            return {"stream": total, "dense32": 0}
         s = self.sampling
         topk_class = (rule == 1) | (s["temperature_milli"] == 0) | \
             ((s["top_k"] >= 1) & (s["top_k"] <= 64))
         untruncated = (s["top_p_milli"] >= 1000) & ((s["top_k"] == 0) | (s["top_k"] >= self.V))
         stream = int(per_session[topk_class | untruncated].sum()) * row
-        return {"stream": stream, "generic": total - stream}
+        return {"stream": stream, "dense32": total - stream}
 
 
 def _to_storage(x32: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
