@@ -87,6 +87,7 @@ struct Window {
   float edge;      // largest value of coarse key anchor: a larger logit moves the window
   float lo_v;      // smallest value of the window's lowest coarse key
   float dref;      // the lanes' departed masses are relative to this value
+  int lo;          // the window's lowest coarse key
 };
 struct Lane {
   float mv;    // this lane's largest logit
@@ -138,7 +139,35 @@ __device__ inline void window_move(Lane& L, Window& W, int tk, const Scales& sc)
   W.dref = nref;
   W.anchor = __builtin_amdgcn_readfirstlane(tk);
   W.edge = uni(top_of(tk));
-  W.lo_v = uni(bottom_of(max(tk - (kWin - 1), kNegInfKey + 1)));
+  W.lo = __builtin_amdgcn_readfirstlane(max(tk - (kWin - 1), kNegInfKey + 1));
+  W.lo_v = uni(bottom_of(W.lo));
+}
+
+// The 4 logits of a vector: counted and weighed in their bins (in the
+// window), else added to the binary32 sum.
+template <bool kPos>
+__device__ __attribute__((always_inline)) inline void pass1_tokens(Lane& L, Window& W,
+                                                                   const float (&f)[4],
+                                                                   const Scales& sc, float df) {
+  float w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // in the window: 2^((l - r) s) relative to the bin's reference r (l - r
+    // exact: the same sign and exponent); below it: 2^(l sf - q).  Selects of
+    // operands, not of two expressions, so that no branch is taken per logit.
+    const bool in = f[e] >= W.lo_v;
+    const float dl = f[e] - (in ? cref(f[e]) : 0.0f);
+    const float ex = __builtin_fmaf(dl, sc.sf, in ? dl * df : -L.q);
+    const float t = __builtin_amdgcn_exp2f(ex);
+    if (in) {
+      const int i = kPos ? (int)__builtin_amdgcn_ubfe(__float_as_uint(f[e]), 16, 10)
+                         : skey_of(f[e]) & (kWin - 1);
+      atomicAdd(&W.cnt[i], 1u);
+      atomicAdd(&W.mass[i], (double)t);
+    }
+    w[e] = in ? 0.0f : t;
+  }
+  L.s += (double)((w[0] + w[1]) + (w[2] + w[3]));
 }
 
 // One 16-byte vector (4 logits) of the first pass.
@@ -154,24 +183,9 @@ __device__ __attribute__((always_inline)) inline void pass1_vec(Lane& L, Window&
     const int tk = wave_reduce(up ? skey_of(lmv) : INT32_MIN, OpMax());
     window_move(L, W, tk, sc);
   }
-  float w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    // in the window: 2^((l - r) s) relative to the bin's reference r (l - r
-    // exact: the same sign and exponent); below it: 2^(l sf - q).  Selects of
-    // operands, not of two expressions, so that no branch is taken per logit.
-    const bool in = f[e] >= W.lo_v;
-    const float dl = f[e] - (in ? cref(f[e]) : 0.0f);
-    const float ex = __builtin_fmaf(dl, sc.sf, in ? dl * df : -L.q);
-    const float t = __builtin_amdgcn_exp2f(ex);
-    if (in) {
-      const int i = skey_of(f[e]) & (kWin - 1);
-      atomicAdd(&W.cnt[i], 1u);
-      atomicAdd(&W.mass[i], (double)t);
-    }
-    w[e] = in ? 0.0f : t;
-  }
-  L.s += (double)((w[0] + w[1]) + (w[2] + w[3]));
+  // a window of positive keys: a logit's bin is bits 16..25 of its bits
+  if (W.lo > 0) pass1_tokens<true>(L, W, f, sc, df);
+  else pass1_tokens<false>(L, W, f, sc, df);
 }
 
 // The row's layout: a 16-byte aligned window in which [head, head + V) is the row.
@@ -281,7 +295,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile(
   const float df = uni((float)sc.d);
   const RowWin R = row_window(row, V);
   Window W{(double*)lds, (uint32_t*)((char*)lds + kWin * 8), kNoAnchor, -__builtin_huge_valf(),
-           __builtin_huge_valf(), 0.0f};
+           __builtin_huge_valf(), 0.0f, kNoAnchor};
   Lane L{-__builtin_huge_valf(), 0.0f, 0.0, 0.0, false};
   stream_row(R, [&](const u32x4& v, int) { pass1_vec(L, W, v, sc, df); });
   const float lmax = dense::wave_max(L.mv);
