@@ -181,6 +181,30 @@ def test_fp32_cut_rows_edge_cases():
     parity.compare(g, o, "fp32-cut-edges", prob_rtol=parity.DENSE_PROB_RTOL)
 
 
+@pytest.mark.parametrize("V", [1, 2, 7, 515, 2049])
+def test_fp32_cut_rows_small_vocabularies(V):
+    """Binary32 cut rows on vocabularies of one token up to a few tiles, with
+    ties, -inf masks and both signs, under top-p and top-k above 64."""
+    parity.log(f"[case] fp32 cut rows, V={V}")
+    B, M = 8, 2
+    rng, t, d = fp32_case(94 + V, B, M, V)
+    s = oracle.make_sampling(B, 1000, 0, 800)
+    rule = np.full(B, 2, np.int32)
+    m = np.full(B, M, np.int32)
+    t[1] = np.round(t[1]); d[1] = t[1, :M]                             # ties
+    t[2][:, rng.random(V) < 0.5] = -np.inf; d[2] = t[2, :M]            # masks
+    t[3] = -np.abs(t[3]); d[3] = -np.abs(d[3])                          # all negative
+    if V > 65:
+        s[4]["top_k"] = 65; s[5]["top_k"] = 65; s[5]["top_p_milli"] = 1000
+    s[6]["top_p_milli"] = 1; s[7]["temperature_milli"] = 250
+    h = dict(target=t, draft=d, tokens=np.zeros((B, M), np.int32), m=m, rule=rule,
+             sampling=s, seed=31, round=5)
+    h["tokens"] = parity.draw_valid_tokens(h, rng)
+    o = parity.run_oracle(h)
+    g = parity.run_gpu(h)
+    parity.compare(g, o, f"fp32-cut-V{V}", prob_rtol=parity.DENSE_PROB_RTOL)
+
+
 @pytest.mark.parametrize("window", [None, 1])
 def test_fp32_ragged_full_size_every_session(window):
     """The B=512, M=16, V=151936 ragged workload (top-p 0.95, 30% greedy

@@ -230,15 +230,15 @@ __device__ __attribute__((always_inline)) inline void stream_row(const RowWin& R
   }
 }
 
-// The tokens of coarse key c (n of them, n <= kMemberCap), listed in LDS by
-// a pass over the row, with their weights at s relative to lmax.
+// The tokens of coarse key c (the first pass counted at most kMemberCap),
+// listed in LDS by a pass over the row, with their weights at s relative to
+// lmax.
 struct List {
   uint64_t* comp;  // composites, in row order
   double* w;       // weights
   int n;
 };
-__device__ inline List list_key(const RowWin& R, int c, int n, float lmax, const Scales& sc,
-                                void* lds) {
+__device__ inline List list_key(const RowWin& R, int c, float lmax, const Scales& sc, void* lds) {
   List Ls{(uint64_t*)lds, (double*)((char*)lds + kMemberCap * 8), 0};
   int k = 0;
   // the upper 16 bits of the key's logits (either sign for key 0); c is above
@@ -258,14 +258,12 @@ __device__ inline List list_key(const RowWin& R, int c, int n, float lmax, const
       }
     }
   });
-  (void)n;  // the first pass's count of the key: k itself
   Ls.n = min(k, kMemberCap);
   for (int i = __lane_id(); i < Ls.n; i += kWave)
     Ls.w[i] = weight64(F32::value(F32::unkey(comp_key(Ls.comp[i]))), lmax, sc.s);
   return Ls;
 }
-// Count and mass of the listed tokens with key >= t (keep: tokens at key kk
-// beyond the first ck by id are not kept; kk = 0 keeps all).
+// Count and mass of the listed tokens with key >= t.
 __device__ inline uint32_t list_count_ge(const List& Ls, uint32_t t) {
   uint32_t c = 0;
   for (int i = __lane_id(); i < Ls.n; i += kWave) c += comp_key(Ls.comp[i]) >= t ? 1u : 0u;
@@ -371,7 +369,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile(
     // above: tokens in the bins before the cut's, whose coarse key is ck_key
     ck_key = W.anchor - kPerLane * qk - ek;
     if (nk > (uint32_t)kMemberCap) return true;
-    Ls = list_key(R, ck_key, (int)nk, lmax, sc, lds);
+    Ls = list_key(R, ck_key, lmax, sc, lds);
     const uint32_t need = K - above;  // 1 <= need <= nk
     kk = list_kth_key(Ls, need);
     ckk = need - list_count_ge(Ls, kk + 1);
@@ -422,7 +420,7 @@ __device__ __attribute__((always_inline)) inline bool row_profile(
     const bool same = top_k && cp_key == ck_key;
     if (!same) {
       if (np > (uint32_t)kMemberCap) return true;
-      Ls = list_key(R, cp_key, (int)np, lmax, sc, lds);
+      Ls = list_key(R, cp_key, lmax, sc, lds);
     }
     // the largest key kp with 1000 * (c + mass(kept, key >= kp)) >= tgt
     uint32_t t = 0;
