@@ -181,10 +181,12 @@ def test_fp32_cut_rows_edge_cases():
     parity.compare(g, o, "fp32-cut-edges", prob_rtol=parity.DENSE_PROB_RTOL)
 
 
-@pytest.mark.parametrize("V", [1, 2, 7, 515, 2049])
+@pytest.mark.parametrize("V", [1, 2, 7, 515, 2049, 4096, 4097])
 def test_fp32_cut_rows_small_vocabularies(V):
     """Binary32 cut rows on vocabularies of one token up to a few tiles, with
-    ties, -inf masks and both signs, under top-p and top-k above 64."""
+    ties, -inf masks and both signs, under top-p and top-k above 64: up to
+    4096 tokens profiled exactly by the single-pass kernel's wave, above by
+    the cut-row kernel."""
     parity.log(f"[case] fp32 cut rows, V={V}")
     B, M = 8, 2
     rng, t, d = fp32_case(94 + V, B, M, V)

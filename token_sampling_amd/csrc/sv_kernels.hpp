@@ -122,6 +122,12 @@ __host__ __device__ inline bool row_uses_dense_kernel(int32_t dtype, int32_t rul
   return s.top_p_milli >= 1000 && (s.top_k == 0 || s.top_k >= (uint32_t)V);
 }
 
+// Binary32 rows with top-p or top-k above 64 of a vocabulary at most this
+// size are profiled exactly by the single-pass kernel's wave (the exact
+// profile's passes over at most 16 KiB, in cache), which spares the launch of
+// the cut-row kernel k_rows_dense32 for small vocabularies.
+constexpr int kDense32MinV = 4096;
+
 struct WorkspaceLayout {
   size_t rows_off, status_off, supid_off, supp_off, unif_off, chunk_off, ctr_off, flag_off,
       decided_off, chain_off, total;

@@ -50,8 +50,9 @@ __attribute__((amdgpu_waves_per_eu(3))) void k_rows_dense32(
 }  // namespace
 
 void launch_rows_dense32(const LaunchArgs& a, hipStream_t st) {
-  // bf16 rows are all profiled by the single-pass kernel: no launch
-  if (a.dtype != SV_FP32) return;
+  // bf16 rows, and binary32 rows of small vocabularies, are all profiled by the
+  // single-pass kernel: no launch
+  if (a.dtype != SV_FP32 || a.V <= kDense32MinV) return;
   const size_t slots =
       a.win_w == 0 ? (size_t)a.B * (2 * a.M + 1) : (size_t)a.B * 2 * (size_t)a.win_w;
   hipLaunchKernelGGL(k_rows_dense32, dim3((unsigned)slots), dim3(kWave), 0, st,

@@ -9,10 +9,11 @@
 // exactly by the same wave (sv_rows_exact.hpp).  Binary32 rows take the top-k
 // path on 32-bit keys (topk32::row_profile) or, with temperature alone, the
 // dense pass (dense::row_profile_f32_untruncated); binary32 rows with top-p or
-// top-k above 64 are left to k_rows_dense32.  Each wave also takes its session's statuses that need no
-// logits (SDCP Table 2, Sec. 6.3 step 5: limit, profile, q availability,
-// drafted tokens in range); the wave of a session's first row slot records
-// them for the kernels that follow.
+// top-k above 64 are left to k_rows_dense32 (vocabularies above kDense32MinV;
+// below, this wave profiles them exactly).  Each wave also takes its
+// session's statuses that need no logits (SDCP Table 2, Sec. 6.3 step 5:
+// limit, profile, q availability, drafted tokens in range); the wave of a
+// session's first row slot records them for the kernels that follow.
 //
 // With SDCP verifier values (Sec. 6.4) the grid starts with extra workgroups
 // that compute them, one value per lane; they depend on no logits, so they
@@ -153,6 +154,8 @@ __attribute__((amdgpu_waves_per_eu(SV_STREAM_WAVES_PER_EU))) void k_rows_stream(
       back = dense::row_profile(row, V, smp, x, rec, (uint32_t*)lds);
     else
       back = dense::row_profile_f32_untruncated(row, V, smp, x, rec);
+  } else if (V <= kDense32MinV) {
+    back = true;  // a binary32 cut row of a small vocabulary: profiled exactly below
   } else {
     return;  // binary32 rows with top-p or top-k above 64: k_rows_dense32
   }
